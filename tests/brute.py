@@ -1,0 +1,93 @@
+"""Brute-force numpy reference for tiny inputs, written independently of the
+oracle (different algorithms: rank counting instead of sorting, an explicit
+dense N x N mask instead of key ranges) so that the two can pin each other.
+
+Everything is fp64; bf16 inputs arrive as uint16 bit patterns.
+"""
+import numpy as np
+
+from content_routed_block_amd.workloads import bf16_bits_to_f32
+
+
+def widen(x_bits):
+    return bf16_bits_to_f32(x_bits).astype(np.float64)
+
+
+def block_means(xf, bs):
+    """xf: float64 [..., N, D] -> float32 [..., N/bs, D] (fp64 mean, one rounding)."""
+    *lead, N, D = xf.shape
+    return xf.reshape(*lead, N // bs, bs, D).mean(axis=-2).astype(np.float32)
+
+
+def rank_select(scores, ncand, k):
+    """Selection by rank counting: candidate c is kept when fewer than k
+    candidates beat it, where c' beats c if s[c'] > s[c], or s[c'] == s[c]
+    and c' < c.  Returns the kept block ids in ascending order."""
+    keep = []
+    for c in range(ncand):
+        beaten = 0
+        for c2 in range(ncand):
+            if scores[c2] > scores[c] or (scores[c2] == scores[c] and c2 < c):
+                beaten += 1
+        if beaten < k:
+            keep.append(c)
+    return keep
+
+
+def causal_mask(N, bs, window, top_k, q_f64, kbar, rep):
+    """Dense boolean mask [Hq, N, N] of the keys each causal query attends to.
+    q_f64: [Hq, N, D]; kbar: float32 [Hkv, nb, D]."""
+    Hq = q_f64.shape[0]
+    mask = np.zeros((Hq, N, N), dtype=bool)
+    wb = window // bs
+    for h in range(Hq):
+        g = h // rep
+        for t in range(N):
+            ncand = max(0, t // bs - wb + 1)
+            s = [float(np.dot(q_f64[h, t], kbar[g, c].astype(np.float64))) for c in range(ncand)]
+            for c in rank_select(s, ncand, top_k):
+                mask[h, t, c * bs:(c + 1) * bs] = True
+            mask[h, t, ncand * bs:t + 1] = True
+    return mask
+
+
+def image_mask(N, bs, top_k, qbar, kbar, rep):
+    Hq = qbar.shape[0]
+    nb = N // bs
+    mask = np.zeros((Hq, N, N), dtype=bool)
+    for h in range(Hq):
+        g = h // rep
+        for i in range(nb):
+            s = [float(np.dot(qbar[h, i].astype(np.float64), kbar[g, c].astype(np.float64)))
+                 for c in range(nb)]
+            for c in rank_select(s, nb, top_k):
+                mask[h, i * bs:(i + 1) * bs, c * bs:(c + 1) * bs] = True
+    return mask
+
+
+def masked_softmax_attention(q_f64, k_f64, v_f64, mask, rep, scale):
+    """q [Hq,N,D], k/v [Hkv,N,D], mask [Hq,N,N] -> [Hq,N,D] fp64."""
+    Hq, N, D = q_f64.shape
+    out = np.empty((Hq, N, D))
+    for h in range(Hq):
+        g = h // rep
+        logits = (q_f64[h] @ k_f64[g].T) * scale
+        logits = np.where(mask[h], logits, -np.inf)
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        out[h] = (p @ v_f64[g]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def forward(q_bits, k_bits, v_bits, bs, top_k, window, causal, scale=None):
+    """End-to-end brute force for one batch element: q [Hq,N,D], k/v [Hkv,N,D]."""
+    qf, kf, vf = widen(q_bits), widen(k_bits), widen(v_bits)
+    Hq, N, D = qf.shape
+    rep = Hq // kf.shape[0]
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    kbar = block_means(kf, bs)
+    if causal:
+        mask = causal_mask(N, bs, window, top_k, qf, kbar, rep)
+    else:
+        mask = image_mask(N, bs, top_k, block_means(qf, bs), kbar, rep)
+    return masked_softmax_attention(qf, kf, vf, mask, rep, scale), mask

@@ -1,0 +1,323 @@
+"""Pins of the CPU oracle against things other than itself: a hand-worked
+example, closed forms, invariants, special cases that reduce to dense
+attention (torch CPU SDPA in fp64), and an independent numpy brute force on
+tiny inputs.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from content_routed_block_amd.workloads import (WORKLOADS, bf16_bits_to_f32, generate,
+                                                to_bf16_bits)
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_bits(rng, shape, scale=1.0):
+    return to_bf16_bits(scale * rng.standard_normal(shape).astype(np.float32))
+
+
+def sdpa_f64(qb, kb, vb, causal, scale=None):
+    """Dense attention, torch CPU, fp64.  q [B,Hq,N,D], k/v [B,Hkv,N,D] bits."""
+    q = torch.from_numpy(brute.widen(qb))
+    k = torch.from_numpy(brute.widen(kb))
+    v = torch.from_numpy(brute.widen(vb))
+    rep = q.shape[1] // k.shape[1]
+    k = k.repeat_interleave(rep, dim=1)
+    v = v.repeat_interleave(rep, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, is_causal=bool(causal), scale=scale).numpy()
+
+
+# ---------------------------------------------------------------- hand example
+def test_hand_example(orc):
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    bs, k, W = g["block"], g["top_k"], g["window"]
+    K = to_bf16_bits(np.array(g["k"], np.float32))[None, None]
+    V = to_bf16_bits(np.array(g["v"], np.float32))[None, None]
+    Q = to_bf16_bits(np.array(g["q"], np.float32))[None, None]
+    kbar = orc.block_means(K, bs)
+    np.testing.assert_array_equal(kbar[0, 0], np.array(g["kbar"], np.float32))
+    idx, gap = orc.route_causal(Q, kbar, bs, k, W, with_gap=True)
+    scores = orc.route_scores(kbar, np.arange(8), q=Q, block=bs, window=W, causal=1)
+    out = orc.attend(Q, K, V, idx.reshape(-1, k), bs, k, W, 1, scale=g["scale"])
+    vv = np.array(g["v"], np.float64)
+    for row in g["rows"]:
+        t = row["t"]
+        assert list(idx[0, 0, t]) == row["sel"], t
+        exp_gap = math.inf if row["gap"] == "inf" else row["gap"]
+        assert gap[0, 0, t] == exp_gap, t
+        E = row["E"]
+        np.testing.assert_array_equal(scores[t, :E], row["scores"])
+        assert np.all(np.isneginf(scores[t, E:]))
+        w = np.exp(np.array(row["dots"], np.float64) / math.sqrt(2.0))
+        expect = (w[:, None] * vv[row["keys"]]).sum(0) / w.sum()
+        np.testing.assert_allclose(out[0, 0, t], expect, rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------- block means
+def test_means_constant_blocks(orc):
+    rng = np.random.default_rng(0)
+    bs, nb, D = 32, 6, 16
+    consts = rand_bits(rng, (2, nb, D))
+    x = np.repeat(consts[:, :, None, :], bs, axis=2).reshape(2, nb * bs, D)
+    got = orc.block_means(x, bs)
+    np.testing.assert_array_equal(got, bf16_bits_to_f32(consts))
+
+
+def test_means_arithmetic_progression(orc):
+    bs, D = 64, 8
+    j = np.arange(bs, dtype=np.float32)[:, None]
+    d = np.arange(D, dtype=np.float32)[None, :]
+    x = to_bf16_bits((j + d) / 4.0)            # exact in bf16
+    got = orc.block_means(x[None], bs)[0, 0]
+    np.testing.assert_array_equal(got, (31.5 + np.arange(D)) / 4.0)
+
+
+def test_means_permutation_invariant_and_local(orc):
+    rng = np.random.default_rng(1)
+    bs, nb, D = 64, 5, 64
+    x = rand_bits(rng, (1, nb * bs, D))
+    base = orc.block_means(x, bs)
+    perm = np.concatenate([c * bs + rng.permutation(bs) for c in range(nb)])
+    np.testing.assert_array_equal(orc.block_means(x[:, perm], bs), base)
+    y = x.copy()
+    y[0, 2 * bs + 7] = to_bf16_bits(bf16_bits_to_f32(y[0, 2 * bs + 7]) + 8.0)
+    changed = orc.block_means(y, bs)
+    for c in range(nb):
+        if c != 2:
+            np.testing.assert_array_equal(changed[0, c], base[0, c])
+    np.testing.assert_allclose(
+        changed[0, 2].astype(np.float64) - base[0, 2],
+        (bf16_bits_to_f32(y[0, 2 * bs + 7]).astype(np.float64)
+         - bf16_bits_to_f32(x[0, 2 * bs + 7])) / bs, atol=1e-6)
+
+
+# ---------------------------------------------------------------- routing
+def test_route_all_ties_pick_lowest_blocks(orc):
+    bs, W, k, N, D = 16, 32, 3, 256, 8
+    Q = to_bf16_bits(np.random.default_rng(2).standard_normal((1, 2, N, D)).astype(np.float32))
+    K = to_bf16_bits(np.full((1, 1, N, D), 0.5, np.float32))
+    kbar = orc.block_means(K, bs)
+    idx, gap = orc.route_causal(Q, kbar, bs, k, W, with_gap=True)
+    for t in range(N):
+        E = max(0, t // bs - W // bs + 1)
+        want = list(range(min(k, E))) + [-1] * (k - min(k, E))
+        assert list(idx[0, 0, t]) == want and list(idx[0, 1, t]) == want
+        assert gap[0, 0, t] == (0.0 if E > k else math.inf)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_route_monotone_scores(orc, sign):
+    bs, W, k, N, D = 16, 48, 4, 320, 8
+    K = np.zeros((1, 1, N, D), np.float32)
+    for c in range(N // bs):
+        K[0, 0, c * bs:(c + 1) * bs, 0] = c + 1
+    Q = np.zeros((1, 1, N, D), np.float32)
+    Q[..., 0] = sign
+    kb, qb = to_bf16_bits(K), to_bf16_bits(Q)
+    idx = orc.route_causal(qb, orc.block_means(kb, bs), bs, k, W)
+    for t in range(N):
+        E = max(0, t // bs - W // bs + 1)
+        n = min(k, E)
+        want = list(range(E - n, E)) if sign > 0 else list(range(n))
+        assert list(idx[0, 0, t]) == want + [-1] * (k - n), t
+
+
+@pytest.mark.parametrize("bs,W,k,Hq,Hkv", [(16, 32, 3, 4, 2), (8, 8, 2, 2, 1), (32, 96, 1, 3, 3)])
+def test_route_matches_rank_brute_force(orc, bs, W, k, Hq, Hkv):
+    rng = np.random.default_rng(bs * 100 + k)
+    N, D = 256, 16
+    Q = rand_bits(rng, (1, Hq, N, D))
+    K = rand_bits(rng, (1, Hkv, N, D))
+    kbar = orc.block_means(K, bs)
+    kbar_np = brute.block_means(brute.widen(K), bs)
+    np.testing.assert_array_equal(kbar, kbar_np)
+    idx, gap = orc.route_causal(Q, kbar, bs, k, W, with_gap=True)
+    qf = brute.widen(Q)
+    rep = Hq // Hkv
+    for h in range(Hq):
+        for t in range(N):
+            E = max(0, t // bs - W // bs + 1)
+            s = [float(np.dot(qf[0, h, t], kbar_np[0, h // rep, c].astype(np.float64)))
+                 for c in range(E)]
+            keep = brute.rank_select(s, E, k)
+            assert list(idx[0, h, t]) == keep + [-1] * (k - len(keep)), (h, t)
+            if E > k:
+                ss = sorted(s, reverse=True)
+                assert gap[0, h, t] == pytest.approx(ss[k - 1] - ss[k], abs=1e-12)
+            else:
+                assert gap[0, h, t] == math.inf
+
+
+def test_route_eligible_counts_tiny_config(orc):
+    """With top-k >= number of blocks every eligible block is selected; the
+    total candidate count of the tiny 1K config is 64 * (1 + ... + 14) per
+    head, and no selected block reaches the window."""
+    w = WORKLOADS["tiny_causal_n1024"]
+    inp = generate(w)
+    kbar = orc.block_means(inp.k, w.block)
+    nb = w.seq_len // w.block
+    idx = orc.route_causal(inp.q, kbar, w.block, nb, w.window)
+    valid = idx >= 0
+    assert valid.sum() == 2 * 64 * sum(range(15)) == 13440
+    t = np.arange(w.seq_len)[None, None, :, None]
+    assert np.all(np.where(valid, idx, -10**9) <= t // w.block - w.window // w.block)
+    for tt in range(w.seq_len):
+        E = max(0, tt // 64 - 1)
+        assert list(idx[0, 0, tt, :E]) == list(range(E))
+
+
+def test_route_invariant_under_signed_permutation(orc):
+    """One common linear isometry of all queries and keys leaves the selected
+    set unchanged (SSA page, 'Mathematical status').  A signed permutation of
+    the coordinates is an isometry that is exact in bf16."""
+    rng = np.random.default_rng(5)
+    bs, W, k, N, D = 16, 32, 4, 512, 32
+    Q = rand_bits(rng, (1, 2, N, D))
+    K = rand_bits(rng, (1, 1, N, D))
+    perm = rng.permutation(D)
+    flip = np.where(rng.random(D) < 0.5, 0x8000, 0).astype(np.uint16)
+    Q2 = Q[..., perm] ^ flip
+    K2 = K[..., perm] ^ flip
+    i1, g1 = orc.route_causal(Q, orc.block_means(K, bs), bs, k, W, with_gap=True)
+    i2 = orc.route_causal(Q2, orc.block_means(K2, bs), bs, k, W)
+    clear = g1 > 1e-9
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(i1[clear], i2[clear])
+
+
+def test_route_huge_needle_always_selected(orc):
+    rng = np.random.default_rng(6)
+    bs, W, k, N, D = 32, 64, 2, 1024, 64
+    Q = rand_bits(rng, (1, 1, N, D))
+    K = rand_bits(rng, (1, 1, N, D))
+    rows = []
+    for t, p in [(1000, 5), (700, 333), (500, 400)]:
+        K[0, 0, p] = to_bf16_bits(1000.0 * bf16_bits_to_f32(Q[0, 0, t]))
+        rows.append((t, p))
+    idx = orc.route_causal(Q, orc.block_means(K, bs), bs, k, W)
+    for t, p in rows:
+        assert p // bs in idx[0, 0, t]
+
+
+# ---------------------------------------------------------------- attention
+def test_topk_covering_all_blocks_is_dense_causal(orc):
+    rng = np.random.default_rng(7)
+    bs, W, N, D = 16, 32, 256, 64
+    Q, K, V = rand_bits(rng, (1, 4, N, D)), rand_bits(rng, (1, 2, N, D)), rand_bits(rng, (1, 2, N, D))
+    out, sel = orc.forward(Q, K, V, bs, N // bs, W, 1)
+    np.testing.assert_allclose(out, sdpa_f64(Q, K, V, True), atol=2e-7, rtol=1e-6)
+
+
+def test_window_covering_sequence_is_dense_causal(orc):
+    rng = np.random.default_rng(8)
+    bs, k, N, D = 16, 2, 256, 32
+    Q, K, V = rand_bits(rng, (2, 2, N, D)), rand_bits(rng, (2, 1, N, D)), rand_bits(rng, (2, 1, N, D))
+    out, sel = orc.forward(Q, K, V, bs, k, N, 1)
+    assert np.all(sel == -1)
+    np.testing.assert_allclose(out, sdpa_f64(Q, K, V, True), atol=2e-7, rtol=1e-6)
+
+
+def test_image_mode_full_topk_is_dense(orc):
+    rng = np.random.default_rng(9)
+    bs, N, D = 16, 256, 32
+    Q, K, V = rand_bits(rng, (2, 2, N, D)), rand_bits(rng, (2, 2, N, D)), rand_bits(rng, (2, 2, N, D))
+    out, sel = orc.forward(Q, K, V, bs, N // bs, 0, 0)
+    np.testing.assert_allclose(out, sdpa_f64(Q, K, V, False), atol=2e-7, rtol=1e-6)
+
+
+def test_zero_query_averages_exactly_the_selected_keys(orc):
+    """q = 0 makes every logit 0, so the output is the plain mean of V over
+    the attended set: routed blocks plus the window [bs*E, t]."""
+    rng = np.random.default_rng(10)
+    bs, W, k, N, D = 16, 48, 3, 384, 16
+    Hq = 2
+    Q = np.zeros((1, Hq, N, D), np.uint16)
+    K, V = rand_bits(rng, (1, 1, N, D)), rand_bits(rng, (1, 1, N, D))
+    nb = N // bs
+    sel = np.full((Hq * N, k), -1, np.int32)
+    for r in range(Hq * N):
+        t = r % N
+        E = max(0, t // bs - W // bs + 1)
+        pick = np.sort(rng.choice(E, size=min(k, E), replace=False)) if E else []
+        sel[r, :len(pick)] = pick
+    out = orc.attend(Q, K, V, sel, bs, k, W, 1)
+    vf = brute.widen(V)[0, 0]
+    for r in range(Hq * N):
+        t = r % N
+        E = max(0, t // bs - W // bs + 1)
+        keys = [j for c in sel[r] if c >= 0 for j in range(c * bs, c * bs + bs)]
+        keys += list(range(E * bs, t + 1))
+        np.testing.assert_allclose(out.reshape(-1, D)[r], vf[keys].mean(0), rtol=1e-6, atol=1e-7)
+    assert nb > 0
+
+
+def test_constant_values_give_that_constant(orc):
+    rng = np.random.default_rng(11)
+    bs, W, k, N, D = 16, 32, 2, 256, 8
+    Q, K = rand_bits(rng, (1, 2, N, D)), rand_bits(rng, (1, 1, N, D))
+    V = np.tile(to_bf16_bits(np.arange(D, dtype=np.float32) - 3.5), (1, 1, N, 1))
+    out, _ = orc.forward(Q, K, V, bs, k, W, 1)
+    np.testing.assert_allclose(out, np.broadcast_to(np.arange(D) - 3.5, out.shape), rtol=1e-6)
+
+
+def test_gqa_head_reads_its_group(orc):
+    rng = np.random.default_rng(12)
+    bs, W, k, N, D = 16, 32, 3, 256, 16
+    Q, K, V = rand_bits(rng, (1, 6, N, D)), rand_bits(rng, (1, 2, N, D)), rand_bits(rng, (1, 2, N, D))
+    full, _ = orc.forward(Q, K, V, bs, k, W, 1)
+    for h in range(6):
+        g = h // 3
+        one, _ = orc.forward(Q[:, h:h + 1], K[:, g:g + 1], V[:, g:g + 1], bs, k, W, 1)
+        np.testing.assert_array_equal(one[0, 0], full[0, h])
+
+
+def test_scale_acts_on_logits_only(orc):
+    rng = np.random.default_rng(13)
+    bs, W, k, N, D = 16, 32, 3, 256, 16
+    Q, K, V = rand_bits(rng, (1, 1, N, D)), rand_bits(rng, (1, 1, N, D)), rand_bits(rng, (1, 1, N, D))
+    Q2 = to_bf16_bits(2.0 * bf16_bits_to_f32(Q))
+    a, sa = orc.forward(Q2, K, V, bs, k, W, 1, scale=0.125)
+    b, sb = orc.forward(Q, K, V, bs, k, W, 1, scale=0.25)
+    np.testing.assert_array_equal(sa, sb)
+    np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_end_to_end_matches_brute_force(orc, causal):
+    rng = np.random.default_rng(14 + causal)
+    bs, N, D = 16, 256, 16
+    Hq, Hkv = 4, 2
+    k, W = (3, 32) if causal else (4, 0)
+    Q, K, V = rand_bits(rng, (1, Hq, N, D)), rand_bits(rng, (1, Hkv, N, D)), rand_bits(rng, (1, Hkv, N, D))
+    out, _ = orc.forward(Q, K, V, bs, k, W, causal)
+    want, _ = brute.forward(Q[0], K[0], V[0], bs, k, W, causal)
+    np.testing.assert_allclose(out[0], want, rtol=1e-6, atol=2e-7)
+
+
+def test_attend_rejects_invalid_selection(orc):
+    rng = np.random.default_rng(15)
+    bs, W, k, N, D = 16, 32, 2, 128, 8
+    Q, K, V = rand_bits(rng, (1, 1, N, D)), rand_bits(rng, (1, 1, N, D)), rand_bits(rng, (1, 1, N, D))
+    t = 100                                   # E = 100//16 - 2 + 1 = 5
+    for bad in ([5, -1], [3, 3], [-1, 2], [4, 1], [-2, -1]):
+        with pytest.raises(ValueError):
+            orc.attend(Q, K, V, np.array([bad], np.int32), bs, k, W, 1, rows=[t])
+    orc.attend(Q, K, V, np.array([[1, 4]], np.int32), bs, k, W, 1, rows=[t])
+
+
+def test_sampled_rows_match_full_run(orc):
+    rng = np.random.default_rng(16)
+    bs, W, k, N, D = 16, 32, 3, 512, 32
+    Q, K, V = rand_bits(rng, (2, 4, N, D)), rand_bits(rng, (2, 2, N, D)), rand_bits(rng, (2, 2, N, D))
+    for causal, Wc in ((1, W), (0, 0)):
+        full_o, full_s = orc.forward(Q, K, V, bs, k, Wc, causal)
+        rows = rng.choice(2 * 4 * N, size=200, replace=False)
+        o, s = orc.forward(Q, K, V, bs, k, Wc, causal, rows=rows)
+        np.testing.assert_array_equal(o, full_o.reshape(-1, D)[rows])
+        np.testing.assert_array_equal(s, full_s.reshape(-1, k)[rows])
