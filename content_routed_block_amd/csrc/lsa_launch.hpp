@@ -1,0 +1,36 @@
+// Internal launchers behind the liblsa C ABI (host side).  Every launcher
+// assumes its arguments were validated by the ABI layer and enqueues work on
+// `stream` without synchronising.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lsa {
+
+struct Geometry {
+    int B, Hq, Hkv, N, D, bs, nb, top_k, window, causal;
+    float scale;  // resolved (> 0)
+};
+
+// x [BH, N, 64] bf16 -> xbar [BH, N/bs, 64] fp32
+hipError_t launch_summarize(const uint16_t* x, float* xbar, int BH, int N, int bs,
+                            hipStream_t s);
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s);
+
+// Routing workspace (bytes) and launch.  qbar may be NULL in causal mode.
+size_t route_workspace_bytes(const Geometry& g);
+hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
+                        int32_t* idx, void* ws, hipStream_t s);
+
+// Sparse attention workspace (bytes) and launch.
+size_t attend_workspace_bytes(const Geometry& g);
+hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const int32_t* idx, float* out, void* ws,
+                         hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace lsa

@@ -1,0 +1,77 @@
+// Block summary: the mean of each block of bs consecutive tokens (the first
+// cumulant mu_c of the SSA routing score, SSA page "Algorithm and
+// complexity").  HBM-bound streaming kernel: one wave per (head, block);
+// lane l reads 16 bytes (8 dims) of token l/8 + 8i, so every load
+// instruction covers 1 KB of consecutive memory.  Sums are kept in fp64 and
+// rounded once to fp32, so the result is the fp32 rounding of the exact
+// mean whenever the fp64 sum is exact (always, for bf16 data whose
+// magnitudes span fewer than ~2^39).
+#include "lsa_common.hpp"
+#include "lsa_launch.hpp"
+
+namespace lsa {
+
+__global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ x,
+                                                   float* __restrict__ xbar,
+                                                   int64_t n_blocks, int N, int bs) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wblk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wblk >= n_blocks) return;
+    const int nb = N / bs;
+    const int64_t bh = wblk / nb;
+    const int64_t c = wblk - bh * nb;
+    const int dg = lane & 7;   // dims 8*dg .. 8*dg+7
+    const int j0 = lane >> 3;  // tokens j0, j0+8, ...
+    const uint16_t* base = x + (bh * N + c * bs) * kD + dg * 8;
+    double acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+    for (int j = j0; j < bs; j += 8) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(base + (int64_t)j * kD);
+        float f[8];
+        unpack8(v, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += (double)f[i];
+    }
+#pragma unroll
+    for (int m = 8; m < 64; m <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], m, kWave);
+    if (j0 == 0) {
+        const double inv = 1.0 / (double)bs;  // bs is a power of two: exact
+        f32x4 lo, hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo[i] = (float)(acc[i] * inv);
+            hi[i] = (float)(acc[4 + i] * inv);
+        }
+        float* o = xbar + wblk * kD + dg * 8;
+        *reinterpret_cast<f32x4*>(o) = lo;
+        *reinterpret_cast<f32x4*>(o + 4) = hi;
+    }
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t value) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+hipError_t launch_summarize(const uint16_t* x, float* xbar, int BH, int N, int bs,
+                            hipStream_t s) {
+    const int64_t n_blocks = (int64_t)BH * (N / bs);
+    const int64_t grid = (n_blocks + 3) / 4;
+    hipLaunchKernelGGL(k_summarize, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks,
+                       N, bs);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    size_t grid = (n + 255) / 256;
+    if (grid > 4096) grid = 4096;
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)grid), dim3(256), 0, s, p, n, value);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,169 @@
+"""Thin Python binding of liblsa.so (the C ABI in include/lsa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the current
+HIP stream.  Importing this module fails loudly when liblsa.so has not been
+built; there is no fallback path.
+
+Tensors are torch tensors on the GPU, contiguous, laid out [B, H, N, D];
+bf16 inputs may be torch.bfloat16 or torch.uint16/int16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsa.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python content_routed_block_amd/build.py`")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+OP_SUMMARIZE, OP_ROUTE, OP_ATTEND, OP_FORWARD = 0, 1, 2, 3
+STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL", 2: "LSA_ERR_SHAPE", 3: "LSA_ERR_UNSUPPORTED",
+          4: "LSA_ERR_ALIGN", 5: "LSA_ERR_WORKSPACE", 6: "LSA_ERR_DEVICE"}
+
+
+class LsaParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+_P = ctypes.POINTER(LsaParams)
+_v = ctypes.c_void_p
+_lib.lsa_workspace_bytes.argtypes = [_P, ctypes.c_int32]
+_lib.lsa_workspace_bytes.restype = ctypes.c_size_t
+_lib.lsa_block_summarize.argtypes = [_P, _v, ctypes.c_int32, _v, _v]
+_lib.lsa_route_topk.argtypes = [_P, _v, _v, _v, _v, ctypes.c_size_t, _v]
+_lib.lsa_sparse_attend.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
+_lib.lsa_forward.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
+for _f in ("lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend", "lsa_forward"):
+    getattr(_lib, _f).restype = ctypes.c_int
+_lib.lsa_status_str.argtypes = [ctypes.c_int]
+_lib.lsa_status_str.restype = ctypes.c_char_p
+
+SIZE_MAX = (1 << 64) - 1
+
+
+class LsaError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({_lib.lsa_status_str(code).decode()})")
+        self.code = code
+
+
+def library():
+    return _lib
+
+
+def params(batch, q_heads, kv_heads, seq_len, head_dim=64, block=64, top_k=16, window=512,
+           causal=1, scale=0.0) -> LsaParams:
+    return LsaParams(batch, q_heads, kv_heads, seq_len, head_dim, block, top_k, window, causal,
+                     float(scale))
+
+
+def workspace_bytes(p: LsaParams, op: int) -> int:
+    n = _lib.lsa_workspace_bytes(ctypes.byref(p), op)
+    if n == SIZE_MAX:
+        raise LsaError(2, "lsa_workspace_bytes")
+    return n
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _bits(t: torch.Tensor, shape, name) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.uint16, torch.int16):
+        raise TypeError(f"{name}: expected bf16 data, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise LsaError(code, what)
+
+
+def _workspace(p, op, workspace, device):
+    need = workspace_bytes(p, op)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def block_summarize(p: LsaParams, x: torch.Tensor, heads: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    heads = p.kv_heads if heads is None else heads
+    x = _bits(x, (p.batch, heads, p.seq_len, p.head_dim), "x")
+    nb = p.seq_len // p.block
+    if out is None:
+        out = torch.empty((p.batch, heads, nb, p.head_dim), dtype=torch.float32, device=x.device)
+    _check(_lib.lsa_block_summarize(ctypes.byref(p), _ptr(x), heads, _ptr(out), _stream(stream)),
+           "lsa_block_summarize")
+    return out
+
+
+def route_topk(p: LsaParams, q: torch.Tensor, kbar: torch.Tensor,
+               idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
+    nb = p.seq_len // p.block
+    rows = p.seq_len if p.causal else nb
+    if idx is None:
+        idx = torch.empty((p.batch, p.q_heads, rows, p.top_k), dtype=torch.int32, device=q.device)
+    workspace, nbytes = _workspace(p, OP_ROUTE, workspace, q.device)
+    _check(_lib.lsa_route_topk(ctypes.byref(p), _ptr(q), _ptr(kbar), _ptr(idx), _ptr(workspace),
+                               nbytes, _stream(stream)), "lsa_route_topk")
+    return idx
+
+
+def sparse_attend(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  idx: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
+    k = _bits(k, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "k")
+    v = _bits(v, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "v")
+    if out is None:
+        out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
+                          device=q.device)
+    workspace, nbytes = _workspace(p, OP_ATTEND, workspace, q.device)
+    _check(_lib.lsa_sparse_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
+                                  _ptr(workspace), nbytes, _stream(stream)), "lsa_sparse_attend")
+    return out
+
+
+def forward(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+            want_idx: bool = True, workspace: Optional[torch.Tensor] = None,
+            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
+    k = _bits(k, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "k")
+    v = _bits(v, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "v")
+    if out is None:
+        out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
+                          device=q.device)
+    if idx is None and want_idx:
+        rows = p.seq_len if p.causal else p.seq_len // p.block
+        idx = torch.empty((p.batch, p.q_heads, rows, p.top_k), dtype=torch.int32, device=q.device)
+    workspace, nbytes = _workspace(p, OP_FORWARD, workspace, q.device)
+    _check(_lib.lsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
+                            _ptr(workspace), nbytes, _stream(stream)), "lsa_forward")
+    return out, idx

@@ -1,0 +1,136 @@
+/*
+ * liblsa: content-routed block sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (SSA page, jonsmirl/ssa, opening paragraph and "Algorithm and
+ * complexity"; LLSA page, "Minimum Usage"; Subquadratic Sparse Attention page,
+ * "Architecture"): keys are mean-pooled into fixed blocks; every query (in the
+ * non-causal image mode, every query block) scores the block summaries,
+ * keeps its top-k blocks and, in causal mode, a local causal window; exact
+ * softmax attention then runs over only the selected keys.  The dense n x n
+ * score matrix is never formed.
+ *
+ * Tensors (all device memory, row-major, the last index fastest):
+ *   q    [B, Hq,  N, D] bf16      k, v [B, Hkv, N, D] bf16
+ *   kbar [B, Hkv, N/bs, D] fp32   (block means)
+ *   idx  causal: [B, Hq, N, top_k] int32; image mode: [B, Hq, N/bs, top_k]
+ *   out  [B, Hq, N, D] fp32
+ * Query head h reads KV head h / (Hq / Hkv) (grouped-query attention with
+ * contiguous head groups).
+ *
+ * Conventions shared by every call:
+ *   - Ownership: the caller owns every buffer.  The library never allocates
+ *     or frees memory and keeps no state between calls.  Scratch space is a
+ *     caller-provided workspace of lsa_workspace_bytes() bytes (256-byte
+ *     aligned).
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  All
+ *     work is enqueued asynchronously on it; no call synchronises the host.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; on error nothing is launched.  LSA_ERR_DEVICE reports a
+ *     failed launch; a device fault surfaces at the caller's next
+ *     synchronisation.
+ *   - Inputs are not checked for finiteness: NaN or Inf give an unspecified
+ *     result but every access stays in bounds.
+ *   - Determinism: the same inputs give bitwise identical outputs.
+ *   - Calls on distinct streams with distinct workspaces may run
+ *     concurrently.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lsa_params {
+    int32_t batch;     /* B >= 1 */
+    int32_t q_heads;   /* Hq >= 1 */
+    int32_t kv_heads;  /* Hkv >= 1, Hq % Hkv == 0 */
+    int32_t seq_len;   /* N, a positive multiple of block; N/block <= 65536 */
+    int32_t head_dim;  /* D; this build supports 64 */
+    int32_t block;     /* bs: 16, 32, 64 or 128 (key block; in image mode also the query block) */
+    int32_t top_k;     /* 1 .. 16 */
+    int32_t window;    /* causal: a multiple of block, >= block; image mode: 0 */
+    int32_t causal;    /* 1: per-query routing + causal window; 0: image mode */
+    float scale;       /* softmax scale; <= 0 selects 1/sqrt(D) */
+} lsa_params;
+
+typedef enum lsa_status {
+    LSA_OK = 0,
+    LSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    LSA_ERR_SHAPE = 2,       /* inconsistent sizes (N % block, Hq % Hkv, window, ...) */
+    LSA_ERR_UNSUPPORTED = 3, /* valid but outside this build (D != 64, top_k > 16, ...) */
+    LSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned (workspace: 256) */
+    LSA_ERR_WORKSPACE = 5,   /* workspace smaller than lsa_workspace_bytes() */
+    LSA_ERR_DEVICE = 6       /* a HIP launch failed */
+} lsa_status;
+
+enum {
+    LSA_OP_SUMMARIZE = 0,
+    LSA_OP_ROUTE = 1,
+    LSA_OP_ATTEND = 2,
+    LSA_OP_FORWARD = 3
+};
+
+/* Workspace bytes needed by `op` for these parameters (0 = none needed;
+ * (size_t)-1 when the parameters are invalid). */
+size_t lsa_workspace_bytes(const lsa_params *p, int32_t op);
+
+/* Block summary (SSA page, "Algorithm and complexity": the first cumulant
+ * mu_c of the routing score r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q).
+ * x [B, heads, N, D] bf16 -> xbar [B, heads, N/bs, D] fp32, where
+ * xbar[c] = the mean of tokens [c*bs, c*bs + bs), summed in fp64 and
+ * rounded once to fp32.  `heads` is Hkv for keys, Hq for pooled queries. */
+lsa_status lsa_block_summarize(const lsa_params *p, const void *x, int32_t heads,
+                               float *xbar, void *stream);
+
+/* Routing: scores <q, kbar_c> (beta = 0) and top-k selection with ties
+ * broken toward the lower block index.
+ * Causal (causal = 1): row t of head h considers the complete blocks
+ *   c < E(t) = max(0, t/bs - window/bs + 1), i.e. the blocks that end before
+ *   the block-aligned local window (SSA page, "Mathematical status" and
+ *   "Known limitations": a routed set is causal only once cut at the query
+ *   position; Subquadratic Sparse Attention page, "Why the layer is
+ *   mathematically subquadratic": completed blocks are exposed only when
+ *   their last token precedes the cutoff).  idx [B, Hq, N, top_k].
+ * Image mode (causal = 0): query block i (tokens [i*bs, i*bs+bs)) is pooled
+ *   to its fp32 mean and scored against all N/bs key blocks (LLSA page,
+ *   "Minimum Usage").  idx [B, Hq, N/bs, top_k].
+ * Each idx row lists min(top_k, #candidates) block ids in ascending order,
+ * then -1 padding. */
+lsa_status lsa_route_topk(const lsa_params *p, const void *q, const float *kbar,
+                          int32_t *idx, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Exact softmax attention over the selected keys only (SSA page, opening
+ * paragraph; Subquadratic Sparse Attention page, "Architecture").
+ * Causal: row t attends to the routed blocks listed in idx plus the window
+ *   keys [bs*E(t), t]; logits (q . k_j) * scale.
+ * Image mode: every token of query block i attends to the union of the
+ *   blocks listed for i.
+ * idx is normally the output of lsa_route_topk.  An entry is used only if it
+ * is a candidate block (causal: 0 <= c < E(t); image mode: 0 <= c < N/bs) and
+ * greater than the previously used entry of its row; anything else is
+ * skipped, so every access stays in bounds for any idx contents.
+ * out [B, Hq, N, D] fp32. */
+lsa_status lsa_sparse_attend(const lsa_params *p, const void *q, const void *k,
+                             const void *v, const int32_t *idx, float *out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* The whole layer: summarize K, route, attend.  idx_out may be NULL (the
+ * selection then lives in the workspace); otherwise it receives idx as
+ * lsa_route_topk writes it. */
+lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
+                       const void *v, float *out, int32_t *idx_out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *lsa_status_str(lsa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

@@ -1,0 +1,76 @@
+"""Parity helpers shared by the GPU tests: move seeded inputs to the device,
+call the HIP path through the C ABI binding, compare with the CPU oracle.
+
+Routing parity (the pages' method gives several correct answers on ties):
+  * rows whose oracle gap (k-th minus (k+1)-th routing score) exceeds 1e-3
+    must select bit-identical block sets;
+  * other rows ("near ties") may differ, but then the GPU set must be a valid
+    top-k under the oracle's fp64 scores to within 1e-3:
+    min s(selected) >= max s(unselected candidates) - 1e-3, with the right
+    count, ascending order and -1 padding.
+Output parity: max-abs <= 2e-2 and mean-abs <= 5e-3 against the fp32 oracle,
+plus a tighter bound derived from the arithmetic: bf16 rounding of the
+probabilities and of the routed partial outputs perturbs each output by at
+most 2^-9 * max|v| each, so |err| <= 2^-8 * max|v| per row.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+GAP = 1e-3
+MAX_ABS, MEAN_ABS = 2e-2, 5e-3
+REL_V = 2.0 ** -8
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def params_of(lsa, w, **over):
+    kw = dict(batch=w.batch, q_heads=w.q_heads, kv_heads=w.kv_heads, seq_len=w.seq_len,
+              head_dim=w.head_dim, block=w.block, top_k=w.top_k, window=w.window,
+              causal=w.causal)
+    kw.update(over)
+    return lsa.params(**kw)
+
+
+def causal_candidates(t, bs, window):
+    return np.maximum(0, t // bs - window // bs + 1)
+
+
+def check_routing(idx_gpu, idx_orc, gap, scores, ncand, k):
+    """idx_gpu / idx_orc: [R, k]; gap: [R]; scores: [R, nb] oracle scores
+    (-inf off the candidate set); ncand: [R].  Returns (n_clear_mismatch,
+    n_near, n_near_differing).  Raises AssertionError on an invalid set."""
+    idx_gpu = np.asarray(idx_gpu)
+    idx_orc = np.asarray(idx_orc)
+    clear = gap > GAP
+    differ = np.any(idx_gpu != idx_orc, axis=1)
+    bad_clear = int(np.sum(differ & clear))
+    near_rows = np.nonzero(differ & ~clear)[0]
+    for r in near_rows:
+        sel = idx_gpu[r]
+        m = min(k, int(ncand[r]))
+        assert np.all(sel[m:] == -1), (r, sel)
+        chosen = sel[:m]
+        assert np.all(chosen >= 0) and np.all(chosen < ncand[r]), (r, sel)
+        assert np.all(np.diff(chosen) > 0), (r, sel)
+        s = scores[r]
+        rest = np.setdiff1d(np.arange(int(ncand[r])), chosen)
+        if rest.size:
+            assert s[chosen].min() >= s[rest].max() - GAP, (r, s[chosen].min(), s[rest].max())
+    return bad_clear, int(np.sum(~clear)), len(near_rows)
+
+
+def check_output(out_gpu, out_ref, vmax_row):
+    """out_*: [R, D] float; vmax_row: [R] max |v| over the row's keys (or a
+    global bound).  Returns (max_abs, mean_abs)."""
+    err = np.abs(np.asarray(out_gpu, np.float64) - np.asarray(out_ref, np.float64))
+    max_abs, mean_abs = float(err.max()), float(err.mean())
+    assert max_abs <= MAX_ABS, max_abs
+    assert mean_abs <= MEAN_ABS, mean_abs
+    row_err = err.max(axis=1)
+    worst = float(np.max(row_err / np.maximum(vmax_row, 1e-30)))
+    assert worst <= REL_V, worst
+    return max_abs, mean_abs

@@ -1,0 +1,90 @@
+"""The C ABI library without a GPU: it loads, exports every function that
+include/lsa.h declares, and its host-side validation returns the documented
+status codes before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsa.h")
+LIB = os.path.join(ROOT, "content_routed_block_amd", "liblsa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="liblsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    from content_routed_block_amd import lsa as m
+    return m
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert set(names) >= {"lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend",
+                          "lsa_forward", "lsa_workspace_bytes", "lsa_status_str"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header(lsa):
+    assert ctypes.sizeof(lsa.LsaParams) == 40
+
+
+def good(lsa, **kw):
+    base = dict(batch=1, q_heads=14, kv_heads=2, seq_len=131072, head_dim=64, block=64,
+                top_k=16, window=512, causal=1)
+    base.update(kw)
+    return lsa.params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_heads=13), 2), (dict(seq_len=1000), 2), (dict(window=100), 2), (dict(window=32), 2),
+    (dict(causal=0, window=512, block=16), 2), (dict(causal=2), 2), (dict(batch=0), 2),
+    (dict(head_dim=128), 3), (dict(top_k=17), 3), (dict(block=48, window=96, seq_len=960), 3),
+    (dict(causal=0, window=0, block=64), 3), (dict(seq_len=1 << 24, block=16, window=512), 3),
+])
+def test_invalid_parameters(lsa, kw, code):
+    p = good(lsa, **kw)
+    assert lsa.library().lsa_workspace_bytes(ctypes.byref(p), lsa.OP_FORWARD) == lsa.SIZE_MAX
+    dummy = ctypes.c_void_p(256)
+    rc = lsa.library().lsa_forward(ctypes.byref(p), dummy, dummy, dummy, dummy, None, dummy,
+                                   1 << 40, None)
+    assert rc == code
+
+
+def test_null_alignment_and_workspace_checks(lsa):
+    L = lsa.library()
+    p = good(lsa)
+    a = ctypes.c_void_p(4096)
+    assert L.lsa_forward(None, a, a, a, a, None, a, 1 << 40, None) == 1
+    assert L.lsa_forward(ctypes.byref(p), None, a, a, a, None, a, 1 << 40, None) == 1
+    assert L.lsa_forward(ctypes.byref(p), ctypes.c_void_p(4098), a, a, a, None, a, 1 << 40, None) == 4
+    assert L.lsa_forward(ctypes.byref(p), a, a, a, a, None, ctypes.c_void_p(4096 + 16), 1 << 40, None) == 4
+    need = lsa.workspace_bytes(p, lsa.OP_FORWARD)
+    assert L.lsa_forward(ctypes.byref(p), a, a, a, a, None, a, need - 1, None) == 5
+    assert L.lsa_route_topk(ctypes.byref(p), a, a, a, a, lsa.workspace_bytes(p, lsa.OP_ROUTE) - 1,
+                            None) == 5
+    assert L.lsa_sparse_attend(ctypes.byref(p), a, a, a, None, a, a, 1 << 40, None) == 1
+    assert L.lsa_block_summarize(ctypes.byref(p), a, 0, a, None) == 2
+    for code in range(7):
+        assert L.lsa_status_str(code)
+
+
+def test_workspace_sizes_are_plausible(lsa):
+    p = good(lsa)
+    pairs = 14 * 131072 * 16
+    att = lsa.workspace_bytes(p, lsa.OP_ATTEND)
+    assert pairs * (64 * 2 + 4 + 4) <= att < pairs * (64 * 2 + 4 + 4) + (1 << 20)
+    assert lsa.workspace_bytes(p, lsa.OP_SUMMARIZE) == 0
+    img = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0)
+    assert lsa.workspace_bytes(img, lsa.OP_ATTEND) == 0
+    assert lsa.workspace_bytes(img, lsa.OP_ROUTE) >= 4 * 16 * 1024 * 64 * 4
