@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of one content-routed sparse attention layer on one MI355X.
+
+A step is one lsa_forward over the whole layer: key block summaries,
+routing + top-k, and exact sparse attention (routed blocks + causal window),
+on seeded synthetic inputs already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the Qwen2.5-0.5B-shaped layer at N=131072 (B=1, 14 query /
+2 KV heads, D=64, block 64, top-k 16, window 512, 32 needles).  `value` is
+TFLOP/s counted on the selected keys only (4*D FLOP per selected key and
+query: QK^T and PV), `ms_per_step` is ms per layer.
+
+`roofline` describes the dominant kernel (largest mean stage time, measured
+with HIP events recorded between the library's kernel launches on the same
+stream), `cpu_baseline` the CPU oracle timed on a bounded row sample on this
+host.  `--copy-calibration` instead runs a plain copy of known size, used to
+scale the FETCH_SIZE / WRITE_SIZE counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc
+# FETCH_SIZE / WRITE_SIZE runs, each scaled by the same counter's reading on a
+# plain copy of known size; tied to the kernel sources it was measured on.
+TRAFFIC = None
+
+
+def csrc_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "content_routed_block_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen05b_n128k_needles")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def selected_flops(w, idx_np):
+    """4*D FLOP per (query, selected key): routed keys from the actual idx plus
+    the causal window keys [bs*E(t), t]."""
+    D = w.head_dim
+    valid = (idx_np >= 0).sum(axis=-1).astype(np.int64)       # per routing row
+    if w.causal:
+        t = np.arange(w.seq_len, dtype=np.int64)
+        E = np.maximum(0, t // w.block - w.window // w.block + 1)
+        win = t - w.block * E + 1
+        routed_keys = int(valid.sum()) * w.block
+        window_keys = int(win.sum()) * w.batch * w.q_heads
+        routed_pairs = int(valid.sum())
+    else:
+        routed_keys = int(valid.sum()) * w.block * w.block     # bs queries x bs keys per block
+        window_keys = 0
+        routed_pairs = int(valid.sum()) * w.block
+    return 4 * D * routed_keys, 4 * D * window_keys, routed_pairs
+
+
+def routing_candidates(w):
+    if w.causal:
+        t = np.arange(w.seq_len, dtype=np.int64)
+        E = np.maximum(0, t // w.block - w.window // w.block + 1)
+        return int(E.sum()) * w.batch * w.q_heads
+    nb = w.seq_len // w.block
+    return w.batch * w.q_heads * nb * nb
+
+
+def cpu_baseline(w, inp, target_s):
+    import oracle
+    R = w.batch * w.q_heads * w.seq_len
+    rng = np.random.default_rng(7)
+    probe = np.sort(rng.choice(R, size=min(R, 2000), replace=False))
+    t0 = time.perf_counter()
+    oracle.forward(inp.q, inp.k, inp.v, w.block, w.top_k, w.window, w.causal, rows=probe)
+    per_row = (time.perf_counter() - t0) / probe.size
+    n = int(min(R, max(2000, target_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(R, size=n, replace=False))
+    t0 = time.perf_counter()
+    _, sel = oracle.forward(inp.q, inp.k, inp.v, w.block, w.top_k, w.window, w.causal, rows=rows)
+    wall = time.perf_counter() - t0
+    D = w.head_dim
+    routed = int((sel >= 0).sum()) * w.block
+    if w.causal:
+        t = rows % w.seq_len
+        E = np.maximum(0, t // w.block - w.window // w.block + 1)
+        win = int((t - w.block * E + 1).sum())
+    else:
+        win = 0
+    flops = 4 * D * (routed + win)
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s (selected keys)",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {R} query rows of {w.name}, uniform without replacement; "
+                      f"{wall:.1f} s wall; full layer extrapolated {wall * R / n * 1e3:.0f} ms",
+            "ms_per_layer_extrapolated": wall * R / n * 1e3}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28                       # 256 Mi float32 = 1 GiB read + 1 GiB written
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                      "kernel": "torch.neg (elementwise)", "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards across GPUs with no exchange per (batch, KV head); "
+              "this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from content_routed_block_amd import lsa
+    from content_routed_block_amd.workloads import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    inp = generate(w)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev)
+
+    q, k, v = up(inp.q), up(inp.k), up(inp.v)
+    p = lsa.params(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.top_k,
+                   w.window, w.causal)
+    out = torch.empty((w.batch, w.q_heads, w.seq_len, w.head_dim), dtype=torch.float32, device=dev)
+    rows = w.seq_len if w.causal else w.seq_len // w.block
+    idx = torch.empty((w.batch, w.q_heads, rows, w.top_k), dtype=torch.int32, device=dev)
+    ws = torch.empty(lsa.workspace_bytes(p, lsa.OP_FORWARD), dtype=torch.uint8, device=dev)
+
+    for _ in range(args.warmup):
+        lsa.forward(p, q, k, v, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    f_routed, f_window, routed_pairs = selected_flops(w, idx.cpu().numpy())
+    f_sel = f_routed + f_window
+
+    events = [lsa.StageEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        lsa.forward_profiled(p, q, k, v, events[i], out, idx, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    stages = np.array([e.stage_ms() for e in events])            # [steps, 8]
+    for e in events:
+        e.close()
+    stage_mean = stages.mean(axis=0)
+
+    # algorithmic work per stage
+    B, Hq, Hkv, N, D, bs = w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block
+    nb = N // bs
+    summary_bytes = B * Hkv * N * D * 2 + B * Hkv * nb * D * 4
+    if not w.causal:
+        summary_bytes += B * Hq * N * D * 2 + B * Hq * nb * D * 4
+    cand = routing_candidates(w)
+    work = {
+        0: ("hbm", summary_bytes / 1e9, "GB/s", PEAK_HBM_GBS),
+        1: ("mfma", 2 * D * cand / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        6: ("mfma", f_routed / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+        7: ("mfma", (f_window if w.causal else f_routed) / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
+    }
+    dom = int(np.argmax(stage_mean))
+    bound, amount, unit, peak = work.get(dom, ("hbm", 0.0, "GB/s", PEAK_HBM_GBS))
+    achieved = amount / (stage_mean[dom] * 1e-3)
+    traffic = None
+    if TRAFFIC and TRAFFIC.get("csrc") == csrc_digest() and TRAFFIC.get("stage") == dom \
+            and TRAFFIC.get("workload") == w.name:
+        traffic = TRAFFIC["bytes_per_launch"]
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": traffic,
+                "kernel": lsa.PROFILE_STAGES[dom], "kernel_ms": float(stage_mean[dom])}
+    breakdown = {lsa.PROFILE_STAGES[i]: round(float(stage_mean[i]), 4) for i in range(8)}
+    hbm_summary = summary_bytes / 1e9 / (stage_mean[0] * 1e-3)
+    route_tflops = 2 * D * cand / 1e12 / (stage_mean[1] * 1e-3)
+    route_bytes = B * Hq * N * D * 2 + B * Hq * rows * w.top_k * 4 + B * Hkv * nb * D * 4
+    attend_ms = float(stage_mean[3:].sum())
+
+    result = {
+        "metric": "sparse-attn ms/layer + selected-key TFLOP/s (%MFMA peak) at N=128K, Qwen0.5B shape",
+        "value": f_sel / 1e12 / (ms * 1e-3),
+        "unit": "TFLOP/s (selected keys)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded numpy PCG64; no dataset or weights)",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": N,
+                   "head_dim": D, "block": bs, "top_k": w.top_k, "window": w.window,
+                   "causal": w.causal},
+        "roofline": roofline,
+        "layer": {"ms": ms, "selected_tflop": f_sel / 1e12,
+                  "mfma_frac": f_sel / 1e12 / (ms * 1e-3) / PEAK_BF16_TFLOPS,
+                  "attend_ms": attend_ms,
+                  "attend_mfma_frac": f_sel / 1e12 / (attend_ms * 1e-3) / PEAK_BF16_TFLOPS,
+                  "summary_hbm_gbs": hbm_summary, "summary_hbm_frac": hbm_summary / PEAK_HBM_GBS,
+                  "routing_tflops": route_tflops,
+                  "routing_mfma_frac": route_tflops / PEAK_BF16_TFLOPS,
+                  "routing_hbm_frac": route_bytes / 1e9 / (stage_mean[1] * 1e-3) / PEAK_HBM_GBS,
+                  "routed_pairs": routed_pairs, "stage_ms": breakdown},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

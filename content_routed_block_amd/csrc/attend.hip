@@ -609,13 +609,15 @@ static void launch_partial(const PartArgs& pa, hipStream_t s) {
 
 hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* idx, float* out, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, const hipEvent_t* ev) {
     const float scale_log2 = g.scale * kLog2e;
     if (!g.causal) {
         ImgArgs a{q, k, v, idx, out, g.Hq, g.Hkv, g.N, g.nb, g.top_k,
                   (int64_t)g.B * g.Hq * g.nb, scale_log2};
         const unsigned grid = (unsigned)((a.n_qblocks + 3) / 4);
+        for (int i = 4; i < 8; ++i) mark(ev, i, s);
         hipLaunchKernelGGL(k_image_attend, dim3(grid), dim3(256), 0, s, a);
+        mark(ev, 8, s);
         return hipGetLastError();
     }
     const AttendLayout L = attend_layout(g);
@@ -636,9 +638,12 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     const dim3 bgrid((unsigned)(g.B * g.Hkv * nch));
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
     hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
+    mark(ev, 4, s);
     hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
                        NB);
+    mark(ev, 5, s);
     hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
+    mark(ev, 6, s);
 
     PartArgs pa{q, k, v, pairs, offsets, unit_off, part_o, part_lse, g.N, g.nb, g.top_k, NB,
                 scale_log2};
@@ -648,10 +653,12 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
         case 64: launch_partial<64>(pa, s); break;
         default: launch_partial<128>(pa, s); break;
     }
+    mark(ev, 7, s);
     WinArgs wa{q, k, v, idx, part_o, part_lse, out, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
                (g.N + 63) / 64, scale_log2};
     hipLaunchKernelGGL(k_window_merge, dim3((unsigned)(g.B * g.Hq * wa.tiles)), dim3(256), 0, s,
                        wa);
+    mark(ev, 8, s);
     return hipGetLastError();
 }
 

@@ -130,9 +130,9 @@ lsa_status lsa_sparse_attend(const lsa_params* p, const void* q, const void* k, 
                                        static_cast<hipStream_t>(stream)));
 }
 
-lsa_status lsa_forward(const lsa_params* p, const void* q, const void* k, const void* v,
-                       float* out, int32_t* idx_out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+static lsa_status forward_impl(const lsa_params* p, const void* q, const void* k, const void* v,
+                               float* out, int32_t* idx_out, void* workspace,
+                               size_t workspace_bytes, void* stream, const hipEvent_t* ev) {
     Geometry g;
     lsa_status st = check_params(p, &g);
     if (st != LSA_OK) return st;
@@ -152,14 +152,32 @@ lsa_status lsa_forward(const lsa_params* p, const void* q, const void* k, const 
         off += lsa::align_up(route_idx_bytes(g), 256);
     }
     void* rest = base + off;
+    lsa::mark(ev, 0, s);
     st = from_hip(lsa::launch_summarize(static_cast<const uint16_t*>(k), kbar, g.B * g.Hkv, g.N,
                                         g.bs, s));
     if (st != LSA_OK) return st;
-    st = from_hip(lsa::launch_route(g, static_cast<const uint16_t*>(q), kbar, idx, rest, s));
+    lsa::mark(ev, 1, s);
+    st = from_hip(lsa::launch_route(g, static_cast<const uint16_t*>(q), kbar, idx, rest, s, ev));
     if (st != LSA_OK) return st;
     return from_hip(lsa::launch_attend(g, static_cast<const uint16_t*>(q),
                                        static_cast<const uint16_t*>(k),
-                                       static_cast<const uint16_t*>(v), idx, out, rest, s));
+                                       static_cast<const uint16_t*>(v), idx, out, rest, s, ev));
+}
+
+lsa_status lsa_forward(const lsa_params* p, const void* q, const void* k, const void* v,
+                       float* out, int32_t* idx_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    return forward_impl(p, q, k, v, out, idx_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+lsa_status lsa_forward_profiled(const lsa_params* p, const void* q, const void* k, const void* v,
+                                float* out, int32_t* idx_out, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* events) {
+    if (!events) return LSA_ERR_NULL;
+    for (int i = 0; i < LSA_PROFILE_EVENTS; ++i)
+        if (!events[i]) return LSA_ERR_NULL;
+    return forward_impl(p, q, k, v, out, idx_out, workspace, workspace_bytes, stream,
+                        reinterpret_cast<const hipEvent_t*>(events));
 }
 
 const char* lsa_status_str(lsa_status s) {

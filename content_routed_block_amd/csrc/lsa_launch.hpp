@@ -23,13 +23,19 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s)
 // Routing workspace (bytes) and launch.  qbar may be NULL in causal mode.
 size_t route_workspace_bytes(const Geometry& g);
 hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
-                        int32_t* idx, void* ws, hipStream_t s);
+                        int32_t* idx, void* ws, hipStream_t s,
+                        const hipEvent_t* ev = nullptr);
 
 // Sparse attention workspace (bytes) and launch.
 size_t attend_workspace_bytes(const Geometry& g);
 hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* idx, float* out, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, const hipEvent_t* ev = nullptr);
+
+// Records profiling event i (if any) on the stream.
+inline void mark(const hipEvent_t* ev, int i, hipStream_t s) {
+    if (ev) (void)hipEventRecord(ev[i], s);
+}
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

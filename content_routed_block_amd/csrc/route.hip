@@ -488,7 +488,7 @@ size_t route_workspace_bytes(const Geometry& g) {
 }
 
 hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar, int32_t* idx,
-                        void* ws, hipStream_t s) {
+                        void* ws, hipStream_t s, const hipEvent_t* ev) {
     char* base = static_cast<char*>(ws);
     RouteArgs a;
     a.ovf_count = reinterpret_cast<uint32_t*>(base);
@@ -521,11 +521,14 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     const dim3 grid((unsigned)((int64_t)g.B * g.Hq * a.tiles));
     if (g.causal) {
         hipLaunchKernelGGL(k_route<true>, grid, dim3(256), 0, s, a);
+        mark(ev, 2, s);
         hipLaunchKernelGGL(k_route_fallback<true>, dim3(FB_GRID), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL(k_route<false>, grid, dim3(256), 0, s, a);
+        mark(ev, 2, s);
         hipLaunchKernelGGL(k_route_fallback<false>, dim3(FB_GRID), dim3(256), 0, s, a);
     }
+    mark(ev, 3, s);
     return hipGetLastError();
 }
 

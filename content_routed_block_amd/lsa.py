@@ -47,10 +47,25 @@ _lib.lsa_sparse_attend.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, 
 _lib.lsa_forward.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
 for _f in ("lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend", "lsa_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
+_lib.lsa_forward_profiled.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v, _v]
+_lib.lsa_forward_profiled.restype = ctypes.c_int
 _lib.lsa_status_str.argtypes = [ctypes.c_int]
 _lib.lsa_status_str.restype = ctypes.c_char_p
 
 SIZE_MAX = (1 << 64) - 1
+PROFILE_EVENTS = 9
+PROFILE_STAGES = ["key summary", "routing", "routing fallback", "bucket count", "bucket scan",
+                  "bucket scatter", "routed-block partials", "window + merge"]
+
+# HIP event calls resolve through liblsa's own dependency (the process's single
+# libamdhip64, already loaded by torch).
+_lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+_lib.hipEventCreate.restype = ctypes.c_int
+_lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+_lib.hipEventDestroy.restype = ctypes.c_int
+_lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                     ctypes.c_void_p]
+_lib.hipEventElapsedTime.restype = ctypes.c_int
 
 
 class LsaError(RuntimeError):
@@ -167,3 +182,41 @@ def forward(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check(_lib.lsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
                             _ptr(workspace), nbytes, _stream(stream)), "lsa_forward")
     return out, idx
+
+
+class StageEvents:
+    """PROFILE_EVENTS HIP events for one lsa_forward_profiled call."""
+
+    def __init__(self):
+        self.handles = []
+        for _ in range(PROFILE_EVENTS):
+            h = ctypes.c_void_p()
+            if _lib.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h)
+        self.array = (ctypes.c_void_p * PROFILE_EVENTS)(*[h.value for h in self.handles])
+
+    def stage_ms(self):
+        """Durations (ms) of the PROFILE_EVENTS-1 stages; call after a sync."""
+        out = []
+        for i in range(1, PROFILE_EVENTS):
+            ms = ctypes.c_float()
+            if _lib.hipEventElapsedTime(ctypes.byref(ms), self.handles[i - 1], self.handles[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for h in self.handles:
+            _lib.hipEventDestroy(h)
+        self.handles = []
+
+
+def forward_profiled(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     events: StageEvents, out: torch.Tensor, idx: Optional[torch.Tensor],
+                     workspace: torch.Tensor, stream=None) -> None:
+    """lsa_forward recording the stage events (buffers must be preallocated)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.lsa_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                     _ptr(idx), _ptr(workspace), nbytes, _stream(stream),
+                                     events.array), "lsa_forward_profiled")

@@ -126,6 +126,21 @@ lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
                        const void *v, float *out, int32_t *idx_out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* lsa_forward with stage timing, for profiling tools.  `events` holds
+ * LSA_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is
+ * recorded on `stream` at the i-th stage boundary:
+ *   0 start, 1 key summary, 2 routing, 3 routing fallback, 4 bucket count,
+ *   5 bucket scan, 6 bucket scatter, 7 routed-block partials, 8 window and
+ *   merge (image mode: 2 includes the query summary, 4-7 are empty and 8 is
+ *   the image-mode attention).
+ * Elapsed time between events i-1 and i is the duration of stage i.  No
+ * synchronisation happens inside; otherwise identical to lsa_forward. */
+#define LSA_PROFILE_EVENTS 9
+lsa_status lsa_forward_profiled(const lsa_params *p, const void *q, const void *k,
+                                const void *v, float *out, int32_t *idx_out,
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                void *const *events);
+
 /* Static description of a status code. */
 const char *lsa_status_str(lsa_status s);
 
