@@ -28,16 +28,16 @@
 // Softmax runs in the log2 domain: logits are scaled by scale*log2(e).
 #include <math.h>
 
+#include <algorithm>
+
 #include "lsa_common.hpp"
 #include "lsa_launch.hpp"
 
 namespace lsa {
 
 constexpr int UNIT_ROWS = 64;   // gathered rows per work unit of the block-major kernel
-constexpr int BK_TCHUNK = 2048; // query positions per bucketing workgroup
 constexpr int BK_LDS_MAX = 16384;  // largest nb histogrammed in LDS
 constexpr int KPITCH = 72;      // LDS pitch of K tiles [key][64 d] (bf16)
-constexpr int PART_GRID = 2048; // workgroups of the persistent block-major kernel
 
 // ------------------------------------------------------------ shared pieces
 // Stages K rows [0, nkeys) of a tile into s_k[key][KPITCH] (16-byte chunks);
@@ -153,18 +153,59 @@ struct BucketArgs {
     uint32_t* counts;    // [NB]
     uint32_t* cursor;    // [NB]
     uint32_t* pairs;     // [total pairs]
-    int Hq, Hkv, N, bs, nb, top_k, window;
+    int Hq, Hkv, N, bs, nb, top_k, window, tchunk;
 };
 
+// Used-slot mask of one idx row, read with 16-byte loads when possible.
+__device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int ncand,
+                                             int (&c)[kMaxTopK]) {
+    if ((top_k & 3) == 0) {
+#pragma unroll
+        for (int s4 = 0; s4 < kMaxTopK / 4; ++s4) {
+            if (4 * s4 < top_k) {
+                const int32_t __attribute__((ext_vector_type(4))) v =
+                    *reinterpret_cast<const int32_t __attribute__((ext_vector_type(4)))*>(ir + 4 * s4);
+                c[4 * s4] = v[0]; c[4 * s4 + 1] = v[1]; c[4 * s4 + 2] = v[2]; c[4 * s4 + 3] = v[3];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+            if (s < top_k) c[s] = ir[s];
+    }
+    uint32_t mask = 0;
+    int prev = -1;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s < top_k && c[s] > prev && c[s] < ncand) {
+            mask |= 1u << s;
+            prev = c[s];
+        }
+    }
+    return mask;
+}
+
+// c[i] for a runtime i < kMaxTopK without dynamic register indexing.
+__device__ __forceinline__ int pick(const int (&c)[kMaxTopK], int i) {
+    int v = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) v = (s == i) ? c[s] : v;
+    return v;
+}
+
+// Workgroup = (batch, KV head, chunk of tchunk positions) over all query
+// heads of the group.  Histogram in LDS (when nb fits), then one global
+// atomic per touched bucket: counts (SCATTER = false) or a reserved range
+// of the pair list that pass B fills (SCATTER = true).
 template <bool SCATTER>
 __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     extern __shared__ uint32_t s_h[];
     const int tid = threadIdx.x;
-    const int nch = (a.N + BK_TCHUNK - 1) / BK_TCHUNK;
+    const int nch = (a.N + a.tchunk - 1) / a.tchunk;
     const int bg = blockIdx.x / nch, ch = blockIdx.x - bg * nch;
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int rep = a.Hq / a.Hkv;
-    const int t0 = ch * BK_TCHUNK, t1 = min(a.N, t0 + BK_TCHUNK);
+    const int t0 = ch * a.tchunk, t1 = min(a.N, t0 + a.tchunk);
     const int span = t1 - t0;
     const bool lds = a.nb <= BK_LDS_MAX;
     const int64_t bucket0 = (int64_t)bg * a.nb;
@@ -172,48 +213,45 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
         for (int c = tid; c < a.nb; c += 256) s_h[c] = 0;
         __syncthreads();
     }
-    // pass A: local histogram (or, without LDS, direct global work)
     for (int i = tid; i < rep * span; i += 256) {
         const int hh = i / span, t = t0 + (i - hh * span);
         const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
-        const int32_t* ir = a.idx + row * a.top_k;
-        uint32_t m = used_slots(ir, a.top_k, eligible_blocks(t, a.bs, a.window));
-        while (m) {
-            const int s = __builtin_ctz(m);
-            m &= m - 1;
-            const int c = ir[s];
+        int c[kMaxTopK];
+        uint32_t m = row_used(a.idx + row * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+            if (!((m >> s) & 1u)) continue;
             if (lds) {
-                atomicAdd(&s_h[c], 1u);
+                atomicAdd(&s_h[c[s]], 1u);
             } else if (!SCATTER) {
-                atomicAdd(&a.counts[bucket0 + c], 1u);
+                atomicAdd(&a.counts[bucket0 + c[s]], 1u);
             } else {
-                const uint32_t pos = atomicAdd(&a.cursor[bucket0 + c], 1u);
+                const uint32_t pos = atomicAdd(&a.cursor[bucket0 + c[s]], 1u);
                 a.pairs[pos] = (uint32_t)(row * a.top_k + s);
             }
         }
     }
     if (!lds) return;
     __syncthreads();
-    for (int c = tid; c < a.nb; c += 256) {
-        const uint32_t n = s_h[c];
+    for (int cc = tid; cc < a.nb; cc += 256) {
+        const uint32_t n = s_h[cc];
         if (!SCATTER) {
-            if (n) atomicAdd(&a.counts[bucket0 + c], n);
+            if (n) atomicAdd(&a.counts[bucket0 + cc], n);
         } else {
-            s_h[c] = n ? atomicAdd(&a.cursor[bucket0 + c], n) : 0u;  // reserved base
+            s_h[cc] = n ? atomicAdd(&a.cursor[bucket0 + cc], n) : 0u;  // reserved base
         }
     }
     if (!SCATTER) return;
     __syncthreads();
-    // pass B: place the pairs
     for (int i = tid; i < rep * span; i += 256) {
         const int hh = i / span, t = t0 + (i - hh * span);
         const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
-        const int32_t* ir = a.idx + row * a.top_k;
-        uint32_t m = used_slots(ir, a.top_k, eligible_blocks(t, a.bs, a.window));
-        while (m) {
-            const int s = __builtin_ctz(m);
-            m &= m - 1;
-            const uint32_t pos = atomicAdd(&s_h[ir[s]], 1u);
+        int c[kMaxTopK];
+        uint32_t m = row_used(a.idx + row * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+            if (!((m >> s) & 1u)) continue;
+            const uint32_t pos = atomicAdd(&s_h[c[s]], 1u);
             a.pairs[pos] = (uint32_t)(row * a.top_k + s);
         }
     }
@@ -273,83 +311,136 @@ struct PartArgs {
     float scale_log2;
 };
 
+// Work units (64 gathered rows of one bucket) are split into contiguous
+// ranges per workgroup, so K/V of a bucket are staged once for all its units.
+// Per wave, pair ids run two units ahead and Q rows one unit ahead of the
+// compute, hiding the dependent gather latency.
+struct UnitCursor {
+    int bucket;
+    __device__ void seek(const uint32_t* unit_off, int NB, uint32_t u) {
+        int lo = 0, hi = NB;  // last bucket b with unit_off[b] <= u
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (unit_off[mid] <= u) lo = mid; else hi = mid;
+        }
+        bucket = lo;
+    }
+    // Rows [p0, p1) of unit u (u >= the unit of the previous call).
+    __device__ void rows(const uint32_t* unit_off, const uint32_t* offsets, uint32_t u,
+                         uint32_t& p0, uint32_t& p1) {
+        while (unit_off[bucket + 1] <= u) ++bucket;
+        p0 = offsets[bucket] + (u - unit_off[bucket]) * UNIT_ROWS;
+        p1 = min(p0 + UNIT_ROWS, offsets[bucket + 1]);
+    }
+};
+
 template <int BS>
 __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     constexpr int KT = BS / 16;
-    constexpr int VP = BS + 8;
+    constexpr int VP = BS + 4;  // 2 mod 4 words: conflict-free 8-byte V^T reads
     __shared__ __attribute__((aligned(16))) __bf16 s_k[BS * KPITCH];
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[kD * VP];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t U = a.unit_off[a.NB];
     const uint32_t per = (U + gridDim.x - 1) / gridDim.x;
     const uint32_t u0 = blockIdx.x * per;
     const uint32_t u1 = min(U, u0 + per);
     if (u0 >= u1) return;
-    // bucket holding unit u0: last b with unit_off[b] <= u0
-    int lo = 0, hi = a.NB;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.unit_off[mid] <= u0) lo = mid; else hi = mid;
+    UnitCursor cur, ahead;
+    cur.seek(a.unit_off, a.NB, u0);
+    ahead = cur;
+    const uint32_t my = 16 * w + (lane & 15);  // this lane's row slot in a unit
+
+    // prologue: pair ids of units u0 and u0+1, Q rows of unit u0
+    uint32_t q0, q1;
+    ahead.rows(a.unit_off, a.offsets, u0, q0, q1);
+    bool v_cur = q0 + my < q1;
+    uint32_t pid_cur = v_cur ? a.pairs[q0 + my] : 0u;
+    bool v_nxt = false;
+    uint32_t pid_nxt = 0u;
+    if (u0 + 1 < u1) {
+        ahead.rows(a.unit_off, a.offsets, u0 + 1, q0, q1);
+        v_nxt = q0 + my < q1;
+        pid_nxt = v_nxt ? a.pairs[q0 + my] : 0u;
     }
-    int bucket = lo;
+    bf16x8 Bq[2];
+    load_q_operand(a.q + (int64_t)(pid_cur / (uint32_t)a.top_k) * kD, lane, v_cur, Bq);
+
     int loaded = -1;
     for (uint32_t u = u0; u < u1; ++u) {
-        while (a.unit_off[bucket + 1] <= u) ++bucket;
-        const uint32_t p0 = a.offsets[bucket] + (u - a.unit_off[bucket]) * UNIT_ROWS;
-        const uint32_t p1 = min(p0 + UNIT_ROWS, a.offsets[bucket + 1]);
-        if (bucket != loaded) {
+        uint32_t p0, p1;
+        cur.rows(a.unit_off, a.offsets, u, p0, p1);
+        // prefetch: pair ids of u+2, Q rows of u+1
+        bool v_n2 = false;
+        uint32_t pid_n2 = 0u;
+        if (u + 2 < u1) {
+            ahead.rows(a.unit_off, a.offsets, u + 2, q0, q1);
+            v_n2 = q0 + my < q1;
+            pid_n2 = v_n2 ? a.pairs[q0 + my] : 0u;
+        }
+        bf16x8 Bq_nxt[2];
+        load_q_operand(a.q + (int64_t)(pid_nxt / (uint32_t)a.top_k) * kD, lane, v_nxt, Bq_nxt);
+
+        if (cur.bucket != loaded) {
             __syncthreads();
-            const int bg = bucket / a.nb, c = bucket - bg * a.nb;
+            const int bg = cur.bucket / a.nb, c = cur.bucket - bg * a.nb;
             const int64_t kv0 = ((int64_t)bg * a.N + (int64_t)c * BS) * kD;
             stage_k(s_k, a.k + kv0, BS, BS, tid, 256);
             stage_vt(s_vt, VP, a.v + kv0, BS, BS, tid, 256);
             __syncthreads();
-            loaded = bucket;
+            loaded = cur.bucket;
         }
-        const uint32_t pi = p0 + 16 * w + (lane & 15);
-        const bool valid = pi < p1;
-        const uint32_t pid = valid ? a.pairs[pi] : 0u;
-        const int64_t row = pid / (uint32_t)a.top_k;
-        if (p0 + 16 * w >= p1) continue;  // whole wave idle (no barrier follows in this unit)
-        bf16x8 Bq[2];
-        load_q_operand(a.q + row * kD, lane, valid, Bq);
-        float x[KT][4];
-        float mx = -INFINITY;
+        if (p0 + 16 * w < p1) {  // wave has rows in this unit
+            float x[KT][4];
+            float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < KT; ++i) {
-            const f32x4 s = score_tile(s_k, i, lane, Bq);
+            for (int i = 0; i < KT; ++i) {
+                const f32x4 sc = score_tile(s_k, i, lane, Bq);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x[i][r] = s[r] * a.scale_log2;
-                mx = fmaxf(mx, x[i][r]);
+                for (int r = 0; r < 4; ++r) {
+                    x[i][r] = sc[r] * a.scale_log2;
+                    mx = fmaxf(mx, x[i][r]);
+                }
+            }
+            mx = row_max4(mx);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < KT; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[i][r] = exp2f(x[i][r] - mx);
+                    sum += x[i][r];
+                }
+            sum = row_sum4(sum);
+            f32x4 o[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            pv_accumulate<KT>(s_vt, VP, lane, x, o);
+            if (v_cur) {
+                // partial row layout: slot 16j + 4mt + r holds dim 16mt + 4j + r,
+                // so lane group j writes 32 contiguous bytes
+                const float inv = 1.f / sum;
+                uint16_t* dst = a.part_o + (int64_t)pid_cur * kD + 16 * (lane >> 4);
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    bf16x8 ob;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ob[r] = (__bf16)(o[2 * h2][r] * inv);
+                        ob[4 + r] = (__bf16)(o[2 * h2 + 1][r] * inv);
+                    }
+                    *reinterpret_cast<bf16x8*>(dst + 8 * h2) = ob;
+                }
+                if (lane < 16) a.part_lse[pid_cur] = mx + log2f(sum);
             }
         }
-        mx = row_max4(mx);
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < KT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                x[i][r] = exp2f(x[i][r] - mx);
-                sum += x[i][r];
-            }
-        sum = row_sum4(sum);
-        f32x4 o[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pv_accumulate<KT>(s_vt, VP, lane, x, o);
-        if (valid) {
-            const float inv = 1.f / sum;
-            uint16_t* dst = a.part_o + (int64_t)pid * kD + 4 * (lane >> 4);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                bf16x4 ob;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ob[r] = (__bf16)(o[mt][r] * inv);
-                *reinterpret_cast<bf16x4*>(dst + 16 * mt) = ob;
-            }
-            if (lane < 16) a.part_lse[pid] = mx + log2f(sum);
-        }
+        v_cur = v_nxt;
+        pid_cur = pid_nxt;
+        v_nxt = v_n2;
+        pid_nxt = pid_n2;
+        Bq[0] = Bq_nxt[0];
+        Bq[1] = Bq_nxt[1];
     }
 }
 
@@ -362,51 +453,109 @@ struct WinArgs {
     const uint16_t* part_o;
     const float* part_lse;
     float* out;
-    int Hq, Hkv, N, bs, top_k, window, tiles;
+    int Hq, Hkv, N, bs, top_k, window, tiles, unused;
     float scale_log2;
 };
 
-__global__ __launch_bounds__(256, 2) void k_window_merge(WinArgs a) {
-    constexpr int VP = 64 + 8;
-    __shared__ __attribute__((aligned(16))) __bf16 s_k[64 * KPITCH];
-    __shared__ __attribute__((aligned(16))) __bf16 s_vt[kD * VP];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int bh = blockIdx.x / a.tiles, tile = blockIdx.x - bh * a.tiles;
-    const int h = bh % a.Hq, b = bh / a.Hq, g = h / (a.Hq / a.Hkv);
+constexpr int WVP = 64 + 4;  // V^T pitch of 64-key tiles (2 mod 4 words)
+
+// One workgroup per (query head, 64 positions); wave w owns rows
+// t0 + 16w .. +15 (lane l holds row l%16).  The window keys stream through
+// double-buffered LDS tiles (the next tile is fetched into registers while
+// the current one is used); the seven heads of a KV group hit the same
+// tiles in L2.  Masks are applied only on chunks that cross a row's window
+// start or its causal end.
+__global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[2][64 * KPITCH];
+    __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][kD * WVP];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = blockIdx.x % a.tiles;
+    const int bh = blockIdx.x / a.tiles;
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
     const int t0 = tile * 64;
-    const int t = t0 + 16 * w + (lane & 15);
-    const bool valid = t < a.N;
-    const int64_t row = (int64_t)bh * a.N + t;
-    const int E = valid ? eligible_blocks(t, a.bs, a.window) : 0;
-    const int lo_t = a.bs * E;  // first window key of this row
     const int key_lo = a.bs * eligible_blocks(t0, a.bs, a.window);
     const int key_hi = min(t0 + 63, a.N - 1);
-    const int64_t kv0 = ((int64_t)b * a.Hkv + g) * a.N * kD;
+    const int lo_max = a.bs * eligible_blocks(key_hi, a.bs, a.window);  // largest row start
+    const int64_t kv0 = (int64_t)bg * a.N * kD;
+    const int t = t0 + 16 * w + (lane & 15);
+    const bool valid = t < a.N;
+    const int E = valid ? eligible_blocks(t, a.bs, a.window) : 0;
+    const int lo_t = valid ? a.bs * E : a.N;
+    const int64_t row = (int64_t)bh * a.N + t;
 
     bf16x8 Bq[2];
     load_q_operand(a.q + row * kD, lane, valid, Bq);
+    // the row's routed slots, read now so the loads overlap the window work
+    int csel[kMaxTopK];
+    const uint32_t used = valid ? row_used(a.idx + row * a.top_k, a.top_k, E, csel) : 0u;
     f32x4 o[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int kc = key_lo; kc <= key_hi; kc += 64) {
+    // staging: K tile = 512 chunks of 16 B (2 per thread), V tile = 256 4x4
+    // sub-tiles (1 per thread)
+    u32x4 kp[2];
+    u32x2 vp[4];
+    const int kg = tid & 15, dg = tid >> 4;
+    auto fetch = [&](int kc) {
         const int nvalid = min(64, a.N - kc);
-        __syncthreads();
-        stage_k(s_k, a.k + kv0 + (int64_t)kc * kD, 64, nvalid, tid, 256);
-        stage_vt(s_vt, VP, a.v + kv0 + (int64_t)kc * kD, 64, nvalid, tid, 256);
-        __syncthreads();
+        const uint16_t* ks = a.k + kv0 + (int64_t)kc * kD;
+        const uint16_t* vs = a.v + kv0 + (int64_t)kc * kD;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ch = tid + 256 * i, key = ch >> 3;
+            kp[i] = key < nvalid
+                        ? *reinterpret_cast<const u32x4*>(ks + (int64_t)key * kD + (ch & 7) * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = kg * 4 + r;
+            vp[r] = key < nvalid ? *reinterpret_cast<const u32x2*>(vs + (int64_t)key * kD + dg * 4)
+                                 : u32x2{0u, 0u};
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ch = tid + 256 * i;
+            *reinterpret_cast<u32x4*>(s_k[buf] + (ch >> 3) * KPITCH + (ch & 7) * 8) = kp[i];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int sh = (jj & 1) * 16, wi = jj >> 1;
+            const uint32_t e0 = (vp[0][wi] >> sh) & 0xFFFFu, e1 = (vp[1][wi] >> sh) & 0xFFFFu;
+            const uint32_t e2 = (vp[2][wi] >> sh) & 0xFFFFu, e3 = (vp[3][wi] >> sh) & 0xFFFFu;
+            *reinterpret_cast<u32x2*>(s_vt[buf] + (dg * 4 + jj) * WVP + kg * 4) =
+                u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+        }
+    };
+
+    fetch(key_lo);
+    commit(0);
+    __syncthreads();
+    for (int kc = key_lo, it = 0; kc <= key_hi; kc += 64, ++it) {
+        const int buf = it & 1;
+        const bool more = kc + 64 <= key_hi;
+        if (more) fetch(kc + 64);
+        const bool edge = kc < lo_max || kc + 63 > t0;
         float x[4][4];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 s = score_tile(s_k, i, lane, Bq);
+            const f32x4 sc = score_tile(s_k[buf], i, lane, Bq);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int j = kc + 16 * i + 4 * (lane >> 4) + r;
-                const bool ok = valid && j >= lo_t && j <= t;
-                x[i][r] = ok ? s[r] * a.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[i][r]);
+                float xv = sc[r] * a.scale_log2;
+                if (edge) {
+                    const int jk = kc + 16 * i + 4 * (lane >> 4) + r;
+                    xv = (jk >= lo_t && jk <= t) ? xv : -INFINITY;
+                }
+                x[i][r] = xv;
+                mx = fmaxf(mx, xv);
             }
         }
         mx = row_max4(mx);
@@ -426,33 +575,66 @@ __global__ __launch_bounds__(256, 2) void k_window_merge(WinArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
         m_run = m_new;
-        pv_accumulate<4>(s_vt, VP, lane, x, o);
+        pv_accumulate<4>(s_vt[buf], WVP, lane, x, o);
+        if (more) commit(buf ^ 1);
+        __syncthreads();
     }
     if (!valid) return;
-    // merge the routed partials (each a normalised output with its log2 mass)
-    const int32_t* ir = a.idx + row * a.top_k;
-    uint32_t used = used_slots(ir, a.top_k, E);
-    while (used) {
-        const int s = __builtin_ctz(used);
-        used &= used - 1;
-        const int64_t pid = row * a.top_k + s;
-        const float lse = a.part_lse[pid];
-        const float m_new = fmaxf(m_run, lse);
-        const float alpha = exp2f(m_run - m_new);
-        const float beta = exp2f(lse - m_new);
-        const uint16_t* src = a.part_o + pid * kD + 4 * (lane >> 4);
-        l_run = l_run * alpha + beta;
+
+    // merge the routed partials (normalised outputs with their log2 mass),
+    // eight slots at a time so their loads are in flight together.  A
+    // partial row stores dim 16mt + 4j + r at slot 16j + 4mt + r, so lane
+    // group j reads its 16 values as 32 contiguous bytes.
+    float lse_all[kMaxTopK];
+    {
+        const float* lp = a.part_lse + row * a.top_k;
+        if ((a.top_k & 3) == 0) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const u32x2 raw = *reinterpret_cast<const u32x2*>(src + 16 * mt);
-            const float v0 = __uint_as_float(raw[0] << 16), v1 = __uint_as_float(raw[0] & 0xFFFF0000u);
-            const float v2 = __uint_as_float(raw[1] << 16), v3 = __uint_as_float(raw[1] & 0xFFFF0000u);
-            o[mt][0] = o[mt][0] * alpha + beta * v0;
-            o[mt][1] = o[mt][1] * alpha + beta * v1;
-            o[mt][2] = o[mt][2] * alpha + beta * v2;
-            o[mt][3] = o[mt][3] * alpha + beta * v3;
+            for (int s4 = 0; s4 < kMaxTopK / 4; ++s4) {
+                f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                if (4 * s4 < a.top_k && ((used >> (4 * s4)) & 0xFu))
+                    v = *reinterpret_cast<const f32x4*>(lp + 4 * s4);
+                lse_all[4 * s4] = v[0]; lse_all[4 * s4 + 1] = v[1];
+                lse_all[4 * s4 + 2] = v[2]; lse_all[4 * s4 + 3] = v[3];
+            }
+        } else {
+#pragma unroll
+            for (int sl = 0; sl < kMaxTopK; ++sl)
+                lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? lp[sl] : -INFINITY;
         }
-        m_run = m_new;
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < kMaxTopK; s0 += 8) {
+        if (s0 >= a.top_k) break;
+        u32x4 po[8][2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int sl = s0 + i;
+            const bool u = sl < a.top_k && ((used >> sl) & 1u);
+            const uint16_t* src = a.part_o + (row * a.top_k + sl) * kD + 16 * (lane >> 4);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                po[i][h2] = u ? *reinterpret_cast<const u32x4*>(src + 8 * h2) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int sl = s0 + i;
+            if (!(sl < a.top_k && ((used >> sl) & 1u))) continue;
+            const float lse = lse_all[sl];
+            const float m_new = fmaxf(m_run, lse);
+            const float alpha = exp2f(m_run - m_new);
+            const float beta = exp2f(lse - m_new);
+            l_run = l_run * alpha + beta;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const uint32_t w0 = po[i][mt >> 1][2 * (mt & 1)], w1 = po[i][mt >> 1][2 * (mt & 1) + 1];
+                o[mt][0] = o[mt][0] * alpha + beta * __uint_as_float(w0 << 16);
+                o[mt][1] = o[mt][1] * alpha + beta * __uint_as_float(w0 & 0xFFFF0000u);
+                o[mt][2] = o[mt][2] * alpha + beta * __uint_as_float(w1 << 16);
+                o[mt][3] = o[mt][3] * alpha + beta * __uint_as_float(w1 & 0xFFFF0000u);
+            }
+            m_run = m_new;
+        }
     }
     const float inv = 1.f / l_run;
     float* dst = a.out + row * kD + 4 * (lane >> 4);
@@ -477,7 +659,7 @@ struct ImgArgs {
 // MFMA straight from global memory, V is transposed through the wave's own
 // LDS region.
 __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
-    constexpr int VP = 64 + 8;
+    constexpr int VP = WVP;
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[4][kD * VP];
     __shared__ int s_n[4];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -492,7 +674,8 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 
     // the used slots of this query block's idx row (wave-uniform)
     const int32_t* ir = a.idx + (active ? qb : 0) * a.top_k;
-    const uint32_t used = active ? used_slots(ir, a.top_k, a.nb) : 0u;
+    int csel[kMaxTopK];
+    const uint32_t used = active ? row_used(ir, a.top_k, a.nb, csel) : 0u;
     const int nused = __builtin_popcount(used);
     if (lane == 0) s_n[w] = nused;
     __syncthreads();
@@ -512,7 +695,7 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const bool have = c0 + jb < nused;
-            const int cblk = have ? ir[nth_slot(used, c0 + jb)] : 0;
+            const int cblk = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
             const uint16_t* src = a.v + kv0 + (int64_t)cblk * 16 * kD;
             // 16 keys x 64 dims = 64 4x4 tiles: one per lane
             const int kg = lane & 3, dg = lane >> 2;
@@ -539,7 +722,7 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const bool have = c0 + jb < nused;
-            const int cblk = have ? ir[nth_slot(used, c0 + jb)] : 0;
+            const int cblk = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (have) {
                 const uint16_t* kr = a.k + kv0 + ((int64_t)cblk * 16 + (lane & 15)) * kD + 8 * (lane >> 4);
@@ -604,7 +787,16 @@ size_t attend_workspace_bytes(const Geometry& g) { return attend_layout(g).total
 
 template <int BS>
 static void launch_partial(const PartArgs& pa, hipStream_t s) {
-    hipLaunchKernelGGL(k_block_partial<BS>, dim3(PART_GRID), dim3(256), 0, s, pa);
+    // one resident wave of workgroups: CUs x workgroups per CU
+    static int grid = 0;
+    if (grid == 0) {
+        int dev = 0, cus = 256, per_cu = 2;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_block_partial<BS>, 256, 0);
+        grid = cus * (per_cu > 0 ? per_cu : 1);
+    }
+    hipLaunchKernelGGL(k_block_partial<BS>, dim3(grid), dim3(256), 0, s, pa);
 }
 
 hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k,
@@ -633,8 +825,14 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
 
     hipError_t e = launch_fill_u32(counts, (size_t)NB, 0u, s);
     if (e != hipSuccess) return e;
-    BucketArgs ba{idx, counts, cursor, pairs, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window};
-    const int nch = (g.N + BK_TCHUNK - 1) / BK_TCHUNK;
+    // positions per bucketing workgroup: ~4096 rows, and enough pairs to
+    // amortise the per-bucket flush
+    const int rep = g.Hq / g.Hkv;
+    int64_t tc = std::max<int64_t>((4096 + rep - 1) / rep,
+                                   (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k));
+    tc = std::min<int64_t>((tc + 63) / 64 * 64, g.N);
+    BucketArgs ba{idx, counts, cursor, pairs, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window, (int)tc};
+    const int nch = (int)((g.N + tc - 1) / tc);
     const dim3 bgrid((unsigned)(g.B * g.Hkv * nch));
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
     hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
@@ -655,9 +853,9 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     }
     mark(ev, 7, s);
     WinArgs wa{q, k, v, idx, part_o, part_lse, out, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
-               (g.N + 63) / 64, scale_log2};
-    hipLaunchKernelGGL(k_window_merge, dim3((unsigned)(g.B * g.Hq * wa.tiles)), dim3(256), 0, s,
-                       wa);
+               (g.N + 63) / 64, 1, scale_log2};
+    hipLaunchKernelGGL(k_window_merge, dim3((unsigned)((int64_t)g.B * g.Hq * wa.tiles)), dim3(256),
+                       0, s, wa);
     mark(ev, 8, s);
     return hipGetLastError();
 }

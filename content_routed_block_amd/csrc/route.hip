@@ -35,23 +35,28 @@
 
 namespace lsa {
 
-constexpr int RT_ROWS = 256;   // query rows per workgroup
+constexpr int RT_ROWS = 256;   // query rows per workgroup (4 waves x 64)
 constexpr int RT_CH = 32;      // candidates per step
-constexpr int RT_CAP = 32;     // survivor slots per query
-constexpr int RT_PITCH = 72;   // padded LDS row pitch (bf16), conflict-free 16-byte reads
+constexpr int RT_CAP = 40;     // survivor slots per query
+constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
 constexpr int FB_GRID = 256;   // workgroups of the exact fallback
 
 struct RouteArgs {
     const uint16_t* q;    // causal: bf16 [B,Hq,N,64]
     const float* qbar;    // image: fp32 [B,Hq,nb,64]
     const float* kbar;    // [B,Hkv,nb,64]
+    const uint16_t* khi;  // bf16 hi part of kbar [B*Hkv][nb_pad][64]
+    const uint16_t* klo;  // bf16 lo part (kbar - hi) [B*Hkv][nb_pad][64]
+    const float* pk;      // prefix max over c of |kbar_c| [B*Hkv][nb]
+    const float* plo;     // prefix max over c of |lo_c| [B*Hkv][nb]
     int32_t* idx;         // [B,Hq,P,top_k]
     uint32_t* ovf_count;  // queued overflow rows
     uint32_t* ovf_rows;   // [B*Hq*P]
     float* fb_scratch;    // [FB_GRID][nb]
     int Hq, Hkv, N, bs, nb, top_k, window;
-    int P;      // rows per (b, h): N (causal) or nb (image)
-    int tiles;  // ceil(P / RT_ROWS)
+    int P;       // rows per (b, h): N (causal) or nb (image)
+    int tiles;   // ceil(P / RT_ROWS)
+    int nb_pad;  // nb rounded up to a multiple of RT_CH
 };
 
 // ------------------------------------------------------------ sorting networks
@@ -141,51 +146,90 @@ __device__ __forceinline__ void write_selection(int32_t* out, const uint64_t (&L
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) cs[j] = j < m ? key_block(L[j]) : 0xFFFFFFFFu;
     bitonic_sort_asc_u32<kMaxTopK>(cs);
+    if ((top_k & 3) == 0) {  // 16-byte stores (rows are 16-byte aligned)
+        typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-        if (j < top_k) out[j] = j < m ? (int32_t)cs[j] : -1;
-}
-
-// ------------------------------------------------------------ staging
-// Thread tid stages candidate row tid/8, dims 8*(tid%8) .. +7 of the chunk.
-__device__ __forceinline__ void load_chunk(const float* kb, int cb, int nb, int tid,
-                                           f32x4& p0, f32x4& p1) {
-    const int c = cb + (tid >> 3);
-    if (c < nb) {
-        const float* src = kb + (int64_t)c * kD + (tid & 7) * 8;
-        p0 = *reinterpret_cast<const f32x4*>(src);
-        p1 = *reinterpret_cast<const f32x4*>(src + 4);
+        for (int j4 = 0; j4 < kMaxTopK / 4; ++j4) {
+            if (4 * j4 < top_k) {
+                i32x4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = 4 * j4 + r < m ? (int32_t)cs[4 * j4 + r] : -1;
+                *reinterpret_cast<i32x4*>(out + 4 * j4) = v;
+            }
+        }
     } else {
-        p0 = f32x4{0.f, 0.f, 0.f, 0.f};
-        p1 = p0;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (j < top_k) out[j] = j < m ? (int32_t)cs[j] : -1;
     }
 }
 
-// Splits the staged floats into bf16 hi/lo, stores them, and returns the
-// squared norms of the full row (kn2) and of its lo part (lo2), reduced over
-// the 8 threads that share the row.
-__device__ __forceinline__ void store_chunk(__bf16* s_hi, __bf16* s_lo, int tid, f32x4 p0,
-                                            f32x4 p1, float& kn2, float& lo2) {
-    float f[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+// ------------------------------------------------------------ preparation
+// One thread per (block row, 8 dims): bf16 hi/lo split of the block means
+// (rows padded to a multiple of 32 with zeros) and the row norms.
+__global__ __launch_bounds__(256) void k_route_prep(const float* __restrict__ kbar,
+                                                    uint16_t* __restrict__ khi,
+                                                    uint16_t* __restrict__ klo,
+                                                    float* __restrict__ kn,
+                                                    float* __restrict__ lon, int n_bg, int nb,
+                                                    int nb_pad) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid >> 3;  // over n_bg * nb_pad rows
+    if (row >= (int64_t)n_bg * nb_pad) return;
+    const int bg = (int)(row / nb_pad), c = (int)(row - (int64_t)bg * nb_pad);
+    const int d0 = (threadIdx.x & 7) * 8;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < nb) {
+        const float* src = kbar + ((int64_t)bg * nb + c) * kD + d0;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+        f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+        f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+    }
     bf16x8 hi, lo;
-    kn2 = 0.f;
-    lo2 = 0.f;
+    float k2 = 0.f, l2 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         hi[i] = (__bf16)f[i];
-        const float r = f[i] - (float)hi[i];
-        lo[i] = (__bf16)r;
+        lo[i] = (__bf16)(f[i] - (float)hi[i]);
         const float lf = (float)lo[i];
-        kn2 = fmaf(f[i], f[i], kn2);
-        lo2 = fmaf(lf, lf, lo2);
+        k2 = fmaf(f[i], f[i], k2);
+        l2 = fmaf(lf, lf, l2);
     }
-    const int off = (tid >> 3) * RT_PITCH + (tid & 7) * 8;
-    *reinterpret_cast<bf16x8*>(s_hi + off) = hi;
-    *reinterpret_cast<bf16x8*>(s_lo + off) = lo;
+    *reinterpret_cast<bf16x8*>(khi + row * kD + d0) = hi;
+    *reinterpret_cast<bf16x8*>(klo + row * kD + d0) = lo;
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) {
-        kn2 += __shfl_xor(kn2, m, kWave);
-        lo2 += __shfl_xor(lo2, m, kWave);
+        k2 += __shfl_xor(k2, m, kWave);
+        l2 += __shfl_xor(l2, m, kWave);
+    }
+    if ((threadIdx.x & 7) == 0 && c < nb) {
+        kn[(int64_t)bg * nb + c] = sqrtf(k2);
+        lon[(int64_t)bg * nb + c] = sqrtf(l2);
+    }
+}
+
+// In-place prefix maximum of rows of length n (one workgroup per row).
+__global__ __launch_bounds__(1024) void k_prefix_max(float* __restrict__ x, int n) {
+    __shared__ float s[1024];
+    float* row = x + (int64_t)blockIdx.x * n;
+    const int tid = threadIdx.x;
+    const int per = (n + 1023) / 1024;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    float m = 0.f;  // norms are >= 0
+    for (int i = lo; i < hi; ++i) m = fmaxf(m, row[i]);
+    s[tid] = m;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const float o = tid >= off ? s[tid - off] : 0.f;
+        __syncthreads();
+        s[tid] = fmaxf(s[tid], o);
+        __syncthreads();
+    }
+    float run = tid > 0 ? s[tid - 1] : 0.f;
+    for (int i = lo; i < hi; ++i) {
+        run = fmaxf(run, row[i]);
+        row[i] = run;
     }
 }
 
@@ -195,36 +239,56 @@ __device__ __forceinline__ int row_candidates(bool causal, int row, int P, int b
     return causal ? eligible_blocks(row, bs, window) : nb;
 }
 
+// Staging of one chunk (32 candidate rows x 64 dims, bf16) through LDS:
+// thread tid carries row tid/8, dims 8*(tid%8) .. +7 (16 bytes).
+__device__ __forceinline__ u32x4 stage_load(const uint16_t* base, int cb, int tid) {
+    return *reinterpret_cast<const u32x4*>(base + (int64_t)(cb + (tid >> 3)) * kD + (tid & 7) * 8);
+}
+__device__ __forceinline__ void stage_store(__bf16* buf, int tid, u32x4 v) {
+    *reinterpret_cast<u32x4*>(buf + (tid >> 3) * RT_PITCH + (tid & 7) * 8) = v;
+}
+// A operands of one step: rows l%32, dims 8*half + 16*ks.
+__device__ __forceinline__ void read_cands(const __bf16* buf, int l32, int half, bf16x8 (&A)[4]) {
+    const __bf16* p = buf + l32 * RT_PITCH + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) A[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks);
+}
+
 // ------------------------------------------------------------ main kernel
+// Each wave is independent (its own 64 rows, its own survivor lists); the
+// only workgroup barrier separates scoring from selection.
 template <bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 s_hi[RT_CH * RT_PITCH];
-    __shared__ __attribute__((aligned(16))) __bf16 s_lo[RT_CH * RT_PITCH];
+    __shared__ __attribute__((aligned(16))) __bf16 s_hi[2][RT_CH * RT_PITCH];
+    __shared__ __attribute__((aligned(16))) __bf16 s_lo[2][RT_CH * RT_PITCH];
     __shared__ float s_score[RT_ROWS * RT_CAP];
     __shared__ uint16_t s_cidx[RT_ROWS * RT_CAP];
     __shared__ int s_cnt[RT_ROWS * 2];
-    __shared__ float s_red[8];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int half = lane >> 5, l32 = lane & 31;
     const int bh = blockIdx.x / a.tiles;
     const int tile = a.tiles - 1 - (int)(blockIdx.x - bh * a.tiles);  // heavy tiles first
     const int h = bh % a.Hq, b = bh / a.Hq;
-    const int g = h / (a.Hq / a.Hkv);
+    const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
     const int P = a.P;
-    const int row0 = tile * RT_ROWS;
-    const float* kb = a.kbar + (int64_t)(b * a.Hkv + g) * a.nb * kD;
+    const int r0 = tile * RT_ROWS + 64 * w;  // first row of this wave
+    const uint16_t* khi = a.khi + (int64_t)bg * a.nb_pad * kD;
+    const uint16_t* klo = a.klo + (int64_t)bg * a.nb_pad * kD;
 
     int rq[2], Erow[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-        rq[tt] = row0 + 64 * w + 32 * tt + l32;
+        rq[tt] = r0 + 32 * tt + l32;
         Erow[tt] = row_candidates(CAUSAL, rq[tt], P, a.bs, a.window, a.nb);
     }
-    const int last = min(row0 + RT_ROWS, P) - 1;
-    const int Emax = row_candidates(CAUSAL, last, P, a.bs, a.window, a.nb);
-    const int wfirst = row0 + 64 * w;
-    const int Ewmin = (wfirst + 63 < P) ? row_candidates(CAUSAL, wfirst, P, a.bs, a.window, a.nb) : 0;
+    const int Emax = r0 < P ? row_candidates(CAUSAL, min(r0 + 63, P - 1), P, a.bs, a.window, a.nb) : 0;
+    const int wg_last = min(tile * RT_ROWS + RT_ROWS, P) - 1;
+    const int Ewg = row_candidates(CAUSAL, wg_last, P, a.bs, a.window, a.nb);  // chunk loop bound
+    const int Emin = (r0 + 63 < P) ? row_candidates(CAUSAL, r0, P, a.bs, a.window, a.nb) : 0;
+    const float kn_max = Emax > 0 ? a.pk[(int64_t)bg * a.nb + Emax - 1] : 0.f;
+    const float lo_max = Emax > 0 ? a.plo[(int64_t)bg * a.nb + Emax - 1] : 0.f;
 
     // ---- queries as the B operand (B[d][t] = Q[t][d]): lane holds dims
     // 8*half + 16*ks .. +7 of row rq[tt].
@@ -279,59 +343,48 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
         qln[tt] = sqrtf(l2);
     }
 
-    // ---- pass 1: hi-only scores, group maxima, norms of the candidates
+    // ---- pass 1: hi-only scores, group maxima
+    // Chunks below Efull are candidates of every row of the wave (no mask).
+    const int Efull = (Emin / RT_CH) * RT_CH;
     float gm[2][16];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) gm[tt][r] = -INFINITY;
-    float kn2max = 0.f, lo2max = 0.f;
-    f32x4 p0, p1;
-    if (Emax > 0) load_chunk(kb, 0, a.nb, tid, p0, p1);
-    for (int cb = 0; cb < Emax; cb += RT_CH) {
+    {
+        // chunk j is staged in buffer j&1; one barrier per chunk
+        u32x4 pre = Ewg > 0 ? stage_load(khi, 0, tid) : u32x4{0u, 0u, 0u, 0u};
+        if (Ewg > 0) stage_store(s_hi[0], tid, pre);
         __syncthreads();
-        float kn2, lo2;
-        store_chunk(s_hi, s_lo, tid, p0, p1, kn2, lo2);
-        if (cb + (tid >> 3) < Emax) {
-            kn2max = fmaxf(kn2max, kn2);
-            lo2max = fmaxf(lo2max, lo2);
-        }
-        __syncthreads();
-        if (cb + RT_CH < Emax) load_chunk(kb, cb + RT_CH, a.nb, tid, p0, p1);
-        bf16x8 A[4];
+        for (int cb = 0, j = 0; cb < Ewg; cb += RT_CH, ++j) {
+            if (cb + RT_CH < Ewg) pre = stage_load(khi, cb + RT_CH, tid);
+            if (cb < Emax) {
+                bf16x8 A[4];
+                read_cands(s_hi[j & 1], l32, half, A);
+                f32x16 acc[2] = {};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            A[ks] = *reinterpret_cast<const bf16x8*>(s_hi + l32 * RT_PITCH + 8 * half + 16 * ks);
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            f32x16 acc = {};
+                    for (int ks = 0; ks < 4; ++ks) acc[tt] = mfma32(A[ks], Bq[tt][ks], acc[tt]);
+                if (cb < Efull) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc = mfma32(A[ks], Bq[tt][ks], acc);
-            if (cb + RT_CH <= Ewmin) {
+                    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) gm[tt][r] = fmaxf(gm[tt][r], acc[r]);
-            } else {
+                        for (int r = 0; r < 16; ++r) gm[tt][r] = fmaxf(gm[tt][r], acc[tt][r]);
+                } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int c = cb + 8 * (r >> 2) + 4 * half + (r & 3);
-                    gm[tt][r] = fmaxf(gm[tt][r], c < Erow[tt] ? acc[r] : -INFINITY);
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int c = cb + 8 * (r >> 2) + 4 * half + (r & 3);
+                            gm[tt][r] = fmaxf(gm[tt][r], c < Erow[tt] ? acc[tt][r] : -INFINITY);
+                        }
                 }
             }
+            if (cb + RT_CH < Ewg) stage_store(s_hi[(j + 1) & 1], tid, pre);
+            __syncthreads();
         }
     }
-    // workgroup maxima of the candidate norms
-#pragma unroll
-    for (int m = 8; m < 64; m <<= 1) {
-        kn2max = fmaxf(kn2max, __shfl_xor(kn2max, m, kWave));
-        lo2max = fmaxf(lo2max, __shfl_xor(lo2max, m, kWave));
-    }
-    if (lane == 0) {
-        s_red[w] = kn2max;
-        s_red[4 + w] = lo2max;
-    }
-    __syncthreads();
-    const float kn_max = sqrtf(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])));
-    const float lo_max = sqrtf(fmaxf(fmaxf(s_red[4], s_red[5]), fmaxf(s_red[6], s_red[7])));
 
     // threshold: k-th largest group maximum minus a bound on |a_c - b_c|:
     // |q_hi . k_lo| + |q_lo . k_hi| + fp32 accumulation error.
@@ -344,52 +397,92 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
         theta[tt] = th - delta;  // -inf stays -inf
     }
 
-    // ---- pass 2: hi+lo scores, survivors to LDS
-    int n[2] = {0, 0};
-    if (Emax > 0) load_chunk(kb, 0, a.nb, tid, p0, p1);
-    for (int cb = 0; cb < Emax; cb += RT_CH) {
-        __syncthreads();
-        float kn2, lo2;
-        store_chunk(s_hi, s_lo, tid, p0, p1, kn2, lo2);
-        __syncthreads();
-        if (cb + RT_CH < Emax) load_chunk(kb, cb + RT_CH, a.nb, tid, p0, p1);
-        bf16x8 Ah[4], Al[4];
+    // ---- pass 2: hi+lo scores, survivors to this wave's LDS lists.
+    // The lane pair (l, l^32) shares a query's list: half 0 fills it upward
+    // from slot 0, half 1 downward from slot RT_CAP-1; slot indices are
+    // clamped to the list, so an overflowing list stays in bounds (the query
+    // is then redone by the fallback).
+    int pos[2], lo_slot[2], hi_slot[2];
+    const int dir = half ? -1 : 1;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            Ah[ks] = *reinterpret_cast<const bf16x8*>(s_hi + l32 * RT_PITCH + 8 * half + 16 * ks);
-            Al[ks] = *reinterpret_cast<const bf16x8*>(s_lo + l32 * RT_PITCH + 8 * half + 16 * ks);
+    for (int tt = 0; tt < 2; ++tt) {
+        const int base = (64 * w + 32 * tt + l32) * RT_CAP;
+        lo_slot[tt] = base;
+        hi_slot[tt] = base + RT_CAP - 1;
+        pos[tt] = half ? hi_slot[tt] : lo_slot[tt];
+    }
+    {
+        u32x4 ph = {0u, 0u, 0u, 0u}, pl = ph;
+        if (Ewg > 0) {
+            ph = stage_load(khi, 0, tid);
+            pl = stage_load(klo, 0, tid);
+            stage_store(s_hi[0], tid, ph);
+            stage_store(s_lo[0], tid, pl);
         }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            f32x16 acc = {};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                acc = mfma32(Ah[ks], Bq[tt][ks], acc);
-                acc = mfma32(Al[ks], Bq[tt][ks], acc);
-                if (!CAUSAL) acc = mfma32(Ah[ks], Bql[tt][ks], acc);
+        __syncthreads();
+        for (int cb = 0, j = 0; cb < Ewg; cb += RT_CH, ++j) {
+            if (cb + RT_CH < Ewg) {
+                ph = stage_load(khi, cb + RT_CH, tid);
+                pl = stage_load(klo, cb + RT_CH, tid);
             }
-            const int qs = 64 * w + 32 * tt + l32;
+            if (cb < Emax) {
+                bf16x8 ch[4], cl[4];
+                read_cands(s_hi[j & 1], l32, half, ch);
+                read_cands(s_lo[j & 1], l32, half, cl);
+                f32x16 acc[2] = {};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = cb + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (acc[r] >= theta[tt] && c < Erow[tt]) {
-                    if (n[tt] < RT_CAP) {
-                        const int pos = half ? (RT_CAP - 1 - n[tt]) : n[tt];
-                        s_score[qs * RT_CAP + pos] = acc[r];
-                        s_cidx[qs * RT_CAP + pos] = (uint16_t)c;
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        acc[tt] = mfma32(ch[ks], Bq[tt][ks], acc[tt]);
+                        acc[tt] = mfma32(cl[ks], Bq[tt][ks], acc[tt]);
+                        if (!CAUSAL) acc[tt] = mfma32(ch[ks], Bql[tt][ks], acc[tt]);
                     }
-                    ++n[tt];
+                const int cl0 = cb + 4 * half;
+                if (cb < Efull) {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            if (acc[tt][r] >= theta[tt]) {
+                                const int at = min(max(pos[tt], lo_slot[tt]), hi_slot[tt]);
+                                s_score[at] = acc[tt][r];
+                                s_cidx[at] = (uint16_t)(cl0 + 8 * (r >> 2) + (r & 3));
+                                pos[tt] += dir;
+                            }
+                        }
+                } else {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int c = cl0 + 8 * (r >> 2) + (r & 3);
+                            if (acc[tt][r] >= theta[tt] && c < Erow[tt]) {
+                                const int at = min(max(pos[tt], lo_slot[tt]), hi_slot[tt]);
+                                s_score[at] = acc[tt][r];
+                                s_cidx[at] = (uint16_t)c;
+                                pos[tt] += dir;
+                            }
+                        }
                 }
             }
+            if (cb + RT_CH < Ewg) {
+                stage_store(s_hi[(j + 1) & 1], tid, ph);
+                stage_store(s_lo[(j + 1) & 1], tid, pl);
+            }
+            __syncthreads();
         }
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) s_cnt[(64 * w + 32 * tt + l32) * 2 + half] = n[tt];
+    for (int tt = 0; tt < 2; ++tt) {
+        const int n = half ? (hi_slot[tt] - pos[tt]) : (pos[tt] - lo_slot[tt]);
+        s_cnt[(64 * w + 32 * tt + l32) * 2 + half] = n;
+    }
     __syncthreads();
 
     // ---- selection: lane -> query 64*w + lane
     const int qs = 64 * w + lane;
-    const int row = row0 + qs;
+    const int row = r0 + lane;
     if (row < P) {
         const int n0 = s_cnt[qs * 2], n1 = s_cnt[qs * 2 + 1];
         const int nt = n0 + n1;
@@ -434,8 +527,16 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
         }
         __syncthreads();
         for (int c = tid; c < E; c += 256) {
+            const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)c * kD);
             float s = 0.f;
-            for (int d = 0; d < kD; ++d) s = fmaf(s_q[d], kb[(int64_t)c * kD + d], s);
+#pragma unroll 4
+            for (int d4 = 0; d4 < kD / 4; ++d4) {
+                const f32x4 v = kr[d4];
+                s = fmaf(s_q[4 * d4], v[0], s);
+                s = fmaf(s_q[4 * d4 + 1], v[1], s);
+                s = fmaf(s_q[4 * d4 + 2], v[2], s);
+                s = fmaf(s_q[4 * d4 + 3], v[3], s);
+            }
             sc[c] = s;
         }
         __syncthreads();
@@ -479,29 +580,49 @@ static size_t route_rows(const Geometry& g) {
     return (size_t)g.B * g.Hq * (g.causal ? (size_t)g.N : (size_t)g.nb);
 }
 
-size_t route_workspace_bytes(const Geometry& g) {
-    size_t off = 256;                                          // overflow counter
-    off += align_up(route_rows(g) * sizeof(uint32_t), 256);    // overflow rows
-    off += align_up((size_t)FB_GRID * g.nb * sizeof(float), 256);
-    if (!g.causal) off += align_up((size_t)g.B * g.Hq * g.nb * kD * sizeof(float), 256);
-    return off;
+struct RouteLayout {
+    size_t ovf_rows, fb, qbar, khi, klo, pk, total;
+    int nb_pad;
+};
+
+static RouteLayout route_layout(const Geometry& g) {
+    RouteLayout L{};
+    L.nb_pad = (g.nb + RT_CH - 1) / RT_CH * RT_CH;
+    const size_t nbg = (size_t)g.B * g.Hkv;
+    size_t off = 256;  // overflow counter
+    L.ovf_rows = off; off += align_up(route_rows(g) * 4, 256);
+    L.fb = off;       off += align_up((size_t)FB_GRID * g.nb * 4, 256);
+    L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * g.nb * kD * 4, 256);
+    L.khi = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
+    L.klo = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
+    L.pk = off;       off += align_up(2 * nbg * g.nb * 4, 256);  // pk then plo
+    L.total = off;
+    return L;
 }
+
+size_t route_workspace_bytes(const Geometry& g) { return route_layout(g).total; }
 
 hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar, int32_t* idx,
                         void* ws, hipStream_t s, const hipEvent_t* ev) {
     char* base = static_cast<char*>(ws);
+    const RouteLayout L = route_layout(g);
+    const int nbg = g.B * g.Hkv;
     RouteArgs a;
     a.ovf_count = reinterpret_cast<uint32_t*>(base);
-    size_t off = 256;
-    a.ovf_rows = reinterpret_cast<uint32_t*>(base + off);
-    off += align_up(route_rows(g) * sizeof(uint32_t), 256);
-    a.fb_scratch = reinterpret_cast<float*>(base + off);
-    off += align_up((size_t)FB_GRID * g.nb * sizeof(float), 256);
-    float* qbar = nullptr;
-    if (!g.causal) qbar = reinterpret_cast<float*>(base + off);
+    a.ovf_rows = reinterpret_cast<uint32_t*>(base + L.ovf_rows);
+    a.fb_scratch = reinterpret_cast<float*>(base + L.fb);
+    float* qbar = g.causal ? nullptr : reinterpret_cast<float*>(base + L.qbar);
+    uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
+    uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
+    float* pk = reinterpret_cast<float*>(base + L.pk);
+    float* plo = pk + (size_t)nbg * g.nb;
     a.q = q;
     a.qbar = qbar;
     a.kbar = kbar;
+    a.khi = khi;
+    a.klo = klo;
+    a.pk = pk;
+    a.plo = plo;
     a.idx = idx;
     a.Hq = g.Hq;
     a.Hkv = g.Hkv;
@@ -512,12 +633,17 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     a.window = g.window;
     a.P = g.causal ? g.N : g.nb;
     a.tiles = (a.P + RT_ROWS - 1) / RT_ROWS;
+    a.nb_pad = L.nb_pad;
     hipError_t e = launch_fill_u32(a.ovf_count, 1, 0u, s);
     if (e != hipSuccess) return e;
     if (!g.causal) {
         e = launch_summarize(q, qbar, g.B * g.Hq, g.N, g.bs, s);
         if (e != hipSuccess) return e;
     }
+    const int64_t prep_threads = (int64_t)nbg * L.nb_pad * 8;
+    hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
+                       kbar, khi, klo, pk, plo, nbg, g.nb, L.nb_pad);
+    hipLaunchKernelGGL(k_prefix_max, dim3((unsigned)(2 * nbg)), dim3(1024), 0, s, pk, g.nb);
     const dim3 grid((unsigned)((int64_t)g.B * g.Hq * a.tiles));
     if (g.causal) {
         hipLaunchKernelGGL(k_route<true>, grid, dim3(256), 0, s, a);
