@@ -4,13 +4,15 @@
 //
 // Causal mode runs key-block-major, because every query routes to its own
 // blocks and a query-major gather would reuse nothing:
+//   0. k_transpose_v    V -> V^T in 64-key tiles, so every kernel stages V^T
+//                       with plain 16-byte copies.
 //   1. k_bucket<false>  counts, per (b, KV head, key block), the (row, slot)
 //                       pairs that selected it (LDS histogram per workgroup).
 //   2. k_bucket_scan    bucket offsets and the work units (64 rows each).
 //   3. k_bucket<true>   scatters pair ids into bucket order.
 //   4. k_block_partial  one K/V block in LDS against up to 64 gathered query
 //                       rows: S = Q K^T and O = P V on bf16 MFMA; writes the
-//                       normalised partial output (bf16) and its log-sum-exp.
+//                       normalised partial output (bf16) and its log2 mass.
 //   5. k_window_merge   flash-style online softmax over the block-aligned
 //                       window [bs*E(t), t] with a causal mask, then merges
 //                       the row's routed partials with the append law of the
@@ -24,8 +26,11 @@
 // row l%16 and keys 16i + 4(l/16) + r.  Those probabilities are exactly the
 // B operand of O^T = V^T . P^T when key slot j of lane l stands for key
 // 32s + 4(l/16) + j (j < 4) or 32s + 16 + 4(l/16) + (j-4): no cross-lane
-// movement.  V is staged transposed in LDS (4x4 register transposes).
-// Softmax runs in the log2 domain: logits are scaled by scale*log2(e).
+// movement.  Softmax runs in the log2 domain: exp2(s * scale*log2(e) - m)
+// is one FMA and one exp per logit.
+//
+// Pair ids: pair (row, slot) is row * SP + slot with SP the power of two
+// >= top_k, so the row is a shift away.
 #include <math.h>
 
 #include <algorithm>
@@ -35,48 +40,71 @@
 
 namespace lsa {
 
-constexpr int UNIT_ROWS = 64;   // gathered rows per work unit of the block-major kernel
+constexpr int UNIT_ROWS = 64;      // gathered rows per work unit of the block-major kernel
 constexpr int BK_LDS_MAX = 16384;  // largest nb histogrammed in LDS
-constexpr int KPITCH = 72;      // LDS pitch of K tiles [key][64 d] (bf16)
+constexpr int KPITCH = 72;         // LDS pitch of K tiles [key][64 d] (bf16), 16-byte rows
+constexpr int VT_TILE = 64;        // keys per V^T tile
+constexpr int WVP = VT_TILE + 4;   // LDS pitch of 64-key V^T tiles: 2 mod 4 words
+constexpr float RESCALE_SLACK = 8.f;  // log2 headroom before a running max is raised
 
-// ------------------------------------------------------------ shared pieces
-// Stages K rows [0, nkeys) of a tile into s_k[key][KPITCH] (16-byte chunks);
-// rows >= valid are zero.
-__device__ __forceinline__ void stage_k(__bf16* s_k, const uint16_t* src, int nkeys, int valid,
-                                        int tid, int nthreads) {
-    for (int ch = tid; ch < nkeys * 8; ch += nthreads) {
-        const int key = ch >> 3, d0 = (ch & 7) * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (key < valid) v = *reinterpret_cast<const u32x4*>(src + (int64_t)key * kD + d0);
-        *reinterpret_cast<u32x4*>(s_k + key * KPITCH + d0) = v;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ V transpose
+// V [BG][N][64] -> V^T tiles [BG][ceil(N/64)][64 d][64 keys]; keys >= N are zero.
+__global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict__ v,
+                                                     uint16_t* __restrict__ vt, int N, int ntiles) {
+    __shared__ uint32_t s[VT_TILE][33];  // [key][d pair], odd pitch
+    const int tid = threadIdx.x;
+    const int bg = blockIdx.x / ntiles, tile = blockIdx.x - bg * ntiles;
+    const int key0 = tile * VT_TILE;
+    const int nvalid = min(VT_TILE, N - key0);
+    const uint16_t* src = v + ((int64_t)bg * N + key0) * kD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ch = tid + 256 * i, key = ch >> 3, d0 = (ch & 7) * 8;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (key < nvalid) x = *reinterpret_cast<const u32x4*>(src + (int64_t)key * kD + d0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[key][d0 / 2 + j] = x[j];
+    }
+    __syncthreads();
+    uint16_t* dst = vt + ((int64_t)bg * ntiles + tile) * (kD * VT_TILE);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ch = tid + 256 * i, d = ch >> 3, k0 = (ch & 7) * 8;
+        const int sh = 16 * (d & 1);
+        u32x4 y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = (s[k0 + 2 * j][d >> 1] >> sh) & 0xFFFFu;
+            const uint32_t hi = (s[k0 + 2 * j + 1][d >> 1] >> sh) & 0xFFFFu;
+            y[j] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(dst + d * VT_TILE + k0) = y;
     }
 }
 
-// Stages V rows [0, nkeys) transposed into s_vt[d][vpitch] with 4x4
-// register transposes; rows >= valid are zero.
-__device__ __forceinline__ void stage_vt(__bf16* s_vt, int vpitch, const uint16_t* src,
-                                         int nkeys, int valid, int tid, int nthreads) {
-    const int kgroups = nkeys >> 2;
-    for (int t = tid; t < kgroups * 16; t += nthreads) {
-        const int kg = t % kgroups, dg = t / kgroups;
-        uint32_t lo[4], hi[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = kg * 4 + i;
-            u32x2 v = {0u, 0u};
-            if (key < valid) v = *reinterpret_cast<const u32x2*>(src + (int64_t)key * kD + dg * 4);
-            lo[i] = v[0];  // d = 4dg, 4dg+1
-            hi[i] = v[1];  // d = 4dg+2, 4dg+3
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t* w = (j < 2) ? lo : hi;
-            const int sh = (j & 1) * 16;
-            const uint32_t e0 = (w[0] >> sh) & 0xFFFFu, e1 = (w[1] >> sh) & 0xFFFFu;
-            const uint32_t e2 = (w[2] >> sh) & 0xFFFFu, e3 = (w[3] >> sh) & 0xFFFFu;
-            u32x2 packed = {e0 | (e1 << 16), e2 | (e3 << 16)};
-            *reinterpret_cast<u32x2*>(s_vt + (dg * 4 + j) * vpitch + kg * 4) = packed;
-        }
+// ------------------------------------------------------------ shared pieces
+// 16 bytes into an LDS row that is only 8-byte aligned (V^T pitches).
+__device__ __forceinline__ void lds_store_2x8(__bf16* dst, u32x4 v) {
+    reinterpret_cast<u32x2*>(dst)[0] = u32x2{v[0], v[1]};
+    reinterpret_cast<u32x2*>(dst)[1] = u32x2{v[2], v[3]};
+}
+
+// Copies 64 rows of 64 bf16 (128 B each) from a source with the given row
+// stride into LDS rows of the given pitch; rows >= valid are zero.  K tiles
+// (16-byte rows) use 16-byte LDS stores, V^T tiles 8-byte ones.
+template <bool ROW16>
+__device__ __forceinline__ void stage_rows(__bf16* dst, int pitch, const uint16_t* src,
+                                           int64_t stride, int rows, int valid, int tid) {
+    for (int ch = tid; ch < rows * 8; ch += 256) {
+        const int r = ch >> 3, c0 = (ch & 7) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < valid) v = *reinterpret_cast<const u32x4*>(src + (int64_t)r * stride + c0);
+        if (ROW16)
+            *reinterpret_cast<u32x4*>(dst + r * pitch + c0) = v;
+        else
+            lds_store_2x8(dst + r * pitch + c0, v);
     }
 }
 
@@ -92,23 +120,23 @@ __device__ __forceinline__ void load_q_operand(const uint16_t* qrow, int lane, b
     }
 }
 
-// S^T tile for keys [16i, 16i+16) of an LDS K tile.
+// Raw scores S^T for keys [16i, 16i+16) of an LDS K tile.
 __device__ __forceinline__ f32x4 score_tile(const __bf16* s_k, int i, int lane,
                                             const bf16x8 (&Bq)[2]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 A =
-            *reinterpret_cast<const bf16x8*>(s_k + (16 * i + (lane & 15)) * KPITCH + 8 * (lane >> 4) + 32 * ks);
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(s_k + (16 * i + (lane & 15)) * KPITCH +
+                                                          8 * (lane >> 4) + 32 * ks);
         acc = mfma16(A, Bq[ks], acc);
     }
     return acc;
 }
 
-// O^T += V^T P^T over KT 16-key tiles whose probabilities are p[i][r]
-// (key 16i + 4(l/16) + r); V^T tile in LDS with pitch vpitch.
+// O^T += V^T P^T over KT 16-key tiles whose probabilities are p[i][r] (key
+// 16i + 4(l/16) + r); V^T in LDS with pitch vpitch, keys from column koff.
 template <int KT>
-__device__ __forceinline__ void pv_accumulate(const __bf16* s_vt, int vpitch, int lane,
+__device__ __forceinline__ void pv_accumulate(const __bf16* s_vt, int vpitch, int koff, int lane,
                                               const float (&p)[KT][4], f32x4 (&o)[4]) {
     constexpr int KS = (KT + 1) / 2;
 #pragma unroll
@@ -121,7 +149,8 @@ __device__ __forceinline__ void pv_accumulate(const __bf16* s_vt, int vpitch, in
         }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const __bf16* vr = s_vt + (16 * mt + (lane & 15)) * vpitch + 32 * s + 4 * (lane >> 4);
+            const __bf16* vr =
+                s_vt + (16 * mt + (lane & 15)) * vpitch + koff + 32 * s + 4 * (lane >> 4);
             const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr);
             u32x2 a1 = {0u, 0u};
             if (2 * s + 1 < KT) a1 = *reinterpret_cast<const u32x2*>(vr + 16);
@@ -129,12 +158,6 @@ __device__ __forceinline__ void pv_accumulate(const __bf16* s_vt, int vpitch, in
             o[mt] = mfma16(__builtin_bit_cast(bf16x8, araw), Bp, o[mt]);
         }
     }
-}
-
-// Slot of the n-th set bit of a mask (n < popcount(mask)).
-__device__ __forceinline__ int nth_slot(uint32_t mask, int n) {
-    for (int i = 0; i < n; ++i) mask &= mask - 1;
-    return __builtin_ctz(mask);
 }
 
 // Row reductions across the 4 lanes that share row l%16.
@@ -147,24 +170,30 @@ __device__ __forceinline__ float row_sum4(float v) {
     return v + __shfl_xor(v, 32, kWave);
 }
 
-// ------------------------------------------------------------ bucketing
-struct BucketArgs {
-    const int32_t* idx;  // [B,Hq,N,top_k]
-    uint32_t* counts;    // [NB]
-    uint32_t* cursor;    // [NB]
-    uint32_t* pairs;     // [total pairs]
-    int Hq, Hkv, N, bs, nb, top_k, window, tchunk;
-};
+// Slot of the n-th set bit of a mask (n < popcount(mask)).
+__device__ __forceinline__ int nth_slot(uint32_t mask, int n) {
+    for (int i = 0; i < n; ++i) mask &= mask - 1;
+    return __builtin_ctz(mask);
+}
 
-// Used-slot mask of one idx row, read with 16-byte loads when possible.
+// c[i] for a runtime i < kMaxTopK without dynamic register indexing.
+__device__ __forceinline__ int pick(const int (&c)[kMaxTopK], int i) {
+    int v = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) v = (s == i) ? c[s] : v;
+    return v;
+}
+
+// Used-slot mask of one idx row: an entry counts when it is a candidate
+// (< ncand) and larger than the previously used entry.  Read with 16-byte
+// loads when the row length allows.
 __device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int ncand,
                                              int (&c)[kMaxTopK]) {
     if ((top_k & 3) == 0) {
 #pragma unroll
         for (int s4 = 0; s4 < kMaxTopK / 4; ++s4) {
             if (4 * s4 < top_k) {
-                const int32_t __attribute__((ext_vector_type(4))) v =
-                    *reinterpret_cast<const int32_t __attribute__((ext_vector_type(4)))*>(ir + 4 * s4);
+                const i32x4 v = *reinterpret_cast<const i32x4*>(ir + 4 * s4);
                 c[4 * s4] = v[0]; c[4 * s4 + 1] = v[1]; c[4 * s4 + 2] = v[2]; c[4 * s4 + 3] = v[3];
             }
         }
@@ -185,13 +214,14 @@ __device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int n
     return mask;
 }
 
-// c[i] for a runtime i < kMaxTopK without dynamic register indexing.
-__device__ __forceinline__ int pick(const int (&c)[kMaxTopK], int i) {
-    int v = 0;
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) v = (s == i) ? c[s] : v;
-    return v;
-}
+// ------------------------------------------------------------ bucketing
+struct BucketArgs {
+    const int32_t* idx;  // [B,Hq,N,top_k]
+    uint32_t* counts;    // [NB]
+    uint32_t* cursor;    // [NB]
+    uint32_t* pairs;     // [total pairs]
+    int Hq, Hkv, N, bs, nb, top_k, window, tchunk, sp_log2;
+};
 
 // Workgroup = (batch, KV head, chunk of tchunk positions) over all query
 // heads of the group.  Histogram in LDS (when nb fits), then one global
@@ -227,7 +257,7 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
                 atomicAdd(&a.counts[bucket0 + c[s]], 1u);
             } else {
                 const uint32_t pos = atomicAdd(&a.cursor[bucket0 + c[s]], 1u);
-                a.pairs[pos] = (uint32_t)(row * a.top_k + s);
+                a.pairs[pos] = (uint32_t)((row << a.sp_log2) | s);
             }
         }
     }
@@ -252,7 +282,7 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
         for (int s = 0; s < kMaxTopK; ++s) {
             if (!((m >> s) & 1u)) continue;
             const uint32_t pos = atomicAdd(&s_h[c[s]], 1u);
-            a.pairs[pos] = (uint32_t)(row * a.top_k + s);
+            a.pairs[pos] = (uint32_t)((row << a.sp_log2) | s);
         }
     }
 }
@@ -301,20 +331,18 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __restrict
 struct PartArgs {
     const uint16_t* q;
     const uint16_t* k;
-    const uint16_t* v;
+    const uint16_t* vt;        // V^T tiles [BG][ntiles][64 d][64 keys]
     const uint32_t* pairs;
     const uint32_t* offsets;   // [NB+1]
     const uint32_t* unit_off;  // [NB+1]
-    uint16_t* part_o;          // bf16 bits [pairs][64]
-    float* part_lse;           // [pairs], log2 domain
-    int N, nb, top_k, NB;
+    uint16_t* part_o;          // bf16 bits [rows * SP][64], permuted (see k_block_partial)
+    float* part_lse;           // [rows * SP], log2 domain
+    int N, nb, NB, ntiles, sp_log2;
     float scale_log2;
 };
 
 // Work units (64 gathered rows of one bucket) are split into contiguous
 // ranges per workgroup, so K/V of a bucket are staged once for all its units.
-// Per wave, pair ids run two units ahead and Q rows one unit ahead of the
-// compute, hiding the dependent gather latency.
 struct UnitCursor {
     int bucket;
     __device__ void seek(const uint32_t* unit_off, int NB, uint32_t u) {
@@ -334,10 +362,15 @@ struct UnitCursor {
     }
 };
 
+// Per wave, pair ids run two units ahead and Q rows one unit ahead of the
+// compute, hiding the dependent gather latency.  Partial rows are stored
+// permuted: slot 16j + 4mt + r holds dim 16mt + 4j + r, so lane group j
+// writes (and the merge reads) 32 contiguous bytes.
 template <int BS>
 __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     constexpr int KT = BS / 16;
-    constexpr int VP = BS + 4;  // 2 mod 4 words: conflict-free 8-byte V^T reads
+    constexpr int VC = BS > VT_TILE ? BS : VT_TILE;  // staged V^T columns
+    constexpr int VP = VC + 4;                       // 2 mod 4 words: conflict-free 8-byte reads
     __shared__ __attribute__((aligned(16))) __bf16 s_k[BS * KPITCH];
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[kD * VP];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -365,9 +398,9 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
         pid_nxt = v_nxt ? a.pairs[q0 + my] : 0u;
     }
     bf16x8 Bq[2];
-    load_q_operand(a.q + (int64_t)(pid_cur / (uint32_t)a.top_k) * kD, lane, v_cur, Bq);
+    load_q_operand(a.q + (int64_t)(pid_cur >> a.sp_log2) * kD, lane, v_cur, Bq);
 
-    int loaded = -1;
+    int loaded = -1, koff = 0;
     for (uint32_t u = u0; u < u1; ++u) {
         uint32_t p0, p1;
         cur.rows(a.unit_off, a.offsets, u, p0, p1);
@@ -380,46 +413,49 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
             pid_n2 = v_n2 ? a.pairs[q0 + my] : 0u;
         }
         bf16x8 Bq_nxt[2];
-        load_q_operand(a.q + (int64_t)(pid_nxt / (uint32_t)a.top_k) * kD, lane, v_nxt, Bq_nxt);
+        load_q_operand(a.q + (int64_t)(pid_nxt >> a.sp_log2) * kD, lane, v_nxt, Bq_nxt);
 
         if (cur.bucket != loaded) {
             __syncthreads();
             const int bg = cur.bucket / a.nb, c = cur.bucket - bg * a.nb;
-            const int64_t kv0 = ((int64_t)bg * a.N + (int64_t)c * BS) * kD;
-            stage_k(s_k, a.k + kv0, BS, BS, tid, 256);
-            stage_vt(s_vt, VP, a.v + kv0, BS, BS, tid, 256);
+            const int key0 = c * BS;
+            stage_rows<true>(s_k, KPITCH, a.k + ((int64_t)bg * a.N + key0) * kD, kD, BS, BS, tid);
+            // V^T columns [VC * (key0 / VC), +VC) from the 64-key tiles
+            const int tile0 = (key0 / VC) * (VC / VT_TILE);
+#pragma unroll
+            for (int tt = 0; tt < VC / VT_TILE; ++tt)
+                stage_rows<false>(s_vt + tt * VT_TILE, VP,
+                                  a.vt + ((int64_t)bg * a.ntiles + tile0 + tt) * (kD * VT_TILE),
+                                  VT_TILE, kD, kD, tid);
+            koff = key0 % VC;
             __syncthreads();
             loaded = cur.bucket;
         }
         if (p0 + 16 * w < p1) {  // wave has rows in this unit
-            float x[KT][4];
+            f32x4 sc[KT];
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < KT; ++i) {
-                const f32x4 sc = score_tile(s_k, i, lane, Bq);
+                sc[i] = score_tile(s_k, i, lane, Bq);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    x[i][r] = sc[r] * a.scale_log2;
-                    mx = fmaxf(mx, x[i][r]);
-                }
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[i][r]);
             }
-            mx = row_max4(mx);
+            const float m2 = row_max4(mx) * a.scale_log2;
+            float p[KT][4];
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < KT; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    x[i][r] = exp2f(x[i][r] - mx);
-                    sum += x[i][r];
+                    p[i][r] = exp2f(fmaf(sc[i][r], a.scale_log2, -m2));
+                    sum += p[i][r];
                 }
             sum = row_sum4(sum);
             f32x4 o[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            pv_accumulate<KT>(s_vt, VP, lane, x, o);
+            pv_accumulate<KT>(s_vt, VP, koff, lane, p, o);
             if (v_cur) {
-                // partial row layout: slot 16j + 4mt + r holds dim 16mt + 4j + r,
-                // so lane group j writes 32 contiguous bytes
                 const float inv = 1.f / sum;
                 uint16_t* dst = a.part_o + (int64_t)pid_cur * kD + 16 * (lane >> 4);
 #pragma unroll
@@ -432,7 +468,7 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
                     }
                     *reinterpret_cast<bf16x8*>(dst + 8 * h2) = ob;
                 }
-                if (lane < 16) a.part_lse[pid_cur] = mx + log2f(sum);
+                if (lane < 16) a.part_lse[pid_cur] = m2 + log2f(sum);
             }
         }
         v_cur = v_nxt;
@@ -448,37 +484,49 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
 struct WinArgs {
     const uint16_t* q;
     const uint16_t* k;
-    const uint16_t* v;
+    const uint16_t* vt;
     const int32_t* idx;
     const uint16_t* part_o;
     const float* part_lse;
     float* out;
-    int Hq, Hkv, N, bs, top_k, window, tiles, unused;
+    int Hq, Hkv, N, bs, top_k, window, tiles, items, ntiles, sp_log2;
     float scale_log2;
 };
 
-constexpr int WVP = 64 + 4;  // V^T pitch of 64-key tiles (2 mod 4 words)
-
 // One workgroup per (query head, 64 positions); wave w owns rows
 // t0 + 16w .. +15 (lane l holds row l%16).  The window keys stream through
-// double-buffered LDS tiles (the next tile is fetched into registers while
-// the current one is used); the seven heads of a KV group hit the same
-// tiles in L2.  Masks are applied only on chunks that cross a row's window
+// double-buffered 64-key LDS tiles (64-aligned, so a V^T tile is one plain
+// copy); the next tile is fetched into registers while the current one is
+// used.  A row's running max is raised only when a chunk exceeds it by
+// RESCALE_SLACK (log2 units), so most chunks skip rescaling the
+// accumulator; masks are applied only on chunks that cross a row's window
 // start or its causal end.
 __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_k[2][64 * KPITCH];
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][kD * WVP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tile = blockIdx.x % a.tiles;
-    const int bh = blockIdx.x / a.tiles;
-    const int h = bh % a.Hq, b = bh / a.Hq;
-    const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+    // item = xcd * (grid / 8) + (blockIdx / 8) keeps consecutive items on one
+    // XCD; items run head-fastest, so the query heads of a KV group that read
+    // the same window tile share that XCD's L2.
+    const int per_xcd = gridDim.x / 8;
+    const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int rep = a.Hq / a.Hkv;
+    if (item >= a.items) return;
+    const int hh = item % rep;
+    const int tile = (item / rep) % a.tiles;
+    const int bg = item / (rep * a.tiles);
+    const int b = bg / a.Hkv;
+    const int h = (bg - b * a.Hkv) * rep + hh;
+    const int bh = b * a.Hq + h;
     const int t0 = tile * 64;
     const int key_lo = a.bs * eligible_blocks(t0, a.bs, a.window);
     const int key_hi = min(t0 + 63, a.N - 1);
     const int lo_max = a.bs * eligible_blocks(key_hi, a.bs, a.window);  // largest row start
-    const int64_t kv0 = (int64_t)bg * a.N * kD;
+    const int kc0 = key_lo / VT_TILE * VT_TILE;
+    const int64_t k0 = (int64_t)bg * a.N * kD;
+    const int64_t vt0 = (int64_t)bg * a.ntiles * (kD * VT_TILE);
     const int t = t0 + 16 * w + (lane & 15);
     const bool valid = t < a.N;
     const int E = valid ? eligible_blocks(t, a.bs, a.window) : 0;
@@ -495,99 +543,86 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // staging: K tile = 512 chunks of 16 B (2 per thread), V tile = 256 4x4
-    // sub-tiles (1 per thread)
-    u32x4 kp[2];
-    u32x2 vp[4];
-    const int kg = tid & 15, dg = tid >> 4;
+    // staging: a K tile and a V^T tile, 512 chunks of 16 B each
+    u32x4 kp[2], vp[2];
     auto fetch = [&](int kc) {
         const int nvalid = min(64, a.N - kc);
-        const uint16_t* ks = a.k + kv0 + (int64_t)kc * kD;
-        const uint16_t* vs = a.v + kv0 + (int64_t)kc * kD;
+        const uint16_t* ks = a.k + k0 + (int64_t)kc * kD;
+        const uint16_t* vs = a.vt + vt0 + (int64_t)(kc / VT_TILE) * (kD * VT_TILE);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int ch = tid + 256 * i, key = ch >> 3;
-            kp[i] = key < nvalid
-                        ? *reinterpret_cast<const u32x4*>(ks + (int64_t)key * kD + (ch & 7) * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = kg * 4 + r;
-            vp[r] = key < nvalid ? *reinterpret_cast<const u32x2*>(vs + (int64_t)key * kD + dg * 4)
-                                 : u32x2{0u, 0u};
+            const int ch = tid + 256 * i, r = ch >> 3, c0 = (ch & 7) * 8;
+            kp[i] = r < nvalid ? *reinterpret_cast<const u32x4*>(ks + (int64_t)r * kD + c0)
+                               : u32x4{0u, 0u, 0u, 0u};
+            vp[i] = *reinterpret_cast<const u32x4*>(vs + r * VT_TILE + c0);
         }
     };
     auto commit = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int ch = tid + 256 * i;
-            *reinterpret_cast<u32x4*>(s_k[buf] + (ch >> 3) * KPITCH + (ch & 7) * 8) = kp[i];
-        }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int sh = (jj & 1) * 16, wi = jj >> 1;
-            const uint32_t e0 = (vp[0][wi] >> sh) & 0xFFFFu, e1 = (vp[1][wi] >> sh) & 0xFFFFu;
-            const uint32_t e2 = (vp[2][wi] >> sh) & 0xFFFFu, e3 = (vp[3][wi] >> sh) & 0xFFFFu;
-            *reinterpret_cast<u32x2*>(s_vt[buf] + (dg * 4 + jj) * WVP + kg * 4) =
-                u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+            const int ch = tid + 256 * i, r = ch >> 3, c0 = (ch & 7) * 8;
+            *reinterpret_cast<u32x4*>(s_k[buf] + r * KPITCH + c0) = kp[i];
+            lds_store_2x8(s_vt[buf] + r * WVP + c0, vp[i]);
         }
     };
 
-    fetch(key_lo);
+    fetch(kc0);
     commit(0);
     __syncthreads();
-    for (int kc = key_lo, it = 0; kc <= key_hi; kc += 64, ++it) {
+    for (int kc = kc0, it = 0; kc <= key_hi; kc += 64, ++it) {
         const int buf = it & 1;
         const bool more = kc + 64 <= key_hi;
         if (more) fetch(kc + 64);
         const bool edge = kc < lo_max || kc + 63 > t0;
-        float x[4][4];
+        f32x4 sc[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 sc = score_tile(s_k[buf], i, lane, Bq);
+            sc[i] = score_tile(s_k[buf], i, lane, Bq);
+            if (edge) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float xv = sc[r] * a.scale_log2;
-                if (edge) {
+                for (int r = 0; r < 4; ++r) {
                     const int jk = kc + 16 * i + 4 * (lane >> 4) + r;
-                    xv = (jk >= lo_t && jk <= t) ? xv : -INFINITY;
+                    sc[i][r] = (jk >= lo_t && jk <= t) ? sc[i][r] : -INFINITY;
                 }
-                x[i][r] = xv;
-                mx = fmaxf(mx, xv);
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[i][r]);
         }
-        mx = row_max4(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float mc = row_max4(mx) * a.scale_log2;
+        const bool raise = mc > m_run + RESCALE_SLACK;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float m_new = raise ? mc : m_run;
+            const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
+            m_run = m_new;
+        }
+        const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+        float p[4][4];
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                x[i][r] = exp2f(x[i][r] - m_use);
-                sum += x[i][r];
+                p[i][r] = exp2f(fmaf(sc[i][r], a.scale_log2, -mu));
+                sum += p[i][r];
             }
-        sum = row_sum4(sum);
-        l_run = l_run * alpha + sum;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
-        m_run = m_new;
-        pv_accumulate<4>(s_vt[buf], WVP, lane, x, o);
+        l_run += row_sum4(sum);
+        pv_accumulate<4>(s_vt[buf], WVP, 0, lane, p, o);
         if (more) commit(buf ^ 1);
         __syncthreads();
     }
     if (!valid) return;
 
     // merge the routed partials (normalised outputs with their log2 mass),
-    // eight slots at a time so their loads are in flight together.  A
-    // partial row stores dim 16mt + 4j + r at slot 16j + 4mt + r, so lane
-    // group j reads its 16 values as 32 contiguous bytes.
+    // eight slots at a time so their loads are in flight together; a
+    // partial row stores dim 16mt + 4j + r at slot 16j + 4mt + r
+    const int64_t prow = row << a.sp_log2;
     float lse_all[kMaxTopK];
     {
-        const float* lp = a.part_lse + row * a.top_k;
+        const float* lp = a.part_lse + prow;
         if ((a.top_k & 3) == 0) {
 #pragma unroll
             for (int s4 = 0; s4 < kMaxTopK / 4; ++s4) {
@@ -611,7 +646,7 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
         for (int i = 0; i < 8; ++i) {
             const int sl = s0 + i;
             const bool u = sl < a.top_k && ((used >> sl) & 1u);
-            const uint16_t* src = a.part_o + (row * a.top_k + sl) * kD + 16 * (lane >> 4);
+            const uint16_t* src = a.part_o + (prow + sl) * kD + 16 * (lane >> 4);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
                 po[i][h2] = u ? *reinterpret_cast<const u32x4*>(src + 8 * h2) : u32x4{0u, 0u, 0u, 0u};
@@ -646,29 +681,31 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
 struct ImgArgs {
     const uint16_t* q;
     const uint16_t* k;
-    const uint16_t* v;
+    const uint16_t* vt;
     const int32_t* idx;  // [B,Hq,nb,top_k]
     float* out;
-    int Hq, Hkv, N, nb, top_k;
+    int Hq, Hkv, N, nb, top_k, ntiles;
     int64_t n_qblocks;   // B*Hq*nb
     float scale_log2;
 };
 
 // One wave per 16-token query block (block size 16).  The selected blocks
 // are processed four at a time (64 keys) with an online softmax; K feeds the
-// MFMA straight from global memory, V is transposed through the wave's own
-// LDS region.
+// MFMA straight from global memory, the blocks' V^T columns are copied into
+// the wave's own LDS region.
 __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
-    constexpr int VP = WVP;
-    __shared__ __attribute__((aligned(16))) __bf16 s_vt[4][kD * VP];
+    __shared__ __attribute__((aligned(16))) __bf16 s_vt[4][kD * WVP];
     __shared__ int s_n[4];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t qb = (int64_t)blockIdx.x * 4 + w;
     const bool active = qb < a.n_qblocks;
     const int64_t bh = active ? qb / a.nb : 0;
     const int i = active ? (int)(qb - bh * a.nb) : 0;
     const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq), g = h / (a.Hq / a.Hkv);
-    const int64_t kv0 = ((int64_t)b * a.Hkv + g) * a.N * kD;
+    const int64_t bg = (int64_t)b * a.Hkv + g;
+    const int64_t k0 = bg * a.N * kD;
+    const int64_t vt0 = bg * a.ntiles * (kD * VT_TILE);
     const int t = 16 * i + (lane & 15);
     const int64_t row = bh * a.N + t;
 
@@ -691,33 +728,23 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 
     for (int c0 = 0; c0 < nmax; c0 += 4) {
         __syncthreads();
-        // stage V^T of up to four blocks (16 keys each) into this wave's region
+        // V^T columns of up to four 16-key blocks: lane d copies row d of
+        // each block (two 16-byte pieces)
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const bool have = c0 + jb < nused;
             const int cblk = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
-            const uint16_t* src = a.v + kv0 + (int64_t)cblk * 16 * kD;
-            // 16 keys x 64 dims = 64 4x4 tiles: one per lane
-            const int kg = lane & 3, dg = lane >> 2;
-            uint32_t lo4[4], hi4[4];
+            const uint16_t* src = a.vt + vt0 + (int64_t)(cblk >> 2) * (kD * VT_TILE) +
+                                  lane * VT_TILE + (cblk & 3) * 16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u32x2 vv = {0u, 0u};
-                if (have) vv = *reinterpret_cast<const u32x2*>(src + (int64_t)(kg * 4 + r) * kD + dg * 4);
-                lo4[r] = vv[0];
-                hi4[r] = vv[1];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t* wv = (j < 2) ? lo4 : hi4;
-                const int sh = (j & 1) * 16;
-                u32x2 packed = {((wv[0] >> sh) & 0xFFFFu) | (((wv[1] >> sh) & 0xFFFFu) << 16),
-                                ((wv[2] >> sh) & 0xFFFFu) | (((wv[3] >> sh) & 0xFFFFu) << 16)};
-                *reinterpret_cast<u32x2*>(vt + (dg * 4 + j) * VP + jb * 16 + kg * 4) = packed;
+            for (int part = 0; part < 2; ++part) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (have) v = *reinterpret_cast<const u32x4*>(src + 8 * part);
+                lds_store_2x8(vt + lane * WVP + jb * 16 + 8 * part, v);
             }
         }
         __syncthreads();
-        float x[4][4];
+        f32x4 sc[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
@@ -725,34 +752,35 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
             const int cblk = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (have) {
-                const uint16_t* kr = a.k + kv0 + ((int64_t)cblk * 16 + (lane & 15)) * kD + 8 * (lane >> 4);
+                const uint16_t* kr =
+                    a.k + k0 + ((int64_t)cblk * 16 + (lane & 15)) * kD + 8 * (lane >> 4);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) acc = mfma16(load_bf16x8(kr + 32 * ks), Bq[ks], acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                x[jb][r] = have ? acc[r] * a.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[jb][r]);
+                sc[jb][r] = have ? acc[r] : -INFINITY;
+                mx = fmaxf(mx, sc[jb][r]);
             }
         }
-        mx = row_max4(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float mc = row_max4(mx) * a.scale_log2;
+        const float m_new = fmaxf(m_run, mc);
+        const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mu);
+        float p[4][4];
         float sum = 0.f;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                x[jb][r] = exp2f(x[jb][r] - m_use);
-                sum += x[jb][r];
+                p[jb][r] = exp2f(fmaf(sc[jb][r], a.scale_log2, -mu));
+                sum += p[jb][r];
             }
-        sum = row_sum4(sum);
-        l_run = l_run * alpha + sum;
+        l_run = l_run * alpha + row_sum4(sum);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
         m_run = m_new;
-        pv_accumulate<4>(vt, VP, lane, x, o);
+        pv_accumulate<4>(vt, WVP, 0, lane, p, o);
     }
     if (!active) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -762,23 +790,35 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 }
 
 // ------------------------------------------------------------ host side
+int pair_stride_log2(int top_k) {
+    int l = 0;
+    while ((1 << l) < top_k) ++l;
+    return l;
+}
+
 struct AttendLayout {
-    size_t counts, offsets, cursor, unit_off, pairs, part_o, part_lse, total;
+    size_t vt, counts, offsets, cursor, unit_off, pairs, part_o, part_lse, total;
 };
 
 static AttendLayout attend_layout(const Geometry& g) {
     AttendLayout L{};
-    if (!g.causal) return L;
-    const size_t NB = (size_t)g.B * g.Hkv * g.nb;
-    const size_t npairs = (size_t)g.B * g.Hq * g.N * g.top_k;
+    const size_t nbg = (size_t)g.B * g.Hkv;
+    const size_t ntiles = ((size_t)g.N + VT_TILE - 1) / VT_TILE;
     size_t off = 0;
-    L.counts = off;   off += align_up(NB * 4, 256);
-    L.offsets = off;  off += align_up((NB + 1) * 4, 256);
-    L.cursor = off;   off += align_up(NB * 4, 256);
-    L.unit_off = off; off += align_up((NB + 1) * 4, 256);
-    L.pairs = off;    off += align_up(npairs * 4, 256);
-    L.part_o = off;   off += align_up(npairs * kD * 2, 256);
-    L.part_lse = off; off += align_up(npairs * 4, 256);
+    L.vt = off;       off += align_up(nbg * ntiles * kD * VT_TILE * 2, 256);
+    if (g.causal) {
+        const size_t NB = nbg * g.nb;
+        const size_t rows = (size_t)g.B * g.Hq * g.N;
+        const size_t npairs = rows * g.top_k;
+        const size_t nslots = rows << pair_stride_log2(g.top_k);
+        L.counts = off;   off += align_up(NB * 4, 256);
+        L.offsets = off;  off += align_up((NB + 1) * 4, 256);
+        L.cursor = off;   off += align_up(NB * 4, 256);
+        L.unit_off = off; off += align_up((NB + 1) * 4, 256);
+        L.pairs = off;    off += align_up(npairs * 4, 256);
+        L.part_o = off;   off += align_up(nslots * kD * 2, 256);
+        L.part_lse = off; off += align_up(nslots * 4, 256);
+    }
     L.total = off;
     return L;
 }
@@ -803,8 +843,15 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
                          const uint16_t* v, const int32_t* idx, float* out, void* ws,
                          hipStream_t s, const hipEvent_t* ev) {
     const float scale_log2 = g.scale * kLog2e;
+    const AttendLayout L = attend_layout(g);
+    char* base = static_cast<char*>(ws);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(base + L.vt);
+    const int ntiles = (g.N + VT_TILE - 1) / VT_TILE;
+    const int nbg = g.B * g.Hkv;
+    hipLaunchKernelGGL(k_transpose_v, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s, v, vt, g.N,
+                       ntiles);
     if (!g.causal) {
-        ImgArgs a{q, k, v, idx, out, g.Hq, g.Hkv, g.N, g.nb, g.top_k,
+        ImgArgs a{q, k, vt, idx, out, g.Hq, g.Hkv, g.N, g.nb, g.top_k, ntiles,
                   (int64_t)g.B * g.Hq * g.nb, scale_log2};
         const unsigned grid = (unsigned)((a.n_qblocks + 3) / 4);
         for (int i = 4; i < 8; ++i) mark(ev, i, s);
@@ -812,8 +859,6 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
         mark(ev, 8, s);
         return hipGetLastError();
     }
-    const AttendLayout L = attend_layout(g);
-    char* base = static_cast<char*>(ws);
     uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
     uint32_t* offsets = reinterpret_cast<uint32_t*>(base + L.offsets);
     uint32_t* cursor = reinterpret_cast<uint32_t*>(base + L.cursor);
@@ -821,19 +866,22 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     uint32_t* pairs = reinterpret_cast<uint32_t*>(base + L.pairs);
     uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
     float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
-    const int NB = g.B * g.Hkv * g.nb;
+    const int NB = nbg * g.nb;
+    const int sp_log2 = pair_stride_log2(g.top_k);
 
     hipError_t e = launch_fill_u32(counts, (size_t)NB, 0u, s);
     if (e != hipSuccess) return e;
     // positions per bucketing workgroup: ~4096 rows, and enough pairs to
     // amortise the per-bucket flush
     const int rep = g.Hq / g.Hkv;
-    int64_t tc = std::max<int64_t>((4096 + rep - 1) / rep,
-                                   (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k));
+    int64_t tc = std::max<int64_t>(
+        (4096 + rep - 1) / rep,
+        (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k));
     tc = std::min<int64_t>((tc + 63) / 64 * 64, g.N);
-    BucketArgs ba{idx, counts, cursor, pairs, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window, (int)tc};
+    BucketArgs ba{idx, counts, cursor, pairs, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window,
+                  (int)tc, sp_log2};
     const int nch = (int)((g.N + tc - 1) / tc);
-    const dim3 bgrid((unsigned)(g.B * g.Hkv * nch));
+    const dim3 bgrid((unsigned)(nbg * nch));
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
     hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
     mark(ev, 4, s);
@@ -843,8 +891,8 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
     mark(ev, 6, s);
 
-    PartArgs pa{q, k, v, pairs, offsets, unit_off, part_o, part_lse, g.N, g.nb, g.top_k, NB,
-                scale_log2};
+    PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, g.N, g.nb, NB, ntiles,
+                sp_log2, scale_log2};
     switch (g.bs) {
         case 16: launch_partial<16>(pa, s); break;
         case 32: launch_partial<32>(pa, s); break;
@@ -852,10 +900,11 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
         default: launch_partial<128>(pa, s); break;
     }
     mark(ev, 7, s);
-    WinArgs wa{q, k, v, idx, part_o, part_lse, out, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
-               (g.N + 63) / 64, 1, scale_log2};
-    hipLaunchKernelGGL(k_window_merge, dim3((unsigned)((int64_t)g.B * g.Hq * wa.tiles)), dim3(256),
-                       0, s, wa);
+    const int wtiles = (g.N + 63) / 64;
+    WinArgs wa{q, k, vt, idx, part_o, part_lse, out, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
+               wtiles, g.B * g.Hq * wtiles, ntiles, sp_log2, scale_log2};
+    const int64_t wgrid = ((int64_t)wa.items + 7) / 8 * 8;  // multiple of the XCD count
+    hipLaunchKernelGGL(k_window_merge, dim3((unsigned)wgrid), dim3(256), 0, s, wa);
     mark(ev, 8, s);
     return hipGetLastError();
 }

@@ -26,6 +26,9 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
                         int32_t* idx, void* ws, hipStream_t s,
                         const hipEvent_t* ev = nullptr);
 
+// log2 of the pair-id stride: the smallest power of two >= top_k.
+int pair_stride_log2(int top_k);
+
 // Sparse attention workspace (bytes) and launch.
 size_t attend_workspace_bytes(const Geometry& g);
 hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k,

@@ -54,7 +54,8 @@ _lib.lsa_status_str.restype = ctypes.c_char_p
 
 SIZE_MAX = (1 << 64) - 1
 PROFILE_EVENTS = 9
-PROFILE_STAGES = ["key summary", "routing", "routing fallback", "bucket count", "bucket scan",
+PROFILE_STAGES = ["key summary", "routing", "routing fallback", "V transpose + bucket count",
+                  "bucket scan",
                   "bucket scatter", "routed-block partials", "window + merge"]
 
 # HIP event calls resolve through liblsa's own dependency (the process's single

@@ -61,7 +61,8 @@ typedef enum lsa_status {
     LSA_OK = 0,
     LSA_ERR_NULL = 1,        /* a required pointer is NULL */
     LSA_ERR_SHAPE = 2,       /* inconsistent sizes (N % block, Hq % Hkv, window, ...) */
-    LSA_ERR_UNSUPPORTED = 3, /* valid but outside this build (D != 64, top_k > 16, ...) */
+    LSA_ERR_UNSUPPORTED = 3, /* valid but outside this build (D != 64, top_k > 16,
+                                B*Hq*N*2^ceil(log2 top_k) >= 2^32, ...) */
     LSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned (workspace: 256) */
     LSA_ERR_WORKSPACE = 5,   /* workspace smaller than lsa_workspace_bytes() */
     LSA_ERR_DEVICE = 6       /* a HIP launch failed */
@@ -129,10 +130,10 @@ lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
 /* lsa_forward with stage timing, for profiling tools.  `events` holds
  * LSA_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is
  * recorded on `stream` at the i-th stage boundary:
- *   0 start, 1 key summary, 2 routing, 3 routing fallback, 4 bucket count,
- *   5 bucket scan, 6 bucket scatter, 7 routed-block partials, 8 window and
- *   merge (image mode: 2 includes the query summary, 4-7 are empty and 8 is
- *   the image-mode attention).
+ *   0 start, 1 key summary, 2 routing, 3 routing fallback, 4 V transpose and
+ *   bucket count, 5 bucket scan, 6 bucket scatter, 7 routed-block partials,
+ *   8 window and merge (image mode: 2 includes the query summary, 4 is the
+ *   V transpose, 5-7 are empty and 8 is the image-mode attention).
  * Elapsed time between events i-1 and i is the duration of stage i.  No
  * synchronisation happens inside; otherwise identical to lsa_forward. */
 #define LSA_PROFILE_EVENTS 9

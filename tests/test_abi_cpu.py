@@ -82,9 +82,10 @@ def test_null_alignment_and_workspace_checks(lsa):
 def test_workspace_sizes_are_plausible(lsa):
     p = good(lsa)
     pairs = 14 * 131072 * 16
+    vt = 2 * 131072 * 64 * 2                      # V^T copy of both KV heads
     att = lsa.workspace_bytes(p, lsa.OP_ATTEND)
-    assert pairs * (64 * 2 + 4 + 4) <= att < pairs * (64 * 2 + 4 + 4) + (1 << 20)
+    assert pairs * (64 * 2 + 4 + 4) + vt <= att < pairs * (64 * 2 + 4 + 4) + vt + (1 << 20)
     assert lsa.workspace_bytes(p, lsa.OP_SUMMARIZE) == 0
     img = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0)
-    assert lsa.workspace_bytes(img, lsa.OP_ATTEND) == 0
+    assert lsa.workspace_bytes(img, lsa.OP_ATTEND) == 4 * 16 * 16384 * 64 * 2
     assert lsa.workspace_bytes(img, lsa.OP_ROUTE) >= 4 * 16 * 1024 * 64 * 4
