@@ -179,33 +179,53 @@ def main():
         e.close()
     stage_mean = stages.mean(axis=0)
 
-    # algorithmic work per stage
+    # algorithmic work per stage (bytes that must cross HBM, or MFMA FLOP)
     B, Hq, Hkv, N, D, bs = w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block
     nb = N // bs
-    summary_bytes = B * Hkv * N * D * 2 + B * Hkv * nb * D * 4
-    if not w.causal:
-        summary_bytes += B * Hq * N * D * 2 + B * Hq * nb * D * 4
+    rows = B * Hq * N
+    kv_bytes = B * Hkv * N * D * 2                      # one of K, V
+    summary_bytes = kv_bytes + B * Hkv * nb * D * 4
     cand = routing_candidates(w)
-    work = {
-        0: ("hbm", summary_bytes / 1e9, "GB/s", PEAK_HBM_GBS),
-        1: ("mfma", 2 * D * cand / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-        6: ("mfma", f_routed / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-        7: ("mfma", (f_window if w.causal else f_routed) / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS),
-    }
+    idx_rows = rows if w.causal else B * Hq * nb
+    route_bytes = B * Hq * N * D * 2 + idx_rows * w.top_k * 4 + B * Hkv * nb * D * 4
+    if not w.causal:
+        route_bytes += B * Hq * nb * D * 4               # pooled queries (read back)
+    work = {0: ("hbm", summary_bytes), 1: ("mfma", 2 * D * cand)}
+    if w.causal:
+        # partials: per routed pair the gathered Q row, the bf16 partial row,
+        # its log-mass and the pair id; per bucket one K block and one V^T block
+        buckets = B * Hkv * nb
+        work[6] = ("hbm", routed_pairs * (D * 2 + D * 2 + 4 + 4) + buckets * 2 * bs * D * 2)
+        # window + merge: Q, idx, the partials read back, fp32 output, K and V once
+        work[7] = ("hbm", rows * (D * 2 + w.top_k * 4 + D * 4) + routed_pairs * (D * 2 + 4)
+                   + 2 * kv_bytes)
+    else:
+        work[7] = ("hbm", rows * D * 2 + 2 * kv_bytes + idx_rows * w.top_k * 4 + rows * D * 4)
+    stage_frac = {}
+    for i, (bound, amount) in work.items():
+        t = stage_mean[i] * 1e-3
+        if bound == "hbm":
+            ach = amount / 1e9 / t
+            stage_frac[lsa.PROFILE_STAGES[i]] = {"bound": "hbm", "achieved": ach, "unit": "GB/s",
+                                                 "frac": ach / PEAK_HBM_GBS, "bytes": amount}
+        else:
+            ach = amount / 1e12 / t
+            stage_frac[lsa.PROFILE_STAGES[i]] = {"bound": "mfma", "achieved": ach,
+                                                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                                                 "flop": amount,
+                                                 "hbm_frac": route_bytes / 1e9 / t / PEAK_HBM_GBS}
     dom = int(np.argmax(stage_mean))
-    bound, amount, unit, peak = work.get(dom, ("hbm", 0.0, "GB/s", PEAK_HBM_GBS))
-    achieved = amount / (stage_mean[dom] * 1e-3)
+    dom_name = lsa.PROFILE_STAGES[dom]
+    d = stage_frac.get(dom_name)
     traffic = None
     if TRAFFIC and TRAFFIC.get("csrc") == csrc_digest() and TRAFFIC.get("stage") == dom \
             and TRAFFIC.get("workload") == w.name:
         traffic = TRAFFIC["bytes_per_launch"]
-    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": traffic,
-                "kernel": lsa.PROFILE_STAGES[dom], "kernel_ms": float(stage_mean[dom])}
+    roofline = {"bound": d["bound"] if d else "hbm", "achieved": d["achieved"] if d else None,
+                "peak": (PEAK_HBM_GBS if (not d or d["bound"] == "hbm") else PEAK_BF16_TFLOPS),
+                "unit": d["unit"] if d else "GB/s", "frac": d["frac"] if d else None,
+                "traffic": traffic, "kernel": dom_name, "kernel_ms": float(stage_mean[dom])}
     breakdown = {lsa.PROFILE_STAGES[i]: round(float(stage_mean[i]), 4) for i in range(8)}
-    hbm_summary = summary_bytes / 1e9 / (stage_mean[0] * 1e-3)
-    route_tflops = 2 * D * cand / 1e12 / (stage_mean[1] * 1e-3)
-    route_bytes = B * Hq * N * D * 2 + B * Hq * rows * w.top_k * 4 + B * Hkv * nb * D * 4
     attend_ms = float(stage_mean[3:].sum())
 
     result = {
@@ -223,11 +243,7 @@ def main():
                   "mfma_frac": f_sel / 1e12 / (ms * 1e-3) / PEAK_BF16_TFLOPS,
                   "attend_ms": attend_ms,
                   "attend_mfma_frac": f_sel / 1e12 / (attend_ms * 1e-3) / PEAK_BF16_TFLOPS,
-                  "summary_hbm_gbs": hbm_summary, "summary_hbm_frac": hbm_summary / PEAK_HBM_GBS,
-                  "routing_tflops": route_tflops,
-                  "routing_mfma_frac": route_tflops / PEAK_BF16_TFLOPS,
-                  "routing_hbm_frac": route_bytes / 1e9 / (stage_mean[1] * 1e-3) / PEAK_HBM_GBS,
-                  "routed_pairs": routed_pairs, "stage_ms": breakdown},
+                  "routed_pairs": routed_pairs, "stage_ms": breakdown, "stage_roofline": stage_frac},
     }
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

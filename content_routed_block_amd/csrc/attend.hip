@@ -337,9 +337,18 @@ struct PartArgs {
     const uint32_t* unit_off;  // [NB+1]
     uint16_t* part_o;          // bf16 bits [rows * SP][64], permuted (see k_block_partial)
     float* part_lse;           // [rows * SP], log2 domain
+    uint32_t dummy_pid;        // rows * SP: first of 64 rows written by lanes without a pair
     int N, nb, NB, ntiles, sp_log2;
     float scale_log2;
 };
+
+// Wave-uniform read of a table that the kernel never writes, through the
+// constant address space so that it becomes a scalar load: a vector load
+// here would make the wave wait for all of its outstanding vector memory
+// operations, prefetches included.
+__device__ __forceinline__ uint32_t uniform_load(const uint32_t* p) {
+    return *(const __attribute__((address_space(4))) uint32_t*)p;
+}
 
 // Work units (64 gathered rows of one bucket) are split into contiguous
 // ranges per workgroup, so K/V of a bucket are staged once for all its units.
@@ -349,16 +358,16 @@ struct UnitCursor {
         int lo = 0, hi = NB;  // last bucket b with unit_off[b] <= u
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (unit_off[mid] <= u) lo = mid; else hi = mid;
+            if (uniform_load(unit_off + mid) <= u) lo = mid; else hi = mid;
         }
         bucket = lo;
     }
     // Rows [p0, p1) of unit u (u >= the unit of the previous call).
     __device__ void rows(const uint32_t* unit_off, const uint32_t* offsets, uint32_t u,
                          uint32_t& p0, uint32_t& p1) {
-        while (unit_off[bucket + 1] <= u) ++bucket;
-        p0 = offsets[bucket] + (u - unit_off[bucket]) * UNIT_ROWS;
-        p1 = min(p0 + UNIT_ROWS, offsets[bucket + 1]);
+        while (uniform_load(unit_off + bucket + 1) <= u) ++bucket;
+        p0 = uniform_load(offsets + bucket) + (u - uniform_load(unit_off + bucket)) * UNIT_ROWS;
+        p1 = min(p0 + UNIT_ROWS, uniform_load(offsets + bucket + 1));
     }
 };
 
@@ -375,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[kD * VP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t U = a.unit_off[a.NB];
+    const uint32_t U = uniform_load(a.unit_off + a.NB);
     const uint32_t per = (U + gridDim.x - 1) / gridDim.x;
     const uint32_t u0 = blockIdx.x * per;
     const uint32_t u1 = min(U, u0 + per);
@@ -384,36 +393,43 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     cur.seek(a.unit_off, a.NB, u0);
     ahead = cur;
     const uint32_t my = 16 * w + (lane & 15);  // this lane's row slot in a unit
+    // Every vector memory operation below is issued unconditionally (lanes
+    // without a row read pair 0 and write a dummy row), so the wait for a
+    // prefetched operand never has to drain the stores issued after it.
+    const uint32_t dummy = a.dummy_pid + my;
+    auto fetch_pid = [&](uint32_t u, uint32_t& pid, bool& v) {
+        uint32_t q0 = 0, q1 = 0;
+        if (u < u1) ahead.rows(a.unit_off, a.offsets, u, q0, q1);
+        v = q0 + my < q1;
+        pid = a.pairs[v ? q0 + my : 0u];
+    };
+    auto fetch_q = [&](uint32_t pid, bf16x8 (&B)[2]) {
+        const uint16_t* qrow = a.q + (int64_t)(pid >> a.sp_log2) * kD + 8 * (lane >> 4);
+        B[0] = load_bf16x8(qrow);
+        B[1] = load_bf16x8(qrow + 32);
+    };
 
     // prologue: pair ids of units u0 and u0+1, Q rows of unit u0
-    uint32_t q0, q1;
-    ahead.rows(a.unit_off, a.offsets, u0, q0, q1);
-    bool v_cur = q0 + my < q1;
-    uint32_t pid_cur = v_cur ? a.pairs[q0 + my] : 0u;
-    bool v_nxt = false;
-    uint32_t pid_nxt = 0u;
-    if (u0 + 1 < u1) {
-        ahead.rows(a.unit_off, a.offsets, u0 + 1, q0, q1);
-        v_nxt = q0 + my < q1;
-        pid_nxt = v_nxt ? a.pairs[q0 + my] : 0u;
-    }
+    bool v_cur, v_nxt;
+    uint32_t pid_cur, pid_nxt;
+    fetch_pid(u0, pid_cur, v_cur);
+    fetch_pid(u0 + 1, pid_nxt, v_nxt);
     bf16x8 Bq[2];
-    load_q_operand(a.q + (int64_t)(pid_cur >> a.sp_log2) * kD, lane, v_cur, Bq);
+    fetch_q(pid_cur, Bq);
+    // drain the prologue loads, so that the loop's first wait (for the
+    // carried pair id) does not fall back to draining everything each trip
+    __builtin_amdgcn_s_waitcnt(0);
 
     int loaded = -1, koff = 0;
     for (uint32_t u = u0; u < u1; ++u) {
         uint32_t p0, p1;
         cur.rows(a.unit_off, a.offsets, u, p0, p1);
         // prefetch: pair ids of u+2, Q rows of u+1
-        bool v_n2 = false;
-        uint32_t pid_n2 = 0u;
-        if (u + 2 < u1) {
-            ahead.rows(a.unit_off, a.offsets, u + 2, q0, q1);
-            v_n2 = q0 + my < q1;
-            pid_n2 = v_n2 ? a.pairs[q0 + my] : 0u;
-        }
+        bool v_n2;
+        uint32_t pid_n2;
+        fetch_pid(u + 2, pid_n2, v_n2);
         bf16x8 Bq_nxt[2];
-        load_q_operand(a.q + (int64_t)(pid_nxt >> a.sp_log2) * kD, lane, v_nxt, Bq_nxt);
+        fetch_q(pid_nxt, Bq_nxt);
 
         if (cur.bucket != loaded) {
             __syncthreads();
@@ -431,46 +447,43 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
             __syncthreads();
             loaded = cur.bucket;
         }
-        if (p0 + 16 * w < p1) {  // wave has rows in this unit
-            f32x4 sc[KT];
-            float mx = -INFINITY;
+        f32x4 sc[KT];
+        float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < KT; ++i) {
-                sc[i] = score_tile(s_k, i, lane, Bq);
+        for (int i = 0; i < KT; ++i) {
+            sc[i] = score_tile(s_k, i, lane, Bq);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[i][r]);
-            }
-            const float m2 = row_max4(mx) * a.scale_log2;
-            float p[KT][4];
-            float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < KT; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    p[i][r] = exp2f(fmaf(sc[i][r], a.scale_log2, -m2));
-                    sum += p[i][r];
-                }
-            sum = row_sum4(sum);
-            f32x4 o[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            pv_accumulate<KT>(s_vt, VP, koff, lane, p, o);
-            if (v_cur) {
-                const float inv = 1.f / sum;
-                uint16_t* dst = a.part_o + (int64_t)pid_cur * kD + 16 * (lane >> 4);
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    bf16x8 ob;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        ob[r] = (__bf16)(o[2 * h2][r] * inv);
-                        ob[4 + r] = (__bf16)(o[2 * h2 + 1][r] * inv);
-                    }
-                    *reinterpret_cast<bf16x8*>(dst + 8 * h2) = ob;
-                }
-                if (lane < 16) a.part_lse[pid_cur] = m2 + log2f(sum);
-            }
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[i][r]);
         }
+        const float m2 = row_max4(mx) * a.scale_log2;
+        float p[KT][4];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < KT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[i][r] = exp2f(fmaf(sc[i][r], a.scale_log2, -m2));
+                sum += p[i][r];
+            }
+        sum = row_sum4(sum);
+        f32x4 o[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pv_accumulate<KT>(s_vt, VP, koff, lane, p, o);
+        const float inv = 1.f / sum;
+        const uint32_t pid_st = v_cur ? pid_cur : dummy;
+        uint16_t* dst = a.part_o + (int64_t)pid_st * kD + 16 * (lane >> 4);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            bf16x8 ob;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                ob[r] = (__bf16)(o[2 * h2][r] * inv);
+                ob[4 + r] = (__bf16)(o[2 * h2 + 1][r] * inv);
+            }
+            *reinterpret_cast<bf16x8*>(dst + 8 * h2) = ob;
+        }
+        a.part_lse[pid_st] = m2 + log2f(sum);  // the row's four lanes store the same value
         v_cur = v_nxt;
         pid_cur = pid_nxt;
         v_nxt = v_n2;
@@ -816,8 +829,8 @@ static AttendLayout attend_layout(const Geometry& g) {
         L.cursor = off;   off += align_up(NB * 4, 256);
         L.unit_off = off; off += align_up((NB + 1) * 4, 256);
         L.pairs = off;    off += align_up(npairs * 4, 256);
-        L.part_o = off;   off += align_up(nslots * kD * 2, 256);
-        L.part_lse = off; off += align_up(nslots * 4, 256);
+        L.part_o = off;   off += align_up((nslots + UNIT_ROWS) * kD * 2, 256);
+        L.part_lse = off; off += align_up((nslots + UNIT_ROWS) * 4, 256);
     }
     L.total = off;
     return L;
@@ -891,8 +904,9 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
     mark(ev, 6, s);
 
-    PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, g.N, g.nb, NB, ntiles,
-                sp_log2, scale_log2};
+    const uint32_t nslots = (uint32_t)(((size_t)g.B * g.Hq * g.N) << sp_log2);
+    PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, nslots, g.N, g.nb, NB,
+                ntiles, sp_log2, scale_log2};
     switch (g.bs) {
         case 16: launch_partial<16>(pa, s); break;
         case 32: launch_partial<32>(pa, s); break;

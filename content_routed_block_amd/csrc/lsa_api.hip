@@ -34,8 +34,8 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     const int64_t nb = p->seq_len / p->block;
     if (nb > 65536) return LSA_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)p->batch * p->q_heads * p->seq_len;
-    if ((rows << lsa::pair_stride_log2(p->top_k)) >= ((int64_t)1 << 32))
-        return LSA_ERR_UNSUPPORTED;  // 32-bit pair ids
+    if ((rows << lsa::pair_stride_log2(p->top_k)) + 64 >= ((int64_t)1 << 32))
+        return LSA_ERR_UNSUPPORTED;  // 32-bit pair ids (+ 64 dummy rows)
     if ((int64_t)p->batch * p->q_heads * ((p->seq_len + 255) / 256) >= ((int64_t)1 << 31))
         return LSA_ERR_UNSUPPORTED;
     if (!(p->scale == p->scale)) return LSA_ERR_SHAPE;  // NaN scale
