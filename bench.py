@@ -38,7 +38,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc
 # FETCH_SIZE / WRITE_SIZE runs, each scaled by the same counter's reading on a
 # plain copy of known size; tied to the kernel sources it was measured on.
-TRAFFIC = None
+TRAFFIC = {
+    "csrc": "6e98d797f6d72e5e", "stage": 6, "workload": "qwen05b_n128k_needles",
+    "fetch_kib": 1.934e6, "write_kib": 4.756e6, "fetch_factor": 2.0, "write_factor": 1.0,
+    "bytes_per_launch": 1.934e6 * 1024 * 2.0 + 4.756e6 * 1024 * 1.0,
+}
 
 
 def csrc_digest() -> str:
