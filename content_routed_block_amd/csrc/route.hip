@@ -22,7 +22,7 @@
 //           of the pass-2 scores b_c reach.
 //   pass 2  hi+lo scores b_c (fp32 accuracy); candidates at or above the
 //           threshold are appended to the query's survivor list in LDS
-//           (~20 per query on random data; capacity 32).
+//           (~20 per query on random data; capacity RT_CAP = 40).
 //   select  one lane per query inserts its survivors into a 16-entry sorted
 //           list of 64-bit keys (score, then lower index), then sorts the
 //           chosen block ids ascending.

@@ -2,7 +2,8 @@
 // cumulant mu_c of the SSA routing score, SSA page "Algorithm and
 // complexity").  HBM-bound streaming kernel: one wave per (head, block);
 // lane l reads 16 bytes (8 dims) of token l/8 + 8i, so every load
-// instruction covers 1 KB of consecutive memory.  Sums are kept in fp64 and
+// instruction covers 1 KB of consecutive memory, and a lane issues all of
+// its loads before the first one is used.  Sums are kept in fp64 and
 // rounded once to fp32, so the result is the fp32 rounding of the exact
 // mean whenever the fp64 sum is exact (always, for bf16 data whose
 // magnitudes span fewer than ~2^39).
@@ -11,39 +12,44 @@
 
 namespace lsa {
 
+template <int BS>
 __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ x,
                                                    float* __restrict__ xbar,
-                                                   int64_t n_blocks, int N, int bs) {
+                                                   int64_t n_blocks, int N) {
+    constexpr int LOADS = BS / 8;  // 16-byte loads per lane, all issued before any use
     const int lane = threadIdx.x & 63;
     const int64_t wblk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wblk >= n_blocks) return;
-    const int nb = N / bs;
+    const int nb = N / BS;
     const int64_t bh = wblk / nb;
     const int64_t c = wblk - bh * nb;
     const int dg = lane & 7;   // dims 8*dg .. 8*dg+7
     const int j0 = lane >> 3;  // tokens j0, j0+8, ...
-    const uint16_t* base = x + (bh * N + c * bs) * kD + dg * 8;
+    const uint16_t* base = x + (bh * N + c * BS + j0) * kD + dg * 8;
+    u32x4 v[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * 8 * kD);
     double acc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
-    for (int j = j0; j < bs; j += 8) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(base + (int64_t)j * kD);
-        float f[8];
-        unpack8(v, f);
+    for (int d = 0; d < 8; ++d) acc[d] = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += (double)f[i];
+    for (int i = 0; i < LOADS; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
     }
 #pragma unroll
     for (int m = 8; m < 64; m <<= 1)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], m, kWave);
+        for (int d = 0; d < 8; ++d) acc[d] += __shfl_xor(acc[d], m, kWave);
     if (j0 == 0) {
-        const double inv = 1.0 / (double)bs;  // bs is a power of two: exact
+        constexpr double inv = 1.0 / (double)BS;  // a power of two: exact
         f32x4 lo, hi;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lo[i] = (float)(acc[i] * inv);
-            hi[i] = (float)(acc[4 + i] * inv);
+        for (int d = 0; d < 4; ++d) {
+            lo[d] = (float)(acc[d] * inv);
+            hi[d] = (float)(acc[4 + d] * inv);
         }
         float* o = xbar + wblk * kD + dg * 8;
         *reinterpret_cast<f32x4*>(o) = lo;
@@ -61,8 +67,12 @@ hipError_t launch_summarize(const uint16_t* x, float* xbar, int BH, int N, int b
                             hipStream_t s) {
     const int64_t n_blocks = (int64_t)BH * (N / bs);
     const int64_t grid = (n_blocks + 3) / 4;
-    hipLaunchKernelGGL(k_summarize, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks,
-                       N, bs);
+    switch (bs) {
+        case 16: hipLaunchKernelGGL(k_summarize<16>, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N); break;
+        case 32: hipLaunchKernelGGL(k_summarize<32>, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N); break;
+        case 64: hipLaunchKernelGGL(k_summarize<64>, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N); break;
+        default: hipLaunchKernelGGL(k_summarize<128>, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N); break;
+    }
     return hipGetLastError();
 }
 
