@@ -2,6 +2,7 @@
 // workspace layout and the launch sequence of each call.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "lsa.h"
 #include "lsa_common.hpp"
@@ -38,7 +39,9 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
         return LSA_ERR_UNSUPPORTED;  // 32-bit pair ids (+ 64 dummy rows)
     if ((int64_t)p->batch * p->q_heads * ((p->seq_len + 255) / 256) >= ((int64_t)1 << 31))
         return LSA_ERR_UNSUPPORTED;
-    if (!(p->scale == p->scale)) return LSA_ERR_SHAPE;  // NaN scale
+    uint32_t scale_bits;
+    memcpy(&scale_bits, &p->scale, 4);
+    if ((scale_bits & 0x7FFFFFFFu) > 0x7F800000u) return LSA_ERR_SHAPE;  // NaN scale
     g->B = p->batch;
     g->Hq = p->q_heads;
     g->Hkv = p->kv_heads;

@@ -9,23 +9,24 @@
 // their last token precedes the cutoff).  Image-mode rows are pooled query
 // blocks scored against every key block (LLSA page, "Minimum Usage").
 //
-// Design (gfx950).  A workgroup owns 256 query rows of one (b, h): four
-// waves x 64 rows.  Candidate block means stream through LDS in chunks of
+// Design (gfx950).  A workgroup owns 128 query rows of one (b, h): four
+// waves x 32 rows.  Candidate block means stream through LDS in chunks of
 // 32, split into bf16 hi + bf16 lo parts.  Scores are 32x32x16 bf16 MFMA
-// tiles S^T = Kbar_chunk . Q^T, so lane l holds query l%32 (of each 32-row
-// tile) and 16 candidates whose indices fall in one residue class mod 32
-// per register.
-//   pass 1  hi-only scores a_c; every lane keeps a running maximum per
-//           register, i.e. the maximum over each residue class: 32 group
-//           maxima per query.  The k-th largest group maximum, lowered by a
-//           rigorous bound on |a_c - b_c|, is a threshold that at least k
-//           of the pass-2 scores b_c reach.
+// tiles S^T = Kbar_chunk . Q^T, so lane l holds query l%32 and 16
+// candidates whose indices fall in one residue class mod 32 per register;
+// lanes l and l^32 hold the two halves of the same query's chunk.
+//   pass 1  hi-only scores a_c; every lane keeps the two largest values of
+//           each of its residue classes.  The k-th largest of those 64
+//           values (over the lane pair), lowered by a rigorous bound on
+//           |a_c - b_c|, is a threshold that at least k of the pass-2
+//           scores b_c reach.
 //   pass 2  hi+lo scores b_c (fp32 accuracy); candidates at or above the
 //           threshold are appended to the query's survivor list in LDS
-//           (~20 per query on random data; capacity RT_CAP = 40).
-//   select  one lane per query inserts its survivors into a 16-entry sorted
-//           list of 64-bit keys (score, then lower index), then sorts the
-//           chosen block ids ascending.
+//           (~17 per query on the topic workloads; capacity RT_CAP = 24).
+//   select  each lane of the pair inserts the survivors it found into a
+//           16-entry sorted list of 64-bit keys (score, then lower index);
+//           the two lists are merged and the chosen block ids written in
+//           ascending order.
 // Queries whose survivor list overflows (ties, adversarial inputs) are
 // queued and redone exactly by k_route_fallback.
 #include <math.h>
@@ -35,9 +36,9 @@
 
 namespace lsa {
 
-constexpr int RT_ROWS = 256;   // query rows per workgroup (4 waves x 64)
+constexpr int RT_ROWS = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int RT_CH = 32;      // candidates per step
-constexpr int RT_CAP = 40;     // survivor slots per query
+constexpr int RT_CAP = 24;     // survivor slots per query
 constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
 constexpr int FB_GRID = 256;   // workgroups of the exact fallback
 
@@ -56,6 +57,7 @@ struct RouteArgs {
     int Hq, Hkv, N, bs, nb, top_k, window;
     int P;       // rows per (b, h): N (causal) or nb (image)
     int tiles;   // ceil(P / RT_ROWS)
+    int items;   // B * Hq * tiles
     int nb_pad;  // nb rounded up to a multiple of RT_CH
 };
 
@@ -111,15 +113,21 @@ __device__ __forceinline__ void bitonic_sort_asc_u32(uint32_t* v) {
             }
 }
 
-// k-th largest (1 <= k <= 16) of the 32 values held as 16 in this lane and 16
-// in lane ^ 32.  Both lanes of the pair return the same value.
-__device__ __forceinline__ float kth_largest_of_pair(float (&v)[16], int k) {
-    bitonic_sort_desc<16>(v);
+// k-th largest (1 <= k <= 16) of the 64 values held as the per-class
+// largest (m1) and second largest (m2) values of 16 classes in this lane and
+// 16 more classes in lane ^ 32.  Both lanes of the pair return the same value.
+__device__ __forceinline__ float kth_largest_top2_pair(float (&m1)[16], float (&m2)[16], int k) {
+    bitonic_sort_desc<16>(m1);
+    bitonic_sort_desc<16>(m2);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = fmaxf(m1[i], m2[15 - i]);  // top 16 of the 32, bitonic
+    bitonic_merge_desc<16>(v);
     float w[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float other = __shfl_xor(v[15 - i], 32, kWave);
-        w[i] = fmaxf(v[i], other);  // bitonic; holds the 16 largest of the union
+        w[i] = fmaxf(v[i], other);  // top 16 of the pair's 64, bitonic
     }
     bitonic_merge_desc<16>(w);
     float r = -INFINITY;
@@ -127,6 +135,22 @@ __device__ __forceinline__ float kth_largest_of_pair(float (&v)[16], int k) {
     for (int i = 0; i < 16; ++i)
         if (i == k - 1) r = w[i];
     return r;
+}
+
+// Bitonic merge of 16 64-bit keys into descending order.
+__device__ __forceinline__ void bitonic_merge_desc_u64(uint64_t (&v)[kMaxTopK]) {
+#pragma unroll
+    for (int stride = kMaxTopK >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+        for (int i = 0; i < kMaxTopK; ++i) {
+            const int j = i ^ stride;
+            if (j > i) {
+                const uint64_t a = v[i], b = v[j];
+                const bool gt = a > b;
+                v[i] = gt ? a : b;
+                v[j] = gt ? b : a;
+            }
+        }
 }
 
 __device__ __forceinline__ void insert_key(uint64_t (&L)[kMaxTopK], uint64_t x) {
@@ -254,53 +278,64 @@ __device__ __forceinline__ void read_cands(const __bf16* buf, int l32, int half,
     for (int ks = 0; ks < 4; ++ks) A[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks);
 }
 
+// min(max(x, lo), hi) for lo <= hi in one instruction.
+__device__ __forceinline__ int clamp_i32(int x, int lo, int hi) {
+    int r;
+    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(lo), "v"(hi));
+    return r;
+}
+
 // ------------------------------------------------------------ main kernel
-// Each wave is independent (its own 64 rows, its own survivor lists); the
-// only workgroup barrier separates scoring from selection.
+// Each wave is independent (its own 32 rows and survivor lists); the
+// workgroup only shares the staged candidate chunks.
 template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
+__global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_hi[2][RT_CH * RT_PITCH];
     __shared__ __attribute__((aligned(16))) __bf16 s_lo[2][RT_CH * RT_PITCH];
-    __shared__ float s_score[RT_ROWS * RT_CAP];
-    __shared__ uint16_t s_cidx[RT_ROWS * RT_CAP];
-    __shared__ int s_cnt[RT_ROWS * 2];
+    // survivor lists, slot-major ([slot][row]) so that the lanes of a wave
+    // touch consecutive words
+    // (scores: RT_CAP*RT_ROWS floats, then the block ids as uint16)
+    __shared__ __attribute__((aligned(16))) char s_list[RT_CAP * RT_ROWS * 6];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int half = lane >> 5, l32 = lane & 31;
-    const int bh = blockIdx.x / a.tiles;
-    const int tile = a.tiles - 1 - (int)(blockIdx.x - bh * a.tiles);  // heavy tiles first
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+    // item = xcd * (grid / 8) + blockIdx / 8 keeps consecutive items, i.e.
+    // the tiles of one head and the heads of one KV group, on one XCD (whose
+    // L2 then holds that group's candidate blocks).  Tiles of a head run
+    // heavy (late positions, most candidates) first.
+    const int per_xcd = gridDim.x / 8;
+    const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= a.items) return;
+    const int bh = item / a.tiles;
+    const int tile = a.tiles - 1 - (item - bh * a.tiles);
     const int h = bh % a.Hq, b = bh / a.Hq;
     const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
     const int P = a.P;
-    const int r0 = tile * RT_ROWS + 64 * w;  // first row of this wave
+    const int r0 = tile * RT_ROWS + 32 * w;  // first row of this wave
     const uint16_t* khi = a.khi + (int64_t)bg * a.nb_pad * kD;
     const uint16_t* klo = a.klo + (int64_t)bg * a.nb_pad * kD;
 
-    int rq[2], Erow[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        rq[tt] = r0 + 32 * tt + l32;
-        Erow[tt] = row_candidates(CAUSAL, rq[tt], P, a.bs, a.window, a.nb);
-    }
-    const int Emax = r0 < P ? row_candidates(CAUSAL, min(r0 + 63, P - 1), P, a.bs, a.window, a.nb) : 0;
+    const int rq = r0 + l32;
+    const int Erow = row_candidates(CAUSAL, rq, P, a.bs, a.window, a.nb);
+    const int Emax = r0 < P ? row_candidates(CAUSAL, min(r0 + 31, P - 1), P, a.bs, a.window, a.nb) : 0;
     const int wg_last = min(tile * RT_ROWS + RT_ROWS, P) - 1;
     const int Ewg = row_candidates(CAUSAL, wg_last, P, a.bs, a.window, a.nb);  // chunk loop bound
-    const int Emin = (r0 + 63 < P) ? row_candidates(CAUSAL, r0, P, a.bs, a.window, a.nb) : 0;
+    const int Emin = (r0 + 31 < P) ? row_candidates(CAUSAL, r0, P, a.bs, a.window, a.nb) : 0;
     const float kn_max = Emax > 0 ? a.pk[(int64_t)bg * a.nb + Emax - 1] : 0.f;
     const float lo_max = Emax > 0 ? a.plo[(int64_t)bg * a.nb + Emax - 1] : 0.f;
 
-    // ---- queries as the B operand (B[d][t] = Q[t][d]): lane holds dims
-    // 8*half + 16*ks .. +7 of row rq[tt].
-    bf16x8 Bq[2][4];
-    bf16x8 Bql[2][4];  // image mode: lo part of the pooled query
-    float qn[2], qln[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    // ---- the query as the B operand (B[d][t] = Q[t][d]): lane holds dims
+    // 8*half + 16*ks .. +7 of row rq.
+    bf16x8 Bq[4];
+    bf16x8 Bql[4];  // image mode: lo part of the pooled query
+    float qn, qln;
+    {
         float s2 = 0.f, l2 = 0.f;
-        if (rq[tt] < P) {
+        if (rq < P) {
             if (CAUSAL) {
-                const uint16_t* qp = a.q + ((int64_t)bh * a.N + rq[tt]) * kD + 8 * half;
+                const uint16_t* qp = a.q + ((int64_t)bh * a.N + rq) * kD + 8 * half;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
@@ -308,11 +343,11 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
                     unpack8(raw, f);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) s2 = fmaf(f[i], f[i], s2);
-                    Bq[tt][ks] = __builtin_bit_cast(bf16x8, raw);
-                    Bql[tt][ks] = bf16x8{};
+                    Bq[ks] = __builtin_bit_cast(bf16x8, raw);
+                    Bql[ks] = bf16x8{};
                 }
             } else {
-                const float* qp = a.qbar + ((int64_t)bh * a.nb + rq[tt]) * kD + 8 * half;
+                const float* qp = a.qbar + ((int64_t)bh * a.nb + rq) * kD + 8 * half;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 16 * ks);
@@ -322,8 +357,8 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
                     for (int i = 0; i < 8; ++i) {
                         const __bf16 hi = (__bf16)f[i];
                         const __bf16 lo = (__bf16)(f[i] - (float)hi);
-                        Bq[tt][ks][i] = hi;
-                        Bql[tt][ks][i] = lo;
+                        Bq[ks][i] = hi;
+                        Bql[ks][i] = lo;
                         const float hf = (float)hi, lf = (float)lo;
                         s2 = fmaf(hf, hf, s2);
                         l2 = fmaf(lf, lf, l2);
@@ -333,24 +368,25 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
         } else {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                Bq[tt][ks] = bf16x8{};
-                Bql[tt][ks] = bf16x8{};
+                Bq[ks] = bf16x8{};
+                Bql[ks] = bf16x8{};
             }
         }
         s2 += __shfl_xor(s2, 32, kWave);
         l2 += __shfl_xor(l2, 32, kWave);
-        qn[tt] = sqrtf(s2);
-        qln[tt] = sqrtf(l2);
+        qn = sqrtf(s2);
+        qln = sqrtf(l2);
     }
 
-    // ---- pass 1: hi-only scores, group maxima
+    // ---- pass 1: hi-only scores, two largest per residue class.
     // Chunks below Efull are candidates of every row of the wave (no mask).
     const int Efull = (Emin / RT_CH) * RT_CH;
-    float gm[2][16];
+    float m1[16], m2[16];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) gm[tt][r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+        m1[r] = -INFINITY;
+        m2[r] = -INFINITY;
+    }
     {
         // chunk j is staged in buffer j&1; one barrier per chunk
         u32x4 pre = Ewg > 0 ? stage_load(khi, 0, tid) : u32x4{0u, 0u, 0u, 0u};
@@ -361,24 +397,21 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
             if (cb < Emax) {
                 bf16x8 A[4];
                 read_cands(s_hi[j & 1], l32, half, A);
-                f32x16 acc[2] = {};
+                f32x16 acc = {};
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+                for (int ks = 0; ks < 4; ++ks) acc = mfma32(A[ks], Bq[ks], acc);
+                if (cb >= Efull) {
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) acc[tt] = mfma32(A[ks], Bq[tt][ks], acc[tt]);
-                if (cb < Efull) {
+                    for (int r = 0; r < 16; ++r) {
+                        const int c = cb + 8 * (r >> 2) + 4 * half + (r & 3);
+                        acc[r] = c < Erow ? acc[r] : -INFINITY;
+                    }
+                }
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) gm[tt][r] = fmaxf(gm[tt][r], acc[tt][r]);
-                } else {
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int c = cb + 8 * (r >> 2) + 4 * half + (r & 3);
-                            gm[tt][r] = fmaxf(gm[tt][r], c < Erow[tt] ? acc[tt][r] : -INFINITY);
-                        }
+                for (int r = 0; r < 16; ++r) {
+                    // m1 >= m2, so the new second largest is the median
+                    m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], acc[r]);
+                    m1[r] = fmaxf(m1[r], acc[r]);
                 }
             }
             if (cb + RT_CH < Ewg) stage_store(s_hi[(j + 1) & 1], tid, pre);
@@ -386,31 +419,27 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
         }
     }
 
-    // threshold: k-th largest group maximum minus a bound on |a_c - b_c|:
+    // threshold: k-th largest class top-2 value minus a bound on |a_c - b_c|:
     // |q_hi . k_lo| + |q_lo . k_hi| + fp32 accumulation error.
-    float theta[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const float th = kth_largest_of_pair(gm[tt], a.top_k);
-        const float delta = 1.0625f * (qn[tt] * lo_max + qln[tt] * kn_max) +
-                            6.2e-5f * (qn[tt] + qln[tt]) * kn_max;
-        theta[tt] = th - delta;  // -inf stays -inf
+    float theta;
+    {
+        const float th = kth_largest_top2_pair(m1, m2, a.top_k);
+        const float delta = 1.0625f * (qn * lo_max + qln * kn_max) + 6.2e-5f * (qn + qln) * kn_max;
+        theta = th - delta;  // -inf stays -inf
     }
 
-    // ---- pass 2: hi+lo scores, survivors to this wave's LDS lists.
-    // The lane pair (l, l^32) shares a query's list: half 0 fills it upward
-    // from slot 0, half 1 downward from slot RT_CAP-1; slot indices are
-    // clamped to the list, so an overflowing list stays in bounds (the query
-    // is then redone by the fallback).
-    int pos[2], lo_slot[2], hi_slot[2];
-    const int dir = half ? -1 : 1;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int base = (64 * w + 32 * tt + l32) * RT_CAP;
-        lo_slot[tt] = base;
-        hi_slot[tt] = base + RT_CAP - 1;
-        pos[tt] = half ? hi_slot[tt] : lo_slot[tt];
-    }
+    // ---- pass 2: hi+lo scores, survivors to the row's LDS list.  The lane
+    // pair (l, l^32) shares a row's list: half 0 fills it upward from slot 0,
+    // half 1 downward from slot RT_CAP-1; slots are clamped to the list, so
+    // an overflowing list stays in bounds (the row is then redone by the
+    // fallback).
+    const int qrow = 32 * w + l32;  // row within the workgroup
+    // list position kept as the byte offset of the score slot; the block
+    // id of slot e sits at byte LIST_IDX + e/2
+    constexpr int LIST_IDX = RT_CAP * RT_ROWS * 4;
+    const int step = half ? -RT_ROWS * 4 : RT_ROWS * 4;
+    const int at_lo = qrow * 4, at_hi = ((RT_CAP - 1) * RT_ROWS + qrow) * 4;
+    int at = half ? at_hi : at_lo;
     {
         u32x4 ph = {0u, 0u, 0u, 0u}, pl = ph;
         if (Ewg > 0) {
@@ -429,41 +458,36 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
                 bf16x8 ch[4], cl[4];
                 read_cands(s_hi[j & 1], l32, half, ch);
                 read_cands(s_lo[j & 1], l32, half, cl);
-                f32x16 acc[2] = {};
+                f32x16 acc = {};
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        acc[tt] = mfma32(ch[ks], Bq[tt][ks], acc[tt]);
-                        acc[tt] = mfma32(cl[ks], Bq[tt][ks], acc[tt]);
-                        if (!CAUSAL) acc[tt] = mfma32(ch[ks], Bql[tt][ks], acc[tt]);
-                    }
+                for (int ks = 0; ks < 4; ++ks) {
+                    acc = mfma32(ch[ks], Bq[ks], acc);
+                    acc = mfma32(cl[ks], Bq[ks], acc);
+                    if (!CAUSAL) acc = mfma32(ch[ks], Bql[ks], acc);
+                }
                 const int cl0 = cb + 4 * half;
                 if (cb < Efull) {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            if (acc[tt][r] >= theta[tt]) {
-                                const int at = min(max(pos[tt], lo_slot[tt]), hi_slot[tt]);
-                                s_score[at] = acc[tt][r];
-                                s_cidx[at] = (uint16_t)(cl0 + 8 * (r >> 2) + (r & 3));
-                                pos[tt] += dir;
-                            }
+                    for (int r = 0; r < 16; ++r) {
+                        if (acc[r] >= theta) {
+                            const int e = clamp_i32(at, at_lo, at_hi);
+                            *reinterpret_cast<float*>(s_list + e) = acc[r];
+                            *reinterpret_cast<uint16_t*>(s_list + LIST_IDX + (e >> 1)) =
+                                (uint16_t)(cl0 + 8 * (r >> 2) + (r & 3));
+                            at += step;
                         }
+                    }
                 } else {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int c = cl0 + 8 * (r >> 2) + (r & 3);
-                            if (acc[tt][r] >= theta[tt] && c < Erow[tt]) {
-                                const int at = min(max(pos[tt], lo_slot[tt]), hi_slot[tt]);
-                                s_score[at] = acc[tt][r];
-                                s_cidx[at] = (uint16_t)c;
-                                pos[tt] += dir;
-                            }
+                    for (int r = 0; r < 16; ++r) {
+                        const int c = cl0 + 8 * (r >> 2) + (r & 3);
+                        if (acc[r] >= theta && c < Erow) {
+                            const int e = clamp_i32(at, at_lo, at_hi);
+                            *reinterpret_cast<float*>(s_list + e) = acc[r];
+                            *reinterpret_cast<uint16_t*>(s_list + LIST_IDX + (e >> 1)) = (uint16_t)c;
+                            at += step;
                         }
+                    }
                 }
             }
             if (cb + RT_CH < Ewg) {
@@ -473,33 +497,41 @@ __global__ __launch_bounds__(256, 2) void k_route(RouteArgs a) {
             __syncthreads();
         }
     }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int n = half ? (hi_slot[tt] - pos[tt]) : (pos[tt] - lo_slot[tt]);
-        s_cnt[(64 * w + 32 * tt + l32) * 2 + half] = n;
-    }
-    __syncthreads();
 
-    // ---- selection: lane -> query 64*w + lane
-    const int qs = 64 * w + lane;
-    const int row = r0 + lane;
-    if (row < P) {
-        const int n0 = s_cnt[qs * 2], n1 = s_cnt[qs * 2 + 1];
-        const int nt = n0 + n1;
-        if (nt > RT_CAP) {
+    // ---- selection: each lane of the pair ranks the survivors it found,
+    // then the pair merges its two sorted lists.
+    const int n_mine = (half ? at_hi - at : at - at_lo) / (RT_ROWS * 4);
+    const int n_pair = n_mine + __shfl_xor(n_mine, 32, kWave);
+    if (rq >= P) return;
+    const int64_t out_row = (int64_t)bh * P + rq;
+    if (n_pair > RT_CAP) {
+        if (half == 0) {
             const uint32_t slot = atomicAdd(a.ovf_count, 1u);
-            a.ovf_rows[slot] = (uint32_t)((int64_t)bh * P + row);
-        } else {
-            uint64_t L[kMaxTopK];
-#pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
-            for (int i = 0; i < nt; ++i) {
-                const int e = i < n0 ? i : (RT_CAP - 1 - (i - n0));
-                insert_key(L, sel_key(s_score[qs * RT_CAP + e], s_cidx[qs * RT_CAP + e]));
-            }
-            const int m = nt < a.top_k ? nt : a.top_k;
-            write_selection(a.idx + ((int64_t)bh * P + row) * a.top_k, L, m, a.top_k);
+            a.ovf_rows[slot] = (uint32_t)out_row;
         }
+        return;
+    }
+    uint64_t L[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
+    for (int i = 0; i < n_mine; ++i) {
+        const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
+        insert_key(L, sel_key(*reinterpret_cast<const float*>(s_list + e),
+                              *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (e >> 1))));
+    }
+    uint64_t M[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        const uint64_t o = L[kMaxTopK - 1 - j];
+        const uint32_t olo = __shfl_xor((uint32_t)o, 32, kWave);
+        const uint32_t ohi = __shfl_xor((uint32_t)(o >> 32), 32, kWave);
+        const uint64_t other = ((uint64_t)ohi << 32) | olo;
+        M[j] = L[j] > other ? L[j] : other;  // top 16 of the pair, bitonic
+    }
+    bitonic_merge_desc_u64(M);
+    if (half == 0) {
+        const int m = n_pair < a.top_k ? n_pair : a.top_k;
+        write_selection(a.idx + out_row * a.top_k, M, m, a.top_k);
     }
 }
 
@@ -633,6 +665,7 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     a.window = g.window;
     a.P = g.causal ? g.N : g.nb;
     a.tiles = (a.P + RT_ROWS - 1) / RT_ROWS;
+    a.items = g.B * g.Hq * a.tiles;
     a.nb_pad = L.nb_pad;
     hipError_t e = launch_fill_u32(a.ovf_count, 1, 0u, s);
     if (e != hipSuccess) return e;
@@ -644,7 +677,7 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
                        kbar, khi, klo, pk, plo, nbg, g.nb, L.nb_pad);
     hipLaunchKernelGGL(k_prefix_max, dim3((unsigned)(2 * nbg)), dim3(1024), 0, s, pk, g.nb);
-    const dim3 grid((unsigned)((int64_t)g.B * g.Hq * a.tiles));
+    const dim3 grid((unsigned)(((int64_t)a.items + 7) / 8 * 8));  // a multiple of the XCD count
     if (g.causal) {
         hipLaunchKernelGGL(k_route<true>, grid, dim3(256), 0, s, a);
         mark(ev, 2, s);
