@@ -9,10 +9,13 @@
 //   1. k_bucket<false>  counts, per (b, KV head, key block), the (row, slot)
 //                       pairs that selected it (LDS histogram per workgroup).
 //   2. k_bucket_scan    bucket offsets and the work units (64 rows each).
-//   3. k_bucket<true>   scatters pair ids into bucket order.
+//   3. k_bucket<true>   scatters pair ids into bucket order and records, per
+//                       (row, slot), the pair's position in that order.
 //   4. k_block_partial  one K/V block in LDS against up to 64 gathered query
 //                       rows: S = Q K^T and O = P V on bf16 MFMA; writes the
-//                       normalised partial output (bf16) and its log2 mass.
+//                       normalised partial output (bf16, by row and slot)
+//                       and its log2 mass (by position, so those writes are
+//                       contiguous).
 //   5. k_window_merge   flash-style online softmax over the block-aligned
 //                       window [bs*E(t), t] with a causal mask, then merges
 //                       the row's routed partials with the append law of the
@@ -220,8 +223,19 @@ struct BucketArgs {
     uint32_t* counts;    // [NB]
     uint32_t* cursor;    // [NB]
     uint32_t* pairs;     // [total pairs]
+    uint32_t* rev;       // [top_k][rows], slot-major: position of pair (row, slot), ~0 if unused
+    int64_t rows;        // B * Hq * N
     int Hq, Hkv, N, bs, nb, top_k, window, tchunk, sp_log2;
 };
+
+// Writes one row's entries of the slot-major position table, so that the
+// lanes of a wave (consecutive rows) store consecutive words.
+__device__ __forceinline__ void write_rev_row(uint32_t* rev, int64_t rows, int64_t row,
+                                              const uint32_t (&pos)[kMaxTopK], int top_k) {
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+        if (s < top_k) rev[s * rows + row] = pos[s];
+}
 
 // Workgroup = (batch, KV head, chunk of tchunk positions) over all query
 // heads of the group.  Histogram in LDS (when nb fits), then one global
@@ -248,8 +262,10 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
         const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
         int c[kMaxTopK];
         uint32_t m = row_used(a.idx + row * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
+        uint32_t posv[kMaxTopK];
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s) {
+            posv[s] = 0xFFFFFFFFu;
             if (!((m >> s) & 1u)) continue;
             if (lds) {
                 atomicAdd(&s_h[c[s]], 1u);
@@ -258,8 +274,10 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
             } else {
                 const uint32_t pos = atomicAdd(&a.cursor[bucket0 + c[s]], 1u);
                 a.pairs[pos] = (uint32_t)((row << a.sp_log2) | s);
+                posv[s] = pos;
             }
         }
+        if (SCATTER && !lds) write_rev_row(a.rev, a.rows, row, posv, a.top_k);
     }
     if (!lds) return;
     __syncthreads();
@@ -278,12 +296,15 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
         const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
         int c[kMaxTopK];
         uint32_t m = row_used(a.idx + row * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
+        // all LDS reservations first (their latencies overlap), then the stores
+        uint32_t posv[kMaxTopK];
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            if (!((m >> s) & 1u)) continue;
-            const uint32_t pos = atomicAdd(&s_h[c[s]], 1u);
-            a.pairs[pos] = (uint32_t)((row << a.sp_log2) | s);
-        }
+        for (int s = 0; s < kMaxTopK; ++s)
+            posv[s] = ((m >> s) & 1u) ? atomicAdd(&s_h[c[s]], 1u) : 0xFFFFFFFFu;
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+            if ((m >> s) & 1u) a.pairs[posv[s]] = (uint32_t)((row << a.sp_log2) | s);
+        write_rev_row(a.rev, a.rows, row, posv, a.top_k);
     }
 }
 
@@ -335,9 +356,10 @@ struct PartArgs {
     const uint32_t* pairs;
     const uint32_t* offsets;   // [NB+1]
     const uint32_t* unit_off;  // [NB+1]
-    uint16_t* part_o;          // bf16 bits [rows * SP][64], permuted (see k_block_partial)
-    float* part_lse;           // [rows * SP], log2 domain
+    uint16_t* part_o;          // bf16 bits [rows * SP + 64][64] by pair id, permuted (see k_block_partial)
+    float* part_lse;           // [rows * top_k + 64] by pair position, log2 domain
     uint32_t dummy_pid;        // rows * SP: first of 64 rows written by lanes without a pair
+    uint32_t dummy_pos;        // rows * top_k: first of 64 log-mass slots for the same lanes
     int N, nb, NB, ntiles, sp_log2;
     float scale_log2;
 };
@@ -397,6 +419,7 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     // without a row read pair 0 and write a dummy row), so the wait for a
     // prefetched operand never has to drain the stores issued after it.
     const uint32_t dummy = a.dummy_pid + my;
+    const uint32_t dummy_pos = a.dummy_pos + my;
     auto fetch_pid = [&](uint32_t u, uint32_t& pid, bool& v) {
         uint32_t q0 = 0, q1 = 0;
         if (u < u1) ahead.rows(a.unit_off, a.offsets, u, q0, q1);
@@ -483,7 +506,9 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
             }
             *reinterpret_cast<bf16x8*>(dst + 8 * h2) = ob;
         }
-        a.part_lse[pid_st] = m2 + log2f(sum);  // the row's four lanes store the same value
+        // by position: the wave's 16 rows are consecutive, so this store is
+        // contiguous (the row's four lanes store the same value)
+        a.part_lse[v_cur ? p0 + my : dummy_pos] = m2 + log2f(sum);
         v_cur = v_nxt;
         pid_cur = pid_nxt;
         v_nxt = v_n2;
@@ -501,7 +526,9 @@ struct WinArgs {
     const int32_t* idx;
     const uint16_t* part_o;
     const float* part_lse;
+    const uint32_t* rev;  // [top_k][rows]
     float* out;
+    int64_t rows;
     int Hq, Hkv, N, bs, top_k, window, tiles, items, ntiles, sp_log2;
     float scale_log2;
 };
@@ -633,23 +660,18 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     // eight slots at a time so their loads are in flight together; a
     // partial row stores dim 16mt + 4j + r at slot 16j + 4mt + r
     const int64_t prow = row << a.sp_log2;
+    // log2 masses: the pair positions from the slot-major table (the wave's
+    // 16 rows are consecutive, so each load is contiguous), then one 4-byte
+    // gather per used slot
     float lse_all[kMaxTopK];
     {
-        const float* lp = a.part_lse + prow;
-        if ((a.top_k & 3) == 0) {
+        uint32_t rs[kMaxTopK];
 #pragma unroll
-            for (int s4 = 0; s4 < kMaxTopK / 4; ++s4) {
-                f32x4 v = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                if (4 * s4 < a.top_k && ((used >> (4 * s4)) & 0xFu))
-                    v = *reinterpret_cast<const f32x4*>(lp + 4 * s4);
-                lse_all[4 * s4] = v[0]; lse_all[4 * s4 + 1] = v[1];
-                lse_all[4 * s4 + 2] = v[2]; lse_all[4 * s4 + 3] = v[3];
-            }
-        } else {
+        for (int sl = 0; sl < kMaxTopK; ++sl)
+            rs[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.rev[sl * a.rows + row] : 0u;
 #pragma unroll
-            for (int sl = 0; sl < kMaxTopK; ++sl)
-                lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? lp[sl] : -INFINITY;
-        }
+        for (int sl = 0; sl < kMaxTopK; ++sl)
+            lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.part_lse[rs[sl]] : -INFINITY;
     }
 #pragma unroll
     for (int s0 = 0; s0 < kMaxTopK; s0 += 8) {
@@ -810,7 +832,7 @@ int pair_stride_log2(int top_k) {
 }
 
 struct AttendLayout {
-    size_t vt, counts, offsets, cursor, unit_off, pairs, part_o, part_lse, total;
+    size_t vt, counts, offsets, cursor, unit_off, pairs, rev, part_o, part_lse, total;
 };
 
 static AttendLayout attend_layout(const Geometry& g) {
@@ -829,8 +851,9 @@ static AttendLayout attend_layout(const Geometry& g) {
         L.cursor = off;   off += align_up(NB * 4, 256);
         L.unit_off = off; off += align_up((NB + 1) * 4, 256);
         L.pairs = off;    off += align_up(npairs * 4, 256);
+        L.rev = off;      off += align_up(npairs * 4, 256);
         L.part_o = off;   off += align_up((nslots + UNIT_ROWS) * kD * 2, 256);
-        L.part_lse = off; off += align_up((nslots + UNIT_ROWS) * 4, 256);
+        L.part_lse = off; off += align_up((npairs + UNIT_ROWS) * 4, 256);
     }
     L.total = off;
     return L;
@@ -879,6 +902,7 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     uint32_t* pairs = reinterpret_cast<uint32_t*>(base + L.pairs);
     uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
     float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
+    uint32_t* rev = reinterpret_cast<uint32_t*>(base + L.rev);
     const int NB = nbg * g.nb;
     const int sp_log2 = pair_stride_log2(g.top_k);
 
@@ -891,7 +915,8 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
         (4096 + rep - 1) / rep,
         (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k));
     tc = std::min<int64_t>((tc + 63) / 64 * 64, g.N);
-    BucketArgs ba{idx, counts, cursor, pairs, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window,
+    const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+    BucketArgs ba{idx, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window,
                   (int)tc, sp_log2};
     const int nch = (int)((g.N + tc - 1) / tc);
     const dim3 bgrid((unsigned)(nbg * nch));
@@ -905,8 +930,9 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     mark(ev, 6, s);
 
     const uint32_t nslots = (uint32_t)(((size_t)g.B * g.Hq * g.N) << sp_log2);
-    PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, nslots, g.N, g.nb, NB,
-                ntiles, sp_log2, scale_log2};
+    const uint32_t npairs_max = (uint32_t)((size_t)g.B * g.Hq * g.N * g.top_k);
+    PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, nslots, npairs_max, g.N,
+                g.nb, NB, ntiles, sp_log2, scale_log2};
     switch (g.bs) {
         case 16: launch_partial<16>(pa, s); break;
         case 32: launch_partial<32>(pa, s); break;
@@ -915,7 +941,7 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     }
     mark(ev, 7, s);
     const int wtiles = (g.N + 63) / 64;
-    WinArgs wa{q, k, vt, idx, part_o, part_lse, out, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
+    WinArgs wa{q, k, vt, idx, part_o, part_lse, rev, out, rows, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
                wtiles, g.B * g.Hq * wtiles, ntiles, sp_log2, scale_log2};
     const int64_t wgrid = ((int64_t)wa.items + 7) / 8 * 8;  // multiple of the XCD count
     hipLaunchKernelGGL(k_window_merge, dim3((unsigned)wgrid), dim3(256), 0, s, wa);

@@ -84,7 +84,8 @@ def test_workspace_sizes_are_plausible(lsa):
     pairs = 14 * 131072 * 16
     vt = 2 * 131072 * 64 * 2                      # V^T copy of both KV heads
     att = lsa.workspace_bytes(p, lsa.OP_ATTEND)
-    assert pairs * (64 * 2 + 4 + 4) + vt <= att < pairs * (64 * 2 + 4 + 4) + vt + (1 << 20)
+    per_pair = 64 * 2 + 4 + 4 + 4                 # partial row, log-mass, pair id, position
+    assert pairs * per_pair + vt <= att < pairs * per_pair + vt + (1 << 20)
     assert lsa.workspace_bytes(p, lsa.OP_SUMMARIZE) == 0
     img = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0)
     assert lsa.workspace_bytes(img, lsa.OP_ATTEND) == 4 * 16 * 16384 * 64 * 2
