@@ -22,7 +22,7 @@
 //           scores b_c reach.
 //   pass 2  hi+lo scores b_c (fp32 accuracy); candidates at or above the
 //           threshold are appended to the query's survivor list in LDS
-//           (~17 per query on the topic workloads; capacity RT_CAP = 24).
+//           (~17 per query on the topic workloads; capacity RT_CAP = 28).
 //   select  each lane of the pair inserts the survivors it found into a
 //           16-entry sorted list of 64-bit keys (score, then lower index);
 //           the two lists are merged and the chosen block ids written in
@@ -38,7 +38,7 @@ namespace lsa {
 
 constexpr int RT_ROWS = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int RT_CH = 32;      // candidates per step
-constexpr int RT_CAP = 24;     // survivor slots per query
+constexpr int RT_CAP = 28;     // survivor slots per query (4 workgroups still fit a CU)
 constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
 constexpr int FB_GRID = 256;   // workgroups of the exact fallback
 
