@@ -387,13 +387,21 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
         m1[r] = -INFINITY;
         m2[r] = -INFINITY;
     }
+    const int nch = (Ewg + RT_CH - 1) / RT_CH;  // chunks of the workgroup
     {
-        // chunk j is staged in buffer j&1; one barrier per chunk
-        u32x4 pre = Ewg > 0 ? stage_load(khi, 0, tid) : u32x4{0u, 0u, 0u, 0u};
-        if (Ewg > 0) stage_store(s_hi[0], tid, pre);
+        // chunk j is staged in buffer j&1, one barrier per chunk; the global
+        // loads run two chunks ahead in two register sets (the loop body is
+        // written twice so that the sets swap roles without copies)
+        u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = r0;
+        if (nch > 0) {
+            r0 = stage_load(khi, 0, tid);
+            stage_store(s_hi[0], tid, r0);
+        }
+        if (nch > 1) r1 = stage_load(khi, RT_CH, tid);
         __syncthreads();
-        for (int cb = 0, j = 0; cb < Ewg; cb += RT_CH, ++j) {
-            if (cb + RT_CH < Ewg) pre = stage_load(khi, cb + RT_CH, tid);
+        auto body = [&](int j, u32x4& r_issue, const u32x4& r_store) {
+            const int cb = j * RT_CH;
+            if (j + 2 < nch) r_issue = stage_load(khi, cb + 2 * RT_CH, tid);
             if (cb < Emax) {
                 bf16x8 A[4];
                 read_cands(s_hi[j & 1], l32, half, A);
@@ -414,8 +422,12 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
                     m1[r] = fmaxf(m1[r], acc[r]);
                 }
             }
-            if (cb + RT_CH < Ewg) stage_store(s_hi[(j + 1) & 1], tid, pre);
+            if (j + 1 < nch) stage_store(s_hi[(j + 1) & 1], tid, r_store);
             __syncthreads();
+        };
+        for (int j = 0; j < nch; j += 2) {
+            body(j, r0, r1);
+            if (j + 1 < nch) body(j + 1, r1, r0);
         }
     }
 
@@ -441,18 +453,25 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
     const int at_lo = qrow * 4, at_hi = ((RT_CAP - 1) * RT_ROWS + qrow) * 4;
     int at = half ? at_hi : at_lo;
     {
-        u32x4 ph = {0u, 0u, 0u, 0u}, pl = ph;
-        if (Ewg > 0) {
-            ph = stage_load(khi, 0, tid);
-            pl = stage_load(klo, 0, tid);
-            stage_store(s_hi[0], tid, ph);
-            stage_store(s_lo[0], tid, pl);
+        // staging as in pass 1, hi and lo parts
+        u32x4 h0 = {0u, 0u, 0u, 0u}, l0 = h0, h1 = h0, l1 = h0;
+        if (nch > 0) {
+            h0 = stage_load(khi, 0, tid);
+            l0 = stage_load(klo, 0, tid);
+            stage_store(s_hi[0], tid, h0);
+            stage_store(s_lo[0], tid, l0);
+        }
+        if (nch > 1) {
+            h1 = stage_load(khi, RT_CH, tid);
+            l1 = stage_load(klo, RT_CH, tid);
         }
         __syncthreads();
-        for (int cb = 0, j = 0; cb < Ewg; cb += RT_CH, ++j) {
-            if (cb + RT_CH < Ewg) {
-                ph = stage_load(khi, cb + RT_CH, tid);
-                pl = stage_load(klo, cb + RT_CH, tid);
+        auto body = [&](int j, u32x4& hi_issue, u32x4& lo_issue, const u32x4& hi_store,
+                        const u32x4& lo_store) {
+            const int cb = j * RT_CH;
+            if (j + 2 < nch) {
+                hi_issue = stage_load(khi, cb + 2 * RT_CH, tid);
+                lo_issue = stage_load(klo, cb + 2 * RT_CH, tid);
             }
             if (cb < Emax) {
                 bf16x8 ch[4], cl[4];
@@ -490,11 +509,15 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
                     }
                 }
             }
-            if (cb + RT_CH < Ewg) {
-                stage_store(s_hi[(j + 1) & 1], tid, ph);
-                stage_store(s_lo[(j + 1) & 1], tid, pl);
+            if (j + 1 < nch) {
+                stage_store(s_hi[(j + 1) & 1], tid, hi_store);
+                stage_store(s_lo[(j + 1) & 1], tid, lo_store);
             }
             __syncthreads();
+        };
+        for (int j = 0; j < nch; j += 2) {
+            body(j, h0, l0, h1, l1);
+            if (j + 1 < nch) body(j + 1, h1, l1, h0, l0);
         }
     }
 
