@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=50,
+                    help="also time single-query decode steps against the workload's cache")
     return ap.parse_args()
 
 
@@ -121,6 +123,39 @@ def cpu_baseline(w, inp, target_s):
             "sample": f"{n} of {R} query rows of {w.name}, uniform without replacement; "
                       f"{wall:.1f} s wall; full layer extrapolated {wall * R / n * 1e3:.0f} ms",
             "ms_per_layer_extrapolated": wall * R / n * 1e3}
+
+
+def decode_bench(lsa, w, q, k, v, steps):
+    """One decode step (lsa_decode) for the last position of the workload's
+    sequence, with the sequence as the key/value cache; steps timed between
+    HIP-synchronised bracket points.  Algorithmic bytes per step: the block
+    means of the eligible blocks of every KV group, plus, per query head, the
+    K and V rows of its routed blocks and window."""
+    import torch
+    B, Hq, Hkv, N, D, bs = w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block
+    p = lsa.params(B, Hq, Hkv, N, D, bs, w.top_k, w.window, 1)
+    kbar = lsa.block_summarize(p, k)
+    qd = q[:, :, N - 1, :].contiguous()
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    idx = torch.empty((B, Hq, w.top_k), dtype=torch.int32, device=q.device)
+    ws = torch.empty(lsa.workspace_bytes(p, lsa.OP_DECODE), dtype=torch.uint8, device=q.device)
+    for _ in range(5):
+        lsa.decode(p, N, qd, k, v, kbar, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        lsa.decode(p, N, qd, k, v, kbar, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    t = N - 1
+    E = max(0, t // bs - w.window // bs + 1)
+    used = int((idx >= 0).sum().item())
+    keys = used * bs + B * Hq * (t - bs * E + 1)
+    nbytes = B * Hkv * E * D * 4 + keys * D * 2 * 2
+    return {"cache_tokens": N, "us_per_step": us, "eligible_blocks": E,
+            "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / 1e3 / us,
+            "hbm_frac": nbytes / 1e3 / us / PEAK_HBM_GBS,
+            "note": "wall time per call, including launch overhead"}
 
 
 def copy_calibration():
@@ -249,6 +284,8 @@ def main():
                   "attend_mfma_frac": f_sel / 1e12 / (attend_ms * 1e-3) / PEAK_BF16_TFLOPS,
                   "routed_pairs": routed_pairs, "stage_ms": breakdown, "stage_roofline": stage_frac},
     }
+    if w.causal and args.decode_steps > 0:
+        result["decode"] = decode_bench(lsa, w, q, k, v, args.decode_steps)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     else:

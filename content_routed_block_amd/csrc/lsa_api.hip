@@ -83,6 +83,7 @@ size_t lsa_workspace_bytes(const lsa_params* p, int32_t op) {
         case LSA_OP_ROUTE: return lsa::route_workspace_bytes(g);
         case LSA_OP_ATTEND: return lsa::attend_workspace_bytes(g);
         case LSA_OP_FORWARD: return forward_ws(g, true);  // enough with or without idx_out
+        case LSA_OP_DECODE: return g.causal ? lsa::decode_workspace_bytes(g, g.N) : (size_t)-1;
         default: return (size_t)-1;
     }
 }
@@ -182,6 +183,31 @@ lsa_status lsa_forward_profiled(const lsa_params* p, const void* q, const void* 
         if (!events[i]) return LSA_ERR_NULL;
     return forward_impl(p, q, k, v, out, idx_out, workspace, workspace_bytes, stream,
                         reinterpret_cast<const hipEvent_t*>(events));
+}
+
+lsa_status lsa_decode(const lsa_params* p, int32_t cache_len, const void* q, const void* k_cache,
+                      const void* v_cache, float* kbar_cache, float* out, int32_t* idx_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (!p) return LSA_ERR_NULL;
+    // the cache geometry is validated as a sequence of cache_len tokens
+    lsa_params pc = *p;
+    pc.seq_len = cache_len;
+    Geometry g;
+    lsa_status st = check_params(&pc, &g);
+    if (st != LSA_OK) return st;
+    if (!p->causal) return LSA_ERR_SHAPE;
+    if (p->seq_len < 1 || p->seq_len > cache_len) return LSA_ERR_SHAPE;
+    if (!q || !k_cache || !v_cache || !kbar_cache || !out || !workspace) return LSA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(kbar_cache, 16) || !aligned(out, 16) || (idx_out && !aligned(idx_out, 16)))
+        return LSA_ERR_ALIGN;
+    if (!aligned(workspace, 256)) return LSA_ERR_ALIGN;
+    if (workspace_bytes < lsa::decode_workspace_bytes(g, cache_len)) return LSA_ERR_WORKSPACE;
+    g.N = p->seq_len;
+    return from_hip(lsa::launch_decode(g, cache_len, static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k_cache),
+                                       static_cast<const uint16_t*>(v_cache), kbar_cache, out,
+                                       idx_out, workspace, static_cast<hipStream_t>(stream)));
 }
 
 const char* lsa_status_str(lsa_status s) {

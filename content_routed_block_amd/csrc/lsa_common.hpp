@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t key_block(uint64_t key) {
 // ---------------------------------------------------------------- causal geometry
 // Routed candidates of causal query position t: the complete blocks that end
 // before the block-aligned window, c in [0, E(t)).
-__device__ __forceinline__ int eligible_blocks(int t, int bs, int window) {
+__host__ __device__ __forceinline__ int eligible_blocks(int t, int bs, int window) {
     int e = t / bs - window / bs + 1;
     return e > 0 ? e : 0;
 }

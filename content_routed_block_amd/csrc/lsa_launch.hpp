@@ -35,6 +35,12 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
                          const uint16_t* v, const int32_t* idx, float* out, void* ws,
                          hipStream_t s, const hipEvent_t* ev = nullptr);
 
+// Single-query decode against a cache of t_max tokens (g.N = tokens filled).
+size_t decode_workspace_bytes(const Geometry& g, int t_max);
+hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, float* kbar, float* out, int32_t* idx_out, void* ws,
+                         hipStream_t s);
+
 // Records profiling event i (if any) on the stream.
 inline void mark(const hipEvent_t* ev, int i, hipStream_t s) {
     if (ev) (void)hipEventRecord(ev[i], s);

@@ -24,7 +24,7 @@ if not os.path.exists(_LIB_PATH):
 
 _lib = ctypes.CDLL(_LIB_PATH)
 
-OP_SUMMARIZE, OP_ROUTE, OP_ATTEND, OP_FORWARD = 0, 1, 2, 3
+OP_SUMMARIZE, OP_ROUTE, OP_ATTEND, OP_FORWARD, OP_DECODE = 0, 1, 2, 3, 4
 STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL", 2: "LSA_ERR_SHAPE", 3: "LSA_ERR_UNSUPPORTED",
           4: "LSA_ERR_ALIGN", 5: "LSA_ERR_WORKSPACE", 6: "LSA_ERR_DEVICE"}
 
@@ -47,6 +47,8 @@ _lib.lsa_sparse_attend.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, 
 _lib.lsa_forward.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
 for _f in ("lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend", "lsa_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
+_lib.lsa_decode.argtypes = [_P, ctypes.c_int32, _v, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
+_lib.lsa_decode.restype = ctypes.c_int
 _lib.lsa_forward_profiled.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v, _v]
 _lib.lsa_forward_profiled.restype = ctypes.c_int
 _lib.lsa_status_str.argtypes = [ctypes.c_int]
@@ -182,6 +184,38 @@ def forward(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     workspace, nbytes = _workspace(p, OP_FORWARD, workspace, q.device)
     _check(_lib.lsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
                             _ptr(workspace), nbytes, _stream(stream)), "lsa_forward")
+    return out, idx
+
+
+def decode(p: LsaParams, cache_len: int, q: torch.Tensor, k_cache: torch.Tensor,
+           v_cache: torch.Tensor, kbar_cache: torch.Tensor, out: Optional[torch.Tensor] = None,
+           idx: Optional[torch.Tensor] = None, want_idx: bool = True,
+           workspace: Optional[torch.Tensor] = None,
+           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One decode step for the query at position p.seq_len - 1 (see lsa_decode).
+
+    q [B, Hq, 64] bf16; k_cache, v_cache [B, Hkv, cache_len, 64] bf16;
+    kbar_cache [B, Hkv, cache_len // block, 64] fp32 (updated in place when
+    p.seq_len is a multiple of the block size)."""
+    q = _bits(q, (p.batch, p.q_heads, p.head_dim), "q")
+    k_cache = _bits(k_cache, (p.batch, p.kv_heads, cache_len, p.head_dim), "k_cache")
+    v_cache = _bits(v_cache, (p.batch, p.kv_heads, cache_len, p.head_dim), "v_cache")
+    if kbar_cache.dtype != torch.float32 or not kbar_cache.is_contiguous() or \
+            tuple(kbar_cache.shape) != (p.batch, p.kv_heads, cache_len // p.block, p.head_dim):
+        raise ValueError("kbar_cache: expected a contiguous fp32 tensor "
+                         f"[{p.batch}, {p.kv_heads}, {cache_len // p.block}, {p.head_dim}]")
+    if out is None:
+        out = torch.empty((p.batch, p.q_heads, p.head_dim), dtype=torch.float32, device=q.device)
+    if idx is None and want_idx:
+        idx = torch.empty((p.batch, p.q_heads, p.top_k), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        pc = LsaParams(*[getattr(p, f) for f, _ in LsaParams._fields_])
+        pc.seq_len = cache_len
+        workspace = torch.empty(workspace_bytes(pc, OP_DECODE), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(_lib.lsa_decode(ctypes.byref(p), cache_len, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                           _ptr(kbar_cache), _ptr(out), _ptr(idx), _ptr(workspace), nbytes,
+                           _stream(stream)), "lsa_decode")
     return out, idx
 
 

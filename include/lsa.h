@@ -72,7 +72,8 @@ enum {
     LSA_OP_SUMMARIZE = 0,
     LSA_OP_ROUTE = 1,
     LSA_OP_ATTEND = 2,
-    LSA_OP_FORWARD = 3
+    LSA_OP_FORWARD = 3,
+    LSA_OP_DECODE = 4     /* p->seq_len read as the cache length */
 };
 
 /* Workspace bytes needed by `op` for these parameters (0 = none needed;
@@ -126,6 +127,30 @@ lsa_status lsa_sparse_attend(const lsa_params *p, const void *q, const void *k,
 lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
                        const void *v, float *out, int32_t *idx_out,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* One decode step: the query at position T-1 (T = p->seq_len, 1 <= T <=
+ * cache_len) attends to a key/value cache with the same selection and
+ * softmax as the prefill path (routing over the complete blocks before the
+ * block-aligned window, top-k with the lower-index tie-break, exact softmax
+ * over the routed blocks and the window [bs*E(T-1), T-1]); the SSA page
+ * ("Other measured evidence") measures such steps against a growing cache
+ * at a fixed selection budget.  causal must be 1.
+ *   q          [B, Hq, D] bf16 (the new token's queries)
+ *   k_cache,   [B, Hkv, cache_len, D] bf16, tokens [0, T) filled
+ *   v_cache
+ *   kbar_cache [B, Hkv, cache_len/bs, D] fp32 block means, in/out: blocks
+ *              complete before the first call must be filled by the caller
+ *              (lsa_block_summarize over the cache); when T is a multiple
+ *              of bs this call writes the mean of block T/bs - 1, which token
+ *              T-1 completes, so consecutive steps keep the cache current.
+ *   out        [B, Hq, D] fp32;  idx_out [B, Hq, top_k] int32 or NULL.
+ * cache_len must be a multiple of bs; workspace: lsa_workspace_bytes(p with
+ * seq_len = cache_len, LSA_OP_DECODE) bytes, enough for every T <= cache_len.
+ * Scores and softmax run in fp32 (no bf16 rounding of probabilities). */
+lsa_status lsa_decode(const lsa_params *p, int32_t cache_len, const void *q,
+                      const void *k_cache, const void *v_cache, float *kbar_cache,
+                      float *out, int32_t *idx_out, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* lsa_forward with stage timing, for profiling tools.  `events` holds
  * LSA_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is
