@@ -51,10 +51,11 @@ def lib():
         L.orc_route_causal.argtypes = [_p, _p] + [_i64] * 8 + [_p, _i64, _p, _p]
         L.orc_route_image.argtypes = [_p, _p] + [_i64] * 6 + [_p, _i64, _p, _p]
         L.orc_route_scores.argtypes = [_p, _p, _p] + [_i64] * 8 + [_p, _i64, _p]
+        L.orc_route_consensus.argtypes = [_p, _p, _p] + [_i64] * 9 + [_p, _i64, _p, _p, _p]
         L.orc_attend.argtypes = [_p, _p, _p] + [_i64] * 9 + [ctypes.c_double, _p, _i64, _p, _p]
         L.orc_forward.argtypes = [_p, _p, _p] + [_i64] * 9 + [ctypes.c_double, _p, _i64, _p, _p]
         for f in ("orc_block_means", "orc_route_causal", "orc_route_image",
-                  "orc_route_scores", "orc_attend", "orc_forward"):
+                  "orc_route_scores", "orc_route_consensus", "orc_attend", "orc_forward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -153,6 +154,75 @@ def route_scores(kbar, rows, *, q=None, qbar=None, block, window=0, causal=1, se
                                   block, window, int(causal), _ptr(r), n, _ptr(out)),
            "route_scores")
     return out
+
+
+def route_consensus(kbar, block, top_k, *, q=None, qbar=None, window=0, causal=1, rows=None,
+                    with_gap=False, with_scores=False):
+    """Consensus routing, one route per KV group, scored by the sum of the
+    group's query heads' routing scores.  Causal: q bf16 bits [B,Hq,N,D],
+    rows (b*Hkv + g)*N + t.  Image mode: qbar fp32 [B,Hq,nb,D], rows
+    (b*Hkv + g)*nb + i.  Returns idx [n_rows, top_k] (or [B,Hkv,P,top_k]
+    when rows is None), then the gap per row and every block's score
+    [n_rows, nb] when asked for."""
+    kbar = _c(kbar, np.float32)
+    B, Hkv, nb, D = kbar.shape
+    if causal:
+        q = _c(q, np.uint16)
+        Hq, N = q.shape[1], q.shape[2]
+        per = N
+    else:
+        qbar = _c(qbar, np.float32)
+        Hq, N = qbar.shape[1], nb * block
+        per = nb
+    r, n = _rows(rows)
+    total = n if r is not None else B * Hkv * per
+    idx = np.empty((total, top_k), dtype=np.int32)
+    gap = np.empty(total, dtype=np.float64) if with_gap else None
+    sc = np.empty((total, nb), dtype=np.float64) if with_scores else None
+    _check(lib().orc_route_consensus(_ptr(q), _ptr(qbar), _ptr(kbar), B, Hq, Hkv, N, D, block,
+                                     top_k, window, int(causal), _ptr(r), n, _ptr(idx),
+                                     _ptr(gap), _ptr(sc)), "route_consensus")
+    if r is None:
+        idx = idx.reshape(B, Hkv, per, top_k)
+        if gap is not None:
+            gap = gap.reshape(B, Hkv, per)
+    res = (idx,) + ((gap,) if with_gap else ()) + ((sc,) if with_scores else ())
+    return res if len(res) > 1 else idx
+
+
+def consensus_rows(rows, q_heads, kv_heads, per):
+    """The group row (b*Hkv + g)*per + p that serves query row
+    (b*Hq + h)*per + p."""
+    rows = np.asarray(rows, dtype=np.int64)
+    bh, p = rows // per, rows % per
+    b, h = bh // q_heads, bh % q_heads
+    return (b * kv_heads + h // (q_heads // kv_heads)) * per + p
+
+
+def forward_consensus(q, k, v, block, top_k, window, causal, scale=0.0, rows=None):
+    """Steps 1-4 with consensus routing: block means, one route per KV group
+    (image mode: per KV group and query block), the group's route shared by
+    its query heads, attention.  Returns (out, sel) shaped as forward's."""
+    q, k, v = (_c(a, np.uint16) for a in (q, k, v))
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    kbar = block_means(k, block)
+    qrows = np.arange(B * Hq * N, dtype=np.int64) if rows is None else _c(rows, np.int64).ravel()
+    if causal:
+        grows = consensus_rows(qrows, Hq, Hkv, N)
+        uniq, inv = np.unique(grows, return_inverse=True)
+        gidx = route_consensus(kbar, block, top_k, q=q, window=window, causal=1, rows=uniq)
+    else:
+        nb = N // block
+        qb = (qrows // N) * nb + (qrows % N) // block
+        grows = consensus_rows(qb, Hq, Hkv, nb)
+        uniq, inv = np.unique(grows, return_inverse=True)
+        gidx = route_consensus(kbar, block, top_k, qbar=block_means(q, block), causal=0, rows=uniq)
+    sel = np.ascontiguousarray(gidx[inv.ravel()])
+    out = attend(q, k, v, sel, block, top_k, window, causal, scale, rows=qrows)
+    if rows is None:
+        return out.reshape(B, Hq, N, D), sel.reshape(B, Hq, N, top_k)
+    return out, sel
 
 
 def attend(q, k, v, sel, block, top_k, window, causal, scale=0.0, rows=None):

@@ -48,7 +48,8 @@
  *     two never overlap, and with every eligible block selected their union
  *     is exactly [0, t] (dense causal attention).
  *   - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
- *     Routing is done per query head.
+ *     Routing is done per query head, or, in consensus mode, once per KV
+ *     group with the sum of the group's heads' scores (orc_route_consensus).
  *   - Image mode (causal == 0): query block i (tokens [i*bs, i*bs+bs)) is
  *     routed with the pooled query mean over all key blocks; every token of
  *     the block attends to the union of the selected blocks; no window.
@@ -274,6 +275,85 @@ int orc_route_scores(const uint16_t *q, const float *qbar, const float *kbar,
             }
             scores[i * nb + c] = s;
         }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Consensus routing, one route per KV group: a group's score for block c is
+ * the sum of the routing scores of the group's query heads,
+ * sum_h <q_h, mu_c> (SSA page, "Complete 10M transformer result": a
+ * cross-head consensus route; here the heads that share one KV head, so
+ * that the route can be shared with them).  Candidates, top-k and tie-break
+ * as in steps 2-3.
+ *   causal != 0: q bf16 [B,Hq,N,D]; rows index (b*Hkv + g)*N + t.
+ *   causal == 0: qbar fp32 [B,Hq,nb,D] pooled queries; rows index
+ *                (b*Hkv + g)*nb + i.
+ * rows NULL = every group row in order.  idx [n_rows, k]; gap (nullable) as
+ * in orc_route_causal; scores (nullable) [n_rows, nb] every block's
+ * consensus score, -inf where the block is not a candidate. */
+int orc_route_consensus(const uint16_t *q, const float *qbar,
+                        const float *kbar, int64_t B, int64_t Hq, int64_t Hkv,
+                        int64_t N, int64_t D, int64_t bs, int64_t k,
+                        int64_t window, int64_t causal, const int64_t *rows,
+                        int64_t n_rows, int32_t *idx, double *gap,
+                        double *scores)
+{
+    if (!kbar || !idx || bs <= 0 || N % bs || Hkv <= 0 || Hq % Hkv || k <= 0)
+        return -1;
+    if (causal ? (!q || window < bs || window % bs) : !qbar)
+        return -1;
+    const int64_t nb = N / bs, rep = Hq / Hkv;
+    const int64_t per = causal ? N : nb;
+    const int64_t total = rows ? n_rows : B * Hkv * per;
+    int bad = 0;
+#pragma omp parallel
+    {
+        cand_t *buf = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nb + 1));
+        if (!buf) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 32)
+        for (int64_t i = 0; i < total; ++i) {
+            if (!buf) continue;
+            const int64_t r = rows ? rows[i] : i;
+            if (r < 0 || r >= B * Hkv * per) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            const int64_t p = r % per, bg = r / per;
+            const int64_t b = bg / Hkv, g = bg % Hkv;
+            const int64_t ncand = causal ? eligible_blocks(p, bs, window) : nb;
+            const float *summ = kbar + bg * nb * D;
+            for (int64_t c = 0; c < ncand; ++c) {
+                double s = 0.0;
+                for (int64_t hh = 0; hh < rep; ++hh) {
+                    const int64_t qr = ((b * Hq + g * rep + hh) * per + p) * D;
+                    double sh = 0.0;
+                    for (int64_t d = 0; d < D; ++d) {
+                        const double qv = causal ? bf16_to_f64(q[qr + d])
+                                                 : (double)qbar[qr + d];
+                        sh += qv * (double)summ[c * D + d];
+                    }
+                    s += sh;
+                }
+                buf[c].s = s;
+                buf[c].c = c;
+            }
+            if (scores)
+                for (int64_t c = 0; c < nb; ++c)
+                    scores[i * nb + c] = c < ncand ? buf[c].s : -INFINITY;
+            qsort(buf, (size_t)ncand, sizeof(cand_t), cand_order);
+            const int64_t keep = ncand < k ? ncand : k;
+            int32_t *out = idx + i * k;
+            for (int64_t j = 0; j < k; ++j)
+                out[j] = j < keep ? (int32_t)buf[j].c : -1;
+            qsort(out, (size_t)keep, sizeof(int32_t), idx_ascending);
+            if (gap)
+                gap[i] = ncand > k ? buf[k - 1].s - buf[k].s : INFINITY;
+        }
+        free(buf);
     }
     return bad ? -1 : 0;
 }

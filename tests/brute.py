@@ -34,7 +34,14 @@ def rank_select(scores, ncand, k):
     return keep
 
 
-def causal_mask(N, bs, window, top_k, q_f64, kbar, rep):
+def _router_heads(h, rep, consensus):
+    """The query heads whose scores are summed to route head h: itself, or,
+    with consensus routing, every head of its KV group."""
+    g = h // rep
+    return range(g * rep, (g + 1) * rep) if consensus else [h]
+
+
+def causal_mask(N, bs, window, top_k, q_f64, kbar, rep, consensus=False):
     """Dense boolean mask [Hq, N, N] of the keys each causal query attends to.
     q_f64: [Hq, N, D]; kbar: float32 [Hkv, nb, D]."""
     Hq = q_f64.shape[0]
@@ -44,22 +51,23 @@ def causal_mask(N, bs, window, top_k, q_f64, kbar, rep):
         g = h // rep
         for t in range(N):
             ncand = max(0, t // bs - wb + 1)
-            s = [float(np.dot(q_f64[h, t], kbar[g, c].astype(np.float64))) for c in range(ncand)]
+            s = [sum(float(np.dot(q_f64[hh, t], kbar[g, c].astype(np.float64)))
+                     for hh in _router_heads(h, rep, consensus)) for c in range(ncand)]
             for c in rank_select(s, ncand, top_k):
                 mask[h, t, c * bs:(c + 1) * bs] = True
             mask[h, t, ncand * bs:t + 1] = True
     return mask
 
 
-def image_mask(N, bs, top_k, qbar, kbar, rep):
+def image_mask(N, bs, top_k, qbar, kbar, rep, consensus=False):
     Hq = qbar.shape[0]
     nb = N // bs
     mask = np.zeros((Hq, N, N), dtype=bool)
     for h in range(Hq):
         g = h // rep
         for i in range(nb):
-            s = [float(np.dot(qbar[h, i].astype(np.float64), kbar[g, c].astype(np.float64)))
-                 for c in range(nb)]
+            s = [sum(float(np.dot(qbar[hh, i].astype(np.float64), kbar[g, c].astype(np.float64)))
+                     for hh in _router_heads(h, rep, consensus)) for c in range(nb)]
             for c in rank_select(s, nb, top_k):
                 mask[h, i * bs:(i + 1) * bs, c * bs:(c + 1) * bs] = True
     return mask
@@ -79,15 +87,16 @@ def masked_softmax_attention(q_f64, k_f64, v_f64, mask, rep, scale):
     return out
 
 
-def forward(q_bits, k_bits, v_bits, bs, top_k, window, causal, scale=None):
-    """End-to-end brute force for one batch element: q [Hq,N,D], k/v [Hkv,N,D]."""
+def forward(q_bits, k_bits, v_bits, bs, top_k, window, causal, scale=None, consensus=False):
+    """End-to-end brute force for one batch element: q [Hq,N,D], k/v [Hkv,N,D].
+    consensus: route once per KV group by the sum of its heads' scores."""
     qf, kf, vf = widen(q_bits), widen(k_bits), widen(v_bits)
     Hq, N, D = qf.shape
     rep = Hq // kf.shape[0]
     scale = 1.0 / np.sqrt(D) if scale is None else scale
     kbar = block_means(kf, bs)
     if causal:
-        mask = causal_mask(N, bs, window, top_k, qf, kbar, rep)
+        mask = causal_mask(N, bs, window, top_k, qf, kbar, rep, consensus)
     else:
-        mask = image_mask(N, bs, top_k, block_means(qf, bs), kbar, rep)
+        mask = image_mask(N, bs, top_k, block_means(qf, bs), kbar, rep, consensus)
     return masked_softmax_attention(qf, kf, vf, mask, rep, scale), mask

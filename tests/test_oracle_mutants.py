@@ -25,6 +25,11 @@ MUTANTS = {
     "keeps_one_block_too_few": ("const int64_t keep = ncand < k ? ncand : k;",
                                 "const int64_t keep = ncand < k ? ncand : k - 1;"),
     "window_excludes_query": ("hi[nr] = t + 1;", "hi[nr] = t;"),
+    "consensus_first_head_only": ("for (int64_t hh = 0; hh < rep; ++hh) {",
+                                  "for (int64_t hh = 0; hh < 1; ++hh) {"),
+    "consensus_interleaved_groups": ("const int64_t qr = ((b * Hq + g * rep + hh) * per + p) * D;",
+                                     "const int64_t qr = ((b * Hq + g + hh * Hkv) * per + p) * D;"),
+    "consensus_scores_last_head": ("s += sh;", "s = sh;"),
 }
 
 

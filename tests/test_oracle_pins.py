@@ -321,3 +321,103 @@ def test_sampled_rows_match_full_run(orc):
         o, s = orc.forward(Q, K, V, bs, k, Wc, causal, rows=rows)
         np.testing.assert_array_equal(o, full_o.reshape(-1, D)[rows])
         np.testing.assert_array_equal(s, full_s.reshape(-1, k)[rows])
+
+
+# ---------------------------------------------------------------- consensus routing
+# One route per KV group, scored by the sum of the group's query heads'
+# routing scores (SSA page, "Complete 10M transformer result": a cross-head
+# consensus route).
+
+@pytest.mark.parametrize("bs,W,k,Hq,Hkv", [(16, 32, 3, 4, 2), (8, 16, 2, 3, 1), (32, 64, 1, 4, 1)])
+def test_consensus_matches_rank_brute_force(orc, bs, W, k, Hq, Hkv):
+    rng = np.random.default_rng(bs * 10 + Hq)
+    N, D = 256, 16
+    Q = rand_bits(rng, (1, Hq, N, D))
+    K = rand_bits(rng, (1, Hkv, N, D))
+    kbar = orc.block_means(K, bs)
+    kbar_np = brute.block_means(brute.widen(K), bs)
+    idx, gap = orc.route_consensus(kbar, bs, k, q=Q, window=W, causal=1, with_gap=True)
+    assert idx.shape == (1, Hkv, N, k)
+    qf = brute.widen(Q)
+    rep = Hq // Hkv
+    for g in range(Hkv):
+        for t in range(N):
+            E = max(0, t // bs - W // bs + 1)
+            s = [sum(float(np.dot(qf[0, h, t], kbar_np[0, g, c].astype(np.float64)))
+                     for h in range(g * rep, (g + 1) * rep)) for c in range(E)]
+            keep = brute.rank_select(s, E, k)
+            assert list(idx[0, g, t]) == keep + [-1] * (k - len(keep)), (g, t)
+            if E > k:
+                ss = sorted(s, reverse=True)
+                assert gap[0, g, t] == pytest.approx(ss[k - 1] - ss[k], abs=1e-12)
+            else:
+                assert gap[0, g, t] == math.inf
+
+
+def test_consensus_image_matches_rank_brute_force(orc):
+    rng = np.random.default_rng(31)
+    bs, k, Hq, Hkv, N, D = 16, 3, 6, 2, 256, 16
+    Q = rand_bits(rng, (1, Hq, N, D))
+    K = rand_bits(rng, (1, Hkv, N, D))
+    qbar = orc.block_means(Q, bs)
+    kbar = orc.block_means(K, bs)
+    idx = orc.route_consensus(kbar, bs, k, qbar=qbar, causal=0)
+    nb, rep = N // bs, Hq // Hkv
+    for g in range(Hkv):
+        for i in range(nb):
+            s = [sum(float(np.dot(qbar[0, h, i].astype(np.float64), kbar[0, g, c].astype(np.float64)))
+                     for h in range(g * rep, (g + 1) * rep)) for c in range(nb)]
+            assert list(idx[0, g, i]) == brute.rank_select(s, nb, k), (g, i)
+
+
+def test_consensus_with_one_head_per_group_is_per_head_routing(orc):
+    rng = np.random.default_rng(32)
+    bs, W, k, N, D = 16, 32, 3, 512, 32
+    Q, K = rand_bits(rng, (2, 3, N, D)), rand_bits(rng, (2, 3, N, D))
+    kbar = orc.block_means(K, bs)
+    np.testing.assert_array_equal(orc.route_consensus(kbar, bs, k, q=Q, window=W, causal=1),
+                                  orc.route_causal(Q, kbar, bs, k, W))
+    qbar = orc.block_means(Q, bs)
+    np.testing.assert_array_equal(orc.route_consensus(kbar, bs, k, qbar=qbar, causal=0),
+                                  orc.route_image(qbar, kbar, k))
+
+
+def test_consensus_of_identical_heads_is_their_own_route(orc):
+    """A group whose heads are copies of one query routes as that query does
+    (the summed score is a positive multiple of it); groups are contiguous
+    head ranges, so distinct queries per group keep distinct routes."""
+    rng = np.random.default_rng(33)
+    bs, W, k, N, D, rep = 16, 32, 4, 512, 32, 3
+    base = rand_bits(rng, (1, 2, N, D))
+    Q = np.repeat(base, rep, axis=1)                    # heads 0-2 = base 0, 3-5 = base 1
+    K = rand_bits(rng, (1, 2, N, D))
+    kbar = orc.block_means(K, bs)
+    got = orc.route_consensus(kbar, bs, k, q=Q, window=W, causal=1)
+    want = orc.route_causal(base, kbar, bs, k, W)       # one head per KV head
+    np.testing.assert_array_equal(got, want)
+
+
+def test_consensus_invariant_under_head_order_within_group(orc):
+    rng = np.random.default_rng(34)
+    bs, W, k, N, D = 16, 32, 3, 384, 16
+    Q, K = rand_bits(rng, (1, 4, N, D)), rand_bits(rng, (1, 2, N, D))
+    kbar = orc.block_means(K, bs)
+    a = orc.route_consensus(kbar, bs, k, q=Q, window=W, causal=1)
+    b = orc.route_consensus(kbar, bs, k, q=Q[:, [1, 0, 3, 2]], window=W, causal=1)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_consensus_end_to_end_matches_brute_force(orc, causal):
+    rng = np.random.default_rng(35 + causal)
+    bs, N, D = 16, 256, 16
+    Hq, Hkv = 4, 2
+    k, W = (3, 32) if causal else (4, 0)
+    Q, K, V = rand_bits(rng, (1, Hq, N, D)), rand_bits(rng, (1, Hkv, N, D)), rand_bits(rng, (1, Hkv, N, D))
+    out, sel = orc.forward_consensus(Q, K, V, bs, k, W, causal)
+    want, mask = brute.forward(Q[0], K[0], V[0], bs, k, W, causal, consensus=True)
+    np.testing.assert_allclose(out[0], want, rtol=1e-6, atol=2e-7)
+    for g in range(Hkv):                                # the group shares one route
+        for h in range(g * 2, g * 2 + 2):
+            np.testing.assert_array_equal(sel[0, h], sel[0, g * 2])
+            np.testing.assert_array_equal(mask[h], mask[g * 2])
