@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--consensus-steps", type=int, default=10,
+                    help="also time the layer with consensus routing (one route per KV group)")
     ap.add_argument("--decode-steps", type=int, default=50,
                     help="also time single-query decode steps against the workload's cache")
     return ap.parse_args()
@@ -156,6 +158,37 @@ def decode_bench(lsa, w, q, k, v, steps):
             "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / 1e3 / us,
             "hbm_frac": nbytes / 1e3 / us / PEAK_HBM_GBS,
             "note": "wall time per call, including launch overhead"}
+
+
+def consensus_bench(lsa, w, q, k, v, steps):
+    """The same layer with consensus routing (one route per KV group, scored
+    by the sum of its query heads' scores): ms per layer, stage times and
+    selected-key TFLOP/s (every query head attends through its group's
+    route)."""
+    import torch
+    p = lsa.params(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.top_k,
+                   w.window, w.causal, consensus=1)
+    out = torch.empty((w.batch, w.q_heads, w.seq_len, w.head_dim), dtype=torch.float32,
+                      device=q.device)
+    idx = torch.empty(lsa.idx_shape(p), dtype=torch.int32, device=q.device)
+    ws = torch.empty(lsa.workspace_bytes(p, lsa.OP_FORWARD), dtype=torch.uint8, device=q.device)
+    for _ in range(3):
+        lsa.forward(p, q, k, v, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    per_head = np.repeat(idx.cpu().numpy(), w.q_heads // w.kv_heads, axis=1)
+    f_routed, f_window, _ = selected_flops(w, per_head)
+    events = [lsa.StageEvents() for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lsa.forward_profiled(p, q, k, v, events[i], out, idx, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    stage = np.array([e.stage_ms() for e in events]).mean(axis=0)
+    for e in events:
+        e.close()
+    return {"ms_per_layer": ms, "selected_tflop": (f_routed + f_window) / 1e12,
+            "tflops": (f_routed + f_window) / 1e12 / (ms * 1e-3),
+            "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
 
 
 def copy_calibration():
@@ -284,6 +317,8 @@ def main():
                   "attend_mfma_frac": f_sel / 1e12 / (attend_ms * 1e-3) / PEAK_BF16_TFLOPS,
                   "routed_pairs": routed_pairs, "stage_ms": breakdown, "stage_roofline": stage_frac},
     }
+    if args.consensus_steps > 0 and w.q_heads > w.kv_heads:
+        result["consensus"] = consensus_bench(lsa, w, q, k, v, args.consensus_steps)
     if w.causal and args.decode_steps > 0:
         result["decode"] = decode_bench(lsa, w, q, k, v, args.decode_steps)
     if args.cpu_seconds > 0:

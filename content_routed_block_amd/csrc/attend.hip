@@ -219,13 +219,14 @@ __device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int n
 
 // ------------------------------------------------------------ bucketing
 struct BucketArgs {
-    const int32_t* idx;  // [B,Hq,N,top_k]
+    const int32_t* idx;  // [B,Hq,N,top_k]; group_route: [B,Hkv,N,top_k]
     uint32_t* counts;    // [NB]
     uint32_t* cursor;    // [NB]
     uint32_t* pairs;     // [total pairs]
     uint32_t* rev;       // [top_k][rows], slot-major: position of pair (row, slot), ~0 if unused
     int64_t rows;        // B * Hq * N
     int Hq, Hkv, N, bs, nb, top_k, window, tchunk, sp_log2;
+    int group_route;     // 1: one route per KV group, shared by its query heads
 };
 
 // Writes one row's entries of the slot-major position table, so that the
@@ -260,8 +261,9 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     for (int i = tid; i < rep * span; i += 256) {
         const int hh = i / span, t = t0 + (i - hh * span);
         const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
+        const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
         int c[kMaxTopK];
-        uint32_t m = row_used(a.idx + row * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
+        uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
         uint32_t posv[kMaxTopK];
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s) {
@@ -294,8 +296,9 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     for (int i = tid; i < rep * span; i += 256) {
         const int hh = i / span, t = t0 + (i - hh * span);
         const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
+        const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
         int c[kMaxTopK];
-        uint32_t m = row_used(a.idx + row * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
+        uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, eligible_blocks(t, a.bs, a.window), c);
         // all LDS reservations first (their latencies overlap), then the stores
         uint32_t posv[kMaxTopK];
 #pragma unroll
@@ -523,7 +526,7 @@ struct WinArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* vt;
-    const int32_t* idx;
+    const int32_t* idx;  // [B,Hq,N,top_k]; group_route: [B,Hkv,N,top_k]
     const uint16_t* part_o;
     const float* part_lse;
     const uint32_t* rev;  // [top_k][rows]
@@ -531,6 +534,7 @@ struct WinArgs {
     int64_t rows;
     int Hq, Hkv, N, bs, top_k, window, tiles, items, ntiles, sp_log2;
     float scale_log2;
+    int group_route;
 };
 
 // One workgroup per (query head, 64 positions); wave w owns rows
@@ -577,7 +581,8 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     load_q_operand(a.q + row * kD, lane, valid, Bq);
     // the row's routed slots, read now so the loads overlap the window work
     int csel[kMaxTopK];
-    const uint32_t used = valid ? row_used(a.idx + row * a.top_k, a.top_k, E, csel) : 0u;
+    const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
+    const uint32_t used = valid ? row_used(a.idx + irow * a.top_k, a.top_k, E, csel) : 0u;
     f32x4 o[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -717,11 +722,12 @@ struct ImgArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* vt;
-    const int32_t* idx;  // [B,Hq,nb,top_k]
+    const int32_t* idx;  // [B,Hq,nb,top_k]; group_route: [B,Hkv,nb,top_k]
     float* out;
     int Hq, Hkv, N, nb, top_k, ntiles;
     int64_t n_qblocks;   // B*Hq*nb
     float scale_log2;
+    int group_route;
 };
 
 // One wave per 16-token query block (block size 16).  The selected blocks
@@ -745,7 +751,8 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
     const int64_t row = bh * a.N + t;
 
     // the used slots of this query block's idx row (wave-uniform)
-    const int32_t* ir = a.idx + (active ? qb : 0) * a.top_k;
+    const int64_t irow = a.group_route ? bg * a.nb + i : qb;
+    const int32_t* ir = a.idx + (active ? irow : 0) * a.top_k;
     int csel[kMaxTopK];
     const uint32_t used = active ? row_used(ir, a.top_k, a.nb, csel) : 0u;
     const int nused = __builtin_popcount(used);
@@ -888,7 +895,7 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
                        ntiles);
     if (!g.causal) {
         ImgArgs a{q, k, vt, idx, out, g.Hq, g.Hkv, g.N, g.nb, g.top_k, ntiles,
-                  (int64_t)g.B * g.Hq * g.nb, scale_log2};
+                  (int64_t)g.B * g.Hq * g.nb, scale_log2, g.consensus};
         const unsigned grid = (unsigned)((a.n_qblocks + 3) / 4);
         for (int i = 4; i < 8; ++i) mark(ev, i, s);
         hipLaunchKernelGGL(k_image_attend, dim3(grid), dim3(256), 0, s, a);
@@ -917,7 +924,7 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     tc = std::min<int64_t>((tc + 63) / 64 * 64, g.N);
     const int64_t rows = (int64_t)g.B * g.Hq * g.N;
     BucketArgs ba{idx, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window,
-                  (int)tc, sp_log2};
+                  (int)tc, sp_log2, g.consensus};
     const int nch = (int)((g.N + tc - 1) / tc);
     const dim3 bgrid((unsigned)(nbg * nch));
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
@@ -942,7 +949,7 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     mark(ev, 7, s);
     const int wtiles = (g.N + 63) / 64;
     WinArgs wa{q, k, vt, idx, part_o, part_lse, rev, out, rows, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
-               wtiles, g.B * g.Hq * wtiles, ntiles, sp_log2, scale_log2};
+               wtiles, g.B * g.Hq * wtiles, ntiles, sp_log2, scale_log2, g.consensus};
     const int64_t wgrid = ((int64_t)wa.items + 7) / 8 * 8;  // multiple of the XCD count
     hipLaunchKernelGGL(k_window_merge, dim3((unsigned)wgrid), dim3(256), 0, s, wa);
     mark(ev, 8, s);

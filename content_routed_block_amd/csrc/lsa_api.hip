@@ -22,6 +22,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
         return LSA_ERR_SHAPE;
     if (p->q_heads % p->kv_heads) return LSA_ERR_SHAPE;
     if (p->causal != 0 && p->causal != 1) return LSA_ERR_SHAPE;
+    if (p->consensus != 0 && p->consensus != 1) return LSA_ERR_SHAPE;
     if (p->seq_len % p->block) return LSA_ERR_SHAPE;
     if (p->causal) {
         if (p->window < p->block || p->window % p->block) return LSA_ERR_SHAPE;
@@ -52,6 +53,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     g->top_k = p->top_k;
     g->window = p->window;
     g->causal = p->causal;
+    g->consensus = p->consensus;
     g->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
     return LSA_OK;
 }
@@ -59,7 +61,8 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 size_t route_idx_bytes(const Geometry& g) {
-    return (size_t)g.B * g.Hq * (g.causal ? (size_t)g.N : (size_t)g.nb) * g.top_k * 4;
+    return (size_t)g.B * (g.consensus ? g.Hkv : g.Hq) * (g.causal ? (size_t)g.N : (size_t)g.nb) *
+           g.top_k * 4;
 }
 
 size_t forward_ws(const Geometry& g, bool with_idx) {
@@ -83,7 +86,8 @@ size_t lsa_workspace_bytes(const lsa_params* p, int32_t op) {
         case LSA_OP_ROUTE: return lsa::route_workspace_bytes(g);
         case LSA_OP_ATTEND: return lsa::attend_workspace_bytes(g);
         case LSA_OP_FORWARD: return forward_ws(g, true);  // enough with or without idx_out
-        case LSA_OP_DECODE: return g.causal ? lsa::decode_workspace_bytes(g, g.N) : (size_t)-1;
+        case LSA_OP_DECODE:
+            return g.causal && !g.consensus ? lsa::decode_workspace_bytes(g, g.N) : (size_t)-1;
         default: return (size_t)-1;
     }
 }
@@ -196,6 +200,7 @@ lsa_status lsa_decode(const lsa_params* p, int32_t cache_len, const void* q, con
     lsa_status st = check_params(&pc, &g);
     if (st != LSA_OK) return st;
     if (!p->causal) return LSA_ERR_SHAPE;
+    if (p->consensus) return LSA_ERR_UNSUPPORTED;
     if (p->seq_len < 1 || p->seq_len > cache_len) return LSA_ERR_SHAPE;
     if (!q || !k_cache || !v_cache || !kbar_cache || !out || !workspace) return LSA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||

@@ -11,7 +11,8 @@ namespace lsa {
 
 struct Geometry {
     int B, Hq, Hkv, N, D, bs, nb, top_k, window, causal;
-    float scale;  // resolved (> 0)
+    int consensus;  // 1: one route per KV group (idx heads = Hkv)
+    float scale;    // resolved (> 0)
 };
 
 // x [BH, N, 64] bf16 -> xbar [BH, N/bs, 64] fp32

@@ -29,6 +29,12 @@
 //           ascending order.
 // Queries whose survivor list overflows (ties, adversarial inputs) are
 // queued and redone exactly by k_route_fallback.
+//
+// Consensus routing (one route per KV group, scored by the sum of the
+// group's query heads' scores; SSA page, "Complete 10M transformer result")
+// runs the same kernels over the group rows, with the group's summed query
+// formed in fp32 by k_group_query and fed as a hi + lo bf16 pair like the
+// pooled image-mode query.
 #include <math.h>
 
 #include "lsa_common.hpp"
@@ -43,14 +49,14 @@ constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), con
 constexpr int FB_GRID = 256;   // workgroups of the exact fallback
 
 struct RouteArgs {
-    const uint16_t* q;    // causal: bf16 [B,Hq,N,64]
-    const float* qbar;    // image: fp32 [B,Hq,nb,64]
+    const uint16_t* q;    // bf16 queries [B,Hq,N,64] (QF32 = false)
+    const float* qbar;    // fp32 queries [B,Hq,P,64] (QF32 = true: pooled, or group sums)
     const float* kbar;    // [B,Hkv,nb,64]
     const uint16_t* khi;  // bf16 hi part of kbar [B*Hkv][nb_pad][64]
     const uint16_t* klo;  // bf16 lo part (kbar - hi) [B*Hkv][nb_pad][64]
     const float* pk;      // prefix max over c of |kbar_c| [B*Hkv][nb]
     const float* plo;     // prefix max over c of |lo_c| [B*Hkv][nb]
-    int32_t* idx;         // [B,Hq,P,top_k]
+    int32_t* idx;         // [B,Hq,P,top_k] (Hq = routed heads: Hkv with consensus)
     uint32_t* ovf_count;  // queued overflow rows
     uint32_t* ovf_rows;   // [B*Hq*P]
     float* fb_scratch;    // [FB_GRID][nb]
@@ -288,7 +294,7 @@ __device__ __forceinline__ int clamp_i32(int x, int lo, int hi) {
 // ------------------------------------------------------------ main kernel
 // Each wave is independent (its own 32 rows and survivor lists); the
 // workgroup only shares the staged candidate chunks.
-template <bool CAUSAL>
+template <bool CAUSAL, bool QF32>
 __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_hi[2][RT_CH * RT_PITCH];
     __shared__ __attribute__((aligned(16))) __bf16 s_lo[2][RT_CH * RT_PITCH];
@@ -329,12 +335,12 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
     // ---- the query as the B operand (B[d][t] = Q[t][d]): lane holds dims
     // 8*half + 16*ks .. +7 of row rq.
     bf16x8 Bq[4];
-    bf16x8 Bql[4];  // image mode: lo part of the pooled query
+    bf16x8 Bql[4];  // fp32 queries: the lo part
     float qn, qln;
     {
         float s2 = 0.f, l2 = 0.f;
         if (rq < P) {
-            if (CAUSAL) {
+            if (!QF32) {
                 const uint16_t* qp = a.q + ((int64_t)bh * a.N + rq) * kD + 8 * half;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
@@ -347,7 +353,7 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
                     Bql[ks] = bf16x8{};
                 }
             } else {
-                const float* qp = a.qbar + ((int64_t)bh * a.nb + rq) * kD + 8 * half;
+                const float* qp = a.qbar + ((int64_t)bh * P + rq) * kD + 8 * half;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const f32x4 x0 = *reinterpret_cast<const f32x4*>(qp + 16 * ks);
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
                 for (int ks = 0; ks < 4; ++ks) {
                     acc = mfma32(ch[ks], Bq[ks], acc);
                     acc = mfma32(cl[ks], Bq[ks], acc);
-                    if (!CAUSAL) acc = mfma32(ch[ks], Bql[ks], acc);
+                    if (QF32) acc = mfma32(ch[ks], Bql[ks], acc);
                 }
                 const int cl0 = cb + 4 * half;
                 if (cb < Efull) {
@@ -562,7 +568,7 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
 // One workgroup per queued row: fp32 scores of every candidate into a
 // private scratch row, then top_k rounds of "largest key below the previous
 // one".  Slow but exact for any input (ties included).
-template <bool CAUSAL>
+template <bool CAUSAL, bool QF32>
 __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
     __shared__ float s_q[kD];
     __shared__ uint64_t s_red[4];
@@ -577,8 +583,8 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
         const float* kb = a.kbar + (int64_t)(b * a.Hkv + g) * a.nb * kD;
         const int E = row_candidates(CAUSAL, row, a.P, a.bs, a.window, a.nb);
         if (tid < kD) {
-            s_q[tid] = CAUSAL ? bf16_bits_to_f32(a.q[((int64_t)bh * a.N + row) * kD + tid])
-                              : a.qbar[((int64_t)bh * a.nb + row) * kD + tid];
+            s_q[tid] = QF32 ? a.qbar[((int64_t)bh * a.P + row) * kD + tid]
+                            : bf16_bits_to_f32(a.q[((int64_t)bh * a.N + row) * kD + tid]);
         }
         __syncthreads();
         for (int c = tid; c < E; c += 256) {
@@ -630,13 +636,50 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
     }
 }
 
+// ------------------------------------------------------------ group queries
+// Consensus routing: out[b, g, p, :] = sum over the group's heads h of
+// in[b, h, p, :], in fp32 (heads in ascending order).  One thread per 8
+// dims of a row.  T = uint16_t (bf16 bits) or float.
+template <typename T>
+__global__ __launch_bounds__(256) void k_group_query(const T* __restrict__ in,
+                                                     float* __restrict__ out, int Hq, int Hkv,
+                                                     int P, int64_t n_threads) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_threads) return;
+    const int rep = Hq / Hkv;
+    const int64_t row = i >> 3;  // (b*Hkv + g)*P + p
+    const int d0 = (int)(i & 7) * 8;
+    const int64_t p = row % P, bg = row / P;
+    const int64_t b = bg / Hkv, g = bg % Hkv;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < rep; ++hh) {
+        const T* src = in + ((b * Hq + g * rep + hh) * P + p) * kD + d0;
+        float f[8];
+        if constexpr (sizeof(T) == 2) {
+            unpack8(*reinterpret_cast<const u32x4*>(src), f);
+        } else {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+            f[0] = x0[0]; f[1] = x0[1]; f[2] = x0[2]; f[3] = x0[3];
+            f[4] = x1[0]; f[5] = x1[1]; f[6] = x1[2]; f[7] = x1[3];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += f[j];
+    }
+    float* dst = out + row * kD + d0;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
 // ------------------------------------------------------------ host side
+static int route_heads(const Geometry& g) { return g.consensus ? g.Hkv : g.Hq; }
+
 static size_t route_rows(const Geometry& g) {
-    return (size_t)g.B * g.Hq * (g.causal ? (size_t)g.N : (size_t)g.nb);
+    return (size_t)g.B * route_heads(g) * (g.causal ? (size_t)g.N : (size_t)g.nb);
 }
 
 struct RouteLayout {
-    size_t ovf_rows, fb, qbar, khi, klo, pk, total;
+    size_t ovf_rows, fb, qbar, qsum, khi, klo, pk, total;
     int nb_pad;
 };
 
@@ -648,6 +691,7 @@ static RouteLayout route_layout(const Geometry& g) {
     L.ovf_rows = off; off += align_up(route_rows(g) * 4, 256);
     L.fb = off;       off += align_up((size_t)FB_GRID * g.nb * 4, 256);
     L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * g.nb * kD * 4, 256);
+    L.qsum = off;     if (g.consensus) off += align_up(route_rows(g) * kD * 4, 256);
     L.khi = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
     L.klo = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
     L.pk = off;       off += align_up(2 * nbg * g.nb * 4, 256);  // pk then plo
@@ -656,6 +700,14 @@ static RouteLayout route_layout(const Geometry& g) {
 }
 
 size_t route_workspace_bytes(const Geometry& g) { return route_layout(g).total; }
+
+template <bool CAUSAL, bool QF32>
+static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
+                                 const hipEvent_t* ev) {
+    hipLaunchKernelGGL((k_route<CAUSAL, QF32>), grid, dim3(256), 0, s, a);
+    mark(ev, 2, s);
+    hipLaunchKernelGGL((k_route_fallback<CAUSAL, QF32>), dim3(FB_GRID), dim3(256), 0, s, a);
+}
 
 hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar, int32_t* idx,
                         void* ws, hipStream_t s, const hipEvent_t* ev) {
@@ -667,19 +719,21 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     a.ovf_rows = reinterpret_cast<uint32_t*>(base + L.ovf_rows);
     a.fb_scratch = reinterpret_cast<float*>(base + L.fb);
     float* qbar = g.causal ? nullptr : reinterpret_cast<float*>(base + L.qbar);
+    float* qsum = g.consensus ? reinterpret_cast<float*>(base + L.qsum) : nullptr;
     uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
     uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
     float* pk = reinterpret_cast<float*>(base + L.pk);
     float* plo = pk + (size_t)nbg * g.nb;
+    const int heads = route_heads(g);
     a.q = q;
-    a.qbar = qbar;
+    a.qbar = g.consensus ? qsum : qbar;
     a.kbar = kbar;
     a.khi = khi;
     a.klo = klo;
     a.pk = pk;
     a.plo = plo;
     a.idx = idx;
-    a.Hq = g.Hq;
+    a.Hq = heads;  // rows of the router: (b, routed head, position)
     a.Hkv = g.Hkv;
     a.N = g.N;
     a.bs = g.bs;
@@ -688,7 +742,7 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     a.window = g.window;
     a.P = g.causal ? g.N : g.nb;
     a.tiles = (a.P + RT_ROWS - 1) / RT_ROWS;
-    a.items = g.B * g.Hq * a.tiles;
+    a.items = g.B * heads * a.tiles;
     a.nb_pad = L.nb_pad;
     hipError_t e = launch_fill_u32(a.ovf_count, 1, 0u, s);
     if (e != hipSuccess) return e;
@@ -696,20 +750,27 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
         e = launch_summarize(q, qbar, g.B * g.Hq, g.N, g.bs, s);
         if (e != hipSuccess) return e;
     }
+    if (g.consensus) {
+        const int64_t n = (int64_t)route_rows(g) * 8;
+        const dim3 gq((unsigned)((n + 255) / 256));
+        if (g.causal)
+            hipLaunchKernelGGL(k_group_query<uint16_t>, gq, dim3(256), 0, s, q, qsum, g.Hq, g.Hkv,
+                               a.P, n);
+        else
+            hipLaunchKernelGGL(k_group_query<float>, gq, dim3(256), 0, s, qbar, qsum, g.Hq, g.Hkv,
+                               a.P, n);
+    }
     const int64_t prep_threads = (int64_t)nbg * L.nb_pad * 8;
     hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
                        kbar, khi, klo, pk, plo, nbg, g.nb, L.nb_pad);
     hipLaunchKernelGGL(k_prefix_max, dim3((unsigned)(2 * nbg)), dim3(1024), 0, s, pk, g.nb);
     const dim3 grid((unsigned)(((int64_t)a.items + 7) / 8 * 8));  // a multiple of the XCD count
-    if (g.causal) {
-        hipLaunchKernelGGL(k_route<true>, grid, dim3(256), 0, s, a);
-        mark(ev, 2, s);
-        hipLaunchKernelGGL(k_route_fallback<true>, dim3(FB_GRID), dim3(256), 0, s, a);
-    } else {
-        hipLaunchKernelGGL(k_route<false>, grid, dim3(256), 0, s, a);
-        mark(ev, 2, s);
-        hipLaunchKernelGGL(k_route_fallback<false>, dim3(FB_GRID), dim3(256), 0, s, a);
-    }
+    if (g.causal && !g.consensus)
+        launch_route_kernels<true, false>(a, grid, s, ev);
+    else if (g.causal)
+        launch_route_kernels<true, true>(a, grid, s, ev);
+    else
+        launch_route_kernels<false, true>(a, grid, s, ev);
     mark(ev, 3, s);
     return hipGetLastError();
 }

@@ -34,7 +34,8 @@ class LsaParams(ctypes.Structure):
                 ("kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("causal", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("consensus", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(LsaParams)
@@ -82,9 +83,16 @@ def library():
 
 
 def params(batch, q_heads, kv_heads, seq_len, head_dim=64, block=64, top_k=16, window=512,
-           causal=1, scale=0.0) -> LsaParams:
+           causal=1, scale=0.0, consensus=0) -> LsaParams:
     return LsaParams(batch, q_heads, kv_heads, seq_len, head_dim, block, top_k, window, causal,
-                     float(scale))
+                     float(scale), consensus)
+
+
+def idx_shape(p: LsaParams):
+    """Shape of the routing output: [B, heads, rows, top_k] with heads = Hq
+    (Hkv with consensus routing) and rows = N (N / block in image mode)."""
+    heads = p.kv_heads if p.consensus else p.q_heads
+    return (p.batch, heads, p.seq_len if p.causal else p.seq_len // p.block, p.top_k)
 
 
 def workspace_bytes(p: LsaParams, op: int) -> int:
@@ -109,6 +117,14 @@ def _bits(t: torch.Tensor, shape, name) -> torch.Tensor:
         raise TypeError(f"{name}: expected bf16 data, got {t.dtype}")
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _tensor(t: torch.Tensor, dtype, shape, name) -> torch.Tensor:
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous GPU {dtype} tensor")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
@@ -143,10 +159,10 @@ def route_topk(p: LsaParams, q: torch.Tensor, kbar: torch.Tensor,
                idx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
-    nb = p.seq_len // p.block
-    rows = p.seq_len if p.causal else nb
+    _tensor(kbar, torch.float32, (p.batch, p.kv_heads, p.seq_len // p.block, p.head_dim), "kbar")
     if idx is None:
-        idx = torch.empty((p.batch, p.q_heads, rows, p.top_k), dtype=torch.int32, device=q.device)
+        idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
+    _tensor(idx, torch.int32, idx_shape(p), "idx")
     workspace, nbytes = _workspace(p, OP_ROUTE, workspace, q.device)
     _check(_lib.lsa_route_topk(ctypes.byref(p), _ptr(q), _ptr(kbar), _ptr(idx), _ptr(workspace),
                                nbytes, _stream(stream)), "lsa_route_topk")
@@ -159,9 +175,11 @@ def sparse_attend(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
     k = _bits(k, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "k")
     v = _bits(v, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "v")
+    _tensor(idx, torch.int32, idx_shape(p), "idx")
     if out is None:
         out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
                           device=q.device)
+    _tensor(out, torch.float32, (p.batch, p.q_heads, p.seq_len, p.head_dim), "out")
     workspace, nbytes = _workspace(p, OP_ATTEND, workspace, q.device)
     _check(_lib.lsa_sparse_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
                                   _ptr(workspace), nbytes, _stream(stream)), "lsa_sparse_attend")
@@ -178,9 +196,11 @@ def forward(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if out is None:
         out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
                           device=q.device)
+    _tensor(out, torch.float32, (p.batch, p.q_heads, p.seq_len, p.head_dim), "out")
     if idx is None and want_idx:
-        rows = p.seq_len if p.causal else p.seq_len // p.block
-        idx = torch.empty((p.batch, p.q_heads, rows, p.top_k), dtype=torch.int32, device=q.device)
+        idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
+    if idx is not None:
+        _tensor(idx, torch.int32, idx_shape(p), "idx")
     workspace, nbytes = _workspace(p, OP_FORWARD, workspace, q.device)
     _check(_lib.lsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
                             _ptr(workspace), nbytes, _stream(stream)), "lsa_forward")

@@ -13,6 +13,7 @@
  *   q    [B, Hq,  N, D] bf16      k, v [B, Hkv, N, D] bf16
  *   kbar [B, Hkv, N/bs, D] fp32   (block means)
  *   idx  causal: [B, Hq, N, top_k] int32; image mode: [B, Hq, N/bs, top_k]
+ *        (consensus routing: Hkv in place of Hq, one route per KV group)
  *   out  [B, Hq, N, D] fp32
  * Query head h reads KV head h / (Hq / Hkv) (grouped-query attention with
  * contiguous head groups).
@@ -55,6 +56,8 @@ typedef struct lsa_params {
     int32_t window;    /* causal: a multiple of block, >= block; image mode: 0 */
     int32_t causal;    /* 1: per-query routing + causal window; 0: image mode */
     float scale;       /* softmax scale; <= 0 selects 1/sqrt(D) */
+    int32_t consensus; /* 0: a route per query head; 1: one route per KV group,
+                          shared by the group's query heads (see lsa_route_topk) */
 } lsa_params;
 
 typedef enum lsa_status {
@@ -101,7 +104,14 @@ lsa_status lsa_block_summarize(const lsa_params *p, const void *x, int32_t heads
  *   to its fp32 mean and scored against all N/bs key blocks (LLSA page,
  *   "Minimum Usage").  idx [B, Hq, N/bs, top_k].
  * Each idx row lists min(top_k, #candidates) block ids in ascending order,
- * then -1 padding. */
+ * then -1 padding.
+ * Consensus routing (consensus = 1; SSA page, "Complete 10M transformer
+ *   result": a cross-head consensus route): one route per KV group, scored
+ *   by the sum of the routing scores of the group's Hq/Hkv query heads,
+ *   sum_h <q_h, kbar_c> (image mode: of their pooled queries); candidates,
+ *   top-k and tie-break as above.  idx [B, Hkv, N, top_k] (image mode
+ *   [B, Hkv, N/bs, top_k]); every query head of the group attends through
+ *   its group's route. */
 lsa_status lsa_route_topk(const lsa_params *p, const void *q, const float *kbar,
                           int32_t *idx, void *workspace, size_t workspace_bytes,
                           void *stream);
@@ -115,7 +125,9 @@ lsa_status lsa_route_topk(const lsa_params *p, const void *q, const float *kbar,
  * idx is normally the output of lsa_route_topk.  An entry is used only if it
  * is a candidate block (causal: 0 <= c < E(t); image mode: 0 <= c < N/bs) and
  * greater than the previously used entry of its row; anything else is
- * skipped, so every access stays in bounds for any idx contents.
+ * skipped, so every access stays in bounds for any idx contents.  With
+ * consensus = 1 idx holds one route per KV group (lsa_route_topk's layout)
+ * and query head h reads the route of its group h / (Hq / Hkv).
  * out [B, Hq, N, D] fp32. */
 lsa_status lsa_sparse_attend(const lsa_params *p, const void *q, const void *k,
                              const void *v, const int32_t *idx, float *out,
@@ -146,7 +158,8 @@ lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
  *   out        [B, Hq, D] fp32;  idx_out [B, Hq, top_k] int32 or NULL.
  * cache_len must be a multiple of bs; workspace: lsa_workspace_bytes(p with
  * seq_len = cache_len, LSA_OP_DECODE) bytes, enough for every T <= cache_len.
- * Scores and softmax run in fp32 (no bf16 rounding of probabilities). */
+ * Scores and softmax run in fp32 (no bf16 rounding of probabilities).
+ * consensus must be 0 (LSA_ERR_UNSUPPORTED otherwise). */
 lsa_status lsa_decode(const lsa_params *p, int32_t cache_len, const void *q,
                       const void *k_cache, const void *v_cache, float *kbar_cache,
                       float *out, int32_t *idx_out, void *workspace,

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header(lsa):
-    assert ctypes.sizeof(lsa.LsaParams) == 40
+    assert ctypes.sizeof(lsa.LsaParams) == 44
+    assert lsa.LsaParams.consensus.offset == 40
 
 
 def good(lsa, **kw):
@@ -49,6 +50,7 @@ def good(lsa, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q_heads=13), 2), (dict(seq_len=1000), 2), (dict(window=100), 2), (dict(window=32), 2),
     (dict(causal=0, window=512, block=16), 2), (dict(causal=2), 2), (dict(batch=0), 2),
+    (dict(consensus=2), 2), (dict(consensus=-1), 2),
     (dict(head_dim=128), 3), (dict(top_k=17), 3), (dict(block=48, window=96, seq_len=960), 3),
     (dict(causal=0, window=0, block=64), 3), (dict(seq_len=1 << 24, block=16, window=512), 3),
 ])
@@ -90,3 +92,20 @@ def test_workspace_sizes_are_plausible(lsa):
     img = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0)
     assert lsa.workspace_bytes(img, lsa.OP_ATTEND) == 4 * 16 * 16384 * 64 * 2
     assert lsa.workspace_bytes(img, lsa.OP_ROUTE) >= 4 * 16 * 1024 * 64 * 4
+
+
+def test_consensus_workspace_and_decode(lsa):
+    """Consensus routing adds the group-summed queries (fp32, one row per KV
+    group and position) to the routing workspace and is not offered by the
+    decode call."""
+    p, pc = good(lsa), good(lsa, consensus=1)
+    extra = lsa.workspace_bytes(pc, lsa.OP_ROUTE) - lsa.workspace_bytes(p, lsa.OP_ROUTE)
+    assert 2 * 131072 * 64 * 4 - 14 * 131072 * 4 <= extra <= 2 * 131072 * 64 * 4 + 4096
+    assert lsa.workspace_bytes(pc, lsa.OP_ATTEND) == lsa.workspace_bytes(p, lsa.OP_ATTEND)
+    assert lsa.library().lsa_workspace_bytes(ctypes.byref(pc), lsa.OP_DECODE) == lsa.SIZE_MAX
+    assert lsa.idx_shape(pc) == (1, 2, 131072, 16)
+    img = lsa.params(4, 16, 4, 16384, 64, 16, 8, 0, 0, consensus=1)
+    assert lsa.idx_shape(img) == (4, 4, 1024, 8)
+    a = ctypes.c_void_p(4096)
+    assert lsa.library().lsa_decode(ctypes.byref(pc), 131072, a, a, a, a, a, None, a, 1 << 40,
+                                    None) == 3

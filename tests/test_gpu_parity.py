@@ -134,7 +134,7 @@ def test_routing_monotone_scores(lsa, sign):
 def attend_gpu(lsa, w, inp, idx_np):
     p = params_of(lsa, w)
     idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).cuda()
-    out = lsa.sparse_attend(p, dev(inp.q), dev(inp.k), dev(inp.v), idx)
+    out = lsa.sparse_attend(p, dev(inp.q), dev(inp.k), dev(inp.v), idx.reshape(lsa.idx_shape(p)))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
