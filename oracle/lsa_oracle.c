@@ -125,6 +125,21 @@ static int idx_ascending(const void *pa, const void *pb)
     return (a > b) - (a < b);
 }
 
+/* Step 3 for one row: buf holds the ncand candidates' scores (buf[c].s) and
+ * ids; orders them, keeps the first min(k, ncand), emits them ascending and
+ * -1 padded, and the k-th / (k+1)-th gap. */
+static void pick_top(cand_t *buf, int64_t ncand, int64_t k, int32_t *idx_out,
+                     double *gap_out)
+{
+    qsort(buf, (size_t)ncand, sizeof(cand_t), cand_order);
+    const int64_t keep = ncand < k ? ncand : k;
+    for (int64_t i = 0; i < k; ++i)
+        idx_out[i] = i < keep ? (int32_t)buf[i].c : -1;
+    qsort(idx_out, (size_t)keep, sizeof(int32_t), idx_ascending);
+    if (gap_out)
+        *gap_out = ncand > k ? buf[k - 1].s - buf[k].s : INFINITY;
+}
+
 /* Steps 2-3 for one row, given its query as doubles and the candidate count.
  * summ: [ncand, D] fp32 summaries of the row's KV head. */
 static void select_top(const double *qd, const float *summ, int64_t ncand,
@@ -138,13 +153,7 @@ static void select_top(const double *qd, const float *summ, int64_t ncand,
         buf[c].s = s;
         buf[c].c = c;
     }
-    qsort(buf, (size_t)ncand, sizeof(cand_t), cand_order);
-    const int64_t keep = ncand < k ? ncand : k;
-    for (int64_t i = 0; i < k; ++i)
-        idx_out[i] = i < keep ? (int32_t)buf[i].c : -1;
-    qsort(idx_out, (size_t)keep, sizeof(int32_t), idx_ascending);
-    if (gap_out)
-        *gap_out = ncand > k ? buf[k - 1].s - buf[k].s : INFINITY;
+    pick_top(buf, ncand, k, idx_out, gap_out);
 }
 
 /* Steps 2-3, causal rows.  rows: n_rows row ids (NULL = all B*Hq*N rows in
@@ -344,14 +353,7 @@ int orc_route_consensus(const uint16_t *q, const float *qbar,
             if (scores)
                 for (int64_t c = 0; c < nb; ++c)
                     scores[i * nb + c] = c < ncand ? buf[c].s : -INFINITY;
-            qsort(buf, (size_t)ncand, sizeof(cand_t), cand_order);
-            const int64_t keep = ncand < k ? ncand : k;
-            int32_t *out = idx + i * k;
-            for (int64_t j = 0; j < k; ++j)
-                out[j] = j < keep ? (int32_t)buf[j].c : -1;
-            qsort(out, (size_t)keep, sizeof(int32_t), idx_ascending);
-            if (gap)
-                gap[i] = ncand > k ? buf[k - 1].s - buf[k].s : INFINITY;
+            pick_top(buf, ncand, k, idx + i * k, gap ? gap + i : NULL);
         }
         free(buf);
     }
