@@ -52,10 +52,13 @@ def lib():
         L.orc_route_image.argtypes = [_p, _p] + [_i64] * 6 + [_p, _i64, _p, _p]
         L.orc_route_scores.argtypes = [_p, _p, _p] + [_i64] * 8 + [_p, _i64, _p]
         L.orc_route_consensus.argtypes = [_p, _p, _p] + [_i64] * 9 + [_p, _i64, _p, _p, _p]
+        L.orc_route_cumulant.argtypes = [_p, _p, _p] + [_i64] * 8 + [ctypes.c_double, _p, _i64,
+                                                                     _p, _p, _p]
         L.orc_attend.argtypes = [_p, _p, _p] + [_i64] * 9 + [ctypes.c_double, _p, _i64, _p, _p]
         L.orc_forward.argtypes = [_p, _p, _p] + [_i64] * 9 + [ctypes.c_double, _p, _i64, _p, _p]
         for f in ("orc_block_means", "orc_route_causal", "orc_route_image",
-                  "orc_route_scores", "orc_route_consensus", "orc_attend", "orc_forward"):
+                  "orc_route_scores", "orc_route_consensus", "orc_route_cumulant", "orc_attend",
+                  "orc_forward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -154,6 +157,33 @@ def route_scores(kbar, rows, *, q=None, qbar=None, block, window=0, causal=1, se
                                   block, window, int(causal), _ptr(r), n, _ptr(out)),
            "route_scores")
     return out
+
+
+def route_cumulant(q, k, kbar, block, top_k, window, beta, rows=None, with_gap=False,
+                   with_scores=False):
+    """Causal routing by the second-cumulant score <q, mu_c> + (beta/2)
+    q^T Sigma_c q.  q bf16 bits [B,Hq,N,D], k bf16 bits [B,Hkv,N,D], kbar the
+    fp32 block means.  Returns idx [n_rows, top_k] (or [B,Hq,N,top_k] when
+    rows is None), then the gap per row and every block's score [n_rows, nb]
+    when asked for."""
+    q, k = _c(q, np.uint16), _c(k, np.uint16)
+    kbar = _c(kbar, np.float32)
+    B, Hq, N, D = q.shape
+    Hkv, nb = k.shape[1], kbar.shape[2]
+    r, n = _rows(rows)
+    total = n if r is not None else B * Hq * N
+    idx = np.empty((total, top_k), dtype=np.int32)
+    gap = np.empty(total, dtype=np.float64) if with_gap else None
+    sc = np.empty((total, nb), dtype=np.float64) if with_scores else None
+    _check(lib().orc_route_cumulant(_ptr(q), _ptr(k), _ptr(kbar), B, Hq, Hkv, N, D, block, top_k,
+                                    window, float(beta), _ptr(r), n, _ptr(idx), _ptr(gap),
+                                    _ptr(sc)), "route_cumulant")
+    if r is None:
+        idx = idx.reshape(B, Hq, N, top_k)
+        if gap is not None:
+            gap = gap.reshape(B, Hq, N)
+    res = (idx,) + ((gap,) if with_gap else ()) + ((sc,) if with_scores else ())
+    return res if len(res) > 1 else idx
 
 
 def route_consensus(kbar, block, top_k, *, q=None, qbar=None, window=0, causal=1, rows=None,

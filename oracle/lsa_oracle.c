@@ -360,6 +360,102 @@ int orc_route_consensus(const uint16_t *q, const float *qbar,
     return bad ? -1 : 0;
 }
 
+/* Second-cumulant routing score (SSA page, "Algorithm and complexity"):
+ *   r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q,
+ * mu_c the fp32 block mean of step 1 and Sigma_c the covariance of the
+ * block's bs keys about their mean, normalised by bs (the second cumulant
+ * of the block's key distribution; fp64 throughout).  beta = 0 gives the
+ * step-2 score.  Causal rows only: q bf16 [B,Hq,N,D], k bf16 [B,Hkv,N,D],
+ * kbar [B,Hkv,nb,D]; rows (b*Hq + h)*N + t (NULL = all).  idx [n_rows, k]
+ * with the step-3 ordering; gap (nullable) as in orc_route_causal; scores
+ * (nullable) [n_rows, nb], -inf where the block is not a candidate. */
+int orc_route_cumulant(const uint16_t *q, const uint16_t *kk, const float *kbar,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                       int64_t D, int64_t bs, int64_t k, int64_t window,
+                       double beta, const int64_t *rows, int64_t n_rows,
+                       int32_t *idx, double *gap, double *scores)
+{
+    if (!q || !kk || !kbar || !idx || bs <= 0 || N % bs || Hkv <= 0 ||
+        Hq % Hkv || k <= 0 || window < bs || window % bs)
+        return -1;
+    const int64_t nb = N / bs, rep = Hq / Hkv;
+    const int64_t total = rows ? n_rows : B * Hq * N;
+    /* Sigma_c of every block: [B*Hkv][nb][D][D] */
+    double *sig = (double *)malloc(sizeof(double) * (size_t)(B * Hkv * nb * D * D));
+    if (!sig)
+        return -1;
+#pragma omp parallel
+    {
+        double *m = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(static)
+        for (int64_t gc = 0; gc < B * Hkv * nb; ++gc) {
+            const int64_t bg = gc / nb, c = gc % nb;
+            const uint16_t *blk = kk + (bg * N + c * bs) * D;
+            double *S = sig + gc * D * D;
+            for (int64_t d = 0; d < D; ++d) {
+                double a = 0.0;
+                for (int64_t j = 0; j < bs; ++j)
+                    a += bf16_to_f64(blk[j * D + d]);
+                m[d] = a / (double)bs;
+            }
+            for (int64_t d = 0; d < D; ++d)
+                for (int64_t e = 0; e < D; ++e) {
+                    double a = 0.0;
+                    for (int64_t j = 0; j < bs; ++j)
+                        a += (bf16_to_f64(blk[j * D + d]) - m[d]) *
+                             (bf16_to_f64(blk[j * D + e]) - m[e]);
+                    S[d * D + e] = a / (double)bs;
+                }
+        }
+        free(m);
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        cand_t *buf = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nb + 1));
+        double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!buf || !qd) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < total; ++i) {
+            if (!buf || !qd) continue;
+            const int64_t r = rows ? rows[i] : i;
+            if (r < 0 || r >= B * Hq * N) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            const int64_t t = r % N, bh = r / N, h = bh % Hq, b = bh / Hq;
+            const int64_t bg = b * Hkv + h / rep;
+            const int64_t ncand = eligible_blocks(t, bs, window);
+            for (int64_t d = 0; d < D; ++d)
+                qd[d] = bf16_to_f64(q[r * D + d]);
+            for (int64_t c = 0; c < ncand; ++c) {
+                const float *mu = kbar + (bg * nb + c) * D;
+                const double *S = sig + (bg * nb + c) * D * D;
+                double first = 0.0, quad = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    first += qd[d] * (double)mu[d];
+                for (int64_t d = 0; d < D; ++d)
+                    for (int64_t e = 0; e < D; ++e)
+                        quad += qd[d] * S[d * D + e] * qd[e];
+                buf[c].s = first + 0.5 * beta * quad;
+                buf[c].c = c;
+            }
+            if (scores)
+                for (int64_t c = 0; c < nb; ++c)
+                    scores[i * nb + c] = c < ncand ? buf[c].s : -INFINITY;
+            pick_top(buf, ncand, k, idx + i * k, gap ? gap + i : NULL);
+        }
+        free(buf);
+        free(qd);
+    }
+    free(sig);
+    return bad ? -1 : 0;
+}
+
 /* Checks one row's selection: entries in [0, ncand), strictly ascending,
  * -1 only as trailing padding.  Returns the number of selected blocks, or
  * -1 when the row is not a valid selection. */

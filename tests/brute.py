@@ -100,3 +100,11 @@ def forward(q_bits, k_bits, v_bits, bs, top_k, window, causal, scale=None, conse
     else:
         mask = image_mask(N, bs, top_k, block_means(qf, bs), kbar, rep, consensus)
     return masked_softmax_attention(qf, kf, vf, mask, rep, scale), mask
+
+
+def cumulant_score(q_f64, keys_f64, mu_f32, beta):
+    """Second-cumulant routing score of one block, computed from the spread
+    of the block's raw scores instead of a covariance matrix:
+    <q, mu> + (beta/2) * (population variance over the block of q . k_j)."""
+    s = keys_f64 @ q_f64
+    return float(np.dot(q_f64, mu_f32.astype(np.float64))) + 0.5 * beta * float(np.var(s))

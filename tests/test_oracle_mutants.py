@@ -30,6 +30,11 @@ MUTANTS = {
     "consensus_interleaved_groups": ("const int64_t qr = ((b * Hq + g * rep + hh) * per + p) * D;",
                                      "const int64_t qr = ((b * Hq + g + hh * Hkv) * per + p) * D;"),
     "consensus_scores_last_head": ("s += sh;", "s = sh;"),
+    "cumulant_sample_covariance": ("S[d * D + e] = a / (double)bs;",
+                                   "S[d * D + e] = a / (double)(bs - 1);"),
+    "cumulant_missing_half": ("buf[c].s = first + 0.5 * beta * quad;",
+                              "buf[c].s = first + beta * quad;"),
+    "cumulant_second_moment": ("m[d] = a / (double)bs;", "m[d] = 0.0 * a;"),
 }
 
 

@@ -421,3 +421,78 @@ def test_consensus_end_to_end_matches_brute_force(orc, causal):
         for h in range(g * 2, g * 2 + 2):
             np.testing.assert_array_equal(sel[0, h], sel[0, g * 2])
             np.testing.assert_array_equal(mask[h], mask[g * 2])
+
+
+# ---------------------------------------------------------------- second-cumulant score
+# r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q (SSA page, "Algorithm and
+# complexity"), Sigma_c the bs-normalised covariance of the block's keys.
+
+def test_cumulant_with_beta_zero_is_the_mean_score(orc):
+    rng = np.random.default_rng(41)
+    bs, W, k, N, D = 16, 32, 3, 512, 32
+    Q, K = rand_bits(rng, (1, 4, N, D)), rand_bits(rng, (1, 2, N, D))
+    kbar = orc.block_means(K, bs)
+    a, ga = orc.route_cumulant(Q, K, kbar, bs, k, W, 0.0, with_gap=True)
+    b, gb = orc.route_causal(Q, kbar, bs, k, W, with_gap=True)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(ga, gb)
+
+
+@pytest.mark.parametrize("bs,W,k,beta", [(16, 32, 3, 0.125), (8, 16, 2, 1.0), (32, 64, 4, -0.5)])
+def test_cumulant_matches_score_variance_brute_force(orc, bs, W, k, beta):
+    rng = np.random.default_rng(bs + k)
+    N, D, Hq, Hkv = 256, 16, 4, 2
+    Q = rand_bits(rng, (1, Hq, N, D))
+    K = rand_bits(rng, (1, Hkv, N, D), scale=1.5)
+    kbar = orc.block_means(K, bs)
+    idx, gap, sc = orc.route_cumulant(Q, K, kbar, bs, k, W, beta, with_gap=True, with_scores=True)
+    qf, kf = brute.widen(Q), brute.widen(K)
+    rep, nb = Hq // Hkv, N // bs
+    checked = 0
+    for h in range(Hq):
+        for t in range(N):
+            E = max(0, t // bs - W // bs + 1)
+            g = h // rep
+            s = [brute.cumulant_score(qf[0, h, t], kf[0, g, c * bs:(c + 1) * bs], kbar[0, g, c], beta)
+                 for c in range(E)]
+            row = h * N + t
+            np.testing.assert_allclose(sc[row, :E], s, rtol=1e-12, atol=1e-12)
+            assert np.all(np.isneginf(sc[row, E:]))
+            if E > k and gap[0, h, t] <= 1e-9:
+                continue
+            keep = brute.rank_select(s, E, k)
+            assert list(idx[0, h, t]) == keep + [-1] * (k - len(keep)), (h, t)
+            checked += 1
+    assert checked > 0.9 * Hq * N
+
+
+def test_cumulant_prefers_a_spread_block_with_lower_mean(orc):
+    """Two candidate blocks along one direction u: block 0 has every key at
+    mean score 1.0 and no spread; block 1 has mean score 0.75 with key scores
+    +-1 around it (variance 1).  k = 1 picks block 1 exactly when
+    0.75 + beta/2 > 1.0, i.e. beta > 0.5."""
+    bs, D, W = 4, 2, 4
+    N = 3 * bs                                  # query at t = 11: E = 2 candidates
+    K = np.zeros((1, 1, N, D), np.float32)
+    K[0, 0, 0:4, 0] = 1.0
+    K[0, 0, 4:8, 0] = [1.75, -0.25, 1.75, -0.25]
+    Q = np.zeros((1, 1, N, D), np.float32)
+    Q[0, 0, :, 0] = 1.0
+    Kb, Qb = to_bf16_bits(K), to_bf16_bits(Q)
+    kbar = orc.block_means(Kb, bs)
+    for beta, want in ((0.0, 0), (0.25, 0), (0.75, 1), (2.0, 1), (-1.0, 0)):
+        idx, sc = orc.route_cumulant(Qb, Kb, kbar, bs, 1, W, beta, rows=[N - 1], with_scores=True)
+        assert idx[0, 0] == want, (beta, idx)
+        assert sc[0, 0] == pytest.approx(1.0)
+        assert sc[0, 1] == pytest.approx(0.75 + beta / 2)
+
+
+def test_cumulant_constant_blocks_reduce_to_the_mean_score(orc):
+    rng = np.random.default_rng(42)
+    bs, W, k, N, D = 16, 32, 3, 512, 16
+    Q = rand_bits(rng, (1, 2, N, D))
+    blocks = rng.standard_normal((1, 1, N // bs, D)).astype(np.float32)
+    K = to_bf16_bits(np.repeat(blocks, bs, axis=2))   # every key of a block equal
+    kbar = orc.block_means(K, bs)
+    np.testing.assert_array_equal(orc.route_cumulant(Q, K, kbar, bs, k, W, 3.0),
+                                  orc.route_causal(Q, kbar, bs, k, W))
