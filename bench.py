@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -65,6 +66,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--consensus-steps", type=int, default=10,
                     help="also time the layer with consensus routing (one route per KV group)")
+    ap.add_argument("--cumulant-steps", type=int, default=3,
+                    help="also time the layer routed by the second-cumulant score (beta = 1/sqrt(D))")
     ap.add_argument("--decode-steps", type=int, default=50,
                     help="also time single-query decode steps against the workload's cache")
     return ap.parse_args()
@@ -188,6 +191,38 @@ def consensus_bench(lsa, w, q, k, v, steps):
         e.close()
     return {"ms_per_layer": ms, "selected_tflop": (f_routed + f_window) / 1e12,
             "tflops": (f_routed + f_window) / 1e12 / (ms * 1e-3),
+            "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+
+
+def cumulant_bench(lsa, w, q, k, v, steps):
+    """The layer routed by the second-cumulant score with beta = 1/sqrt(D):
+    ms per layer, stage times, and the routing kernel against the bf16 MFMA
+    peak, counting 2*D FLOP per (row, eligible key) for the raw scores whose
+    per-block mean and variance form the score."""
+    import torch
+    beta = 1.0 / math.sqrt(w.head_dim)
+    p = lsa.params(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.top_k,
+                   w.window, 1, beta=beta)
+    out = torch.empty((w.batch, w.q_heads, w.seq_len, w.head_dim), dtype=torch.float32,
+                      device=q.device)
+    idx = torch.empty(lsa.idx_shape(p), dtype=torch.int32, device=q.device)
+    ws = torch.empty(lsa.workspace_bytes(p, lsa.OP_FORWARD), dtype=torch.uint8, device=q.device)
+    lsa.forward(p, q, k, v, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    events = [lsa.StageEvents() for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lsa.forward_profiled(p, q, k, v, events[i], out, idx, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    stage = np.array([e.stage_ms() for e in events]).mean(axis=0)
+    for e in events:
+        e.close()
+    flop = 2 * w.head_dim * w.block * routing_candidates(w)
+    route_ms = float(stage[1])
+    return {"beta": beta, "ms_per_layer": ms, "routing_ms": route_ms,
+            "routing_tflop": flop / 1e12, "routing_tflops": flop / 1e12 / (route_ms * 1e-3),
+            "routing_mfma_frac": flop / 1e12 / (route_ms * 1e-3) / PEAK_BF16_TFLOPS,
             "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
 
 
@@ -319,6 +354,8 @@ def main():
     }
     if args.consensus_steps > 0 and w.q_heads > w.kv_heads:
         result["consensus"] = consensus_bench(lsa, w, q, k, v, args.consensus_steps)
+    if w.causal and args.cumulant_steps > 0 and w.seq_len <= 262144:
+        result["cumulant"] = cumulant_bench(lsa, w, q, k, v, args.cumulant_steps)
     if w.causal and args.decode_steps > 0:
         result["decode"] = decode_bench(lsa, w, q, k, v, args.decode_steps)
     if args.cpu_seconds > 0:

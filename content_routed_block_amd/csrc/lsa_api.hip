@@ -23,6 +23,9 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     if (p->q_heads % p->kv_heads) return LSA_ERR_SHAPE;
     if (p->causal != 0 && p->causal != 1) return LSA_ERR_SHAPE;
     if (p->consensus != 0 && p->consensus != 1) return LSA_ERR_SHAPE;
+    uint32_t beta_bits;
+    memcpy(&beta_bits, &p->beta, 4);
+    if ((beta_bits & 0x7FFFFFFFu) >= 0x7F800000u) return LSA_ERR_SHAPE;  // beta not finite
     if (p->seq_len % p->block) return LSA_ERR_SHAPE;
     if (p->causal) {
         if (p->window < p->block || p->window % p->block) return LSA_ERR_SHAPE;
@@ -33,6 +36,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     if (!pow2_block(p->block)) return LSA_ERR_UNSUPPORTED;
     if (!p->causal && p->block != 16) return LSA_ERR_UNSUPPORTED;
     if (p->top_k > lsa::kMaxTopK) return LSA_ERR_UNSUPPORTED;
+    if (p->beta != 0.f && (!p->causal || p->consensus)) return LSA_ERR_UNSUPPORTED;
     const int64_t nb = p->seq_len / p->block;
     if (nb > 65536) return LSA_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)p->batch * p->q_heads * p->seq_len;
@@ -54,6 +58,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     g->window = p->window;
     g->causal = p->causal;
     g->consensus = p->consensus;
+    g->beta = p->beta;
     g->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
     return LSA_OK;
 }
@@ -87,7 +92,8 @@ size_t lsa_workspace_bytes(const lsa_params* p, int32_t op) {
         case LSA_OP_ATTEND: return lsa::attend_workspace_bytes(g);
         case LSA_OP_FORWARD: return forward_ws(g, true);  // enough with or without idx_out
         case LSA_OP_DECODE:
-            return g.causal && !g.consensus ? lsa::decode_workspace_bytes(g, g.N) : (size_t)-1;
+            return g.causal && !g.consensus && g.beta == 0.f ? lsa::decode_workspace_bytes(g, g.N)
+                                                            : (size_t)-1;
         default: return (size_t)-1;
     }
 }
@@ -109,12 +115,26 @@ lsa_status lsa_route_topk(const lsa_params* p, const void* q, const float* kbar,
     Geometry g;
     lsa_status st = check_params(p, &g);
     if (st != LSA_OK) return st;
+    if (g.beta != 0.f) return LSA_ERR_UNSUPPORTED;  // the score needs the keys: lsa_route_cumulant
     if (!q || !kbar || !idx || !workspace) return LSA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(kbar, 16) || !aligned(idx, 16)) return LSA_ERR_ALIGN;
     if (!aligned(workspace, 256)) return LSA_ERR_ALIGN;
     if (workspace_bytes < lsa::route_workspace_bytes(g)) return LSA_ERR_WORKSPACE;
     return from_hip(lsa::launch_route(g, static_cast<const uint16_t*>(q), kbar, idx, workspace,
                                       static_cast<hipStream_t>(stream)));
+}
+
+lsa_status lsa_route_cumulant(const lsa_params* p, const void* q, const void* k, int32_t* idx,
+                              void* stream) {
+    Geometry g;
+    lsa_status st = check_params(p, &g);
+    if (st != LSA_OK) return st;
+    if (!g.causal || g.consensus) return LSA_ERR_UNSUPPORTED;
+    if (!q || !k || !idx) return LSA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(idx, 16)) return LSA_ERR_ALIGN;
+    return from_hip(lsa::launch_route_cumulant(g, static_cast<const uint16_t*>(q),
+                                               static_cast<const uint16_t*>(k), idx,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 lsa_status lsa_sparse_attend(const lsa_params* p, const void* q, const void* k, const void* v,
@@ -162,12 +182,22 @@ static lsa_status forward_impl(const lsa_params* p, const void* q, const void* k
     }
     void* rest = base + off;
     lsa::mark(ev, 0, s);
-    st = from_hip(lsa::launch_summarize(static_cast<const uint16_t*>(k), kbar, g.B * g.Hkv, g.N,
-                                        g.bs, s));
-    if (st != LSA_OK) return st;
-    lsa::mark(ev, 1, s);
-    st = from_hip(lsa::launch_route(g, static_cast<const uint16_t*>(q), kbar, idx, rest, s, ev));
-    if (st != LSA_OK) return st;
+    if (g.beta != 0.f) {  // second-cumulant score: routed from the keys themselves
+        lsa::mark(ev, 1, s);
+        st = from_hip(lsa::launch_route_cumulant(g, static_cast<const uint16_t*>(q),
+                                                 static_cast<const uint16_t*>(k), idx, s));
+        if (st != LSA_OK) return st;
+        lsa::mark(ev, 2, s);
+        lsa::mark(ev, 3, s);
+    } else {
+        st = from_hip(lsa::launch_summarize(static_cast<const uint16_t*>(k), kbar, g.B * g.Hkv,
+                                            g.N, g.bs, s));
+        if (st != LSA_OK) return st;
+        lsa::mark(ev, 1, s);
+        st = from_hip(lsa::launch_route(g, static_cast<const uint16_t*>(q), kbar, idx, rest, s,
+                                        ev));
+        if (st != LSA_OK) return st;
+    }
     return from_hip(lsa::launch_attend(g, static_cast<const uint16_t*>(q),
                                        static_cast<const uint16_t*>(k),
                                        static_cast<const uint16_t*>(v), idx, out, rest, s, ev));
@@ -200,7 +230,7 @@ lsa_status lsa_decode(const lsa_params* p, int32_t cache_len, const void* q, con
     lsa_status st = check_params(&pc, &g);
     if (st != LSA_OK) return st;
     if (!p->causal) return LSA_ERR_SHAPE;
-    if (p->consensus) return LSA_ERR_UNSUPPORTED;
+    if (p->consensus || p->beta != 0.f) return LSA_ERR_UNSUPPORTED;
     if (p->seq_len < 1 || p->seq_len > cache_len) return LSA_ERR_SHAPE;
     if (!q || !k_cache || !v_cache || !kbar_cache || !out || !workspace) return LSA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||

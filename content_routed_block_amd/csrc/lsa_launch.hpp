@@ -13,6 +13,7 @@ struct Geometry {
     int B, Hq, Hkv, N, D, bs, nb, top_k, window, causal;
     int consensus;  // 1: one route per KV group (idx heads = Hkv)
     float scale;    // resolved (> 0)
+    float beta;     // second-cumulant weight (0: the block-mean score)
 };
 
 // x [BH, N, 64] bf16 -> xbar [BH, N/bs, 64] fp32
@@ -31,6 +32,11 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
 int pair_stride_log2(int top_k);
 
 // Sparse attention workspace (bytes) and launch.
+// Second-cumulant routing (beta != 0, causal, per query head): needs no
+// workspace.
+hipError_t launch_route_cumulant(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                 int32_t* idx, hipStream_t s);
+
 size_t attend_workspace_bytes(const Geometry& g);
 hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* idx, float* out, void* ws,

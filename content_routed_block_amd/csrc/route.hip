@@ -636,6 +636,175 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
     }
 }
 
+// ------------------------------------------------------------ second-cumulant routing
+// Score r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q (SSA page, "Algorithm
+// and complexity"), with Sigma_c the bs-normalised covariance of block c's
+// keys.  Since q^T Sigma_c q is the variance over the block of the raw
+// scores q . k_j, and <q, mu_c> their mean, the kernel computes the raw
+// scores of every eligible key with bf16 MFMA (exact products, fp32 sums)
+// and reduces each block to mean + (beta/2) * variance.
+//
+// A workgroup owns 128 query rows of one (b, h), four waves of 32 rows; the
+// keys stream through LDS in chunks of 32 (double-buffered, loads two chunks
+// ahead).  Tiles S^T = K_chunk . Q^T leave each lane 16 scores of its row,
+// the lane pair (l, l^32) holding the chunk's 32.  Per chunk the pair forms
+// the chunk's mean and squared deviations; chunks of one block are combined
+// with the parallel-variance update (no cancellation between the mean and
+// the second moment).  The two lanes of a pair keep the even and the odd
+// blocks respectively in sorted 16-entry key lists (score, then lower
+// index), merged once at the end.  No survivor lists, so no fallback.
+struct CumArgs {
+    const uint16_t* q;  // [B,Hq,N,64] bf16
+    const uint16_t* k;  // [B,Hkv,N,64] bf16
+    int32_t* idx;       // [B,Hq,N,top_k]
+    int Hq, Hkv, N, top_k, window, tiles, items;
+    float half_beta_over_bs;  // beta / (2 bs)
+};
+
+template <int BS>
+__global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 s_k[2][RT_CH * RT_PITCH];
+    constexpr int CPB = BS >= RT_CH ? BS / RT_CH : 1;  // chunks per block (BS >= 32)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, l32 = lane & 31;
+    // XCD-aware order as in k_route: the tiles of one head, and the heads of
+    // one KV group, on one XCD, whose L2 then serves the group's keys.
+    const int per_xcd = gridDim.x / 8;
+    const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (item >= a.items) return;
+    const int bh = item / a.tiles;
+    const int tile = a.tiles - 1 - (item - bh * a.tiles);
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
+    const int N = a.N;
+    const int r0 = tile * RT_ROWS + 32 * w;
+    const int rq = r0 + l32;
+    const int Erow = rq < N ? eligible_blocks(rq, BS, a.window) : 0;
+    const int Emax = r0 < N ? eligible_blocks(min(r0 + 31, N - 1), BS, a.window) : 0;
+    const int wg_last = min(tile * RT_ROWS + RT_ROWS, N) - 1;
+    const int Ewg = eligible_blocks(wg_last, BS, a.window);
+    const uint16_t* kb = a.k + (int64_t)bg * N * kD;
+    const float hb = a.half_beta_over_bs;
+
+    bf16x8 Bq[4];
+    if (rq < N) {
+        const uint16_t* qp = a.q + ((int64_t)bh * N + rq) * kD + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            Bq[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) Bq[ks] = bf16x8{};
+    }
+
+    uint64_t L[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
+    float Mb = 0.f, Qb = 0.f;  // running mean and squared deviations of the block (BS >= 32)
+    const int nch = Ewg * BS / RT_CH;
+    const int wave_keys = Emax * BS;
+
+    u32x4 r0v = {0u, 0u, 0u, 0u}, r1v = r0v;
+    if (nch > 0) {
+        r0v = stage_load(kb, 0, tid);
+        stage_store(s_k[0], tid, r0v);
+    }
+    if (nch > 1) r1v = stage_load(kb, RT_CH, tid);
+    __syncthreads();
+    auto offer = [&](float score, int c) {
+        if (c < Erow) {
+            const uint64_t key = sel_key(score, (uint32_t)c);
+            if (key > L[kMaxTopK - 1]) insert_key(L, key);
+        }
+    };
+    auto body = [&](int j, u32x4& r_issue, const u32x4& r_store) {
+        const int key0 = j * RT_CH;
+        if (j + 2 < nch) r_issue = stage_load(kb, key0 + 2 * RT_CH, tid);
+        if (key0 < wave_keys) {
+            bf16x8 A[4];
+            read_cands(s_k[j & 1], l32, half, A);
+            f32x16 acc = {};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc = mfma32(A[ks], Bq[ks], acc);
+            // register r holds key 8*(r/4) + 4*half + r%4 of the chunk
+            if constexpr (BS == 16) {
+                // keys 0-15 (block 2j) sit in registers 0-7, keys 16-31 in 8-15
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    s0 += acc[r];
+                    s1 += acc[r + 8];
+                }
+                s0 += __shfl_xor(s0, 32, kWave);
+                s1 += __shfl_xor(s1, 32, kWave);
+                const float m0 = s0 * (1.f / 16.f), m1 = s1 * (1.f / 16.f);
+                float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float d0 = acc[r] - m0, d1 = acc[r + 8] - m1;
+                    q0 = fmaf(d0, d0, q0);
+                    q1 = fmaf(d1, d1, q1);
+                }
+                q0 += __shfl_xor(q0, 32, kWave);
+                q1 += __shfl_xor(q1, 32, kWave);
+                offer(half ? fmaf(hb, q1, m1) : fmaf(hb, q0, m0), 2 * j + half);
+            } else {
+                float sum = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sum += acc[r];
+                sum += __shfl_xor(sum, 32, kWave);
+                const float m = sum * (1.f / 32.f);
+                float sq = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float d = acc[r] - m;
+                    sq = fmaf(d, d, sq);
+                }
+                sq += __shfl_xor(sq, 32, kWave);
+                const int jb = j % CPB;
+                if (jb == 0) {
+                    Mb = m;
+                    Qb = sq;
+                } else {
+                    // parallel-variance update: n_prev = 32 jb keys so far, 32 new
+                    const float n_prev = 32.f * (float)jb;
+                    const float f = 32.f / (n_prev + 32.f);
+                    const float delta = m - Mb;
+                    Mb = fmaf(delta, f, Mb);
+                    Qb += sq + delta * delta * n_prev * f;
+                }
+                if (jb == CPB - 1) {
+                    const int c = j / CPB;
+                    if ((c & 1) == half) offer(fmaf(hb, Qb, Mb), c);
+                }
+            }
+        }
+        if (j + 1 < nch) stage_store(s_k[(j + 1) & 1], tid, r_store);
+        __syncthreads();
+    };
+    for (int j = 0; j < nch; j += 2) {
+        body(j, r0v, r1v);
+        if (j + 1 < nch) body(j + 1, r1v, r0v);
+    }
+
+    // the pair's lists hold disjoint candidates (even and odd blocks)
+    uint64_t Mx[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        const uint64_t o = L[kMaxTopK - 1 - j];
+        const uint32_t olo = __shfl_xor((uint32_t)o, 32, kWave);
+        const uint32_t ohi = __shfl_xor((uint32_t)(o >> 32), 32, kWave);
+        const uint64_t other = ((uint64_t)ohi << 32) | olo;
+        Mx[j] = L[j] > other ? L[j] : other;
+    }
+    bitonic_merge_desc_u64(Mx);
+    if (rq < N && half == 0) {
+        const int m = Erow < a.top_k ? Erow : a.top_k;
+        write_selection(a.idx + ((int64_t)bh * N + rq) * a.top_k, Mx, m, a.top_k);
+    }
+}
+
 // ------------------------------------------------------------ group queries
 // Consensus routing: out[b, g, p, :] = sum over the group's heads h of
 // in[b, h, p, :], in fp32 (heads in ascending order).  One thread per 8
@@ -772,6 +941,30 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     else
         launch_route_kernels<false, true>(a, grid, s, ev);
     mark(ev, 3, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_cumulant(const Geometry& g, const uint16_t* q, const uint16_t* k,
+                                 int32_t* idx, hipStream_t s) {
+    CumArgs a;
+    a.q = q;
+    a.k = k;
+    a.idx = idx;
+    a.Hq = g.Hq;
+    a.Hkv = g.Hkv;
+    a.N = g.N;
+    a.top_k = g.top_k;
+    a.window = g.window;
+    a.tiles = (g.N + RT_ROWS - 1) / RT_ROWS;
+    a.items = g.B * g.Hq * a.tiles;
+    a.half_beta_over_bs = 0.5f * g.beta / (float)g.bs;
+    const dim3 grid((unsigned)(((int64_t)a.items + 7) / 8 * 8));  // a multiple of the XCD count
+    switch (g.bs) {
+        case 16: hipLaunchKernelGGL(k_route_cumulant<16>, grid, dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL(k_route_cumulant<32>, grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL(k_route_cumulant<64>, grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(k_route_cumulant<128>, grid, dim3(256), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ class LsaParams(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("consensus", ctypes.c_int32)]
+                ("consensus", ctypes.c_int32), ("beta", ctypes.c_float)]
 
 
 _P = ctypes.POINTER(LsaParams)
@@ -44,6 +44,8 @@ _lib.lsa_workspace_bytes.argtypes = [_P, ctypes.c_int32]
 _lib.lsa_workspace_bytes.restype = ctypes.c_size_t
 _lib.lsa_block_summarize.argtypes = [_P, _v, ctypes.c_int32, _v, _v]
 _lib.lsa_route_topk.argtypes = [_P, _v, _v, _v, _v, ctypes.c_size_t, _v]
+_lib.lsa_route_cumulant.argtypes = [_P, _v, _v, _v, _v]
+_lib.lsa_route_cumulant.restype = ctypes.c_int
 _lib.lsa_sparse_attend.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
 _lib.lsa_forward.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
 for _f in ("lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend", "lsa_forward"):
@@ -83,9 +85,9 @@ def library():
 
 
 def params(batch, q_heads, kv_heads, seq_len, head_dim=64, block=64, top_k=16, window=512,
-           causal=1, scale=0.0, consensus=0) -> LsaParams:
+           causal=1, scale=0.0, consensus=0, beta=0.0) -> LsaParams:
     return LsaParams(batch, q_heads, kv_heads, seq_len, head_dim, block, top_k, window, causal,
-                     float(scale), consensus)
+                     float(scale), consensus, float(beta))
 
 
 def idx_shape(p: LsaParams):
@@ -166,6 +168,20 @@ def route_topk(p: LsaParams, q: torch.Tensor, kbar: torch.Tensor,
     workspace, nbytes = _workspace(p, OP_ROUTE, workspace, q.device)
     _check(_lib.lsa_route_topk(ctypes.byref(p), _ptr(q), _ptr(kbar), _ptr(idx), _ptr(workspace),
                                nbytes, _stream(stream)), "lsa_route_topk")
+    return idx
+
+
+def route_cumulant(p: LsaParams, q: torch.Tensor, k: torch.Tensor,
+                   idx: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Routing by the second-cumulant score with weight p.beta (see
+    lsa_route_cumulant)."""
+    q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
+    k = _bits(k, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "k")
+    if idx is None:
+        idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
+    _tensor(idx, torch.int32, idx_shape(p), "idx")
+    _check(_lib.lsa_route_cumulant(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(idx), _stream(stream)),
+           "lsa_route_cumulant")
     return idx
 
 

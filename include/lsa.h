@@ -58,6 +58,9 @@ typedef struct lsa_params {
     float scale;       /* softmax scale; <= 0 selects 1/sqrt(D) */
     int32_t consensus; /* 0: a route per query head; 1: one route per KV group,
                           shared by the group's query heads (see lsa_route_topk) */
+    float beta;        /* second-cumulant weight of the routing score (see
+                          lsa_route_cumulant); 0: the block-mean score.  Must be
+                          finite; nonzero needs causal = 1 and consensus = 0 */
 } lsa_params;
 
 typedef enum lsa_status {
@@ -111,10 +114,25 @@ lsa_status lsa_block_summarize(const lsa_params *p, const void *x, int32_t heads
  *   sum_h <q_h, kbar_c> (image mode: of their pooled queries); candidates,
  *   top-k and tie-break as above.  idx [B, Hkv, N, top_k] (image mode
  *   [B, Hkv, N/bs, top_k]); every query head of the group attends through
- *   its group's route. */
+ *   its group's route.
+ * beta != 0 is LSA_ERR_UNSUPPORTED here: that score needs the keys
+ * themselves (lsa_route_cumulant). */
 lsa_status lsa_route_topk(const lsa_params *p, const void *q, const float *kbar,
                           int32_t *idx, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/* Routing by the second-cumulant score (SSA page, "Algorithm and
+ * complexity"):  r_c(q) = <q, mu_c> + (beta/2) q^T Sigma_c q, where mu_c is
+ * the mean and Sigma_c the covariance (normalised by bs) of block c's keys;
+ * beta = p->beta.  Candidates (causal only), top-k, tie-break and the idx
+ * layout [B, Hq, N, top_k] are those of lsa_route_topk.  q^T Sigma_c q is
+ * evaluated as the variance over the block of the raw scores q . k_j, so
+ * the call reads the keys k [B, Hkv, N, D] bf16 and needs no block means
+ * and no workspace.  Scores are fp32 sums of exact bf16 products; each
+ * block's mean and variance are formed without cancellation.  Needs
+ * causal = 1 and consensus = 0 (LSA_ERR_UNSUPPORTED otherwise). */
+lsa_status lsa_route_cumulant(const lsa_params *p, const void *q, const void *k,
+                              int32_t *idx, void *stream);
 
 /* Exact softmax attention over the selected keys only (SSA page, opening
  * paragraph; Subquadratic Sparse Attention page, "Architecture").
@@ -135,7 +153,8 @@ lsa_status lsa_sparse_attend(const lsa_params *p, const void *q, const void *k,
 
 /* The whole layer: summarize K, route, attend.  idx_out may be NULL (the
  * selection then lives in the workspace); otherwise it receives idx as
- * lsa_route_topk writes it. */
+ * lsa_route_topk writes it.  With beta != 0 the routing is
+ * lsa_route_cumulant's (the key summary stage is then empty). */
 lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
                        const void *v, float *out, int32_t *idx_out,
                        void *workspace, size_t workspace_bytes, void *stream);
@@ -159,7 +178,7 @@ lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
  * cache_len must be a multiple of bs; workspace: lsa_workspace_bytes(p with
  * seq_len = cache_len, LSA_OP_DECODE) bytes, enough for every T <= cache_len.
  * Scores and softmax run in fp32 (no bf16 rounding of probabilities).
- * consensus must be 0 (LSA_ERR_UNSUPPORTED otherwise). */
+ * consensus and beta must be 0 (LSA_ERR_UNSUPPORTED otherwise). */
 lsa_status lsa_decode(const lsa_params *p, int32_t cache_len, const void *q,
                       const void *k_cache, const void *v_cache, float *kbar_cache,
                       float *out, int32_t *idx_out, void *workspace,

@@ -36,8 +36,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header(lsa):
-    assert ctypes.sizeof(lsa.LsaParams) == 44
+    assert ctypes.sizeof(lsa.LsaParams) == 48
     assert lsa.LsaParams.consensus.offset == 40
+    assert lsa.LsaParams.beta.offset == 44
 
 
 def good(lsa, **kw):
@@ -50,7 +51,9 @@ def good(lsa, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q_heads=13), 2), (dict(seq_len=1000), 2), (dict(window=100), 2), (dict(window=32), 2),
     (dict(causal=0, window=512, block=16), 2), (dict(causal=2), 2), (dict(batch=0), 2),
-    (dict(consensus=2), 2), (dict(consensus=-1), 2),
+    (dict(consensus=2), 2), (dict(consensus=-1), 2), (dict(beta=float("nan")), 2),
+    (dict(beta=float("inf")), 2), (dict(beta=0.5, consensus=1), 3),
+    (dict(beta=0.5, causal=0, window=0, block=16), 3),
     (dict(head_dim=128), 3), (dict(top_k=17), 3), (dict(block=48, window=96, seq_len=960), 3),
     (dict(causal=0, window=0, block=64), 3), (dict(seq_len=1 << 24, block=16, window=512), 3),
 ])
@@ -109,3 +112,14 @@ def test_consensus_workspace_and_decode(lsa):
     a = ctypes.c_void_p(4096)
     assert lsa.library().lsa_decode(ctypes.byref(pc), 131072, a, a, a, a, a, None, a, 1 << 40,
                                     None) == 3
+
+
+def test_cumulant_routing_checks(lsa):
+    L = lsa.library()
+    a = ctypes.c_void_p(4096)
+    p = good(lsa, beta=0.125)
+    assert L.lsa_route_topk(ctypes.byref(p), a, a, a, a, 1 << 40, None) == 3
+    assert L.lsa_route_cumulant(ctypes.byref(p), None, a, a, None) == 1
+    assert L.lsa_route_cumulant(ctypes.byref(p), a, ctypes.c_void_p(4100), a, None) == 4
+    assert L.lsa_route_cumulant(ctypes.byref(good(lsa, beta=0.5, consensus=1)), a, a, a, None) == 3
+    assert L.lsa_workspace_bytes(ctypes.byref(p), lsa.OP_DECODE) == lsa.SIZE_MAX
