@@ -647,23 +647,43 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
 // A workgroup owns 128 query rows of one (b, h), four waves of 32 rows; the
 // keys stream through LDS in chunks of 32 (double-buffered, loads two chunks
 // ahead).  Tiles S^T = K_chunk . Q^T leave each lane 16 scores of its row,
-// the lane pair (l, l^32) holding the chunk's 32.  Per chunk the pair forms
-// the chunk's mean and squared deviations; chunks of one block are combined
-// with the parallel-variance update (no cancellation between the mean and
-// the second moment).  The two lanes of a pair keep the even and the odd
-// blocks respectively in sorted 16-entry key lists (score, then lower
-// index), merged once at the end.  No survivor lists, so no fallback.
+// the lane pair (l, l^32) holding the chunk's 32.  Each lane accumulates the
+// sum and the sum of squares of its scores over the block; at the block's
+// end the pair adds its halves (one cross-half swap each) and forms
+// variance = sum of squares / bs - mean^2.
+//
+// Selection: the two lanes of a pair take the even and the odd blocks
+// respectively.  Each lane keeps its 16 best (score, block) pairs sorted by
+// score.  A lane sees its blocks in ascending order, so a newcomer beats a
+// kept entry exactly when its score is strictly larger (equal scores keep
+// the lower, older block): the order (score desc, block asc) needs only
+// float compares.  Blocks that beat the lane's 16th score are appended to a
+// per-lane LDS queue and inserted in batches of CUM_Q offers, so that a wave
+// runs the insertion about as often as its busiest lane needs it rather
+// than whenever any lane does.  The pair's lists are merged once at the end.
+// No survivor capacity, so no fallback.
+constexpr int CUM_Q = 8;  // offers per lane between insertion batches
+
 struct CumArgs {
     const uint16_t* q;  // [B,Hq,N,64] bf16
     const uint16_t* k;  // [B,Hkv,N,64] bf16
     int32_t* idx;       // [B,Hq,N,top_k]
     int Hq, Hkv, N, top_k, window, tiles, items;
-    float half_beta_over_bs;  // beta / (2 bs)
+    float half_beta;    // beta / 2
 };
+
+// v[l % 32] + v[l % 32 + 32] in every lane l (bitwise equal in both lanes).
+__device__ __forceinline__ float pair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int BS>
 __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_k[2][RT_CH * RT_PITCH];
+    __shared__ float s_qs[CUM_Q][256];  // queued scores, slot-major
+    __shared__ int s_qc[CUM_Q][256];    // queued block ids
     constexpr int CPB = BS >= RT_CH ? BS / RT_CH : 1;  // chunks per block (BS >= 32)
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -685,7 +705,8 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
     const int wg_last = min(tile * RT_ROWS + RT_ROWS, N) - 1;
     const int Ewg = eligible_blocks(wg_last, BS, a.window);
     const uint16_t* kb = a.k + (int64_t)bg * N * kD;
-    const float hb = a.half_beta_over_bs;
+    const float hb = a.half_beta;
+    constexpr float inv_bs = 1.f / (float)BS;
 
     bf16x8 Bq[4];
     if (rq < N) {
@@ -698,29 +719,61 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
         for (int ks = 0; ks < 4; ++ks) Bq[ks] = bf16x8{};
     }
 
-    uint64_t L[kMaxTopK];
+    float Ls[kMaxTopK];  // kept scores, descending
+    int Lc[kMaxTopK];    // their blocks
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
-    float Mb = 0.f, Qb = 0.f;  // running mean and squared deviations of the block (BS >= 32)
+    for (int j = 0; j < kMaxTopK; ++j) {
+        Ls[j] = -INFINITY;
+        Lc[j] = 0;
+    }
+    int nq = 0;  // queued offers of this lane
+    auto flush = [&]() {
+        for (int i = 0; __builtin_amdgcn_ballot_w64(i < nq) != 0; ++i) {
+            if (i < nq) {
+                float x = s_qs[i][tid];
+                int xc = s_qc[i][tid];
+                if (x > Ls[kMaxTopK - 1]) {
+#pragma unroll
+                    for (int j = 0; j < kMaxTopK; ++j) {
+                        const bool gt = x > Ls[j];
+                        const float ts = Ls[j];
+                        const int tc = Lc[j];
+                        Ls[j] = gt ? x : ts;
+                        Lc[j] = gt ? xc : tc;
+                        x = gt ? ts : x;
+                        xc = gt ? tc : xc;
+                    }
+                }
+            }
+        }
+        nq = 0;
+    };
+    float s1 = 0.f, s2 = 0.f;  // this lane's sum and sum of squares over the block (BS >= 32)
     const int nch = Ewg * BS / RT_CH;
     const int wave_keys = Emax * BS;
 
-    u32x4 r0v = {0u, 0u, 0u, 0u}, r1v = r0v;
-    if (nch > 0) {
-        r0v = stage_load(kb, 0, tid);
-        stage_store(s_k[0], tid, r0v);
-    }
-    if (nch > 1) r1v = stage_load(kb, RT_CH, tid);
-    __syncthreads();
-    auto offer = [&](float score, int c) {
-        if (c < Erow) {
-            const uint64_t key = sel_key(score, (uint32_t)c);
-            if (key > L[kMaxTopK - 1]) insert_key(L, key);
+    // Staging loads are issued unconditionally (the address clamped to the
+    // last chunk), so the in-order load counter always has exactly one
+    // younger load in flight when a staged chunk is stored, and the query
+    // loads are complete before the loop: no wait drains the prefetch.
+    const int last = (nch - 1) * RT_CH;  // used only when nch > 0 (workgroup-uniform)
+    // block score from the pair's sums; queued by the lane of its parity when
+    // it beats that lane's 16th kept score.  Every 2 * CUM_Q blocks (CUM_Q
+    // offers per lane) the queues are inserted.
+    auto offer = [&](float sum, float sq, int c) {
+        const float m = pair_sum(sum) * inv_bs;
+        const float var = pair_sum(sq) * inv_bs - m * m;
+        const float score = fmaf(hb, var, m);
+        if ((c & 1) == half && c < Erow && score > Ls[kMaxTopK - 1]) {
+            s_qs[nq][tid] = score;
+            s_qc[nq][tid] = c;
+            ++nq;
         }
+        if ((c & (2 * CUM_Q - 1)) == 2 * CUM_Q - 1) flush();
     };
     auto body = [&](int j, u32x4& r_issue, const u32x4& r_store) {
         const int key0 = j * RT_CH;
-        if (j + 2 < nch) r_issue = stage_load(kb, key0 + 2 * RT_CH, tid);
+        r_issue = stage_load(kb, min(key0 + 2 * RT_CH, last), tid);
         if (key0 < wave_keys) {
             bf16x8 A[4];
             read_cands(s_k[j & 1], l32, half, A);
@@ -730,73 +783,63 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
             // register r holds key 8*(r/4) + 4*half + r%4 of the chunk
             if constexpr (BS == 16) {
                 // keys 0-15 (block 2j) sit in registers 0-7, keys 16-31 in 8-15
-                float s0 = 0.f, s1 = 0.f;
+                float a0 = 0.f, a1 = 0.f, q0 = 0.f, q1 = 0.f;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    s0 += acc[r];
-                    s1 += acc[r + 8];
+                    a0 += acc[r];
+                    a1 += acc[r + 8];
+                    q0 = fmaf(acc[r], acc[r], q0);
+                    q1 = fmaf(acc[r + 8], acc[r + 8], q1);
                 }
-                s0 += __shfl_xor(s0, 32, kWave);
-                s1 += __shfl_xor(s1, 32, kWave);
-                const float m0 = s0 * (1.f / 16.f), m1 = s1 * (1.f / 16.f);
-                float q0 = 0.f, q1 = 0.f;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float d0 = acc[r] - m0, d1 = acc[r + 8] - m1;
-                    q0 = fmaf(d0, d0, q0);
-                    q1 = fmaf(d1, d1, q1);
-                }
-                q0 += __shfl_xor(q0, 32, kWave);
-                q1 += __shfl_xor(q1, 32, kWave);
-                offer(half ? fmaf(hb, q1, m1) : fmaf(hb, q0, m0), 2 * j + half);
+                offer(a0, q0, 2 * j);
+                offer(a1, q1, 2 * j + 1);
             } else {
-                float sum = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sum += acc[r];
-                sum += __shfl_xor(sum, 32, kWave);
-                const float m = sum * (1.f / 32.f);
-                float sq = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float d = acc[r] - m;
-                    sq = fmaf(d, d, sq);
-                }
-                sq += __shfl_xor(sq, 32, kWave);
                 const int jb = j % CPB;
                 if (jb == 0) {
-                    Mb = m;
-                    Qb = sq;
-                } else {
-                    // parallel-variance update: n_prev = 32 jb keys so far, 32 new
-                    const float n_prev = 32.f * (float)jb;
-                    const float f = 32.f / (n_prev + 32.f);
-                    const float delta = m - Mb;
-                    Mb = fmaf(delta, f, Mb);
-                    Qb += sq + delta * delta * n_prev * f;
+                    s1 = 0.f;
+                    s2 = 0.f;
                 }
-                if (jb == CPB - 1) {
-                    const int c = j / CPB;
-                    if ((c & 1) == half) offer(fmaf(hb, Qb, Mb), c);
+                float t1 = 0.f, t2 = 0.f;  // two chains for the adder latency
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    s1 += acc[r];
+                    t1 += acc[r + 1];
+                    s2 = fmaf(acc[r], acc[r], s2);
+                    t2 = fmaf(acc[r + 1], acc[r + 1], t2);
                 }
+                s1 += t1;
+                s2 += t2;
+                if (jb == CPB - 1) offer(s1, s2, j / CPB);
             }
         }
-        if (j + 1 < nch) stage_store(s_k[(j + 1) & 1], tid, r_store);
+        stage_store(s_k[(j + 1) & 1], tid, r_store);
         __syncthreads();
     };
-    for (int j = 0; j < nch; j += 2) {
-        body(j, r0v, r1v);
-        if (j + 1 < nch) body(j + 1, r1v, r0v);
+    if (nch > 0) {
+        u32x4 r0v = stage_load(kb, 0, tid);
+        u32x4 r1v = stage_load(kb, min(RT_CH, last), tid);
+        __builtin_amdgcn_s_waitcnt(0);
+        stage_store(s_k[0], tid, r0v);
+        __syncthreads();
+        for (int j = 0; j < nch; j += 2) {
+            body(j, r0v, r1v);
+            if (j + 1 < nch) body(j + 1, r1v, r0v);
+        }
+        flush();
     }
 
-    // the pair's lists hold disjoint candidates (even and odd blocks)
+    // the pair's lists hold disjoint candidates (even and odd blocks); as
+    // 64-bit keys (score, then lower block) they merge in one bitonic step
     uint64_t Mx[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
-        const uint64_t o = L[kMaxTopK - 1 - j];
+        const int jj = kMaxTopK - 1 - j;
+        const uint64_t o = Ls[jj] == -INFINITY ? 0ull : sel_key(Ls[jj], (uint32_t)Lc[jj]);
+        const uint64_t mine = Ls[j] == -INFINITY ? 0ull : sel_key(Ls[j], (uint32_t)Lc[j]);
         const uint32_t olo = __shfl_xor((uint32_t)o, 32, kWave);
         const uint32_t ohi = __shfl_xor((uint32_t)(o >> 32), 32, kWave);
         const uint64_t other = ((uint64_t)ohi << 32) | olo;
-        Mx[j] = L[j] > other ? L[j] : other;
+        Mx[j] = mine > other ? mine : other;
     }
     bitonic_merge_desc_u64(Mx);
     if (rq < N && half == 0) {
@@ -957,7 +1000,7 @@ hipError_t launch_route_cumulant(const Geometry& g, const uint16_t* q, const uin
     a.window = g.window;
     a.tiles = (g.N + RT_ROWS - 1) / RT_ROWS;
     a.items = g.B * g.Hq * a.tiles;
-    a.half_beta_over_bs = 0.5f * g.beta / (float)g.bs;
+    a.half_beta = 0.5f * g.beta;
     const dim3 grid((unsigned)(((int64_t)a.items + 7) / 8 * 8));  // a multiple of the XCD count
     switch (g.bs) {
         case 16: hipLaunchKernelGGL(k_route_cumulant<16>, grid, dim3(256), 0, s, a); break;
