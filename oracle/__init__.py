@@ -54,11 +54,12 @@ def lib():
         L.orc_route_consensus.argtypes = [_p, _p, _p] + [_i64] * 9 + [_p, _i64, _p, _p, _p]
         L.orc_route_cumulant.argtypes = [_p, _p, _p] + [_i64] * 8 + [ctypes.c_double, _p, _i64,
                                                                      _p, _p, _p]
+        L.orc_route_tree.argtypes = [_p, _p, _p] + [_i64] * 11 + [_p, _i64, _p, _p, _p, _p, _p]
         L.orc_attend.argtypes = [_p, _p, _p] + [_i64] * 9 + [ctypes.c_double, _p, _i64, _p, _p]
         L.orc_forward.argtypes = [_p, _p, _p] + [_i64] * 9 + [ctypes.c_double, _p, _i64, _p, _p]
         for f in ("orc_block_means", "orc_route_causal", "orc_route_image",
-                  "orc_route_scores", "orc_route_consensus", "orc_route_cumulant", "orc_attend",
-                  "orc_forward"):
+                  "orc_route_scores", "orc_route_consensus", "orc_route_cumulant",
+                  "orc_route_tree", "orc_attend", "orc_forward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,6 +185,43 @@ def route_cumulant(q, k, kbar, block, top_k, window, beta, rows=None, with_gap=F
             gap = gap.reshape(B, Hq, N)
     res = (idx,) + ((gap,) if with_gap else ()) + ((sc,) if with_scores else ())
     return res if len(res) > 1 else idx
+
+
+def route_tree(kbar, block, top_k, beam, *, q=None, qbar=None, window=0, causal=1, fanout=16,
+               rows=None, details=False):
+    """Two-level routing: nodes of `fanout` blocks summarised by the mean of
+    their block means, the best `beam` complete candidate nodes kept, then
+    top-k over the kept nodes' blocks plus the incomplete tail.  Causal: q
+    bf16 bits [B,Hq,N,D]; image mode: qbar fp32 [B,Hq,nb,D].  Returns idx
+    [n_rows, top_k] (or [B,Hq,P,top_k] when rows is None); with details,
+    also a dict of per-row gap1 (node level), gap2 (block level), node
+    scores [n_rows, nb // fanout] and the kept nodes [n_rows, beam]."""
+    kbar = _c(kbar, np.float32)
+    B, Hkv, nb, D = kbar.shape
+    if causal:
+        q = _c(q, np.uint16)
+        Hq, N = q.shape[1], q.shape[2]
+        per = N
+    else:
+        qbar = _c(qbar, np.float32)
+        Hq, N = qbar.shape[1], nb * block
+        per = nb
+    r, n = _rows(rows)
+    total = n if r is not None else B * Hq * per
+    idx = np.empty((total, top_k), dtype=np.int32)
+    nn = nb // fanout
+    g1 = np.empty(total, np.float64) if details else None
+    g2 = np.empty(total, np.float64) if details else None
+    ns = np.empty((total, max(nn, 1)), np.float64) if details else None
+    bo = np.empty((total, beam), np.int32) if details else None
+    _check(lib().orc_route_tree(_ptr(q), _ptr(qbar), _ptr(kbar), B, Hq, Hkv, N, D, block, top_k,
+                                window, int(causal), fanout, beam, _ptr(r), n, _ptr(idx),
+                                _ptr(g1), _ptr(g2), _ptr(ns), _ptr(bo)), "route_tree")
+    if r is None:
+        idx = idx.reshape(B, Hq, per, top_k)
+    if details:
+        return idx, {"gap1": g1, "gap2": g2, "node_scores": ns[:, :nn], "beam": bo}
+    return idx
 
 
 def route_consensus(kbar, block, top_k, *, q=None, qbar=None, window=0, causal=1, rows=None,

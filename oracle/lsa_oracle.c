@@ -456,6 +456,120 @@ int orc_route_cumulant(const uint16_t *q, const uint16_t *kk, const float *kbar,
     return bad ? -1 : 0;
 }
 
+/* Two-level (tree) routing (SSA page, "Algorithm and complexity": a
+ * hierarchical router with fixed block size and budget, the measured tree
+ * at fanout 16; "Complete 10M transformer result": a bounded hierarchical
+ * router).  Nodes group F consecutive key blocks; a node's summary is the
+ * mean of its F block means (fp64 sum, one fp32 rounding).  For a row with
+ * E candidate blocks (causal: E(t); image mode: all nb):
+ *   1. the S = floor(E / F) complete candidate nodes are scored <q, nu_s>
+ *      and the best min(beam, S) are kept (score desc, index asc);
+ *   2. the candidate blocks are those of the kept nodes plus the tail
+ *      blocks [F*S, E) of the incomplete node;
+ *   3. those blocks are scored <q, mu_c> and the top-k taken as in step 3.
+ * With beam >= S every block is a candidate and the result is the flat
+ * selection.  Causal: q bf16 [B,Hq,N,D], rows (b*Hq + h)*N + t.  Image
+ * mode: qbar fp32 [B,Hq,nb,D], rows (b*Hq + h)*nb + i.  idx [n_rows, k].
+ * Optional outputs per row: gap1 (beam-th minus (beam+1)-th node score,
+ * +inf when no node is left out), gap2 (k-th minus (k+1)-th score among the
+ * candidates), node_scores [n_rows, nb/F] (-inf beyond S), beam_out
+ * [n_rows, beam] (kept nodes ascending, -1 padded). */
+int orc_route_tree(const uint16_t *q, const float *qbar, const float *kbar,
+                   int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                   int64_t bs, int64_t k, int64_t window, int64_t causal,
+                   int64_t F, int64_t beam, const int64_t *rows,
+                   int64_t n_rows, int32_t *idx, double *gap1, double *gap2,
+                   double *node_scores, int32_t *beam_out)
+{
+    if (!kbar || !idx || bs <= 0 || N % bs || Hkv <= 0 || Hq % Hkv || k <= 0 ||
+        F <= 0 || beam <= 0)
+        return -1;
+    if (causal ? (!q || window < bs || window % bs) : !qbar)
+        return -1;
+    const int64_t nb = N / bs, rep = Hq / Hkv, nn = nb / F;
+    const int64_t per = causal ? N : nb;
+    const int64_t total = rows ? n_rows : B * Hq * per;
+    float *nu = (float *)malloc(sizeof(float) * (size_t)((B * Hkv * nn > 0 ? B * Hkv * nn : 1) * D));
+    if (!nu)
+        return -1;
+    for (int64_t gs = 0; gs < B * Hkv * nn; ++gs) {
+        const int64_t bg = gs / nn, sn = gs % nn;
+        for (int64_t d = 0; d < D; ++d) {
+            double a = 0.0;
+            for (int64_t i = 0; i < F; ++i)
+                a += (double)kbar[(bg * nb + sn * F + i) * D + d];
+            nu[gs * D + d] = (float)(a / (double)F);
+        }
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        cand_t *nbuf = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nn + 1));
+        cand_t *cbuf = (cand_t *)malloc(sizeof(cand_t) * (size_t)(nb + 1));
+        int32_t *kept = (int32_t *)malloc(sizeof(int32_t) * (size_t)beam);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!nbuf || !cbuf || !kept || !qd) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 32)
+        for (int64_t i = 0; i < total; ++i) {
+            if (!nbuf || !cbuf || !kept || !qd) continue;
+            const int64_t r = rows ? rows[i] : i;
+            if (r < 0 || r >= B * Hq * per) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            const int64_t p = r % per, bh = r / per, h = bh % Hq, b = bh / Hq;
+            const int64_t bg = b * Hkv + h / rep;
+            const int64_t E = causal ? eligible_blocks(p, bs, window) : nb;
+            const int64_t S = E / F;
+            for (int64_t d = 0; d < D; ++d)
+                qd[d] = causal ? bf16_to_f64(q[r * D + d]) : (double)qbar[r * D + d];
+            /* level 1: the nodes */
+            for (int64_t sn = 0; sn < S; ++sn) {
+                double sc = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    sc += qd[d] * (double)nu[(bg * nn + sn) * D + d];
+                nbuf[sn].s = sc;
+                nbuf[sn].c = sn;
+            }
+            if (node_scores)
+                for (int64_t sn = 0; sn < nn; ++sn)
+                    node_scores[i * nn + sn] = sn < S ? nbuf[sn].s : -INFINITY;
+            pick_top(nbuf, S, beam, kept, gap1 ? gap1 + i : NULL);
+            if (beam_out)
+                memcpy(beam_out + i * beam, kept, sizeof(int32_t) * (size_t)beam);
+            /* level 2: blocks of the kept nodes, then the tail */
+            int64_t nc = 0;
+            for (int64_t j = 0; j < beam && kept[j] >= 0; ++j)
+                for (int64_t x = 0; x < F; ++x) {
+                    cbuf[nc].c = kept[j] * F + x;
+                    ++nc;
+                }
+            for (int64_t c = S * F; c < E; ++c) {
+                cbuf[nc].c = c;
+                ++nc;
+            }
+            const float *summ = kbar + bg * nb * D;
+            for (int64_t j = 0; j < nc; ++j) {
+                double sc = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    sc += qd[d] * (double)summ[cbuf[j].c * D + d];
+                cbuf[j].s = sc;
+            }
+            pick_top(cbuf, nc, k, idx + i * k, gap2 ? gap2 + i : NULL);
+        }
+        free(nbuf);
+        free(cbuf);
+        free(kept);
+        free(qd);
+    }
+    free(nu);
+    return bad ? -1 : 0;
+}
+
 /* Checks one row's selection: entries in [0, ncand), strictly ascending,
  * -1 only as trailing padding.  Returns the number of selected blocks, or
  * -1 when the row is not a valid selection. */

@@ -108,3 +108,25 @@ def cumulant_score(q_f64, keys_f64, mu_f32, beta):
     <q, mu> + (beta/2) * (population variance over the block of q . k_j)."""
     s = keys_f64 @ q_f64
     return float(np.dot(q_f64, mu_f32.astype(np.float64))) + 0.5 * beta * float(np.var(s))
+
+
+def tree_select(q_f64, kbar_g, E, F, beam, k):
+    """Two-level selection for one row by rank counting: node summaries are
+    the fp32-rounded fp64 means of F consecutive block means; the best beam
+    of the floor(E/F) complete nodes are kept; top-k over their blocks plus
+    blocks [F*floor(E/F), E).  kbar_g: float32 [nb, D]."""
+    S = E // F
+    nu = [kbar_g[s * F:(s + 1) * F].astype(np.float64).mean(axis=0).astype(np.float32)
+          for s in range(S)]
+    ns = [float(np.dot(q_f64, nu[s].astype(np.float64))) for s in range(S)]
+    kept = rank_select(ns, S, beam)
+    cands = [s * F + x for s in kept for x in range(F)] + list(range(S * F, E))
+    cs = [float(np.dot(q_f64, kbar_g[c].astype(np.float64))) for c in cands]
+    # rank over the candidate set (ties to the lower block id)
+    keep = []
+    for a, ca in enumerate(cands):
+        beaten = sum(1 for b, cb in enumerate(cands)
+                     if cs[b] > cs[a] or (cs[b] == cs[a] and cb < ca))
+        if beaten < k:
+            keep.append(ca)
+    return sorted(keep)

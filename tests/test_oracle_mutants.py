@@ -35,6 +35,11 @@ MUTANTS = {
     "cumulant_missing_half": ("buf[c].s = first + 0.5 * beta * quad;",
                               "buf[c].s = first + beta * quad;"),
     "cumulant_second_moment": ("m[d] = a / (double)bs;", "m[d] = 0.0 * a;"),
+    "tree_tail_dropped": ("for (int64_t c = S * F; c < E; ++c) {",
+                          "for (int64_t c = S * F; c < S * F; ++c) {"),
+    "tree_node_strided": ("cbuf[nc].c = kept[j] * F + x;", "cbuf[nc].c = kept[j] + x * nn;"),
+    "tree_node_mean_divisor": ("nu[gs * D + d] = (float)(a / (double)F);",
+                               "nu[gs * D + d] = (float)(a / (double)(F - 1));"),
 }
 
 

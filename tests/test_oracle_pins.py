@@ -496,3 +496,84 @@ def test_cumulant_constant_blocks_reduce_to_the_mean_score(orc):
     kbar = orc.block_means(K, bs)
     np.testing.assert_array_equal(orc.route_cumulant(Q, K, kbar, bs, k, W, 3.0),
                                   orc.route_causal(Q, kbar, bs, k, W))
+
+
+# ---------------------------------------------------------------- two-level (tree) routing
+# Nodes of 16 blocks summarised by the mean of their block means; the best
+# `beam` complete candidate nodes are opened, plus the incomplete tail
+# (SSA page, "Algorithm and complexity": hierarchical router, fanout 16).
+
+def test_tree_with_wide_beam_is_flat_routing(orc):
+    rng = np.random.default_rng(61)
+    bs, W, k, N, D = 16, 32, 5, 4096, 16
+    Q, K = rand_bits(rng, (1, 4, N, D)), rand_bits(rng, (1, 2, N, D))
+    kbar = orc.block_means(K, bs)
+    S_max = (N // bs) // 16
+    np.testing.assert_array_equal(orc.route_tree(kbar, bs, k, S_max, q=Q, window=W),
+                                  orc.route_causal(Q, kbar, bs, k, W))
+    qbar = orc.block_means(Q, bs)
+    np.testing.assert_array_equal(orc.route_tree(kbar, bs, k, S_max, qbar=qbar, causal=0),
+                                  orc.route_image(qbar, kbar, k))
+
+
+@pytest.mark.parametrize("bs,W,k,beam,F", [(8, 16, 4, 2, 16), (4, 8, 3, 1, 4), (8, 32, 6, 3, 8)])
+def test_tree_matches_rank_brute_force(orc, bs, W, k, beam, F):
+    rng = np.random.default_rng(bs * 7 + beam)
+    N, D, Hq, Hkv = 1024, 8, 2, 1
+    Q, K = rand_bits(rng, (1, Hq, N, D)), rand_bits(rng, (1, Hkv, N, D))
+    kbar = orc.block_means(K, bs)
+    idx, det = orc.route_tree(kbar, bs, k, beam, q=Q, window=W, fanout=F, details=True)
+    qf = brute.widen(Q)
+    checked = 0
+    for h in range(Hq):
+        for t in range(0, N, 3):
+            E = max(0, t // bs - W // bs + 1)
+            row = h * N + t
+            if min(det["gap1"][row], det["gap2"][row]) <= 1e-12:
+                continue
+            want = brute.tree_select(qf[0, h, t], kbar[0, 0], E, F, beam, k)
+            assert list(idx[0, h, t]) == want + [-1] * (k - len(want)), (h, t)
+            checked += 1
+    assert checked > 0.9 * Hq * N / 3
+
+
+def test_tree_misses_a_strong_block_in_a_weak_node(orc):
+    """All blocks score 0 except: node 0 has every block at 1.0 (node mean
+    1.0) and node 1 has one block at 8.0 and the rest at -1.0 (node mean
+    1/16 * (8 - 15) < 1).  With beam 1 the tree opens node 0 only, so block
+    16 (the 8.0) is not selected; with beam 2 it is; the flat selection
+    always has it.  Tail blocks (past the last complete node) are always
+    candidates."""
+    bs, D, F = 1, 1, 16
+    nb = 40                                  # nodes 0, 1; tail blocks 32..39
+    vals = np.zeros(nb, np.float32)
+    vals[0:16] = 1.0
+    vals[16] = 8.0
+    vals[17:32] = -1.0
+    vals[35] = 4.0                           # a tail block
+    kbar = vals.reshape(1, 1, nb, 1)
+    qbar = np.ones((1, 1, nb, 1), np.float32)
+    idx1 = orc.route_tree(kbar, bs, 2, 1, qbar=qbar, causal=0)[0, 0, 0]
+    assert list(idx1) == [0, 35]             # node 0's first block (ties -> lowest) and the tail block
+    idx2 = orc.route_tree(kbar, bs, 2, 2, qbar=qbar, causal=0)[0, 0, 0]
+    assert list(idx2) == [16, 35]
+    flat = orc.route_image(qbar, kbar, 2)[0, 0, 0]
+    assert list(flat) == [16, 35]
+
+
+def test_tree_node_scores_are_means_of_block_scores(orc):
+    """<q, nu_s> equals the mean over the node of <q, mu_c> (linearity), up
+    to the fp32 rounding of nu_s."""
+    rng = np.random.default_rng(62)
+    bs, W, k, N, D = 16, 32, 4, 8192, 32
+    Q, K = rand_bits(rng, (1, 1, N, D)), rand_bits(rng, (1, 1, N, D))
+    kbar = orc.block_means(K, bs)
+    rows = np.array([N - 1, N // 2, 3000])
+    _, det = orc.route_tree(kbar, bs, k, 4, q=Q, window=W, rows=rows, details=True)
+    qf = brute.widen(Q)
+    for i, t in enumerate(rows):
+        S = max(0, t // bs - W // bs + 1) // 16
+        bsc = kbar[0, 0].astype(np.float64) @ qf[0, 0, t]
+        want = bsc[:S * 16].reshape(S, 16).mean(axis=1)
+        np.testing.assert_allclose(det["node_scores"][i, :S], want, rtol=1e-6, atol=1e-6)
+        assert np.all(np.isneginf(det["node_scores"][i, S:]))
