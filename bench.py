@@ -68,6 +68,8 @@ def parse():
                     help="also time the layer with consensus routing (one route per KV group)")
     ap.add_argument("--cumulant-steps", type=int, default=3,
                     help="also time the layer routed by the second-cumulant score (beta = 1/sqrt(D))")
+    ap.add_argument("--tree-beam", type=int, default=8,
+                    help="also time the layer with two-level routing keeping this many nodes (0: skip)")
     ap.add_argument("--decode-steps", type=int, default=50,
                     help="also time single-query decode steps against the workload's cache")
     return ap.parse_args()
@@ -226,6 +228,41 @@ def cumulant_bench(lsa, w, q, k, v, steps):
             "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
 
 
+def tree_bench(lsa, w, q, k, v, beam, steps):
+    """The layer with two-level routing (nodes of 16 blocks, `beam` kept per
+    row): ms per layer and stage times (for this mode stage "routing" is the
+    node level with the tail slots, and "routing fallback" is the block
+    level over the kept nodes)."""
+    import torch
+    p = lsa.params(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.top_k,
+                   w.window, 1, beam=beam)
+    out = torch.empty((w.batch, w.q_heads, w.seq_len, w.head_dim), dtype=torch.float32,
+                      device=q.device)
+    idx = torch.empty(lsa.idx_shape(p), dtype=torch.int32, device=q.device)
+    ws = torch.empty(lsa.workspace_bytes(p, lsa.OP_FORWARD), dtype=torch.uint8, device=q.device)
+    for _ in range(2):
+        lsa.forward(p, q, k, v, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    events = [lsa.StageEvents() for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lsa.forward_profiled(p, q, k, v, events[i], out, idx, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    stage = np.array([e.stage_ms() for e in events]).mean(axis=0)
+    for e in events:
+        e.close()
+    t = np.arange(w.seq_len, dtype=np.int64)
+    E = np.maximum(0, t // w.block - w.window // w.block + 1)
+    S = E // 16
+    scored = int((S + 16 * np.minimum(beam, S) + (E - 16 * S)).sum()) * w.batch * w.q_heads
+    return {"beam": beam, "ms_per_layer": ms,
+            "node_level_ms": float(stage[1]), "block_level_ms": float(stage[2]),
+            "routing_ms": float(stage[1] + stage[2]),
+            "scores_per_layer": scored, "flat_scores_per_layer": routing_candidates(w),
+            "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+
+
 def copy_calibration():
     import torch
     n = 1 << 28                       # 256 Mi float32 = 1 GiB read + 1 GiB written
@@ -356,6 +393,8 @@ def main():
         result["consensus"] = consensus_bench(lsa, w, q, k, v, args.consensus_steps)
     if w.causal and args.cumulant_steps > 0 and w.seq_len <= 262144:
         result["cumulant"] = cumulant_bench(lsa, w, q, k, v, args.cumulant_steps)
+    if w.causal and args.tree_beam > 0:
+        result["tree"] = tree_bench(lsa, w, q, k, v, args.tree_beam, max(3, min(args.steps, 10)))
     if w.causal and args.decode_steps > 0:
         result["decode"] = decode_bench(lsa, w, q, k, v, args.decode_steps)
     if args.cpu_seconds > 0:

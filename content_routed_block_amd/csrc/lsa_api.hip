@@ -37,11 +37,17 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     if (!p->causal && p->block != 16) return LSA_ERR_UNSUPPORTED;
     if (p->top_k > lsa::kMaxTopK) return LSA_ERR_UNSUPPORTED;
     if (p->beta != 0.f && (!p->causal || p->consensus)) return LSA_ERR_UNSUPPORTED;
+    if (p->beam < 0) return LSA_ERR_SHAPE;
+    if (p->beam > 0 &&
+        (p->beam >= lsa::kMaxTopK || !p->causal || p->consensus || p->beta != 0.f))
+        return LSA_ERR_UNSUPPORTED;
     const int64_t nb = p->seq_len / p->block;
     if (nb > 65536) return LSA_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)p->batch * p->q_heads * p->seq_len;
     if ((rows << lsa::pair_stride_log2(p->top_k)) + 64 >= ((int64_t)1 << 32))
         return LSA_ERR_UNSUPPORTED;  // 32-bit pair ids (+ 64 dummy rows)
+    if (p->beam > 0 && (rows << lsa::pair_stride_log2(p->beam + 1)) + 64 >= ((int64_t)1 << 32))
+        return LSA_ERR_UNSUPPORTED;  // the same for the two-level router's (row, node) pairs
     if ((int64_t)p->batch * p->q_heads * ((p->seq_len + 255) / 256) >= ((int64_t)1 << 31))
         return LSA_ERR_UNSUPPORTED;
     uint32_t scale_bits;
@@ -59,6 +65,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     g->causal = p->causal;
     g->consensus = p->consensus;
     g->beta = p->beta;
+    g->beam = p->beam;
     g->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
     return LSA_OK;
 }
@@ -92,8 +99,9 @@ size_t lsa_workspace_bytes(const lsa_params* p, int32_t op) {
         case LSA_OP_ATTEND: return lsa::attend_workspace_bytes(g);
         case LSA_OP_FORWARD: return forward_ws(g, true);  // enough with or without idx_out
         case LSA_OP_DECODE:
-            return g.causal && !g.consensus && g.beta == 0.f ? lsa::decode_workspace_bytes(g, g.N)
-                                                            : (size_t)-1;
+            return g.causal && !g.consensus && g.beta == 0.f && !g.beam
+                       ? lsa::decode_workspace_bytes(g, g.N)
+                       : (size_t)-1;
         default: return (size_t)-1;
     }
 }
@@ -230,7 +238,7 @@ lsa_status lsa_decode(const lsa_params* p, int32_t cache_len, const void* q, con
     lsa_status st = check_params(&pc, &g);
     if (st != LSA_OK) return st;
     if (!p->causal) return LSA_ERR_SHAPE;
-    if (p->consensus || p->beta != 0.f) return LSA_ERR_UNSUPPORTED;
+    if (p->consensus || p->beta != 0.f || p->beam) return LSA_ERR_UNSUPPORTED;
     if (p->seq_len < 1 || p->seq_len > cache_len) return LSA_ERR_SHAPE;
     if (!q || !k_cache || !v_cache || !kbar_cache || !out || !workspace) return LSA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||

@@ -15,6 +15,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 64;          // head dim supported by this build
 constexpr int kMaxTopK = 16;    // selection list length held in registers
+constexpr int kTreeFanout = 16;  // key blocks per node of two-level routing
+constexpr int kTreeFanoutLog2 = 4;
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -14,6 +14,7 @@ struct Geometry {
     int consensus;  // 1: one route per KV group (idx heads = Hkv)
     float scale;    // resolved (> 0)
     float beta;     // second-cumulant weight (0: the block-mean score)
+    int beam;       // two-level routing: nodes kept per row (0: flat routing)
 };
 
 // x [BH, N, 64] bf16 -> xbar [BH, N/bs, 64] fp32
@@ -32,6 +33,14 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
 int pair_stride_log2(int top_k);
 
 // Sparse attention workspace (bytes) and launch.
+// Second level of two-level routing: scores every block of the nodes listed
+// in slots [B*Hq*N][beam + 1] (kept nodes, then the tail node) and writes
+// the top-k to idx.  bhi/blo: bf16 hi/lo block means [B*Hkv][nb_pad][64].
+size_t tree_level2_bytes(const Geometry& g);
+hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16_t* bhi,
+                              const uint16_t* blo, int nb_pad, const int32_t* slots, int32_t* idx,
+                              void* ws, hipStream_t s);
+
 // Second-cumulant routing (beta != 0, causal, per query head): needs no
 // workspace.
 hipError_t launch_route_cumulant(const Geometry& g, const uint16_t* q, const uint16_t* k,

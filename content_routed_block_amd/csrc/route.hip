@@ -65,6 +65,8 @@ struct RouteArgs {
     int tiles;   // ceil(P / RT_ROWS)
     int items;   // B * Hq * tiles
     int nb_pad;  // nb rounded up to a multiple of RT_CH
+    int cshift;      // causal candidates are E(t) >> cshift (two-level routing: nodes of 16 blocks)
+    int idx_stride;  // idx row stride (>= top_k)
 };
 
 // ------------------------------------------------------------ sorting networks
@@ -169,14 +171,15 @@ __device__ __forceinline__ void insert_key(uint64_t (&L)[kMaxTopK], uint64_t x) 
     }
 }
 
-// Writes one idx row from a key list sorted by rank (m valid keys).
+// Writes one idx row (row stride `stride`) from a key list sorted by rank
+// (m valid keys).
 __device__ __forceinline__ void write_selection(int32_t* out, const uint64_t (&L)[kMaxTopK],
-                                                int m, int top_k) {
+                                                int m, int top_k, int stride) {
     uint32_t cs[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) cs[j] = j < m ? key_block(L[j]) : 0xFFFFFFFFu;
     bitonic_sort_asc_u32<kMaxTopK>(cs);
-    if ((top_k & 3) == 0) {  // 16-byte stores (rows are 16-byte aligned)
+    if (((top_k | stride) & 3) == 0) {  // 16-byte stores (rows are 16-byte aligned)
         typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int j4 = 0; j4 < kMaxTopK / 4; ++j4) {
@@ -264,9 +267,9 @@ __global__ __launch_bounds__(1024) void k_prefix_max(float* __restrict__ x, int 
 }
 
 __device__ __forceinline__ int row_candidates(bool causal, int row, int P, int bs, int window,
-                                              int nb) {
+                                              int nb, int cshift) {
     if (row >= P) return 0;
-    return causal ? eligible_blocks(row, bs, window) : nb;
+    return causal ? eligible_blocks(row, bs, window) >> cshift : nb;
 }
 
 // Staging of one chunk (32 candidate rows x 64 dims, bf16) through LDS:
@@ -324,11 +327,13 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
     const uint16_t* klo = a.klo + (int64_t)bg * a.nb_pad * kD;
 
     const int rq = r0 + l32;
-    const int Erow = row_candidates(CAUSAL, rq, P, a.bs, a.window, a.nb);
-    const int Emax = r0 < P ? row_candidates(CAUSAL, min(r0 + 31, P - 1), P, a.bs, a.window, a.nb) : 0;
+    const int Erow = row_candidates(CAUSAL, rq, P, a.bs, a.window, a.nb, a.cshift);
+    const int Emax =
+        r0 < P ? row_candidates(CAUSAL, min(r0 + 31, P - 1), P, a.bs, a.window, a.nb, a.cshift) : 0;
     const int wg_last = min(tile * RT_ROWS + RT_ROWS, P) - 1;
-    const int Ewg = row_candidates(CAUSAL, wg_last, P, a.bs, a.window, a.nb);  // chunk loop bound
-    const int Emin = (r0 + 31 < P) ? row_candidates(CAUSAL, r0, P, a.bs, a.window, a.nb) : 0;
+    const int Ewg = row_candidates(CAUSAL, wg_last, P, a.bs, a.window, a.nb, a.cshift);  // loop bound
+    const int Emin =
+        (r0 + 31 < P) ? row_candidates(CAUSAL, r0, P, a.bs, a.window, a.nb, a.cshift) : 0;
     const float kn_max = Emax > 0 ? a.pk[(int64_t)bg * a.nb + Emax - 1] : 0.f;
     const float lo_max = Emax > 0 ? a.plo[(int64_t)bg * a.nb + Emax - 1] : 0.f;
 
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
     bitonic_merge_desc_u64(M);
     if (half == 0) {
         const int m = n_pair < a.top_k ? n_pair : a.top_k;
-        write_selection(a.idx + out_row * a.top_k, M, m, a.top_k);
+        write_selection(a.idx + out_row * a.idx_stride, M, m, a.top_k, a.idx_stride);
     }
 }
 
@@ -581,7 +586,7 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
         const int bh = (int)(rid / (uint32_t)a.P), row = (int)(rid % (uint32_t)a.P);
         const int h = bh % a.Hq, b = bh / a.Hq, g = h / (a.Hq / a.Hkv);
         const float* kb = a.kbar + (int64_t)(b * a.Hkv + g) * a.nb * kD;
-        const int E = row_candidates(CAUSAL, row, a.P, a.bs, a.window, a.nb);
+        const int E = row_candidates(CAUSAL, row, a.P, a.bs, a.window, a.nb, a.cshift);
         if (tid < kD) {
             s_q[tid] = QF32 ? a.qbar[((int64_t)bh * a.P + row) * kD + tid]
                             : bf16_bits_to_f32(a.q[((int64_t)bh * a.N + row) * kD + tid]);
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
             uint64_t L[kMaxTopK];
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) L[j] = j < m ? s_keys[j] : 0;
-            write_selection(a.idx + (int64_t)rid * a.top_k, L, m, a.top_k);
+            write_selection(a.idx + (int64_t)rid * a.idx_stride, L, m, a.top_k, a.idx_stride);
         }
         __syncthreads();
     }
@@ -844,7 +849,7 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
     bitonic_merge_desc_u64(Mx);
     if (rq < N && half == 0) {
         const int m = Erow < a.top_k ? Erow : a.top_k;
-        write_selection(a.idx + ((int64_t)bh * N + rq) * a.top_k, Mx, m, a.top_k);
+        write_selection(a.idx + ((int64_t)bh * N + rq) * a.top_k, Mx, m, a.top_k, a.top_k);
     }
 }
 
@@ -883,6 +888,46 @@ __global__ __launch_bounds__(256) void k_group_query(const T* __restrict__ in,
     *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
+// ------------------------------------------------------------ two-level routing, first level
+// Node summaries: the mean of 16 consecutive block means (fp64 sum, one
+// fp32 rounding), for the nn complete nodes of each group.  One thread per
+// (node, 8 dims).
+__global__ __launch_bounds__(256) void k_node_means(const float* __restrict__ kbar,
+                                                    float* __restrict__ nu, int nb, int nn,
+                                                    int64_t n_threads) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_threads) return;
+    const int64_t gs = i >> 3;  // bg * nn + node
+    const int d0 = (int)(i & 7) * 8;
+    const int64_t bg = gs / nn, node = gs % nn;
+    const float* src = kbar + (bg * nb + node * kTreeFanout) * kD + d0;
+    double acc[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
+    for (int c = 0; c < kTreeFanout; ++c) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + (int64_t)c * kD);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + (int64_t)c * kD + 4);
+        acc[0] += x0[0]; acc[1] += x0[1]; acc[2] += x0[2]; acc[3] += x0[3];
+        acc[4] += x1[0]; acc[5] += x1[1]; acc[6] += x1[2]; acc[7] += x1[3];
+    }
+    float* dst = nu + gs * kD + d0;
+    *reinterpret_cast<f32x4*>(dst) =
+        f32x4{(float)(acc[0] / kTreeFanout), (float)(acc[1] / kTreeFanout),
+              (float)(acc[2] / kTreeFanout), (float)(acc[3] / kTreeFanout)};
+    *reinterpret_cast<f32x4*>(dst + 4) =
+        f32x4{(float)(acc[4] / kTreeFanout), (float)(acc[5] / kTreeFanout),
+              (float)(acc[6] / kTreeFanout), (float)(acc[7] / kTreeFanout)};
+}
+
+// Slot `beam` of each row's slot list: the incomplete tail node S = E / 16
+// when it holds candidates (16 S < E), else -1.
+__global__ __launch_bounds__(256) void k_tree_tail(int32_t* __restrict__ slots, int beam,
+                                                   int64_t rows, int N, int bs, int window) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows) return;
+    const int E = eligible_blocks((int)(row % N), bs, window);
+    const int S = E >> kTreeFanoutLog2;
+    slots[row * (beam + 1) + beam] = (S << kTreeFanoutLog2) < E ? S : -1;
+}
+
 // ------------------------------------------------------------ host side
 static int route_heads(const Geometry& g) { return g.consensus ? g.Hkv : g.Hq; }
 
@@ -911,7 +956,48 @@ static RouteLayout route_layout(const Geometry& g) {
     return L;
 }
 
-size_t route_workspace_bytes(const Geometry& g) { return route_layout(g).total; }
+// Two-level routing: the first level is flat routing over the complete
+// nodes (a geometry with nb = nodes and top_k = beam), followed by the node
+// summaries, the slot lists, the block means' bf16 hi/lo split and the
+// second level's own workspace.
+struct TreeRouteLayout {
+    RouteLayout L1;
+    size_t lvl1, nu, slots, bhi, blo, bnorm, lvl2, total;
+    int nn, nb_pad;
+};
+
+static Geometry tree_level1_geometry(const Geometry& g) {
+    Geometry g1 = g;
+    g1.nb = g.nb >> kTreeFanoutLog2;
+    g1.top_k = g.beam;
+    return g1;
+}
+
+static TreeRouteLayout tree_route_layout(const Geometry& g) {
+    TreeRouteLayout T{};
+    const size_t nbg = (size_t)g.B * g.Hkv;
+    const size_t rows = (size_t)g.B * g.Hq * g.N;
+    T.nn = g.nb >> kTreeFanoutLog2;
+    T.nb_pad = (g.nb + RT_CH - 1) / RT_CH * RT_CH;
+    size_t off = 0;
+    T.lvl1 = off;
+    if (T.nn > 0) {
+        T.L1 = route_layout(tree_level1_geometry(g));
+        off += align_up(T.L1.total, 256);
+    }
+    T.nu = off;    off += align_up(nbg * (T.nn > 0 ? T.nn : 1) * kD * 4, 256);
+    T.slots = off; off += align_up(rows * (g.beam + 1) * 4, 256);
+    T.bhi = off;   off += align_up(nbg * T.nb_pad * kD * 2, 256);
+    T.blo = off;   off += align_up(nbg * T.nb_pad * kD * 2, 256);
+    T.bnorm = off; off += align_up(2 * nbg * g.nb * 4, 256);
+    T.lvl2 = off;  off += tree_level2_bytes(g);
+    T.total = off;
+    return T;
+}
+
+size_t route_workspace_bytes(const Geometry& g) {
+    return g.beam > 0 ? tree_route_layout(g).total : route_layout(g).total;
+}
 
 template <bool CAUSAL, bool QF32>
 static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
@@ -921,8 +1007,12 @@ static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
     hipLaunchKernelGGL((k_route_fallback<CAUSAL, QF32>), dim3(FB_GRID), dim3(256), 0, s, a);
 }
 
-hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar, int32_t* idx,
-                        void* ws, hipStream_t s, const hipEvent_t* ev) {
+// Flat routing of g's rows over g.nb summaries `summ` into idx (row stride
+// idx_stride), candidates E >> cshift in causal mode; ws holds
+// route_layout(g).
+static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* summ,
+                             int32_t* idx, int idx_stride, int cshift, void* ws, hipStream_t s,
+                             const hipEvent_t* ev) {
     char* base = static_cast<char*>(ws);
     const RouteLayout L = route_layout(g);
     const int nbg = g.B * g.Hkv;
@@ -939,7 +1029,7 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     const int heads = route_heads(g);
     a.q = q;
     a.qbar = g.consensus ? qsum : qbar;
-    a.kbar = kbar;
+    a.kbar = summ;
     a.khi = khi;
     a.klo = klo;
     a.pk = pk;
@@ -956,6 +1046,8 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     a.tiles = (a.P + RT_ROWS - 1) / RT_ROWS;
     a.items = g.B * heads * a.tiles;
     a.nb_pad = L.nb_pad;
+    a.cshift = cshift;
+    a.idx_stride = idx_stride;
     hipError_t e = launch_fill_u32(a.ovf_count, 1, 0u, s);
     if (e != hipSuccess) return e;
     if (!g.causal) {
@@ -974,7 +1066,7 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     }
     const int64_t prep_threads = (int64_t)nbg * L.nb_pad * 8;
     hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
-                       kbar, khi, klo, pk, plo, nbg, g.nb, L.nb_pad);
+                       summ, khi, klo, pk, plo, nbg, g.nb, L.nb_pad);
     hipLaunchKernelGGL(k_prefix_max, dim3((unsigned)(2 * nbg)), dim3(1024), 0, s, pk, g.nb);
     const dim3 grid((unsigned)(((int64_t)a.items + 7) / 8 * 8));  // a multiple of the XCD count
     if (g.causal && !g.consensus)
@@ -983,8 +1075,52 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
         launch_route_kernels<true, true>(a, grid, s, ev);
     else
         launch_route_kernels<false, true>(a, grid, s, ev);
-    mark(ev, 3, s);
     return hipGetLastError();
+}
+
+// Two-level routing (causal, per query head).  Stage events: 2 after the
+// first level and the tail slots, 3 after the second level.
+static hipError_t route_tree(const Geometry& g, const uint16_t* q, const float* kbar,
+                             int32_t* idx, void* ws, hipStream_t s, const hipEvent_t* ev) {
+    char* base = static_cast<char*>(ws);
+    const TreeRouteLayout T = tree_route_layout(g);
+    const int nbg = g.B * g.Hkv;
+    const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+    const int stride = g.beam + 1;
+    float* nu = reinterpret_cast<float*>(base + T.nu);
+    int32_t* slots = reinterpret_cast<int32_t*>(base + T.slots);
+    uint16_t* bhi = reinterpret_cast<uint16_t*>(base + T.bhi);
+    uint16_t* blo = reinterpret_cast<uint16_t*>(base + T.blo);
+    float* bn = reinterpret_cast<float*>(base + T.bnorm);
+    hipError_t e;
+    if (T.nn > 0) {
+        const int64_t n = (int64_t)nbg * T.nn * 8;
+        hipLaunchKernelGGL(k_node_means, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kbar,
+                           nu, g.nb, T.nn, n);
+        e = route_flat(tree_level1_geometry(g), q, nu, slots, stride, kTreeFanoutLog2,
+                       base + T.lvl1, s, nullptr);
+    } else {
+        e = launch_fill_u32(reinterpret_cast<uint32_t*>(slots), (size_t)rows * stride,
+                            0xFFFFFFFFu, s);
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tree_tail, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, slots,
+                       g.beam, rows, g.N, g.bs, g.window);
+    const int64_t prep_threads = (int64_t)nbg * T.nb_pad * 8;
+    hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
+                       kbar, bhi, blo, bn, bn + (size_t)nbg * g.nb, nbg, g.nb, T.nb_pad);
+    mark(ev, 2, s);
+    e = launch_tree_level2(g, q, bhi, blo, T.nb_pad, slots, idx, base + T.lvl2, s);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar, int32_t* idx,
+                        void* ws, hipStream_t s, const hipEvent_t* ev) {
+    hipError_t e = g.beam > 0 ? route_tree(g, q, kbar, idx, ws, s, ev)
+                              : route_flat(g, q, kbar, idx, g.top_k, 0, ws, s, ev);
+    mark(ev, 3, s);
+    return e;
 }
 
 hipError_t launch_route_cumulant(const Geometry& g, const uint16_t* q, const uint16_t* k,

@@ -1,0 +1,252 @@
+// Second level of two-level routing (SSA page, "Algorithm and complexity":
+// a hierarchical router with fixed block size and budget, the measured tree
+// at fanout 16).  The first level (in the routing file) leaves, per causal
+// row, a slot list: the beam of kept nodes (16 consecutive key blocks each,
+// ascending, -1 padded) followed by the row's incomplete tail node, if any.
+// Here every block of those nodes is scored and the row's top-k taken:
+//   1. k_bucket<false> / k_bucket_scan / k_bucket<true> group the (row, slot)
+//      pairs by node, as the attention groups them by block;
+//   2. k_tree_score: one node's 16 block means (bf16 hi + lo) in LDS against
+//      up to 64 gathered query rows, on 16x16x32 bf16 MFMA tiles: 16 scores
+//      per pair (fp32 accuracy), written by pair position (contiguous);
+//   3. k_tree_select: one lane per row walks its used slots in ascending
+//      node order and keeps the 16 best (score, block) pairs; blocks arrive
+//      in ascending order, so a newcomer beats a kept entry exactly when its
+//      score is strictly larger (ties stay with the lower block).  Blocks of
+//      the tail node past the row's candidates are skipped.
+// The node-major scoring gathers one 128-byte query row per pair instead of
+// a node's 4 KB of block means per pair.
+#include <math.h>
+
+#include <algorithm>
+
+#include "bucket.hpp"
+#include "lsa_common.hpp"
+#include "lsa_launch.hpp"
+
+namespace lsa {
+
+constexpr int TR_PITCH = 72;  // LDS pitch of the staged block means (bf16)
+
+struct TreeScoreArgs {
+    const uint16_t* q;         // [B,Hq,N,64] bf16
+    const uint16_t* bhi;       // block means, bf16 hi part [B*Hkv][nb_pad][64]
+    const uint16_t* blo;       // bf16 lo part
+    const uint32_t* pairs;     // pair ids in node order
+    const uint32_t* offsets;   // [NB+1]
+    const uint32_t* unit_off;  // [NB+1]
+    float* scores;             // [npairs + 64][16] by pair position
+    uint32_t dummy_pos;        // npairs: first of 64 rows written by lanes without a pair
+    int nodes, NB, nb_pad, sp_log2;
+};
+
+// One resident wave of workgroups; each takes a contiguous range of 64-pair
+// units, so a node's block means are staged once for all its units.  Wave w
+// owns pairs 16w..16w+15 of a unit.  Tiles D = Kbar_node . Q^T: lane l holds
+// pair l%16 and blocks 4(l/16)+r, i.e. 16 contiguous bytes of the pair's
+// 64-byte score row.
+__global__ __launch_bounds__(256, 4) void k_tree_score(TreeScoreArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 s_h[kTreeFanout * TR_PITCH];
+    __shared__ __attribute__((aligned(16))) __bf16 s_l[kTreeFanout * TR_PITCH];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t U = uniform_load(a.unit_off + a.NB);
+    const uint32_t per = (U + gridDim.x - 1) / gridDim.x;
+    const uint32_t u0 = blockIdx.x * per;
+    const uint32_t u1 = min(U, u0 + per);
+    if (u0 >= u1) return;
+    UnitCursor cur;
+    cur.seek(a.unit_off, a.NB, u0);
+    const uint32_t my = 16 * w + (lane & 15);
+    int loaded = -1;
+    for (uint32_t u = u0; u < u1; ++u) {
+        uint32_t p0, p1;
+        cur.rows(a.unit_off, a.offsets, u, p0, p1);
+        // every lane loads (a pair id, a query row), lanes past the unit's
+        // end use pair 0 and store to a dummy row
+        const bool valid = p0 + my < p1;
+        const uint32_t pid = a.pairs[valid ? p0 + my : 0u];
+        const uint16_t* qrow = a.q + (int64_t)(pid >> a.sp_log2) * kD + 8 * (lane >> 4);
+        const bf16x8 b0 = load_bf16x8(qrow);
+        const bf16x8 b1 = load_bf16x8(qrow + 32);
+        if (cur.bucket != loaded) {
+            __syncthreads();
+            const int bg = cur.bucket / a.nodes, node = cur.bucket - bg * a.nodes;
+            // 16 rows x 8 chunks of 16 bytes, hi then lo: one chunk per thread
+            const int part = tid >> 7, r = (tid >> 3) & 15, ch = tid & 7;
+            const uint16_t* src = (part ? a.blo : a.bhi) +
+                                  ((int64_t)bg * a.nb_pad + node * kTreeFanout + r) * kD + 8 * ch;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+            *reinterpret_cast<u32x4*>((part ? s_l : s_h) + r * TR_PITCH + 8 * ch) = v;
+            __syncthreads();
+            loaded = cur.bucket;
+        }
+        const int ar = lane & 15, ak = 8 * (lane >> 4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(*reinterpret_cast<const bf16x8*>(s_h + ar * TR_PITCH + ak), b0, acc);
+        acc = mfma16(*reinterpret_cast<const bf16x8*>(s_l + ar * TR_PITCH + ak), b0, acc);
+        acc = mfma16(*reinterpret_cast<const bf16x8*>(s_h + ar * TR_PITCH + 32 + ak), b1, acc);
+        acc = mfma16(*reinterpret_cast<const bf16x8*>(s_l + ar * TR_PITCH + 32 + ak), b1, acc);
+        const uint32_t pos = valid ? p0 + my : a.dummy_pos + my;
+        *reinterpret_cast<f32x4*>(a.scores + (int64_t)pos * kTreeFanout + 4 * (lane >> 4)) = acc;
+    }
+}
+
+struct TreeSelectArgs {
+    const int32_t* slots;  // [rows][beam + 1]
+    const uint32_t* rev;   // [beam + 1][rows] pair positions, ~0 when the slot is unused
+    const float* scores;   // [npairs][16] by position
+    int32_t* idx;          // [rows][top_k]
+    int64_t rows;
+    int N, bs, window, top_k, beam;
+};
+
+__global__ __launch_bounds__(256) void k_tree_select(TreeSelectArgs a) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= a.rows) return;
+    const int t = (int)(row % a.N);
+    const int E = eligible_blocks(t, a.bs, a.window);
+    const int stride = a.beam + 1;
+    float Ls[kMaxTopK];
+    int Lc[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        Ls[j] = -INFINITY;
+        Lc[j] = 0;
+    }
+    int ncand = 0;
+    for (int j = 0; j < stride; ++j) {
+        const uint32_t pos = a.rev[(int64_t)j * a.rows + row];
+        if (pos == 0xFFFFFFFFu) continue;
+        const int node = a.slots[row * stride + j];
+        const float* sp = a.scores + (int64_t)pos * kTreeFanout;
+        float sc[kTreeFanout];
+#pragma unroll
+        for (int i4 = 0; i4 < kTreeFanout / 4; ++i4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sp + 4 * i4);
+            sc[4 * i4] = v[0]; sc[4 * i4 + 1] = v[1]; sc[4 * i4 + 2] = v[2]; sc[4 * i4 + 3] = v[3];
+        }
+        const int c0 = node * kTreeFanout;
+        const int nvalid = min(kTreeFanout, E - c0);
+        ncand += nvalid;
+#pragma unroll
+        for (int i = 0; i < kTreeFanout; ++i) {
+            float x = sc[i];
+            if (i < nvalid && x > Ls[kMaxTopK - 1]) {
+                int xc = c0 + i;
+#pragma unroll
+                for (int s = 0; s < kMaxTopK; ++s) {
+                    const bool gt = x > Ls[s];
+                    const float ts = Ls[s];
+                    const int tc = Lc[s];
+                    Ls[s] = gt ? x : ts;
+                    Lc[s] = gt ? xc : tc;
+                    x = gt ? ts : x;
+                    xc = gt ? tc : xc;
+                }
+            }
+        }
+    }
+    // the chosen blocks in ascending order, -1 padded
+    const int m = ncand < a.top_k ? ncand : a.top_k;
+    uint32_t cs[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) cs[j] = j < m ? (uint32_t)Lc[j] : 0xFFFFFFFFu;
+#pragma unroll
+    for (int size = 2; size <= kMaxTopK; size <<= 1)
+#pragma unroll
+        for (int stride2 = size >> 1; stride2 > 0; stride2 >>= 1)
+#pragma unroll
+            for (int i = 0; i < kMaxTopK; ++i) {
+                const int jx = i ^ stride2;
+                if (jx > i) {
+                    const uint32_t x = cs[i], y = cs[jx];
+                    const uint32_t mx = x > y ? x : y, mn = x > y ? y : x;
+                    if ((i & size) == 0) { cs[i] = mn; cs[jx] = mx; }
+                    else { cs[i] = mx; cs[jx] = mn; }
+                }
+            }
+    int32_t* out = a.idx + row * a.top_k;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < a.top_k) out[j] = j < m ? (int32_t)cs[j] : -1;
+}
+
+// ------------------------------------------------------------ host side
+struct TreeLayout {
+    size_t counts, offsets, cursor, unit_off, pairs, rev, scores, total;
+    int nodes, NB;
+};
+
+static TreeLayout tree_layout(const Geometry& g) {
+    TreeLayout L{};
+    L.nodes = (g.nb + kTreeFanout - 1) / kTreeFanout;
+    L.NB = g.B * g.Hkv * L.nodes;
+    const size_t rows = (size_t)g.B * g.Hq * g.N;
+    const size_t slots = (size_t)g.beam + 1;
+    size_t off = 0;
+    L.counts = off;   off += align_up(((size_t)L.NB + 1) * 4, 256);
+    L.offsets = off;  off += align_up(((size_t)L.NB + 1) * 4, 256);
+    L.cursor = off;   off += align_up(((size_t)L.NB + 1) * 4, 256);
+    L.unit_off = off; off += align_up(((size_t)L.NB + 1) * 4, 256);
+    L.pairs = off;    off += align_up(rows * slots * 4, 256);
+    L.rev = off;      off += align_up(rows * slots * 4, 256);
+    L.scores = off;   off += align_up((rows * slots + 64) * kTreeFanout * 4, 256);
+    L.total = off;
+    return L;
+}
+
+size_t tree_level2_bytes(const Geometry& g) { return tree_layout(g).total; }
+
+hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16_t* bhi,
+                              const uint16_t* blo, int nb_pad, const int32_t* slots, int32_t* idx,
+                              void* ws, hipStream_t s) {
+    const TreeLayout L = tree_layout(g);
+    char* base = static_cast<char*>(ws);
+    uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
+    uint32_t* offsets = reinterpret_cast<uint32_t*>(base + L.offsets);
+    uint32_t* cursor = reinterpret_cast<uint32_t*>(base + L.cursor);
+    uint32_t* unit_off = reinterpret_cast<uint32_t*>(base + L.unit_off);
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(base + L.pairs);
+    uint32_t* rev = reinterpret_cast<uint32_t*>(base + L.rev);
+    float* scores = reinterpret_cast<float*>(base + L.scores);
+    const int nslots = g.beam + 1;
+    const int sp_log2 = pair_stride_log2(nslots);
+    const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+    const int nbg = g.B * g.Hkv;
+
+    hipError_t e = launch_fill_u32(counts, (size_t)L.NB, 0u, s);
+    if (e != hipSuccess) return e;
+    const int rep = g.Hq / g.Hkv;
+    int64_t tc = std::max<int64_t>(
+        (4096 + rep - 1) / rep,
+        (4 * (int64_t)L.nodes + (int64_t)rep * nslots - 1) / ((int64_t)rep * nslots));
+    tc = std::min<int64_t>((tc + 63) / 64 * 64, g.N);
+    BucketArgs ba{slots, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, g.N, g.bs, L.nodes, nslots,
+                  g.window, (int)tc, sp_log2, 0, kTreeFanoutLog2};
+    const int nch = (int)((g.N + tc - 1) / tc);
+    const dim3 bgrid((unsigned)(nbg * nch));
+    const size_t lds = L.nodes <= BK_LDS_MAX ? (size_t)L.nodes * 4 : 0;
+    hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
+    hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
+                       L.NB);
+    hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
+
+    TreeScoreArgs sa{q, bhi, blo, pairs, offsets, unit_off, scores,
+                     (uint32_t)(rows * nslots), L.nodes, L.NB, nb_pad, sp_log2};
+    static int grid = 0;
+    if (grid == 0) {
+        int dev = 0, cus = 256, per_cu = 4;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tree_score, 256, 0);
+        grid = cus * (per_cu > 0 ? per_cu : 1);
+    }
+    hipLaunchKernelGGL(k_tree_score, dim3(grid), dim3(256), 0, s, sa);
+
+    TreeSelectArgs ta{slots, rev, scores, idx, rows, g.N, g.bs, g.window, g.top_k, g.beam};
+    hipLaunchKernelGGL(k_tree_select, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, ta);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -35,7 +35,8 @@ class LsaParams(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("consensus", ctypes.c_int32), ("beta", ctypes.c_float)]
+                ("consensus", ctypes.c_int32), ("beta", ctypes.c_float),
+                ("beam", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(LsaParams)
@@ -85,9 +86,9 @@ def library():
 
 
 def params(batch, q_heads, kv_heads, seq_len, head_dim=64, block=64, top_k=16, window=512,
-           causal=1, scale=0.0, consensus=0, beta=0.0) -> LsaParams:
+           causal=1, scale=0.0, consensus=0, beta=0.0, beam=0) -> LsaParams:
     return LsaParams(batch, q_heads, kv_heads, seq_len, head_dim, block, top_k, window, causal,
-                     float(scale), consensus, float(beta))
+                     float(scale), consensus, float(beta), beam)
 
 
 def idx_shape(p: LsaParams):

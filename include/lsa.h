@@ -61,6 +61,9 @@ typedef struct lsa_params {
     float beta;        /* second-cumulant weight of the routing score (see
                           lsa_route_cumulant); 0: the block-mean score.  Must be
                           finite; nonzero needs causal = 1 and consensus = 0 */
+    int32_t beam;      /* two-level routing: nodes kept per query (see
+                          lsa_route_topk); 0: flat routing.  1..15, needs
+                          causal = 1, consensus = 0 and beta = 0 */
 } lsa_params;
 
 typedef enum lsa_status {
@@ -115,6 +118,16 @@ lsa_status lsa_block_summarize(const lsa_params *p, const void *x, int32_t heads
  *   top-k and tie-break as above.  idx [B, Hkv, N, top_k] (image mode
  *   [B, Hkv, N/bs, top_k]); every query head of the group attends through
  *   its group's route.
+ * Two-level routing (beam > 0; SSA page, "Algorithm and complexity": a
+ *   hierarchical router with fixed block size and budget, the measured tree
+ *   at fanout 16): nodes group 16 consecutive key blocks and are summarised
+ *   by the mean of their block means (fp32).  Row t scores its S =
+ *   floor(E(t)/16) complete candidate nodes, keeps the best min(beam, S)
+ *   (ties to the lower node), and takes its top-k among the blocks of those
+ *   nodes plus the tail blocks [16 S, E(t)) of the incomplete node.  With
+ *   beam >= S every candidate is scored and the result is the flat
+ *   selection.  Routing work per row falls from E(t) to about
+ *   E(t)/16 + 16 beam + 15 scores.
  * beta != 0 is LSA_ERR_UNSUPPORTED here: that score needs the keys
  * themselves (lsa_route_cumulant). */
 lsa_status lsa_route_topk(const lsa_params *p, const void *q, const float *kbar,
@@ -178,7 +191,7 @@ lsa_status lsa_forward(const lsa_params *p, const void *q, const void *k,
  * cache_len must be a multiple of bs; workspace: lsa_workspace_bytes(p with
  * seq_len = cache_len, LSA_OP_DECODE) bytes, enough for every T <= cache_len.
  * Scores and softmax run in fp32 (no bf16 rounding of probabilities).
- * consensus and beta must be 0 (LSA_ERR_UNSUPPORTED otherwise). */
+ * consensus, beta and beam must be 0 (LSA_ERR_UNSUPPORTED otherwise). */
 lsa_status lsa_decode(const lsa_params *p, int32_t cache_len, const void *q,
                       const void *k_cache, const void *v_cache, float *kbar_cache,
                       float *out, int32_t *idx_out, void *workspace,

@@ -74,3 +74,53 @@ def check_output(out_gpu, out_ref, vmax_row):
     worst = float(np.max(row_err / np.maximum(vmax_row, 1e-30)))
     assert worst <= REL_V, worst
     return max_abs, mean_abs
+
+
+def check_tree_routing(idx_gpu, idx_orc, det, block_scores, ncand, k, beam, fanout=16):
+    """Two-level routing parity.  Rows whose node-level and block-level gaps
+    both exceed GAP must match the oracle bit for bit.  Any other row that
+    differs must be a valid outcome: some beam B* of min(beam, S) complete
+    candidate nodes, holding every node that beats the beam-th node score by
+    more than GAP and only nodes within GAP of it otherwise, for which the
+    GPU set is a valid top-k (within GAP) of B*'s blocks plus the tail.
+    det: the oracle's details (gap1, gap2, node_scores); block_scores: [R, nb]
+    fp64 oracle block scores.  Returns (n_clear_mismatch, n_near,
+    n_near_differing)."""
+    idx_gpu = np.asarray(idx_gpu)
+    idx_orc = np.asarray(idx_orc)
+    clear = (det["gap1"] > GAP) & (det["gap2"] > GAP)
+    differ = np.any(idx_gpu != idx_orc, axis=1)
+    bad_clear = int(np.sum(differ & clear))
+    near_rows = np.nonzero(differ & ~clear)[0]
+    for r in near_rows:
+        E = int(ncand[r])
+        S = E // fanout
+        nb_keep = min(beam, S)
+        ns = det["node_scores"][r][:S]
+        s = block_scores[r]
+        order = np.sort(ns)[::-1]
+        th = order[nb_keep - 1] if S > nb_keep else -np.inf
+        certain = [x for x in range(S) if ns[x] > th + GAP] if S > nb_keep else list(range(S))
+        maybe = [x for x in range(S) if abs(ns[x] - th) <= GAP and x not in certain] \
+            if S > nb_keep else []
+        sel = idx_gpu[r]
+        tail = list(range(S * fanout, E))
+        m = min(k, fanout * nb_keep + len(tail))
+        assert np.all(sel[m:] == -1), (r, sel)
+        chosen = sel[:m]
+        assert np.all(chosen >= 0) and np.all(chosen < E) and np.all(np.diff(chosen) > 0), (r, sel)
+        nodes = set(int(c) // fanout for c in chosen if c < S * fanout)
+        assert nodes <= set(certain) | set(maybe), (r, sorted(nodes), certain, maybe)
+        used_maybe = nodes - set(certain)
+        free = nb_keep - len(certain) - len(used_maybe)
+        assert free >= 0, (r, len(certain), len(used_maybe), nb_keep)
+        lo = s[chosen].min() if m else np.inf
+        opened = set(certain) | used_maybe
+        rest = [c for x in opened for c in range(x * fanout, x * fanout + fanout)] + tail
+        rest = np.setdiff1d(np.array(rest, dtype=np.int64), chosen)
+        if rest.size:
+            assert s[rest].max() <= lo + GAP, (r, s[rest].max(), lo)
+        harmless = [x for x in maybe if x not in used_maybe
+                    and s[x * fanout:(x + 1) * fanout].max() <= lo + GAP]
+        assert len(harmless) >= free, (r, len(harmless), free)
+    return bad_clear, int(np.sum(~clear)), len(near_rows)

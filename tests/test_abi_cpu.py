@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header(lsa):
-    assert ctypes.sizeof(lsa.LsaParams) == 48
+    assert ctypes.sizeof(lsa.LsaParams) == 52
+    assert lsa.LsaParams.beam.offset == 48
     assert lsa.LsaParams.consensus.offset == 40
     assert lsa.LsaParams.beta.offset == 44
 
@@ -53,7 +54,9 @@ def good(lsa, **kw):
     (dict(causal=0, window=512, block=16), 2), (dict(causal=2), 2), (dict(batch=0), 2),
     (dict(consensus=2), 2), (dict(consensus=-1), 2), (dict(beta=float("nan")), 2),
     (dict(beta=float("inf")), 2), (dict(beta=0.5, consensus=1), 3),
-    (dict(beta=0.5, causal=0, window=0, block=16), 3),
+    (dict(beta=0.5, causal=0, window=0, block=16), 3), (dict(beam=-1), 2), (dict(beam=16), 3),
+    (dict(beam=4, consensus=1), 3), (dict(beam=4, beta=0.5), 3),
+    (dict(beam=4, causal=0, window=0, block=16), 3),
     (dict(head_dim=128), 3), (dict(top_k=17), 3), (dict(block=48, window=96, seq_len=960), 3),
     (dict(causal=0, window=0, block=64), 3), (dict(seq_len=1 << 24, block=16, window=512), 3),
 ])
@@ -123,3 +126,14 @@ def test_cumulant_routing_checks(lsa):
     assert L.lsa_route_cumulant(ctypes.byref(p), a, ctypes.c_void_p(4100), a, None) == 4
     assert L.lsa_route_cumulant(ctypes.byref(good(lsa, beta=0.5, consensus=1)), a, a, a, None) == 3
     assert L.lsa_workspace_bytes(ctypes.byref(p), lsa.OP_DECODE) == lsa.SIZE_MAX
+
+
+def test_tree_routing_workspace(lsa):
+    """Two-level routing adds, per row, beam + 1 slots, pair ids, positions
+    and 64-byte score rows to the routing workspace; decode refuses it."""
+    p, pt = good(lsa), good(lsa, beam=8)
+    rows = 14 * 131072
+    extra = lsa.workspace_bytes(pt, lsa.OP_ROUTE)
+    assert rows * 9 * (4 + 4 + 4 + 64) <= extra <= rows * 9 * (4 + 4 + 4 + 64) + (64 << 20)
+    assert lsa.workspace_bytes(pt, lsa.OP_ATTEND) == lsa.workspace_bytes(p, lsa.OP_ATTEND)
+    assert lsa.library().lsa_workspace_bytes(ctypes.byref(pt), lsa.OP_DECODE) == lsa.SIZE_MAX
