@@ -7,18 +7,24 @@
 //
 // A decode step is latency-bound and touches little data (per query head
 // about top_k + window/bs blocks of K/V and the eligible block means), so it
-// runs on the vector ALUs in fp32 with enough workgroups to spread the reads:
-//   0. k_decode_summarize   the mean of the block that token T-1 completes
-//                           (when T is a multiple of bs), kept in the caller's
-//                           block-mean cache for later steps.
-//   1. k_decode_route_chunk scores q . kbar_c for a chunk of 1024 eligible
-//                           blocks per workgroup and keeps the chunk's top-k
-//                           as 64-bit keys (score, then lower index).
-//   2. k_decode_route_merge merges the chunk lists of a row into its top-k and
-//                           writes the block ids in ascending order.
-//   3. k_decode_attend      one workgroup per query head: exact softmax over
-//                           the routed blocks and the block-aligned window,
-//                           in passes of 1024 keys with an online softmax.
+// runs on the vector ALUs in fp32, in two launches with enough workgroups to
+// spread the reads:
+//   1. k_decode_route   per (row, chunk of 1024 eligible blocks): scores
+//                       q . kbar_c and keeps the chunk's top-k keys (score,
+//                       then lower index).  Extra workgroups write the mean
+//                       of the block that token T-1 completes (when T is a
+//                       multiple of bs) into the caller's block-mean cache;
+//                       no routing of this step reads that block, which
+//                       lies in the window.
+//   2. k_decode_attend  per (row, split of 256 keys): merges the row's chunk
+//                       lists into its top-k, then an exact softmax over its
+//                       share of the routed blocks and the block-aligned
+//                       window; the last split of a row to finish (a device
+//                       counter) combines the row's partial (max, mass,
+//                       output) triples.
+// Top-k sets are found by a radix select over the 64-bit keys with wave
+// ballots: the k-th largest key is built bit by bit from the count of keys
+// at or above each candidate, so no shuffles or LDS round trips are needed.
 #include <math.h>
 
 #include <algorithm>
@@ -29,17 +35,20 @@
 namespace lsa {
 
 constexpr int DC_CHUNK = 1024;  // candidate blocks per routing workgroup
-constexpr int DC_KEYS = 1024;   // keys per attention pass
+constexpr int DC_SPLIT = 256;   // keys per attention workgroup
+constexpr int DC_MAXCH = 64;    // chunk lists per row (E <= nb <= 65536)
 
 struct DecodeArgs {
     const uint16_t* q;   // [B*Hq][64]
     const uint16_t* k;   // [B*Hkv][t_max][64]
     const uint16_t* v;   // [B*Hkv][t_max][64]
     float* kbar;         // [B*Hkv][t_max/bs][64]
-    int32_t* idx;        // [B*Hq][top_k]
+    int32_t* idx;        // [B*Hq][top_k] or NULL
     float* out;          // [B*Hq][64]
-    uint64_t* keys;      // [B*Hq][nchunk][kMaxTopK]
-    int Hq, Hkv, T, t_max, bs, top_k, window, E, nchunk;
+    uint64_t* keys;      // [B*Hq][nchunk][kMaxTopK] chunk key sets, zero-padded
+    uint32_t* counters;  // [B*Hq] finished splits per row
+    float* part;         // [B*Hq][nsplit][2 + 64]: max, mass, output (log2 domain)
+    int rows, Hq, Hkv, T, t_max, bs, top_k, window, E, nchunk, nsplit, summ_block;
     float scale_log2;
 };
 
@@ -65,65 +74,87 @@ __device__ __forceinline__ float block_sum_f32(float x, float* s_red) {
     return r;
 }
 
-// ------------------------------------------------------------ 0. block mean
-// One wave per (b, KV head): the mean of block c (tokens [c*bs, c*bs + bs)),
-// summed in fp64 and rounded once to fp32, as lsa_block_summarize does.
-__global__ __launch_bounds__(64) void k_decode_summarize(DecodeArgs a, int c) {
-    const int bg = blockIdx.x, lane = threadIdx.x;
-    const int dg = lane & 7, j0 = lane >> 3;
-    const uint16_t* base = a.k + ((int64_t)bg * a.t_max + (int64_t)c * a.bs) * kD + dg * 8;
-    double acc[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[d] = 0.0;
-    for (int j = j0; j < a.bs; j += 8) {
-        float f[8];
-        unpack8(*reinterpret_cast<const u32x4*>(base + (int64_t)j * kD), f);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
-    }
-#pragma unroll
-    for (int m = 8; m < 64; m <<= 1)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] += __shfl_xor(acc[d], m, kWave);
-    if (j0 == 0) {
-        const double inv = 1.0 / (double)a.bs;  // a power of two: exact
-        float* o = a.kbar + ((int64_t)bg * (a.t_max / a.bs) + c) * kD + dg * 8;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[d] = (float)(acc[d] * inv);
-    }
-}
-
-// ------------------------------------------------------------ top-k helpers
-// The wave's keys are key[0..n) in every lane; returns, in every lane, the
-// largest key below `below` over the wave (0 if none).
+// ------------------------------------------------------------ wave radix select
+// The k-th largest of the wave's nonzero keys (0 when fewer than k are
+// nonzero), built from the most significant bit down: a bit is set when at
+// least k keys reach the candidate.  Keys are distinct, so exactly
+// min(k, #nonzero) keys are >= the result and nonzero.
 template <int n>
-__device__ __forceinline__ uint64_t wave_max_below(const uint64_t (&key)[n], uint64_t below) {
-    uint64_t best = 0;
+__device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&key)[n], int k) {
+    uint64_t th = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = th | (1ull << bit);
+        int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < n; ++i)
-        if (key[i] < below && key[i] > best) best = key[i];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t o = __shfl_xor(best, off, kWave);
-        best = o > best ? o : best;
+        for (int i = 0; i < n; ++i) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= cand));
+        if (cnt >= k) th = cand;
     }
-    return best;
+    return th;
 }
 
-// ------------------------------------------------------------ 1. chunk top-k
+// Appends the wave's keys >= th (and nonzero) to list[0..), in lane order;
+// returns their number (wave-uniform).
+template <int n>
+__device__ __forceinline__ int wave_compact(const uint64_t (&key)[n], uint64_t th, uint64_t* list) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+        const bool sel = key[i] != 0 && key[i] >= th;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
+        if (sel) list[base + __popcll(m & below)] = key[i];
+        base += __popcll(m);
+    }
+    return base;
+}
+
+// ------------------------------------------------------------ 1. routing
 // Workgroup (row, chunk): fp32 scores of the chunk's eligible blocks (the dot
-// product accumulated over d in order).  Each wave extracts the top_k of its
-// 256 candidates by rounds of "largest key below the previous one"; the first
-// wave then does the same over the four wave lists.  The chunk list is
-// written in descending order, ended by a zero key when shorter than top_k.
-__global__ __launch_bounds__(256) void k_decode_route_chunk(DecodeArgs a) {
+// product accumulated over d in order); each wave selects its top_k, then the
+// first wave selects the chunk's top_k among the four wave sets.  Workgroups
+// past rows * nchunk update the block-mean cache instead (one per KV head);
+// workgroup 0 also clears the rows' split counters for step 2.
+__global__ __launch_bounds__(256) void k_decode_route(DecodeArgs a) {
     __shared__ float s_q[kD];
-    __shared__ uint64_t s_list[4][kMaxTopK];
+    __shared__ uint64_t s_list[4 * kMaxTopK];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nroute = a.rows * a.nchunk;
+    if ((int)blockIdx.x >= nroute) {
+        // the mean of block summ_block (tokens [c*bs, c*bs + bs)), fp64 sum,
+        // one fp32 rounding, as lsa_block_summarize
+        if (w != 0) return;
+        const int bg = blockIdx.x - nroute, c = a.summ_block;
+        const int dg = lane & 7, j0 = lane >> 3;
+        const uint16_t* base = a.k + ((int64_t)bg * a.t_max + (int64_t)c * a.bs) * kD + dg * 8;
+        double acc[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[d] = 0.0;
+        for (int j = j0; j < a.bs; j += 8) {
+            float f[8];
+            unpack8(*reinterpret_cast<const u32x4*>(base + (int64_t)j * kD), f);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
+        }
+#pragma unroll
+        for (int m = 8; m < 64; m <<= 1)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[d] += __shfl_xor(acc[d], m, kWave);
+        if (j0 == 0) {
+            const double inv = 1.0 / (double)a.bs;  // a power of two: exact
+            float* o = a.kbar + ((int64_t)bg * (a.t_max / a.bs) + c) * kD + dg * 8;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) o[d] = (float)(acc[d] * inv);
+        }
+        return;
+    }
+    if (blockIdx.x == 0)
+        for (int r = tid; r < a.rows; r += 256) a.counters[r] = 0u;
     const int row = blockIdx.x / a.nchunk, ch = blockIdx.x - row * a.nchunk;
     const int h = row % a.Hq, b = row / a.Hq;
     const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
     if (tid < kD) s_q[tid] = bf16_bits_to_f32(a.q[(int64_t)row * kD + tid]);
+    for (int i = tid; i < 4 * kMaxTopK; i += 256) s_list[i] = 0;
     __syncthreads();
     const int c0 = ch * DC_CHUNK + w * (DC_CHUNK / 4);
     const float* kb = a.kbar + (int64_t)bg * (a.t_max / a.bs) * kD;
@@ -146,193 +177,190 @@ __global__ __launch_bounds__(256) void k_decode_route_chunk(DecodeArgs a) {
             key[i] = sel_key(s, (uint32_t)c);
         }
     }
-    uint64_t prev = ~0ull;
-    for (int j = 0; j < kMaxTopK; ++j) {
-        const uint64_t best = j < a.top_k ? wave_max_below(key, prev) : 0;
-        if (lane == 0) s_list[w][j] = best;
-        prev = best;
-    }
+    wave_compact(key, wave_kth_key(key, a.top_k), s_list + w * kMaxTopK);
     __syncthreads();
     if (w == 0) {
-        uint64_t k4[1];
-        k4[0] = s_list[lane >> 4][lane & 15];
+        uint64_t k1[1] = {s_list[lane]};
+        const uint64_t th = wave_kth_key(k1, a.top_k);
         uint64_t* out = a.keys + ((int64_t)row * a.nchunk + ch) * kMaxTopK;
-        prev = ~0ull;
-        for (int j = 0; j < a.top_k; ++j) {
-            const uint64_t best = wave_max_below(k4, prev);
-            if (lane == 0) out[j] = best;
-            prev = best;
-            if (best == 0) break;
-        }
+        const int n = wave_compact(k1, th, out);
+        if (lane >= n && lane < kMaxTopK) out[lane] = 0;  // zero-pad the set
     }
 }
 
-// ------------------------------------------------------------ 2. merge
-// One wave per row: lane c holds chunk list c (descending, zero-ended), the
-// row's top_k comes from rounds of "largest key below the previous one", and
-// lane j < m writes the j-th smallest chosen block id.
-__global__ __launch_bounds__(256) void k_decode_route_merge(DecodeArgs a, int rows) {
+// The top_k of a row's chunk sets (ntot keys, lane l holding keys l, l+64,
+// ...), appended to list; returns their number.
+template <int NPL>
+__device__ __forceinline__ int merge_chunk_sets(const uint64_t* in, int ntot, int top_k,
+                                                uint64_t* list) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    uint64_t key[kMaxTopK];
-    bool live = lane < a.nchunk;
-    const uint64_t* in = a.keys + ((int64_t)row * a.nchunk + (live ? lane : 0)) * kMaxTopK;
+    uint64_t kk[NPL];
 #pragma unroll
-    for (int i = 0; i < kMaxTopK; ++i) {
-        key[i] = (live && i < a.top_k) ? in[i] : 0;
-        live = live && key[i] != 0;  // entries after the terminating zero are stale
+    for (int i = 0; i < NPL; ++i) {
+        const int j = lane + 64 * i;
+        kk[i] = j < ntot ? in[j] : 0;
     }
-    int32_t sel[kMaxTopK];
-    int m = 0;
-    uint64_t prev = ~0ull;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        const uint64_t best = j < a.top_k ? wave_max_below(key, prev) : 0;
-        sel[j] = best ? (int32_t)key_block(best) : 0x7FFFFFFF;
-        m += best ? 1 : 0;
-        prev = best ? best : prev;
-    }
-    // lane j < top_k: the j-th smallest of the m chosen ids (wave-uniform list)
-    int32_t mine = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        int rank = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxTopK; ++i) rank += sel[i] < sel[j] ? 1 : 0;
-        if (j < m && rank == lane) mine = sel[j];
-    }
-    if (lane < a.top_k) a.idx[(int64_t)row * a.top_k + lane] = lane < m ? mine : -1;
+    return wave_compact(kk, wave_kth_key(kk, top_k), list);
 }
 
-// ------------------------------------------------------------ 3. attention
-// One workgroup per query head.  The keys are the used routed blocks (an
-// entry counts when it is eligible and above the previous used entry) and
-// the window [bs*E, T-1], visited as one virtual list in passes of DC_KEYS:
-// scores (fp32, in log2 units) into LDS, the pass maximum, probabilities,
-// then P.V with thread (key group kg, dims 8dg..8dg+7) summing keys
-// kg, kg+32, ... of the pass.
+// ------------------------------------------------------------ 2. attention
+// Workgroup (row, split): wave 0 merges the row's chunk sets into its top_k
+// blocks (ascending).  The keys are the routed blocks, then the window
+// [bs*E, T-1], as one virtual list; this split takes keys
+// [256 split, 256 split + 256): fp32 scores in log2 units, the split's
+// maximum and mass, and P.V with thread (key group kg, dims 8dg..8dg+7).
+// The split's (max, mass, output) goes to the workspace; the row's last
+// split to finish combines them.
 __global__ __launch_bounds__(256) void k_decode_attend(DecodeArgs a) {
     __shared__ float s_q[kD];
-    __shared__ float s_p[DC_KEYS];
+    __shared__ float s_p[DC_SPLIT];
     __shared__ float s_red[4];
     __shared__ float s_acc[32][kD + 1];
+    __shared__ uint64_t s_sel[kMaxTopK];
     __shared__ int s_blk[kMaxTopK];
-    __shared__ int s_nused;
-    const int tid = threadIdx.x;
-    const int row = blockIdx.x;
+    __shared__ int s_nused, s_last;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int row = blockIdx.x / a.nsplit, sp = blockIdx.x - row * a.nsplit;
     const int h = row % a.Hq, b = row / a.Hq;
     const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
     const uint16_t* kbase = a.k + (int64_t)bg * a.t_max * kD;
     const uint16_t* vbase = a.v + (int64_t)bg * a.t_max * kD;
     if (tid < kD) s_q[tid] = bf16_bits_to_f32(a.q[(int64_t)row * kD + tid]) * a.scale_log2;
-    if (tid == 0) {
-        const int32_t* ir = a.idx + (int64_t)row * a.top_k;
-        int n = 0, prev = -1;
-        for (int s = 0; s < a.top_k; ++s) {
-            const int c = ir[s];
-            if (c > prev && c < a.E) {
-                s_blk[n++] = c;
-                prev = c;
-            }
+    if (w == 0) {
+        const uint64_t* in = a.keys + (int64_t)row * a.nchunk * kMaxTopK;
+        const int ntot = a.nchunk * kMaxTopK;
+        int n;
+        if (ntot <= 64) n = merge_chunk_sets<1>(in, ntot, a.top_k, s_sel);
+        else if (ntot <= 128) n = merge_chunk_sets<2>(in, ntot, a.top_k, s_sel);
+        else if (ntot <= 256) n = merge_chunk_sets<4>(in, ntot, a.top_k, s_sel);
+        else if (ntot <= 512) n = merge_chunk_sets<8>(in, ntot, a.top_k, s_sel);
+        else n = merge_chunk_sets<16>(in, ntot, a.top_k, s_sel);
+        // ascending block ids: rank of each selected id among the n
+        if (lane < n) {
+            const int c = (int)key_block(s_sel[lane]);
+            int rank = 0;
+            for (int i = 0; i < n; ++i) rank += (int)key_block(s_sel[i]) < c ? 1 : 0;
+            s_blk[rank] = c;
         }
-        s_nused = n;
+        if (lane == 0) s_nused = n;
     }
     __syncthreads();
-    const int n_routed = s_nused * a.bs;
+    const int nused = s_nused;
+    if (sp == 0 && a.idx && tid < a.top_k)
+        a.idx[(int64_t)row * a.top_k + tid] = tid < nused ? s_blk[tid] : -1;
+    const int n_routed = nused * a.bs;
     const int win0 = a.bs * a.E;
     const int total = n_routed + (a.T - win0);
+    const int p0 = sp * DC_SPLIT;
+    const int np = max(0, min(DC_SPLIT, total - p0));
     auto token_of = [&](int j) {
         return j < n_routed ? s_blk[j / a.bs] * a.bs + (j % a.bs) : win0 + (j - n_routed);
     };
-    const int kg = tid >> 3, dg = tid & 7;  // P.V: key group, 8-dim group
-    float o_acc[8];  // running output of dims 8dg.. (kept by threads with kg == 0)
+    float s = -INFINITY;
+    if (tid < np) {
+        const uint16_t* kr = kbase + (int64_t)token_of(p0 + tid) * kD;
+        u32x4 raw[kD / 8];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) o_acc[d] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    for (int p0 = 0; p0 < total; p0 += DC_KEYS) {
-        const int np = min(DC_KEYS, total - p0);
-        float mx = -INFINITY;
-        for (int j = tid; j < np; j += 256) {
-            const uint16_t* kr = kbase + (int64_t)token_of(p0 + j) * kD;
-            float s = 0.f;
+        for (int d8 = 0; d8 < kD / 8; ++d8) raw[d8] = *reinterpret_cast<const u32x4*>(kr + 8 * d8);
+        s = 0.f;
 #pragma unroll
-            for (int d8 = 0; d8 < kD / 8; ++d8) {
-                float f[8];
-                unpack8(*reinterpret_cast<const u32x4*>(kr + 8 * d8), f);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s = fmaf(s_q[8 * d8 + e], f[e], s);
-            }
-            s_p[j] = s;
-            mx = fmaxf(mx, s);
-        }
-        mx = block_max_f32(mx, s_red);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-        float sum = 0.f;
-        for (int j = tid; j < np; j += 256) {
-            const float pj = exp2f(s_p[j] - m_new);
-            s_p[j] = pj;
-            sum += pj;
-        }
-        sum = block_sum_f32(sum, s_red);  // its barrier also publishes s_p
-        l_run = l_run * alpha + sum;
-        m_run = m_new;
-        float acc[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] = 0.f;
-        for (int j = kg; j < np; j += 32) {
-            const float pj = s_p[j];
+        for (int d8 = 0; d8 < kD / 8; ++d8) {
             float f[8];
-            unpack8(*reinterpret_cast<const u32x4*>(vbase + (int64_t)token_of(p0 + j) * kD + 8 * dg), f);
+            unpack8(raw[d8], f);
 #pragma unroll
-            for (int d = 0; d < 8; ++d) acc[d] = fmaf(pj, f[d], acc[d]);
+            for (int e = 0; e < 8; ++e) s = fmaf(s_q[8 * d8 + e], f[e], s);
         }
-#pragma unroll
-        for (int d = 0; d < 8; ++d) s_acc[kg][8 * dg + d] = acc[d];
-        __syncthreads();
-        if (kg == 0) {
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                float t = 0.f;
-                for (int g2 = 0; g2 < 32; ++g2) t += s_acc[g2][8 * dg + d];
-                o_acc[d] = o_acc[d] * alpha + t;
-            }
-        }
-        __syncthreads();
     }
-    if (kg == 0) {
-        const float inv = 1.f / l_run;  // the window always holds key T-1
-        float* o = a.out + (int64_t)row * kD + 8 * dg;
+    const float mx = block_max_f32(s, s_red);
+    const float pj = tid < np ? exp2f(s - mx) : 0.f;
+    s_p[tid] = pj;
+    const float l = block_sum_f32(pj, s_red);  // its barriers also publish s_p
+    const int kg = tid >> 3, dg = tid & 7;
+    float acc[8];
 #pragma unroll
-        for (int d = 0; d < 8; ++d) o[d] = o_acc[d] * inv;
+    for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+    for (int j = kg; j < np; j += 32) {
+        float f[8];
+        unpack8(*reinterpret_cast<const u32x4*>(vbase + (int64_t)token_of(p0 + j) * kD + 8 * dg), f);
+        const float pv = s_p[j];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[d] = fmaf(pv, f[d], acc[d]);
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) s_acc[kg][8 * dg + d] = acc[d];
+    __syncthreads();
+    float* part = a.part + ((int64_t)row * a.nsplit + sp) * (2 + kD);
+    if (tid < kD) {
+        float t = 0.f;
+        for (int g2 = 0; g2 < 32; ++g2) t += s_acc[g2][tid];
+        part[2 + tid] = t;
+    }
+    if (tid == 0) {
+        part[0] = mx;
+        part[1] = l;
+    }
+    // the last split of the row to finish combines the row's splits
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(a.counters + row, 1u) == (uint32_t)(a.nsplit - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (tid < kD) {
+        const float* pr = a.part + (int64_t)row * a.nsplit * (2 + kD);
+        float M = -INFINITY;
+        for (int i = 0; i < a.nsplit; ++i) M = fmaxf(M, pr[i * (2 + kD)]);
+        float L = 0.f, O = 0.f;
+        for (int i = 0; i < a.nsplit; ++i) {
+            const float mi = pr[i * (2 + kD)];
+            const float f = mi == -INFINITY ? 0.f : exp2f(mi - M);
+            L = fmaf(pr[i * (2 + kD) + 1], f, L);
+            O = fmaf(pr[i * (2 + kD) + 2 + tid], f, O);
+        }
+        a.out[(int64_t)row * kD + tid] = O / L;  // the window always holds key T-1
     }
 }
 
 // ------------------------------------------------------------ host side
-static int decode_chunks(const Geometry& g) {
-    // sized for the longest sequence the parameters allow (g.N = T <= t_max)
-    const int E = eligible_blocks(g.N - 1, g.bs, g.window);
-    return std::max(1, (E + DC_CHUNK - 1) / DC_CHUNK);
+struct DecodeLayout {
+    size_t keys, counters, part, total;
+    int nchunk, nsplit;
+};
+
+static DecodeLayout decode_layout(const Geometry& g, int t_max) {
+    DecodeLayout L{};
+    // sized for the longest sequence the cache allows (T <= t_max)
+    const int E = eligible_blocks(t_max - 1, g.bs, g.window);
+    L.nchunk = std::max(1, (E + DC_CHUNK - 1) / DC_CHUNK);
+    // keys per row: at most top_k routed blocks plus a window of < window + bs keys
+    L.nsplit = (g.top_k * g.bs + g.window + g.bs + DC_SPLIT - 1) / DC_SPLIT;
+    const size_t rows = (size_t)g.B * g.Hq;
+    size_t off = 0;
+    L.keys = off;     off += align_up(rows * L.nchunk * kMaxTopK * 8, 256);
+    L.counters = off; off += align_up(rows * 4, 256);
+    L.part = off;     off += align_up(rows * L.nsplit * (2 + kD) * 4, 256);
+    L.total = off;
+    return L;
 }
 
-size_t decode_workspace_bytes(const Geometry& g, int t_max) {
-    Geometry gm = g;
-    gm.N = t_max;
-    const size_t rows = (size_t)g.B * g.Hq;
-    return align_up(rows * decode_chunks(gm) * kMaxTopK * 8, 256) + align_up(rows * g.top_k * 4, 256);
-}
+size_t decode_workspace_bytes(const Geometry& g, int t_max) { return decode_layout(g, t_max).total; }
 
 hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, float* kbar, float* out, int32_t* idx_out, void* ws,
                          hipStream_t s) {
-    const int rows = g.B * g.Hq;
+    const DecodeLayout L = decode_layout(g, t_max);
+    char* base = static_cast<char*>(ws);
     DecodeArgs a;
     a.q = q;
     a.k = k;
     a.v = v;
     a.kbar = kbar;
+    a.idx = idx_out;
     a.out = out;
+    a.keys = reinterpret_cast<uint64_t*>(base + L.keys);
+    a.counters = reinterpret_cast<uint32_t*>(base + L.counters);
+    a.part = reinterpret_cast<float*>(base + L.part);
+    a.rows = g.B * g.Hq;
     a.Hq = g.Hq;
     a.Hkv = g.Hkv;
     a.T = g.N;
@@ -342,21 +370,15 @@ hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const 
     a.window = g.window;
     a.E = eligible_blocks(g.N - 1, g.bs, g.window);
     a.nchunk = std::max(1, (a.E + DC_CHUNK - 1) / DC_CHUNK);
+    // this step's keys: at most top_k routed blocks plus the window [bs*E, T-1]
+    const int keys = std::min(a.E, g.top_k) * g.bs + (g.N - g.bs * a.E);
+    a.nsplit = std::max(1, (keys + DC_SPLIT - 1) / DC_SPLIT);
+    a.summ_block = g.N / g.bs - 1;  // token T-1 completes this block when bs divides T
     a.scale_log2 = g.scale * kLog2e;
-    Geometry gm = g;
-    gm.N = t_max;
-    char* base = static_cast<char*>(ws);
-    a.keys = reinterpret_cast<uint64_t*>(base);
-    a.idx = idx_out ? idx_out
-                    : reinterpret_cast<int32_t*>(
-                          base + align_up((size_t)rows * decode_chunks(gm) * kMaxTopK * 8, 256));
-    if (g.N % g.bs == 0)  // token T-1 completes block T/bs - 1
-        hipLaunchKernelGGL(k_decode_summarize, dim3((unsigned)(g.B * g.Hkv)), dim3(64), 0, s, a,
-                           g.N / g.bs - 1);
-    hipLaunchKernelGGL(k_decode_route_chunk, dim3((unsigned)(rows * a.nchunk)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_decode_route_merge, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a,
-                       rows);
-    hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)rows), dim3(256), 0, s, a);
+    const int summ_wgs = g.N % g.bs == 0 ? g.B * g.Hkv : 0;
+    hipLaunchKernelGGL(k_decode_route, dim3((unsigned)(a.rows * a.nchunk + summ_wgs)), dim3(256),
+                       0, s, a);
+    hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)(a.rows * a.nsplit)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

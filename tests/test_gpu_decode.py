@@ -42,6 +42,7 @@ CASES = [
     (custom(1, 3, 1, 1536, 16, 8, 32), [17, 48, 511, 1536]),
     (custom(1, 2, 2, 4096, 32, 5, 64), [96, 2049, 4095]),
     (custom(1, 2, 1, 2048, 128, 3, 256), [300, 1280, 2048]),
+    (custom(1, 4, 2, 40960, 16, 16, 128, dist="topics"), [16384, 40000, 40960]),
 ]
 
 
@@ -117,3 +118,15 @@ def test_decode_consecutive_steps_match_prefill(lsa):
     assert np.array_equal(kbar.cpu().numpy(), kbar_o)
     near, near_diff, mx = check_steps(w, inp, kbar_o, Ts, np.concatenate(outs), np.concatenate(idxs))
     say("consecutive: near", near, "near-differing", near_diff, "max-abs", mx)
+
+
+def test_decode_at_a_million_tokens(lsa):
+    """The last position of the million-token workload: 16 chunk sets per
+    row, the top-k merge over 256 keys and several attention splits."""
+    w = WORKLOADS["qwen05b_n1m_needles"]
+    inp = generate(w)
+    kbar = lsa.block_summarize(params_of(lsa, w), dev(inp.k))
+    T = w.seq_len
+    out, idx = run_decode(lsa, w, inp, T, kbar)
+    near, near_diff, mx = check_steps(w, inp, oracle.block_means(inp.k, w.block), [T], out, idx)
+    say("  1M: near", near, "near-differing", near_diff, "max-abs", mx)
