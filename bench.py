@@ -132,7 +132,15 @@ def cpu_baseline(w, inp, target_s):
             "ms_per_layer_extrapolated": wall * R / n * 1e3}
 
 
-def decode_bench(lsa, w, q, k, v, steps):
+def oracle_rate(fn, n_rows):
+    """Rows per second of a CPU-oracle call over n_rows sampled rows."""
+    t0 = time.perf_counter()
+    fn()
+    wall = time.perf_counter() - t0
+    return {"rows": n_rows, "s": wall, "rows_per_s": n_rows / wall}
+
+
+def decode_bench(lsa, w, q, k, v, steps, inp=None):
     """One decode step (lsa_decode) for the last position of the workload's
     sequence, with the sequence as the key/value cache; steps timed between
     HIP-synchronised bracket points.  Algorithmic bytes per step: the block
@@ -159,13 +167,23 @@ def decode_bench(lsa, w, q, k, v, steps):
     used = int((idx >= 0).sum().item())
     keys = used * bs + B * Hq * (t - bs * E + 1)
     nbytes = B * Hkv * E * D * 4 + keys * D * 2 * 2
-    return {"cache_tokens": N, "us_per_step": us, "eligible_blocks": E,
+    res = {"cache_tokens": N, "us_per_step": us, "eligible_blocks": E,
             "algorithmic_bytes": nbytes, "hbm_gbs": nbytes / 1e3 / us,
             "hbm_frac": nbytes / 1e3 / us / PEAK_HBM_GBS,
             "note": "wall time per call, including launch overhead"}
+    if inp is not None:
+        import oracle
+        rows = np.arange(B * Hq, dtype=np.int64) * N + (N - 1)
+        r = oracle_rate(lambda: oracle.forward(inp.q, inp.k, inp.v, bs, w.top_k, w.window, 1,
+                                               rows=rows), rows.size)
+        res["cpu_oracle"] = {"kind": "oracle", "cores": oracle.num_threads(),
+                             "us_per_step": r["s"] * 1e6,
+                             "sample": "the step's rows: block means of the whole cache, "
+                                       "routing and attention of position N-1 in every head"}
+    return res
 
 
-def consensus_bench(lsa, w, q, k, v, steps):
+def consensus_bench(lsa, w, q, k, v, steps, inp=None):
     """The same layer with consensus routing (one route per KV group, scored
     by the sum of its query heads' scores): ms per layer, stage times and
     selected-key TFLOP/s (every query head attends through its group's
@@ -191,12 +209,38 @@ def consensus_bench(lsa, w, q, k, v, steps):
     stage = np.array([e.stage_ms() for e in events]).mean(axis=0)
     for e in events:
         e.close()
-    return {"ms_per_layer": ms, "selected_tflop": (f_routed + f_window) / 1e12,
-            "tflops": (f_routed + f_window) / 1e12 / (ms * 1e-3),
-            "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+    rep = w.q_heads // w.kv_heads
+    route_ms = float(stage[1] + stage[2])
+    flop = 2 * w.head_dim * routing_candidates(w) // rep   # one fp32-accurate score per candidate
+    res = {"ms_per_layer": ms, "selected_tflop": (f_routed + f_window) / 1e12,
+           "tflops": (f_routed + f_window) / 1e12 / (ms * 1e-3), "routing_ms": route_ms,
+           "roofline": {"kernel": "routing (group rows)", "bound": "mfma",
+                        "achieved": flop / 1e12 / (float(stage[1]) * 1e-3), "unit": "TFLOP/s",
+                        "peak": PEAK_BF16_TFLOPS,
+                        "frac": flop / 1e12 / (float(stage[1]) * 1e-3) / PEAK_BF16_TFLOPS},
+           "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+    if inp is not None:
+        import oracle
+        per = w.seq_len if w.causal else w.seq_len // w.block
+        G = w.batch * w.kv_heads * per
+        rows = np.sort(np.random.default_rng(8).choice(G, size=min(G, 1000), replace=False))
+        kbar = oracle.block_means(inp.k, w.block)
+        if w.causal:
+            fn = lambda: oracle.route_consensus(kbar, w.block, w.top_k, q=inp.q, window=w.window,
+                                                causal=1, rows=rows)
+        else:
+            qbar = oracle.block_means(inp.q, w.block)
+            fn = lambda: oracle.route_consensus(kbar, w.block, w.top_k, qbar=qbar, causal=0,
+                                                rows=rows)
+        r = oracle_rate(fn, rows.size)
+        res["cpu_oracle"] = {"kind": "oracle", "cores": oracle.num_threads(),
+                             "routing_rows_per_s": r["rows_per_s"],
+                             "gpu_routing_rows_per_s": G / (route_ms * 1e-3),
+                             "sample": f"routing of {rows.size} of {G} group rows"}
+    return res
 
 
-def cumulant_bench(lsa, w, q, k, v, steps):
+def cumulant_bench(lsa, w, q, k, v, steps, inp=None):
     """The layer routed by the second-cumulant score with beta = 1/sqrt(D):
     ms per layer, stage times, and the routing kernel against the bf16 MFMA
     peak, counting 2*D FLOP per (row, eligible key) for the raw scores whose
@@ -222,13 +266,26 @@ def cumulant_bench(lsa, w, q, k, v, steps):
         e.close()
     flop = 2 * w.head_dim * w.block * routing_candidates(w)
     route_ms = float(stage[1])
-    return {"beta": beta, "ms_per_layer": ms, "routing_ms": route_ms,
-            "routing_tflop": flop / 1e12, "routing_tflops": flop / 1e12 / (route_ms * 1e-3),
-            "routing_mfma_frac": flop / 1e12 / (route_ms * 1e-3) / PEAK_BF16_TFLOPS,
-            "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+    res = {"beta": beta, "ms_per_layer": ms, "routing_ms": route_ms,
+           "routing_tflop": flop / 1e12, "routing_tflops": flop / 1e12 / (route_ms * 1e-3),
+           "routing_mfma_frac": flop / 1e12 / (route_ms * 1e-3) / PEAK_BF16_TFLOPS,
+           "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+    if inp is not None:
+        import oracle
+        R = w.batch * w.q_heads * w.seq_len
+        rows = np.sort(np.random.default_rng(9).choice(R, size=min(R, 200), replace=False))
+        kbar = oracle.block_means(inp.k, w.block)
+        r = oracle_rate(lambda: oracle.route_cumulant(inp.q, inp.k, kbar, w.block, w.top_k,
+                                                      w.window, beta, rows=rows), rows.size)
+        res["cpu_oracle"] = {"kind": "oracle", "cores": oracle.num_threads(),
+                             "routing_rows_per_s": r["rows_per_s"],
+                             "gpu_routing_rows_per_s": R / (route_ms * 1e-3),
+                             "sample": f"routing of {rows.size} of {R} query rows "
+                                       "(includes forming every block covariance once)"}
+    return res
 
 
-def tree_bench(lsa, w, q, k, v, beam, steps):
+def tree_bench(lsa, w, q, k, v, beam, steps, inp=None):
     """The layer with two-level routing (nodes of 16 blocks, `beam` kept per
     row): ms per layer and stage times (for this mode stage "routing" is the
     node level with the tail slots, and "routing fallback" is the block
@@ -256,11 +313,39 @@ def tree_bench(lsa, w, q, k, v, beam, steps):
     E = np.maximum(0, t // w.block - w.window // w.block + 1)
     S = E // 16
     scored = int((S + 16 * np.minimum(beam, S) + (E - 16 * S)).sum()) * w.batch * w.q_heads
-    return {"beam": beam, "ms_per_layer": ms,
-            "node_level_ms": float(stage[1]), "block_level_ms": float(stage[2]),
-            "routing_ms": float(stage[1] + stage[2]),
-            "scores_per_layer": scored, "flat_scores_per_layer": routing_candidates(w),
-            "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+    rows = w.batch * w.q_heads * w.seq_len
+    node_flop = 2 * w.head_dim * int(S.sum()) * w.batch * w.q_heads
+    # block level: per (row, node) pair the pair id, the gathered query row,
+    # 16 fp32 scores written and read back, the pair position; per row its
+    # slot list and idx row
+    pairs = int((np.minimum(beam, S) + (16 * S < E)).sum()) * w.batch * w.q_heads
+    blk_bytes = pairs * (4 + 2 * w.head_dim + 2 * 64 + 4) + rows * ((beam + 1) * 4 + w.top_k * 4)
+    res = {"beam": beam, "ms_per_layer": ms,
+           "node_level_ms": float(stage[1]), "block_level_ms": float(stage[2]),
+           "routing_ms": float(stage[1] + stage[2]),
+           "scores_per_layer": scored, "flat_scores_per_layer": routing_candidates(w),
+           "node_level_roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+                                   "achieved": node_flop / 1e12 / (float(stage[1]) * 1e-3),
+                                   "frac": node_flop / 1e12 / (float(stage[1]) * 1e-3)
+                                   / PEAK_BF16_TFLOPS},
+           "block_level_roofline": {"bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                    "bytes": blk_bytes, "pairs": pairs,
+                                    "achieved": blk_bytes / 1e9 / (float(stage[2]) * 1e-3),
+                                    "frac": blk_bytes / 1e9 / (float(stage[2]) * 1e-3)
+                                    / PEAK_HBM_GBS},
+           "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+    if inp is not None:
+        import oracle
+        sample = np.sort(np.random.default_rng(10).choice(rows, size=min(rows, 2000),
+                                                          replace=False))
+        kbar = oracle.block_means(inp.k, w.block)
+        r = oracle_rate(lambda: oracle.route_tree(kbar, w.block, w.top_k, beam, q=inp.q,
+                                                  window=w.window, rows=sample), sample.size)
+        res["cpu_oracle"] = {"kind": "oracle", "cores": oracle.num_threads(),
+                             "routing_rows_per_s": r["rows_per_s"],
+                             "gpu_routing_rows_per_s": rows / (res["routing_ms"] * 1e-3),
+                             "sample": f"routing of {sample.size} of {rows} query rows"}
+    return res
 
 
 def copy_calibration():
@@ -390,13 +475,17 @@ def main():
                   "routed_pairs": routed_pairs, "stage_ms": breakdown, "stage_roofline": stage_frac},
     }
     if args.consensus_steps > 0 and w.q_heads > w.kv_heads:
-        result["consensus"] = consensus_bench(lsa, w, q, k, v, args.consensus_steps)
+        result["consensus"] = consensus_bench(lsa, w, q, k, v, args.consensus_steps,
+                                              inp if args.cpu_seconds > 0 else None)
     if w.causal and args.cumulant_steps > 0 and w.seq_len <= 262144:
-        result["cumulant"] = cumulant_bench(lsa, w, q, k, v, args.cumulant_steps)
+        result["cumulant"] = cumulant_bench(lsa, w, q, k, v, args.cumulant_steps,
+                                            inp if args.cpu_seconds > 0 else None)
     if w.causal and args.tree_beam > 0:
-        result["tree"] = tree_bench(lsa, w, q, k, v, args.tree_beam, max(3, min(args.steps, 10)))
+        result["tree"] = tree_bench(lsa, w, q, k, v, args.tree_beam, max(3, min(args.steps, 10)),
+                                    inp if args.cpu_seconds > 0 else None)
     if w.causal and args.decode_steps > 0:
-        result["decode"] = decode_bench(lsa, w, q, k, v, args.decode_steps)
+        result["decode"] = decode_bench(lsa, w, q, k, v, args.decode_steps,
+                                        inp if args.cpu_seconds > 0 else None)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     else:
