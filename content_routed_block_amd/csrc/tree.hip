@@ -9,11 +9,10 @@
 //   2. k_tree_score: one node's 16 block means (bf16 hi + lo) in LDS against
 //      up to 64 gathered query rows, on 16x16x32 bf16 MFMA tiles: 16 scores
 //      per pair (fp32 accuracy), written by pair position (contiguous);
-//   3. k_tree_select: one lane per row walks its used slots in ascending
-//      node order and keeps the 16 best (score, block) pairs; blocks arrive
-//      in ascending order, so a newcomer beats a kept entry exactly when its
-//      score is strictly larger (ties stay with the lower block).  Blocks of
-//      the tail node past the row's candidates are skipped.
+//   3. k_tree_select: one lane per row merges each used slot's 16 scores,
+//      as sorted 64-bit keys (score, then lower block), into the row's
+//      running top-16 with a bitonic merge.  Blocks of the tail node past
+//      the row's candidates are left out.
 // The node-major scoring gathers one 128-byte query row per pair instead of
 // a node's 4 KB of block means per pair.
 #include <math.h>
@@ -101,57 +100,91 @@ struct TreeSelectArgs {
     int N, bs, window, top_k, beam;
 };
 
+// Compare-exchange toward descending order.
+__device__ __forceinline__ void cx_desc(uint64_t& a, uint64_t& b) {
+    const bool gt = a > b;
+    const uint64_t hi = gt ? a : b, lo = gt ? b : a;
+    a = hi;
+    b = lo;
+}
+
+// Bitonic sort of 16 keys into descending order.
+__device__ __forceinline__ void sort16_desc(uint64_t (&v)[kTreeFanout]) {
+#pragma unroll
+    for (int size = 2; size <= kTreeFanout; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < kTreeFanout; ++i) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    if ((i & size) == 0) cx_desc(v[i], v[j]);
+                    else cx_desc(v[j], v[i]);
+                }
+            }
+}
+
+// One lane per row.  Per used slot the 16 block scores become 64-bit keys
+// (score, then lower block; 0 for blocks past the row's candidates), are
+// sorted, and merged into the row's running top-16 by one bitonic merge:
+// branch-free, so the lanes of a wave never wait on each other's
+// insertions.  The next slot's scores are loaded while the current one is
+// merged.
 __global__ __launch_bounds__(256) void k_tree_select(TreeSelectArgs a) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (row >= a.rows) return;
     const int t = (int)(row % a.N);
     const int E = eligible_blocks(t, a.bs, a.window);
     const int stride = a.beam + 1;
-    float Ls[kMaxTopK];
-    int Lc[kMaxTopK];
+    uint64_t L[kTreeFanout];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        Ls[j] = -INFINITY;
-        Lc[j] = 0;
-    }
+    for (int j = 0; j < kTreeFanout; ++j) L[j] = 0;
     int ncand = 0;
+    auto fetch = [&](int j, f32x4 (&sc)[4], int& c0) {
+        const uint32_t pos = j < stride ? a.rev[(int64_t)j * a.rows + row] : 0xFFFFFFFFu;
+        c0 = -1;
+        if (pos != 0xFFFFFFFFu) {
+            c0 = a.slots[row * stride + j] * kTreeFanout;
+            const f32x4* sp = reinterpret_cast<const f32x4*>(a.scores + (int64_t)pos * kTreeFanout);
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) sc[i4] = sp[i4];
+        }
+    };
+    f32x4 cur[4], nxt[4];
+    int c_cur, c_nxt;
+    fetch(0, cur, c_cur);
     for (int j = 0; j < stride; ++j) {
-        const uint32_t pos = a.rev[(int64_t)j * a.rows + row];
-        if (pos == 0xFFFFFFFFu) continue;
-        const int node = a.slots[row * stride + j];
-        const float* sp = a.scores + (int64_t)pos * kTreeFanout;
-        float sc[kTreeFanout];
+        fetch(j + 1, nxt, c_nxt);
+        if (c_cur >= 0) {
+            const int nvalid = min(kTreeFanout, E - c_cur);
+            ncand += nvalid;
+            uint64_t Nk[kTreeFanout];
 #pragma unroll
-        for (int i4 = 0; i4 < kTreeFanout / 4; ++i4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sp + 4 * i4);
-            sc[4 * i4] = v[0]; sc[4 * i4 + 1] = v[1]; sc[4 * i4 + 2] = v[2]; sc[4 * i4 + 3] = v[3];
-        }
-        const int c0 = node * kTreeFanout;
-        const int nvalid = min(kTreeFanout, E - c0);
-        ncand += nvalid;
+            for (int i = 0; i < kTreeFanout; ++i)
+                Nk[i] = i < nvalid ? sel_key(cur[i >> 2][i & 3], (uint32_t)(c_cur + i)) : 0ull;
+            sort16_desc(Nk);
 #pragma unroll
-        for (int i = 0; i < kTreeFanout; ++i) {
-            float x = sc[i];
-            if (i < nvalid && x > Ls[kMaxTopK - 1]) {
-                int xc = c0 + i;
-#pragma unroll
-                for (int s = 0; s < kMaxTopK; ++s) {
-                    const bool gt = x > Ls[s];
-                    const float ts = Ls[s];
-                    const int tc = Lc[s];
-                    Ls[s] = gt ? x : ts;
-                    Lc[s] = gt ? xc : tc;
-                    x = gt ? ts : x;
-                    xc = gt ? tc : xc;
-                }
+            for (int i = 0; i < kTreeFanout; ++i) {
+                const uint64_t o = Nk[kTreeFanout - 1 - i];
+                L[i] = L[i] > o ? L[i] : o;  // top 16 of the union, bitonic
             }
+#pragma unroll
+            for (int stride2 = kTreeFanout >> 1; stride2 > 0; stride2 >>= 1)
+#pragma unroll
+                for (int i = 0; i < kTreeFanout; ++i) {
+                    const int jx = i ^ stride2;
+                    if (jx > i) cx_desc(L[i], L[jx]);
+                }
         }
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) cur[i4] = nxt[i4];
+        c_cur = c_nxt;
     }
     // the chosen blocks in ascending order, -1 padded
     const int m = ncand < a.top_k ? ncand : a.top_k;
     uint32_t cs[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) cs[j] = j < m ? (uint32_t)Lc[j] : 0xFFFFFFFFu;
+    for (int j = 0; j < kMaxTopK; ++j) cs[j] = j < m ? key_block(L[j]) : 0xFFFFFFFFu;
 #pragma unroll
     for (int size = 2; size <= kMaxTopK; size <<= 1)
 #pragma unroll
