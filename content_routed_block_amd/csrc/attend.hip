@@ -51,7 +51,10 @@ constexpr float RESCALE_SLACK = 8.f;  // log2 headroom before a running max is r
 
 
 // ------------------------------------------------------------ V transpose
-// V [BG][N][64] -> V^T tiles [BG][ceil(N/64)][64 d][64 keys]; keys >= N are zero.
+// V [BG][N][64] -> V^T tiles [BG][ceil(N/TW)][64 d][TW keys]; keys >= N are
+// zero.  TW = 64 for the causal kernels; TW = 16 (one image-mode block per
+// tile) makes a block's V^T 2 KB of contiguous memory.
+template <int TW>
 __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict__ v,
                                                      uint16_t* __restrict__ vt, int N, int ntiles) {
     __shared__ uint32_t s[VT_TILE][33];  // [key][d pair], odd pitch
@@ -73,6 +76,7 @@ __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int ch = tid + 256 * i, d = ch >> 3, k0 = (ch & 7) * 8;
+        uint16_t* out = dst + (k0 / TW) * (kD * TW) + d * TW + (k0 % TW);
         const int sh = 16 * (d & 1);
         u32x4 y;
 #pragma unroll
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict_
             const uint32_t hi = (s[k0 + 2 * j + 1][d >> 1] >> sh) & 0xFFFFu;
             y[j] = lo | (hi << 16);
         }
-        *reinterpret_cast<u32x4*>(dst + d * VT_TILE + k0) = y;
+        *reinterpret_cast<u32x4*>(out) = y;
     }
 }
 
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
 struct ImgArgs {
     const uint16_t* q;
     const uint16_t* k;
-    const uint16_t* vt;
+    const uint16_t* vt;  // V^T per 16-key block [BG][nb][64 d][16 keys]
     const int32_t* idx;  // [B,Hq,nb,top_k]; group_route: [B,Hkv,nb,top_k]
     float* out;
     int Hq, Hkv, N, nb, top_k, ntiles;
@@ -541,13 +545,17 @@ struct ImgArgs {
 // the wave's own LDS region.
 __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[4][kD * WVP];
-    __shared__ int s_n[4];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t qb = (int64_t)blockIdx.x * 4 + w;
-    const bool active = qb < a.n_qblocks;
-    const int64_t bh = active ? qb / a.nb : 0;
-    const int i = active ? (int)(qb - bh * a.nb) : 0;
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
+    // item = xcd * (grid / 8) + blockIdx / 8 gives each XCD a contiguous run
+    // of query blocks, i.e. whole heads, whose K and V^T its L2 then holds.
+    const int per_xcd = gridDim.x / 8;
+    const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int64_t qb = (int64_t)item * 4 + w;
+    if (qb >= a.n_qblocks) return;  // the waves share no LDS and no barrier
+    const int64_t bh = qb / a.nb;
+    const int i = (int)(qb - bh * a.nb);
     const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq), g = h / (a.Hq / a.Hkv);
     const int64_t bg = (int64_t)b * a.Hkv + g;
     const int64_t k0 = bg * a.N * kD;
@@ -557,53 +565,58 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 
     // the used slots of this query block's idx row (wave-uniform)
     const int64_t irow = a.group_route ? bg * a.nb + i : qb;
-    const int32_t* ir = a.idx + (active ? irow : 0) * a.top_k;
     int csel[kMaxTopK];
-    const uint32_t used = active ? row_used(ir, a.top_k, a.nb, csel) : 0u;
+    const uint32_t used = row_used(a.idx + irow * a.top_k, a.top_k, a.nb, csel);
     const int nused = __builtin_popcount(used);
-    if (lane == 0) s_n[w] = nused;
-    __syncthreads();
-    const int nmax = max(max(s_n[0], s_n[1]), max(s_n[2], s_n[3]));
 
     bf16x8 Bq[2];
-    load_q_operand(a.q + row * kD, lane, active, Bq);
+    load_q_operand(a.q + row * kD, lane, true, Bq);
     f32x4 o[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     __bf16* vt = s_vt[w];
 
-    for (int c0 = 0; c0 < nmax; c0 += 4) {
-        __syncthreads();
-        // V^T columns of up to four 16-key blocks: lane d copies row d of
-        // each block (two 16-byte pieces)
+    for (int c0 = 0; c0 < nused; c0 += 4) {
+        // up to four 16-key blocks: their K rows (MFMA operands) and V^T
+        // (lane d takes row d of each block's contiguous 2 KB, two 16-byte
+        // pieces) are all requested before any is used, so the two gathers
+        // overlap
+        int cblk[4];
+        bf16x8 kop[4][2];
+        u32x4 vpart[4][2];
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const bool have = c0 + jb < nused;
-            const int cblk = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
-            const uint16_t* src = a.vt + vt0 + (int64_t)(cblk >> 2) * (kD * VT_TILE) +
-                                  lane * VT_TILE + (cblk & 3) * 16;
+            cblk[jb] = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
+            const uint16_t* kr =
+                a.k + k0 + ((int64_t)cblk[jb] * 16 + (lane & 15)) * kD + 8 * (lane >> 4);
+            const uint16_t* src = a.vt + vt0 + (int64_t)cblk[jb] * (kD * 16) + lane * 16;
 #pragma unroll
-            for (int part = 0; part < 2; ++part) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (have) v = *reinterpret_cast<const u32x4*>(src + 8 * part);
-                lds_store_2x8(vt + lane * WVP + jb * 16 + 8 * part, v);
-            }
+            for (int ks = 0; ks < 2; ++ks) kop[jb][ks] = load_bf16x8(kr + 32 * ks);
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+                vpart[jb][part] = *reinterpret_cast<const u32x4*>(src + 8 * part);
         }
-        __syncthreads();
+        // the previous group's P.V reads of this wave's region are done
+        // (LDS operations of one wave complete in order)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const bool have = c0 + jb < nused;
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+                lds_store_2x8(vt + lane * WVP + jb * 16 + 8 * part,
+                              have ? vpart[jb][part] : u32x4{0u, 0u, 0u, 0u});
+        }
         f32x4 sc[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const bool have = c0 + jb < nused;
-            const int cblk = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (have) {
-                const uint16_t* kr =
-                    a.k + k0 + ((int64_t)cblk * 16 + (lane & 15)) * kD + 8 * (lane >> 4);
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) acc = mfma16(load_bf16x8(kr + 32 * ks), Bq[ks], acc);
-            }
+            for (int ks = 0; ks < 2; ++ks) acc = mfma16(kop[jb][ks], Bq[ks], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 sc[jb][r] = have ? acc[r] : -INFINITY;
@@ -627,9 +640,9 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
         m_run = m_new;
+        __builtin_amdgcn_wave_barrier();  // the V^T stores above precede these reads
         pv_accumulate<4>(vt, WVP, 0, lane, p, o);
     }
-    if (!active) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* dst = a.out + row * kD + 4 * (lane >> 4);
 #pragma unroll
@@ -696,12 +709,16 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     uint16_t* vt = reinterpret_cast<uint16_t*>(base + L.vt);
     const int ntiles = (g.N + VT_TILE - 1) / VT_TILE;
     const int nbg = g.B * g.Hkv;
-    hipLaunchKernelGGL(k_transpose_v, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s, v, vt, g.N,
-                       ntiles);
+    if (g.causal)
+        hipLaunchKernelGGL(k_transpose_v<VT_TILE>, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s,
+                           v, vt, g.N, ntiles);
+    else
+        hipLaunchKernelGGL(k_transpose_v<16>, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s, v,
+                           vt, g.N, ntiles);
     if (!g.causal) {
         ImgArgs a{q, k, vt, idx, out, g.Hq, g.Hkv, g.N, g.nb, g.top_k, ntiles,
                   (int64_t)g.B * g.Hq * g.nb, scale_log2, g.consensus};
-        const unsigned grid = (unsigned)((a.n_qblocks + 3) / 4);
+        const unsigned grid = (unsigned)(((a.n_qblocks + 3) / 4 + 7) / 8 * 8);  // multiple of 8
         for (int i = 4; i < 8; ++i) mark(ev, i, s);
         hipLaunchKernelGGL(k_image_attend, dim3(grid), dim3(256), 0, s, a);
         mark(ev, 8, s);
