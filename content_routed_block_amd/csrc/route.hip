@@ -298,9 +298,13 @@ __device__ __forceinline__ int clamp_i32(int x, int lo, int hi) {
 // Each wave is independent (its own 32 rows and survivor lists); the
 // workgroup only shares the staged candidate chunks.
 template <bool CAUSAL, bool QF32>
-__global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 s_hi[2][RT_CH * RT_PITCH];
-    __shared__ __attribute__((aligned(16))) __bf16 s_lo[2][RT_CH * RT_PITCH];
+__global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
+    // candidate staging: pass 1 double-buffers the hi parts in s_stage[0..1];
+    // pass 2 holds one chunk's hi part in s_stage[0] and lo part in
+    // s_stage[1] (two barriers per chunk), which keeps the workgroup's LDS
+    // small enough for five workgroups per CU (bf16 queries; the fp32-query
+    // variant needs more registers and runs four)
+    __shared__ __attribute__((aligned(16))) __bf16 s_stage[2][RT_CH * RT_PITCH];
     // survivor lists, slot-major ([slot][row]) so that the lanes of a wave
     // touch consecutive words
     // (scores: RT_CAP*RT_ROWS floats, then the block ids as uint16)
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
         u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = r0;
         if (nch > 0) {
             r0 = stage_load(khi, 0, tid);
-            stage_store(s_hi[0], tid, r0);
+            stage_store(s_stage[0], tid, r0);
         }
         if (nch > 1) r1 = stage_load(khi, RT_CH, tid);
         __syncthreads();
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
             if (j + 2 < nch) r_issue = stage_load(khi, cb + 2 * RT_CH, tid);
             if (cb < Emax) {
                 bf16x8 A[4];
-                read_cands(s_hi[j & 1], l32, half, A);
+                read_cands(s_stage[j & 1], l32, half, A);
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) acc = mfma32(A[ks], Bq[ks], acc);
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
                     m1[r] = fmaxf(m1[r], acc[r]);
                 }
             }
-            if (j + 1 < nch) stage_store(s_hi[(j + 1) & 1], tid, r_store);
+            if (j + 1 < nch) stage_store(s_stage[(j + 1) & 1], tid, r_store);
             __syncthreads();
         };
         for (int j = 0; j < nch; j += 2) {
@@ -469,8 +473,8 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
         if (nch > 0) {
             h0 = stage_load(khi, 0, tid);
             l0 = stage_load(klo, 0, tid);
-            stage_store(s_hi[0], tid, h0);
-            stage_store(s_lo[0], tid, l0);
+            stage_store(s_stage[0], tid, h0);
+            stage_store(s_stage[1], tid, l0);
         }
         if (nch > 1) {
             h1 = stage_load(khi, RT_CH, tid);
@@ -486,8 +490,8 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
             }
             if (cb < Emax) {
                 bf16x8 ch[4], cl[4];
-                read_cands(s_hi[j & 1], l32, half, ch);
-                read_cands(s_lo[j & 1], l32, half, cl);
+                read_cands(s_stage[0], l32, half, ch);
+                read_cands(s_stage[1], l32, half, cl);
                 f32x16 acc = {};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
@@ -520,9 +524,10 @@ __global__ __launch_bounds__(256, 4) void k_route(RouteArgs a) {
                     }
                 }
             }
+            __syncthreads();  // every wave is done with chunk j
             if (j + 1 < nch) {
-                stage_store(s_hi[(j + 1) & 1], tid, hi_store);
-                stage_store(s_lo[(j + 1) & 1], tid, lo_store);
+                stage_store(s_stage[0], tid, hi_store);
+                stage_store(s_stage[1], tid, lo_store);
             }
             __syncthreads();
         };
