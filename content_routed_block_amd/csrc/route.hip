@@ -44,7 +44,7 @@ namespace lsa {
 
 constexpr int RT_ROWS = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int RT_CH = 32;      // candidates per step
-constexpr int RT_CAP = 28;     // survivor slots per query (4 workgroups still fit a CU)
+constexpr int RT_CAP = 28;     // survivor slots per query (five workgroups still fit a CU)
 constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
 constexpr int FB_GRID = 256;   // workgroups of the exact fallback
 
