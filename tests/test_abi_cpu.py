@@ -137,3 +137,34 @@ def test_tree_routing_workspace(lsa):
     assert rows * 9 * (4 + 4 + 4 + 64) <= extra <= rows * 9 * (4 + 4 + 4 + 64) + (64 << 20)
     assert lsa.workspace_bytes(pt, lsa.OP_ATTEND) == lsa.workspace_bytes(p, lsa.OP_ATTEND)
     assert lsa.library().lsa_workspace_bytes(ctypes.byref(pt), lsa.OP_DECODE) == lsa.SIZE_MAX
+
+
+def test_decode_argument_checks(lsa):
+    """lsa_decode validates the step position against the cache and the
+    cache geometry before anything is launched."""
+    L = lsa.library()
+    a = ctypes.c_void_p(4096)
+    big = 1 << 40
+    ok = good(lsa, seq_len=1000)                       # T = 1000 (need not be a block multiple)
+    assert L.lsa_decode(ctypes.byref(good(lsa, seq_len=0)), 131072, a, a, a, a, a, None, a, big,
+                        None) == 2                    # T < 1
+    assert L.lsa_decode(ctypes.byref(good(lsa, seq_len=131136)), 131072, a, a, a, a, a, None, a,
+                        big, None) == 2               # T > cache_len
+    assert L.lsa_decode(ctypes.byref(ok), 131072 + 1, a, a, a, a, a, None, a, big, None) == 2
+    assert L.lsa_decode(ctypes.byref(good(lsa, seq_len=1000, causal=0, window=0, block=16)),
+                        131072, a, a, a, a, a, None, a, big, None) == 2
+    assert L.lsa_decode(ctypes.byref(ok), 131072, None, a, a, a, a, None, a, big, None) == 1
+    assert L.lsa_decode(ctypes.byref(ok), 131072, ctypes.c_void_p(4100), a, a, a, a, None, a, big,
+                        None) == 4
+    pc = good(lsa, seq_len=131072)
+    need = L.lsa_workspace_bytes(ctypes.byref(pc), lsa.OP_DECODE)
+    assert L.lsa_decode(ctypes.byref(ok), 131072, a, a, a, a, a, None, a, need - 1, None) == 5
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
