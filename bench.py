@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # FETCH_SIZE / WRITE_SIZE runs, each scaled by the same counter's reading on a
 # plain copy of known size; tied to the kernel sources it was measured on.
 TRAFFIC = {
-    "csrc": "f735eba06642c913", "stage": 6, "workload": "qwen05b_n128k_needles",
+    "csrc": "6738973853f55129", "stage": 6, "workload": "qwen05b_n128k_needles",
     "fetch_kib": 1.919e+06, "write_kib": 3.934e+06, "fetch_factor": 2.0, "write_factor": 1.0,
     "bytes_per_launch": 1.919e+06 * 1024 * 2.0 + 3.934e+06 * 1024 * 1.0,
 }
