@@ -370,6 +370,7 @@ hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const 
     a.window = g.window;
     a.E = eligible_blocks(g.N - 1, g.bs, g.window);
     a.nchunk = std::max(1, (a.E + DC_CHUNK - 1) / DC_CHUNK);
+    if (a.nchunk > DC_MAXCH) return hipErrorInvalidValue;  // the merge holds 64 chunk sets
     // this step's keys: at most top_k routed blocks plus the window [bs*E, T-1]
     const int keys = std::min(a.E, g.top_k) * g.bs + (g.N - g.bs * a.E);
     a.nsplit = std::max(1, (keys + DC_SPLIT - 1) / DC_SPLIT);
