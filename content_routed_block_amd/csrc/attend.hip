@@ -165,6 +165,13 @@ __device__ __forceinline__ void pv_accumulate(const __bf16* s_vt, int vpitch, in
     }
 }
 
+// 2^x with the bare hardware instruction (v_exp_f32).  Results below the
+// smallest normal float come out as zero; a softmax weight that small is lost
+// without effect on any sum it enters.  The libm exp2f wraps the same
+// instruction in a denormal-range rescale (a compare, a select, an add and an
+// ldexp per call).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Row reductions across the 4 lanes that share row l%16.
 __device__ __forceinline__ float row_max4(float v) {
     v = fmaxf(v, __shfl_xor(v, 16, kWave));
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
         for (int i = 0; i < KT; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[i][r] = exp2f(fmaf(sc[i][r], a.scale_log2, -m2));
+                p[i][r] = exp2_hw(fmaf(sc[i][r], a.scale_log2, -m2));
                 sum += p[i][r];
             }
         sum = row_sum4(sum);
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
         const bool raise = mc > m_run + RESCALE_SLACK;
         if (__builtin_amdgcn_ballot_w64(raise)) {
             const float m_new = raise ? mc : m_run;
-            const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+            const float alpha = (m_run == -INFINITY) ? 0.f : exp2_hw(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
@@ -460,7 +467,7 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[i][r] = exp2f(fmaf(sc[i][r], a.scale_log2, -mu));
+                p[i][r] = exp2_hw(fmaf(sc[i][r], a.scale_log2, -mu));
                 sum += p[i][r];
             }
         l_run += row_sum4(sum);
@@ -506,8 +513,8 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
             if (!(sl < a.top_k && ((used >> sl) & 1u))) continue;
             const float lse = lse_all[sl];
             const float m_new = fmaxf(m_run, lse);
-            const float alpha = exp2f(m_run - m_new);
-            const float beta = exp2f(lse - m_new);
+            const float alpha = exp2_hw(m_run - m_new);
+            const float beta = exp2_hw(lse - m_new);
             l_run = l_run * alpha + beta;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
@@ -626,14 +633,14 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
         const float mc = row_max4(mx) * a.scale_log2;
         const float m_new = fmaxf(m_run, mc);
         const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mu);
+        const float alpha = (m_run == -INFINITY) ? 0.f : exp2_hw(m_run - mu);
         float p[4][4];
         float sum = 0.f;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[jb][r] = exp2f(fmaf(sc[jb][r], a.scale_log2, -mu));
+                p[jb][r] = exp2_hw(fmaf(sc[jb][r], a.scale_log2, -mu));
                 sum += p[jb][r];
             }
         l_run = l_run * alpha + row_sum4(sum);
