@@ -40,9 +40,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # FETCH_SIZE / WRITE_SIZE runs, each scaled by the same counter's reading on a
 # plain copy of known size; tied to the kernel sources it was measured on.
 TRAFFIC = {
-    "csrc": "6738973853f55129", "stage": 6, "workload": "qwen05b_n128k_needles",
-    "fetch_kib": 1.919e+06, "write_kib": 3.934e+06, "fetch_factor": 2.0, "write_factor": 1.0,
-    "bytes_per_launch": 1.919e+06 * 1024 * 2.0 + 3.934e+06 * 1024 * 1.0,
+    "csrc": "6effa1d55f971ff0", "stage": 6, "workload": "qwen05b_n128k_needles",
+    "fetch_kib": 1.918e+06, "write_kib": 3.91e+06, "fetch_factor": 2.0, "write_factor": 1.0,
+    "bytes_per_launch": 1.918e+06 * 1024 * 2.0 + 3.91e+06 * 1024 * 1.0,
 }
 
 
