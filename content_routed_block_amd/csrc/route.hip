@@ -759,7 +759,10 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
         nq = 0;
     };
     float s1 = 0.f, s2 = 0.f;  // this lane's sum and sum of squares over the block (BS >= 32)
-    const int nch = Ewg * BS / RT_CH;
+    // chunks of 32 keys covering the eligible blocks; with BS = 16 an odd
+    // block count ends half-way through the last chunk, whose other block
+    // exists (it is at most the query's own block) and is masked by Erow
+    const int nch = (Ewg * BS + RT_CH - 1) / RT_CH;
     const int wave_keys = Emax * BS;
 
     // Staging loads are issued unconditionally (the address clamped to the

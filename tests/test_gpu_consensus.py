@@ -43,6 +43,8 @@ CASES = [
     custom(1, 6, 2, 2048, 128, 3, 256),
     custom(1, 4, 2, 4096, 16, 16, 0, causal=0, seed=3),
     custom(2, 6, 2, 1024, 16, 8, 0, causal=0, seed=6),
+    custom(1, 4, 2, 16 * 65, 16, 4, 32, seed=14),   # N not a multiple of 64
+    custom(1, 4, 2, 2048, 16, 6, 48, seed=19),      # odd W / bs
 ]
 
 

@@ -43,6 +43,8 @@ CASES = [
     (custom(1, 2, 2, 4096, 32, 5, 64), -0.5),
     (custom(1, 2, 1, 2048, 128, 3, 256), BETA),
     (custom(1, 7, 1, 3072, 64, 16, 512, dist="topics", seed=5), 0.5),
+    (custom(1, 2, 1, 16 * 65, 16, 4, 32, seed=15), BETA),   # N not a multiple of 64
+    (custom(1, 2, 1, 2048, 16, 6, 48, seed=16), BETA),      # odd W / bs: odd block counts
 ]
 
 

@@ -43,6 +43,7 @@ CASES = [
     (custom(1, 2, 2, 4096, 32, 5, 64), [96, 2049, 4095]),
     (custom(1, 2, 1, 2048, 128, 3, 256), [300, 1280, 2048]),
     (custom(1, 4, 2, 40960, 16, 16, 128, dist="topics"), [16384, 40000, 40960]),
+    (custom(1, 2, 1, 16 * 130, 16, 6, 48, seed=22), [1, 47, 49, 1000, 2080]),  # odd W / bs
 ]
 
 

@@ -43,6 +43,13 @@ CAUSAL_CASES = [
     custom(1, 2, 1, 2048, 128, 3, 256),
     custom(1, 7, 1, 3072, 64, 16, 512, dist="topics", seed=5),
     custom(1, 1, 1, 64 * 40, 64, 1, 64),
+    # N not a multiple of the 64-position attention tiles nor of the 128-row
+    # routing tiles: partial last V^T tile, partial last query tile
+    custom(1, 2, 1, 16 * 65, 16, 4, 32, seed=12),
+    custom(3, 3, 3, 32 * 33, 32, 5, 64, dist="topics", seed=13),
+    # an odd number of window blocks (W / bs = 3): odd eligible-block counts
+    custom(1, 2, 1, 2048, 16, 6, 48, seed=17),
+    custom(1, 2, 2, 32 * 40, 32, 3, 96, seed=18),
 ]
 IMAGE_CASES = [
     custom(2, 4, 4, 1024, 16, 8, 0, causal=0),

@@ -41,6 +41,7 @@ CASES = [
     (custom(1, 7, 1, 32768, 64, 16, 512, dist="topics", seed=5), 8),
     (custom(1, 2, 2, 32768, 128, 3, 256), 2),
     (custom(1, 3, 1, 8192, 16, 5, 32), 1),
+    (custom(1, 2, 1, 16 * 1001, 16, 6, 48, seed=73), 3),   # odd W / bs, N not a multiple of 64
 ]
 
 
