@@ -38,19 +38,30 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc
 # FETCH_SIZE / WRITE_SIZE runs, each scaled by the same counter's reading on a
-# plain copy of known size; tied to the kernel sources it was measured on.
+# plain copy of known size; tied to the sources of that kernel's translation
+# unit and the compile flags it was measured with (kernel_digest).
 TRAFFIC = {
-    "csrc": "6effa1d55f971ff0", "stage": 6, "workload": "qwen05b_n128k_needles",
+    "csrc": "fd4fc761c639f352", "stage": 6, "workload": "qwen05b_n128k_needles",
     "fetch_kib": 1.918e+06, "write_kib": 3.91e+06, "fetch_factor": 2.0, "write_factor": 1.0,
     "bytes_per_launch": 1.918e+06 * 1024 * 2.0 + 3.91e+06 * 1024 * 1.0,
 }
 
 
-def csrc_digest() -> str:
+# The attention kernels' translation unit: its source, the headers it
+# includes, and the build script that holds the compile flags.
+KERNEL_SOURCES = [
+    "content_routed_block_amd/csrc/attend.hip",
+    "content_routed_block_amd/csrc/bucket.hpp",
+    "content_routed_block_amd/csrc/lsa_common.hpp",
+    "content_routed_block_amd/csrc/lsa_launch.hpp",
+    "content_routed_block_amd/build.py",
+]
+
+
+def kernel_digest() -> str:
     h = hashlib.sha256()
-    d = os.path.join(ROOT, "content_routed_block_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -447,7 +458,7 @@ def main():
     dom_name = lsa.PROFILE_STAGES[dom]
     d = stage_frac.get(dom_name)
     traffic = None
-    if TRAFFIC and TRAFFIC.get("csrc") == csrc_digest() and TRAFFIC.get("stage") == dom \
+    if TRAFFIC and TRAFFIC.get("csrc") == kernel_digest() and TRAFFIC.get("stage") == dom \
             and TRAFFIC.get("workload") == w.name:
         traffic = TRAFFIC["bytes_per_launch"]
     roofline = {"bound": d["bound"] if d else "hbm", "achieved": d["achieved"] if d else None,
