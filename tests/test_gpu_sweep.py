@@ -1,0 +1,91 @@
+"""Parity over a seeded sweep of random valid shapes, for every routing
+variant (per-head, consensus, second-cumulant, two-level) and for decode.
+
+The fixed cases in the other GPU suites pick shapes by hand; this sweep draws
+them: block size, window width in blocks (odd counts included), top-k, GQA
+ratio, batch, sequence length down to a single block, and the value
+distribution.  Each case runs the same checks as the fixed cases (routing
+bit-exact on rows with a clear gap and valid on near ties, outputs within the
+prefill tolerances, block means bit-exact), through the same helpers.
+"""
+import numpy as np
+import pytest
+
+import tests.test_gpu_consensus as C
+import tests.test_gpu_cumulant as U
+import tests.test_gpu_decode as D
+import tests.test_gpu_parity as P
+import tests.test_gpu_tree as T
+from content_routed_block_amd.workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+lsa = P.lsa  # the module fixture: skips without a GPU
+MAX_ROWS = 120_000  # B * Hq * N per case, so the oracle finishes in about a second
+
+
+def draw(n, seed, causal=True, tag="sw"):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        bs = int(rng.choice([16, 32, 64, 128])) if causal else 16
+        m = int(rng.integers(1, 4096 // bs + 1))            # blocks in the sequence
+        N = bs * m
+        W = bs * int(rng.integers(1, 9)) if causal else 0   # 1 to 8 window blocks
+        k = int(rng.integers(1, 17))
+        Hkv = int(rng.integers(1, 4))
+        rep = int(rng.choice([1, 2, 3, 7]))
+        B = int(rng.integers(1, 3))
+        if B * Hkv * rep * N > MAX_ROWS:
+            continue
+        dist = "topics" if rng.random() < 0.5 else "normal"
+        i = len(out)
+        out.append(Workload(f"{tag}{i}_b{B}_h{Hkv * rep}x{Hkv}_n{N}_bs{bs}_k{k}_w{W}_{dist}",
+                            B, Hkv * rep, Hkv, N, 64, bs, k, W, int(causal), dist,
+                            topics=16 if dist == "topics" else 0, seed=seed * 100 + i))
+    return out
+
+
+FLAT = draw(64, 31) + draw(16, 32, causal=False, tag="img")
+CONSENSUS = draw(20, 33, tag="cons") + draw(8, 34, causal=False, tag="consimg")
+CUMULANT = [(w, float(b)) for w, b in zip(draw(20, 35, tag="cum"),
+                                          np.random.default_rng(40).choice([0.125, 1.0, -0.5, 2.0], 20))]
+TREE = [(w, int(b)) for w, b in zip(draw(20, 36, tag="tree"),
+                                    np.random.default_rng(37).integers(1, 16, 20))]
+DECODE = [(w, sorted({1, w.seq_len, *np.random.default_rng(39 + i).integers(1, w.seq_len + 1, 3)
+                      .tolist()}))
+          for i, w in enumerate(draw(16, 38, tag="dec"))]
+
+
+def name(x):
+    return x.name if hasattr(x, "name") else str(x)
+
+
+@pytest.mark.parametrize("w", FLAT, ids=name)
+def test_sweep_summary(lsa, w):
+    P.test_summary_matches_oracle(lsa, w)
+
+
+@pytest.mark.parametrize("w", FLAT, ids=name)
+def test_sweep_forward(lsa, w):
+    P.test_forward_matches_oracle(lsa, w)
+
+
+@pytest.mark.parametrize("w", CONSENSUS, ids=name)
+def test_sweep_consensus_forward(lsa, w):
+    C.test_consensus_forward_matches_oracle(lsa, w)
+
+
+@pytest.mark.parametrize("w,beta", CUMULANT, ids=name)
+def test_sweep_cumulant_forward(lsa, w, beta):
+    U.test_cumulant_forward_matches_oracle(lsa, w, beta)
+
+
+@pytest.mark.parametrize("w,beam", TREE, ids=name)
+def test_sweep_tree_forward(lsa, w, beam):
+    T.test_tree_forward_matches_oracle(lsa, w, beam)
+
+
+@pytest.mark.parametrize("w,steps", DECODE, ids=name)
+def test_sweep_decode(lsa, w, steps):
+    D.test_decode_matches_oracle(lsa, w, steps)
