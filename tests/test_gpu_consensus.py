@@ -138,7 +138,11 @@ def test_consensus_with_one_head_per_group_is_per_head_routing(lsa, w):
 @pytest.mark.parametrize("name", ["qwen05b_n128k_needles", "qwen05b_n1m_needles",
                                   "image_zorder_128x128"])
 def test_consensus_full_size_sampled_rows(lsa, name):
-    w = WORKLOADS[name]
+    check_consensus_sampled_rows(lsa, WORKLOADS[name])
+
+
+def check_consensus_sampled_rows(lsa, w):
+    name = w.name
     say("consensus full", name, "generating")
     inp = generate(w)
     say("consensus full", name, "gpu forward")

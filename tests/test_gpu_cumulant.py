@@ -117,7 +117,11 @@ def test_cumulant_reduces_to_block_mean_score(lsa, beta):
 
 @pytest.mark.parametrize("name", ["qwen05b_n32k", "qwen05b_n128k_needles"])
 def test_cumulant_full_size_sampled_rows(lsa, name):
-    w = WORKLOADS[name]
+    check_cumulant_sampled_rows(lsa, WORKLOADS[name])
+
+
+def check_cumulant_sampled_rows(lsa, w):
+    name = w.name
     say("cumulant full", name, "generating")
     inp = generate(w)
     say("cumulant full", name, "gpu forward")

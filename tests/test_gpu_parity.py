@@ -254,7 +254,13 @@ FULL = ["qwen05b_n32k", "qwen05b_n128k_needles", "image_zorder_128x128", "qwen05
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_rows(lsa, name):
-    w = WORKLOADS[name]
+    check_sampled_rows(lsa, WORKLOADS[name])
+
+
+def check_sampled_rows(lsa, w, nrows=6000):
+    """The whole layer on the GPU, then routing and output parity on a
+    uniform sample of nrows rows (plus every needle row) against the oracle."""
+    name = w.name
     say("full", name, "generating")
     inp = generate(w)
     say("full", name, "gpu forward")
@@ -264,7 +270,7 @@ def test_full_size_sampled_rows(lsa, name):
     D = 64
     if w.causal:
         R = w.batch * w.q_heads * w.seq_len
-        rows = np.sort(rng.choice(R, size=min(R, 6000), replace=False))
+        rows = np.sort(rng.choice(R, size=min(R, nrows), replace=False))
         if inp.needles:  # every needle query row is checked too
             extra = [(n.b * w.q_heads + n.h) * w.seq_len + n.t for n in inp.needles]
             rows = np.unique(np.concatenate([rows, np.array(extra)]))

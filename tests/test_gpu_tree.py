@@ -114,8 +114,11 @@ def test_tree_with_beam_covering_every_node_is_flat_routing(lsa):
 
 @pytest.mark.parametrize("name", ["qwen05b_n128k_needles", "qwen05b_n1m_needles"])
 def test_tree_full_size_sampled_rows(lsa, name):
-    w = WORKLOADS[name]
-    beam = 8
+    check_tree_sampled_rows(lsa, WORKLOADS[name], 8)
+
+
+def check_tree_sampled_rows(lsa, w, beam):
+    name = w.name
     say("tree full", name, "generating")
     inp = generate(w)
     say("tree full", name, "gpu forward")
