@@ -16,7 +16,9 @@ query: QK^T and PV), `ms_per_step` is ms per layer.
 with HIP events recorded between the library's kernel launches on the same
 stream), `cpu_baseline` the CPU oracle timed on a bounded row sample on this
 host.  `--copy-calibration` instead runs a plain copy of known size, used to
-scale the FETCH_SIZE / WRITE_SIZE counters.
+scale the FETCH_SIZE / WRITE_SIZE counters; `--access-calibration` times
+128-byte row copies with sequential and random sides, the attainable rate of
+the partial kernel's access pattern.
 """
 from __future__ import annotations
 
@@ -41,28 +43,29 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # plain copy of known size; tied to the sources of that kernel's translation
 # unit and the compile flags it was measured with (kernel_digest).
 TRAFFIC = {
-    "csrc": "fd4fc761c639f352", "stage": 6, "workload": "qwen05b_n128k_needles",
+    "csrc": "6990aa67ee61b96d", "stage": 6, "workload": "qwen05b_n128k_needles",
     "fetch_kib": 1.918e+06, "write_kib": 3.91e+06, "fetch_factor": 2.0, "write_factor": 1.0,
     "bytes_per_launch": 1.918e+06 * 1024 * 2.0 + 3.91e+06 * 1024 * 1.0,
 }
 
 
-# The attention kernels' translation unit: its source, the headers it
-# includes, and the build script that holds the compile flags.
+# The attention kernels' translation unit: its source and the headers it
+# includes; with them the compile flags (paths relative to the repository).
 KERNEL_SOURCES = [
     "content_routed_block_amd/csrc/attend.hip",
     "content_routed_block_amd/csrc/bucket.hpp",
     "content_routed_block_amd/csrc/lsa_common.hpp",
     "content_routed_block_amd/csrc/lsa_launch.hpp",
-    "content_routed_block_amd/build.py",
 ]
 
 
 def kernel_digest() -> str:
+    from content_routed_block_amd import build as lsa_build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    h.update("\0".join(f.replace(lsa_build.ROOT, "") for f in lsa_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -75,6 +78,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--access-calibration", action="store_true",
+                    help="time 128-byte row copies with sequential and random sides "
+                         "(the partial kernel's access pattern) and exit")
     ap.add_argument("--consensus-steps", type=int, default=10,
                     help="also time the layer with consensus routing (one route per KV group)")
     ap.add_argument("--cumulant-steps", type=int, default=3,
@@ -371,6 +377,36 @@ def copy_calibration():
                       "kernel": "torch.neg (elementwise)", "launches": 3}))
 
 
+def access_calibration():
+    """Attainable rates of the partial kernel's access pattern on this GPU:
+    30 M copies of 128-byte rows between two 4 GiB tables, sequential, with a
+    random read side, a random write side, or both (lsa_calibrate_access)."""
+    import torch
+    from content_routed_block_amd import lsa
+    rows, n = 32 * 1024 * 1024, 30_000_000
+    src = torch.zeros(rows * 32, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    ridx = torch.randperm(rows, device="cuda", generator=g)[:n].to(torch.int32)
+    widx = torch.randperm(rows, device="cuda", generator=g)[:n].to(torch.int32)
+    res = {}
+    for mode, name in ((0, "sequential"), (1, "random_read"), (2, "random_write"), (3, "random_both")):
+        for _ in range(2):
+            lsa.calibrate_access(src, dst, n, mode, ridx, widx)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            lsa.calibrate_access(src, dst, n, mode, ridx, widx)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        nbytes = n * 128 * 2 + n * 4 * ((mode & 1) + ((mode >> 1) & 1))
+        res[name] = {"ms": ms, "GB/s": nbytes / ms / 1e6}
+    print(json.dumps({"access_calibration": res, "row_bytes": 128, "copies": n,
+                      "table_bytes": rows * 128, "kernel": "lsa_calibrate_access"}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -381,6 +417,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.access_calibration:
+        access_calibration()
         return
     from content_routed_block_amd import lsa
     from content_routed_block_amd.workloads import WORKLOADS, generate

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblsa.so")
-SOURCES = ["summarize.hip", "route.hip", "tree.hip", "attend.hip", "decode.hip", "lsa_api.hip"]
+SOURCES = ["summarize.hip", "route.hip", "tree.hip", "attend.hip", "decode.hip", "lsa_api.hip",
+           "calibrate.hip"]
 ARCH = os.environ.get("LSA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -55,6 +55,9 @@ _lib.lsa_decode.argtypes = [_P, ctypes.c_int32, _v, _v, _v, _v, _v, _v, _v, ctyp
 _lib.lsa_decode.restype = ctypes.c_int
 _lib.lsa_forward_profiled.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v, _v]
 _lib.lsa_forward_profiled.restype = ctypes.c_int
+_lib.lsa_calibrate_access.argtypes = [_v, _v, _v, _v, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int32, _v]
+_lib.lsa_calibrate_access.restype = ctypes.c_int
 _lib.lsa_status_str.argtypes = [ctypes.c_int]
 _lib.lsa_status_str.restype = ctypes.c_char_p
 
@@ -292,3 +295,20 @@ def forward_profiled(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     _check(_lib.lsa_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                      _ptr(idx), _ptr(workspace), nbytes, _stream(stream),
                                      events.array), "lsa_forward_profiled")
+
+
+def calibrate_access(src: torch.Tensor, dst: torch.Tensor, n: int, mode: int,
+                     ridx: Optional[torch.Tensor] = None, widx: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """lsa_calibrate_access: n copies of 128-byte rows between two tables of
+    the same row count (modes: 0 sequential, 1 random read, 2 random write,
+    3 both; ridx/widx int32 row numbers on the device)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or nbytes % 128:
+        raise ValueError("src and dst must be tables of the same number of 128-byte rows")
+    for t, used, what in ((ridx, mode & 1, "ridx"), (widx, mode & 2, "widx")):
+        if used and (t is None or t.dtype != torch.int32 or t.numel() < n or not t.is_cuda):
+            raise ValueError(f"{what}: int32 device tensor of at least n entries required")
+    _check(_lib.lsa_calibrate_access(_ptr(src), _ptr(dst), _ptr(ridx) if mode & 1 else None,
+                                     _ptr(widx) if mode & 2 else None, nbytes // 128, n, mode,
+                                     _stream(stream)), "lsa_calibrate_access")

@@ -1,5 +1,5 @@
 """The C ABI library without a GPU: it loads, exports every function that
-include/lsa.h declares, and its host-side validation returns the documented
+include/*.h declares, and its host-side validation returns the documented
 status codes before anything is launched."""
 import ctypes
 import os
@@ -8,16 +8,19 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lsa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 LIB = os.path.join(ROOT, "content_routed_block_amd", "liblsa.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="liblsa.so not built")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +33,8 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(LIB)
     names = declared_functions()
     assert set(names) >= {"lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend",
-                          "lsa_forward", "lsa_workspace_bytes", "lsa_status_str"}
+                          "lsa_forward", "lsa_workspace_bytes", "lsa_status_str",
+                          "lsa_calibrate_access"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -168,3 +172,28 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("args,code", [
+    # (src, dst, ridx, widx, table_rows, n, mode)
+    ((0, 256, 512, 768, 100, 10, 3), 1),        # src NULL
+    ((256, 0, 512, 768, 100, 10, 0), 1),        # dst NULL
+    ((256, 512, 0, 768, 100, 10, 1), 1),        # ridx NULL, read side random
+    ((256, 512, 768, 0, 100, 10, 2), 1),        # widx NULL, write side random
+    ((256, 512, 0, 0, 100, 10, 4), 2),          # mode out of range
+    ((256, 512, 0, 0, 100, -1, 0), 2),          # negative n
+    ((256, 512, 0, 0, -1, 0, 0), 2),            # negative table
+    ((256, 512, 768, 0, 100, 101, 1), 2),       # sequential write side past the table
+    ((256, 512, 768, 1024, 100, 1 << 28, 3), 2),  # n too large
+    ((264, 512, 0, 0, 100, 10, 0), 4),          # src misaligned
+    ((256, 520, 0, 0, 100, 10, 0), 4),          # dst misaligned
+    ((256, 512, 0, 0, 100, 0, 0), 0),           # nothing to do: returns before any launch
+])
+def test_calibrate_access_argument_checks(args, code):
+    lib = ctypes.CDLL(LIB)
+    f = lib.lsa_calibrate_access
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    ptrs = [ctypes.c_void_p(a) if a else None for a in args[:4]]
+    assert f(*ptrs, args[4], args[5], args[6], None) == code
