@@ -121,6 +121,25 @@ __device__ __forceinline__ void bitonic_sort_asc_u32(uint32_t* v) {
             }
 }
 
+// Sorts 16 64-bit keys into descending order.
+__device__ __forceinline__ void bitonic_sort_desc_u64(uint64_t (&v)[kMaxTopK]) {
+#pragma unroll
+    for (int size = 2; size <= kMaxTopK; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int i = 0; i < kMaxTopK; ++i) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const uint64_t a = v[i], b = v[j];
+                    const bool desc = (i & size) == 0;
+                    const bool swap = desc ? a < b : a > b;
+                    v[i] = swap ? b : a;
+                    v[j] = swap ? a : b;
+                }
+            }
+}
+
 // k-th largest (1 <= k <= 16) of the 64 values held as the per-class
 // largest (m1) and second largest (m2) values of 16 classes in this lane and
 // 16 more classes in lane ^ 32.  Both lanes of the pair return the same value.
@@ -551,12 +570,25 @@ __global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
         return;
     }
     uint64_t L[kMaxTopK];
+    if (__builtin_amdgcn_ballot_w64(n_mine > kMaxTopK) == 0) {
+        // every lane found at most 16: read them all at once (slots past
+        // n_mine hold stale values and become the zero key) and sort
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
-    for (int i = 0; i < n_mine; ++i) {
-        const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
-        insert_key(L, sel_key(*reinterpret_cast<const float*>(s_list + e),
-                              *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (e >> 1))));
+        for (int i = 0; i < kMaxTopK; ++i) {
+            const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
+            const uint64_t key = sel_key(*reinterpret_cast<const float*>(s_list + e),
+                                         *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (e >> 1)));
+            L[i] = i < n_mine ? key : 0;
+        }
+        bitonic_sort_desc_u64(L);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
+        for (int i = 0; i < n_mine; ++i) {
+            const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
+            insert_key(L, sel_key(*reinterpret_cast<const float*>(s_list + e),
+                                  *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (e >> 1))));
+        }
     }
     uint64_t M[kMaxTopK];
 #pragma unroll
