@@ -9,7 +9,8 @@
 // about top_k + window/bs blocks of K/V and the eligible block means), so it
 // runs on the vector ALUs in fp32, in two launches with enough workgroups to
 // spread the reads:
-//   1. k_decode_route   per (row, chunk of 1024 eligible blocks): scores
+//   1. k_decode_route   per (row, chunk of 256, 512 or 1024 eligible blocks,
+//                       the smallest that keeps 16 chunks per row): scores
 //                       q . kbar_c and keeps the chunk's top-k keys (score,
 //                       then lower index).  Extra workgroups write the mean
 //                       of the block that token T-1 completes (when T is a
@@ -34,9 +35,15 @@
 
 namespace lsa {
 
-constexpr int DC_CHUNK = 1024;  // candidate blocks per routing workgroup
 constexpr int DC_SPLIT = 256;   // keys per attention workgroup
 constexpr int DC_MAXCH = 64;    // chunk lists per row (E <= nb <= 65536)
+
+// Candidate blocks per lane of a routing wave: the smallest chunk (256, 512
+// or 1024 blocks) that covers the row in at most 16 chunks, so that the
+// attention step merges at most 256 keys per row; past 16384 blocks, 1024
+// (at most 64 chunks, as N/bs <= 65536).  Smaller chunks spread the block
+// means over more workgroups; more chunks cost the merge more than they save.
+static inline int decode_kpl(int E) { return E <= 16 * 256 ? 1 : (E <= 16 * 512 ? 2 : 4); }
 
 struct DecodeArgs {
     const uint16_t* q;   // [B*Hq][64]
@@ -115,6 +122,7 @@ __device__ __forceinline__ int wave_compact(const uint64_t (&key)[n], uint64_t t
 // first wave selects the chunk's top_k among the four wave sets.  Workgroups
 // past rows * nchunk update the block-mean cache instead (one per KV head);
 // workgroup 0 also clears the rows' split counters for step 2.
+template <int KPL>
 __global__ __launch_bounds__(256) void k_decode_route(DecodeArgs a) {
     __shared__ float s_q[kD];
     __shared__ uint64_t s_list[4 * kMaxTopK];
@@ -156,11 +164,11 @@ __global__ __launch_bounds__(256) void k_decode_route(DecodeArgs a) {
     if (tid < kD) s_q[tid] = bf16_bits_to_f32(a.q[(int64_t)row * kD + tid]);
     for (int i = tid; i < 4 * kMaxTopK; i += 256) s_list[i] = 0;
     __syncthreads();
-    const int c0 = ch * DC_CHUNK + w * (DC_CHUNK / 4);
+    const int c0 = ch * (256 * KPL) + w * (64 * KPL);
     const float* kb = a.kbar + (int64_t)bg * (a.t_max / a.bs) * kD;
-    uint64_t key[DC_CHUNK / 256];
+    uint64_t key[KPL];
 #pragma unroll
-    for (int i = 0; i < DC_CHUNK / 256; ++i) {
+    for (int i = 0; i < KPL; ++i) {
         const int c = c0 + lane + 64 * i;
         key[i] = 0;
         if (c < a.E) {
@@ -331,7 +339,8 @@ static DecodeLayout decode_layout(const Geometry& g, int t_max) {
     DecodeLayout L{};
     // sized for the longest sequence the cache allows (T <= t_max)
     const int E = eligible_blocks(t_max - 1, g.bs, g.window);
-    L.nchunk = std::max(1, (E + DC_CHUNK - 1) / DC_CHUNK);
+    L.nchunk = std::max(1, (E + 256 * decode_kpl(E) - 1) / (256 * decode_kpl(E)));
+    L.nchunk = std::max(L.nchunk, std::min(DC_MAXCH, (E + 255) / 256));  // any T <= t_max
     // keys per row: at most top_k routed blocks plus a window of < window + bs keys
     L.nsplit = (g.top_k * g.bs + g.window + g.bs + DC_SPLIT - 1) / DC_SPLIT;
     const size_t rows = (size_t)g.B * g.Hq;
@@ -369,16 +378,22 @@ hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const 
     a.top_k = g.top_k;
     a.window = g.window;
     a.E = eligible_blocks(g.N - 1, g.bs, g.window);
-    a.nchunk = std::max(1, (a.E + DC_CHUNK - 1) / DC_CHUNK);
-    if (a.nchunk > DC_MAXCH) return hipErrorInvalidValue;  // the merge holds 64 chunk sets
+    const int kpl = decode_kpl(a.E);
+    a.nchunk = std::max(1, (a.E + 256 * kpl - 1) / (256 * kpl));
+    if (a.nchunk > DC_MAXCH || a.nchunk > L.nchunk)
+        return hipErrorInvalidValue;  // the merge holds 64 chunk sets
     // this step's keys: at most top_k routed blocks plus the window [bs*E, T-1]
     const int keys = std::min(a.E, g.top_k) * g.bs + (g.N - g.bs * a.E);
     a.nsplit = std::max(1, (keys + DC_SPLIT - 1) / DC_SPLIT);
     a.summ_block = g.N / g.bs - 1;  // token T-1 completes this block when bs divides T
     a.scale_log2 = g.scale * kLog2e;
     const int summ_wgs = g.N % g.bs == 0 ? g.B * g.Hkv : 0;
-    hipLaunchKernelGGL(k_decode_route, dim3((unsigned)(a.rows * a.nchunk + summ_wgs)), dim3(256),
-                       0, s, a);
+    const dim3 rgrid((unsigned)(a.rows * a.nchunk + summ_wgs));
+    switch (kpl) {
+        case 1: hipLaunchKernelGGL(k_decode_route<1>, rgrid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(k_decode_route<2>, rgrid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(k_decode_route<4>, rgrid, dim3(256), 0, s, a); break;
+    }
     hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)(a.rows * a.nsplit)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
