@@ -36,6 +36,7 @@
 namespace lsa {
 
 constexpr int DC_SPLIT = 256;   // keys per attention workgroup
+constexpr int kMaxBlock = 128;  // largest key block (bs)
 constexpr int DC_MAXCH = 64;    // chunk lists per row (E <= nb <= 65536)
 
 // Candidate blocks per lane of a routing wave: the smallest chunk (256, 512
@@ -138,11 +139,22 @@ __global__ __launch_bounds__(256) void k_decode_route(DecodeArgs a) {
         double acc[8];
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[d] = 0.0;
-        for (int j = j0; j < a.bs; j += 8) {
-            float f[8];
-            unpack8(*reinterpret_cast<const u32x4*>(base + (int64_t)j * kD), f);
+        // all of this lane's rows requested before any is summed (bs / 8 <= 16)
+        u32x4 raw[kMaxBlock / 8];
 #pragma unroll
-            for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
+        for (int i = 0; i < kMaxBlock / 8; ++i) {
+            const int j = j0 + 8 * i;
+            raw[i] = j < a.bs ? *reinterpret_cast<const u32x4*>(base + (int64_t)j * kD)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxBlock / 8; ++i) {
+            if (j0 + 8 * i < a.bs) {
+                float f[8];
+                unpack8(raw[i], f);
+#pragma unroll
+                for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
+            }
         }
 #pragma unroll
         for (int m = 8; m < 64; m <<= 1)
@@ -265,6 +277,17 @@ __global__ __launch_bounds__(256) void k_decode_attend(DecodeArgs a) {
         return j < n_routed ? s_blk[j / a.bs] * a.bs + (j % a.bs) : win0 + (j - n_routed);
     };
     float s = -INFINITY;
+    // this thread's V pieces for the P.V step (keys kg, kg + 32, ..., dims
+    // 8dg..8dg+7), requested together with the K row so that their latency
+    // overlaps the scores and the softmax reductions
+    const int kg = tid >> 3, dg = tid & 7;
+    u32x4 vraw[DC_SPLIT / 32];
+#pragma unroll
+    for (int i = 0; i < DC_SPLIT / 32; ++i) {
+        const int j = kg + 32 * i;
+        vraw[i] = j < np ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)token_of(p0 + j) * kD + 8 * dg)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
     if (tid < np) {
         const uint16_t* kr = kbase + (int64_t)token_of(p0 + tid) * kD;
         u32x4 raw[kD / 8];
@@ -283,16 +306,19 @@ __global__ __launch_bounds__(256) void k_decode_attend(DecodeArgs a) {
     const float pj = tid < np ? exp2f(s - mx) : 0.f;
     s_p[tid] = pj;
     const float l = block_sum_f32(pj, s_red);  // its barriers also publish s_p
-    const int kg = tid >> 3, dg = tid & 7;
     float acc[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[d] = 0.f;
-    for (int j = kg; j < np; j += 32) {
-        float f[8];
-        unpack8(*reinterpret_cast<const u32x4*>(vbase + (int64_t)token_of(p0 + j) * kD + 8 * dg), f);
-        const float pv = s_p[j];
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] = fmaf(pv, f[d], acc[d]);
+    for (int i = 0; i < DC_SPLIT / 32; ++i) {
+        const int j = kg + 32 * i;
+        if (j < np) {
+            float f[8];
+            unpack8(vraw[i], f);
+            const float pv = s_p[j];
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[d] = fmaf(pv, f[d], acc[d]);
+        }
     }
 #pragma unroll
     for (int d = 0; d < 8; ++d) s_acc[kg][8 * dg + d] = acc[d];
@@ -315,15 +341,33 @@ __global__ __launch_bounds__(256) void k_decode_attend(DecodeArgs a) {
     if (!s_last) return;
     __threadfence();
     if (tid < kD) {
+        // the splits in batches of eight, each batch's partials requested
+        // before any is used; running maximum with rescaling between batches
         const float* pr = a.part + (int64_t)row * a.nsplit * (2 + kD);
-        float M = -INFINITY;
-        for (int i = 0; i < a.nsplit; ++i) M = fmaxf(M, pr[i * (2 + kD)]);
-        float L = 0.f, O = 0.f;
-        for (int i = 0; i < a.nsplit; ++i) {
-            const float mi = pr[i * (2 + kD)];
-            const float f = mi == -INFINITY ? 0.f : exp2f(mi - M);
-            L = fmaf(pr[i * (2 + kD) + 1], f, L);
-            O = fmaf(pr[i * (2 + kD) + 2 + tid], f, O);
+        float M = -INFINITY, L = 0.f, O = 0.f;
+        for (int i0 = 0; i0 < a.nsplit; i0 += 8) {
+            float mi[8], li[8], oi[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u;
+                const bool have = i < a.nsplit;
+                mi[u] = have ? pr[i * (2 + kD)] : -INFINITY;
+                li[u] = have ? pr[i * (2 + kD) + 1] : 0.f;
+                oi[u] = have ? pr[i * (2 + kD) + 2 + tid] : 0.f;
+            }
+            float mb = M;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mb = fmaxf(mb, mi[u]);
+            const float alpha = M == -INFINITY ? 0.f : exp2f(M - mb);
+            L *= alpha;
+            O *= alpha;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float f = mi[u] == -INFINITY ? 0.f : exp2f(mi[u] - mb);
+                L = fmaf(li[u], f, L);
+                O = fmaf(oi[u], f, O);
+            }
+            M = mb;
         }
         a.out[(int64_t)row * kD + tid] = O / L;  // the window always holds key T-1
     }
