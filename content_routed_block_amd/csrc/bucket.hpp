@@ -156,9 +156,11 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
     const int per = (NB + 1023) / 1024;
     const int lo = min(NB, tid * per), hi = min(NB, lo + per);
     uint32_t sp = 0, su = 0;
+#pragma unroll 8
     for (int i = lo; i < hi; ++i) {
-        sp += counts[i];
-        su += (counts[i] + UNIT_ROWS - 1) / UNIT_ROWS;
+        const uint32_t n = counts[i];
+        sp += n;
+        su += (n + UNIT_ROWS - 1) / UNIT_ROWS;
     }
     s_p[tid] = sp;
     s_u[tid] = su;
@@ -172,12 +174,14 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
         __syncthreads();
     }
     uint32_t rp = s_p[tid] - sp, ru = s_u[tid] - su;
+#pragma unroll 8
     for (int i = lo; i < hi; ++i) {
+        const uint32_t n = counts[i];
         offsets[i] = rp;
         cursor[i] = rp;
         unit_off[i] = ru;
-        rp += counts[i];
-        ru += (counts[i] + UNIT_ROWS - 1) / UNIT_ROWS;
+        rp += n;
+        ru += (n + UNIT_ROWS - 1) / UNIT_ROWS;
     }
     if (tid == 1023) {
         offsets[NB] = s_p[1023];

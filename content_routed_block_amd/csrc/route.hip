@@ -216,6 +216,15 @@ __device__ __forceinline__ void write_selection(int32_t* out, const uint64_t (&L
     }
 }
 
+// Two-level routing's tail slot of causal row t: the partial node (fewer
+// than kTreeFanout eligible blocks) that every row keeps after its beam, or
+// -1 when the eligible blocks fill whole nodes.
+__device__ __forceinline__ int tail_node(int t, int bs, int window) {
+    const int E = eligible_blocks(t, bs, window);
+    const int S = E >> kTreeFanoutLog2;
+    return (S << kTreeFanoutLog2) < E ? S : -1;
+}
+
 // ------------------------------------------------------------ preparation
 // One thread per (block row, 8 dims): bf16 hi/lo split of the block means
 // (rows padded to a multiple of 32 with zeros) and the row norms.
@@ -603,6 +612,10 @@ __global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
     if (half == 0) {
         const int m = n_pair < a.top_k ? n_pair : a.top_k;
         write_selection(a.idx + out_row * a.idx_stride, M, m, a.top_k, a.idx_stride);
+        // two-level routing (rows of beam + 1 slots): the tail node, written
+        // beside the row's other slots
+        if (CAUSAL && a.idx_stride > a.top_k)
+            a.idx[out_row * a.idx_stride + a.top_k] = tail_node(rq, a.bs, a.window);
     }
 }
 
@@ -629,6 +642,8 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
                             : bf16_bits_to_f32(a.q[((int64_t)bh * a.N + row) * kD + tid]);
         }
         __syncthreads();
+        // unrolled so that several rows' loads are in flight per trip
+#pragma unroll 4
         for (int c = tid; c < E; c += 256) {
             const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)c * kD);
             float s = 0.f;
@@ -647,6 +662,7 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
         int m = 0;
         for (int j = 0; j < a.top_k; ++j) {
             uint64_t best = 0;
+#pragma unroll 8
             for (int c = tid; c < E; c += 256) {
                 const uint64_t key = sel_key(sc[c], (uint32_t)c);
                 if (key < prev && key > best) best = key;
@@ -673,6 +689,8 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) L[j] = j < m ? s_keys[j] : 0;
             write_selection(a.idx + (int64_t)rid * a.idx_stride, L, m, a.top_k, a.idx_stride);
+            if (CAUSAL && a.idx_stride > a.top_k)
+                a.idx[(int64_t)rid * a.idx_stride + a.top_k] = tail_node(row, a.bs, a.window);
         }
         __syncthreads();
     }
@@ -957,15 +975,13 @@ __global__ __launch_bounds__(256) void k_node_means(const float* __restrict__ kb
               (float)(acc[6] / kTreeFanout), (float)(acc[7] / kTreeFanout)};
 }
 
-// Slot `beam` of each row's slot list: the incomplete tail node S = E / 16
-// when it holds candidates (16 S < E), else -1.
+// Slot `beam` of each row's slot list (tail_node), for launches where no row
+// has a complete node and so no routing kernel runs to write it.
 __global__ __launch_bounds__(256) void k_tree_tail(int32_t* __restrict__ slots, int beam,
                                                    int64_t rows, int N, int bs, int window) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (row >= rows) return;
-    const int E = eligible_blocks((int)(row % N), bs, window);
-    const int S = E >> kTreeFanoutLog2;
-    slots[row * (beam + 1) + beam] = (S << kTreeFanoutLog2) < E ? S : -1;
+    slots[row * (beam + 1) + beam] = tail_node((int)(row % N), bs, window);
 }
 
 // ------------------------------------------------------------ host side
@@ -1139,13 +1155,15 @@ static hipError_t route_tree(const Geometry& g, const uint16_t* q, const float* 
                            nu, g.nb, T.nn, n);
         e = route_flat(tree_level1_geometry(g), q, nu, slots, stride, kTreeFanoutLog2,
                        base + T.lvl1, s, nullptr);
+        // the routing kernels write each row's tail slot with its beam
     } else {
         e = launch_fill_u32(reinterpret_cast<uint32_t*>(slots), (size_t)rows * stride,
                             0xFFFFFFFFu, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_tree_tail, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                           slots, g.beam, rows, g.N, g.bs, g.window);
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_tree_tail, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, slots,
-                       g.beam, rows, g.N, g.bs, g.window);
     const int64_t prep_threads = (int64_t)nbg * T.nb_pad * 8;
     hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
                        kbar, bhi, blo, bn, bn + (size_t)nbg * g.nb, nbg, g.nb, T.nb_pad);
