@@ -744,13 +744,17 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
 
     hipError_t e = launch_fill_u32(counts, (size_t)NB, 0u, s);
     if (e != hipSuccess) return e;
-    // positions per bucketing workgroup: ~4096 rows, and enough pairs to
-    // amortise the per-bucket flush
+    // positions per bucketing workgroup: ~4096 rows, or fewer when that
+    // leaves under ~256 workgroups (short sequences), but always enough
+    // pairs to amortise the per-bucket flush.  (Smaller chunks at long
+    // sequences speed the bucketing up but interleave each bucket's pairs
+    // more, which the partial and merge kernels pay back.)
     const int rep = g.Hq / g.Hkv;
-    int64_t tc = std::max<int64_t>(
-        (4096 + rep - 1) / rep,
-        (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k));
-    tc = std::min<int64_t>((tc + 63) / 64 * 64, g.N);
+    const int64_t flush_min =
+        (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k);
+    int64_t tc = std::min<int64_t>((4096 + rep - 1) / rep, (int64_t)nbg * g.N / 256);
+    tc = std::max<int64_t>(tc, flush_min);
+    tc = std::min<int64_t>(std::max<int64_t>((tc + 63) / 64 * 64, 64), g.N);
     const int64_t rows = (int64_t)g.B * g.Hq * g.N;
     BucketArgs ba{idx, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window,
                   (int)tc, sp_log2, g.consensus, 0};
