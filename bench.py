@@ -43,9 +43,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # plain copy of known size; tied to the sources of that kernel's translation
 # unit and the compile flags it was measured with (kernel_digest).
 TRAFFIC = {
-    "csrc": "6990aa67ee61b96d", "stage": 6, "workload": "qwen05b_n128k_needles",
-    "fetch_kib": 1.919e+06, "write_kib": 3.911e+06, "fetch_factor": 2.0, "write_factor": 1.0,
-    "bytes_per_launch": 1.919e+06 * 1024 * 2.0 + 3.911e+06 * 1024 * 1.0,
+    "csrc": "7c96de04c47523eb", "stage": 6, "workload": "qwen05b_n128k_needles",
+    "fetch_kib": 1.918e+06, "write_kib": 3.911e+06, "fetch_factor": 2.0, "write_factor": 1.0,
+    "bytes_per_launch": 1.918e+06 * 1024 * 2.0 + 3.911e+06 * 1024 * 1.0,
 }
 
 
