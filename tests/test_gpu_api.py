@@ -1,0 +1,90 @@
+"""The C ABI's conventions on the GPU: lsa_forward without idx_out (the
+routes then live in the workspace) equals the call that returns them, for
+every routing variant; a call on a side stream equals one on the default
+stream bit for bit; a workspace of exactly lsa_workspace_bytes works and,
+when the routes must live in it, one byte less is refused before anything
+runs."""
+import numpy as np
+import pytest
+import torch
+
+from content_routed_block_amd.workloads import Workload, generate
+from tests.parity import dev, params_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from content_routed_block_amd import lsa as m
+    return m
+
+
+def causal_w(seed=61):
+    return Workload("api_causal", 1, 4, 2, 2048 + 64, 64, 64, 8, 192, 1, "topics", topics=16,
+                    seed=seed)
+
+
+def image_w(seed=62):
+    return Workload("api_image", 2, 2, 2, 1024, 64, 16, 6, 0, 0, "normal", seed=seed)
+
+
+VARIANTS = [
+    (causal_w, {}),
+    (causal_w, {"consensus": 1}),
+    (causal_w, {"beta": 0.25}),
+    (causal_w, {"beam": 3}),
+    (image_w, {}),
+    (image_w, {"consensus": 1}),
+]
+
+
+@pytest.mark.parametrize("make,over", VARIANTS,
+                         ids=["flat", "consensus", "cumulant", "tree", "image", "image-consensus"])
+def test_forward_without_idx_out_equals_with(lsa, make, over):
+    w = make()
+    inp = generate(w)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    p = params_of(lsa, w, **over)
+    o1, i1 = lsa.forward(p, q, k, v)
+    o2, i2 = lsa.forward(p, q, k, v, want_idx=False)
+    torch.cuda.synchronize()
+    assert i2 is None
+    assert torch.equal(o1, o2)
+
+
+def test_forward_on_a_side_stream_equals_default_stream(lsa):
+    w = causal_w()
+    inp = generate(w)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    p = params_of(lsa, w)
+    o1, i1 = lsa.forward(p, q, k, v)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o2, i2 = lsa.forward(p, q, k, v, stream=side)
+    side.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(o1, o2)
+
+
+def test_workspace_exact_size_and_one_byte_short(lsa):
+    w = causal_w()
+    inp = generate(w)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    p = params_of(lsa, w)
+    need = lsa.workspace_bytes(p, lsa.OP_FORWARD)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o1, _ = lsa.forward(p, q, k, v, workspace=ws)
+    o0, _ = lsa.forward(p, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)
+    # without idx_out the routes live in the workspace, so all of it is needed
+    o2, _ = lsa.forward(p, q, k, v, want_idx=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o2)
+    short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(Exception, match="LSA_ERR_WORKSPACE"):
+        lsa.forward(p, q, k, v, want_idx=False, workspace=short)
