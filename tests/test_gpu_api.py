@@ -88,3 +88,31 @@ def test_workspace_exact_size_and_one_byte_short(lsa):
     short = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
     with pytest.raises(Exception, match="LSA_ERR_WORKSPACE"):
         lsa.forward(p, q, k, v, want_idx=False, workspace=short)
+
+
+def test_concurrent_calls_on_two_streams(lsa):
+    """Two layers in flight at once on two streams, each with its own
+    workspace and outputs, give what each gives alone."""
+    wa, wb = causal_w(seed=63), causal_w(seed=64)
+    ia, ib = generate(wa), generate(wb)
+    qa, ka, va = dev(ia.q), dev(ia.k), dev(ia.v)
+    qb, kb, vb = dev(ib.q), dev(ib.k), dev(ib.v)
+    pa, pb = params_of(lsa, wa), params_of(lsa, wb)
+    ref_a, ref_ia = lsa.forward(pa, qa, ka, va)
+    ref_b, ref_ib = lsa.forward(pb, qb, kb, vb)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa, xa = lsa.forward(pa, qa, ka, va, stream=s1)
+        with torch.cuda.stream(s2):
+            ob, xb = lsa.forward(pb, qb, kb, vb, stream=s2)
+        outs.append((oa, xa, ob, xb))
+    s1.synchronize()
+    s2.synchronize()
+    for oa, xa, ob, xb in outs:
+        assert torch.equal(oa, ref_a) and torch.equal(xa, ref_ia)
+        assert torch.equal(ob, ref_b) and torch.equal(xb, ref_ib)
