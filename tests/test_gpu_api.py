@@ -116,3 +116,41 @@ def test_concurrent_calls_on_two_streams(lsa):
     for oa, xa, ob, xb in outs:
         assert torch.equal(oa, ref_a) and torch.equal(xa, ref_ia)
         assert torch.equal(ob, ref_b) and torch.equal(xb, ref_ib)
+
+
+def test_forward_replays_from_a_graph(lsa):
+    """lsa_forward captured in a HIP graph (preallocated outputs and
+    workspace) replays to the eager result, also after the inputs change in
+    place, with eager work and synchronisations between replays."""
+    w = causal_w(seed=65)
+    i1, i2 = generate(w), generate(causal_w(seed=66))
+    q, k, v = dev(i1.q), dev(i1.k), dev(i1.v)
+    p = params_of(lsa, w)
+    out = torch.empty((w.batch, w.q_heads, w.seq_len, 64), dtype=torch.float32, device="cuda")
+    idx = torch.empty(lsa.idx_shape(p), dtype=torch.int32, device="cuda")
+    ws = torch.empty(lsa.workspace_bytes(p, lsa.OP_FORWARD), dtype=torch.uint8, device="cuda")
+    ref1, rid1 = lsa.forward(p, q, k, v)
+    ref2, rid2 = lsa.forward(p, dev(i2.q), dev(i2.k), dev(i2.v))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        lsa.forward(p, q, k, v, out=out, idx=idx, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lsa.forward(p, q, k, v, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src = i1 if rep % 2 == 0 else i2
+        q.copy_(dev(src.q))
+        k.copy_(dev(src.k))
+        v.copy_(dev(src.v))
+        lsa.forward(p, dev(i2.q), dev(i2.k), dev(i2.v))   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want_o, want_i = (ref1, rid1) if rep % 2 == 0 else (ref2, rid2)
+        assert torch.equal(out, want_o), rep
+        assert torch.equal(idx, want_i), rep
