@@ -46,7 +46,7 @@ constexpr int RT_ROWS = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int RT_CH = 32;      // candidates per step
 constexpr int RT_CAP = 28;     // survivor slots per query (five workgroups still fit a CU)
 constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
-constexpr int FB_GRID = 256;   // workgroups of the exact fallback
+constexpr int FB_GRID = 1024;  // workgroups of the exact fallback
 
 struct RouteArgs {
     const uint16_t* q;    // bf16 queries [B,Hq,N,64] (QF32 = false)
@@ -59,7 +59,6 @@ struct RouteArgs {
     int32_t* idx;         // [B,Hq,P,top_k] (Hq = routed heads: Hkv with consensus)
     uint32_t* ovf_count;  // queued overflow rows
     uint32_t* ovf_rows;   // [B*Hq*P]
-    float* fb_scratch;    // [FB_GRID][nb]
     int Hq, Hkv, N, bs, nb, top_k, window;
     int P;       // rows per (b, h): N (causal) or nb (image)
     int tiles;   // ceil(P / RT_ROWS)
@@ -620,79 +619,137 @@ __global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
 }
 
 // ------------------------------------------------------------ exact fallback
-// One workgroup per queued row: fp32 scores of every candidate into a
-// private scratch row, then top_k rounds of "largest key below the previous
-// one".  Slow but exact for any input (ties included).
+// Largest 32-bit value of the wave, in every lane: quad swaps, the half-row
+// and row mirrors (DPP, folded into the max), then the 16- and 32-lane
+// swaps, all in registers.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t x) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+    return o > x ? o : x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max_dpp_u32<0xB1>(x);   // quad_perm(1,0,3,2): lane ^ 1
+    x = max_dpp_u32<0x4E>(x);   // quad_perm(2,3,0,1): lane ^ 2
+    x = max_dpp_u32<0x141>(x);  // row_half_mirror: the other quad of the 8
+    x = max_dpp_u32<0x140>(x);  // row_mirror: the other 8 of the row
+    // each swap leaves a lane its own value and its partner's, in some order
+    const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = s16[0] > s16[1] ? s16[0] : s16[1];
+    const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return s32[0] > s32[1] ? s32[0] : s32[1];
+}
+
+// The wave's kMaxTopK largest keys, descending (0 past the last), from
+// per-lane lists sorted descending; the lists are consumed.  Rank r takes the
+// largest score word over the lanes' heads, then the largest id word among
+// the heads with that score word; the lane holding it drops its head.  After
+// rank r a list is read at most kMaxTopK - 1 - r more times, so the drop
+// shifts only that many entries.  Returns how many keys are valid.
+__device__ __forceinline__ int wave_top_keys(uint64_t (&L)[kMaxTopK], uint64_t (&R)[kMaxTopK],
+                                             int top_k) {
+    int m = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) {
+        R[r] = 0;
+        if (r < top_k && m == r) {
+            const uint32_t hh = (uint32_t)(L[0] >> 32);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane(wave_max_u32(hh));
+            if (hi != 0) {  // keys are unique and nonzero: exactly one lane holds the max
+                const uint32_t lo = __builtin_amdgcn_readfirstlane(
+                    wave_max_u32(hh == hi ? (uint32_t)L[0] : 0u));
+                const uint64_t mx = ((uint64_t)hi << 32) | lo;
+                R[r] = mx;
+                m = r + 1;
+                if (L[0] == mx) {
+#pragma unroll
+                    for (int j = 0; j + 1 < kMaxTopK - r; ++j) L[j] = L[j + 1];
+                }
+            }
+        }
+    }
+    return m;
+}
+
+// Queued rows are redone exactly: fp32 scores of every candidate (fma chain
+// over d = 0..63), each lane keeping the 16 best keys of the candidates it
+// scored in registers, then rank-by-rank wave maxima.  Exact for any input,
+// ties included.  With more rows than workgroups a wave takes a row of its
+// own (no barriers); otherwise the four waves of a workgroup split each
+// row's candidates and wave 0 merges their four lists through LDS.
 template <bool CAUSAL, bool QF32>
 __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
-    __shared__ float s_q[kD];
-    __shared__ uint64_t s_red[4];
-    __shared__ uint64_t s_keys[kMaxTopK];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const uint32_t count = *a.ovf_count;
-    float* sc = a.fb_scratch + (size_t)blockIdx.x * a.nb;
-    for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
-        const uint32_t rid = a.ovf_rows[i];
+    __shared__ uint64_t s_top[4][kMaxTopK];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t count = __builtin_amdgcn_readfirstlane(*a.ovf_count);
+    const int ways = count <= gridDim.x ? 4 : 1;  // waves per row, uniform over the grid
+    const int groups = 4 / ways;
+    const int sub = w % ways;
+    for (uint32_t i = blockIdx.x * groups + w / ways; i < count; i += gridDim.x * groups) {
+        const uint32_t rid = __builtin_amdgcn_readfirstlane(a.ovf_rows[i]);
         const int bh = (int)(rid / (uint32_t)a.P), row = (int)(rid % (uint32_t)a.P);
         const int h = bh % a.Hq, b = bh / a.Hq, g = h / (a.Hq / a.Hkv);
         const float* kb = a.kbar + (int64_t)(b * a.Hkv + g) * a.nb * kD;
         const int E = row_candidates(CAUSAL, row, a.P, a.bs, a.window, a.nb, a.cshift);
-        if (tid < kD) {
-            s_q[tid] = QF32 ? a.qbar[((int64_t)bh * a.P + row) * kD + tid]
-                            : bf16_bits_to_f32(a.q[((int64_t)bh * a.N + row) * kD + tid]);
+        // the query row is the same for every lane: scalar loads
+        float qv[kD];
+        if (QF32) {
+            const __attribute__((address_space(4))) float* qp =
+                (const __attribute__((address_space(4))) float*)(a.qbar + ((int64_t)bh * a.P + row) * kD);
+#pragma unroll
+            for (int d = 0; d < kD; ++d) qv[d] = qp[d];
+        } else {
+            const __attribute__((address_space(4))) uint32_t* qp =
+                (const __attribute__((address_space(4))) uint32_t*)(a.q + ((int64_t)bh * a.N + row) * kD);
+#pragma unroll
+            for (int d2 = 0; d2 < kD / 2; ++d2) {
+                const uint32_t u = qp[d2];
+                qv[2 * d2] = __uint_as_float(u << 16);
+                qv[2 * d2 + 1] = __uint_as_float(u & 0xFFFF0000u);
+            }
         }
-        __syncthreads();
-        // unrolled so that several rows' loads are in flight per trip
-#pragma unroll 4
-        for (int c = tid; c < E; c += 256) {
+        uint64_t L[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
+        // one candidate per lane per trip: 64 VGPRs of loads keep the kernel
+        // at four waves per SIMD, which serves the many-rows case better than
+        // more loads in flight per wave
+        const int step = 64 * ways;
+        for (int c = sub * 64 + lane; c < E; c += step) {
             const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)c * kD);
-            float s = 0.f;
-#pragma unroll 4
-            for (int d4 = 0; d4 < kD / 4; ++d4) {
-                const f32x4 v = kr[d4];
-                s = fmaf(s_q[4 * d4], v[0], s);
-                s = fmaf(s_q[4 * d4 + 1], v[1], s);
-                s = fmaf(s_q[4 * d4 + 2], v[2], s);
-                s = fmaf(s_q[4 * d4 + 3], v[3], s);
-            }
-            sc[c] = s;
+            f32x4 v[kD / 4];
+#pragma unroll
+            for (int d4 = 0; d4 < kD / 4; ++d4) v[d4] = kr[d4];
+            float sc = 0.f;
+#pragma unroll
+            for (int d4 = 0; d4 < kD / 4; ++d4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc = fmaf(qv[4 * d4 + e], v[d4][e], sc);
+            const uint64_t key = sel_key(sc, (uint32_t)c);
+            if (key > L[kMaxTopK - 1]) insert_key(L, key);
         }
-        __syncthreads();
-        uint64_t prev = ~0ull;
-        int m = 0;
-        for (int j = 0; j < a.top_k; ++j) {
-            uint64_t best = 0;
-#pragma unroll 8
-            for (int c = tid; c < E; c += 256) {
-                const uint64_t key = sel_key(sc[c], (uint32_t)c);
-                if (key < prev && key > best) best = key;
-            }
+        uint64_t R[kMaxTopK];
+        int m = wave_top_keys(L, R, a.top_k);
+        if (ways > 1) {
+            if (lane == 0) {
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const uint64_t o = __shfl_xor(best, off, kWave);
-                best = o > best ? o : best;
+                for (int r = 0; r < kMaxTopK; ++r) s_top[w][r] = R[r];
             }
-            if (lane == 0) s_red[w] = best;
             __syncthreads();
-            best = s_red[0];
+            if (w == 0) {
+                // one key per lane, four sorted lists of 16
+                L[0] = s_top[lane >> 4][lane & 15];
 #pragma unroll
-            for (int q = 1; q < 4; ++q) best = s_red[q] > best ? s_red[q] : best;
+                for (int j = 1; j < kMaxTopK; ++j) L[j] = 0;
+                m = wave_top_keys(L, R, a.top_k);
+            }
             __syncthreads();
-            if (best == 0) break;
-            if (tid == 0) s_keys[j] = best;
-            prev = best;
-            ++m;
         }
-        __syncthreads();
-        if (tid == 0) {
-            uint64_t L[kMaxTopK];
-#pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) L[j] = j < m ? s_keys[j] : 0;
-            write_selection(a.idx + (int64_t)rid * a.idx_stride, L, m, a.top_k, a.idx_stride);
+        if (w % ways == 0 && lane == 0) {
+            write_selection(a.idx + (int64_t)rid * a.idx_stride, R, m, a.top_k, a.idx_stride);
             if (CAUSAL && a.idx_stride > a.top_k)
                 a.idx[(int64_t)rid * a.idx_stride + a.top_k] = tail_node(row, a.bs, a.window);
         }
-        __syncthreads();
     }
 }
 
@@ -992,7 +1049,7 @@ static size_t route_rows(const Geometry& g) {
 }
 
 struct RouteLayout {
-    size_t ovf_rows, fb, qbar, qsum, khi, klo, pk, total;
+    size_t ovf_rows, qbar, qsum, khi, klo, pk, total;
     int nb_pad;
 };
 
@@ -1002,7 +1059,6 @@ static RouteLayout route_layout(const Geometry& g) {
     const size_t nbg = (size_t)g.B * g.Hkv;
     size_t off = 256;  // overflow counter
     L.ovf_rows = off; off += align_up(route_rows(g) * 4, 256);
-    L.fb = off;       off += align_up((size_t)FB_GRID * g.nb * 4, 256);
     L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * g.nb * kD * 4, 256);
     L.qsum = off;     if (g.consensus) off += align_up(route_rows(g) * kD * 4, 256);
     L.khi = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
@@ -1075,7 +1131,6 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     RouteArgs a;
     a.ovf_count = reinterpret_cast<uint32_t*>(base);
     a.ovf_rows = reinterpret_cast<uint32_t*>(base + L.ovf_rows);
-    a.fb_scratch = reinterpret_cast<float*>(base + L.fb);
     float* qbar = g.causal ? nullptr : reinterpret_cast<float*>(base + L.qbar);
     float* qsum = g.consensus ? reinterpret_cast<float*>(base + L.qsum) : nullptr;
     uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);

@@ -129,7 +129,11 @@ lsa_status lsa_block_summarize(const lsa_params *p, const void *x, int32_t heads
  *   selection.  Routing work per row falls from E(t) to about
  *   E(t)/16 + 16 beam + 15 scores.
  * beta != 0 is LSA_ERR_UNSUPPORTED here: that score needs the keys
- * themselves (lsa_route_cumulant). */
+ * themselves (lsa_route_cumulant).
+ * Diagnostic: after a call with beam = 0 has run, the workspace's first
+ * 4 bytes hold (uint32) how many rows overflowed the fast path's survivor
+ * lists and were redone by the exact pass (ties on many blocks cause this);
+ * the result is the same either way. */
 lsa_status lsa_route_topk(const lsa_params *p, const void *q, const float *kbar,
                           int32_t *idx, void *workspace, size_t workspace_bytes,
                           void *stream);

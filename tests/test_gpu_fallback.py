@@ -1,0 +1,132 @@
+"""The exact pass that redoes routing rows whose survivor list overflowed,
+through the C ABI against the CPU oracle.
+
+Keys whose blocks all repeat one of a few patterns make every row's scores
+tie in groups, so the survivor lists overflow and the exact pass decides the
+selection, ties to the lower block.  Equal summaries give equal scores on
+both sides, so the selection is compared exactly on every row whose distinct
+scores are more than 1e-3 apart.  The first word of the routing workspace
+counts the rows the exact pass redid; each case checks that it ran.  The
+"few" cases queue fewer rows than the exact pass has workgroups (the four
+waves of a workgroup then share a row); the "many" cases queue thousands
+(a wave per row)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from content_routed_block_amd.workloads import Workload, generate, to_bf16_bits
+from tests.parity import GAP, causal_candidates, dev, params_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from content_routed_block_amd import lsa as m
+    return m
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def case(B, Hq, Hkv, N, bs, k, W, npat, causal=1, consensus=0, seed=61):
+    w = Workload(f"fb_b{B}_h{Hq}x{Hkv}_n{N}_bs{bs}_k{k}_w{W}_p{npat}_c{causal}{consensus}", B, Hq,
+                 Hkv, N, 64, bs, k, W, causal, "normal", seed=seed)
+    return w, npat, consensus
+
+
+CASES = [
+    # causal, per-head routes
+    case(1, 2, 1, 2048, 64, 4, 128, 1),     # few: every score ties
+    case(1, 4, 1, 8192, 64, 16, 512, 1),    # many
+    case(1, 4, 2, 8192, 64, 16, 512, 2),    # many, two tie groups
+    case(2, 3, 1, 4096, 32, 5, 64, 3),      # odd top-k, three groups
+    case(1, 2, 1, 4096, 64, 16, 256, 2),
+    # image mode (pooled fp32 queries)
+    case(1, 1, 1, 4096, 16, 8, 0, 1, causal=0),
+    case(1, 4, 4, 4096, 16, 8, 0, 1, causal=0),
+    case(1, 4, 2, 4096, 16, 16, 0, 2, causal=0),
+    # consensus (group-summed fp32 queries)
+    case(1, 2, 1, 2048, 64, 16, 128, 1, consensus=1),
+    case(1, 4, 2, 4096, 64, 16, 256, 1, consensus=1),
+    case(1, 4, 2, 4096, 64, 16, 256, 2, consensus=1),
+]
+
+
+def patterned_keys(w, npat, seed):
+    """Block c's keys all equal pattern c % npat (random normal rows)."""
+    rng = np.random.default_rng(seed)
+    P = rng.standard_normal((npat, 64)).astype(np.float32)
+    nb = w.seq_len // w.block
+    K = np.repeat(P[np.arange(nb) % npat], w.block, axis=0)  # [N, 64]
+    K = np.broadcast_to(K, (w.batch, w.kv_heads, w.seq_len, 64))
+    return to_bf16_bits(K)
+
+
+def clear_rows(scores):
+    """Rows whose distinct finite scores are all more than GAP apart."""
+    ok = np.ones(scores.shape[0], bool)
+    for r in range(scores.shape[0]):
+        s = scores[r]
+        u = np.unique(s[np.isfinite(s)])
+        ok[r] = u.size < 2 or np.diff(u).min() > GAP
+    return ok
+
+
+@pytest.mark.parametrize("w,npat,consensus", CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_exact_pass_matches_oracle(lsa, w, npat, consensus):
+    say("exact pass", w.name)
+    inp = generate(w)
+    inp.k[:] = patterned_keys(w, npat, w.seed + 1)
+    p = params_of(lsa, w, consensus=consensus)
+    q, k = dev(inp.q), dev(inp.k)
+    kbar = lsa.block_summarize(p, k)
+    ws = torch.zeros(lsa.workspace_bytes(p, lsa.OP_ROUTE), dtype=torch.uint8, device="cuda")
+    idx = lsa.route_topk(p, q, kbar, workspace=ws)
+    torch.cuda.synchronize()
+    redone = int(ws[:4].view(torch.int32).item())
+    idx = idx.cpu().numpy().reshape(-1, w.top_k)
+    kbar_o = oracle.block_means(inp.k, w.block)
+    np.testing.assert_array_equal(kbar.cpu().numpy(), kbar_o)
+    nb = w.seq_len // w.block
+    per = w.seq_len if w.causal else nb
+    R = idx.shape[0]
+    rows = np.arange(R)
+    if consensus:
+        if w.causal:
+            io, _, sc = oracle.route_consensus(kbar_o, w.block, w.top_k, q=inp.q, window=w.window,
+                                               causal=1, rows=rows, with_gap=True, with_scores=True)
+        else:
+            qbar = oracle.block_means(inp.q, w.block)
+            io, _, sc = oracle.route_consensus(kbar_o, w.block, w.top_k, qbar=qbar, causal=0,
+                                               rows=rows, with_gap=True, with_scores=True)
+    elif w.causal:
+        io = oracle.route_causal(inp.q, kbar_o, w.block, w.top_k, w.window, rows=rows)
+        sc = oracle.route_scores(kbar_o, rows, q=inp.q, block=w.block, window=w.window, causal=1)
+    else:
+        qbar = oracle.block_means(inp.q, w.block)
+        io = oracle.route_image(qbar, kbar_o, w.top_k, rows=rows)
+        sc = oracle.route_scores(kbar_o, rows, qbar=qbar, block=w.block, causal=0)
+    io = np.asarray(io).reshape(R, w.top_k)
+    ok = clear_rows(np.asarray(sc))
+    say("  rows", R, "redone exactly", redone, "clear", int(ok.sum()))
+    assert redone > 0
+    assert ok.mean() > 0.9
+    bad = np.nonzero(ok & np.any(idx != io, axis=1))[0]
+    assert bad.size == 0, (bad[:5], idx[bad[:1]], io[bad[:1]])
+    # the rest: ascending candidate ids, padded with -1
+    t = rows % per
+    ncand = causal_candidates(t, w.block, w.window) if w.causal else np.full(R, nb)
+    for r in np.nonzero(~ok)[0][:200]:
+        m = min(w.top_k, int(ncand[r]))
+        sel = idx[r]
+        assert np.all(sel[m:] == -1) and np.all(np.diff(sel[:m]) > 0), (r, sel)
+        if m:
+            assert sel[0] >= 0 and sel[m - 1] < ncand[r], (r, sel)
