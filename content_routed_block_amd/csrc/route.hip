@@ -46,7 +46,8 @@ constexpr int RT_ROWS = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int RT_CH = 32;      // candidates per step
 constexpr int RT_CAP = 28;     // survivor slots per query (five workgroups still fit a CU)
 constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
-constexpr int FB_GRID = 1024;  // workgroups of the exact fallback
+constexpr int FB_GRID = 1024;  // rows the per-row exact pass takes (one workgroup each);
+                               // above this the queued tiles are redone whole
 
 struct RouteArgs {
     const uint16_t* q;    // bf16 queries [B,Hq,N,64] (QF32 = false)
@@ -59,6 +60,8 @@ struct RouteArgs {
     int32_t* idx;         // [B,Hq,P,top_k] (Hq = routed heads: Hkv with consensus)
     uint32_t* ovf_count;  // queued overflow rows
     uint32_t* ovf_rows;   // [B*Hq*P]
+    uint32_t* tile_count; // queued tiles (workgroups with an overflowing row)
+    uint32_t* tile_queue; // [items]
     int Hq, Hkv, N, bs, nb, top_k, window;
     int P;       // rows per (b, h): N (causal) or nb (image)
     int tiles;   // ceil(P / RT_ROWS)
@@ -324,8 +327,8 @@ __device__ __forceinline__ int clamp_i32(int x, int lo, int hi) {
 // ------------------------------------------------------------ main kernel
 // Each wave is independent (its own 32 rows and survivor lists); the
 // workgroup only shares the staged candidate chunks.
-template <bool CAUSAL, bool QF32>
-__global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
+template <bool CAUSAL, bool QF32, bool EXACT>
+__global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(RouteArgs a) {
     // candidate staging: pass 1 double-buffers the hi parts in s_stage[0..1];
     // pass 2 holds one chunk's hi part in s_stage[0] and lo part in
     // s_stage[1] (two barriers per chunk), which keeps the workgroup's LDS
@@ -345,9 +348,19 @@ __global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
     // the tiles of one head and the heads of one KV group, on one XCD (whose
     // L2 then holds that group's candidate blocks).  Tiles of a head run
     // heavy (late positions, most candidates) first.
-    const int per_xcd = gridDim.x / 8;
-    const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (item >= a.items) return;
+    int item;
+    if constexpr (EXACT) {
+        // the queued tiles, when more rows overflowed than the per-row pass takes
+        if (__builtin_amdgcn_readfirstlane(*a.ovf_count) <= (uint32_t)FB_GRID) return;
+        if (blockIdx.x >= __builtin_amdgcn_readfirstlane(*a.tile_count)) return;
+        item = (int)__builtin_amdgcn_readfirstlane(a.tile_queue[blockIdx.x]);
+    } else {
+        const int per_xcd = gridDim.x / 8;
+        item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+        if (item >= a.items) return;
+    }
+    __shared__ uint32_t s_ovf;  // some row of the workgroup overflowed
+    if (tid == 0) s_ovf = 0u;   // read after the passes' barriers
     const int bh = item / a.tiles;
     const int tile = a.tiles - 1 - (item - bh * a.tiles);
     const int h = bh % a.Hq, b = bh / a.Hq;
@@ -488,6 +501,10 @@ __global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
     // an overflowing list stays in bounds (the row is then redone by the
     // fallback).
     const int qrow = 32 * w + l32;  // row within the workgroup
+    // whole-tile exact pass: each lane's 16 best selection keys, descending
+    uint64_t Lk[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) Lk[j] = 0;
     // list position kept as the byte offset of the score slot; the block
     // id of slot e sits at byte LIST_IDX + e/2
     constexpr int LIST_IDX = RT_CAP * RT_ROWS * 4;
@@ -527,7 +544,15 @@ __global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
                     if (QF32) acc = mfma32(ch[ks], Bql[ks], acc);
                 }
                 const int cl0 = cb + 4 * half;
-                if (cb < Efull) {
+                if constexpr (EXACT) {
+                    // 64-bit keys carry the tie-break (lower block) themselves
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int c = cl0 + 8 * (r >> 2) + (r & 3);
+                        const uint64_t key = sel_key(acc[r], (uint32_t)c);
+                        if (acc[r] >= theta && c < Erow && key > Lk[kMaxTopK - 1]) insert_key(Lk, key);
+                    }
+                } else if (cb < Efull) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         if (acc[r] >= theta) {
@@ -566,10 +591,38 @@ __global__ __launch_bounds__(256, QF32 ? 4 : 5) void k_route(RouteArgs a) {
 
     // ---- selection: each lane of the pair ranks the survivors it found,
     // then the pair merges its two sorted lists.
+    const int64_t out_row = (int64_t)bh * P + rq;
+    if constexpr (EXACT) {
+        // the pair's lists hold disjoint candidates and merge in one
+        // bitonic step
+        uint64_t Mx[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            const uint64_t o = Lk[kMaxTopK - 1 - j];
+            const uint32_t olo = __shfl_xor((uint32_t)o, 32, kWave);
+            const uint32_t ohi = __shfl_xor((uint32_t)(o >> 32), 32, kWave);
+            const uint64_t other = ((uint64_t)ohi << 32) | olo;
+            Mx[j] = Lk[j] > other ? Lk[j] : other;
+        }
+        bitonic_merge_desc_u64(Mx);
+        if (rq < P && half == 0) {
+            int m = 0;
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) m += (j < a.top_k && Mx[j] != 0ull) ? 1 : 0;
+            write_selection(a.idx + out_row * a.idx_stride, Mx, m, a.top_k, a.idx_stride);
+            if (CAUSAL && a.idx_stride > a.top_k)
+                a.idx[out_row * a.idx_stride + a.top_k] = tail_node(rq, a.bs, a.window);
+        }
+        return;
+    }
     const int n_mine = (half ? at_hi - at : at - at_lo) / (RT_ROWS * 4);
     const int n_pair = n_mine + __shfl_xor(n_mine, 32, kWave);
+    // a workgroup with an overflowing row queues its tile once, for the
+    // whole-tile exact pass that runs when many rows overflow
+    if (rq < P && n_pair > RT_CAP && half == 0) s_ovf = 1u;
+    __syncthreads();
+    if (tid == 0 && s_ovf != 0u) a.tile_queue[atomicAdd(a.tile_count, 1u)] = (uint32_t)item;
     if (rq >= P) return;
-    const int64_t out_row = (int64_t)bh * P + rq;
     if (n_pair > RT_CAP) {
         if (half == 0) {
             const uint32_t slot = atomicAdd(a.ovf_count, 1u);
@@ -670,22 +723,20 @@ __device__ __forceinline__ int wave_top_keys(uint64_t (&L)[kMaxTopK], uint64_t (
     return m;
 }
 
-// Queued rows are redone exactly: fp32 scores of every candidate (fma chain
-// over d = 0..63), each lane keeping the 16 best keys of the candidates it
-// scored in registers, then rank-by-rank wave maxima.  Exact for any input,
-// ties included.  With more rows than workgroups a wave takes a row of its
-// own (no barriers); otherwise the four waves of a workgroup split each
-// row's candidates and wave 0 merges their four lists through LDS.
+// Queued rows are redone exactly, one workgroup per row, when there are at
+// most FB_GRID of them (more are redone by whole tiles, k_route<.., true>):
+// fp32 scores of every candidate (fma chain over d = 0..63), each lane
+// keeping the 16 best keys of the candidates it scored in registers, then
+// rank-by-rank wave maxima; wave 0 merges the four waves' lists through
+// LDS.  Exact for any input, ties included.
 template <bool CAUSAL, bool QF32>
 __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
     __shared__ uint64_t s_top[4][kMaxTopK];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t count = __builtin_amdgcn_readfirstlane(*a.ovf_count);
-    const int ways = count <= gridDim.x ? 4 : 1;  // waves per row, uniform over the grid
-    const int groups = 4 / ways;
-    const int sub = w % ways;
-    for (uint32_t i = blockIdx.x * groups + w / ways; i < count; i += gridDim.x * groups) {
+    if (count > (uint32_t)FB_GRID) return;  // the whole-tile pass takes them
+    for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
         const uint32_t rid = __builtin_amdgcn_readfirstlane(a.ovf_rows[i]);
         const int bh = (int)(rid / (uint32_t)a.P), row = (int)(rid % (uint32_t)a.P);
         const int h = bh % a.Hq, b = bh / a.Hq, g = h / (a.Hq / a.Hkv);
@@ -711,11 +762,8 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
         uint64_t L[kMaxTopK];
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
-        // one candidate per lane per trip: 64 VGPRs of loads keep the kernel
-        // at four waves per SIMD, which serves the many-rows case better than
-        // more loads in flight per wave
-        const int step = 64 * ways;
-        for (int c = sub * 64 + lane; c < E; c += step) {
+        // one candidate per lane per trip (64 VGPRs of loads, four waves per SIMD)
+        for (int c = threadIdx.x; c < E; c += 256) {
             const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)c * kD);
             f32x4 v[kD / 4];
 #pragma unroll
@@ -730,22 +778,20 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
         }
         uint64_t R[kMaxTopK];
         int m = wave_top_keys(L, R, a.top_k);
-        if (ways > 1) {
-            if (lane == 0) {
+        if (lane == 0) {
 #pragma unroll
-                for (int r = 0; r < kMaxTopK; ++r) s_top[w][r] = R[r];
-            }
-            __syncthreads();
-            if (w == 0) {
-                // one key per lane, four sorted lists of 16
-                L[0] = s_top[lane >> 4][lane & 15];
-#pragma unroll
-                for (int j = 1; j < kMaxTopK; ++j) L[j] = 0;
-                m = wave_top_keys(L, R, a.top_k);
-            }
-            __syncthreads();
+            for (int r = 0; r < kMaxTopK; ++r) s_top[w][r] = R[r];
         }
-        if (w % ways == 0 && lane == 0) {
+        __syncthreads();
+        if (w == 0) {
+            // one key per lane, four sorted lists of 16
+            L[0] = s_top[lane >> 4][lane & 15];
+#pragma unroll
+            for (int j = 1; j < kMaxTopK; ++j) L[j] = 0;
+            m = wave_top_keys(L, R, a.top_k);
+        }
+        __syncthreads();
+        if (w == 0 && lane == 0) {
             write_selection(a.idx + (int64_t)rid * a.idx_stride, R, m, a.top_k, a.idx_stride);
             if (CAUSAL && a.idx_stride > a.top_k)
                 a.idx[(int64_t)rid * a.idx_stride + a.top_k] = tail_node(row, a.bs, a.window);
@@ -1048,8 +1094,14 @@ static size_t route_rows(const Geometry& g) {
     return (size_t)g.B * route_heads(g) * (g.causal ? (size_t)g.N : (size_t)g.nb);
 }
 
+// Routing workgroups (tiles of RT_ROWS rows) over all (b, routed head).
+static size_t route_items(const Geometry& g) {
+    const size_t P = g.causal ? (size_t)g.N : (size_t)g.nb;
+    return (size_t)g.B * route_heads(g) * ((P + RT_ROWS - 1) / RT_ROWS);
+}
+
 struct RouteLayout {
-    size_t ovf_rows, qbar, qsum, khi, klo, pk, total;
+    size_t ovf_rows, tiles, qbar, qsum, khi, klo, pk, total;
     int nb_pad;
 };
 
@@ -1059,6 +1111,7 @@ static RouteLayout route_layout(const Geometry& g) {
     const size_t nbg = (size_t)g.B * g.Hkv;
     size_t off = 256;  // overflow counter
     L.ovf_rows = off; off += align_up(route_rows(g) * 4, 256);
+    L.tiles = off;    off += align_up(route_items(g) * 4, 256);
     L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * g.nb * kD * 4, 256);
     L.qsum = off;     if (g.consensus) off += align_up(route_rows(g) * kD * 4, 256);
     L.khi = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
@@ -1114,9 +1167,12 @@ size_t route_workspace_bytes(const Geometry& g) {
 template <bool CAUSAL, bool QF32>
 static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
                                  const hipEvent_t* ev) {
-    hipLaunchKernelGGL((k_route<CAUSAL, QF32>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_route<CAUSAL, QF32, false>), grid, dim3(256), 0, s, a);
     mark(ev, 2, s);
+    // exactly one of the two exact passes does work, chosen on the device by
+    // the number of overflowing rows
     hipLaunchKernelGGL((k_route_fallback<CAUSAL, QF32>), dim3(FB_GRID), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_route<CAUSAL, QF32, true>), grid, dim3(256), 0, s, a);
 }
 
 // Flat routing of g's rows over g.nb summaries `summ` into idx (row stride
@@ -1131,6 +1187,8 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     RouteArgs a;
     a.ovf_count = reinterpret_cast<uint32_t*>(base);
     a.ovf_rows = reinterpret_cast<uint32_t*>(base + L.ovf_rows);
+    a.tile_count = a.ovf_count + 1;  // the word after the row count
+    a.tile_queue = reinterpret_cast<uint32_t*>(base + L.tiles);
     float* qbar = g.causal ? nullptr : reinterpret_cast<float*>(base + L.qbar);
     float* qsum = g.consensus ? reinterpret_cast<float*>(base + L.qsum) : nullptr;
     uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
@@ -1159,7 +1217,7 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     a.nb_pad = L.nb_pad;
     a.cshift = cshift;
     a.idx_stride = idx_stride;
-    hipError_t e = launch_fill_u32(a.ovf_count, 1, 0u, s);
+    hipError_t e = launch_fill_u32(a.ovf_count, 2, 0u, s);  // row and tile counts
     if (e != hipSuccess) return e;
     if (!g.causal) {
         e = launch_summarize(q, qbar, g.B * g.Hq, g.N, g.bs, s);

@@ -132,8 +132,10 @@ lsa_status lsa_block_summarize(const lsa_params *p, const void *x, int32_t heads
  * themselves (lsa_route_cumulant).
  * Diagnostic: after a call with beam = 0 has run, the workspace's first
  * 4 bytes hold (uint32) how many rows overflowed the fast path's survivor
- * lists and were redone by the exact pass (ties on many blocks cause this);
- * the result is the same either way. */
+ * lists (ties on many blocks cause this), and the next 4 bytes how many
+ * 128-row tiles held such a row.  Up to 1024 such rows are redone one by
+ * one; beyond that, those tiles are redone whole.  The result is the same
+ * either way. */
 lsa_status lsa_route_topk(const lsa_params *p, const void *q, const float *kbar,
                           int32_t *idx, void *workspace, size_t workspace_bytes,
                           void *stream);

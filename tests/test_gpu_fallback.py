@@ -5,11 +5,10 @@ Keys whose blocks all repeat one of a few patterns make every row's scores
 tie in groups, so the survivor lists overflow and the exact pass decides the
 selection, ties to the lower block.  Equal summaries give equal scores on
 both sides, so the selection is compared exactly on every row whose distinct
-scores are more than 1e-3 apart.  The first word of the routing workspace
-counts the rows the exact pass redid; each case checks that it ran.  The
-"few" cases queue fewer rows than the exact pass has workgroups (the four
-waves of a workgroup then share a row); the "many" cases queue thousands
-(a wave per row)."""
+scores are more than 1e-3 apart.  The first two words of the routing
+workspace count the overflowing rows and the 128-row tiles holding them;
+each case checks that the exact pass ran.  Up to 1024 rows are redone one by
+one (the "few" cases), beyond that whole tiles are (the "many" cases)."""
 import sys
 
 import numpy as np
@@ -36,26 +35,30 @@ def say(*a):
     sys.stdout.flush()
 
 
-def case(B, Hq, Hkv, N, bs, k, W, npat, causal=1, consensus=0, seed=61):
+ROWS_ONE_BY_ONE = 1024  # overflowing rows redone one by one; more: whole tiles
+
+
+def case(B, Hq, Hkv, N, bs, k, W, npat, causal=1, consensus=0, expect=None, seed=61):
     w = Workload(f"fb_b{B}_h{Hq}x{Hkv}_n{N}_bs{bs}_k{k}_w{W}_p{npat}_c{causal}{consensus}", B, Hq,
                  Hkv, N, 64, bs, k, W, causal, "normal", seed=seed)
-    return w, npat, consensus
+    return w, npat, consensus, expect
 
 
 CASES = [
     # causal, per-head routes
-    case(1, 2, 1, 2048, 64, 4, 128, 1),     # few: every score ties
-    case(1, 4, 1, 8192, 64, 16, 512, 1),    # many
-    case(1, 4, 2, 8192, 64, 16, 512, 2),    # many, two tie groups
-    case(2, 3, 1, 4096, 32, 5, 64, 3),      # odd top-k, three groups
+    case(1, 2, 1, 2048, 64, 4, 128, 1, expect="few"),   # every score ties
+    case(1, 4, 1, 8192, 64, 16, 512, 1, expect="many"),
+    case(1, 4, 2, 8192, 64, 16, 512, 2, expect="many"),  # two tie groups
+    case(2, 3, 1, 4096, 32, 5, 64, 3, expect="many"),    # odd top-k, three groups
     case(1, 2, 1, 4096, 64, 16, 256, 2),
+    case(1, 3, 1, 16 * 700, 16, 6, 32, 2, expect="many"),  # 16-key blocks, partial last tile
     # image mode (pooled fp32 queries)
-    case(1, 1, 1, 4096, 16, 8, 0, 1, causal=0),
-    case(1, 4, 4, 4096, 16, 8, 0, 1, causal=0),
+    case(1, 1, 1, 4096, 16, 8, 0, 1, causal=0, expect="few"),
+    case(1, 8, 4, 4096, 16, 8, 0, 1, causal=0, expect="many"),
     case(1, 4, 2, 4096, 16, 16, 0, 2, causal=0),
     # consensus (group-summed fp32 queries)
-    case(1, 2, 1, 2048, 64, 16, 128, 1, consensus=1),
-    case(1, 4, 2, 4096, 64, 16, 256, 1, consensus=1),
+    case(1, 2, 1, 2048, 64, 16, 128, 1, consensus=1, expect="few"),
+    case(1, 4, 2, 4096, 64, 16, 256, 1, consensus=1, expect="many"),
     case(1, 4, 2, 4096, 64, 16, 256, 2, consensus=1),
 ]
 
@@ -80,8 +83,9 @@ def clear_rows(scores):
     return ok
 
 
-@pytest.mark.parametrize("w,npat,consensus", CASES, ids=lambda c: getattr(c, "name", str(c)))
-def test_exact_pass_matches_oracle(lsa, w, npat, consensus):
+@pytest.mark.parametrize("w,npat,consensus,expect", CASES,
+                         ids=lambda c: getattr(c, "name", str(c)))
+def test_exact_pass_matches_oracle(lsa, w, npat, consensus, expect):
     say("exact pass", w.name)
     inp = generate(w)
     inp.k[:] = patterned_keys(w, npat, w.seed + 1)
@@ -91,7 +95,7 @@ def test_exact_pass_matches_oracle(lsa, w, npat, consensus):
     ws = torch.zeros(lsa.workspace_bytes(p, lsa.OP_ROUTE), dtype=torch.uint8, device="cuda")
     idx = lsa.route_topk(p, q, kbar, workspace=ws)
     torch.cuda.synchronize()
-    redone = int(ws[:4].view(torch.int32).item())
+    redone, tiles = (int(x) for x in ws[:8].view(torch.int32).cpu())
     idx = idx.cpu().numpy().reshape(-1, w.top_k)
     kbar_o = oracle.block_means(inp.k, w.block)
     np.testing.assert_array_equal(kbar.cpu().numpy(), kbar_o)
@@ -116,8 +120,12 @@ def test_exact_pass_matches_oracle(lsa, w, npat, consensus):
         sc = oracle.route_scores(kbar_o, rows, qbar=qbar, block=w.block, causal=0)
     io = np.asarray(io).reshape(R, w.top_k)
     ok = clear_rows(np.asarray(sc))
-    say("  rows", R, "redone exactly", redone, "clear", int(ok.sum()))
-    assert redone > 0
+    say("  rows", R, "overflowing", redone, "in tiles", tiles, "clear", int(ok.sum()))
+    assert redone > 0 and 0 < tiles <= redone
+    if expect == "few":
+        assert redone <= ROWS_ONE_BY_ONE
+    elif expect == "many":
+        assert redone > ROWS_ONE_BY_ONE
     assert ok.mean() > 0.9
     bad = np.nonzero(ok & np.any(idx != io, axis=1))[0]
     assert bad.size == 0, (bad[:5], idx[bad[:1]], io[bad[:1]])
@@ -130,3 +138,25 @@ def test_exact_pass_matches_oracle(lsa, w, npat, consensus):
         assert np.all(sel[m:] == -1) and np.all(np.diff(sel[:m]) > 0), (r, sel)
         if m:
             assert sel[0] >= 0 and sel[m - 1] < ncand[r], (r, sel)
+
+
+@pytest.mark.parametrize("N,Hq", [(8192, 1), (16384, 2)])
+def test_exact_pass_two_level_all_ties(lsa, N, Hq):
+    """Two-level routing scores nodes with the flat router, so with equal
+    keys its node level overflows too (a few hundred rows at N = 8192, many
+    thousands at N = 16384).  Every score ties, so every row must take the
+    lowest min(k, E(t)) blocks."""
+    w = Workload(f"fb_tree_n{N}_h{Hq}", 1, Hq, 1, N, 64, 16, 8, 32, 1, "normal", seed=71)
+    say("exact pass, two-level", w.name)
+    inp = generate(w)
+    inp.k[:] = patterned_keys(w, 1, 72)
+    p = params_of(lsa, w, beam=4)
+    q, k = dev(inp.q), dev(inp.k)
+    kbar = lsa.block_summarize(p, k)
+    idx = lsa.route_topk(p, q, kbar).cpu().numpy().reshape(Hq, N, w.top_k)
+    E = causal_candidates(np.arange(N), w.block, w.window)
+    m = np.minimum(w.top_k, E)
+    want = np.where(np.arange(w.top_k)[None, :] < m[:, None], np.arange(w.top_k)[None, :], -1)
+    for h in range(Hq):
+        bad = np.nonzero(np.any(idx[h] != want, axis=1))[0]
+        assert bad.size == 0, (h, bad[:5], idx[h, bad[:1]], want[bad[:1]])
