@@ -12,6 +12,10 @@ Default workload: the Qwen2.5-0.5B-shaped layer at N=131072 (B=1, 14 query /
 TFLOP/s counted on the selected keys only (4*D FLOP per selected key and
 query: QK^T and PV), `ms_per_step` is ms per layer.
 
+Variant legs in the same line: consensus routing, the second-cumulant
+score, two-level routing, decode, and `ties` (every key equal, so every
+routing score ties: the exact routing passes' worst case).
+
 `roofline` describes the dominant kernel (largest mean stage time, measured
 with HIP events recorded between the library's kernel launches on the same
 stream), `cpu_baseline` the CPU oracle timed on a bounded row sample on this
@@ -89,6 +93,9 @@ def parse():
                     help="also time the layer with two-level routing keeping this many nodes (0: skip)")
     ap.add_argument("--decode-steps", type=int, default=50,
                     help="also time single-query decode steps against the workload's cache")
+    ap.add_argument("--ties-steps", type=int, default=5,
+                    help="also time the layer with every key equal (every routing score ties: "
+                         "the exact routing passes' worst case)")
     return ap.parse_args()
 
 
@@ -365,6 +372,47 @@ def tree_bench(lsa, w, q, k, v, beam, steps, inp=None):
     return res
 
 
+def ties_bench(lsa, w, q, k, v, steps):
+    """The same layer with every key replaced by the first one, so that every
+    routing score ties: the survivor lists overflow and the exact routing
+    passes decide every selection.  ms per layer and stage times, the counts
+    of overflowing rows and routing tiles (the routing workspace's first two
+    words), and whether every row took its lowest min(k, E) blocks."""
+    import torch
+    p = lsa.params(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.top_k,
+                   w.window, w.causal)
+    kt = k[:, :, :1, :].expand_as(k).contiguous()
+    out = torch.empty((w.batch, w.q_heads, w.seq_len, w.head_dim), dtype=torch.float32,
+                      device=q.device)
+    idx = torch.empty(lsa.idx_shape(p), dtype=torch.int32, device=q.device)
+    ws = torch.empty(lsa.workspace_bytes(p, lsa.OP_FORWARD), dtype=torch.uint8, device=q.device)
+    for _ in range(2):
+        lsa.forward(p, q, kt, v, out=out, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    events = [lsa.StageEvents() for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        lsa.forward_profiled(p, q, kt, v, events[i], out, idx, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    stage = np.array([e.stage_ms() for e in events]).mean(axis=0)
+    for e in events:
+        e.close()
+    got = idx.cpu().numpy().reshape(-1, w.seq_len if w.causal else w.seq_len // w.block, w.top_k)
+    pos = np.arange(got.shape[1])
+    E = np.maximum(0, pos // w.block - w.window // w.block + 1) if w.causal else np.full(pos.size, pos.size)
+    m = np.minimum(w.top_k, E)
+    slots = np.arange(w.top_k)[None, :]
+    want = np.where(slots < m[:, None], slots, -1)
+    wsr = torch.zeros(lsa.workspace_bytes(p, lsa.OP_ROUTE), dtype=torch.uint8, device=q.device)
+    lsa.route_topk(p, q, lsa.block_summarize(p, kt), workspace=wsr)
+    counts = wsr[:8].view(torch.int32).cpu().numpy()
+    return {"ms_per_layer": ms, "rows": int(got.shape[0] * got.shape[1]),
+            "overflow_rows": int(counts[0]), "overflow_tiles": int(counts[1]),
+            "lowest_ids": bool(np.all(got == want[None])),
+            "stage_ms": {lsa.PROFILE_STAGES[i]: round(float(stage[i]), 4) for i in range(8)}}
+
+
 def copy_calibration():
     import torch
     n = 1 << 28                       # 256 Mi float32 = 1 GiB read + 1 GiB written
@@ -536,6 +584,8 @@ def main():
     if w.causal and args.decode_steps > 0:
         result["decode"] = decode_bench(lsa, w, q, k, v, args.decode_steps,
                                         inp if args.cpu_seconds > 0 else None)
+    if args.ties_steps > 0:
+        result["ties"] = ties_bench(lsa, w, q, k, v, args.ties_steps)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     else:

@@ -21,7 +21,7 @@ def line():
     out = subprocess.run(
         [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "qwen05b_n32k", "--steps", "2",
          "--warmup", "1", "--cpu-seconds", "1", "--decode-steps", "3", "--consensus-steps", "1",
-         "--cumulant-steps", "1", "--tree-beam", "4"],
+         "--cumulant-steps", "1", "--tree-beam", "4", "--ties-steps", "1"],
         capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert out.returncode == 0, out.stderr[-2000:]
     lines = [l for l in out.stdout.splitlines() if l.strip()]
@@ -50,5 +50,14 @@ def test_bench_roofline_and_cpu_baseline(line):
 
 
 def test_bench_variant_legs_present(line):
-    for leg in ("consensus", "cumulant", "tree", "decode"):
+    for leg in ("consensus", "cumulant", "tree", "decode", "ties"):
         assert line.get(leg), leg
+
+
+def test_bench_ties_leg_is_exact(line):
+    """Every key equal: every row overflows the survivor lists and must still
+    take its lowest blocks."""
+    t = line["ties"]
+    assert t["lowest_ids"] is True
+    assert 0 < t["overflow_tiles"] <= t["overflow_rows"] <= t["rows"]
+    assert t["ms_per_layer"] > 0
