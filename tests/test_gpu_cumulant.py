@@ -140,3 +140,31 @@ def check_cumulant_sampled_rows(lsa, w):
     ref = oracle.attend(inp.q, inp.k, inp.v, gi[rows], w.block, w.top_k, w.window, 1, rows=rows)
     mx, mean = check_output(out[rows], ref, vmax_of(w, inp, rows))
     say("  max-abs", mx, "mean-abs", mean)
+
+
+@pytest.mark.parametrize("N,bs,W,k", [(4096, 64, 512, 16), (4096, 32, 64, 16), (2048, 16, 32, 8)])
+def test_cumulant_tied_block_patterns(lsa, N, bs, W, k):
+    """Blocks repeating two multi-token key patterns: equal blocks have equal
+    means and variances, so scores tie in groups and the lower block must win
+    every tie.  Compared exactly with the oracle on rows whose distinct
+    scores are more than 1e-3 apart."""
+    w = Workload(f"cum_ties_n{N}_bs{bs}", 1, 2, 1, N, 64, bs, k, W, 1, "normal", seed=5)
+    say("cumulant tied patterns", w.name)
+    inp = generate(w)
+    P = np.random.default_rng(9).standard_normal((2, bs, 64)).astype(np.float32)
+    K = np.concatenate([P[c % 2] for c in range(N // bs)], axis=0)
+    inp.k[:] = to_bf16_bits(np.broadcast_to(K, inp.k.shape))
+    beta = 0.125
+    p = params_of(lsa, w, beta=beta)
+    idx = lsa.route_cumulant(p, dev(inp.q), dev(inp.k)).cpu().numpy().reshape(-1, k)
+    rows = np.arange(idx.shape[0])
+    io, _, sc = oracle.route_cumulant(inp.q, inp.k, oracle.block_means(inp.k, bs), bs, k, W, beta,
+                                      rows=rows, with_gap=True, with_scores=True)
+    sc = np.asarray(sc)
+    clear = np.ones(rows.size, bool)
+    for r in rows:
+        u = np.unique(sc[r][np.isfinite(sc[r])])
+        clear[r] = u.size < 2 or np.diff(u).min() > 1e-3
+    assert clear.mean() > 0.9
+    bad = np.nonzero(clear & np.any(idx != np.asarray(io).reshape(-1, k), axis=1))[0]
+    assert bad.size == 0, (bad[:5], idx[bad[:1]])

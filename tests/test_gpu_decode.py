@@ -131,3 +131,22 @@ def test_decode_at_a_million_tokens(lsa):
     out, idx = run_decode(lsa, w, inp, T, kbar)
     near, near_diff, mx = check_steps(w, inp, oracle.block_means(inp.k, w.block), [T], out, idx)
     say("  1M: near", near, "near-differing", near_diff, "max-abs", mx)
+
+
+@pytest.mark.parametrize("bs,k,W", [(64, 16, 512), (16, 5, 48)])
+def test_decode_equal_keys_take_the_lowest_blocks(lsa, bs, k, W):
+    """Every key equal: every routing score ties, so every decode step must
+    take the lowest min(k, E) blocks (the radix select over score-then-index
+    keys has no capacity to overflow)."""
+    w = custom(1, 2, 1, 8192, bs, k, W, seed=23)
+    inp = generate(w)
+    inp.k[:] = inp.k[:, :, :1, :]
+    kbar = lsa.block_summarize(params_of(lsa, w), dev(inp.k))
+    for T in (W + bs, 2 * W + 3, 4096, 8192):
+        say("decode equal keys", w.name, T)
+        _, idx = run_decode(lsa, w, inp, T, kbar)
+        E = max(0, (T - 1) // bs - W // bs + 1)
+        m = min(k, E)
+        want = list(range(m)) + [-1] * (k - m)
+        for r in range(idx.shape[0]):
+            assert list(idx[r]) == want, (T, r, idx[r])
