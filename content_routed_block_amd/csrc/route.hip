@@ -27,8 +27,12 @@
 //           16-entry sorted list of 64-bit keys (score, then lower index);
 //           the two lists are merged and the chosen block ids written in
 //           ascending order.
-// Queries whose survivor list overflows (ties, adversarial inputs) are
-// queued and redone exactly by k_route_fallback.
+// Queries whose survivor list overflows (ties on many blocks, adversarial
+// inputs) are queued, and so is each workgroup holding one.  Up to FB_GRID
+// such rows are redone one by one by k_route_fallback.  With more, the
+// queued workgroups rerun as k_route<.., EXACT = true>: the same scores,
+// but each lane keeps its 16 best 64-bit keys, with no capacity to
+// overflow.
 //
 // Consensus routing (one route per KV group, scored by the sum of the
 // group's query heads' scores; SSA page, "Complete 10M transformer result")
