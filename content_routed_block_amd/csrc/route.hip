@@ -31,8 +31,8 @@
 // inputs) are queued, and so is each workgroup holding one.  Up to FB_GRID
 // such rows are redone one by one by k_route_fallback.  With more, the
 // queued workgroups rerun as k_route<.., EXACT = true>: the same scores,
-// but each lane keeps its 16 best 64-bit keys, with no capacity to
-// overflow.
+// no threshold pass, and each lane keeps its 16 best 64-bit keys, with no
+// capacity to overflow.
 //
 // Consensus routing (one route per KV group, scored by the sum of the
 // group's query heads' scores; SSA page, "Complete 10M transformer result")
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         m2[r] = -INFINITY;
     }
     const int nch = (Ewg + RT_CH - 1) / RT_CH;  // chunks of the workgroup
-    {
+    if constexpr (!EXACT) {  // the whole-tile exact pass keeps every candidate it needs
         // chunk j is staged in buffer j&1, one barrier per chunk; the global
         // loads run two chunks ahead in two register sets (the loop body is
         // written twice so that the sets swap roles without copies)
@@ -492,8 +492,8 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
 
     // threshold: k-th largest class top-2 value minus a bound on |a_c - b_c|:
     // |q_hi . k_lo| + |q_lo . k_hi| + fp32 accumulation error.
-    float theta;
-    {
+    float theta = -INFINITY;
+    if constexpr (!EXACT) {
         const float th = kth_largest_top2_pair(m1, m2, a.top_k);
         const float delta = 1.0625f * (qn * lo_max + qln * kn_max) + 6.2e-5f * (qn + qln) * kn_max;
         theta = th - delta;  // -inf stays -inf
