@@ -20,9 +20,7 @@ routing score ties: the exact routing passes' worst case).
 with HIP events recorded between the library's kernel launches on the same
 stream), `cpu_baseline` the CPU oracle timed on a bounded row sample on this
 host.  `--copy-calibration` instead runs a plain copy of known size, used to
-scale the FETCH_SIZE / WRITE_SIZE counters; `--access-calibration` times
-128-byte row copies with sequential and random sides, the attainable rate of
-the partial kernel's access pattern.
+scale the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
@@ -42,15 +40,21 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
-# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc
-# FETCH_SIZE / WRITE_SIZE runs, each scaled by the same counter's reading on a
-# plain copy of known size; tied to the sources of that kernel's translation
-# unit and the compile flags it was measured with (kernel_digest).
-TRAFFIC = {
-    "csrc": "7c96de04c47523eb", "stage": 6, "workload": "qwen05b_n128k_needles",
-    "fetch_kib": 1.918e+06, "write_kib": 3.911e+06, "fetch_factor": 2.0, "write_factor": 1.0,
-    "bytes_per_launch": 1.918e+06 * 1024 * 2.0 + 3.911e+06 * 1024 * 1.0,
-}
+# HBM traffic per launch of the layer's kernels, by stage, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE runs, each scaled by the same counter's reading on
+# a plain copy of known size (FETCH x 2.0, WRITE x 1.0); valid only for the
+# kernel sources and compile flags they were measured with (kernel_digest).
+TRAFFIC = {}
+
+
+def traffic_counters(w):
+    """{stage name: HBM bytes per launch} when the stored counters belong to
+    this workload and to the current kernel sources, else None."""
+    t = TRAFFIC.get(w.name)
+    if not t or t.get("csrc") != kernel_digest():
+        return None
+    return {stage: fetch * 1024 * t["fetch_factor"] + write * 1024 * t["write_factor"]
+            for stage, (fetch, write) in t["kib"].items()}
 
 
 # The attention kernels' translation unit: its source and the headers it
@@ -82,9 +86,6 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--access-calibration", action="store_true",
-                    help="time 128-byte row copies with sequential and random sides "
-                         "(the partial kernel's access pattern) and exit")
     ap.add_argument("--consensus-steps", type=int, default=10,
                     help="also time the layer with consensus routing (one route per KV group)")
     ap.add_argument("--cumulant-steps", type=int, default=3,
@@ -127,6 +128,103 @@ def routing_candidates(w):
     return w.batch * w.q_heads * nb * nb
 
 
+def host_cpu():
+    """The host's CPU model and logical core counts (for the CPU baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "logical_cpus": os.cpu_count()}
+
+
+PARITY_GAP = 1e-3              # routing-score gap below which a row is a near tie
+PARITY_MAX_ABS, PARITY_MEAN_ABS = 2e-2, 5e-3
+
+
+def parity_sample(w, inp, idx_gpu, out_gpu, nrows=4000):
+    """The GPU's routing and output against the CPU oracle on a seeded sample
+    of routing rows plus every needle row (part of the CPU-baseline leg: the
+    oracle's results for these rows are computed there anyway).
+
+    Counts: clear_mismatches = rows whose oracle gap (k-th minus (k+1)-th
+    score) exceeds 1e-3 but whose GPU set differs (must be 0); near_ties =
+    rows with gap <= 1e-3; near_differing / near_invalid = near rows whose
+    GPU set differs / is not a top-k within 1e-3 under the oracle's fp64
+    scores; needle recall on GPU and oracle; max-abs and mean-abs output error
+    against the oracle attending over the GPU's own selection."""
+    import oracle
+    k = w.top_k
+    kbar = oracle.block_means(inp.k, w.block)
+    rng = np.random.default_rng(17)
+    if w.causal:
+        R = w.batch * w.q_heads * w.seq_len
+        rows = rng.choice(R, size=min(R, nrows), replace=False)
+        needle_rows = np.array([(n.b * w.q_heads + n.h) * w.seq_len + n.t for n in inp.needles],
+                               dtype=np.int64)
+        rows = np.unique(np.concatenate([rows, needle_rows]))
+        io, gap = oracle.route_causal(inp.q, kbar, w.block, k, w.window, rows=rows, with_gap=True)
+        scores = oracle.route_scores(kbar, rows, q=inp.q, block=w.block, window=w.window, causal=1)
+        t = rows % w.seq_len
+        ncand = np.maximum(0, t // w.block - w.window // w.block + 1)
+    else:
+        nb = w.seq_len // w.block
+        R = w.batch * w.q_heads * nb
+        rows = np.sort(rng.choice(R, size=min(R, nrows), replace=False))
+        needle_rows = np.zeros(0, np.int64)
+        qbar = oracle.block_means(inp.q, w.block)
+        io, gap = oracle.route_image(qbar, kbar, k, rows=rows, with_gap=True)
+        scores = oracle.route_scores(kbar, rows, qbar=qbar, block=w.block, causal=0)
+        ncand = np.full(rows.size, nb)
+    ig = idx_gpu.reshape(-1, k)[rows]
+    io = io.reshape(-1, k)
+    clear = gap.reshape(-1) > PARITY_GAP
+    differ = np.any(ig != io, axis=1)
+    invalid = 0
+    for r in np.nonzero(differ & ~clear)[0]:
+        m = min(k, int(ncand[r]))
+        sel = ig[r]
+        chosen = sel[:m]
+        ok = np.all(sel[m:] == -1) and np.all(chosen >= 0) and np.all(chosen < ncand[r]) \
+            and np.all(np.diff(chosen) > 0)
+        if ok:
+            rest = np.setdiff1d(np.arange(int(ncand[r])), chosen)
+            ok = rest.size == 0 or scores[r][chosen].min() >= scores[r][rest].max() - PARITY_GAP
+        invalid += int(not ok)
+    hits_g = hits_o = 0
+    pos = {int(r): j for j, r in enumerate(rows)}
+    for n, r in zip(inp.needles, needle_rows):
+        j = pos[int(r)]
+        hits_g += int(n.p // w.block in ig[j])
+        hits_o += int(n.p // w.block in io[j])
+    if w.causal:
+        out_rows, sel = rows, ig
+    else:
+        bh, i = rows // nb, rows % nb
+        out_rows = bh * w.seq_len + i * w.block + rng.integers(0, w.block, rows.size)
+        sel = ig
+    ref = oracle.attend(inp.q, inp.k, inp.v, sel, w.block, k, w.window, w.causal, rows=out_rows)
+    err = np.abs(out_gpu.reshape(-1, w.head_dim)[out_rows].astype(np.float64) - ref)
+    return {"rows": int(rows.size), "clear_mismatches": int(np.sum(differ & clear)),
+            "near_ties": int(np.sum(~clear)), "near_differing": int(np.sum(differ & ~clear)),
+            "near_invalid": invalid,
+            "needles": len(inp.needles), "needle_recall_gpu": hits_g,
+            "needle_recall_oracle": hits_o,
+            "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+            "tolerance": {"gap": PARITY_GAP, "max_abs": PARITY_MAX_ABS,
+                          "mean_abs": PARITY_MEAN_ABS},
+            "sample": f"{rows.size} routing rows of {R} (seeded uniform sample plus every "
+                      "needle row), compared with the CPU oracle"}
+
+
 def cpu_baseline(w, inp, target_s):
     import oracle
     R = w.batch * w.q_heads * w.seq_len
@@ -150,7 +248,7 @@ def cpu_baseline(w, inp, target_s):
         win = 0
     flops = 4 * D * (routed + win)
     return {"value": flops / wall / 1e12, "unit": "TFLOP/s (selected keys)",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", **host_cpu(),
             "sample": f"{n} of {R} query rows of {w.name}, uniform without replacement; "
                       f"{wall:.1f} s wall; full layer extrapolated {wall * R / n * 1e3:.0f} ms",
             "ms_per_layer_extrapolated": wall * R / n * 1e3}
@@ -425,36 +523,6 @@ def copy_calibration():
                       "kernel": "torch.neg (elementwise)", "launches": 3}))
 
 
-def access_calibration():
-    """Attainable rates of the partial kernel's access pattern on this GPU:
-    30 M copies of 128-byte rows between two 4 GiB tables, sequential, with a
-    random read side, a random write side, or both (lsa_calibrate_access)."""
-    import torch
-    from content_routed_block_amd import lsa
-    rows, n = 32 * 1024 * 1024, 30_000_000
-    src = torch.zeros(rows * 32, dtype=torch.int32, device="cuda")
-    dst = torch.empty_like(src)
-    g = torch.Generator(device="cuda")
-    g.manual_seed(1)
-    ridx = torch.randperm(rows, device="cuda", generator=g)[:n].to(torch.int32)
-    widx = torch.randperm(rows, device="cuda", generator=g)[:n].to(torch.int32)
-    res = {}
-    for mode, name in ((0, "sequential"), (1, "random_read"), (2, "random_write"), (3, "random_both")):
-        for _ in range(2):
-            lsa.calibrate_access(src, dst, n, mode, ridx, widx)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            lsa.calibrate_access(src, dst, n, mode, ridx, widx)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 5
-        nbytes = n * 128 * 2 + n * 4 * ((mode & 1) + ((mode >> 1) & 1))
-        res[name] = {"ms": ms, "GB/s": nbytes / ms / 1e6}
-    print(json.dumps({"access_calibration": res, "row_bytes": 128, "copies": n,
-                      "table_bytes": rows * 128, "kernel": "lsa_calibrate_access"}))
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -465,9 +533,6 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration()
-        return
-    if args.access_calibration:
-        access_calibration()
         return
     from content_routed_block_amd import lsa
     from content_routed_block_amd.workloads import WORKLOADS, generate
@@ -506,7 +571,11 @@ def main():
         e.close()
     stage_mean = stages.mean(axis=0)
 
-    # algorithmic work per stage (bytes that must cross HBM, or MFMA FLOP)
+    # Rooflines.  Summary: HBM-bound on its bytes.  Routing: MFMA-bound, 2*D
+    # FLOP per (row, candidate block) score.  Causal attention kernels:
+    # MFMA-bound on the selected-key FLOPs they compute (4*D per query and
+    # selected key: the partials the routed keys, window + merge the window
+    # keys).  Image-mode attention: HBM-bound on Q + K + V + idx + fp32 out.
     B, Hq, Hkv, N, D, bs = w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block
     nb = N // bs
     rows = B * Hq * N
@@ -517,43 +586,64 @@ def main():
     route_bytes = B * Hq * N * D * 2 + idx_rows * w.top_k * 4 + B * Hkv * nb * D * 4
     if not w.causal:
         route_bytes += B * Hq * nb * D * 4               # pooled queries (read back)
+    # the attention's algorithmic bytes: Q, K, V, idx and the fp32 output once
+    attend_bytes = rows * D * 2 + 2 * kv_bytes + idx_rows * w.top_k * 4 + rows * D * 4
     work = {0: ("hbm", summary_bytes), 1: ("mfma", 2 * D * cand)}
+    schedule = {}
     if w.causal:
-        # partials: per routed pair the gathered Q row, the bf16 partial row,
-        # its log-mass and the pair id; per bucket one K block and one V^T block
+        work[6] = ("mfma", f_routed)
+        work[7] = ("mfma", f_window)
+        # what the key-block-major schedule itself moves: per routed pair the
+        # gathered Q row, the bf16 partial row, its log-mass and the pair id,
+        # per bucket one K block and one V^T block; the merge reads the
+        # partials back and streams Q, idx, K, V and the fp32 output
         buckets = B * Hkv * nb
-        work[6] = ("hbm", routed_pairs * (D * 2 + D * 2 + 4 + 4) + buckets * 2 * bs * D * 2)
-        # window + merge: Q, idx, the partials read back, fp32 output, K and V once
-        work[7] = ("hbm", rows * (D * 2 + w.top_k * 4 + D * 4) + routed_pairs * (D * 2 + 4)
-                   + 2 * kv_bytes)
+        schedule[6] = routed_pairs * (D * 2 + D * 2 + 4 + 4) + buckets * 2 * bs * D * 2
+        schedule[7] = (rows * (D * 2 + w.top_k * 4 + D * 4) + routed_pairs * (D * 2 + 4)
+                       + 2 * kv_bytes)
     else:
-        work[7] = ("hbm", rows * D * 2 + 2 * kv_bytes + idx_rows * w.top_k * 4 + rows * D * 4)
+        work[7] = ("hbm", attend_bytes)
     stage_frac = {}
     for i, (bound, amount) in work.items():
         t = stage_mean[i] * 1e-3
+        name = lsa.PROFILE_STAGES[i]
         if bound == "hbm":
             ach = amount / 1e9 / t
-            stage_frac[lsa.PROFILE_STAGES[i]] = {"bound": "hbm", "achieved": ach, "unit": "GB/s",
-                                                 "frac": ach / PEAK_HBM_GBS, "bytes": amount}
+            stage_frac[name] = {"bound": "hbm", "achieved": ach, "unit": "GB/s",
+                                "peak": PEAK_HBM_GBS, "frac": ach / PEAK_HBM_GBS, "bytes": amount}
         else:
             ach = amount / 1e12 / t
-            stage_frac[lsa.PROFILE_STAGES[i]] = {"bound": "mfma", "achieved": ach,
-                                                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                                                 "flop": amount,
-                                                 "hbm_frac": route_bytes / 1e9 / t / PEAK_HBM_GBS}
+            stage_frac[name] = {"bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
+                                "peak": PEAK_BF16_TFLOPS, "frac": ach / PEAK_BF16_TFLOPS,
+                                "flop": amount}
+        if i == 1:
+            stage_frac[name]["hbm_frac"] = route_bytes / 1e9 / t / PEAK_HBM_GBS
+        if i in schedule:
+            stage_frac[name]["schedule_bytes"] = schedule[i]
+            stage_frac[name]["schedule_traffic_frac"] = schedule[i] / 1e9 / t / PEAK_HBM_GBS
     dom = int(np.argmax(stage_mean))
     dom_name = lsa.PROFILE_STAGES[dom]
     d = stage_frac.get(dom_name)
-    traffic = None
-    if TRAFFIC and TRAFFIC.get("csrc") == kernel_digest() and TRAFFIC.get("stage") == dom \
-            and TRAFFIC.get("workload") == w.name:
-        traffic = TRAFFIC["bytes_per_launch"]
+    counters = traffic_counters(w)
+    traffic = counters.get(dom_name) if counters else None
     roofline = {"bound": d["bound"] if d else "hbm", "achieved": d["achieved"] if d else None,
-                "peak": (PEAK_HBM_GBS if (not d or d["bound"] == "hbm") else PEAK_BF16_TFLOPS),
+                "peak": d["peak"] if d else PEAK_HBM_GBS,
                 "unit": d["unit"] if d else "GB/s", "frac": d["frac"] if d else None,
                 "traffic": traffic, "kernel": dom_name, "kernel_ms": float(stage_mean[dom])}
+    if d and "schedule_traffic_frac" in d:
+        roofline["schedule_traffic_frac"] = d["schedule_traffic_frac"]
+    attend_stages = [lsa.PROFILE_STAGES[i] for i in range(3, 8)]
+    attend_traffic = None
+    if counters:
+        measured = sum(counters.get(n, 0.0) for n in attend_stages)
+        attend_traffic = {"counter_bytes": measured, "algorithmic_bytes": attend_bytes,
+                          "ratio": measured / attend_bytes,
+                          "note": "HBM bytes of the attention stages from FETCH_SIZE / "
+                                  "WRITE_SIZE counters over Q + K + V + idx + fp32 out"}
     breakdown = {lsa.PROFILE_STAGES[i]: round(float(stage_mean[i]), 4) for i in range(8)}
     attend_ms = float(stage_mean[3:].sum())
+    # the timed steps' own selection and output, for the parity sample
+    idx_host, out_host = idx.cpu().numpy(), out.cpu().numpy()
 
     result = {
         "metric": "sparse-attn ms/layer + selected-key TFLOP/s (%MFMA peak) at N=128K, Qwen0.5B shape",
@@ -570,6 +660,7 @@ def main():
                   "mfma_frac": f_sel / 1e12 / (ms * 1e-3) / PEAK_BF16_TFLOPS,
                   "attend_ms": attend_ms,
                   "attend_mfma_frac": f_sel / 1e12 / (attend_ms * 1e-3) / PEAK_BF16_TFLOPS,
+                  "attend_traffic": attend_traffic,
                   "routed_pairs": routed_pairs, "stage_ms": breakdown, "stage_roofline": stage_frac},
     }
     if args.consensus_steps > 0 and w.q_heads > w.kv_heads:
@@ -588,6 +679,7 @@ def main():
         result["ties"] = ties_bench(lsa, w, q, k, v, args.ties_steps)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        result["parity"] = parity_sample(w, inp, idx_host, out_host)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

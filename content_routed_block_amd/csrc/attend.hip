@@ -696,14 +696,8 @@ size_t attend_workspace_bytes(const Geometry& g) { return attend_layout(g).total
 template <int BS>
 static void launch_partial(const PartArgs& pa, hipStream_t s) {
     // one resident wave of workgroups: CUs x workgroups per CU
-    static int grid = 0;
-    if (grid == 0) {
-        int dev = 0, cus = 256, per_cu = 2;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_block_partial<BS>, 256, 0);
-        grid = cus * (per_cu > 0 ? per_cu : 1);
-    }
+    static std::atomic<int> cache[kMaxDevices];
+    const int grid = resident_grid(k_block_partial<BS>, 256, cache);
     hipLaunchKernelGGL(k_block_partial<BS>, dim3(grid), dim3(256), 0, s, pa);
 }
 

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace lsa {
 
 struct Geometry {
@@ -63,5 +65,29 @@ inline void mark(const hipEvent_t* ev, int i, hipStream_t s) {
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Grid of a persistent kernel: one resident wave of workgroups on the current
+// device (CUs x workgroups per CU at `threads` threads and no dynamic LDS).
+// Each kernel keeps one cached value per device; concurrent first calls from
+// several host threads compute the same value, so plain atomic stores suffice.
+constexpr int kMaxDevices = 64;
+template <typename Kernel>
+inline int resident_grid(Kernel kernel, int threads, std::atomic<int> (&cache)[kMaxDevices]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    std::atomic<int>* slot = dev < kMaxDevices ? &cache[dev] : nullptr;
+    int grid = slot ? slot->load(std::memory_order_relaxed) : 0;
+    if (grid > 0) return grid;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    grid = cus * per_cu;
+    if (slot) slot->store(grid, std::memory_order_relaxed);
+    return grid;
+}
 
 }  // namespace lsa

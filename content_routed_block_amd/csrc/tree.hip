@@ -267,14 +267,8 @@ hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16
 
     TreeScoreArgs sa{q, bhi, blo, pairs, offsets, unit_off, scores,
                      (uint32_t)(rows * nslots), L.nodes, L.NB, nb_pad, sp_log2};
-    static int grid = 0;
-    if (grid == 0) {
-        int dev = 0, cus = 256, per_cu = 4;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tree_score, 256, 0);
-        grid = cus * (per_cu > 0 ? per_cu : 1);
-    }
+    static std::atomic<int> cache[kMaxDevices];
+    const int grid = resident_grid(k_tree_score, 256, cache);
     hipLaunchKernelGGL(k_tree_score, dim3(grid), dim3(256), 0, s, sa);
 
     TreeSelectArgs ta{slots, rev, scores, idx, rows, g.N, g.bs, g.window, g.top_k, g.beam};

@@ -55,9 +55,6 @@ _lib.lsa_decode.argtypes = [_P, ctypes.c_int32, _v, _v, _v, _v, _v, _v, _v, ctyp
 _lib.lsa_decode.restype = ctypes.c_int
 _lib.lsa_forward_profiled.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v, _v]
 _lib.lsa_forward_profiled.restype = ctypes.c_int
-_lib.lsa_calibrate_access.argtypes = [_v, _v, _v, _v, ctypes.c_int64, ctypes.c_int64,
-                                      ctypes.c_int32, _v]
-_lib.lsa_calibrate_access.restype = ctypes.c_int
 _lib.lsa_status_str.argtypes = [ctypes.c_int]
 _lib.lsa_status_str.restype = ctypes.c_char_p
 
@@ -141,6 +138,16 @@ def _check(code: int, what: str):
         raise LsaError(code, what)
 
 
+def _on(stream):
+    """The torch stream a call runs on: `stream`, or the current stream.
+
+    Every buffer a call allocates for itself (workspace, and out / idx when
+    the caller passes none) is allocated while that stream is current, so
+    torch's caching allocator ties it to the stream the kernels run on: once
+    freed it is handed out again only to work ordered after those kernels."""
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _workspace(p, op, workspace, device):
     need = workspace_bytes(p, op)
     if workspace is None and need:
@@ -154,9 +161,12 @@ def block_summarize(p: LsaParams, x: torch.Tensor, heads: Optional[int] = None,
     heads = p.kv_heads if heads is None else heads
     x = _bits(x, (p.batch, heads, p.seq_len, p.head_dim), "x")
     nb = p.seq_len // p.block
+    s = _on(stream)
     if out is None:
-        out = torch.empty((p.batch, heads, nb, p.head_dim), dtype=torch.float32, device=x.device)
-    _check(_lib.lsa_block_summarize(ctypes.byref(p), _ptr(x), heads, _ptr(out), _stream(stream)),
+        with torch.cuda.stream(s):
+            out = torch.empty((p.batch, heads, nb, p.head_dim), dtype=torch.float32,
+                              device=x.device)
+    _check(_lib.lsa_block_summarize(ctypes.byref(p), _ptr(x), heads, _ptr(out), _stream(s)),
            "lsa_block_summarize")
     return out
 
@@ -166,12 +176,14 @@ def route_topk(p: LsaParams, q: torch.Tensor, kbar: torch.Tensor,
                stream=None) -> torch.Tensor:
     q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
     _tensor(kbar, torch.float32, (p.batch, p.kv_heads, p.seq_len // p.block, p.head_dim), "kbar")
-    if idx is None:
-        idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        if idx is None:
+            idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
+        workspace, nbytes = _workspace(p, OP_ROUTE, workspace, q.device)
     _tensor(idx, torch.int32, idx_shape(p), "idx")
-    workspace, nbytes = _workspace(p, OP_ROUTE, workspace, q.device)
     _check(_lib.lsa_route_topk(ctypes.byref(p), _ptr(q), _ptr(kbar), _ptr(idx), _ptr(workspace),
-                               nbytes, _stream(stream)), "lsa_route_topk")
+                               nbytes, _stream(s)), "lsa_route_topk")
     return idx
 
 
@@ -181,10 +193,12 @@ def route_cumulant(p: LsaParams, q: torch.Tensor, k: torch.Tensor,
     lsa_route_cumulant)."""
     q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
     k = _bits(k, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "k")
+    s = _on(stream)
     if idx is None:
-        idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
+        with torch.cuda.stream(s):
+            idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
     _tensor(idx, torch.int32, idx_shape(p), "idx")
-    _check(_lib.lsa_route_cumulant(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(idx), _stream(stream)),
+    _check(_lib.lsa_route_cumulant(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(idx), _stream(s)),
            "lsa_route_cumulant")
     return idx
 
@@ -196,13 +210,15 @@ def sparse_attend(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     k = _bits(k, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "k")
     v = _bits(v, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "v")
     _tensor(idx, torch.int32, idx_shape(p), "idx")
-    if out is None:
-        out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
-                          device=q.device)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
+                              device=q.device)
+        workspace, nbytes = _workspace(p, OP_ATTEND, workspace, q.device)
     _tensor(out, torch.float32, (p.batch, p.q_heads, p.seq_len, p.head_dim), "out")
-    workspace, nbytes = _workspace(p, OP_ATTEND, workspace, q.device)
     _check(_lib.lsa_sparse_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
-                                  _ptr(workspace), nbytes, _stream(stream)), "lsa_sparse_attend")
+                                  _ptr(workspace), nbytes, _stream(s)), "lsa_sparse_attend")
     return out
 
 
@@ -213,18 +229,27 @@ def forward(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     q = _bits(q, (p.batch, p.q_heads, p.seq_len, p.head_dim), "q")
     k = _bits(k, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "k")
     v = _bits(v, (p.batch, p.kv_heads, p.seq_len, p.head_dim), "v")
-    if out is None:
-        out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
-                          device=q.device)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty((p.batch, p.q_heads, p.seq_len, p.head_dim), dtype=torch.float32,
+                              device=q.device)
+        if idx is None and want_idx:
+            idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
+        workspace, nbytes = _workspace(p, OP_FORWARD, workspace, q.device)
     _tensor(out, torch.float32, (p.batch, p.q_heads, p.seq_len, p.head_dim), "out")
-    if idx is None and want_idx:
-        idx = torch.empty(idx_shape(p), dtype=torch.int32, device=q.device)
     if idx is not None:
         _tensor(idx, torch.int32, idx_shape(p), "idx")
-    workspace, nbytes = _workspace(p, OP_FORWARD, workspace, q.device)
     _check(_lib.lsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx),
-                            _ptr(workspace), nbytes, _stream(stream)), "lsa_forward")
+                            _ptr(workspace), nbytes, _stream(s)), "lsa_forward")
     return out, idx
+
+
+def _cache_params(p: LsaParams, cache_len: int) -> LsaParams:
+    """p with seq_len = cache_len (the geometry decode workspaces are sized by)."""
+    pc = LsaParams(*[getattr(p, f) for f, _ in LsaParams._fields_])
+    pc.seq_len = cache_len
+    return pc
 
 
 def decode(p: LsaParams, cache_len: int, q: torch.Tensor, k_cache: torch.Tensor,
@@ -244,18 +269,20 @@ def decode(p: LsaParams, cache_len: int, q: torch.Tensor, k_cache: torch.Tensor,
             tuple(kbar_cache.shape) != (p.batch, p.kv_heads, cache_len // p.block, p.head_dim):
         raise ValueError("kbar_cache: expected a contiguous fp32 tensor "
                          f"[{p.batch}, {p.kv_heads}, {cache_len // p.block}, {p.head_dim}]")
-    if out is None:
-        out = torch.empty((p.batch, p.q_heads, p.head_dim), dtype=torch.float32, device=q.device)
-    if idx is None and want_idx:
-        idx = torch.empty((p.batch, p.q_heads, p.top_k), dtype=torch.int32, device=q.device)
-    if workspace is None:
-        pc = LsaParams(*[getattr(p, f) for f, _ in LsaParams._fields_])
-        pc.seq_len = cache_len
-        workspace = torch.empty(workspace_bytes(pc, OP_DECODE), dtype=torch.uint8, device=q.device)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty((p.batch, p.q_heads, p.head_dim), dtype=torch.float32,
+                              device=q.device)
+        if idx is None and want_idx:
+            idx = torch.empty((p.batch, p.q_heads, p.top_k), dtype=torch.int32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(workspace_bytes(_cache_params(p, cache_len), OP_DECODE),
+                                    dtype=torch.uint8, device=q.device)
     nbytes = workspace.numel() * workspace.element_size()
     _check(_lib.lsa_decode(ctypes.byref(p), cache_len, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                            _ptr(kbar_cache), _ptr(out), _ptr(idx), _ptr(workspace), nbytes,
-                           _stream(stream)), "lsa_decode")
+                           _stream(s)), "lsa_decode")
     return out, idx
 
 
@@ -296,19 +323,3 @@ def forward_profiled(p: LsaParams, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                                      _ptr(idx), _ptr(workspace), nbytes, _stream(stream),
                                      events.array), "lsa_forward_profiled")
 
-
-def calibrate_access(src: torch.Tensor, dst: torch.Tensor, n: int, mode: int,
-                     ridx: Optional[torch.Tensor] = None, widx: Optional[torch.Tensor] = None,
-                     stream=None) -> None:
-    """lsa_calibrate_access: n copies of 128-byte rows between two tables of
-    the same row count (modes: 0 sequential, 1 random read, 2 random write,
-    3 both; ridx/widx int32 row numbers on the device)."""
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() != nbytes or nbytes % 128:
-        raise ValueError("src and dst must be tables of the same number of 128-byte rows")
-    for t, used, what in ((ridx, mode & 1, "ridx"), (widx, mode & 2, "widx")):
-        if used and (t is None or t.dtype != torch.int32 or t.numel() < n or not t.is_cuda):
-            raise ValueError(f"{what}: int32 device tensor of at least n entries required")
-    _check(_lib.lsa_calibrate_access(_ptr(src), _ptr(dst), _ptr(ridx) if mode & 1 else None,
-                                     _ptr(widx) if mode & 2 else None, nbytes // 128, n, mode,
-                                     _stream(stream)), "lsa_calibrate_access")

@@ -31,7 +31,13 @@
  *     synchronisation.
  *   - Inputs are not checked for finiteness: NaN or Inf give an unspecified
  *     result but every access stays in bounds.
- *   - Determinism: the same inputs give bitwise identical outputs.
+ *   - Determinism: the same inputs give bitwise identical outputs.  A row
+ *     whose k-th and (k+1)-th routing scores agree to within fp32 rounding
+ *     may keep either block; which one can depend on the rest of the input
+ *     (rows that overflow the router's fast path are rescored by an exact
+ *     pass, one by one with fp32 FMA chains when few rows need it, by whole
+ *     tiles with the fast path's bf16 hi+lo products when many do), but never
+ *     on the stream, the run or the calling thread.
  *   - Calls on distinct streams with distinct workspaces may run
  *     concurrently.
  */

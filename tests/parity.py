@@ -63,6 +63,31 @@ def check_routing(idx_gpu, idx_orc, gap, scores, ncand, k):
     return bad_clear, int(np.sum(~clear)), len(near_rows)
 
 
+def check_needles(sel_gpu, sel_orc, gap, scores, ncand, needle_blocks, k):
+    """Needle rows.  Mean-pooled block summaries can lose an isolated key (SSA
+    page, "The retrieval law"), so a needle's selection is measured, not
+    assumed, and the GPU must agree with the oracle row by row: the needle's
+    block is in the GPU set exactly when it is in the oracle's.  Where the two
+    differ the row must be a near tie (gap <= GAP) and the needle block's
+    oracle score must lie within GAP of the row's k-th best score, so that
+    either choice is a valid top-k.  sel_*: [R, k] sets of the needle rows;
+    gap: [R]; scores: [R, nb] oracle scores; ncand: [R]; needle_blocks: [R].
+    Returns (recall_gpu, recall_oracle, n_differing)."""
+    hits_g = hits_o = differing = 0
+    for r in range(len(needle_blocks)):
+        c = int(needle_blocks[r])
+        hg, ho = c in sel_gpu[r], c in sel_orc[r]
+        hits_g += int(hg)
+        hits_o += int(ho)
+        if hg != ho:
+            differing += 1
+            assert gap[r] <= GAP, (r, c, gap[r])
+            s = np.asarray(scores[r][:int(ncand[r])], np.float64)
+            kth = np.sort(s)[::-1][min(k, s.size) - 1]
+            assert abs(s[c] - kth) <= GAP, (r, c, s[c], kth)
+    return hits_g, hits_o, differing
+
+
 def check_output(out_gpu, out_ref, vmax_row):
     """out_*: [R, D] float; vmax_row: [R] max |v| over the row's keys (or a
     global bound).  Returns (max_abs, mean_abs)."""

@@ -33,8 +33,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(LIB)
     names = declared_functions()
     assert set(names) >= {"lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend",
-                          "lsa_forward", "lsa_workspace_bytes", "lsa_status_str",
-                          "lsa_calibrate_access"}
+                          "lsa_forward", "lsa_workspace_bytes", "lsa_status_str"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -172,28 +171,3 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
-
-
-@pytest.mark.parametrize("args,code", [
-    # (src, dst, ridx, widx, table_rows, n, mode)
-    ((0, 256, 512, 768, 100, 10, 3), 1),        # src NULL
-    ((256, 0, 512, 768, 100, 10, 0), 1),        # dst NULL
-    ((256, 512, 0, 768, 100, 10, 1), 1),        # ridx NULL, read side random
-    ((256, 512, 768, 0, 100, 10, 2), 1),        # widx NULL, write side random
-    ((256, 512, 0, 0, 100, 10, 4), 2),          # mode out of range
-    ((256, 512, 0, 0, 100, -1, 0), 2),          # negative n
-    ((256, 512, 0, 0, -1, 0, 0), 2),            # negative table
-    ((256, 512, 768, 0, 100, 101, 1), 2),       # sequential write side past the table
-    ((256, 512, 768, 1024, 100, 1 << 28, 3), 2),  # n too large
-    ((264, 512, 0, 0, 100, 10, 0), 4),          # src misaligned
-    ((256, 520, 0, 0, 100, 10, 0), 4),          # dst misaligned
-    ((256, 512, 0, 0, 100, 0, 0), 0),           # nothing to do: returns before any launch
-])
-def test_calibrate_access_argument_checks(args, code):
-    lib = ctypes.CDLL(LIB)
-    f = lib.lsa_calibrate_access
-    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
-                                         ctypes.c_void_p]
-    f.restype = ctypes.c_int
-    ptrs = [ctypes.c_void_p(a) if a else None for a in args[:4]]
-    assert f(*ptrs, args[4], args[5], args[6], None) == code

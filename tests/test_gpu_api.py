@@ -70,6 +70,35 @@ def test_forward_on_a_side_stream_equals_default_stream(lsa):
     assert torch.equal(i1, i2) and torch.equal(o1, o2)
 
 
+def test_side_stream_call_from_the_default_stream_keeps_its_buffers(lsa):
+    """forward(stream=side) called while the default stream is current: the
+    buffers the binding allocates for the call (workspace, out, idx) belong to
+    the side stream, so allocations and writes on the default stream made
+    before the side stream finishes cannot reuse them mid-flight."""
+    w = causal_w(seed=67)
+    inp = generate(w)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    p = params_of(lsa, w)
+    ref_o, ref_i = lsa.forward(p, q, k, v)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    need = lsa.workspace_bytes(p, lsa.OP_FORWARD)
+    results = []
+    for _ in range(3):
+        results.append(lsa.forward(p, q, k, v, stream=side))   # default stream stays current
+        # the call's own workspace is freed on return; allocations of the same
+        # size on the default stream, written at once, must not land on it
+        junk = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        for j in junk:
+            j.fill_(0xA5)
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for o, i in results:
+        assert torch.equal(o, ref_o) and torch.equal(i, ref_i)
+
+
 def test_workspace_exact_size_and_one_byte_short(lsa):
     w = causal_w()
     inp = generate(w)

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from content_routed_block_amd.workloads import WORKLOADS, Workload, bf16_bits_to_f32, generate
-from tests.parity import check_output, check_routing, causal_candidates, dev, params_of
+from tests.parity import (check_needles, check_output, check_routing, causal_candidates, dev,
+                          params_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -154,15 +155,20 @@ def check_consensus_sampled_rows(lsa, w):
     kbar_o = oracle.block_means(inp.k, w.block)
     rng = np.random.default_rng(321)
     R, per = group_rows_of(w)
-    grows = np.sort(rng.choice(R, size=min(R, 3000), replace=False))
+    grows = rng.choice(R, size=min(R, 3000), replace=False)
+    needle_rows = np.array([(n.b * w.kv_heads + n.h // (w.q_heads // w.kv_heads)) * w.seq_len + n.t
+                            for n in inp.needles], dtype=np.int64)
+    grows = np.unique(np.concatenate([grows, needle_rows]))   # every needle's group row too
     io, gap, sc, ncand = oracle_consensus(w, inp, kbar_o, grows)
     bad, near, near_diff = check_routing(gidx[grows], io, gap, sc, ncand, w.top_k)
     say("  group rows", grows.size, "near", near, "near-differing", near_diff, "clear mismatches", bad)
     assert bad == 0
     if inp.needles:
-        hits = sum(int(n.p // w.block in gidx[(n.b * w.kv_heads + n.h // (w.q_heads // w.kv_heads))
-                                                * w.seq_len + n.t]) for n in inp.needles)
-        say("  needle blocks in the group route", hits, "of", len(inp.needles))
+        j = np.searchsorted(grows, needle_rows)
+        hits_g, hits_o, ndiff = check_needles(gidx[grows][j], io[j], gap[j], sc[j], ncand[j],
+                                              [n.p // w.block for n in inp.needles], w.top_k)
+        say("  needle blocks in the group route: gpu", hits_g, "oracle", hits_o, "of",
+            len(inp.needles), "differing (near ties)", ndiff)
     # query rows: every head of a sample of group rows
     rep = w.q_heads // w.kv_heads
     bg, pos = grows // per, grows % per

@@ -12,7 +12,8 @@ import torch
 import oracle
 from content_routed_block_amd.workloads import WORKLOADS, Workload, bf16_bits_to_f32, generate, to_bf16_bits
 from tests import brute
-from tests.parity import (check_output, check_routing, causal_candidates, dev, params_of)
+from tests.parity import (check_needles, check_output, check_routing, causal_candidates, dev,
+                          params_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -285,13 +286,12 @@ def check_sampled_rows(lsa, w, nrows=6000):
         out_rows = rows
         sel = ig
         if inp.needles:
-            hit_g = hit_o = 0
-            for n in inp.needles:
-                r = (n.b * w.q_heads + n.h) * w.seq_len + n.t
-                j = int(np.searchsorted(rows, r))
-                hit_g += int(n.p // w.block in idx.reshape(-1, w.top_k)[r])
-                hit_o += int(n.p // w.block in io[j])
-            say("  needle recall gpu", hit_g, "oracle", hit_o, "of", len(inp.needles))
+            j = np.searchsorted(rows, [(n.b * w.q_heads + n.h) * w.seq_len + n.t
+                                       for n in inp.needles])
+            hit_g, hit_o, ndiff = check_needles(ig[j], io[j], gap[j], scores[j], ncand[j],
+                                                [n.p // w.block for n in inp.needles], w.top_k)
+            say("  needle recall gpu", hit_g, "oracle", hit_o, "of", len(inp.needles),
+                "differing (near ties)", ndiff)
     else:
         nb = w.seq_len // w.block
         qbar = oracle.block_means(inp.q, w.block)

@@ -10,8 +10,8 @@ import torch
 
 import oracle
 from content_routed_block_amd.workloads import WORKLOADS, Workload, bf16_bits_to_f32, generate
-from tests.parity import (check_output, check_routing, check_tree_routing, causal_candidates, dev,
-                          params_of)
+from tests.parity import (GAP, check_output, check_routing, check_tree_routing, causal_candidates,
+                          dev, params_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,12 +51,14 @@ def vmax_of(w, inp, rows):
     return per_head[rows // w.seq_len]
 
 
-def check_rows(w, inp, beam, gi, rows):
+def check_rows(w, inp, beam, gi, rows, oracle_out=None):
     kbar_o = oracle.block_means(inp.k, w.block)
     io, det = oracle.route_tree(kbar_o, w.block, w.top_k, beam, q=inp.q, window=w.window,
                                 rows=rows, details=True)
     bsc = oracle.route_scores(kbar_o, rows, q=inp.q, block=w.block, window=w.window, causal=1)
     ncand = causal_candidates(rows % w.seq_len, w.block, w.window)
+    if oracle_out is not None:
+        oracle_out.update(idx=io, det=det)
     return check_tree_routing(gi, io, det, bsc, ncand, w.top_k, beam)
 
 
@@ -127,14 +129,29 @@ def check_tree_sampled_rows(lsa, w, beam):
     torch.cuda.synchronize()
     gi_all = idx.cpu().numpy().reshape(-1, w.top_k)
     R = w.batch * w.q_heads * w.seq_len
-    rows = np.sort(np.random.default_rng(5).choice(R, 3000, False))
-    bad, near, near_diff = check_rows(w, inp, beam, gi_all[rows], rows)
+    rows = np.random.default_rng(5).choice(R, 3000, False)
+    needle_rows = np.array([(n.b * w.q_heads + n.h) * w.seq_len + n.t for n in inp.needles],
+                           dtype=np.int64)
+    rows = np.unique(np.concatenate([rows, needle_rows]))   # every needle row is checked too
+    orc = {}
+    bad, near, near_diff = check_rows(w, inp, beam, gi_all[rows], rows, orc)
     say("  rows", rows.size, "near", near, "near-differing", near_diff, "clear mismatches", bad)
     assert bad == 0
     if inp.needles:
-        hits = sum(int(n.p // w.block in gi_all[(n.b * w.q_heads + n.h) * w.seq_len + n.t])
-                   for n in inp.needles)
-        say("  needle blocks selected", hits, "of", len(inp.needles))
+        # the needle's block is selected on the GPU exactly when the oracle
+        # selects it, unless the row is near a tie at some level (then
+        # check_tree_routing above has shown the GPU's set to be valid)
+        j = np.searchsorted(rows, needle_rows)
+        hits_g = hits_o = ndiff = 0
+        for jj, n in zip(j, inp.needles):
+            hg = n.p // w.block in gi_all[rows[jj]]
+            ho = n.p // w.block in orc["idx"][jj]
+            hits_g, hits_o = hits_g + int(hg), hits_o + int(ho)
+            if hg != ho:
+                ndiff += 1
+                assert orc["det"]["gap1"][jj] <= GAP or orc["det"]["gap2"][jj] <= GAP, (n, jj)
+        say("  needle recall gpu", hits_g, "oracle", hits_o, "of", len(inp.needles),
+            "differing (near ties)", ndiff)
     ref = oracle.attend(inp.q, inp.k, inp.v, gi_all[rows], w.block, w.top_k, w.window, 1, rows=rows)
     mx, mean = check_output(out.cpu().numpy().reshape(-1, 64)[rows], ref, vmax_of(w, inp, rows))
     say("  max-abs", mx, "mean-abs", mean)
