@@ -29,11 +29,19 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "lsa_common.hpp"
 #include "lsa_launch.hpp"
 
 namespace lsa {
+
+// Scratch of the allocation-free decode entry point (lsa_decode_noalloc): a
+// file-scope device array, so every GPU the library runs on holds its own
+// copy from the moment the library's code is loaded there until the process
+// ends.  Host code must not use its name as an address (in host code the name
+// is a host-side stand-in); static_scratch() looks the device address up.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 constexpr int DC_SPLIT = 256;   // keys per attention workgroup
 constexpr int kMaxBlock = 128;  // largest key block (bs)
@@ -397,6 +405,27 @@ static DecodeLayout decode_layout(const Geometry& g, int t_max) {
 }
 
 size_t decode_workspace_bytes(const Geometry& g, int t_max) { return decode_layout(g, t_max).total; }
+
+hipError_t static_scratch(void** ptr) {
+    // one lookup per device, with that device current; the address is kept
+    // for every later call on the device
+    static std::mutex mu;
+    static void* addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, float* kbar, float* out, int32_t* idx_out, void* ws,

@@ -227,23 +227,33 @@ lsa_status lsa_forward_profiled(const lsa_params* p, const void* q, const void* 
                         reinterpret_cast<const hipEvent_t*>(events));
 }
 
-lsa_status lsa_decode(const lsa_params* p, int32_t cache_len, const void* q, const void* k_cache,
-                      const void* v_cache, float* kbar_cache, float* out, int32_t* idx_out,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+// Validation shared by the two decode entry points; fills g (g.N = T).
+static lsa_status decode_check(const lsa_params* p, int32_t cache_len, const void* q,
+                               const void* k_cache, const void* v_cache, const float* kbar_cache,
+                               const float* out, const int32_t* idx_out, Geometry* g) {
     if (!p) return LSA_ERR_NULL;
     // the cache geometry is validated as a sequence of cache_len tokens
     lsa_params pc = *p;
     pc.seq_len = cache_len;
-    Geometry g;
-    lsa_status st = check_params(&pc, &g);
+    lsa_status st = check_params(&pc, g);
     if (st != LSA_OK) return st;
     if (!p->causal) return LSA_ERR_SHAPE;
     if (p->consensus || p->beta != 0.f || p->beam) return LSA_ERR_UNSUPPORTED;
     if (p->seq_len < 1 || p->seq_len > cache_len) return LSA_ERR_SHAPE;
-    if (!q || !k_cache || !v_cache || !kbar_cache || !out || !workspace) return LSA_ERR_NULL;
+    if (!q || !k_cache || !v_cache || !kbar_cache || !out) return LSA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(kbar_cache, 16) || !aligned(out, 16) || (idx_out && !aligned(idx_out, 16)))
         return LSA_ERR_ALIGN;
+    return LSA_OK;
+}
+
+lsa_status lsa_decode(const lsa_params* p, int32_t cache_len, const void* q, const void* k_cache,
+                      const void* v_cache, float* kbar_cache, float* out, int32_t* idx_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    Geometry g;
+    lsa_status st = decode_check(p, cache_len, q, k_cache, v_cache, kbar_cache, out, idx_out, &g);
+    if (st != LSA_OK) return st;
+    if (!workspace) return LSA_ERR_NULL;
     if (!aligned(workspace, 256)) return LSA_ERR_ALIGN;
     if (workspace_bytes < lsa::decode_workspace_bytes(g, cache_len)) return LSA_ERR_WORKSPACE;
     g.N = p->seq_len;
@@ -251,6 +261,25 @@ lsa_status lsa_decode(const lsa_params* p, int32_t cache_len, const void* q, con
                                        static_cast<const uint16_t*>(k_cache),
                                        static_cast<const uint16_t*>(v_cache), kbar_cache, out,
                                        idx_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+lsa_status lsa_decode_noalloc(const lsa_params* p, int32_t cache_len, const void* q,
+                              const void* k_cache, const void* v_cache, float* kbar_cache,
+                              float* out, int32_t* idx_out, void* stream) {
+    Geometry g;
+    lsa_status st = decode_check(p, cache_len, q, k_cache, v_cache, kbar_cache, out, idx_out, &g);
+    if (st != LSA_OK) return st;
+    // the same workspace layout as lsa_decode, placed in the static array
+    static_assert(lsa::kStaticScratchBytes == LSA_STATIC_SCRATCH_BYTES, "header and library");
+    if (lsa::decode_workspace_bytes(g, cache_len) > lsa::kStaticScratchBytes)
+        return LSA_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (lsa::static_scratch(&scratch) != hipSuccess) return LSA_ERR_DEVICE;
+    g.N = p->seq_len;
+    return from_hip(lsa::launch_decode(g, cache_len, static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k_cache),
+                                       static_cast<const uint16_t*>(v_cache), kbar_cache, out,
+                                       idx_out, scratch, static_cast<hipStream_t>(stream)));
 }
 
 const char* lsa_status_str(lsa_status s) {
@@ -262,6 +291,7 @@ const char* lsa_status_str(lsa_status s) {
         case LSA_ERR_ALIGN: return "misaligned pointer";
         case LSA_ERR_WORKSPACE: return "workspace too small";
         case LSA_ERR_DEVICE: return "HIP launch failed";
+        case LSA_ERR_SCRATCH: return "needs more scratch than the library's static array holds";
         default: return "unknown status";
     }
 }

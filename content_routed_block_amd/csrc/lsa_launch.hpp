@@ -55,6 +55,10 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
 
 // Single-query decode against a cache of t_max tokens (g.N = tokens filled).
 size_t decode_workspace_bytes(const Geometry& g, int t_max);
+// The library's static scratch array on the current device (see decode.hip):
+// its size, and its device address (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, float* kbar, float* out, int32_t* idx_out, void* ws,
                          hipStream_t s);

@@ -26,7 +26,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 OP_SUMMARIZE, OP_ROUTE, OP_ATTEND, OP_FORWARD, OP_DECODE = 0, 1, 2, 3, 4
 STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL", 2: "LSA_ERR_SHAPE", 3: "LSA_ERR_UNSUPPORTED",
-          4: "LSA_ERR_ALIGN", 5: "LSA_ERR_WORKSPACE", 6: "LSA_ERR_DEVICE"}
+          4: "LSA_ERR_ALIGN", 5: "LSA_ERR_WORKSPACE", 6: "LSA_ERR_DEVICE", 7: "LSA_ERR_SCRATCH"}
+STATIC_SCRATCH_BYTES = 16 << 20   # LSA_STATIC_SCRATCH_BYTES
 
 
 class LsaParams(ctypes.Structure):
@@ -53,6 +54,8 @@ for _f in ("lsa_block_summarize", "lsa_route_topk", "lsa_sparse_attend", "lsa_fo
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.lsa_decode.argtypes = [_P, ctypes.c_int32, _v, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v]
 _lib.lsa_decode.restype = ctypes.c_int
+_lib.lsa_decode_noalloc.argtypes = [_P, ctypes.c_int32, _v, _v, _v, _v, _v, _v, _v]
+_lib.lsa_decode_noalloc.restype = ctypes.c_int
 _lib.lsa_forward_profiled.argtypes = [_P, _v, _v, _v, _v, _v, _v, ctypes.c_size_t, _v, _v]
 _lib.lsa_forward_profiled.restype = ctypes.c_int
 _lib.lsa_status_str.argtypes = [ctypes.c_int]
@@ -284,6 +287,25 @@ def decode(p: LsaParams, cache_len: int, q: torch.Tensor, k_cache: torch.Tensor,
                            _ptr(kbar_cache), _ptr(out), _ptr(idx), _ptr(workspace), nbytes,
                            _stream(s)), "lsa_decode")
     return out, idx
+
+
+def decode_noalloc(p: LsaParams, cache_len: int, q: torch.Tensor, k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, kbar_cache: torch.Tensor, out: torch.Tensor,
+                   idx: Optional[torch.Tensor] = None, stream=None) -> None:
+    """lsa_decode_noalloc: one decode step with the library's static scratch
+    array instead of a workspace.  Allocates nothing: out (and idx, if wanted)
+    must be preallocated.  Calls that overlap on one GPU race."""
+    q = _bits(q, (p.batch, p.q_heads, p.head_dim), "q")
+    k_cache = _bits(k_cache, (p.batch, p.kv_heads, cache_len, p.head_dim), "k_cache")
+    v_cache = _bits(v_cache, (p.batch, p.kv_heads, cache_len, p.head_dim), "v_cache")
+    _tensor(kbar_cache, torch.float32, (p.batch, p.kv_heads, cache_len // p.block, p.head_dim),
+            "kbar_cache")
+    _tensor(out, torch.float32, (p.batch, p.q_heads, p.head_dim), "out")
+    if idx is not None:
+        _tensor(idx, torch.int32, (p.batch, p.q_heads, p.top_k), "idx")
+    _check(_lib.lsa_decode_noalloc(ctypes.byref(p), cache_len, _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(kbar_cache), _ptr(out), _ptr(idx),
+                                   _stream(_on(stream))), "lsa_decode_noalloc")
 
 
 class StageEvents:

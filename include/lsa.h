@@ -80,7 +80,9 @@ typedef enum lsa_status {
                                 B*Hq*N*2^ceil(log2 top_k) >= 2^32, ...) */
     LSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned (workspace: 256) */
     LSA_ERR_WORKSPACE = 5,   /* workspace smaller than lsa_workspace_bytes() */
-    LSA_ERR_DEVICE = 6       /* a HIP launch failed */
+    LSA_ERR_DEVICE = 6,      /* a HIP launch failed */
+    LSA_ERR_SCRATCH = 7      /* needs more scratch than the static array holds
+                                (lsa_decode_noalloc) */
 } lsa_status;
 
 enum {
@@ -208,6 +210,24 @@ lsa_status lsa_decode(const lsa_params *p, int32_t cache_len, const void *q,
                       const void *k_cache, const void *v_cache, float *kbar_cache,
                       float *out, int32_t *idx_out, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* lsa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, layouts, results and errors are those of lsa_decode, without
+ * the workspace: its scratch (the same layout, lsa_workspace_bytes(p with
+ * seq_len = cache_len, LSA_OP_DECODE) bytes) lives in a static device array of
+ * LSA_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  A geometry that needs more returns
+ * LSA_ERR_SCRATCH before anything is enqueued.  The call allocates and frees
+ * nothing; the first call on a device looks the array's address up once.
+ * The array keeps the last call's contents and everything that must start at
+ * zero is cleared by the call's own kernels, but it is shared by every call
+ * on that GPU: calls that overlap on one GPU (concurrent streams or host
+ * threads) race and must be serialised by the caller. */
+#define LSA_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+lsa_status lsa_decode_noalloc(const lsa_params *p, int32_t cache_len, const void *q,
+                              const void *k_cache, const void *v_cache, float *kbar_cache,
+                              float *out, int32_t *idx_out, void *stream);
 
 /* lsa_forward with stage timing, for profiling tools.  `events` holds
  * LSA_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is

@@ -171,3 +171,20 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_noalloc_decode_argument_checks(lsa):
+    """lsa_decode_noalloc validates like lsa_decode and refuses, before
+    anything runs, a geometry whose scratch exceeds the static array."""
+    L = lsa.library()
+    a = ctypes.c_void_p(256)
+    ok = good(lsa, seq_len=4096)
+    assert L.lsa_decode_noalloc(None, 4096, a, a, a, a, a, None, None) == 1
+    assert L.lsa_decode_noalloc(ctypes.byref(ok), 4096, None, a, a, a, a, None, None) == 1
+    assert L.lsa_decode_noalloc(ctypes.byref(ok), 4096, ctypes.c_void_p(264), a, a, a, a, None,
+                                None) == 4
+    assert L.lsa_decode_noalloc(ctypes.byref(ok), 2048, a, a, a, a, a, None, None) == 2  # T > cache
+    big = lsa.params(1, 64, 8, 1 << 20, 64, 64, 16, 1 << 19, 1)   # a 512K-token window
+    assert L.lsa_workspace_bytes(ctypes.byref(big), lsa.OP_DECODE) > lsa.STATIC_SCRATCH_BYTES
+    assert L.lsa_decode_noalloc(ctypes.byref(big), 1 << 20, a, a, a, a, a, None, None) == 7
+    assert L.lsa_status_str(7).decode().startswith("needs more scratch")
