@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen05b_n128k_needles")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="query positions per attention chunk (0: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -546,7 +548,7 @@ def main():
 
     q, k, v = up(inp.q), up(inp.k), up(inp.v)
     p = lsa.params(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.top_k,
-                   w.window, w.causal)
+                   w.window, w.causal, chunk=args.chunk)
     out = torch.empty((w.batch, w.q_heads, w.seq_len, w.head_dim), dtype=torch.float32, device=dev)
     rows = w.seq_len if w.causal else w.seq_len // w.block
     idx = torch.empty((w.batch, w.q_heads, rows, w.top_k), dtype=torch.int32, device=dev)

@@ -201,14 +201,17 @@ struct PartArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* vt;        // V^T tiles [BG][ntiles][64 d][64 keys]
-    const uint32_t* pairs;
+    const uint32_t* pairs;     // chunk-local pair ids, in bucket order
     const uint32_t* offsets;   // [NB+1]
     const uint32_t* unit_off;  // [NB+1]
-    uint16_t* part_o;          // bf16 bits [rows * SP + 64][64] by pair id, permuted (see k_block_partial)
-    float* part_lse;           // [rows * top_k + 64] by pair position, log2 domain
-    uint32_t dummy_pid;        // rows * SP: first of 64 rows written by lanes without a pair
-    uint32_t dummy_pos;        // rows * top_k: first of 64 log-mass slots for the same lanes
+    uint16_t* part_o;          // bf16 bits [crows * SP + 64][64] by chunk-local pair id,
+                               // permuted (see k_block_partial)
+    float* part_lse;           // [crows * top_k + 64] by pair position in the chunk, log2 domain
+    uint32_t dummy_pid;        // crows * SP: first of 64 rows written by lanes without a pair
+    uint32_t dummy_pos;        // crows * top_k: first of 64 log-mass slots for the same lanes
     int N, nb, NB, ntiles, sp_log2;
+    int b0, b1;                // this launch's buckets [b0, b1): one position chunk
+    int pc_log2, t_base;       // positions per chunk (log2); the chunk's first position
     float scale_log2;
 };
 
@@ -225,28 +228,35 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[kD * VP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t U = uniform_load(a.unit_off + a.NB);
-    const uint32_t per = (U + gridDim.x - 1) / gridDim.x;
-    const uint32_t u0 = blockIdx.x * per;
-    const uint32_t u1 = min(U, u0 + per);
+    // this chunk's units [ulo, uhi) and the position of its first pair
+    const uint32_t ulo = uniform_load(a.unit_off + a.b0), uhi = uniform_load(a.unit_off + a.b1);
+    const uint32_t pos_base = uniform_load(a.offsets + a.b0);
+    const uint32_t per = (uhi - ulo + gridDim.x - 1) / gridDim.x;
+    const uint32_t u0 = ulo + blockIdx.x * per;
+    const uint32_t u1 = min(uhi, u0 + per);
     if (u0 >= u1) return;
     UnitCursor cur, ahead;
     cur.seek(a.unit_off, a.NB, u0);
     ahead = cur;
     const uint32_t my = 16 * w + (lane & 15);  // this lane's row slot in a unit
     // Every vector memory operation below is issued unconditionally (lanes
-    // without a row read pair 0 and write a dummy row), so the wait for a
-    // prefetched operand never has to drain the stores issued after it.
+    // without a row read the chunk's first pair, whose row lies in this
+    // chunk, and write a dummy row), so the wait for a prefetched operand
+    // never has to drain the stores issued after it.
     const uint32_t dummy = a.dummy_pid + my;
     const uint32_t dummy_pos = a.dummy_pos + my;
     auto fetch_pid = [&](uint32_t u, uint32_t& pid, bool& v) {
         uint32_t q0 = 0, q1 = 0;
         if (u < u1) ahead.rows(a.unit_off, a.offsets, u, q0, q1);
         v = q0 + my < q1;
-        pid = a.pairs[v ? q0 + my : 0u];
+        pid = a.pairs[v ? q0 + my : pos_base];
     };
+    const uint32_t pmask = (1u << a.pc_log2) - 1u;
     auto fetch_q = [&](uint32_t pid, bf16x8 (&B)[2]) {
-        const uint16_t* qrow = a.q + (int64_t)(pid >> a.sp_log2) * kD + 8 * (lane >> 4);
+        // chunk-local row -> (query head bh, position t) -> global row
+        const uint32_t lrow = pid >> a.sp_log2;
+        const int64_t grow = (int64_t)(lrow >> a.pc_log2) * a.N + a.t_base + (lrow & pmask);
+        const uint16_t* qrow = a.q + grow * kD + 8 * (lane >> 4);
         B[0] = load_bf16x8(qrow);
         B[1] = load_bf16x8(qrow + 32);
     };
@@ -275,7 +285,9 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
 
         if (cur.bucket != loaded) {
             __syncthreads();
-            const int bg = cur.bucket / a.nb, c = cur.bucket - bg * a.nb;
+            // buckets of this chunk: [b0, b1) = (b * Hkv + g, key block) pairs
+            const int rel = cur.bucket - a.b0;
+            const int bg = rel / a.nb, c = rel - bg * a.nb;
             const int key0 = c * BS;
             stage_rows<true>(s_k, KPITCH, a.k + ((int64_t)bg * a.N + key0) * kD, kD, BS, BS, tid);
             // V^T columns [VC * (key0 / VC), +VC) from the 64-key tiles
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
         }
         // by position: the wave's 16 rows are consecutive, so this store is
         // contiguous (the row's four lanes store the same value)
-        a.part_lse[v_cur ? p0 + my : dummy_pos] = m2 + log2f(sum);
+        a.part_lse[v_cur ? p0 + my - pos_base : dummy_pos] = m2 + log2f(sum);
         v_cur = v_nxt;
         pid_cur = pid_nxt;
         v_nxt = v_n2;
@@ -343,12 +355,14 @@ struct WinArgs {
     const uint16_t* k;
     const uint16_t* vt;
     const int32_t* idx;  // [B,Hq,N,top_k]; group_route: [B,Hkv,N,top_k]
-    const uint16_t* part_o;
-    const float* part_lse;
-    const uint32_t* rev;  // [top_k][rows]
+    const uint16_t* part_o;   // the chunk's partial rows, by chunk-local pair id
+    const float* part_lse;    // the chunk's log2 masses, by pair position in the chunk
+    const uint32_t* rev;      // [top_k][rows]: global pair positions
+    const uint32_t* offsets;  // [NB+1] bucket offsets (the chunk's first pair: offsets[b0])
     float* out;
     int64_t rows;
     int Hq, Hkv, N, bs, top_k, window, tiles, items, ntiles, sp_log2;
+    int b0, pc_log2, t_base;  // the chunk: first bucket, positions (log2), first position
     float scale_log2;
     int group_route;
 };
@@ -375,12 +389,12 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     const int rep = a.Hq / a.Hkv;
     if (item >= a.items) return;
     const int hh = item % rep;
-    const int tile = (item / rep) % a.tiles;
+    const int tile = (item / rep) % a.tiles;  // tiles of this chunk
     const int bg = item / (rep * a.tiles);
     const int b = bg / a.Hkv;
     const int h = (bg - b * a.Hkv) * rep + hh;
     const int bh = b * a.Hq + h;
-    const int t0 = tile * 64;
+    const int t0 = a.t_base + tile * 64;
     const int key_lo = a.bs * eligible_blocks(t0, a.bs, a.window);
     const int key_hi = min(t0 + 63, a.N - 1);
     const int lo_max = a.bs * eligible_blocks(key_hi, a.bs, a.window);  // largest row start
@@ -480,7 +494,8 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     // merge the routed partials (normalised outputs with their log2 mass),
     // eight slots at a time so their loads are in flight together; a
     // partial row stores dim 16mt + 4j + r at slot 16j + 4mt + r
-    const int64_t prow = row << a.sp_log2;
+    const int64_t prow = (((int64_t)bh << a.pc_log2) + (t - a.t_base)) << a.sp_log2;
+    const uint32_t pos_base = uniform_load(a.offsets + a.b0);
     // log2 masses: the pair positions from the slot-major table (the wave's
     // 16 rows are consecutive, so each load is contiguous), then one 4-byte
     // gather per used slot
@@ -492,7 +507,8 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
             rs[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.rev[sl * a.rows + row] : 0u;
 #pragma unroll
         for (int sl = 0; sl < kMaxTopK; ++sl)
-            lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.part_lse[rs[sl]] : -INFINITY;
+            lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.part_lse[rs[sl] - pos_base]
+                                                                 : -INFINITY;
     }
 #pragma unroll
     for (int s0 = 0; s0 < kMaxTopK; s0 += 8) {
@@ -663,8 +679,62 @@ int pair_stride_log2(int top_k) {
     return l;
 }
 
+// Causal attention runs over position chunks of 2^pc_log2 positions (all
+// query heads of every batch).  A chunk's partial rows are written by the
+// partial kernel and read back by the merge before the next chunk starts, so
+// the partial storage is one chunk's worth.  Chunks cost time: each chunk
+// splits every key block's bucket, so its staged K/V block serves fewer
+// 64-row units, and adds two launches.  (Chunks small enough for their
+// partials to stay in the 256 MB memory-side cache were measured slower,
+// not faster.)  So a layer is one chunk unless its partials would exceed
+// kChunkPartialBytes, and a chunk always gives each key block a few units.
+constexpr int64_t kChunkPartialBytes = int64_t(32) << 30;  // partial rows per chunk
+constexpr int64_t kMinPairsPerBucket = 192;                 // three 64-row units
+
+struct ChunkPlan {
+    int pc_log2;   // positions per chunk (log2), >= 6
+    int nchunk;    // ceil(N / 2^pc_log2)
+    int tc_log2;   // positions per bucketing workgroup (log2), <= pc_log2
+};
+
+static ChunkPlan chunk_plan(const Geometry& g) {
+    ChunkPlan c{};
+    const int rep = g.Hq / g.Hkv;
+    const int sp_log2 = pair_stride_log2(g.top_k);
+    const int64_t row_bytes = (int64_t)g.B * g.Hq * ((int64_t)kD * 2) << sp_log2;  // per position
+    int lmall = 6;
+    while ((row_bytes << (lmall + 1)) <= kChunkPartialBytes) ++lmall;
+    int locc = 6;
+    while (((int64_t)rep * g.top_k << locc) < kMinPairsPerBucket * g.nb) ++locc;
+    int ln = 6;
+    while ((1 << ln) < g.N) ++ln;
+    c.pc_log2 = std::min(std::max(lmall, locc), ln);
+    if (g.chunk > 0) {  // the caller's choice (a power of two >= 64)
+        int lc = 6;
+        while ((1 << lc) < g.chunk) ++lc;
+        c.pc_log2 = std::min(lc, ln);
+    }
+    c.nchunk = (int)(((int64_t)g.N + (1 << c.pc_log2) - 1) >> c.pc_log2);
+    // bucketing workgroups: ~4096 rows over the group's query heads, fewer
+    // when that would leave under ~256 workgroups, but enough pairs to
+    // amortise the per-bucket flush of the LDS histogram; a power of two
+    // within one chunk
+    const int nbg = g.B * g.Hkv;
+    const int64_t flush_min =
+        (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k);
+    int64_t tc = std::min<int64_t>((4096 + rep - 1) / rep, (int64_t)nbg * g.N / 256);
+    tc = std::max<int64_t>(tc, flush_min);
+    int lt = 6;
+    while (lt < c.pc_log2 && ((int64_t)1 << (lt + 1)) <= tc) ++lt;
+    c.tc_log2 = lt;
+    return c;
+}
+
 struct AttendLayout {
     size_t vt, counts, offsets, cursor, unit_off, pairs, rev, part_o, part_lse, total;
+    ChunkPlan plan;
+    int64_t NB;     // buckets: chunks x (b, KV head) x key blocks
+    int64_t crows;  // rows of one chunk: B * Hq * 2^pc_log2
 };
 
 static AttendLayout attend_layout(const Geometry& g) {
@@ -674,18 +744,21 @@ static AttendLayout attend_layout(const Geometry& g) {
     size_t off = 0;
     L.vt = off;       off += align_up(nbg * ntiles * kD * VT_TILE * 2, 256);
     if (g.causal) {
-        const size_t NB = nbg * g.nb;
+        L.plan = chunk_plan(g);
+        L.NB = (int64_t)L.plan.nchunk * nbg * g.nb;
+        L.crows = (int64_t)g.B * g.Hq << L.plan.pc_log2;
+        const size_t NB = (size_t)L.NB;
         const size_t rows = (size_t)g.B * g.Hq * g.N;
         const size_t npairs = rows * g.top_k;
-        const size_t nslots = rows << pair_stride_log2(g.top_k);
+        const size_t cslots = (size_t)L.crows << pair_stride_log2(g.top_k);
         L.counts = off;   off += align_up(NB * 4, 256);
         L.offsets = off;  off += align_up((NB + 1) * 4, 256);
         L.cursor = off;   off += align_up(NB * 4, 256);
         L.unit_off = off; off += align_up((NB + 1) * 4, 256);
         L.pairs = off;    off += align_up(npairs * 4, 256);
         L.rev = off;      off += align_up(npairs * 4, 256);
-        L.part_o = off;   off += align_up((nslots + UNIT_ROWS) * kD * 2, 256);
-        L.part_lse = off; off += align_up((npairs + UNIT_ROWS) * 4, 256);
+        L.part_o = off;   off += align_up((cslots + UNIT_ROWS) * kD * 2, 256);
+        L.part_lse = off; off += align_up(((size_t)L.crows * g.top_k + UNIT_ROWS) * 4, 256);
     }
     L.total = off;
     return L;
@@ -733,26 +806,16 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     uint16_t* part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
     float* part_lse = reinterpret_cast<float*>(base + L.part_lse);
     uint32_t* rev = reinterpret_cast<uint32_t*>(base + L.rev);
-    const int NB = nbg * g.nb;
+    const ChunkPlan& P = L.plan;
+    const int NB = (int)L.NB;
     const int sp_log2 = pair_stride_log2(g.top_k);
 
     hipError_t e = launch_fill_u32(counts, (size_t)NB, 0u, s);
     if (e != hipSuccess) return e;
-    // positions per bucketing workgroup: ~4096 rows, or fewer when that
-    // leaves under ~256 workgroups (short sequences), but always enough
-    // pairs to amortise the per-bucket flush.  (Smaller chunks at long
-    // sequences speed the bucketing up but interleave each bucket's pairs
-    // more, which the partial and merge kernels pay back.)
-    const int rep = g.Hq / g.Hkv;
-    const int64_t flush_min =
-        (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k);
-    int64_t tc = std::min<int64_t>((4096 + rep - 1) / rep, (int64_t)nbg * g.N / 256);
-    tc = std::max<int64_t>(tc, flush_min);
-    tc = std::min<int64_t>(std::max<int64_t>((tc + 63) / 64 * 64, 64), g.N);
     const int64_t rows = (int64_t)g.B * g.Hq * g.N;
     BucketArgs ba{idx, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window,
-                  (int)tc, sp_log2, g.consensus, 0};
-    const int nch = (int)((g.N + tc - 1) / tc);
+                  1 << P.tc_log2, sp_log2, g.consensus, 0, P.pc_log2, nbg};
+    const int nch = (g.N + (1 << P.tc_log2) - 1) >> P.tc_log2;
     const dim3 bgrid((unsigned)(nbg * nch));
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
     hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
@@ -763,22 +826,32 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
     mark(ev, 6, s);
 
-    const uint32_t nslots = (uint32_t)(((size_t)g.B * g.Hq * g.N) << sp_log2);
-    const uint32_t npairs_max = (uint32_t)((size_t)g.B * g.Hq * g.N * g.top_k);
-    PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, nslots, npairs_max, g.N,
-                g.nb, NB, ntiles, sp_log2, scale_log2};
-    switch (g.bs) {
-        case 16: launch_partial<16>(pa, s); break;
-        case 32: launch_partial<32>(pa, s); break;
-        case 64: launch_partial<64>(pa, s); break;
-        default: launch_partial<128>(pa, s); break;
+    // stage events: with one chunk, 7 follows the partials and 8 the merge;
+    // with several, 7 follows the last chunk's merge and stage 8 is empty
+    const uint32_t cslots = (uint32_t)(L.crows << sp_log2);
+    const uint32_t cpairs = (uint32_t)(L.crows * g.top_k);
+    const int rep = g.Hq / g.Hkv;
+    for (int c = 0; c < P.nchunk; ++c) {
+        const int t_base = c << P.pc_log2;
+        const int b0 = c * nbg * g.nb, b1 = b0 + nbg * g.nb;
+        PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, cslots, cpairs, g.N,
+                    g.nb, NB, ntiles, sp_log2, b0, b1, P.pc_log2, t_base, scale_log2};
+        switch (g.bs) {
+            case 16: launch_partial<16>(pa, s); break;
+            case 32: launch_partial<32>(pa, s); break;
+            case 64: launch_partial<64>(pa, s); break;
+            default: launch_partial<128>(pa, s); break;
+        }
+        if (P.nchunk == 1) mark(ev, 7, s);
+        const int span = std::min(1 << P.pc_log2, g.N - t_base);
+        const int wtiles = (span + 63) / 64;
+        WinArgs wa{q, k, vt, idx, part_o, part_lse, rev, offsets, out, rows, g.Hq, g.Hkv, g.N,
+                   g.bs, g.top_k, g.window, wtiles, nbg * rep * wtiles, ntiles, sp_log2, b0,
+                   P.pc_log2, t_base, scale_log2, g.consensus};
+        const int64_t wgrid = ((int64_t)wa.items + 7) / 8 * 8;  // multiple of the XCD count
+        hipLaunchKernelGGL(k_window_merge, dim3((unsigned)wgrid), dim3(256), 0, s, wa);
     }
-    mark(ev, 7, s);
-    const int wtiles = (g.N + 63) / 64;
-    WinArgs wa{q, k, vt, idx, part_o, part_lse, rev, out, rows, g.Hq, g.Hkv, g.N, g.bs, g.top_k, g.window,
-               wtiles, g.B * g.Hq * wtiles, ntiles, sp_log2, scale_log2, g.consensus};
-    const int64_t wgrid = ((int64_t)wa.items + 7) / 8 * 8;  // multiple of the XCD count
-    hipLaunchKernelGGL(k_window_merge, dim3((unsigned)wgrid), dim3(256), 0, s, wa);
+    if (P.nchunk > 1) mark(ev, 7, s);
     mark(ev, 8, s);
     return hipGetLastError();
 }

@@ -56,6 +56,13 @@ struct BucketArgs {
     int group_route;     // 1: one route per KV group, shared by its query heads
     int cshift;          // buckets group 2^cshift blocks: a row's candidate buckets are
                          // ceil(E(t) / 2^cshift) (0: buckets are blocks)
+    // Position chunks (pc_log2 >= 0): buckets are (chunk, b * Hkv + g, block)
+    // with chunk = t >> pc_log2, and pair ids are chunk-local: row (bh, t) is
+    // local row bh * 2^pc_log2 + (t mod 2^pc_log2).  A workgroup's positions
+    // must lie in one chunk (tchunk divides 2^pc_log2).  pc_log2 < 0: buckets
+    // are (b * Hkv + g, block) and pair ids use the global row bh * N + t.
+    int pc_log2 = -1;
+    int nbg = 0;         // B * Hkv (with position chunks)
 };
 
 __device__ __forceinline__ int bucket_candidates(const BucketArgs& a, int t) {
@@ -87,7 +94,14 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     const int t0 = ch * a.tchunk, t1 = min(a.N, t0 + a.tchunk);
     const int span = t1 - t0;
     const bool lds = a.nb <= BK_LDS_MAX;
-    const int64_t bucket0 = (int64_t)bg * a.nb;
+    const bool chunked = a.pc_log2 >= 0;
+    const int64_t bucket0 =
+        chunked ? ((int64_t)(t0 >> a.pc_log2) * a.nbg + bg) * a.nb : (int64_t)bg * a.nb;
+    // pair-id row of query head hh at position t
+    auto pair_row = [&](int hh, int t, int64_t row) -> int64_t {
+        if (!chunked) return row;
+        return (((int64_t)b * a.Hq + g * rep + hh) << a.pc_log2) + (t & ((1 << a.pc_log2) - 1));
+    };
     if (lds) {
         for (int c = tid; c < a.nb; c += 256) s_h[c] = 0;
         __syncthreads();
@@ -109,7 +123,7 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
                 atomicAdd(&a.counts[bucket0 + c[s]], 1u);
             } else {
                 const uint32_t pos = atomicAdd(&a.cursor[bucket0 + c[s]], 1u);
-                a.pairs[pos] = (uint32_t)((row << a.sp_log2) | s);
+                a.pairs[pos] = (uint32_t)((pair_row(hh, t, row) << a.sp_log2) | s);
                 posv[s] = pos;
             }
         }
@@ -138,9 +152,10 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s)
             posv[s] = ((m >> s) & 1u) ? atomicAdd(&s_h[c[s]], 1u) : 0xFFFFFFFFu;
+        const int64_t prow = pair_row(hh, t, row);
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s)
-            if ((m >> s) & 1u) a.pairs[posv[s]] = (uint32_t)((row << a.sp_log2) | s);
+            if ((m >> s) & 1u) a.pairs[posv[s]] = (uint32_t)((prow << a.sp_log2) | s);
         write_rev_row(a.rev, a.rows, row, posv, a.top_k);
     }
 }

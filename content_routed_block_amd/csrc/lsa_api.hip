@@ -38,6 +38,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     if (p->top_k > lsa::kMaxTopK) return LSA_ERR_UNSUPPORTED;
     if (p->beta != 0.f && (!p->causal || p->consensus)) return LSA_ERR_UNSUPPORTED;
     if (p->beam < 0) return LSA_ERR_SHAPE;
+    if (p->chunk != 0 && (p->chunk < 64 || (p->chunk & (p->chunk - 1)))) return LSA_ERR_SHAPE;
     if (p->beam > 0 &&
         (p->beam >= lsa::kMaxTopK || !p->causal || p->consensus || p->beta != 0.f))
         return LSA_ERR_UNSUPPORTED;
@@ -66,6 +67,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     g->consensus = p->consensus;
     g->beta = p->beta;
     g->beam = p->beam;
+    g->chunk = p->chunk;
     g->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
     return LSA_OK;
 }

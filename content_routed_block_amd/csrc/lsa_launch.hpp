@@ -17,6 +17,7 @@ struct Geometry {
     float scale;    // resolved (> 0)
     float beta;     // second-cumulant weight (0: the block-mean score)
     int beam;       // two-level routing: nodes kept per row (0: flat routing)
+    int chunk;      // causal attention: positions per chunk (0: chosen from the geometry)
 };
 
 // x [BH, N, 64] bf16 -> xbar [BH, N/bs, 64] fp32

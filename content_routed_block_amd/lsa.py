@@ -37,7 +37,7 @@ class LsaParams(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("consensus", ctypes.c_int32), ("beta", ctypes.c_float),
-                ("beam", ctypes.c_int32)]
+                ("beam", ctypes.c_int32), ("chunk", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(LsaParams)
@@ -89,9 +89,9 @@ def library():
 
 
 def params(batch, q_heads, kv_heads, seq_len, head_dim=64, block=64, top_k=16, window=512,
-           causal=1, scale=0.0, consensus=0, beta=0.0, beam=0) -> LsaParams:
+           causal=1, scale=0.0, consensus=0, beta=0.0, beam=0, chunk=0) -> LsaParams:
     return LsaParams(batch, q_heads, kv_heads, seq_len, head_dim, block, top_k, window, causal,
-                     float(scale), consensus, float(beta), beam)
+                     float(scale), consensus, float(beta), beam, chunk)
 
 
 def idx_shape(p: LsaParams):

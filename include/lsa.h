@@ -70,6 +70,10 @@ typedef struct lsa_params {
     int32_t beam;      /* two-level routing: nodes kept per query (see
                           lsa_route_topk); 0: flat routing.  1..15, needs
                           causal = 1, consensus = 0 and beta = 0 */
+    int32_t chunk;     /* causal attention: query positions per chunk (see
+                          lsa_sparse_attend); 0 chooses it from the geometry,
+                          otherwise a power of two >= 64.  Results do not
+                          depend on it; the workspace does */
 } lsa_params;
 
 typedef enum lsa_status {
@@ -173,7 +177,17 @@ lsa_status lsa_route_cumulant(const lsa_params *p, const void *q, const void *k,
  * skipped, so every access stays in bounds for any idx contents.  With
  * consensus = 1 idx holds one route per KV group (lsa_route_topk's layout)
  * and query head h reads the route of its group h / (Hq / Hkv).
- * out [B, Hq, N, D] fp32. */
+ * out [B, Hq, N, D] fp32.
+ * Causal mode runs key-block-major over chunks of query positions (all
+ * heads): per chunk, every (row, routed block) pair's partial softmax is
+ * formed with its key block staged once for all rows that chose it, then the
+ * window attention merges the row's partials.  p->chunk sets the positions
+ * per chunk (0: the whole sequence, unless its partials would exceed
+ * 32 GiB; chunks cost time, as each splits every key block's rows).  The
+ * output does not depend on the chunk size; the workspace holds one chunk's
+ * partials (B * Hq * chunk * 2^ceil(log2 top_k) rows of 128 bytes, plus
+ * 4 bytes per routed pair of the chunk) and 8 bytes per routed pair of the
+ * whole layer. */
 lsa_status lsa_sparse_attend(const lsa_params *p, const void *q, const void *k,
                              const void *v, const int32_t *idx, float *out,
                              void *workspace, size_t workspace_bytes, void *stream);

@@ -39,8 +39,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header(lsa):
-    assert ctypes.sizeof(lsa.LsaParams) == 52
+    assert ctypes.sizeof(lsa.LsaParams) == 56
     assert lsa.LsaParams.beam.offset == 48
+    assert lsa.LsaParams.chunk.offset == 52
     assert lsa.LsaParams.consensus.offset == 40
     assert lsa.LsaParams.beta.offset == 44
 
@@ -60,6 +61,7 @@ def good(lsa, **kw):
     (dict(beta=0.5, causal=0, window=0, block=16), 3), (dict(beam=-1), 2), (dict(beam=16), 3),
     (dict(beam=4, consensus=1), 3), (dict(beam=4, beta=0.5), 3),
     (dict(beam=4, causal=0, window=0, block=16), 3),
+    (dict(chunk=-64), 2), (dict(chunk=32), 2), (dict(chunk=96), 2),
     (dict(head_dim=128), 3), (dict(top_k=17), 3), (dict(block=48, window=96, seq_len=960), 3),
     (dict(causal=0, window=0, block=64), 3), (dict(seq_len=1 << 24, block=16, window=512), 3),
 ])
@@ -95,8 +97,18 @@ def test_workspace_sizes_are_plausible(lsa):
     pairs = 14 * 131072 * 16
     vt = 2 * 131072 * 64 * 2                      # V^T copy of both KV heads
     att = lsa.workspace_bytes(p, lsa.OP_ATTEND)
-    per_pair = 64 * 2 + 4 + 4 + 4                 # partial row, log-mass, pair id, position
-    assert pairs * per_pair + vt <= att < pairs * per_pair + vt + (1 << 20)
+    # per routed pair of the layer: pair id and position; per pair of one
+    # chunk (here the whole layer): the bf16 partial row and its log-mass
+    want = pairs * (8 + 64 * 2 + 4) + vt
+    assert want <= att < want + (1 << 20)
+    # chunks of 4096 positions: the partial rows of one chunk only, and
+    # buckets per (chunk, KV head, key block)
+    chunked = lsa.workspace_bytes(good(lsa, chunk=4096), lsa.OP_ATTEND)
+    want_c = pairs * 8 + 14 * 4096 * 16 * (64 * 2 + 4) + vt + 32 * 2 * 2048 * 16
+    assert want_c <= chunked < want_c + (1 << 20)
+    # past 32 GiB of partial rows the layer is chunked by itself
+    big = good(lsa, batch=4, seq_len=1 << 20)
+    assert lsa.workspace_bytes(big, lsa.OP_ATTEND) < 4 * 14 * (1 << 20) * 16 * 8 + (33 << 30)
     assert lsa.workspace_bytes(p, lsa.OP_SUMMARIZE) == 0
     img = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0)
     assert lsa.workspace_bytes(img, lsa.OP_ATTEND) == 4 * 16 * 16384 * 64 * 2

@@ -220,6 +220,34 @@ def test_dense_special_cases(lsa, w, causal):
     check_output(out.reshape(-1, 64), ref.reshape(-1, 64), vmax_rows(w, inp))
 
 
+@pytest.mark.parametrize("over", [dict(chunk=64), dict(chunk=128), dict(chunk=512),
+                                  dict(chunk=64, consensus=1), dict(chunk=256, consensus=1)],
+                         ids=["c64", "c128", "c512", "c64-consensus", "c256-consensus"])
+def test_forward_is_independent_of_the_attention_chunk(lsa, over):
+    """Causal attention runs over chunks of query positions; forcing small
+    chunks (many partial passes, ragged last chunk) changes nothing, bit for
+    bit, and the result matches the oracle."""
+    w = custom(2, 6, 2, 2048 + 3 * 64 + 32, 32, 8, 192, dist="topics", seed=21)
+    say("chunked forward", w.name, over)
+    inp = generate(w)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    base = {"consensus": over["consensus"]} if "consensus" in over else {}
+    o0, i0 = lsa.forward(params_of(lsa, w, **base), q, k, v)
+    o1, i1 = lsa.forward(params_of(lsa, w, **over), q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1)
+    assert torch.equal(o0.view(torch.int32), o1.view(torch.int32))
+    if "consensus" in over:
+        return
+    out, idx = o1.cpu().numpy(), i1.cpu().numpy()
+    io, gap, scores, ncand = oracle_route(w, inp, oracle.block_means(inp.k, w.block))
+    bad, _, _ = check_routing(idx.reshape(io.shape), io, gap, scores, ncand, w.top_k)
+    assert bad == 0
+    ref = oracle.attend(inp.q, inp.k, inp.v, per_row_selection(w, idx), w.block, w.top_k,
+                        w.window, w.causal)
+    check_output(out.reshape(-1, 64), ref.reshape(-1, 64), vmax_rows(w, inp))
+
+
 def test_forward_is_deterministic(lsa):
     w = WORKLOADS["qwen05b_n32k"].replace(seq_len=8192, name="det")
     inp = generate(w)
