@@ -411,12 +411,13 @@ def cumulant_bench(lsa, w, q, k, v, steps, inp=None):
 
 def tree_bench(lsa, w, q, k, v, beam, steps, inp=None):
     """The layer with two-level routing (nodes of 16 blocks, `beam` kept per
-    row): ms per layer and stage times (for this mode stage "routing" is the
-    node level with the tail slots, and "routing fallback" is the block
-    level over the kept nodes)."""
+    row; in image mode the rows are the pooled query blocks): ms per layer
+    and stage times (for this mode stage "routing" is the node level with
+    the tail slots, and "routing fallback" is the block level over the kept
+    nodes)."""
     import torch
     p = lsa.params(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.top_k,
-                   w.window, 1, beam=beam)
+                   w.window, w.causal, beam=beam)
     out = torch.empty((w.batch, w.q_heads, w.seq_len, w.head_dim), dtype=torch.float32,
                       device=q.device)
     idx = torch.empty(lsa.idx_shape(p), dtype=torch.int32, device=q.device)
@@ -433,21 +434,30 @@ def tree_bench(lsa, w, q, k, v, beam, steps, inp=None):
     stage = np.array([e.stage_ms() for e in events]).mean(axis=0)
     for e in events:
         e.close()
-    t = np.arange(w.seq_len, dtype=np.int64)
-    E = np.maximum(0, t // w.block - w.window // w.block + 1)
+    nb = w.seq_len // w.block
+    if w.causal:
+        t = np.arange(w.seq_len, dtype=np.int64)
+        E = np.maximum(0, t // w.block - w.window // w.block + 1)
+        per_head = w.seq_len
+    else:
+        E = np.full(nb, nb, dtype=np.int64)              # every query block, every key block
+        per_head = nb
     S = E // 16
-    scored = int((S + 16 * np.minimum(beam, S) + (E - 16 * S)).sum()) * w.batch * w.q_heads
-    rows = w.batch * w.q_heads * w.seq_len
-    node_flop = 2 * w.head_dim * int(S.sum()) * w.batch * w.q_heads
-    # block level: per (row, node) pair the pair id, the gathered query row,
-    # 16 fp32 scores written and read back, the pair position; per row its
-    # slot list and idx row
-    pairs = int((np.minimum(beam, S) + (16 * S < E)).sum()) * w.batch * w.q_heads
-    blk_bytes = pairs * (4 + 2 * w.head_dim + 2 * 64 + 4) + rows * ((beam + 1) * 4 + w.top_k * 4)
+    heads = w.batch * w.q_heads
+    scored = int((S + 16 * np.minimum(beam, S) + (E - 16 * S)).sum()) * heads
+    rows = heads * per_head
+    node_flop = 2 * w.head_dim * int(S.sum()) * heads
+    # block level: per (row, node) pair the pair id, the gathered query row
+    # (bf16, or the fp32 pooled query in image mode), 16 fp32 scores written
+    # and read back, the pair position; per row its slot list and idx row
+    qbytes = (2 if w.causal else 4) * w.head_dim
+    pairs = int((np.minimum(beam, S) + (16 * S < E)).sum()) * heads
+    blk_bytes = pairs * (4 + qbytes + 2 * 64 + 4) + rows * ((beam + 1) * 4 + w.top_k * 4)
+    flat = routing_candidates(w)
     res = {"beam": beam, "ms_per_layer": ms,
            "node_level_ms": float(stage[1]), "block_level_ms": float(stage[2]),
            "routing_ms": float(stage[1] + stage[2]),
-           "scores_per_layer": scored, "flat_scores_per_layer": routing_candidates(w),
+           "scores_per_layer": scored, "flat_scores_per_layer": flat,
            "node_level_roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
                                    "achieved": node_flop / 1e12 / (float(stage[1]) * 1e-3),
                                    "frac": node_flop / 1e12 / (float(stage[1]) * 1e-3)
@@ -463,12 +473,19 @@ def tree_bench(lsa, w, q, k, v, beam, steps, inp=None):
         sample = np.sort(np.random.default_rng(10).choice(rows, size=min(rows, 2000),
                                                           replace=False))
         kbar = oracle.block_means(inp.k, w.block)
-        r = oracle_rate(lambda: oracle.route_tree(kbar, w.block, w.top_k, beam, q=inp.q,
-                                                  window=w.window, rows=sample), sample.size)
+        if w.causal:
+            fn = lambda: oracle.route_tree(kbar, w.block, w.top_k, beam, q=inp.q,
+                                           window=w.window, rows=sample)
+        else:
+            qbar = oracle.block_means(inp.q, w.block)
+            fn = lambda: oracle.route_tree(kbar, w.block, w.top_k, beam, qbar=qbar, causal=0,
+                                           rows=sample)
+        r = oracle_rate(fn, sample.size)
         res["cpu_oracle"] = {"kind": "oracle", "cores": oracle.num_threads(),
                              "routing_rows_per_s": r["rows_per_s"],
                              "gpu_routing_rows_per_s": rows / (res["routing_ms"] * 1e-3),
-                             "sample": f"routing of {sample.size} of {rows} query rows"}
+                             "sample": f"routing of {sample.size} of {rows} "
+                                       f"{'query rows' if w.causal else 'query blocks'}"}
     return res
 
 
@@ -671,7 +688,7 @@ def main():
     if w.causal and args.cumulant_steps > 0 and w.seq_len <= 262144:
         result["cumulant"] = cumulant_bench(lsa, w, q, k, v, args.cumulant_steps,
                                             inp if args.cpu_seconds > 0 else None)
-    if w.causal and args.tree_beam > 0:
+    if args.tree_beam > 0:
         result["tree"] = tree_bench(lsa, w, q, k, v, args.tree_beam, max(3, min(args.steps, 10)),
                                     inp if args.cpu_seconds > 0 else None)
     if w.causal and args.decode_steps > 0:

@@ -63,9 +63,11 @@ struct BucketArgs {
     // are (b * Hkv + g, block) and pair ids use the global row bh * N + t.
     int pc_log2 = -1;
     int nbg = 0;         // B * Hkv (with position chunks)
+    int fixed_cand = 0;  // > 0: every row's candidate buckets (image-mode rows); else causal
 };
 
 __device__ __forceinline__ int bucket_candidates(const BucketArgs& a, int t) {
+    if (a.fixed_cand > 0) return a.fixed_cand;
     const int e = eligible_blocks(t, a.bs, a.window);
     return (e + (1 << a.cshift) - 1) >> a.cshift;
 }

@@ -39,8 +39,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     if (p->beta != 0.f && (!p->causal || p->consensus)) return LSA_ERR_UNSUPPORTED;
     if (p->beam < 0) return LSA_ERR_SHAPE;
     if (p->chunk != 0 && (p->chunk < 64 || (p->chunk & (p->chunk - 1)))) return LSA_ERR_SHAPE;
-    if (p->beam > 0 &&
-        (p->beam >= lsa::kMaxTopK || !p->causal || p->consensus || p->beta != 0.f))
+    if (p->beam > 0 && (p->beam >= lsa::kMaxTopK || p->consensus || p->beta != 0.f))
         return LSA_ERR_UNSUPPORTED;
     const int64_t nb = p->seq_len / p->block;
     if (nb > 65536) return LSA_ERR_UNSUPPORTED;

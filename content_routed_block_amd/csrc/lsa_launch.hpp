@@ -37,12 +37,14 @@ int pair_stride_log2(int top_k);
 
 // Sparse attention workspace (bytes) and launch.
 // Second level of two-level routing: scores every block of the nodes listed
-// in slots [B*Hq*N][beam + 1] (kept nodes, then the tail node) and writes
-// the top-k to idx.  bhi/blo: bf16 hi/lo block means [B*Hkv][nb_pad][64].
+// in slots [rows][beam + 1] (kept nodes, then the tail node) and writes the
+// top-k to idx.  Rows are causal positions (B*Hq*N, queries q) or, in image
+// mode, query blocks (B*Hq*nb, pooled fp32 queries qbar).  bhi/blo: bf16
+// hi/lo block means [B*Hkv][nb_pad][64].
 size_t tree_level2_bytes(const Geometry& g);
-hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16_t* bhi,
-                              const uint16_t* blo, int nb_pad, const int32_t* slots, int32_t* idx,
-                              void* ws, hipStream_t s);
+hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const float* qbar,
+                              const uint16_t* bhi, const uint16_t* blo, int nb_pad,
+                              const int32_t* slots, int32_t* idx, void* ws, hipStream_t s);
 
 // Second-cumulant routing (beta != 0, causal, per query head): needs no
 // workspace.

@@ -73,6 +73,7 @@ struct RouteArgs {
     int nb_pad;  // nb rounded up to a multiple of RT_CH
     int cshift;      // causal candidates are E(t) >> cshift (two-level routing: nodes of 16 blocks)
     int idx_stride;  // idx row stride (>= top_k)
+    int tail_img;    // image-mode two-level routing: every row's tail node (-1: none)
 };
 
 // ------------------------------------------------------------ sorting networks
@@ -614,8 +615,9 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) m += (j < a.top_k && Mx[j] != 0ull) ? 1 : 0;
             write_selection(a.idx + out_row * a.idx_stride, Mx, m, a.top_k, a.idx_stride);
-            if (CAUSAL && a.idx_stride > a.top_k)
-                a.idx[out_row * a.idx_stride + a.top_k] = tail_node(rq, a.bs, a.window);
+            if (a.idx_stride > a.top_k)
+                a.idx[out_row * a.idx_stride + a.top_k] =
+                    CAUSAL ? tail_node(rq, a.bs, a.window) : a.tail_img;
         }
         return;
     }
@@ -670,8 +672,9 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         write_selection(a.idx + out_row * a.idx_stride, M, m, a.top_k, a.idx_stride);
         // two-level routing (rows of beam + 1 slots): the tail node, written
         // beside the row's other slots
-        if (CAUSAL && a.idx_stride > a.top_k)
-            a.idx[out_row * a.idx_stride + a.top_k] = tail_node(rq, a.bs, a.window);
+        if (a.idx_stride > a.top_k)
+            a.idx[out_row * a.idx_stride + a.top_k] =
+                CAUSAL ? tail_node(rq, a.bs, a.window) : a.tail_img;
     }
 }
 
@@ -797,8 +800,9 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
         __syncthreads();
         if (w == 0 && lane == 0) {
             write_selection(a.idx + (int64_t)rid * a.idx_stride, R, m, a.top_k, a.idx_stride);
-            if (CAUSAL && a.idx_stride > a.top_k)
-                a.idx[(int64_t)rid * a.idx_stride + a.top_k] = tail_node(row, a.bs, a.window);
+            if (a.idx_stride > a.top_k)
+                a.idx[(int64_t)rid * a.idx_stride + a.top_k] =
+                    CAUSAL ? tail_node(row, a.bs, a.window) : a.tail_img;
         }
     }
 }
@@ -1082,25 +1086,32 @@ __global__ __launch_bounds__(256) void k_node_means(const float* __restrict__ kb
               (float)(acc[6] / kTreeFanout), (float)(acc[7] / kTreeFanout)};
 }
 
-// Slot `beam` of each row's slot list (tail_node), for launches where no row
-// has a complete node and so no routing kernel runs to write it.
+// Slot `beam` of each row's slot list (causal rows: tail_node; image-mode
+// rows: the same tail for every row), for launches where no row has a
+// complete node and so no routing kernel runs to write it.
 __global__ __launch_bounds__(256) void k_tree_tail(int32_t* __restrict__ slots, int beam,
-                                                   int64_t rows, int N, int bs, int window) {
+                                                   int64_t rows, int N, int bs, int window,
+                                                   int causal, int tail_img) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (row >= rows) return;
-    slots[row * (beam + 1) + beam] = tail_node((int)(row % N), bs, window);
+    slots[row * (beam + 1) + beam] = causal ? tail_node((int)(row % N), bs, window) : tail_img;
 }
 
 // ------------------------------------------------------------ host side
 static int route_heads(const Geometry& g) { return g.consensus ? g.Hkv : g.Hq; }
 
+// Rows per (b, routed head): positions, or query blocks in image mode (the
+// first level of two-level routing keeps N and bs and routes over nodes, so
+// its nb is not the row count).
+static int route_P(const Geometry& g) { return g.causal ? g.N : g.N / g.bs; }
+
 static size_t route_rows(const Geometry& g) {
-    return (size_t)g.B * route_heads(g) * (g.causal ? (size_t)g.N : (size_t)g.nb);
+    return (size_t)g.B * route_heads(g) * (size_t)route_P(g);
 }
 
 // Routing workgroups (tiles of RT_ROWS rows) over all (b, routed head).
 static size_t route_items(const Geometry& g) {
-    const size_t P = g.causal ? (size_t)g.N : (size_t)g.nb;
+    const size_t P = (size_t)route_P(g);
     return (size_t)g.B * route_heads(g) * ((P + RT_ROWS - 1) / RT_ROWS);
 }
 
@@ -1116,7 +1127,7 @@ static RouteLayout route_layout(const Geometry& g) {
     size_t off = 256;  // overflow counter
     L.ovf_rows = off; off += align_up(route_rows(g) * 4, 256);
     L.tiles = off;    off += align_up(route_items(g) * 4, 256);
-    L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * g.nb * kD * 4, 256);
+    L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * route_P(g) * kD * 4, 256);
     L.qsum = off;     if (g.consensus) off += align_up(route_rows(g) * kD * 4, 256);
     L.khi = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
     L.klo = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
@@ -1131,7 +1142,7 @@ static RouteLayout route_layout(const Geometry& g) {
 // second level's own workspace.
 struct TreeRouteLayout {
     RouteLayout L1;
-    size_t lvl1, nu, slots, bhi, blo, bnorm, lvl2, total;
+    size_t lvl1, nu, qbar, slots, bhi, blo, bnorm, lvl2, total;
     int nn, nb_pad;
 };
 
@@ -1145,7 +1156,7 @@ static Geometry tree_level1_geometry(const Geometry& g) {
 static TreeRouteLayout tree_route_layout(const Geometry& g) {
     TreeRouteLayout T{};
     const size_t nbg = (size_t)g.B * g.Hkv;
-    const size_t rows = (size_t)g.B * g.Hq * g.N;
+    const size_t rows = (size_t)g.B * g.Hq * (g.causal ? (size_t)g.N : (size_t)g.nb);
     T.nn = g.nb >> kTreeFanoutLog2;
     T.nb_pad = (g.nb + RT_CH - 1) / RT_CH * RT_CH;
     size_t off = 0;
@@ -1155,6 +1166,7 @@ static TreeRouteLayout tree_route_layout(const Geometry& g) {
         off += align_up(T.L1.total, 256);
     }
     T.nu = off;    off += align_up(nbg * (T.nn > 0 ? T.nn : 1) * kD * 4, 256);
+    T.qbar = off;  if (!g.causal) off += align_up(rows * kD * 4, 256);  // pooled queries
     T.slots = off; off += align_up(rows * (g.beam + 1) * 4, 256);
     T.bhi = off;   off += align_up(nbg * T.nb_pad * kD * 2, 256);
     T.blo = off;   off += align_up(nbg * T.nb_pad * kD * 2, 256);
@@ -1184,7 +1196,8 @@ static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
 // route_layout(g).
 static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* summ,
                              int32_t* idx, int idx_stride, int cshift, void* ws, hipStream_t s,
-                             const hipEvent_t* ev) {
+                             const hipEvent_t* ev, const float* qbar_in = nullptr,
+                             int tail_img = -1) {
     char* base = static_cast<char*>(ws);
     const RouteLayout L = route_layout(g);
     const int nbg = g.B * g.Hkv;
@@ -1193,7 +1206,9 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     a.ovf_rows = reinterpret_cast<uint32_t*>(base + L.ovf_rows);
     a.tile_count = a.ovf_count + 1;  // the word after the row count
     a.tile_queue = reinterpret_cast<uint32_t*>(base + L.tiles);
-    float* qbar = g.causal ? nullptr : reinterpret_cast<float*>(base + L.qbar);
+    float* qbar = g.causal ? nullptr
+                           : (qbar_in ? const_cast<float*>(qbar_in)
+                                      : reinterpret_cast<float*>(base + L.qbar));
     float* qsum = g.consensus ? reinterpret_cast<float*>(base + L.qsum) : nullptr;
     uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
     uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
@@ -1215,15 +1230,16 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     a.nb = g.nb;
     a.top_k = g.top_k;
     a.window = g.window;
-    a.P = g.causal ? g.N : g.nb;
+    a.P = route_P(g);
     a.tiles = (a.P + RT_ROWS - 1) / RT_ROWS;
     a.items = g.B * heads * a.tiles;
     a.nb_pad = L.nb_pad;
     a.cshift = cshift;
     a.idx_stride = idx_stride;
+    a.tail_img = tail_img;
     hipError_t e = launch_fill_u32(a.ovf_count, 2, 0u, s);  // row and tile counts
     if (e != hipSuccess) return e;
-    if (!g.causal) {
+    if (!g.causal && !qbar_in) {
         e = launch_summarize(q, qbar, g.B * g.Hq, g.N, g.bs, s);
         if (e != hipSuccess) return e;
     }
@@ -1251,41 +1267,51 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     return hipGetLastError();
 }
 
-// Two-level routing (causal, per query head).  Stage events: 2 after the
-// first level and the tail slots, 3 after the second level.
+// Two-level routing (per query head; causal rows, or pooled query blocks in
+// image mode).  Stage events: 2 after the first level and the tail slots, 3
+// after the second level.
 static hipError_t route_tree(const Geometry& g, const uint16_t* q, const float* kbar,
                              int32_t* idx, void* ws, hipStream_t s, const hipEvent_t* ev) {
     char* base = static_cast<char*>(ws);
     const TreeRouteLayout T = tree_route_layout(g);
     const int nbg = g.B * g.Hkv;
-    const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+    const int P = g.causal ? g.N : g.nb;  // rows per (b, query head)
+    const int64_t rows = (int64_t)g.B * g.Hq * P;
     const int stride = g.beam + 1;
     float* nu = reinterpret_cast<float*>(base + T.nu);
     int32_t* slots = reinterpret_cast<int32_t*>(base + T.slots);
     uint16_t* bhi = reinterpret_cast<uint16_t*>(base + T.bhi);
     uint16_t* blo = reinterpret_cast<uint16_t*>(base + T.blo);
     float* bn = reinterpret_cast<float*>(base + T.bnorm);
+    // image mode: every row's candidates are all nb blocks, so its tail is
+    // the same partial node for every row
+    const int tail_img = (T.nn << kTreeFanoutLog2) < g.nb ? T.nn : -1;
+    float* qbar = g.causal ? nullptr : reinterpret_cast<float*>(base + T.qbar);
     hipError_t e;
+    if (!g.causal) {  // pooled queries, shared by both levels
+        e = launch_summarize(q, qbar, g.B * g.Hq, g.N, g.bs, s);
+        if (e != hipSuccess) return e;
+    }
     if (T.nn > 0) {
         const int64_t n = (int64_t)nbg * T.nn * 8;
         hipLaunchKernelGGL(k_node_means, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kbar,
                            nu, g.nb, T.nn, n);
         e = route_flat(tree_level1_geometry(g), q, nu, slots, stride, kTreeFanoutLog2,
-                       base + T.lvl1, s, nullptr);
+                       base + T.lvl1, s, nullptr, qbar, tail_img);
         // the routing kernels write each row's tail slot with its beam
     } else {
         e = launch_fill_u32(reinterpret_cast<uint32_t*>(slots), (size_t)rows * stride,
                             0xFFFFFFFFu, s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_tree_tail, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
-                           slots, g.beam, rows, g.N, g.bs, g.window);
+                           slots, g.beam, rows, P, g.bs, g.window, g.causal, tail_img);
     }
     if (e != hipSuccess) return e;
     const int64_t prep_threads = (int64_t)nbg * T.nb_pad * 8;
     hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
                        kbar, bhi, blo, bn, bn + (size_t)nbg * g.nb, nbg, g.nb, T.nb_pad);
     mark(ev, 2, s);
-    e = launch_tree_level2(g, q, bhi, blo, T.nb_pad, slots, idx, base + T.lvl2, s);
+    e = launch_tree_level2(g, q, qbar, bhi, blo, T.nb_pad, slots, idx, base + T.lvl2, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

@@ -28,7 +28,8 @@ namespace lsa {
 constexpr int TR_PITCH = 72;  // LDS pitch of the staged block means (bf16)
 
 struct TreeScoreArgs {
-    const uint16_t* q;         // [B,Hq,N,64] bf16
+    const uint16_t* q;         // [B,Hq,N,64] bf16 (causal rows)
+    const float* qbar;         // [B*Hq*nb][64] fp32 pooled queries (image-mode rows)
     const uint16_t* bhi;       // block means, bf16 hi part [B*Hkv][nb_pad][64]
     const uint16_t* blo;       // bf16 lo part
     const uint32_t* pairs;     // pair ids in node order
@@ -44,6 +45,7 @@ struct TreeScoreArgs {
 // owns pairs 16w..16w+15 of a unit.  Tiles D = Kbar_node . Q^T: lane l holds
 // pair l%16 and blocks 4(l/16)+r, i.e. 16 contiguous bytes of the pair's
 // 64-byte score row.
+template <bool QF32>
 __global__ __launch_bounds__(256, 4) void k_tree_score(TreeScoreArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_h[kTreeFanout * TR_PITCH];
     __shared__ __attribute__((aligned(16))) __bf16 s_l[kTreeFanout * TR_PITCH];
@@ -65,9 +67,29 @@ __global__ __launch_bounds__(256, 4) void k_tree_score(TreeScoreArgs a) {
         // end use pair 0 and store to a dummy row
         const bool valid = p0 + my < p1;
         const uint32_t pid = a.pairs[valid ? p0 + my : 0u];
-        const uint16_t* qrow = a.q + (int64_t)(pid >> a.sp_log2) * kD + 8 * (lane >> 4);
-        const bf16x8 b0 = load_bf16x8(qrow);
-        const bf16x8 b1 = load_bf16x8(qrow + 32);
+        // the query as the B operand: dims 8(l/16) .. +7 and 32 + 8(l/16) .. +7;
+        // an fp32 query is split into bf16 hi + lo parts
+        bf16x8 b0, b1, b0l, b1l;
+        if constexpr (QF32) {
+            const float* qrow = a.qbar + (int64_t)(pid >> a.sp_log2) * kD + 8 * (lane >> 4);
+#pragma unroll
+            for (int hblk = 0; hblk < 2; ++hblk) {
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(qrow + 32 * hblk);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(qrow + 32 * hblk + 4);
+                const float f[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    hi[i] = (__bf16)f[i];
+                    lo[i] = (__bf16)(f[i] - (float)hi[i]);
+                }
+                if (hblk == 0) { b0 = hi; b0l = lo; } else { b1 = hi; b1l = lo; }
+            }
+        } else {
+            const uint16_t* qrow = a.q + (int64_t)(pid >> a.sp_log2) * kD + 8 * (lane >> 4);
+            b0 = load_bf16x8(qrow);
+            b1 = load_bf16x8(qrow + 32);
+        }
         if (cur.bucket != loaded) {
             __syncthreads();
             const int bg = cur.bucket / a.nodes, node = cur.bucket - bg * a.nodes;
@@ -86,6 +108,10 @@ __global__ __launch_bounds__(256, 4) void k_tree_score(TreeScoreArgs a) {
         acc = mfma16(*reinterpret_cast<const bf16x8*>(s_l + ar * TR_PITCH + ak), b0, acc);
         acc = mfma16(*reinterpret_cast<const bf16x8*>(s_h + ar * TR_PITCH + 32 + ak), b1, acc);
         acc = mfma16(*reinterpret_cast<const bf16x8*>(s_l + ar * TR_PITCH + 32 + ak), b1, acc);
+        if constexpr (QF32) {  // q_lo . k_hi: with the two above, fp32-accurate
+            acc = mfma16(*reinterpret_cast<const bf16x8*>(s_h + ar * TR_PITCH + ak), b0l, acc);
+            acc = mfma16(*reinterpret_cast<const bf16x8*>(s_h + ar * TR_PITCH + 32 + ak), b1l, acc);
+        }
         const uint32_t pos = valid ? p0 + my : a.dummy_pos + my;
         *reinterpret_cast<f32x4*>(a.scores + (int64_t)pos * kTreeFanout + 4 * (lane >> 4)) = acc;
     }
@@ -97,7 +123,8 @@ struct TreeSelectArgs {
     const float* scores;   // [npairs][16] by position
     int32_t* idx;          // [rows][top_k]
     int64_t rows;
-    int N, bs, window, top_k, beam;
+    int N, bs, window, top_k, beam;  // N: rows per (b, head) (image mode: query blocks)
+    int causal, nb;                  // image mode: every row's candidates are all nb blocks
 };
 
 // Compare-exchange toward descending order.
@@ -134,7 +161,7 @@ __global__ __launch_bounds__(256) void k_tree_select(TreeSelectArgs a) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (row >= a.rows) return;
     const int t = (int)(row % a.N);
-    const int E = eligible_blocks(t, a.bs, a.window);
+    const int E = a.causal ? eligible_blocks(t, a.bs, a.window) : a.nb;
     const int stride = a.beam + 1;
     uint64_t L[kTreeFanout];
 #pragma unroll
@@ -215,7 +242,7 @@ static TreeLayout tree_layout(const Geometry& g) {
     TreeLayout L{};
     L.nodes = (g.nb + kTreeFanout - 1) / kTreeFanout;
     L.NB = g.B * g.Hkv * L.nodes;
-    const size_t rows = (size_t)g.B * g.Hq * g.N;
+    const size_t rows = (size_t)g.B * g.Hq * (g.causal ? (size_t)g.N : (size_t)g.nb);
     const size_t slots = (size_t)g.beam + 1;
     size_t off = 0;
     L.counts = off;   off += align_up(((size_t)L.NB + 1) * 4, 256);
@@ -231,9 +258,9 @@ static TreeLayout tree_layout(const Geometry& g) {
 
 size_t tree_level2_bytes(const Geometry& g) { return tree_layout(g).total; }
 
-hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16_t* bhi,
-                              const uint16_t* blo, int nb_pad, const int32_t* slots, int32_t* idx,
-                              void* ws, hipStream_t s) {
+hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const float* qbar,
+                              const uint16_t* bhi, const uint16_t* blo, int nb_pad,
+                              const int32_t* slots, int32_t* idx, void* ws, hipStream_t s) {
     const TreeLayout L = tree_layout(g);
     char* base = static_cast<char*>(ws);
     uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
@@ -245,7 +272,8 @@ hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16
     float* scores = reinterpret_cast<float*>(base + L.scores);
     const int nslots = g.beam + 1;
     const int sp_log2 = pair_stride_log2(nslots);
-    const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+    const int P = g.causal ? g.N : g.nb;  // rows per (b, query head)
+    const int64_t rows = (int64_t)g.B * g.Hq * P;
     const int nbg = g.B * g.Hkv;
 
     hipError_t e = launch_fill_u32(counts, (size_t)L.NB, 0u, s);
@@ -254,10 +282,11 @@ hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16
     int64_t tc = std::max<int64_t>(
         (4096 + rep - 1) / rep,
         (4 * (int64_t)L.nodes + (int64_t)rep * nslots - 1) / ((int64_t)rep * nslots));
-    tc = std::min<int64_t>((tc + 63) / 64 * 64, g.N);
-    BucketArgs ba{slots, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, g.N, g.bs, L.nodes, nslots,
+    tc = std::min<int64_t>((tc + 63) / 64 * 64, P);
+    BucketArgs ba{slots, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, P, g.bs, L.nodes, nslots,
                   g.window, (int)tc, sp_log2, 0, kTreeFanoutLog2};
-    const int nch = (int)((g.N + tc - 1) / tc);
+    if (!g.causal) ba.fixed_cand = L.nodes;  // every query block may open every node
+    const int nch = (int)((P + tc - 1) / tc);
     const dim3 bgrid((unsigned)(nbg * nch));
     const size_t lds = L.nodes <= BK_LDS_MAX ? (size_t)L.nodes * 4 : 0;
     hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
@@ -265,13 +294,20 @@ hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const uint16
                        L.NB);
     hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
 
-    TreeScoreArgs sa{q, bhi, blo, pairs, offsets, unit_off, scores,
+    TreeScoreArgs sa{q, qbar, bhi, blo, pairs, offsets, unit_off, scores,
                      (uint32_t)(rows * nslots), L.nodes, L.NB, nb_pad, sp_log2};
-    static std::atomic<int> cache[kMaxDevices];
-    const int grid = resident_grid(k_tree_score, 256, cache);
-    hipLaunchKernelGGL(k_tree_score, dim3(grid), dim3(256), 0, s, sa);
+    if (g.causal) {
+        static std::atomic<int> cache[kMaxDevices];
+        const int grid = resident_grid(k_tree_score<false>, 256, cache);
+        hipLaunchKernelGGL(k_tree_score<false>, dim3(grid), dim3(256), 0, s, sa);
+    } else {
+        static std::atomic<int> cache[kMaxDevices];
+        const int grid = resident_grid(k_tree_score<true>, 256, cache);
+        hipLaunchKernelGGL(k_tree_score<true>, dim3(grid), dim3(256), 0, s, sa);
+    }
 
-    TreeSelectArgs ta{slots, rev, scores, idx, rows, g.N, g.bs, g.window, g.top_k, g.beam};
+    TreeSelectArgs ta{slots, rev, scores, idx, rows, P, g.bs, g.window, g.top_k, g.beam,
+                      g.causal, g.nb};
     hipLaunchKernelGGL(k_tree_select, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, ta);
     return hipGetLastError();
 }

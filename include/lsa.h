@@ -67,9 +67,9 @@ typedef struct lsa_params {
     float beta;        /* second-cumulant weight of the routing score (see
                           lsa_route_cumulant); 0: the block-mean score.  Must be
                           finite; nonzero needs causal = 1 and consensus = 0 */
-    int32_t beam;      /* two-level routing: nodes kept per query (see
-                          lsa_route_topk); 0: flat routing.  1..15, needs
-                          causal = 1, consensus = 0 and beta = 0 */
+    int32_t beam;      /* two-level routing: nodes kept per query or query
+                          block (see lsa_route_topk); 0: flat routing.
+                          1..15, needs consensus = 0 and beta = 0 */
     int32_t chunk;     /* causal attention: query positions per chunk (see
                           lsa_sparse_attend); 0 chooses it from the geometry,
                           otherwise a power of two >= 64.  Results do not
@@ -139,7 +139,10 @@ lsa_status lsa_block_summarize(const lsa_params *p, const void *x, int32_t heads
  *   nodes plus the tail blocks [16 S, E(t)) of the incomplete node.  With
  *   beam >= S every candidate is scored and the result is the flat
  *   selection.  Routing work per row falls from E(t) to about
- *   E(t)/16 + 16 beam + 15 scores.
+ *   E(t)/16 + 16 beam + 15 scores.  In image mode (LLSA page, "Minimum
+ *   Usage": the two-level kernel for 16384 tokens and more) the rows are
+ *   the pooled query blocks and every row's candidates are all N/bs key
+ *   blocks: S = floor(N/bs/16) nodes and the tail [16 S, N/bs).
  * beta != 0 is LSA_ERR_UNSUPPORTED here: that score needs the keys
  * themselves (lsa_route_cumulant).
  * Diagnostic: after a call with beam = 0 has run, the workspace's first

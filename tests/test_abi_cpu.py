@@ -60,7 +60,7 @@ def good(lsa, **kw):
     (dict(beta=float("inf")), 2), (dict(beta=0.5, consensus=1), 3),
     (dict(beta=0.5, causal=0, window=0, block=16), 3), (dict(beam=-1), 2), (dict(beam=16), 3),
     (dict(beam=4, consensus=1), 3), (dict(beam=4, beta=0.5), 3),
-    (dict(beam=4, causal=0, window=0, block=16), 3),
+    (dict(beam=4, causal=0, window=0, block=16, consensus=1), 3),
     (dict(chunk=-64), 2), (dict(chunk=32), 2), (dict(chunk=96), 2),
     (dict(head_dim=128), 3), (dict(top_k=17), 3), (dict(block=48, window=96, seq_len=960), 3),
     (dict(causal=0, window=0, block=64), 3), (dict(seq_len=1 << 24, block=16, window=512), 3),
@@ -200,3 +200,18 @@ def test_noalloc_decode_argument_checks(lsa):
     assert L.lsa_workspace_bytes(ctypes.byref(big), lsa.OP_DECODE) > lsa.STATIC_SCRATCH_BYTES
     assert L.lsa_decode_noalloc(ctypes.byref(big), 1 << 20, a, a, a, a, a, None, None) == 7
     assert L.lsa_status_str(7).decode().startswith("needs more scratch")
+
+
+def test_image_tree_routing_workspace(lsa):
+    """Image-mode two-level routing is accepted: its rows are query blocks,
+    so its slot lists and pair tables scale with B * Hq * N / 16."""
+    L = lsa.library()
+    flat = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0)
+    tree = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0, beam=8)
+    wf = L.lsa_workspace_bytes(ctypes.byref(flat), lsa.OP_ROUTE)
+    wt = L.lsa_workspace_bytes(ctypes.byref(tree), lsa.OP_ROUTE)
+    assert wf != lsa.SIZE_MAX and wt != lsa.SIZE_MAX
+    qblocks = 4 * 16 * 1024
+    # slots, pair ids, positions (9 words each) and 9 score rows of 64 bytes per query block
+    assert wt >= qblocks * 9 * (4 + 4 + 4 + 64)
+    assert wt < qblocks * 9 * (4 + 4 + 4 + 64) + 3 * wf + (64 << 20)
