@@ -198,6 +198,15 @@ static lsa_status forward_impl(const lsa_params* p, const void* q, const void* k
         if (st != LSA_OK) return st;
         lsa::mark(ev, 2, s);
         lsa::mark(ev, 3, s);
+    } else if (g.beam == 0) {
+        // flat routing: the key summary also prepares the router's inputs
+        st = from_hip(lsa::launch_summary_and_route_prep(g, static_cast<const uint16_t*>(k), kbar,
+                                                         rest, s));
+        if (st != LSA_OK) return st;
+        lsa::mark(ev, 1, s);
+        st = from_hip(lsa::launch_route_prepared(g, static_cast<const uint16_t*>(q), kbar, idx,
+                                                 rest, s, ev));
+        if (st != LSA_OK) return st;
     } else {
         st = from_hip(lsa::launch_summarize(static_cast<const uint16_t*>(k), kbar, g.B * g.Hkv,
                                             g.N, g.bs, s));

@@ -88,6 +88,44 @@ __device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, in
     return mask;
 }
 
+// ---------------------------------------------------------------- routing preparation
+// The routing kernels read block means as bf16 hi + lo parts (hi = bf16(x),
+// lo = bf16(x - hi)) and bound their error with the largest norms |x| and
+// |lo| over each chunk of 32 blocks.  One lane holds 8 dims of a row; the
+// row's 8 lanes are consecutive.  Writes the row's hi and lo parts and
+// returns its norms (the same in all 8 lanes).
+constexpr int kChunkMaxStride = 32;  // floats between chunk maxima: one 128-byte line each
+
+__device__ __forceinline__ void route_split_store(const float (&f)[8], uint16_t* hi_dst,
+                                                  uint16_t* lo_dst, float& kn, float& ln) {
+    bf16x8 hi, lo;
+    float k2 = 0.f, l2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        hi[i] = (__bf16)f[i];
+        lo[i] = (__bf16)(f[i] - (float)hi[i]);
+        const float lf = (float)lo[i];
+        k2 = fmaf(f[i], f[i], k2);
+        l2 = fmaf(lf, lf, l2);
+    }
+    *reinterpret_cast<bf16x8*>(hi_dst) = hi;
+    *reinterpret_cast<bf16x8*>(lo_dst) = lo;
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+        k2 += __shfl_xor(k2, m, 64);
+        l2 += __shfl_xor(l2, m, 64);
+    }
+    kn = sqrtf(k2);
+    ln = sqrtf(l2);
+}
+
+// Maximum over the wave of a non-negative float (its bits order as integers).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+    return x;
+}
+
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, kWave));

@@ -59,8 +59,8 @@ struct RouteArgs {
     const float* kbar;    // [B,Hkv,nb,64]
     const uint16_t* khi;  // bf16 hi part of kbar [B*Hkv][nb_pad][64]
     const uint16_t* klo;  // bf16 lo part (kbar - hi) [B*Hkv][nb_pad][64]
-    const float* pk;      // prefix max over c of |kbar_c| [B*Hkv][nb]
-    const float* plo;     // prefix max over c of |lo_c| [B*Hkv][nb]
+    const float* ckn;     // per chunk of RT_CH blocks: max over its blocks of |kbar_c| [B*Hkv][ncb]
+    const float* clo;     // the same for |lo_c| (lo = kbar - hi) [B*Hkv][ncb]
     int32_t* idx;         // [B,Hq,P,top_k] (Hq = routed heads: Hkv with consensus)
     uint32_t* ovf_count;  // queued overflow rows
     uint32_t* ovf_rows;   // [B*Hq*P]
@@ -71,6 +71,7 @@ struct RouteArgs {
     int tiles;   // ceil(P / RT_ROWS)
     int items;   // B * Hq * tiles
     int nb_pad;  // nb rounded up to a multiple of RT_CH
+    int ncb;     // nb_pad / RT_CH
     int cshift;      // causal candidates are E(t) >> cshift (two-level routing: nodes of 16 blocks)
     int idx_stride;  // idx row stride (>= top_k)
     int tail_img;    // image-mode two-level routing: every row's tail node (-1: none)
@@ -234,70 +235,44 @@ __device__ __forceinline__ int tail_node(int t, int bs, int window) {
 
 // ------------------------------------------------------------ preparation
 // One thread per (block row, 8 dims): bf16 hi/lo split of the block means
-// (rows padded to a multiple of 32 with zeros) and the row norms.
+// (rows padded to a multiple of 32 with zeros), and per chunk of 32 rows
+// (one workgroup) the largest norms |kbar_c| and |lo_c| of its valid rows.
 __global__ __launch_bounds__(256) void k_route_prep(const float* __restrict__ kbar,
                                                     uint16_t* __restrict__ khi,
                                                     uint16_t* __restrict__ klo,
-                                                    float* __restrict__ kn,
-                                                    float* __restrict__ lon, int n_bg, int nb,
+                                                    float* __restrict__ ckn,
+                                                    float* __restrict__ clo, int n_bg, int nb,
                                                     int nb_pad) {
+    __shared__ float s_n[2][4];
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gid >> 3;  // over n_bg * nb_pad rows
-    if (row >= (int64_t)n_bg * nb_pad) return;
+    const int64_t row = gid >> 3;  // over n_bg * nb_pad rows: 32 per workgroup, one chunk
+    const bool in = row < (int64_t)n_bg * nb_pad;
     const int bg = (int)(row / nb_pad), c = (int)(row - (int64_t)bg * nb_pad);
     const int d0 = (threadIdx.x & 7) * 8;
     float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (c < nb) {
+    if (in && c < nb) {
         const float* src = kbar + ((int64_t)bg * nb + c) * kD + d0;
         const f32x4 a = *reinterpret_cast<const f32x4*>(src);
         const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
         f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
         f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
     }
-    bf16x8 hi, lo;
-    float k2 = 0.f, l2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        hi[i] = (__bf16)f[i];
-        lo[i] = (__bf16)(f[i] - (float)hi[i]);
-        const float lf = (float)lo[i];
-        k2 = fmaf(f[i], f[i], k2);
-        l2 = fmaf(lf, lf, l2);
+    float kn = 0.f, ln = 0.f;
+    if (in) route_split_store(f, khi + row * kD + d0, klo + row * kD + d0, kn, ln);
+    kn = wave_max_nonneg(in ? kn : 0.f);  // padding rows hold zeros
+    ln = wave_max_nonneg(in ? ln : 0.f);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        s_n[0][w] = kn;
+        s_n[1][w] = ln;
     }
-    *reinterpret_cast<bf16x8*>(khi + row * kD + d0) = hi;
-    *reinterpret_cast<bf16x8*>(klo + row * kD + d0) = lo;
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-        k2 += __shfl_xor(k2, m, kWave);
-        l2 += __shfl_xor(l2, m, kWave);
-    }
-    if ((threadIdx.x & 7) == 0 && c < nb) {
-        kn[(int64_t)bg * nb + c] = sqrtf(k2);
-        lon[(int64_t)bg * nb + c] = sqrtf(l2);
-    }
-}
-
-// In-place prefix maximum of rows of length n (one workgroup per row).
-__global__ __launch_bounds__(1024) void k_prefix_max(float* __restrict__ x, int n) {
-    __shared__ float s[1024];
-    float* row = x + (int64_t)blockIdx.x * n;
-    const int tid = threadIdx.x;
-    const int per = (n + 1023) / 1024;
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
-    float m = 0.f;  // norms are >= 0
-    for (int i = lo; i < hi; ++i) m = fmaxf(m, row[i]);
-    s[tid] = m;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const float o = tid >= off ? s[tid - off] : 0.f;
-        __syncthreads();
-        s[tid] = fmaxf(s[tid], o);
-        __syncthreads();
-    }
-    float run = tid > 0 ? s[tid - 1] : 0.f;
-    for (int i = lo; i < hi; ++i) {
-        run = fmaxf(run, row[i]);
-        row[i] = run;
+    if (threadIdx.x == 0 && (int64_t)blockIdx.x * 32 < (int64_t)n_bg * nb_pad) {
+        const int64_t chunk = (int64_t)blockIdx.x;  // = bg * (nb_pad / 32) + c / 32
+        ckn[chunk * kChunkMaxStride] =
+            fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3]));
+        clo[chunk * kChunkMaxStride] =
+            fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3]));
     }
 }
 
@@ -327,6 +302,27 @@ __device__ __forceinline__ int clamp_i32(int x, int lo, int hi) {
     int r;
     asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(lo), "v"(hi));
     return r;
+}
+
+// ------------------------------------------------------------ wave maxima
+// Largest 32-bit value of the wave, in every lane: quad swaps, the half-row
+// and row mirrors (DPP, folded into the max), then the 16- and 32-lane
+// swaps, all in registers.
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t x) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+    return o > x ? o : x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max_dpp_u32<0xB1>(x);   // quad_perm(1,0,3,2): lane ^ 1
+    x = max_dpp_u32<0x4E>(x);   // quad_perm(2,3,0,1): lane ^ 2
+    x = max_dpp_u32<0x141>(x);  // row_half_mirror: the other quad of the 8
+    x = max_dpp_u32<0x140>(x);  // row_mirror: the other 8 of the row
+    // each swap leaves a lane its own value and its partner's, in some order
+    const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = s16[0] > s16[1] ? s16[0] : s16[1];
+    const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return s32[0] > s32[1] ? s32[0] : s32[1];
 }
 
 // ------------------------------------------------------------ main kernel
@@ -383,8 +379,20 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     const int Ewg = row_candidates(CAUSAL, wg_last, P, a.bs, a.window, a.nb, a.cshift);  // loop bound
     const int Emin =
         (r0 + 31 < P) ? row_candidates(CAUSAL, r0, P, a.bs, a.window, a.nb, a.cshift) : 0;
-    const float kn_max = Emax > 0 ? a.pk[(int64_t)bg * a.nb + Emax - 1] : 0.f;
-    const float lo_max = Emax > 0 ? a.plo[(int64_t)bg * a.nb + Emax - 1] : 0.f;
+    // the largest |kbar_c| and |lo_c| over the wave's candidates (chunk
+    // maxima over c < Emax, rounded up to whole chunks); requested now,
+    // reduced after pass 1
+    uint32_t kn_bits = 0u, lo_bits = 0u;  // norms are >= 0: their bits order as integers
+    if constexpr (!EXACT) {
+        const int nc = (Emax + RT_CH - 1) / RT_CH;
+        for (int i = lane; i < nc; i += 64) {
+            const int64_t e = ((int64_t)bg * a.ncb + i) * kChunkMaxStride;
+            const uint32_t kb = __float_as_uint(a.ckn[e]);
+            const uint32_t lb = __float_as_uint(a.clo[e]);
+            kn_bits = kb > kn_bits ? kb : kn_bits;
+            lo_bits = lb > lo_bits ? lb : lo_bits;
+        }
+    }
 
     // ---- the query as the B operand (B[d][t] = Q[t][d]): lane holds dims
     // 8*half + 16*ks .. +7 of row rq.
@@ -495,6 +503,8 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     // |q_hi . k_lo| + |q_lo . k_hi| + fp32 accumulation error.
     float theta = -INFINITY;
     if constexpr (!EXACT) {
+        const float kn_max = __uint_as_float(wave_max_u32(kn_bits));
+        const float lo_max = __uint_as_float(wave_max_u32(lo_bits));
         const float th = kth_largest_top2_pair(m1, m2, a.top_k);
         const float delta = 1.0625f * (qn * lo_max + qln * kn_max) + 6.2e-5f * (qn + qln) * kn_max;
         theta = th - delta;  // -inf stays -inf
@@ -679,26 +689,6 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
 }
 
 // ------------------------------------------------------------ exact fallback
-// Largest 32-bit value of the wave, in every lane: quad swaps, the half-row
-// and row mirrors (DPP, folded into the max), then the 16- and 32-lane
-// swaps, all in registers.
-template <int CTRL>
-__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t x) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-    return o > x ? o : x;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-    x = max_dpp_u32<0xB1>(x);   // quad_perm(1,0,3,2): lane ^ 1
-    x = max_dpp_u32<0x4E>(x);   // quad_perm(2,3,0,1): lane ^ 2
-    x = max_dpp_u32<0x141>(x);  // row_half_mirror: the other quad of the 8
-    x = max_dpp_u32<0x140>(x);  // row_mirror: the other 8 of the row
-    // each swap leaves a lane its own value and its partner's, in some order
-    const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = s16[0] > s16[1] ? s16[0] : s16[1];
-    const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return s32[0] > s32[1] ? s32[0] : s32[1];
-}
-
 // The wave's kMaxTopK largest keys, descending (0 past the last), from
 // per-lane lists sorted descending; the lists are consumed.  Rank r takes the
 // largest score word over the lanes' heads, then the largest id word among
@@ -1115,23 +1105,30 @@ static size_t route_items(const Geometry& g) {
     return (size_t)g.B * route_heads(g) * ((P + RT_ROWS - 1) / RT_ROWS);
 }
 
+// The workspace starts with the words the router clears before each call:
+// the two overflow counters (in the first 256 bytes) and the chunk maxima of
+// the block-mean norms; one fill covers them.
 struct RouteLayout {
-    size_t ovf_rows, tiles, qbar, qsum, khi, klo, pk, total;
-    int nb_pad;
+    size_t cmax, ovf_rows, tiles, qbar, qsum, khi, klo, total;
+    size_t fill_words;  // words cleared from the start of the workspace
+    int nb_pad, ncb;
 };
 
 static RouteLayout route_layout(const Geometry& g) {
     RouteLayout L{};
     L.nb_pad = (g.nb + RT_CH - 1) / RT_CH * RT_CH;
+    L.ncb = L.nb_pad / RT_CH;
     const size_t nbg = (size_t)g.B * g.Hkv;
-    size_t off = 256;  // overflow counter
+    size_t off = 256;  // overflow counters
+    L.cmax = off;     off += align_up(2 * nbg * L.ncb * kChunkMaxStride * 4, 256);  // norms, then lo
+    L.fill_words = off / 4;
     L.ovf_rows = off; off += align_up(route_rows(g) * 4, 256);
     L.tiles = off;    off += align_up(route_items(g) * 4, 256);
     L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * route_P(g) * kD * 4, 256);
     L.qsum = off;     if (g.consensus) off += align_up(route_rows(g) * kD * 4, 256);
     L.khi = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
     L.klo = off;      off += align_up(nbg * L.nb_pad * kD * 2, 256);
-    L.pk = off;       off += align_up(2 * nbg * g.nb * 4, 256);  // pk then plo
+
     L.total = off;
     return L;
 }
@@ -1170,7 +1167,8 @@ static TreeRouteLayout tree_route_layout(const Geometry& g) {
     T.slots = off; off += align_up(rows * (g.beam + 1) * 4, 256);
     T.bhi = off;   off += align_up(nbg * T.nb_pad * kD * 2, 256);
     T.blo = off;   off += align_up(nbg * T.nb_pad * kD * 2, 256);
-    T.bnorm = off; off += align_up(2 * nbg * g.nb * 4, 256);
+    T.bnorm = off;  // chunk maxima of the block-mean norms (unused by the second level)
+    off += align_up(2 * nbg * (T.nb_pad / RT_CH) * kChunkMaxStride * 4, 256);
     T.lvl2 = off;  off += tree_level2_bytes(g);
     T.total = off;
     return T;
@@ -1197,7 +1195,7 @@ static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
 static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* summ,
                              int32_t* idx, int idx_stride, int cshift, void* ws, hipStream_t s,
                              const hipEvent_t* ev, const float* qbar_in = nullptr,
-                             int tail_img = -1) {
+                             int tail_img = -1, bool prepared = false) {
     char* base = static_cast<char*>(ws);
     const RouteLayout L = route_layout(g);
     const int nbg = g.B * g.Hkv;
@@ -1212,16 +1210,16 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     float* qsum = g.consensus ? reinterpret_cast<float*>(base + L.qsum) : nullptr;
     uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
     uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
-    float* pk = reinterpret_cast<float*>(base + L.pk);
-    float* plo = pk + (size_t)nbg * g.nb;
+    float* ckn = reinterpret_cast<float*>(base + L.cmax);
+    float* clo = ckn + (size_t)nbg * L.ncb * kChunkMaxStride;
     const int heads = route_heads(g);
     a.q = q;
     a.qbar = g.consensus ? qsum : qbar;
     a.kbar = summ;
     a.khi = khi;
     a.klo = klo;
-    a.pk = pk;
-    a.plo = plo;
+    a.ckn = ckn;
+    a.clo = clo;
     a.idx = idx;
     a.Hq = heads;  // rows of the router: (b, routed head, position)
     a.Hkv = g.Hkv;
@@ -1234,11 +1232,15 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     a.tiles = (a.P + RT_ROWS - 1) / RT_ROWS;
     a.items = g.B * heads * a.tiles;
     a.nb_pad = L.nb_pad;
+    a.ncb = L.ncb;
     a.cshift = cshift;
     a.idx_stride = idx_stride;
     a.tail_img = tail_img;
-    hipError_t e = launch_fill_u32(a.ovf_count, 2, 0u, s);  // row and tile counts
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!prepared) {  // the counters (prepared: cleared by the caller, with the norm maxima)
+        e = launch_fill_u32(a.ovf_count, 64, 0u, s);
+        if (e != hipSuccess) return e;
+    }
     if (!g.causal && !qbar_in) {
         e = launch_summarize(q, qbar, g.B * g.Hq, g.N, g.bs, s);
         if (e != hipSuccess) return e;
@@ -1253,10 +1255,11 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
             hipLaunchKernelGGL(k_group_query<float>, gq, dim3(256), 0, s, qbar, qsum, g.Hq, g.Hkv,
                                a.P, n);
     }
-    const int64_t prep_threads = (int64_t)nbg * L.nb_pad * 8;
-    hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
-                       summ, khi, klo, pk, plo, nbg, g.nb, L.nb_pad);
-    hipLaunchKernelGGL(k_prefix_max, dim3((unsigned)(2 * nbg)), dim3(1024), 0, s, pk, g.nb);
+    if (!prepared) {
+        const int64_t prep_threads = (int64_t)nbg * L.nb_pad * 8;
+        hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256),
+                           0, s, summ, khi, klo, ckn, clo, nbg, g.nb, L.nb_pad);
+    }
     const dim3 grid((unsigned)(((int64_t)a.items + 7) / 8 * 8));  // a multiple of the XCD count
     if (g.causal && !g.consensus)
         launch_route_kernels<true, false>(a, grid, s, ev);
@@ -1309,11 +1312,33 @@ static hipError_t route_tree(const Geometry& g, const uint16_t* q, const float* 
     if (e != hipSuccess) return e;
     const int64_t prep_threads = (int64_t)nbg * T.nb_pad * 8;
     hipLaunchKernelGGL(k_route_prep, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, s,
-                       kbar, bhi, blo, bn, bn + (size_t)nbg * g.nb, nbg, g.nb, T.nb_pad);
+                       kbar, bhi, blo, bn, bn + (size_t)nbg * (T.nb_pad / RT_CH) * kChunkMaxStride,
+                       nbg, g.nb, T.nb_pad);
     mark(ev, 2, s);
     e = launch_tree_level2(g, q, qbar, bhi, blo, T.nb_pad, slots, idx, base + T.lvl2, s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
+}
+
+hipError_t launch_summary_and_route_prep(const Geometry& g, const uint16_t* k, float* kbar,
+                                         void* ws, hipStream_t s) {
+    const RouteLayout L = route_layout(g);
+    char* base = static_cast<char*>(ws);
+    const size_t nbg = (size_t)g.B * g.Hkv;
+    float* ckn = reinterpret_cast<float*>(base + L.cmax);
+    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(base), L.fill_words, 0u, s);
+    if (e != hipSuccess) return e;
+    return launch_summarize_route(k, kbar, g.B * g.Hkv, g.N, g.bs,
+                                  reinterpret_cast<uint16_t*>(base + L.khi),
+                                  reinterpret_cast<uint16_t*>(base + L.klo), ckn,
+                                  ckn + nbg * L.ncb * kChunkMaxStride, L.nb_pad, s);
+}
+
+hipError_t launch_route_prepared(const Geometry& g, const uint16_t* q, const float* kbar,
+                                 int32_t* idx, void* ws, hipStream_t s, const hipEvent_t* ev) {
+    hipError_t e = route_flat(g, q, kbar, idx, g.top_k, 0, ws, s, ev, nullptr, -1, true);
+    mark(ev, 3, s);
+    return e;
 }
 
 hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar, int32_t* idx,

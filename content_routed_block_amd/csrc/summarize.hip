@@ -13,85 +13,179 @@
 
 namespace lsa {
 
+// With RouteOut (the layer's key summary feeding its own routing), the
+// summary kernels also write the routing kernels' inputs: the bf16 hi/lo
+// split of each block mean into rows of nb_pad per head (rows past nb
+// zero), and per chunk of 32 rows the largest norms |mean| and |lo| of its
+// rows (route_split_store).
+struct RouteOut {
+    uint16_t* khi;
+    uint16_t* klo;
+    float* ckn;    // chunk maxima, kChunkMaxStride floats apart
+    float* clo;
+    int nb_pad;
+};
+
 // Blocks of 16 tokens: a lane owns 8 dims of one block and sums its 16 rows
 // itself (eight blocks per wave), so no cross-lane reduction is needed; a
 // load instruction still reads whole 128-byte rows (eight lanes per row).
+// With PREP, rows run over heads x nb_pad, so a workgroup (32 rows) is one
+// chunk and stores its maxima itself.
+template <bool PREP>
 __global__ __launch_bounds__(256) void k_summarize16(const uint16_t* __restrict__ x,
                                                      float* __restrict__ xbar,
-                                                     int64_t n_blocks) {
+                                                     int64_t n_blocks, int nb, RouteOut ro) {
+    __shared__ float s_n[2][4];
     const int lane = threadIdx.x & 63;
-    const int64_t blk = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
-    if (blk >= n_blocks) return;
+    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
     const int dg = lane & 7;  // dims 8*dg .. 8*dg+7
-    // blocks are consecutive runs of 16 tokens, so block blk starts at row 16*blk
-    const uint16_t* base = x + blk * 16 * kD + dg * 8;
-    u32x4 v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * kD);
-    double acc[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[d] = 0.0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float f[8];
-        unpack8(v[i], f);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
+    int64_t blk = r;          // the block summarised (PREP: row r of the padded layout)
+    bool have = r < n_blocks;
+    if (PREP) {
+        const int64_t bh = r / ro.nb_pad;
+        const int c = (int)(r - bh * ro.nb_pad);
+        blk = bh * nb + c;
+        have = bh * nb < n_blocks && c < nb;
+        if (bh * nb < n_blocks && c >= nb) {  // padding row
+            const int64_t o = r * kD + dg * 8;
+            *reinterpret_cast<u32x4*>(ro.khi + o) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(ro.klo + o) = u32x4{0u, 0u, 0u, 0u};
+        }
     }
-    constexpr double inv = 1.0 / 16.0;
-    f32x4 lo, hi;
+    float kn = 0.f, ln = 0.f;
+    if (have) {
+        // blocks are consecutive runs of 16 tokens, so block blk starts at row 16*blk
+        const uint16_t* base = x + blk * 16 * kD + dg * 8;
+        u32x4 v[16];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        lo[d] = (float)(acc[d] * inv);
-        hi[d] = (float)(acc[4 + d] * inv);
-    }
-    float* o = xbar + blk * kD + dg * 8;
-    *reinterpret_cast<f32x4*>(o) = lo;
-    *reinterpret_cast<f32x4*>(o + 4) = hi;
-}
-
-template <int BS>
-__global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ x,
-                                                   float* __restrict__ xbar,
-                                                   int64_t n_blocks, int N) {
-    constexpr int LOADS = BS / 8;  // 16-byte loads per lane, all issued before any use
-    const int lane = threadIdx.x & 63;
-    const int64_t wblk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wblk >= n_blocks) return;
-    const int nb = N / BS;
-    const int64_t bh = wblk / nb;
-    const int64_t c = wblk - bh * nb;
-    const int dg = lane & 7;   // dims 8*dg .. 8*dg+7
-    const int j0 = lane >> 3;  // tokens j0, j0+8, ...
-    const uint16_t* base = x + (bh * N + c * BS + j0) * kD + dg * 8;
-    u32x4 v[LOADS];
+        for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * kD);
+        double acc[8];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * 8 * kD);
-    double acc[8];
+        for (int d = 0; d < 8; ++d) acc[d] = 0.0;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[d] = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            float f[8];
+            unpack8(v[i], f);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        float f[8];
-        unpack8(v[i], f);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
-    }
-#pragma unroll
-    for (int m = 8; m < 64; m <<= 1)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] += __shfl_xor(acc[d], m, kWave);
-    if (j0 == 0) {
-        constexpr double inv = 1.0 / (double)BS;  // a power of two: exact
+            for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
+        }
+        constexpr double inv = 1.0 / 16.0;
         f32x4 lo, hi;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             lo[d] = (float)(acc[d] * inv);
             hi[d] = (float)(acc[4 + d] * inv);
         }
-        float* o = xbar + wblk * kD + dg * 8;
+        float* o = xbar + blk * kD + dg * 8;
         *reinterpret_cast<f32x4*>(o) = lo;
         *reinterpret_cast<f32x4*>(o + 4) = hi;
+        if (PREP) {
+            const float f[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            route_split_store(f, ro.khi + r * kD + dg * 8, ro.klo + r * kD + dg * 8, kn, ln);
+        }
+    }
+    if (!PREP) return;
+    kn = wave_max_nonneg(kn);
+    ln = wave_max_nonneg(ln);
+    const int w = threadIdx.x >> 6;
+    if (lane == 0) {
+        s_n[0][w] = kn;
+        s_n[1][w] = ln;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int64_t r0 = (int64_t)blockIdx.x * 32;  // this workgroup's chunk
+        if ((r0 / ro.nb_pad) * nb < n_blocks) {
+            ro.ckn[blockIdx.x * (int64_t)kChunkMaxStride] =
+                fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3]));
+            ro.clo[blockIdx.x * (int64_t)kChunkMaxStride] =
+                fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3]));
+        }
+    }
+}
+
+// One wave per block.  With PREP, waves run over heads x nb_pad; a
+// workgroup (four rows of one chunk) folds its norms into the chunk's
+// maxima with one atomic maximum each (the maxima start at zero).
+template <int BS, bool PREP>
+__global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ x,
+                                                   float* __restrict__ xbar,
+                                                   int64_t n_blocks, int N, RouteOut ro) {
+    constexpr int LOADS = BS / 8;  // 16-byte loads per lane, all issued before any use
+    __shared__ float s_n[2][4];
+    const int lane = threadIdx.x & 63;
+    const int64_t wblk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nb = N / BS;
+    const int dg = lane & 7;   // dims 8*dg .. 8*dg+7
+    const int j0 = lane >> 3;  // tokens j0, j0+8, ...
+    int64_t bh = wblk / nb, c = wblk - bh * nb;
+    bool have = wblk < n_blocks;
+    if (PREP) {
+        bh = wblk / ro.nb_pad;
+        c = wblk - bh * ro.nb_pad;
+        have = bh * nb < n_blocks && c < nb;
+        if (bh * nb < n_blocks && c >= nb && j0 == 0) {  // padding row
+            const int64_t o = wblk * kD + dg * 8;
+            *reinterpret_cast<u32x4*>(ro.khi + o) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(ro.klo + o) = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    float kn = 0.f, ln = 0.f;
+    if (have) {
+        const uint16_t* base = x + (bh * N + c * BS + j0) * kD + dg * 8;
+        u32x4 v[LOADS];
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * 8 * kD);
+        double acc[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[d] = 0.0;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            float f[8];
+            unpack8(v[i], f);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[d] += (double)f[d];
+        }
+#pragma unroll
+        for (int m = 8; m < 64; m <<= 1)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[d] += __shfl_xor(acc[d], m, kWave);
+        if (j0 == 0) {
+            constexpr double inv = 1.0 / (double)BS;  // a power of two: exact
+            f32x4 lo, hi;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                lo[d] = (float)(acc[d] * inv);
+                hi[d] = (float)(acc[4 + d] * inv);
+            }
+            float* o = xbar + (bh * nb + c) * kD + dg * 8;
+            *reinterpret_cast<f32x4*>(o) = lo;
+            *reinterpret_cast<f32x4*>(o + 4) = hi;
+            if (PREP) {
+                const float f[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const int64_t r = wblk * kD + dg * 8;
+                route_split_store(f, ro.khi + r, ro.klo + r, kn, ln);
+            }
+        }
+    }
+    if (!PREP) return;
+    const int w = threadIdx.x >> 6;
+    if (lane == 0) {  // lanes 0..7 hold the row's norms
+        s_n[0][w] = kn;
+        s_n[1][w] = ln;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int64_t r0 = (int64_t)blockIdx.x * 4;  // this workgroup's rows: one chunk
+        if ((r0 / ro.nb_pad) * nb < n_blocks) {
+            const int64_t e = (r0 / 32) * kChunkMaxStride;
+            atomicMax(reinterpret_cast<uint32_t*>(ro.ckn + e),
+                      __float_as_uint(fmaxf(fmaxf(s_n[0][0], s_n[0][1]),
+                                            fmaxf(s_n[0][2], s_n[0][3]))));
+            atomicMax(reinterpret_cast<uint32_t*>(ro.clo + e),
+                      __float_as_uint(fmaxf(fmaxf(s_n[1][0], s_n[1][1]),
+                                            fmaxf(s_n[1][2], s_n[1][3]))));
+        }
     }
 }
 
@@ -101,20 +195,34 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t value) {
         p[i] = value;
 }
 
-hipError_t launch_summarize(const uint16_t* x, float* xbar, int BH, int N, int bs,
+template <bool PREP>
+static hipError_t summarize(const uint16_t* x, float* xbar, int BH, int N, int bs, RouteOut ro,
                             hipStream_t s) {
-    const int64_t n_blocks = (int64_t)BH * (N / bs);
-    const int64_t grid = (n_blocks + 3) / 4;
+    const int nb = N / bs;
+    const int64_t n_blocks = (int64_t)BH * nb;
+    const int64_t rows = PREP ? (int64_t)BH * ro.nb_pad : n_blocks;  // waves (16: lane groups)
+    const int64_t grid = (rows + 3) / 4;
     switch (bs) {
         case 16:
-            hipLaunchKernelGGL(k_summarize16, dim3((unsigned)((n_blocks + 31) / 32)), dim3(256), 0, s,
-                               x, xbar, n_blocks);
+            hipLaunchKernelGGL(k_summarize16<PREP>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0,
+                               s, x, xbar, n_blocks, nb, ro);
             break;
-        case 32: hipLaunchKernelGGL(k_summarize<32>, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N); break;
-        case 64: hipLaunchKernelGGL(k_summarize<64>, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N); break;
-        default: hipLaunchKernelGGL(k_summarize<128>, dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N); break;
+        case 32: hipLaunchKernelGGL((k_summarize<32, PREP>), dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N, ro); break;
+        case 64: hipLaunchKernelGGL((k_summarize<64, PREP>), dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N, ro); break;
+        default: hipLaunchKernelGGL((k_summarize<128, PREP>), dim3((unsigned)grid), dim3(256), 0, s, x, xbar, n_blocks, N, ro); break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_summarize(const uint16_t* x, float* xbar, int BH, int N, int bs,
+                            hipStream_t s) {
+    return summarize<false>(x, xbar, BH, N, bs, RouteOut{}, s);
+}
+
+hipError_t launch_summarize_route(const uint16_t* x, float* xbar, int BH, int N, int bs,
+                                  uint16_t* khi, uint16_t* klo, float* ckn, float* clo,
+                                  int nb_pad, hipStream_t s) {
+    return summarize<true>(x, xbar, BH, N, bs, RouteOut{khi, klo, ckn, clo, nb_pad}, s);
 }
 
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s) {
