@@ -16,19 +16,30 @@
 // candidates whose indices fall in one residue class mod 32 per register;
 // lanes l and l^32 hold the two halves of the same query's chunk.
 //   pass 1  hi-only scores a_c; every lane keeps the two largest values of
-//           each of its residue classes.  The k-th largest of those 64
-//           values (over the lane pair), lowered by a rigorous bound on
-//           |a_c - b_c|, is a threshold that at least k of the pass-2
-//           scores b_c reach.
-//   pass 2  hi+lo scores b_c (fp32 accuracy); candidates at or above the
-//           threshold are appended to the query's survivor list in LDS
-//           (~17 per query on the topic workloads; capacity RT_CAP = 28).
+//           each of its residue classes.  Their k-th largest over the lane
+//           pair, th, is reached by at least k candidates' a_c; delta
+//           bounds |a_c - b_c| against the fp32-accurate score b_c, so at
+//           least k candidates have b_c >= th - delta.
+//   pass 2  one of two forms, chosen per launch by the row length:
+//           full  hi+lo scores b_c (three MFMA products with fp32 queries,
+//                 two otherwise); candidates with b_c >= th - delta join
+//                 the query's survivor list in LDS (capacity RT_CAP = 29);
+//           lean  the hi-only a_c again (one product, half the staging and
+//                 one barrier per chunk); candidates with a_c >= th - 2
+//                 delta join the list, and each survivor's b_c = a_c +
+//                 q_hi . lo_c (+ q_lo . hi_c) is then formed with bf16 dot
+//                 products (v_dot2c_f32_bf16) over rows of the lo (hi) split
+//                 read from L2, the lane pair splitting the 64 dims.
+//           Either way every member of the exact top k survives.  The lean
+//           form saves a third of the MFMA work per candidate but pays a
+//           fixed, latency-bound rescoring per row, so it pays off only for
+//           long rows (kRouteLeanMinCand candidates and more).
 //   select  each lane of the pair inserts the survivors it found into a
-//           16-entry sorted list of 64-bit keys (score, then lower index);
-//           the two lists are merged and the chosen block ids written in
-//           ascending order.
+//           16-entry sorted list of 64-bit keys (score b_c, then lower
+//           index); the two lists are merged and the chosen block ids
+//           written in ascending order.
 // Queries whose survivor list overflows (ties on many blocks, adversarial
-// inputs) are queued, and so is each workgroup holding one.  Up to FB_GRID
+// inputs) are queued, and so is each workgroup holding one.  Up to FB_ROWS
 // such rows are redone one by one by k_route_fallback.  With more, the
 // queued workgroups rerun as k_route<.., EXACT = true>: the same scores,
 // no threshold pass, and each lane keeps its 16 best 64-bit keys, with no
@@ -48,10 +59,12 @@ namespace lsa {
 
 constexpr int RT_ROWS = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int RT_CH = 32;      // candidates per step
-constexpr int RT_CAP = 28;     // survivor slots per query (five workgroups still fit a CU)
+constexpr int RT_CAP = 29;     // survivor slots per query (five workgroups still fit a CU)
 constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
-constexpr int FB_GRID = 1024;  // rows the per-row exact pass takes (one workgroup each);
-                               // above this the queued tiles are redone whole
+constexpr int FB_GRID = 1024;   // workgroups of the per-row exact pass (one row at a time)
+constexpr int FB_ROWS = 16384;  // rows it takes; above this the queued tiles are redone whole
+// the lean pass 2 is used when a row can have this many candidates
+constexpr int kRouteLeanMinCand = 4096;
 
 struct RouteArgs {
     const uint16_t* q;    // bf16 queries [B,Hq,N,64] (QF32 = false)
@@ -297,6 +310,22 @@ __device__ __forceinline__ void read_cands(const __bf16* buf, int l32, int half,
     for (int ks = 0; ks < 4; ++ks) A[ks] = *reinterpret_cast<const bf16x8*>(p + 16 * ks);
 }
 
+// acc + sum of the eight products a_i * b_i of two rows of 8 bf16, fp32
+// accumulation (v_dot2c_f32_bf16, two products per step).  The pairs are
+// taken with vector shuffles: a bit cast of one 32-bit element of a u32x4
+// to bf16x2 inside an unrolled loop is compiled to element 0 every time.
+__device__ __forceinline__ float dot8_bf16(bf16x8 a, bf16x8 b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1),
+                                          __builtin_shufflevector(b, b, 0, 1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3),
+                                          __builtin_shufflevector(b, b, 2, 3), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5),
+                                          __builtin_shufflevector(b, b, 4, 5), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7),
+                                          __builtin_shufflevector(b, b, 6, 7), acc, false);
+    return acc;
+}
+
 // min(max(x, lo), hi) for lo <= hi in one instruction.
 __device__ __forceinline__ int clamp_i32(int x, int lo, int hi) {
     int r;
@@ -328,8 +357,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // ------------------------------------------------------------ main kernel
 // Each wave is independent (its own 32 rows and survivor lists); the
 // workgroup only shares the staged candidate chunks.
-template <bool CAUSAL, bool QF32, bool EXACT>
+template <bool CAUSAL, bool QF32, bool EXACT, bool LEAN>
 __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(RouteArgs a) {
+    static_assert(!(EXACT && LEAN), "the whole-tile exact pass scores b_c directly");
     // candidate staging: pass 1 double-buffers the hi parts in s_stage[0..1];
     // pass 2 holds one chunk's hi part in s_stage[0] and lo part in
     // s_stage[1] (two barriers per chunk), which keeps the workgroup's LDS
@@ -352,7 +382,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     int item;
     if constexpr (EXACT) {
         // the queued tiles, when more rows overflowed than the per-row pass takes
-        if (__builtin_amdgcn_readfirstlane(*a.ovf_count) <= (uint32_t)FB_GRID) return;
+        if (__builtin_amdgcn_readfirstlane(*a.ovf_count) <= (uint32_t)FB_ROWS) return;
         if (blockIdx.x >= __builtin_amdgcn_readfirstlane(*a.tile_count)) return;
         item = (int)__builtin_amdgcn_readfirstlane(a.tile_queue[blockIdx.x]);
     } else {
@@ -499,22 +529,24 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         }
     }
 
-    // threshold: k-th largest class top-2 value minus a bound on |a_c - b_c|:
-    // |q_hi . k_lo| + |q_lo . k_hi| + fp32 accumulation error.
+    // threshold: k-th largest class top-2 value minus delta (full: tested on
+    // b_c) or twice delta (lean: tested on a_c), delta >= |a_c - b_c| =
+    // |q_hi . k_lo + q_lo . k_hi| + rounding (Cauchy-Schwarz with the chunk
+    // maxima of |kbar_c| and |lo_c|; the second term covers fp32
+    // accumulation in the MFMA and the dot products)
     float theta = -INFINITY;
     if constexpr (!EXACT) {
         const float kn_max = __uint_as_float(wave_max_u32(kn_bits));
         const float lo_max = __uint_as_float(wave_max_u32(lo_bits));
         const float th = kth_largest_top2_pair(m1, m2, a.top_k);
         const float delta = 1.0625f * (qn * lo_max + qln * kn_max) + 6.2e-5f * (qn + qln) * kn_max;
-        theta = th - delta;  // -inf stays -inf
+        theta = th - (LEAN ? 2.f : 1.f) * delta;  // -inf stays -inf
     }
 
-    // ---- pass 2: hi+lo scores, survivors to the row's LDS list.  The lane
-    // pair (l, l^32) shares a row's list: half 0 fills it upward from slot 0,
-    // half 1 downward from slot RT_CAP-1; slots are clamped to the list, so
-    // an overflowing list stays in bounds (the row is then redone by the
-    // fallback).
+    // ---- pass 2: survivors to the row's LDS list.  The lane pair (l, l^32)
+    // shares a row's list: half 0 fills it upward from slot 0, half 1
+    // downward from slot RT_CAP-1; slots are clamped to the list, so an
+    // overflowing list stays in bounds (the row is then redone exactly).
     const int qrow = 32 * w + l32;  // row within the workgroup
     // whole-tile exact pass: each lane's 16 best selection keys, descending
     uint64_t Lk[kMaxTopK];
@@ -526,8 +558,36 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     const int step = half ? -RT_ROWS * 4 : RT_ROWS * 4;
     const int at_lo = qrow * 4, at_hi = ((RT_CAP - 1) * RT_ROWS + qrow) * 4;
     int at = half ? at_hi : at_lo;
-    {
-        // staging as in pass 1, hi and lo parts
+    // appends the chunk's scores at or above theta (masked to the row's
+    // candidates in chunks past Efull); cl0 = first candidate of this lane
+    auto append_survivors = [&](const f32x16& acc, int cb, int cl0) {
+        if (cb < Efull) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (acc[r] >= theta) {
+                    const int e = clamp_i32(at, at_lo, at_hi);
+                    *reinterpret_cast<float*>(s_list + e) = acc[r];
+                    *reinterpret_cast<uint16_t*>(s_list + LIST_IDX + (e >> 1)) =
+                        (uint16_t)(cl0 + 8 * (r >> 2) + (r & 3));
+                    at += step;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = cl0 + 8 * (r >> 2) + (r & 3);
+                if (acc[r] >= theta && c < Erow) {
+                    const int e = clamp_i32(at, at_lo, at_hi);
+                    *reinterpret_cast<float*>(s_list + e) = acc[r];
+                    *reinterpret_cast<uint16_t*>(s_list + LIST_IDX + (e >> 1)) = (uint16_t)c;
+                    at += step;
+                }
+            }
+        }
+    };
+    if constexpr (EXACT || !LEAN) {
+        // hi+lo scores b_c (one chunk's hi part in s_stage[0] and lo part in
+        // s_stage[1], two barriers per chunk)
         u32x4 h0 = {0u, 0u, 0u, 0u}, l0 = h0, h1 = h0, l1 = h0;
         if (nch > 0) {
             h0 = stage_load(khi, 0, tid);
@@ -565,30 +625,10 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
                     for (int r = 0; r < 16; ++r) {
                         const int c = cl0 + 8 * (r >> 2) + (r & 3);
                         const uint64_t key = sel_key(acc[r], (uint32_t)c);
-                        if (acc[r] >= theta && c < Erow && key > Lk[kMaxTopK - 1]) insert_key(Lk, key);
-                    }
-                } else if (cb < Efull) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        if (acc[r] >= theta) {
-                            const int e = clamp_i32(at, at_lo, at_hi);
-                            *reinterpret_cast<float*>(s_list + e) = acc[r];
-                            *reinterpret_cast<uint16_t*>(s_list + LIST_IDX + (e >> 1)) =
-                                (uint16_t)(cl0 + 8 * (r >> 2) + (r & 3));
-                            at += step;
-                        }
+                        if (c < Erow && key > Lk[kMaxTopK - 1]) insert_key(Lk, key);
                     }
                 } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int c = cl0 + 8 * (r >> 2) + (r & 3);
-                        if (acc[r] >= theta && c < Erow) {
-                            const int e = clamp_i32(at, at_lo, at_hi);
-                            *reinterpret_cast<float*>(s_list + e) = acc[r];
-                            *reinterpret_cast<uint16_t*>(s_list + LIST_IDX + (e >> 1)) = (uint16_t)c;
-                            at += step;
-                        }
-                    }
+                    append_survivors(acc, cb, cl0);
                 }
             }
             __syncthreads();  // every wave is done with chunk j
@@ -601,6 +641,33 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         for (int j = 0; j < nch; j += 2) {
             body(j, h0, l0, h1, l1);
             if (j + 1 < nch) body(j + 1, h1, l1, h0, l0);
+        }
+    } else {
+        // lean: hi-only scores a_c, staged and double-buffered as in pass 1
+        u32x4 r0 = {0u, 0u, 0u, 0u}, r1 = r0;
+        if (nch > 0) {
+            r0 = stage_load(khi, 0, tid);
+            stage_store(s_stage[0], tid, r0);
+        }
+        if (nch > 1) r1 = stage_load(khi, RT_CH, tid);
+        __syncthreads();
+        auto body = [&](int j, u32x4& r_issue, const u32x4& r_store) {
+            const int cb = j * RT_CH;
+            if (j + 2 < nch) r_issue = stage_load(khi, cb + 2 * RT_CH, tid);
+            if (cb < Emax) {
+                bf16x8 A[4];
+                read_cands(s_stage[j & 1], l32, half, A);
+                f32x16 acc = {};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) acc = mfma32(A[ks], Bq[ks], acc);
+                append_survivors(acc, cb, cb + 4 * half);
+            }
+            if (j + 1 < nch) stage_store(s_stage[(j + 1) & 1], tid, r_store);
+            __syncthreads();
+        };
+        for (int j = 0; j < nch; j += 2) {
+            body(j, r0, r1);
+            if (j + 1 < nch) body(j + 1, r1, r0);
         }
     }
 
@@ -645,6 +712,59 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
             a.ovf_rows[slot] = (uint32_t)out_row;
         }
         return;
+    }
+    // lean form: exact scores of the survivors.  Step i takes half 0's i-th
+    // entry (A) and half 1's i-th entry (B); each lane forms the correction
+    // over its 32 dims for both, and the partner's half of its own entry
+    // arrives by one cross-half swap.  Both lanes of a pair run the same
+    // trip count.  The scattered row loads dominate a step; loading the
+    // next step's rows ahead measured slower, as the extra registers cost a
+    // workgroup per CU.
+    if constexpr (LEAN) {
+        const int n_oth = __shfl_xor(n_mine, 32, kWave);
+        const int nA = half ? n_oth : n_mine, nB = half ? n_mine : n_oth;
+        const int trips = nA > nB ? nA : nB;
+        const int dim0 = 8 * half;
+        constexpr int NV = QF32 ? 8 : 4;  // rows of 8 dims per entry: lo (and hi)
+        // an empty entry reads block 0 (a valid row) and is discarded
+        auto fetch = [&](int i, bf16x8 (&vA)[NV], bf16x8 (&vB)[NV]) {
+            const int eA = at_lo + i * RT_ROWS * 4;
+            const int eB = at_lo + (RT_CAP - 1 - i) * RT_ROWS * 4;
+            const int cA = i < nA ? *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (eA >> 1)) : 0;
+            const int cB = i < nB ? *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (eB >> 1)) : 0;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                vA[ks] = load_bf16x8(klo + (int64_t)cA * kD + dim0 + 16 * ks);
+                vB[ks] = load_bf16x8(klo + (int64_t)cB * kD + dim0 + 16 * ks);
+                if constexpr (QF32) {
+                    vA[4 + ks] = load_bf16x8(khi + (int64_t)cA * kD + dim0 + 16 * ks);
+                    vB[4 + ks] = load_bf16x8(khi + (int64_t)cB * kD + dim0 + 16 * ks);
+                }
+            }
+        };
+        auto apply = [&](int i, const bf16x8 (&vA)[NV], const bf16x8 (&vB)[NV]) {
+            float pA = 0.f, pB = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                pA = dot8_bf16(Bq[ks], vA[ks], pA);
+                pB = dot8_bf16(Bq[ks], vB[ks], pB);
+                if constexpr (QF32) {
+                    pA = dot8_bf16(Bql[ks], vA[4 + ks], pA);
+                    pB = dot8_bf16(Bql[ks], vB[4 + ks], pB);
+                }
+            }
+            const float other = __shfl_xor(half ? pA : pB, 32, kWave);
+            if (i < n_mine) {
+                const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
+                float* sp = reinterpret_cast<float*>(s_list + e);
+                *sp = *sp + ((half ? pB : pA) + other);
+            }
+        };
+        bf16x8 xA[NV], xB[NV];
+        for (int i = 0; i < trips; ++i) {
+            fetch(i, xA, xB);
+            apply(i, xA, xB);
+        }
     }
     uint64_t L[kMaxTopK];
     if (__builtin_amdgcn_ballot_w64(n_mine > kMaxTopK) == 0) {
@@ -721,7 +841,7 @@ __device__ __forceinline__ int wave_top_keys(uint64_t (&L)[kMaxTopK], uint64_t (
 }
 
 // Queued rows are redone exactly, one workgroup per row, when there are at
-// most FB_GRID of them (more are redone by whole tiles, k_route<.., true>):
+// most FB_ROWS of them (more are redone by whole tiles, k_route<.., true>):
 // fp32 scores of every candidate (fma chain over d = 0..63), each lane
 // keeping the 16 best keys of the candidates it scored in registers, then
 // rank-by-rank wave maxima; wave 0 merges the four waves' lists through
@@ -732,7 +852,7 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t count = __builtin_amdgcn_readfirstlane(*a.ovf_count);
-    if (count > (uint32_t)FB_GRID) return;  // the whole-tile pass takes them
+    if (count > (uint32_t)FB_ROWS) return;  // the whole-tile pass takes them
     for (uint32_t i = blockIdx.x; i < count; i += gridDim.x) {
         const uint32_t rid = __builtin_amdgcn_readfirstlane(a.ovf_rows[i]);
         const int bh = (int)(rid / (uint32_t)a.P), row = (int)(rid % (uint32_t)a.P);
@@ -1181,12 +1301,17 @@ size_t route_workspace_bytes(const Geometry& g) {
 template <bool CAUSAL, bool QF32>
 static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
                                  const hipEvent_t* ev) {
-    hipLaunchKernelGGL((k_route<CAUSAL, QF32, false>), grid, dim3(256), 0, s, a);
+    // the longest row's candidate count picks the pass-2 form
+    const int cmax = CAUSAL ? (eligible_blocks(a.P - 1, a.bs, a.window) >> a.cshift) : a.nb;
+    if (cmax >= kRouteLeanMinCand)
+        hipLaunchKernelGGL((k_route<CAUSAL, QF32, false, true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_route<CAUSAL, QF32, false, false>), grid, dim3(256), 0, s, a);
     mark(ev, 2, s);
     // exactly one of the two exact passes does work, chosen on the device by
     // the number of overflowing rows
     hipLaunchKernelGGL((k_route_fallback<CAUSAL, QF32>), dim3(FB_GRID), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_route<CAUSAL, QF32, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_route<CAUSAL, QF32, true, false>), grid, dim3(256), 0, s, a);
 }
 
 // Flat routing of g's rows over g.nb summaries `summ` into idx (row stride

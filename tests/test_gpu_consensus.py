@@ -102,6 +102,30 @@ def test_consensus_routing_matches_oracle(lsa, w):
     assert bad == 0
 
 
+# rows with 4096 or more candidate blocks: the router's lean second pass
+@pytest.mark.parametrize("w", [custom(1, 4, 2, 81920, 16, 16, 128, dist="topics", seed=24),
+                               custom(1, 4, 2, 65536, 16, 8, 0, causal=0, seed=25)],
+                         ids=lambda w: w.name)
+def test_consensus_routing_long_rows_sampled(lsa, w):
+    say("consensus routing long rows", w.name)
+    inp = generate(w)
+    p = params_of(lsa, w, consensus=1)
+    kbar = lsa.block_summarize(p, dev(inp.k))
+    idx = lsa.route_topk(p, dev(inp.q), kbar)
+    torch.cuda.synchronize()
+    R, per = group_rows_of(w)
+    rng = np.random.default_rng(6)
+    tail = np.concatenate([np.arange(g * per + per - 128, g * per + per)
+                           for g in range(w.batch * w.kv_heads)])
+    rows = np.unique(np.concatenate([rng.choice(R, size=2000, replace=False), tail]))
+    io, gap, sc, ncand = oracle_consensus(w, inp, oracle.block_means(inp.k, w.block), rows=rows)
+    ig = idx.cpu().numpy().reshape(-1, w.top_k)[rows]
+    bad, near, near_diff = check_routing(ig, io.reshape(rows.size, -1), gap.reshape(-1), sc,
+                                         ncand, w.top_k)
+    say("  rows", rows.size, "near ties", near, "differing", near_diff)
+    assert bad == 0
+
+
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_consensus_forward_matches_oracle(lsa, w):
     say("consensus forward", w.name)

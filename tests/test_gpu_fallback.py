@@ -7,8 +7,10 @@ selection, ties to the lower block.  Equal summaries give equal scores on
 both sides, so the selection is compared exactly on every row whose distinct
 scores are more than 1e-3 apart.  The first two words of the routing
 workspace count the overflowing rows and the 128-row tiles holding them;
-each case checks that the exact pass ran.  Up to 1024 rows are redone one by
-one (the "few" cases), beyond that whole tiles are (the "many" cases)."""
+each case checks that the exact pass ran.  Up to 16384 rows are redone one
+by one (the "few" cases), beyond that whole tiles are (the "many" cases).
+A survivor list holds 29 entries, so an all-ties row overflows once it has
+more than 29 candidates."""
 import sys
 
 import numpy as np
@@ -35,7 +37,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-ROWS_ONE_BY_ONE = 1024  # overflowing rows redone one by one; more: whole tiles
+ROWS_ONE_BY_ONE = 16384  # overflowing rows redone one by one; more: whole tiles
 
 
 def case(B, Hq, Hkv, N, bs, k, W, npat, causal=1, consensus=0, expect=None, seed=61):
@@ -46,19 +48,19 @@ def case(B, Hq, Hkv, N, bs, k, W, npat, causal=1, consensus=0, expect=None, seed
 
 CASES = [
     # causal, per-head routes
-    case(1, 2, 1, 2048, 64, 4, 128, 1, expect="few"),   # every score ties
+    case(1, 2, 1, 2560, 64, 4, 128, 1, expect="few"),   # every score ties
     case(1, 4, 1, 8192, 64, 16, 512, 1, expect="many"),
-    case(1, 4, 2, 8192, 64, 16, 512, 2, expect="many"),  # two tie groups
-    case(2, 3, 1, 4096, 32, 5, 64, 3, expect="many"),    # odd top-k, three groups
+    case(1, 4, 2, 12288, 64, 16, 512, 2, expect="many"),  # two tie groups
+    case(2, 3, 1, 8192, 32, 5, 64, 3, expect="many"),    # odd top-k, three groups
     case(1, 2, 1, 4096, 64, 16, 256, 2),
     case(1, 3, 1, 16 * 700, 16, 6, 32, 2, expect="many"),  # 16-key blocks, partial last tile
     # image mode (pooled fp32 queries)
     case(1, 1, 1, 4096, 16, 8, 0, 1, causal=0, expect="few"),
-    case(1, 8, 4, 4096, 16, 8, 0, 1, causal=0, expect="many"),
+    case(3, 8, 4, 16384, 16, 8, 0, 1, causal=0, expect="many"),
     case(1, 4, 2, 4096, 16, 16, 0, 2, causal=0),
     # consensus (group-summed fp32 queries)
-    case(1, 2, 1, 2048, 64, 16, 128, 1, consensus=1, expect="few"),
-    case(1, 4, 2, 4096, 64, 16, 256, 1, consensus=1, expect="many"),
+    case(1, 2, 1, 4096, 64, 16, 128, 1, consensus=1, expect="few"),
+    case(1, 4, 2, 16384, 64, 16, 256, 1, consensus=1, expect="many"),
     case(1, 4, 2, 4096, 64, 16, 256, 2, consensus=1),
 ]
 

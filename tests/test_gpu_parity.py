@@ -105,11 +105,67 @@ def test_routing_matches_oracle(lsa, w):
     assert bad == 0
 
 
+# Rows with 4096 or more candidate blocks take the router's lean second pass
+# (hi-only scores, survivors rescored exactly); these cases reach it at a
+# modest size with 16-token blocks.
+LONG_ROW_CASES = [
+    custom(1, 2, 1, 81920, 16, 16, 128, dist="topics", seed=21),
+    custom(1, 3, 1, 65536 + 16 * 300, 16, 7, 64, seed=22),
+    custom(1, 2, 2, 65536, 16, 8, 0, causal=0, seed=23),
+]
+
+
+@pytest.mark.parametrize("w", LONG_ROW_CASES, ids=lambda w: w.name)
+def test_routing_long_rows_sampled(lsa, w):
+    """Routing parity on a sample of rows (plus the last routing tile of
+    every head) for rows long enough for the lean second pass."""
+    say("routing long rows", w.name)
+    inp = generate(w)
+    _, idx = run_route(lsa, w, inp)
+    kbar_o = oracle.block_means(inp.k, w.block)
+    rng = np.random.default_rng(5)
+    P = w.seq_len if w.causal else w.seq_len // w.block
+    R = w.batch * w.q_heads * P
+    tail = np.concatenate([np.arange(h * P + P - 128, h * P + P)
+                           for h in range(w.batch * w.q_heads)])
+    rows = np.unique(np.concatenate([rng.choice(R, size=3000, replace=False), tail]))
+    if w.causal:
+        io, gap = oracle.route_causal(inp.q, kbar_o, w.block, w.top_k, w.window, rows=rows,
+                                      with_gap=True)
+        scores = oracle.route_scores(kbar_o, rows, q=inp.q, block=w.block, window=w.window,
+                                     causal=1)
+        ncand = causal_candidates(rows % w.seq_len, w.block, w.window)
+    else:
+        qbar = oracle.block_means(inp.q, w.block)
+        io, gap = oracle.route_image(qbar, kbar_o, w.top_k, rows=rows, with_gap=True)
+        scores = oracle.route_scores(kbar_o, rows, qbar=qbar, block=w.block, causal=0)
+        ncand = np.full(rows.size, P)
+    ig = idx.reshape(-1, w.top_k)[rows]
+    bad, near, near_diff = check_routing(ig, io.reshape(rows.size, -1), gap.reshape(-1), scores,
+                                         ncand, w.top_k)
+    say("  rows", rows.size, "near ties", near, "differing", near_diff)
+    assert bad == 0
+
+
+def test_routing_all_ties_long_rows(lsa):
+    """All scores equal on rows long enough for the lean second pass: every
+    row overflows its survivor list, more rows than the per-row exact pass
+    takes, so the queued tiles are redone whole."""
+    w = custom(1, 1, 1, 81920, 16, 4, 64)
+    inp = generate(w)
+    inp.k[:] = to_bf16_bits(np.full(inp.k.shape, 0.25, np.float32))
+    _, idx = run_route(lsa, w, inp)
+    t = np.arange(w.seq_len)
+    E = np.maximum(0, t // 16 - 4 + 1)
+    want = np.where(np.arange(4)[None, :] < np.minimum(4, E)[:, None], np.arange(4)[None, :], -1)
+    np.testing.assert_array_equal(idx.reshape(w.seq_len, 4), want)
+
+
 def test_routing_all_ties_pick_lowest_blocks(lsa):
     """Constant keys make every routing score equal: every row must take the
-    lowest eligible block ids (these rows overflow the fast path and run the
-    exact fallback)."""
-    w = custom(1, 2, 1, 2048, 64, 4, 128)
+    lowest eligible block ids (rows with more than 29 candidates overflow the
+    fast path and run the exact fallback)."""
+    w = custom(1, 2, 1, 4096, 64, 4, 128)
     inp = generate(w)
     inp.k[:] = to_bf16_bits(np.full(inp.k.shape, 0.25, np.float32))
     _, idx = run_route(lsa, w, inp)
