@@ -213,6 +213,10 @@ struct PartArgs {
     int b0, b1;                // this launch's buckets [b0, b1): one position chunk
     int pc_log2, t_base;       // positions per chunk (log2); the chunk's first position
     float scale_log2;
+    // 1, or the query heads per KV group when pairs are group pairs (one
+    // route per group): gathered row e of the chunk is then head e % expand
+    // of the group pair at position e / expand
+    int expand;
 };
 
 // Per wave, pair ids run two units ahead and Q rows one unit ahead of the
@@ -245,13 +249,27 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     // never has to drain the stores issued after it.
     const uint32_t dummy = a.dummy_pid + my;
     const uint32_t dummy_pos = a.dummy_pos + my;
+    const uint32_t pmask = (1u << a.pc_log2) - 1u;
+    const uint32_t smask = (1u << a.sp_log2) - 1u;
+    // the query pair id of this lane's gathered row of unit u
     auto fetch_pid = [&](uint32_t u, uint32_t& pid, bool& v) {
         uint32_t q0 = 0, q1 = 0;
-        if (u < u1) ahead.rows(a.unit_off, a.offsets, u, q0, q1);
-        v = q0 + my < q1;
-        pid = a.pairs[v ? q0 + my : pos_base];
+        if (u < u1) ahead.rows(a.unit_off, a.offsets, u, q0, q1, (uint32_t)a.expand);
+        const uint32_t e = q0 + my;
+        v = e < q1;
+        if (a.expand == 1) {
+            pid = a.pairs[v ? e : pos_base];
+        } else {
+            // group pair (KV group bg, position, slot) -> the same position
+            // and slot of query head bg * expand + h
+            const uint32_t pos = e / (uint32_t)a.expand, h = e - pos * (uint32_t)a.expand;
+            const uint32_t gp = a.pairs[v ? pos : pos_base];
+            const uint32_t grow = gp >> a.sp_log2;
+            const uint32_t qrow = (((grow >> a.pc_log2) * (uint32_t)a.expand + h) << a.pc_log2) |
+                                  (grow & pmask);
+            pid = (qrow << a.sp_log2) | (gp & smask);
+        }
     };
-    const uint32_t pmask = (1u << a.pc_log2) - 1u;
     auto fetch_q = [&](uint32_t pid, bf16x8 (&B)[2]) {
         // chunk-local row -> (query head bh, position t) -> global row
         const uint32_t lrow = pid >> a.sp_log2;
@@ -275,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
     int loaded = -1, koff = 0;
     for (uint32_t u = u0; u < u1; ++u) {
         uint32_t p0, p1;
-        cur.rows(a.unit_off, a.offsets, u, p0, p1);
+        cur.rows(a.unit_off, a.offsets, u, p0, p1, (uint32_t)a.expand);
         // prefetch: pair ids of u+2, Q rows of u+1
         bool v_n2;
         uint32_t pid_n2;
@@ -339,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void k_block_partial(PartArgs a) {
         }
         // by position: the wave's 16 rows are consecutive, so this store is
         // contiguous (the row's four lanes store the same value)
-        a.part_lse[v_cur ? p0 + my - pos_base : dummy_pos] = m2 + log2f(sum);
+        a.part_lse[v_cur ? p0 + my - pos_base * (uint32_t)a.expand : dummy_pos] = m2 + log2f(sum);
         v_cur = v_nxt;
         pid_cur = pid_nxt;
         v_nxt = v_n2;
@@ -360,11 +378,12 @@ struct WinArgs {
     const uint32_t* rev;      // [top_k][rows]: global pair positions
     const uint32_t* offsets;  // [NB+1] bucket offsets (the chunk's first pair: offsets[b0])
     float* out;
-    int64_t rows;
+    int64_t rows;             // rows of rev: query rows, or group rows with group pairs
     int Hq, Hkv, N, bs, top_k, window, tiles, items, ntiles, sp_log2;
     int b0, pc_log2, t_base;  // the chunk: first bucket, positions (log2), first position
     float scale_log2;
     int group_route;
+    int expand;               // as in PartArgs: > 1 with group pairs
 };
 
 // One workgroup per (query head, 64 positions); wave w owns rows
@@ -406,6 +425,10 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     const int E = valid ? eligible_blocks(t, a.bs, a.window) : 0;
     const int lo_t = valid ? a.bs * E : a.N;
     const int64_t row = (int64_t)bh * a.N + t;
+    // rows of the pair-position table, and this head's gathered row of a
+    // pair: group rows and head hh with group pairs
+    const int64_t rev_row = a.expand > 1 ? (int64_t)bg * a.N + t : row;
+    const uint32_t head_off = a.expand > 1 ? (uint32_t)hh : 0u;
 
     bf16x8 Bq[2];
     load_q_operand(a.q + row * kD, lane, valid, Bq);
@@ -498,17 +521,18 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     const uint32_t pos_base = uniform_load(a.offsets + a.b0);
     // log2 masses: the pair positions from the slot-major table (the wave's
     // 16 rows are consecutive, so each load is contiguous), then one 4-byte
-    // gather per used slot
+    // gather per used slot (group pairs: head hh's gathered row of the pair)
     float lse_all[kMaxTopK];
     {
         uint32_t rs[kMaxTopK];
 #pragma unroll
         for (int sl = 0; sl < kMaxTopK; ++sl)
-            rs[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.rev[sl * a.rows + row] : 0u;
+            rs[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.rev[sl * a.rows + rev_row] : 0u;
 #pragma unroll
         for (int sl = 0; sl < kMaxTopK; ++sl)
-            lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.part_lse[rs[sl] - pos_base]
-                                                                 : -INFINITY;
+            lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u))
+                              ? a.part_lse[(rs[sl] - pos_base) * (uint32_t)a.expand + head_off]
+                              : -INFINITY;
     }
 #pragma unroll
     for (int s0 = 0; s0 < kMaxTopK; s0 += 8) {
@@ -715,14 +739,15 @@ static ChunkPlan chunk_plan(const Geometry& g) {
         c.pc_log2 = std::min(lc, ln);
     }
     c.nchunk = (int)(((int64_t)g.N + (1 << c.pc_log2) - 1) >> c.pc_log2);
-    // bucketing workgroups: ~4096 rows over the group's query heads, fewer
-    // when that would leave under ~256 workgroups, but enough pairs to
-    // amortise the per-bucket flush of the LDS histogram; a power of two
-    // within one chunk
+    // bucketing workgroups: ~4096 rows over the group's query heads (one
+    // group row per position with group routes), fewer when that would
+    // leave under ~256 workgroups, but enough pairs to amortise the
+    // per-bucket flush of the LDS histogram; a power of two within one chunk
     const int nbg = g.B * g.Hkv;
+    const int hw = g.consensus ? 1 : rep;  // rows walked per position
     const int64_t flush_min =
-        (4 * (int64_t)g.nb + (int64_t)rep * g.top_k - 1) / ((int64_t)rep * g.top_k);
-    int64_t tc = std::min<int64_t>((4096 + rep - 1) / rep, (int64_t)nbg * g.N / 256);
+        (4 * (int64_t)g.nb + (int64_t)hw * g.top_k - 1) / ((int64_t)hw * g.top_k);
+    int64_t tc = std::min<int64_t>((4096 + hw - 1) / hw, (int64_t)nbg * g.N / 256);
     tc = std::max<int64_t>(tc, flush_min);
     int lt = 6;
     while (lt < c.pc_log2 && ((int64_t)1 << (lt + 1)) <= tc) ++lt;
@@ -812,16 +837,21 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
 
     hipError_t e = launch_fill_u32(counts, (size_t)NB, 0u, s);
     if (e != hipSuccess) return e;
-    const int64_t rows = (int64_t)g.B * g.Hq * g.N;
+    // one route per KV group: bucket (group row, slot) pairs, each gathered
+    // once per query head of the group
+    const int rep = g.Hq / g.Hkv;
+    const int expand = g.consensus ? rep : 1;
+    const int64_t rows = (int64_t)g.B * (g.consensus ? g.Hkv : g.Hq) * g.N;
     BucketArgs ba{idx, counts, cursor, pairs, rev, rows, g.Hq, g.Hkv, g.N, g.bs, g.nb, g.top_k, g.window,
                   1 << P.tc_log2, sp_log2, g.consensus, 0, P.pc_log2, nbg};
+    ba.group_pairs = g.consensus;
     const int nch = (g.N + (1 << P.tc_log2) - 1) >> P.tc_log2;
     const dim3 bgrid((unsigned)(nbg * nch));
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
     hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
     mark(ev, 4, s);
     hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
-                       NB);
+                       NB, expand);
     mark(ev, 5, s);
     hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
     mark(ev, 6, s);
@@ -830,12 +860,11 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     // with several, 7 follows the last chunk's merge and stage 8 is empty
     const uint32_t cslots = (uint32_t)(L.crows << sp_log2);
     const uint32_t cpairs = (uint32_t)(L.crows * g.top_k);
-    const int rep = g.Hq / g.Hkv;
     for (int c = 0; c < P.nchunk; ++c) {
         const int t_base = c << P.pc_log2;
         const int b0 = c * nbg * g.nb, b1 = b0 + nbg * g.nb;
         PartArgs pa{q, k, vt, pairs, offsets, unit_off, part_o, part_lse, cslots, cpairs, g.N,
-                    g.nb, NB, ntiles, sp_log2, b0, b1, P.pc_log2, t_base, scale_log2};
+                    g.nb, NB, ntiles, sp_log2, b0, b1, P.pc_log2, t_base, scale_log2, expand};
         switch (g.bs) {
             case 16: launch_partial<16>(pa, s); break;
             case 32: launch_partial<32>(pa, s); break;
@@ -847,7 +876,7 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
         const int wtiles = (span + 63) / 64;
         WinArgs wa{q, k, vt, idx, part_o, part_lse, rev, offsets, out, rows, g.Hq, g.Hkv, g.N,
                    g.bs, g.top_k, g.window, wtiles, nbg * rep * wtiles, ntiles, sp_log2, b0,
-                   P.pc_log2, t_base, scale_log2, g.consensus};
+                   P.pc_log2, t_base, scale_log2, g.consensus, expand};
         const int64_t wgrid = ((int64_t)wa.items + 7) / 8 * 8;  // multiple of the XCD count
         hipLaunchKernelGGL(k_window_merge, dim3((unsigned)wgrid), dim3(256), 0, s, wa);
     }

@@ -54,6 +54,9 @@ struct BucketArgs {
     int64_t rows;        // B * Hq * N
     int Hq, Hkv, N, bs, nb, top_k, window, tchunk, sp_log2;
     int group_route;     // 1: one route per KV group, shared by its query heads
+    // group_pairs (requires group_route): pairs are (group row, slot), one per
+    // position and slot for all the group's query heads; rows (of rev and of
+    // pair ids) are then the B * Hkv * N group rows, bg * N + t.
     int cshift;          // buckets group 2^cshift blocks: a row's candidate buckets are
                          // ceil(E(t) / 2^cshift) (0: buckets are blocks)
     // Position chunks (pc_log2 >= 0): buckets are (chunk, b * Hkv + g, block)
@@ -64,6 +67,7 @@ struct BucketArgs {
     int pc_log2 = -1;
     int nbg = 0;         // B * Hkv (with position chunks)
     int fixed_cand = 0;  // > 0: every row's candidate buckets (image-mode rows); else causal
+    int group_pairs = 0;
 };
 
 __device__ __forceinline__ int bucket_candidates(const BucketArgs& a, int t) {
@@ -99,18 +103,25 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     const bool chunked = a.pc_log2 >= 0;
     const int64_t bucket0 =
         chunked ? ((int64_t)(t0 >> a.pc_log2) * a.nbg + bg) * a.nb : (int64_t)bg * a.nb;
-    // pair-id row of query head hh at position t
+    // heads walked per position: the group's query heads, or one group row
+    const int nh = a.group_pairs ? 1 : rep;
+    // row (of rev) and idx row of head hh at position t
+    auto row_of = [&](int hh, int t) -> int64_t {
+        return a.group_pairs ? (int64_t)bg * a.N + t : ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
+    };
+    // pair-id row of head hh (group pairs: the group row) at position t
     auto pair_row = [&](int hh, int t, int64_t row) -> int64_t {
         if (!chunked) return row;
-        return (((int64_t)b * a.Hq + g * rep + hh) << a.pc_log2) + (t & ((1 << a.pc_log2) - 1));
+        const int64_t r = a.group_pairs ? (int64_t)bg : (int64_t)b * a.Hq + g * rep + hh;
+        return (r << a.pc_log2) + (t & ((1 << a.pc_log2) - 1));
     };
     if (lds) {
         for (int c = tid; c < a.nb; c += 256) s_h[c] = 0;
         __syncthreads();
     }
-    for (int i = tid; i < rep * span; i += 256) {
+    for (int i = tid; i < nh * span; i += 256) {
         const int hh = i / span, t = t0 + (i - hh * span);
-        const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
+        const int64_t row = row_of(hh, t);
         const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
         int c[kMaxTopK];
         uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, bucket_candidates(a, t), c);
@@ -143,9 +154,9 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     }
     if (!SCATTER) return;
     __syncthreads();
-    for (int i = tid; i < rep * span; i += 256) {
+    for (int i = tid; i < nh * span; i += 256) {
         const int hh = i / span, t = t0 + (i - hh * span);
-        const int64_t row = ((int64_t)b * a.Hq + g * rep + hh) * a.N + t;
+        const int64_t row = row_of(hh, t);
         const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
         int c[kMaxTopK];
         uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, bucket_candidates(a, t), c);
@@ -163,11 +174,13 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
 }
 
 // Single workgroup: exclusive scans of bucket sizes and of work units
-// (ceil(count / UNIT_ROWS)); cursor starts at the bucket offsets.
+// (ceil(count * expand / UNIT_ROWS): each pair stands for `expand` gathered
+// rows); cursor starts at the bucket offsets.
 static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __restrict__ counts,
                                                       uint32_t* __restrict__ offsets,
                                                       uint32_t* __restrict__ cursor,
-                                                      uint32_t* __restrict__ unit_off, int NB) {
+                                                      uint32_t* __restrict__ unit_off, int NB,
+                                                      int expand) {
     __shared__ uint32_t s_p[1024], s_u[1024];
     const int tid = threadIdx.x;
     const int per = (NB + 1023) / 1024;
@@ -177,7 +190,7 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
     for (int i = lo; i < hi; ++i) {
         const uint32_t n = counts[i];
         sp += n;
-        su += (n + UNIT_ROWS - 1) / UNIT_ROWS;
+        su += (n * expand + UNIT_ROWS - 1) / UNIT_ROWS;
     }
     s_p[tid] = sp;
     s_u[tid] = su;
@@ -198,7 +211,7 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
         cursor[i] = rp;
         unit_off[i] = ru;
         rp += n;
-        ru += (n + UNIT_ROWS - 1) / UNIT_ROWS;
+        ru += (n * expand + UNIT_ROWS - 1) / UNIT_ROWS;
     }
     if (tid == 1023) {
         offsets[NB] = s_p[1023];
@@ -216,6 +229,7 @@ __device__ __forceinline__ uint32_t uniform_load(const uint32_t* p) {
 
 // Work units (64 gathered rows of one bucket) are split into contiguous
 // ranges per workgroup, so K/V of a bucket are staged once for all its units.
+// Gathered rows are numbered expand * (pair position) + (0 .. expand - 1).
 struct UnitCursor {
     int bucket;
     __device__ void seek(const uint32_t* unit_off, int NB, uint32_t u) {
@@ -226,12 +240,13 @@ struct UnitCursor {
         }
         bucket = lo;
     }
-    // Rows [p0, p1) of unit u (u >= the unit of the previous call).
+    // Gathered rows [p0, p1) of unit u (u >= the unit of the previous call).
     __device__ void rows(const uint32_t* unit_off, const uint32_t* offsets, uint32_t u,
-                         uint32_t& p0, uint32_t& p1) {
+                         uint32_t& p0, uint32_t& p1, uint32_t expand = 1) {
         while (uniform_load(unit_off + bucket + 1) <= u) ++bucket;
-        p0 = uniform_load(offsets + bucket) + (u - uniform_load(unit_off + bucket)) * UNIT_ROWS;
-        p1 = min(p0 + UNIT_ROWS, uniform_load(offsets + bucket + 1));
+        p0 = uniform_load(offsets + bucket) * expand +
+             (u - uniform_load(unit_off + bucket)) * UNIT_ROWS;
+        p1 = min(p0 + UNIT_ROWS, uniform_load(offsets + bucket + 1) * expand);
     }
 };
 

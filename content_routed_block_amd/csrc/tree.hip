@@ -291,7 +291,7 @@ hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const float*
     const size_t lds = L.nodes <= BK_LDS_MAX ? (size_t)L.nodes * 4 : 0;
     hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
     hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
-                       L.NB);
+                       L.NB, 1);
     hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
 
     TreeScoreArgs sa{q, qbar, bhi, blo, pairs, offsets, unit_off, scores,
