@@ -44,7 +44,57 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # FETCH_SIZE and WRITE_SIZE runs, each scaled by the same counter's reading on
 # a plain copy of known size (FETCH x 2.0, WRITE x 1.0); valid only for the
 # kernel sources and compile flags they were measured with (kernel_digest).
-TRAFFIC = {}
+TRAFFIC = {
+    "qwen05b_n32k": {
+        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "kib": {
+            "V transpose + bucket count": (18491.9, 8444.0),
+            "bucket scan": (5.6, 12.1),
+            "bucket scatter": (26330.4, 69724.1),
+            "key summary": (4141.7, 528.0),
+            "routed-block partials": (460850.5, 964073.3),
+            "routing": (29523.3, 28672.0),
+            "routing fallback": (36.0, 0.0),
+            "window + merge": (531057.3, 114688.4),
+        },
+    },
+    "qwen05b_n128k_needles": {
+        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "kib": {
+            "V transpose + bucket count": (73789.0, 34808.0),
+            "bucket scan": (11.6, 48.1),
+            "bucket scatter": (115495.1, 514376.6),
+            "key summary": (16430.8, 2112.0),
+            "routed-block partials": (1918627.4, 3909815.3),
+            "routing": (119631.2, 114690.5),
+            "routing fallback": (36.0, 0.0),
+            "window + merge": (2187562.6, 458753.1),
+        },
+    },
+    "image_zorder_128x128": {
+        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "kib": {
+            "V transpose + bucket count": (65553.7, 131072.0),
+            "key summary": (131162.0, 49283.0),
+            "routing": (16818.5, 2048.0),
+            "routing fallback": (37.8, 0.0),
+            "window + merge": (211851.8, 262159.8),
+        },
+    },
+    "qwen05b_n1m_needles": {
+        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "kib": {
+            "V transpose + bucket count": (589886.5, 393151.9),
+            "bucket scan": (67.6, 384.1),
+            "bucket scatter": (964467.3, 6938793.5),
+            "key summary": (131120.6, 16896.0),
+            "routed-block partials": (15571569.7, 31407445.1),
+            "routing": (1431195.6, 917588.7),
+            "routing fallback": (469584.4, 91.4),
+            "window + merge": (19910359.2, 3670022.8),
+        },
+    },
+}
 
 
 def traffic_counters(w):
@@ -57,20 +107,19 @@ def traffic_counters(w):
             for stage, (fetch, write) in t["kib"].items()}
 
 
-# The attention kernels' translation unit: its source and the headers it
-# includes; with them the compile flags (paths relative to the repository).
-KERNEL_SOURCES = [
-    "content_routed_block_amd/csrc/attend.hip",
-    "content_routed_block_amd/csrc/bucket.hpp",
-    "content_routed_block_amd/csrc/lsa_common.hpp",
-    "content_routed_block_amd/csrc/lsa_launch.hpp",
-]
+def kernel_sources():
+    """Every kernel source and header of the library (paths relative to the
+    repository), in a fixed order."""
+    csrc = os.path.join(ROOT, "content_routed_block_amd", "csrc")
+    return sorted(os.path.join("content_routed_block_amd", "csrc", f) for f in os.listdir(csrc)
+                  if f.endswith((".hip", ".hpp")))
 
 
 def kernel_digest() -> str:
+    """Digest of the kernel sources and the compile flags."""
     from content_routed_block_amd import build as lsa_build
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources():
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     h.update("\0".join(f.replace(lsa_build.ROOT, "") for f in lsa_build.FLAGS).encode())
@@ -680,6 +729,7 @@ def main():
                   "attend_ms": attend_ms,
                   "attend_mfma_frac": f_sel / 1e12 / (attend_ms * 1e-3) / PEAK_BF16_TFLOPS,
                   "attend_traffic": attend_traffic,
+                  "workspace_bytes": lsa.workspace_bytes(p, lsa.OP_FORWARD),
                   "routed_pairs": routed_pairs, "stage_ms": breakdown, "stage_roofline": stage_frac},
     }
     if args.consensus_steps > 0 and w.q_heads > w.kv_heads:
