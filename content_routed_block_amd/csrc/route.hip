@@ -27,13 +27,14 @@
 //           lean  the hi-only a_c again (one product, half the staging and
 //                 one barrier per chunk); candidates with a_c >= th - 2
 //                 delta join the list, and each survivor's b_c = a_c +
-//                 q_hi . lo_c (+ q_lo . hi_c) is then formed with bf16 dot
-//                 products (v_dot2c_f32_bf16) over rows of the lo (hi) split
-//                 read from L2, the lane pair splitting the 64 dims.
+//                 q . lo_c is then formed with bf16 dot products
+//                 (v_dot2c_f32_bf16) over rows of the lo split read from
+//                 L2, the lane pair splitting the 64 dims.
 //           Either way every member of the exact top k survives.  The lean
 //           form saves a third of the MFMA work per candidate but pays a
 //           fixed, latency-bound rescoring per row, so it pays off only for
-//           long rows (kRouteLeanMinCand candidates and more).
+//           long rows (kRouteLeanMinCand candidates and more) of bf16
+//           queries.
 //   select  each lane of the pair inserts the survivors it found into a
 //           16-entry sorted list of 64-bit keys (score b_c, then lower
 //           index); the two lists are merged and the chosen block ids
@@ -360,6 +361,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 template <bool CAUSAL, bool QF32, bool EXACT, bool LEAN>
 __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(RouteArgs a) {
     static_assert(!(EXACT && LEAN), "the whole-tile exact pass scores b_c directly");
+    static_assert(!(QF32 && LEAN), "fp32 queries take the full form");
     // candidate staging: pass 1 double-buffers the hi parts in s_stage[0..1];
     // pass 2 holds one chunk's hi part in s_stage[0] and lo part in
     // s_stage[1] (two barriers per chunk), which keeps the workgroup's LDS
@@ -713,7 +715,8 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         }
         return;
     }
-    // lean form: exact scores of the survivors.  Step i takes half 0's i-th
+    // lean form (bf16 queries): exact scores of the survivors, b_c = a_c +
+    // q . lo_c.  Step i takes half 0's i-th
     // entry (A) and half 1's i-th entry (B); each lane forms the correction
     // over its 32 dims for both, and the partner's half of its own entry
     // arrives by one cross-half swap.  Both lanes of a pair run the same
@@ -725,9 +728,8 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         const int nA = half ? n_oth : n_mine, nB = half ? n_mine : n_oth;
         const int trips = nA > nB ? nA : nB;
         const int dim0 = 8 * half;
-        constexpr int NV = QF32 ? 8 : 4;  // rows of 8 dims per entry: lo (and hi)
         // an empty entry reads block 0 (a valid row) and is discarded
-        auto fetch = [&](int i, bf16x8 (&vA)[NV], bf16x8 (&vB)[NV]) {
+        auto fetch = [&](int i, bf16x8 (&vA)[4], bf16x8 (&vB)[4]) {
             const int eA = at_lo + i * RT_ROWS * 4;
             const int eB = at_lo + (RT_CAP - 1 - i) * RT_ROWS * 4;
             const int cA = i < nA ? *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (eA >> 1)) : 0;
@@ -736,22 +738,14 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
             for (int ks = 0; ks < 4; ++ks) {
                 vA[ks] = load_bf16x8(klo + (int64_t)cA * kD + dim0 + 16 * ks);
                 vB[ks] = load_bf16x8(klo + (int64_t)cB * kD + dim0 + 16 * ks);
-                if constexpr (QF32) {
-                    vA[4 + ks] = load_bf16x8(khi + (int64_t)cA * kD + dim0 + 16 * ks);
-                    vB[4 + ks] = load_bf16x8(khi + (int64_t)cB * kD + dim0 + 16 * ks);
-                }
             }
         };
-        auto apply = [&](int i, const bf16x8 (&vA)[NV], const bf16x8 (&vB)[NV]) {
+        auto apply = [&](int i, const bf16x8 (&vA)[4], const bf16x8 (&vB)[4]) {
             float pA = 0.f, pB = 0.f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 pA = dot8_bf16(Bq[ks], vA[ks], pA);
                 pB = dot8_bf16(Bq[ks], vB[ks], pB);
-                if constexpr (QF32) {
-                    pA = dot8_bf16(Bql[ks], vA[4 + ks], pA);
-                    pB = dot8_bf16(Bql[ks], vB[4 + ks], pB);
-                }
             }
             const float other = __shfl_xor(half ? pA : pB, 32, kWave);
             if (i < n_mine) {
@@ -760,7 +754,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
                 *sp = *sp + ((half ? pB : pA) + other);
             }
         };
-        bf16x8 xA[NV], xB[NV];
+        bf16x8 xA[4], xB[4];
         for (int i = 0; i < trips; ++i) {
             fetch(i, xA, xB);
             apply(i, xA, xB);
@@ -1301,12 +1295,17 @@ size_t route_workspace_bytes(const Geometry& g) {
 template <bool CAUSAL, bool QF32>
 static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
                                  const hipEvent_t* ev) {
-    // the longest row's candidate count picks the pass-2 form
+    // the longest row's candidate count picks the pass-2 form; fp32 queries
+    // (group sums, pooled blocks) always take the full form: their delta
+    // carries the q_lo term too, and the lean form's 2 * delta band
+    // overflows the survivor lists
     const int cmax = CAUSAL ? (eligible_blocks(a.P - 1, a.bs, a.window) >> a.cshift) : a.nb;
-    if (cmax >= kRouteLeanMinCand)
-        hipLaunchKernelGGL((k_route<CAUSAL, QF32, false, true>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_route<CAUSAL, QF32, false, false>), grid, dim3(256), 0, s, a);
+    bool lean = false;
+    if constexpr (!QF32) lean = cmax >= kRouteLeanMinCand;
+    if constexpr (!QF32) {
+        if (lean) hipLaunchKernelGGL((k_route<CAUSAL, false, false, true>), grid, dim3(256), 0, s, a);
+    }
+    if (!lean) hipLaunchKernelGGL((k_route<CAUSAL, QF32, false, false>), grid, dim3(256), 0, s, a);
     mark(ev, 2, s);
     // exactly one of the two exact passes does work, chosen on the device by
     // the number of overflowing rows

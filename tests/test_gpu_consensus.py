@@ -102,7 +102,8 @@ def test_consensus_routing_matches_oracle(lsa, w):
     assert bad == 0
 
 
-# rows with 4096 or more candidate blocks: the router's lean second pass
+# rows with 4096 or more candidate blocks (fp32 group queries keep the router's
+# full second pass at any length)
 @pytest.mark.parametrize("w", [custom(1, 4, 2, 81920, 16, 16, 128, dist="topics", seed=24),
                                custom(1, 4, 2, 65536, 16, 8, 0, causal=0, seed=25)],
                          ids=lambda w: w.name)

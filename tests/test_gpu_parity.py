@@ -106,8 +106,10 @@ def test_routing_matches_oracle(lsa, w):
 
 
 # Rows with 4096 or more candidate blocks take the router's lean second pass
-# (hi-only scores, survivors rescored exactly); these cases reach it at a
-# modest size with 16-token blocks.
+# (hi-only scores, survivors rescored exactly) when the queries are bf16;
+# the causal cases reach it at a modest size with 16-token blocks, the image
+# case (pooled fp32 queries) checks that long fp32-query rows keep the full
+# pass.
 LONG_ROW_CASES = [
     custom(1, 2, 1, 81920, 16, 16, 128, dist="topics", seed=21),
     custom(1, 3, 1, 65536 + 16 * 300, 16, 7, 64, seed=22),
