@@ -34,10 +34,13 @@
  *   - Determinism: the same inputs give bitwise identical outputs.  A row
  *     whose k-th and (k+1)-th routing scores agree to within fp32 rounding
  *     may keep either block; which one can depend on the rest of the input
- *     (rows that overflow the router's fast path are rescored by an exact
- *     pass, one by one with fp32 FMA chains when few rows need it, by whole
- *     tiles with the fast path's bf16 hi+lo products when many do), but never
- *     on the stream, the run or the calling thread.
+ *     (the fp32-accurate scores come from bf16 hi+lo MFMA products, or, when
+ *     the launch's longest bf16-query row has 4096 or more candidates, from
+ *     the hi product plus a bf16 dot product with the lo part; rows that
+ *     overflow the router's fast path are rescored by an exact pass, one by
+ *     one with fp32 FMA chains when at most 16384 rows need it, by whole
+ *     tiles with the hi+lo products when more do), but never on the stream,
+ *     the run or the calling thread.
  *   - Calls on distinct streams with distinct workspaces may run
  *     concurrently.
  */
