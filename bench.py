@@ -46,52 +46,52 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18491.9, 8444.0),
+            "V transpose + bucket count": (18491.8, 8444.0),
             "bucket scan": (5.6, 12.1),
-            "bucket scatter": (26330.4, 69724.1),
+            "bucket scatter": (26329.9, 69937.8),
             "key summary": (4141.7, 528.0),
-            "routed-block partials": (460850.5, 964073.3),
-            "routing": (29523.3, 28672.0),
-            "routing fallback": (36.0, 0.0),
-            "window + merge": (531057.3, 114688.4),
+            "routed-block partials": (460656.6, 963995.3),
+            "routing": (29525.0, 28672.0),
+            "routing fallback": (30.0, 0.0),
+            "window + merge": (531154.2, 114688.5),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (73789.0, 34808.0),
             "bucket scan": (11.6, 48.1),
-            "bucket scatter": (115495.1, 514376.6),
-            "key summary": (16430.8, 2112.0),
-            "routed-block partials": (1918627.4, 3909815.3),
-            "routing": (119631.2, 114690.5),
-            "routing fallback": (36.0, 0.0),
-            "window + merge": (2187562.6, 458753.1),
+            "bucket scatter": (115513.9, 514158.9),
+            "key summary": (16430.9, 2112.0),
+            "routed-block partials": (1918581.0, 3909760.0),
+            "routing": (119632.5, 114693.7),
+            "routing fallback": (30.0, 0.0),
+            "window + merge": (2187314.2, 458753.1),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (65553.7, 131072.0),
-            "key summary": (131162.0, 49283.0),
-            "routing": (16818.5, 2048.0),
-            "routing fallback": (37.8, 0.0),
-            "window + merge": (211851.8, 262159.8),
+            "V transpose + bucket count": (65553.5, 131072.0),
+            "key summary": (131162.5, 49282.2),
+            "routing": (16815.4, 2048.0),
+            "routing fallback": (32.0, 0.0),
+            "window + merge": (211827.3, 262169.8),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "0e8dc9e24424637d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589886.5, 393151.9),
+            "V transpose + bucket count": (589886.7, 393151.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (964467.3, 6938793.5),
-            "key summary": (131120.6, 16896.0),
-            "routed-block partials": (15571569.7, 31407445.1),
-            "routing": (1431195.6, 917588.7),
-            "routing fallback": (469584.4, 91.4),
-            "window + merge": (19910359.2, 3670022.8),
+            "bucket scatter": (964285.5, 6944686.5),
+            "key summary": (131120.1, 16896.0),
+            "routed-block partials": (15570910.9, 31402906.4),
+            "routing": (1431175.2, 917588.7),
+            "routing fallback": (474757.0, 90.9),
+            "window + merge": (19910629.9, 3670024.6),
         },
     },
 }
