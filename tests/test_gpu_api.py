@@ -1,6 +1,7 @@
 """The C ABI's conventions on the GPU: lsa_forward without idx_out (the
 routes then live in the workspace) equals the call that returns them, for
-every routing variant; a call on a side stream equals one on the default
+every routing variant; lsa_forward's routes equal lsa_route_topk's on the
+same inputs; a call on a side stream equals one on the default
 stream bit for bit; a workspace of exactly lsa_workspace_bytes works and,
 when the routes must live in it, one byte less is refused before anything
 runs."""
@@ -53,6 +54,32 @@ def test_forward_without_idx_out_equals_with(lsa, make, over):
     torch.cuda.synchronize()
     assert i2 is None
     assert torch.equal(o1, o2)
+
+
+# lsa_forward writes the router's hi/lo split and chunk norm maxima from the
+# key-summary kernel; lsa_route_topk, handed K-bar, prepares them separately.
+# Both use the same arithmetic, so the routes must agree bit for bit:
+# block sizes 16 to 128, block counts that leave a partial 32-block chunk,
+# rows long enough for the lean second pass, and image mode.
+PREP_CASES = [
+    Workload("prep_bs16", 1, 3, 1, 16 * 150, 64, 16, 8, 64, 1, "topics", topics=8, seed=71),
+    Workload("prep_bs32", 2, 2, 2, 32 * 77, 64, 32, 5, 96, 1, "normal", seed=72),
+    Workload("prep_bs64", 1, 4, 2, 64 * 70, 64, 64, 16, 192, 1, "topics", topics=16, seed=73),
+    Workload("prep_bs128", 1, 2, 1, 128 * 41, 64, 128, 4, 256, 1, "normal", seed=74),
+    Workload("prep_long", 1, 2, 1, 16 * 4200, 64, 16, 16, 64, 1, "topics", topics=16, seed=75),
+    Workload("prep_image", 2, 2, 2, 16 * 80, 64, 16, 6, 0, 0, "normal", seed=76),
+]
+
+
+@pytest.mark.parametrize("w", PREP_CASES, ids=lambda w: w.name)
+def test_forward_routes_equal_route_topk_routes(lsa, w):
+    inp = generate(w)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    p = params_of(lsa, w)
+    _, i_fwd = lsa.forward(p, q, k, v)
+    i_rt = lsa.route_topk(p, q, lsa.block_summarize(p, k))
+    torch.cuda.synchronize()
+    assert torch.equal(i_fwd, i_rt)
 
 
 def test_forward_on_a_side_stream_equals_default_stream(lsa):
