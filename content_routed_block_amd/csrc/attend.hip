@@ -425,9 +425,7 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     const int E = valid ? eligible_blocks(t, a.bs, a.window) : 0;
     const int lo_t = valid ? a.bs * E : a.N;
     const int64_t row = (int64_t)bh * a.N + t;
-    // rows of the pair-position table, and this head's gathered row of a
-    // pair: group rows and head hh with group pairs
-    const int64_t rev_row = a.expand > 1 ? (int64_t)bg * a.N + t : row;
+    // this head's gathered row of a pair: head hh with group pairs
     const uint32_t head_off = a.expand > 1 ? (uint32_t)hh : 0u;
 
     bf16x8 Bq[2];
@@ -436,6 +434,15 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     int csel[kMaxTopK];
     const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
     const uint32_t used = valid ? row_used(a.idx + irow * a.top_k, a.top_k, E, csel) : 0u;
+    // the pair positions of the row's routed slots from the slot-major table
+    // (rows are group rows with group pairs; the wave's 16 rows are
+    // consecutive, so each load is contiguous), requested before the window
+    // so that the merge's log-mass gathers can start as soon as it is done
+    const int64_t rev_row = a.expand > 1 ? (int64_t)bg * a.N + t : row;
+    uint32_t rs[kMaxTopK];
+#pragma unroll
+    for (int sl = 0; sl < kMaxTopK; ++sl)
+        rs[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.rev[sl * a.rows + rev_row] : 0u;
     f32x4 o[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -519,15 +526,10 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     // partial row stores dim 16mt + 4j + r at slot 16j + 4mt + r
     const int64_t prow = (((int64_t)bh << a.pc_log2) + (t - a.t_base)) << a.sp_log2;
     const uint32_t pos_base = uniform_load(a.offsets + a.b0);
-    // log2 masses: the pair positions from the slot-major table (the wave's
-    // 16 rows are consecutive, so each load is contiguous), then one 4-byte
-    // gather per used slot (group pairs: head hh's gathered row of the pair)
+    // log2 masses: one 4-byte gather per used slot at its pair position
+    // (group pairs: head hh's gathered row of the pair)
     float lse_all[kMaxTopK];
     {
-        uint32_t rs[kMaxTopK];
-#pragma unroll
-        for (int sl = 0; sl < kMaxTopK; ++sl)
-            rs[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.rev[sl * a.rows + rev_row] : 0u;
 #pragma unroll
         for (int sl = 0; sl < kMaxTopK; ++sl)
             lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u))
