@@ -46,52 +46,52 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18491.8, 8444.0),
+            "V transpose + bucket count": (18492.0, 8444.0),
             "bucket scan": (5.6, 12.1),
-            "bucket scatter": (26329.9, 69937.8),
-            "key summary": (4141.7, 528.0),
-            "routed-block partials": (460656.6, 963995.3),
-            "routing": (29525.0, 28672.0),
+            "bucket scatter": (26334.6, 69984.6),
+            "key summary": (4141.5, 528.0),
+            "routed-block partials": (460551.8, 964158.2),
+            "routing": (29519.6, 28672.0),
             "routing fallback": (30.0, 0.0),
-            "window + merge": (531154.2, 114688.5),
+            "window + merge": (531067.4, 114688.9),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73789.0, 34808.0),
+            "V transpose + bucket count": (73788.9, 34808.0),
             "bucket scan": (11.6, 48.1),
-            "bucket scatter": (115513.9, 514158.9),
-            "key summary": (16430.9, 2112.0),
-            "routed-block partials": (1918581.0, 3909760.0),
-            "routing": (119632.5, 114693.7),
+            "bucket scatter": (115483.2, 512981.5),
+            "key summary": (16430.8, 2112.0),
+            "routed-block partials": (1918862.5, 3909894.8),
+            "routing": (119546.0, 114688.5),
             "routing fallback": (30.0, 0.0),
-            "window + merge": (2187314.2, 458753.1),
+            "window + merge": (2194645.5, 458758.5),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (65553.5, 131072.0),
-            "key summary": (131162.5, 49282.2),
+            "key summary": (131162.5, 49282.1),
             "routing": (16815.4, 2048.0),
             "routing fallback": (32.0, 0.0),
-            "window + merge": (211827.3, 262169.8),
+            "window + merge": (211885.2, 262167.9),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "dd401e9e99f520fa", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589886.7, 393151.9),
+            "V transpose + bucket count": (589886.4, 393151.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (964285.5, 6944686.5),
+            "bucket scatter": (964337.0, 6945591.1),
             "key summary": (131120.1, 16896.0),
-            "routed-block partials": (15570910.9, 31402906.4),
-            "routing": (1431175.2, 917588.7),
-            "routing fallback": (474757.0, 90.9),
-            "window + merge": (19910629.9, 3670024.6),
+            "routed-block partials": (15570056.7, 31401846.8),
+            "routing": (1431436.1, 917587.3),
+            "routing fallback": (480913.9, 91.0),
+            "window + merge": (20133533.2, 3670085.0),
         },
     },
 }
