@@ -850,12 +850,12 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     const int nch = (g.N + (1 << P.tc_log2) - 1) >> P.tc_log2;
     const dim3 bgrid((unsigned)(nbg * nch));
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
-    hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
+    launch_bucket<false>(bgrid, lds, s, ba);
     mark(ev, 4, s);
     hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
                        NB, expand);
     mark(ev, 5, s);
-    hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
+    launch_bucket<true>(bgrid, lds, s, ba);
     mark(ev, 6, s);
 
     // stage events: with one chunk, 7 follows the partials and 8 the merge;

@@ -14,11 +14,9 @@ constexpr int BK_LDS_MAX = 16384;  // largest bucket count per group histogramme
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// Used-slot mask of one idx row: an entry counts when it is a candidate
-// (< ncand) and larger than the previously used entry.  Read with 16-byte
-// loads when the row length allows.
-__device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int ncand,
-                                             int (&c)[kMaxTopK]) {
+// The top_k entries of one idx row (16-byte loads when the row length
+// allows); entries past top_k are left as they are.
+__device__ __forceinline__ void load_idx_row(const int32_t* ir, int top_k, int (&c)[kMaxTopK]) {
     if ((top_k & 3) == 0) {
 #pragma unroll
         for (int s4 = 0; s4 < kMaxTopK / 4; ++s4) {
@@ -32,6 +30,28 @@ __device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int n
         for (int s = 0; s < kMaxTopK; ++s)
             if (s < top_k) c[s] = ir[s];
     }
+}
+
+// The same with the row's length fixed at compile time: KV 16-byte loads
+// (top_k = 4 * KV), or, for KV = 0, the runtime-length form above.  Fixed
+// lengths leave no guard between the loads of consecutive rows, so a
+// thread's loads for several rows issue back to back.
+template <int KV>
+__device__ __forceinline__ void load_idx_row_kv(const int32_t* ir, int top_k, int (&c)[kMaxTopK]) {
+    if constexpr (KV == 0) {
+        load_idx_row(ir, top_k, c);
+    } else {
+#pragma unroll
+        for (int s4 = 0; s4 < KV; ++s4) {
+            const i32x4 v = *reinterpret_cast<const i32x4*>(ir + 4 * s4);
+            c[4 * s4] = v[0]; c[4 * s4 + 1] = v[1]; c[4 * s4 + 2] = v[2]; c[4 * s4 + 3] = v[3];
+        }
+    }
+}
+
+// Used-slot mask of loaded idx entries: an entry counts when it is a
+// candidate (< ncand) and larger than the previously used entry.
+__device__ __forceinline__ uint32_t used_mask(const int (&c)[kMaxTopK], int top_k, int ncand) {
     uint32_t mask = 0;
     int prev = -1;
 #pragma unroll
@@ -43,6 +63,14 @@ __device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int n
     }
     return mask;
 }
+
+// Used-slot mask of one idx row, loading it.
+__device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int ncand,
+                                             int (&c)[kMaxTopK]) {
+    load_idx_row(ir, top_k, c);
+    return used_mask(c, top_k, ncand);
+}
+
 
 // ------------------------------------------------------------ bucketing
 struct BucketArgs {
@@ -89,7 +117,9 @@ __device__ __forceinline__ void write_rev_row(uint32_t* rev, int64_t rows, int64
 // heads of the group.  Histogram in LDS (when nb fits), then one global
 // atomic per touched bucket: counts (SCATTER = false) or a reserved range
 // of the pair list that pass B fills (SCATTER = true).
-template <bool SCATTER>
+// KV: the idx row length in 16-byte vectors when top_k is a multiple of 4
+// (top_k = 4 * KV), else 0.
+template <bool SCATTER, int KV>
 __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     extern __shared__ uint32_t s_h[];
     const int tid = threadIdx.x;
@@ -115,34 +145,65 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
         const int64_t r = a.group_pairs ? (int64_t)bg : (int64_t)b * a.Hq + g * rep + hh;
         return (r << a.pc_log2) + (t & ((1 << a.pc_log2) - 1));
     };
-    if (lds) {
-        for (int c = tid; c < a.nb; c += 256) s_h[c] = 0;
-        __syncthreads();
-    }
-    for (int i = tid; i < nh * span; i += 256) {
-        const int hh = i / span, t = t0 + (i - hh * span);
-        const int64_t row = row_of(hh, t);
-        const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
-        int c[kMaxTopK];
-        uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, bucket_candidates(a, t), c);
-        uint32_t posv[kMaxTopK];
+    const int total = nh * span;
+    if (!lds) {
+        // block counts beyond the LDS histogram: global atomics per pair
+        for (int i = tid; i < total; i += 256) {
+            const int hh = i / span, t = t0 + (i - hh * span);
+            const int64_t row = row_of(hh, t);
+            const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
+            int c[kMaxTopK];
+            uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, bucket_candidates(a, t), c);
+            uint32_t posv[kMaxTopK];
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            posv[s] = 0xFFFFFFFFu;
-            if (!((m >> s) & 1u)) continue;
-            if (lds) {
-                atomicAdd(&s_h[c[s]], 1u);
-            } else if (!SCATTER) {
-                atomicAdd(&a.counts[bucket0 + c[s]], 1u);
-            } else {
-                const uint32_t pos = atomicAdd(&a.cursor[bucket0 + c[s]], 1u);
-                a.pairs[pos] = (uint32_t)((pair_row(hh, t, row) << a.sp_log2) | s);
-                posv[s] = pos;
+            for (int s = 0; s < kMaxTopK; ++s) {
+                posv[s] = 0xFFFFFFFFu;
+                if (!((m >> s) & 1u)) continue;
+                if (!SCATTER) {
+                    atomicAdd(&a.counts[bucket0 + c[s]], 1u);
+                } else {
+                    const uint32_t pos = atomicAdd(&a.cursor[bucket0 + c[s]], 1u);
+                    a.pairs[pos] = (uint32_t)((pair_row(hh, t, row) << a.sp_log2) | s);
+                    posv[s] = pos;
+                }
             }
+            if (SCATTER) write_rev_row(a.rev, a.rows, row, posv, a.top_k);
         }
-        if (SCATTER && !lds) write_rev_row(a.rev, a.rows, row, posv, a.top_k);
+        return;
     }
-    if (!lds) return;
+    // The LDS passes walk BU rows per thread per step: every idx load of the
+    // step is issued before the first mask needs one (a thread past the end
+    // loads the chunk's last row and drops it).
+    constexpr int BU = 4;
+    struct Rows {
+        int c[BU][kMaxTopK];
+        int t[BU], hh[BU];
+    };
+    auto load_rows = [&](int i0, Rows& r) {
+#pragma unroll
+        for (int u = 0; u < BU; ++u) {
+            const int i = min(i0 + 256 * u, total - 1);
+            r.hh[u] = i / span;
+            r.t[u] = t0 + (i - r.hh[u] * span);
+            const int64_t irow = a.group_route ? (int64_t)bg * a.N + r.t[u] : row_of(r.hh[u], r.t[u]);
+            load_idx_row_kv<KV>(a.idx + irow * a.top_k, a.top_k, r.c[u]);
+        }
+    };
+    for (int c = tid; c < a.nb; c += 256) s_h[c] = 0;
+    __syncthreads();
+    for (int i0 = tid; i0 < total; i0 += 256 * BU) {
+        Rows r;
+        load_rows(i0, r);
+#pragma unroll
+        for (int u = 0; u < BU; ++u) {
+            const uint32_t m = (i0 + 256 * u < total)
+                                   ? used_mask(r.c[u], a.top_k, bucket_candidates(a, r.t[u]))
+                                   : 0u;
+#pragma unroll
+            for (int s = 0; s < kMaxTopK; ++s)
+                if ((m >> s) & 1u) atomicAdd(&s_h[r.c[u][s]], 1u);
+        }
+    }
     __syncthreads();
     for (int cc = tid; cc < a.nb; cc += 256) {
         const uint32_t n = s_h[cc];
@@ -154,22 +215,37 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     }
     if (!SCATTER) return;
     __syncthreads();
-    for (int i = tid; i < nh * span; i += 256) {
-        const int hh = i / span, t = t0 + (i - hh * span);
-        const int64_t row = row_of(hh, t);
-        const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
-        int c[kMaxTopK];
-        uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, bucket_candidates(a, t), c);
-        // all LDS reservations first (their latencies overlap), then the stores
-        uint32_t posv[kMaxTopK];
+    for (int i0 = tid; i0 < total; i0 += 256 * BU) {
+        Rows r;
+        load_rows(i0, r);
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
-            posv[s] = ((m >> s) & 1u) ? atomicAdd(&s_h[c[s]], 1u) : 0xFFFFFFFFu;
-        const int64_t prow = pair_row(hh, t, row);
+        for (int u = 0; u < BU; ++u) {
+            if (i0 + 256 * u >= total) break;
+            const uint32_t m = used_mask(r.c[u], a.top_k, bucket_candidates(a, r.t[u]));
+            const int64_t row = row_of(r.hh[u], r.t[u]);
+            // all LDS reservations first (their latencies overlap), then the stores
+            uint32_t posv[kMaxTopK];
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
-            if ((m >> s) & 1u) a.pairs[posv[s]] = (uint32_t)((prow << a.sp_log2) | s);
-        write_rev_row(a.rev, a.rows, row, posv, a.top_k);
+            for (int s = 0; s < kMaxTopK; ++s)
+                posv[s] = ((m >> s) & 1u) ? atomicAdd(&s_h[r.c[u][s]], 1u) : 0xFFFFFFFFu;
+            const int64_t prow = pair_row(r.hh[u], r.t[u], row);
+#pragma unroll
+            for (int s = 0; s < kMaxTopK; ++s)
+                if ((m >> s) & 1u) a.pairs[posv[s]] = (uint32_t)((prow << a.sp_log2) | s);
+            write_rev_row(a.rev, a.rows, row, posv, a.top_k);
+        }
+    }
+}
+
+// Launches k_bucket<SCATTER, KV> with KV picked from a.top_k.
+template <bool SCATTER>
+static inline void launch_bucket(dim3 grid, size_t lds, hipStream_t s, const BucketArgs& a) {
+    switch ((a.top_k & 3) == 0 ? a.top_k / 4 : 0) {
+        case 1: hipLaunchKernelGGL((k_bucket<SCATTER, 1>), grid, dim3(256), lds, s, a); break;
+        case 2: hipLaunchKernelGGL((k_bucket<SCATTER, 2>), grid, dim3(256), lds, s, a); break;
+        case 3: hipLaunchKernelGGL((k_bucket<SCATTER, 3>), grid, dim3(256), lds, s, a); break;
+        case 4: hipLaunchKernelGGL((k_bucket<SCATTER, 4>), grid, dim3(256), lds, s, a); break;
+        default: hipLaunchKernelGGL((k_bucket<SCATTER, 0>), grid, dim3(256), lds, s, a); break;
     }
 }
 

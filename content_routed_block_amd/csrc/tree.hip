@@ -289,10 +289,10 @@ hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const float*
     const int nch = (int)((P + tc - 1) / tc);
     const dim3 bgrid((unsigned)(nbg * nch));
     const size_t lds = L.nodes <= BK_LDS_MAX ? (size_t)L.nodes * 4 : 0;
-    hipLaunchKernelGGL(k_bucket<false>, bgrid, dim3(256), lds, s, ba);
+    launch_bucket<false>(bgrid, lds, s, ba);
     hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
                        L.NB, 1);
-    hipLaunchKernelGGL(k_bucket<true>, bgrid, dim3(256), lds, s, ba);
+    launch_bucket<true>(bgrid, lds, s, ba);
 
     TreeScoreArgs sa{q, qbar, bhi, blo, pairs, offsets, unit_off, scores,
                      (uint32_t)(rows * nslots), L.nodes, L.NB, nb_pad, sp_log2};
