@@ -46,52 +46,52 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18492.0, 8444.0),
-            "bucket scan": (5.6, 12.1),
-            "bucket scatter": (26334.6, 69984.6),
-            "key summary": (4141.5, 528.0),
-            "routed-block partials": (460551.8, 964158.2),
-            "routing": (29519.6, 28672.0),
+            "V transpose + bucket count": (18536.6, 8444.0),
+            "bucket scan": (5.4, 12.1),
+            "bucket scatter": (21088.2, 69528.7),
+            "key summary": (4141.7, 528.0),
+            "routed-block partials": (460322.5, 963904.0),
+            "routing": (29537.7, 28672.0),
             "routing fallback": (30.0, 0.0),
-            "window + merge": (531067.4, 114688.9),
+            "window + merge": (530956.4, 114688.8),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73788.9, 34808.0),
-            "bucket scan": (11.6, 48.1),
-            "bucket scatter": (115483.2, 512981.5),
+            "V transpose + bucket count": (73834.2, 34808.0),
+            "bucket scan": (11.4, 48.1),
+            "bucket scatter": (115612.9, 480827.6),
             "key summary": (16430.8, 2112.0),
-            "routed-block partials": (1918862.5, 3909894.8),
-            "routing": (119546.0, 114688.5),
+            "routed-block partials": (1919022.7, 3909892.2),
+            "routing": (119047.6, 114688.8),
             "routing fallback": (30.0, 0.0),
-            "window + merge": (2194645.5, 458758.5),
+            "window + merge": (2194363.3, 458758.1),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (65553.5, 131072.0),
-            "key summary": (131162.5, 49282.1),
+            "key summary": (131162.5, 49282.0),
             "routing": (16815.4, 2048.0),
             "routing fallback": (32.0, 0.0),
-            "window + merge": (211885.2, 262167.9),
+            "window + merge": (211808.1, 262169.0),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "7b107d1b2ce18b17", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589886.4, 393151.9),
+            "V transpose + bucket count": (589931.3, 393151.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (964337.0, 6945591.1),
-            "key summary": (131120.1, 16896.0),
-            "routed-block partials": (15570056.7, 31401846.8),
-            "routing": (1431436.1, 917587.3),
-            "routing fallback": (480913.9, 91.0),
-            "window + merge": (20133533.2, 3670085.0),
+            "bucket scatter": (955176.9, 6898283.7),
+            "key summary": (131120.5, 16896.0),
+            "routed-block partials": (15570444.5, 31398167.5),
+            "routing": (1430447.8, 917589.0),
+            "routing fallback": (475921.0, 90.8),
+            "window + merge": (20125695.7, 3670086.4),
         },
     },
 }
