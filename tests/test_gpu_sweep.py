@@ -1,5 +1,6 @@
 """Parity over a seeded sweep of random valid shapes, for every routing
-variant (per-head, consensus, second-cumulant, two-level) and for decode.
+variant (per-head, consensus, second-cumulant, two-level) and for decode,
+plus causal shapes long enough for the router's lean second pass.
 
 The fixed cases in the other GPU suites pick shapes by hand; this sweep draws
 them: block size, window width in blocks (odd counts included), top-k, GQA
@@ -46,7 +47,27 @@ def draw(n, seed, causal=True, tag="sw"):
     return out
 
 
+def draw_long(n, seed, tag="long"):
+    """Causal shapes whose longest rows have 4096 or more candidate blocks
+    (the router's lean second pass), checked on sampled rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        bs = int(rng.choice([16, 32]))
+        wb = int(rng.integers(1, 9))
+        m = 4096 + wb - 1 + int(rng.integers(0, 1200))       # blocks: E(N-1) >= 4096
+        k = int(rng.integers(1, 17))
+        Hkv = int(rng.integers(1, 3))
+        rep = int(rng.choice([1, 2, 3, 7]))
+        dist = "topics" if rng.random() < 0.5 else "normal"
+        out.append(Workload(f"{tag}{i}_h{Hkv * rep}x{Hkv}_n{bs * m}_bs{bs}_k{k}_w{bs * wb}_{dist}",
+                            1, Hkv * rep, Hkv, bs * m, 64, bs, k, bs * wb, 1, dist,
+                            topics=16 if dist == "topics" else 0, seed=seed * 100 + i))
+    return out
+
+
 FLAT = draw(64, 31) + draw(16, 32, causal=False, tag="img")
+LONG = draw_long(12, 41)
 CONSENSUS = draw(20, 33, tag="cons") + draw(8, 34, causal=False, tag="consimg")
 CUMULANT = [(w, float(b)) for w, b in zip(draw(20, 35, tag="cum"),
                                           np.random.default_rng(40).choice([0.125, 1.0, -0.5, 2.0], 20))]
@@ -69,6 +90,11 @@ def test_sweep_summary(lsa, w):
 @pytest.mark.parametrize("w", FLAT, ids=name)
 def test_sweep_forward(lsa, w):
     P.test_forward_matches_oracle(lsa, w)
+
+
+@pytest.mark.parametrize("w", LONG, ids=name)
+def test_sweep_long_rows_routing(lsa, w):
+    P.test_routing_long_rows_sampled(lsa, w)
 
 
 @pytest.mark.parametrize("w", CONSENSUS, ids=name)
