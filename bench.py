@@ -134,6 +134,9 @@ def parse():
     ap.add_argument("--workload", default="qwen05b_n128k_needles")
     ap.add_argument("--chunk", type=int, default=0,
                     help="query positions per attention chunk (0: the library's choice)")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="run the workload with this many routed blocks per query (1..32; "
+                         "0: the workload's own); the line then names the changed workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -606,6 +609,9 @@ def main():
     from content_routed_block_amd.workloads import WORKLOADS, generate
 
     w = WORKLOADS[args.workload]
+    if args.top_k and args.top_k != w.top_k:
+        import dataclasses
+        w = dataclasses.replace(w, name=f"{w.name}_k{args.top_k}", top_k=args.top_k)
     inp = generate(w)
     dev = torch.device("cuda:0")
 

@@ -188,11 +188,12 @@ __device__ __forceinline__ int nth_slot(uint32_t mask, int n) {
     return __builtin_ctz(mask);
 }
 
-// c[i] for a runtime i < kMaxTopK without dynamic register indexing.
-__device__ __forceinline__ int pick(const int (&c)[kMaxTopK], int i) {
+// c[i] for a runtime i < KM without dynamic register indexing.
+template <int KM>
+__device__ __forceinline__ int pick(const int (&c)[KM], int i) {
     int v = 0;
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) v = (s == i) ? c[s] : v;
+    for (int s = 0; s < KM; ++s) v = (s == i) ? c[s] : v;
     return v;
 }
 
@@ -393,8 +394,10 @@ struct WinArgs {
 // used.  A row's running max is raised only when a chunk exceeds it by
 // RESCALE_SLACK (log2 units), so most chunks skip rescaling the
 // accumulator; masks are applied only on chunks that cross a row's window
-// start or its causal end.
-__global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
+// start or its causal end.  KM: the row's slot list length (kMaxTopK, or
+// kMaxTopKWide for top_k above it, at lower occupancy).
+template <int KM>
+__global__ __launch_bounds__(256, KM > kMaxTopK ? 2 : 4) void k_window_merge(WinArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_k[2][64 * KPITCH];
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][kD * WVP];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -431,17 +434,17 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     bf16x8 Bq[2];
     load_q_operand(a.q + row * kD, lane, valid, Bq);
     // the row's routed slots, read now so the loads overlap the window work
-    int csel[kMaxTopK];
+    int csel[KM];
     const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
-    const uint32_t used = valid ? row_used(a.idx + irow * a.top_k, a.top_k, E, csel) : 0u;
+    const uint32_t used = valid ? row_used<KM>(a.idx + irow * a.top_k, a.top_k, E, csel) : 0u;
     // the pair positions of the row's routed slots from the slot-major table
     // (rows are group rows with group pairs; the wave's 16 rows are
     // consecutive, so each load is contiguous), requested before the window
     // so that the merge's log-mass gathers can start as soon as it is done
     const int64_t rev_row = a.expand > 1 ? (int64_t)bg * a.N + t : row;
-    uint32_t rs[kMaxTopK];
+    uint32_t rs[KM];
 #pragma unroll
-    for (int sl = 0; sl < kMaxTopK; ++sl)
+    for (int sl = 0; sl < KM; ++sl)
         rs[sl] = (sl < a.top_k && ((used >> sl) & 1u)) ? a.rev[sl * a.rows + rev_row] : 0u;
     f32x4 o[4];
 #pragma unroll
@@ -528,16 +531,16 @@ __global__ __launch_bounds__(256, 4) void k_window_merge(WinArgs a) {
     const uint32_t pos_base = uniform_load(a.offsets + a.b0);
     // log2 masses: one 4-byte gather per used slot at its pair position
     // (group pairs: head hh's gathered row of the pair)
-    float lse_all[kMaxTopK];
+    float lse_all[KM];
     {
 #pragma unroll
-        for (int sl = 0; sl < kMaxTopK; ++sl)
+        for (int sl = 0; sl < KM; ++sl)
             lse_all[sl] = (sl < a.top_k && ((used >> sl) & 1u))
                               ? a.part_lse[(rs[sl] - pos_base) * (uint32_t)a.expand + head_off]
                               : -INFINITY;
     }
 #pragma unroll
-    for (int s0 = 0; s0 < kMaxTopK; s0 += 8) {
+    for (int s0 = 0; s0 < KM; s0 += 8) {
         if (s0 >= a.top_k) break;
         u32x4 po[8][2];
 #pragma unroll
@@ -591,7 +594,8 @@ struct ImgArgs {
 // One wave per 16-token query block (block size 16).  The selected blocks
 // are processed four at a time (64 keys) with an online softmax; K feeds the
 // MFMA straight from global memory, the blocks' V^T columns are copied into
-// the wave's own LDS region.
+// the wave's own LDS region.  KM: the slot list length, as in k_window_merge.
+template <int KM>
 __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_vt[4][kD * WVP];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -614,8 +618,8 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 
     // the used slots of this query block's idx row (wave-uniform)
     const int64_t irow = a.group_route ? bg * a.nb + i : qb;
-    int csel[kMaxTopK];
-    const uint32_t used = row_used(a.idx + irow * a.top_k, a.top_k, a.nb, csel);
+    int csel[KM];
+    const uint32_t used = row_used<KM>(a.idx + irow * a.top_k, a.top_k, a.nb, csel);
     const int nused = __builtin_popcount(used);
 
     bf16x8 Bq[2];
@@ -637,7 +641,7 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             const bool have = c0 + jb < nused;
-            cblk[jb] = have ? pick(csel, nth_slot(used, c0 + jb)) : 0;
+            cblk[jb] = have ? pick<KM>(csel, nth_slot(used, c0 + jb)) : 0;
             const uint16_t* kr =
                 a.k + k0 + ((int64_t)cblk[jb] * 16 + (lane & 15)) * kD + 8 * (lane >> 4);
             const uint16_t* src = a.vt + vt0 + (int64_t)cblk[jb] * (kD * 16) + lane * 16;
@@ -821,7 +825,10 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
                   (int64_t)g.B * g.Hq * g.nb, scale_log2, g.consensus};
         const unsigned grid = (unsigned)(((a.n_qblocks + 3) / 4 + 7) / 8 * 8);  // multiple of 8
         for (int i = 4; i < 8; ++i) mark(ev, i, s);
-        hipLaunchKernelGGL(k_image_attend, dim3(grid), dim3(256), 0, s, a);
+        if (g.top_k <= kMaxTopK)
+            hipLaunchKernelGGL(k_image_attend<kMaxTopK>, dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_image_attend<kMaxTopKWide>, dim3(grid), dim3(256), 0, s, a);
         mark(ev, 8, s);
         return hipGetLastError();
     }
@@ -880,7 +887,11 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
                    g.bs, g.top_k, g.window, wtiles, nbg * rep * wtiles, ntiles, sp_log2, b0,
                    P.pc_log2, t_base, scale_log2, g.consensus, expand};
         const int64_t wgrid = ((int64_t)wa.items + 7) / 8 * 8;  // multiple of the XCD count
-        hipLaunchKernelGGL(k_window_merge, dim3((unsigned)wgrid), dim3(256), 0, s, wa);
+        if (g.top_k <= kMaxTopK)
+            hipLaunchKernelGGL(k_window_merge<kMaxTopK>, dim3((unsigned)wgrid), dim3(256), 0, s, wa);
+        else
+            hipLaunchKernelGGL(k_window_merge<kMaxTopKWide>, dim3((unsigned)wgrid), dim3(256), 0, s,
+                               wa);
     }
     if (P.nchunk > 1) mark(ev, 7, s);
     mark(ev, 8, s);

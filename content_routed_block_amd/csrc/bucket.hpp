@@ -15,11 +15,13 @@ constexpr int BK_LDS_MAX = 16384;  // largest bucket count per group histogramme
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // The top_k entries of one idx row (16-byte loads when the row length
-// allows); entries past top_k are left as they are.
-__device__ __forceinline__ void load_idx_row(const int32_t* ir, int top_k, int (&c)[kMaxTopK]) {
+// allows); entries past top_k are left as they are.  KM: the list length
+// the caller holds (kMaxTopK, or kMaxTopKWide for top_k above it).
+template <int KM = kMaxTopK>
+__device__ __forceinline__ void load_idx_row(const int32_t* ir, int top_k, int (&c)[KM]) {
     if ((top_k & 3) == 0) {
 #pragma unroll
-        for (int s4 = 0; s4 < kMaxTopK / 4; ++s4) {
+        for (int s4 = 0; s4 < KM / 4; ++s4) {
             if (4 * s4 < top_k) {
                 const i32x4 v = *reinterpret_cast<const i32x4*>(ir + 4 * s4);
                 c[4 * s4] = v[0]; c[4 * s4 + 1] = v[1]; c[4 * s4 + 2] = v[2]; c[4 * s4 + 3] = v[3];
@@ -27,7 +29,7 @@ __device__ __forceinline__ void load_idx_row(const int32_t* ir, int top_k, int (
         }
     } else {
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
+        for (int s = 0; s < KM; ++s)
             if (s < top_k) c[s] = ir[s];
     }
 }
@@ -36,10 +38,11 @@ __device__ __forceinline__ void load_idx_row(const int32_t* ir, int top_k, int (
 // (top_k = 4 * KV), or, for KV = 0, the runtime-length form above.  Fixed
 // lengths leave no guard between the loads of consecutive rows, so a
 // thread's loads for several rows issue back to back.
-template <int KV>
-__device__ __forceinline__ void load_idx_row_kv(const int32_t* ir, int top_k, int (&c)[kMaxTopK]) {
+template <int KV, int KM = kMaxTopK>
+__device__ __forceinline__ void load_idx_row_kv(const int32_t* ir, int top_k, int (&c)[KM]) {
+    static_assert(4 * KV <= KM, "row longer than the list");
     if constexpr (KV == 0) {
-        load_idx_row(ir, top_k, c);
+        load_idx_row<KM>(ir, top_k, c);
     } else {
 #pragma unroll
         for (int s4 = 0; s4 < KV; ++s4) {
@@ -51,11 +54,12 @@ __device__ __forceinline__ void load_idx_row_kv(const int32_t* ir, int top_k, in
 
 // Used-slot mask of loaded idx entries: an entry counts when it is a
 // candidate (< ncand) and larger than the previously used entry.
-__device__ __forceinline__ uint32_t used_mask(const int (&c)[kMaxTopK], int top_k, int ncand) {
+template <int KM = kMaxTopK>
+__device__ __forceinline__ uint32_t used_mask(const int (&c)[KM], int top_k, int ncand) {
     uint32_t mask = 0;
     int prev = -1;
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
+    for (int s = 0; s < KM; ++s) {
         if (s < top_k && c[s] > prev && c[s] < ncand) {
             mask |= 1u << s;
             prev = c[s];
@@ -65,10 +69,11 @@ __device__ __forceinline__ uint32_t used_mask(const int (&c)[kMaxTopK], int top_
 }
 
 // Used-slot mask of one idx row, loading it.
+template <int KM = kMaxTopK>
 __device__ __forceinline__ uint32_t row_used(const int32_t* ir, int top_k, int ncand,
-                                             int (&c)[kMaxTopK]) {
-    load_idx_row(ir, top_k, c);
-    return used_mask(c, top_k, ncand);
+                                             int (&c)[KM]) {
+    load_idx_row<KM>(ir, top_k, c);
+    return used_mask<KM>(c, top_k, ncand);
 }
 
 
@@ -106,10 +111,11 @@ __device__ __forceinline__ int bucket_candidates(const BucketArgs& a, int t) {
 
 // Writes one row's entries of the slot-major position table, so that the
 // lanes of a wave (consecutive rows) store consecutive words.
+template <int KM = kMaxTopK>
 __device__ __forceinline__ void write_rev_row(uint32_t* rev, int64_t rows, int64_t row,
-                                              const uint32_t (&pos)[kMaxTopK], int top_k) {
+                                              const uint32_t (&pos)[KM], int top_k) {
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s)
+    for (int s = 0; s < KM; ++s)
         if (s < top_k) rev[s * rows + row] = pos[s];
 }
 
@@ -118,8 +124,9 @@ __device__ __forceinline__ void write_rev_row(uint32_t* rev, int64_t rows, int64
 // atomic per touched bucket: counts (SCATTER = false) or a reserved range
 // of the pair list that pass B fills (SCATTER = true).
 // KV: the idx row length in 16-byte vectors when top_k is a multiple of 4
-// (top_k = 4 * KV), else 0.
-template <bool SCATTER, int KV>
+// (top_k = 4 * KV), else 0.  KM: the row list length held per row
+// (kMaxTopK, or kMaxTopKWide for top_k above it).
+template <bool SCATTER, int KV, int KM>
 __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     extern __shared__ uint32_t s_h[];
     const int tid = threadIdx.x;
@@ -152,11 +159,11 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
             const int hh = i / span, t = t0 + (i - hh * span);
             const int64_t row = row_of(hh, t);
             const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
-            int c[kMaxTopK];
-            uint32_t m = row_used(a.idx + irow * a.top_k, a.top_k, bucket_candidates(a, t), c);
-            uint32_t posv[kMaxTopK];
+            int c[KM];
+            uint32_t m = row_used<KM>(a.idx + irow * a.top_k, a.top_k, bucket_candidates(a, t), c);
+            uint32_t posv[KM];
 #pragma unroll
-            for (int s = 0; s < kMaxTopK; ++s) {
+            for (int s = 0; s < KM; ++s) {
                 posv[s] = 0xFFFFFFFFu;
                 if (!((m >> s) & 1u)) continue;
                 if (!SCATTER) {
@@ -167,16 +174,16 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
                     posv[s] = pos;
                 }
             }
-            if (SCATTER) write_rev_row(a.rev, a.rows, row, posv, a.top_k);
+            if (SCATTER) write_rev_row<KM>(a.rev, a.rows, row, posv, a.top_k);
         }
         return;
     }
     // The LDS passes walk BU rows per thread per step: every idx load of the
     // step is issued before the first mask needs one (a thread past the end
     // loads the chunk's last row and drops it).
-    constexpr int BU = 4;
+    constexpr int BU = KM > kMaxTopK ? 2 : 4;
     struct Rows {
-        int c[BU][kMaxTopK];
+        int c[BU][KM];
         int t[BU], hh[BU];
     };
     auto load_rows = [&](int i0, Rows& r) {
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
             r.hh[u] = i / span;
             r.t[u] = t0 + (i - r.hh[u] * span);
             const int64_t irow = a.group_route ? (int64_t)bg * a.N + r.t[u] : row_of(r.hh[u], r.t[u]);
-            load_idx_row_kv<KV>(a.idx + irow * a.top_k, a.top_k, r.c[u]);
+            load_idx_row_kv<KV, KM>(a.idx + irow * a.top_k, a.top_k, r.c[u]);
         }
     };
     for (int c = tid; c < a.nb; c += 256) s_h[c] = 0;
@@ -197,10 +204,10 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
 #pragma unroll
         for (int u = 0; u < BU; ++u) {
             const uint32_t m = (i0 + 256 * u < total)
-                                   ? used_mask(r.c[u], a.top_k, bucket_candidates(a, r.t[u]))
+                                   ? used_mask<KM>(r.c[u], a.top_k, bucket_candidates(a, r.t[u]))
                                    : 0u;
 #pragma unroll
-            for (int s = 0; s < kMaxTopK; ++s)
+            for (int s = 0; s < KM; ++s)
                 if ((m >> s) & 1u) atomicAdd(&s_h[r.c[u][s]], 1u);
         }
     }
@@ -221,31 +228,41 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
 #pragma unroll
         for (int u = 0; u < BU; ++u) {
             if (i0 + 256 * u >= total) break;
-            const uint32_t m = used_mask(r.c[u], a.top_k, bucket_candidates(a, r.t[u]));
+            const uint32_t m = used_mask<KM>(r.c[u], a.top_k, bucket_candidates(a, r.t[u]));
             const int64_t row = row_of(r.hh[u], r.t[u]);
             // all LDS reservations first (their latencies overlap), then the stores
-            uint32_t posv[kMaxTopK];
+            uint32_t posv[KM];
 #pragma unroll
-            for (int s = 0; s < kMaxTopK; ++s)
+            for (int s = 0; s < KM; ++s)
                 posv[s] = ((m >> s) & 1u) ? atomicAdd(&s_h[r.c[u][s]], 1u) : 0xFFFFFFFFu;
             const int64_t prow = pair_row(r.hh[u], r.t[u], row);
 #pragma unroll
-            for (int s = 0; s < kMaxTopK; ++s)
+            for (int s = 0; s < KM; ++s)
                 if ((m >> s) & 1u) a.pairs[posv[s]] = (uint32_t)((prow << a.sp_log2) | s);
-            write_rev_row(a.rev, a.rows, row, posv, a.top_k);
+            write_rev_row<KM>(a.rev, a.rows, row, posv, a.top_k);
         }
     }
 }
 
-// Launches k_bucket<SCATTER, KV> with KV picked from a.top_k.
+// Launches k_bucket<SCATTER, KV, KM> with KV and KM picked from a.top_k.
 template <bool SCATTER>
 static inline void launch_bucket(dim3 grid, size_t lds, hipStream_t s, const BucketArgs& a) {
+    constexpr int W = kMaxTopKWide;
     switch ((a.top_k & 3) == 0 ? a.top_k / 4 : 0) {
-        case 1: hipLaunchKernelGGL((k_bucket<SCATTER, 1>), grid, dim3(256), lds, s, a); break;
-        case 2: hipLaunchKernelGGL((k_bucket<SCATTER, 2>), grid, dim3(256), lds, s, a); break;
-        case 3: hipLaunchKernelGGL((k_bucket<SCATTER, 3>), grid, dim3(256), lds, s, a); break;
-        case 4: hipLaunchKernelGGL((k_bucket<SCATTER, 4>), grid, dim3(256), lds, s, a); break;
-        default: hipLaunchKernelGGL((k_bucket<SCATTER, 0>), grid, dim3(256), lds, s, a); break;
+        case 1: hipLaunchKernelGGL((k_bucket<SCATTER, 1, kMaxTopK>), grid, dim3(256), lds, s, a); break;
+        case 2: hipLaunchKernelGGL((k_bucket<SCATTER, 2, kMaxTopK>), grid, dim3(256), lds, s, a); break;
+        case 3: hipLaunchKernelGGL((k_bucket<SCATTER, 3, kMaxTopK>), grid, dim3(256), lds, s, a); break;
+        case 4: hipLaunchKernelGGL((k_bucket<SCATTER, 4, kMaxTopK>), grid, dim3(256), lds, s, a); break;
+        case 5: hipLaunchKernelGGL((k_bucket<SCATTER, 5, W>), grid, dim3(256), lds, s, a); break;
+        case 6: hipLaunchKernelGGL((k_bucket<SCATTER, 6, W>), grid, dim3(256), lds, s, a); break;
+        case 7: hipLaunchKernelGGL((k_bucket<SCATTER, 7, W>), grid, dim3(256), lds, s, a); break;
+        case 8: hipLaunchKernelGGL((k_bucket<SCATTER, 8, W>), grid, dim3(256), lds, s, a); break;
+        default:
+            if (a.top_k <= kMaxTopK)
+                hipLaunchKernelGGL((k_bucket<SCATTER, 0, kMaxTopK>), grid, dim3(256), lds, s, a);
+            else
+                hipLaunchKernelGGL((k_bucket<SCATTER, 0, W>), grid, dim3(256), lds, s, a);
+            break;
     }
 }
 

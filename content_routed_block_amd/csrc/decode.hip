@@ -61,7 +61,7 @@ struct DecodeArgs {
     float* kbar;         // [B*Hkv][t_max/bs][64]
     int32_t* idx;        // [B*Hq][top_k] or NULL
     float* out;          // [B*Hq][64]
-    uint64_t* keys;      // [B*Hq][nchunk][kMaxTopK] chunk key sets, zero-padded
+    uint64_t* keys;      // [B*Hq][nchunk][KS] chunk key sets, zero-padded (KS: see below)
     uint32_t* counters;  // [B*Hq] finished splits per row
     float* part;         // [B*Hq][nsplit][2 + 64]: max, mass, output (log2 domain)
     int rows, Hq, Hkv, T, t_max, bs, top_k, window, E, nchunk, nsplit, summ_block;
@@ -130,11 +130,12 @@ __device__ __forceinline__ int wave_compact(const uint64_t (&key)[n], uint64_t t
 // product accumulated over d in order); each wave selects its top_k, then the
 // first wave selects the chunk's top_k among the four wave sets.  Workgroups
 // past rows * nchunk update the block-mean cache instead (one per KV head);
-// workgroup 0 also clears the rows' split counters for step 2.
-template <int KPL>
+// workgroup 0 also clears the rows' split counters for step 2.  KS: the
+// length of a chunk key set (kMaxTopK, or kMaxTopKWide for top_k above it).
+template <int KPL, int KS>
 __global__ __launch_bounds__(256) void k_decode_route(DecodeArgs a) {
     __shared__ float s_q[kD];
-    __shared__ uint64_t s_list[4 * kMaxTopK];
+    __shared__ uint64_t s_list[4 * KS];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nroute = a.rows * a.nchunk;
     if ((int)blockIdx.x >= nroute) {
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(256) void k_decode_route(DecodeArgs a) {
     const int h = row % a.Hq, b = row / a.Hq;
     const int bg = b * a.Hkv + h / (a.Hq / a.Hkv);
     if (tid < kD) s_q[tid] = bf16_bits_to_f32(a.q[(int64_t)row * kD + tid]);
-    for (int i = tid; i < 4 * kMaxTopK; i += 256) s_list[i] = 0;
+    for (int i = tid; i < 4 * KS; i += 256) s_list[i] = 0;
     __syncthreads();
     const int c0 = ch * (256 * KPL) + w * (64 * KPL);
     const float* kb = a.kbar + (int64_t)bg * (a.t_max / a.bs) * kD;
@@ -205,14 +206,17 @@ __global__ __launch_bounds__(256) void k_decode_route(DecodeArgs a) {
             key[i] = sel_key(s, (uint32_t)c);
         }
     }
-    wave_compact(key, wave_kth_key(key, a.top_k), s_list + w * kMaxTopK);
+    wave_compact(key, wave_kth_key(key, a.top_k), s_list + w * KS);
     __syncthreads();
     if (w == 0) {
-        uint64_t k1[1] = {s_list[lane]};
+        constexpr int NW = 4 * KS / 64;  // the four wave sets, one or two keys per lane
+        uint64_t k1[NW];
+#pragma unroll
+        for (int i = 0; i < NW; ++i) k1[i] = s_list[lane + 64 * i];
         const uint64_t th = wave_kth_key(k1, a.top_k);
-        uint64_t* out = a.keys + ((int64_t)row * a.nchunk + ch) * kMaxTopK;
+        uint64_t* out = a.keys + ((int64_t)row * a.nchunk + ch) * KS;
         const int n = wave_compact(k1, th, out);
-        if (lane >= n && lane < kMaxTopK) out[lane] = 0;  // zero-pad the set
+        if (lane >= n && lane < KS) out[lane] = 0;  // zero-pad the set
     }
 }
 
@@ -238,14 +242,15 @@ __device__ __forceinline__ int merge_chunk_sets(const uint64_t* in, int ntot, in
 // [256 split, 256 split + 256): fp32 scores in log2 units, the split's
 // maximum and mass, and P.V with thread (key group kg, dims 8dg..8dg+7).
 // The split's (max, mass, output) goes to the workspace; the row's last
-// split to finish combines them.
+// split to finish combines them.  KS: the chunk key set length, as in step 1.
+template <int KS>
 __global__ __launch_bounds__(256) void k_decode_attend(DecodeArgs a) {
     __shared__ float s_q[kD];
     __shared__ float s_p[DC_SPLIT];
     __shared__ float s_red[4];
     __shared__ float s_acc[32][kD + 1];
-    __shared__ uint64_t s_sel[kMaxTopK];
-    __shared__ int s_blk[kMaxTopK];
+    __shared__ uint64_t s_sel[KS];
+    __shared__ int s_blk[KS];
     __shared__ int s_nused, s_last;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int row = blockIdx.x / a.nsplit, sp = blockIdx.x - row * a.nsplit;
@@ -255,14 +260,15 @@ __global__ __launch_bounds__(256) void k_decode_attend(DecodeArgs a) {
     const uint16_t* vbase = a.v + (int64_t)bg * a.t_max * kD;
     if (tid < kD) s_q[tid] = bf16_bits_to_f32(a.q[(int64_t)row * kD + tid]) * a.scale_log2;
     if (w == 0) {
-        const uint64_t* in = a.keys + (int64_t)row * a.nchunk * kMaxTopK;
-        const int ntot = a.nchunk * kMaxTopK;
+        const uint64_t* in = a.keys + (int64_t)row * a.nchunk * KS;
+        const int ntot = a.nchunk * KS;  // <= DC_MAXCH * KS
         int n;
         if (ntot <= 64) n = merge_chunk_sets<1>(in, ntot, a.top_k, s_sel);
         else if (ntot <= 128) n = merge_chunk_sets<2>(in, ntot, a.top_k, s_sel);
         else if (ntot <= 256) n = merge_chunk_sets<4>(in, ntot, a.top_k, s_sel);
         else if (ntot <= 512) n = merge_chunk_sets<8>(in, ntot, a.top_k, s_sel);
-        else n = merge_chunk_sets<16>(in, ntot, a.top_k, s_sel);
+        else if (KS <= kMaxTopK || ntot <= 1024) n = merge_chunk_sets<16>(in, ntot, a.top_k, s_sel);
+        else n = merge_chunk_sets<32>(in, ntot, a.top_k, s_sel);
         // ascending block ids: rank of each selected id among the n
         if (lane < n) {
             const int c = (int)key_block(s_sel[lane]);
@@ -387,6 +393,9 @@ struct DecodeLayout {
     int nchunk, nsplit;
 };
 
+// Chunk key set length for a selection of top_k blocks.
+static inline int decode_ks(int top_k) { return top_k <= kMaxTopK ? kMaxTopK : kMaxTopKWide; }
+
 static DecodeLayout decode_layout(const Geometry& g, int t_max) {
     DecodeLayout L{};
     // sized for the longest sequence the cache allows (T <= t_max)
@@ -397,7 +406,7 @@ static DecodeLayout decode_layout(const Geometry& g, int t_max) {
     L.nsplit = (g.top_k * g.bs + g.window + g.bs + DC_SPLIT - 1) / DC_SPLIT;
     const size_t rows = (size_t)g.B * g.Hq;
     size_t off = 0;
-    L.keys = off;     off += align_up(rows * L.nchunk * kMaxTopK * 8, 256);
+    L.keys = off;     off += align_up(rows * L.nchunk * decode_ks(g.top_k) * 8, 256);
     L.counters = off; off += align_up(rows * 4, 256);
     L.part = off;     off += align_up(rows * L.nsplit * (2 + kD) * 4, 256);
     L.total = off;
@@ -425,6 +434,17 @@ hipError_t static_scratch(void** ptr) {
     }
     *ptr = addr[dev];
     return hipSuccess;
+}
+
+template <int KS>
+static void launch_decode_steps(int kpl, dim3 rgrid, const DecodeArgs& a, hipStream_t s) {
+    switch (kpl) {
+        case 1: hipLaunchKernelGGL((k_decode_route<1, KS>), rgrid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_decode_route<2, KS>), rgrid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_decode_route<4, KS>), rgrid, dim3(256), 0, s, a); break;
+    }
+    hipLaunchKernelGGL(k_decode_attend<KS>, dim3((unsigned)(a.rows * a.nsplit)), dim3(256), 0, s,
+                       a);
 }
 
 hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const uint16_t* k,
@@ -462,12 +482,10 @@ hipError_t launch_decode(const Geometry& g, int t_max, const uint16_t* q, const 
     a.scale_log2 = g.scale * kLog2e;
     const int summ_wgs = g.N % g.bs == 0 ? g.B * g.Hkv : 0;
     const dim3 rgrid((unsigned)(a.rows * a.nchunk + summ_wgs));
-    switch (kpl) {
-        case 1: hipLaunchKernelGGL(k_decode_route<1>, rgrid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_decode_route<2>, rgrid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL(k_decode_route<4>, rgrid, dim3(256), 0, s, a); break;
-    }
-    hipLaunchKernelGGL(k_decode_attend, dim3((unsigned)(a.rows * a.nsplit)), dim3(256), 0, s, a);
+    if (decode_ks(g.top_k) == kMaxTopK)
+        launch_decode_steps<kMaxTopK>(kpl, rgrid, a, s);
+    else
+        launch_decode_steps<kMaxTopKWide>(kpl, rgrid, a, s);
     return hipGetLastError();
 }
 

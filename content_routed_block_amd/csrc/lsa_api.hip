@@ -35,7 +35,7 @@ lsa_status check_params(const lsa_params* p, Geometry* g) {
     if (p->head_dim != 64) return LSA_ERR_UNSUPPORTED;
     if (!pow2_block(p->block)) return LSA_ERR_UNSUPPORTED;
     if (!p->causal && p->block != 16) return LSA_ERR_UNSUPPORTED;
-    if (p->top_k > lsa::kMaxTopK) return LSA_ERR_UNSUPPORTED;
+    if (p->top_k > lsa::kMaxTopKWide) return LSA_ERR_UNSUPPORTED;
     if (p->beta != 0.f && (!p->causal || p->consensus)) return LSA_ERR_UNSUPPORTED;
     if (p->beam < 0) return LSA_ERR_SHAPE;
     if (p->chunk != 0 && (p->chunk < 64 || (p->chunk & (p->chunk - 1)))) return LSA_ERR_SHAPE;

@@ -15,7 +15,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 64;          // head dim supported by this build
-constexpr int kMaxTopK = 16;    // selection list length held in registers
+constexpr int kMaxTopK = 16;    // selection list length of the tuned kernels (top_k <= 16)
+constexpr int kMaxTopKWide = 32;  // the longest selection (top_k 17..32 take wider lists)
 constexpr int kTreeFanout = 16;  // key blocks per node of two-level routing
 constexpr int kTreeFanoutLog2 = 4;
 constexpr int kWave = 64;
@@ -75,7 +76,7 @@ __host__ __device__ __forceinline__ int eligible_blocks(int t, int bs, int windo
 
 // Which entries of one idx row are used: entry s counts when it is a
 // candidate (0 <= c < ncand) and larger than the previously used entry.
-// Returns a bit mask over the row's top_k (<= 16) slots.
+// Returns a bit mask over the row's top_k (<= 32) slots.
 __device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int ncand) {
     uint32_t mask = 0;
     int prev = -1;

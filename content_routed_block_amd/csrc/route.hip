@@ -186,12 +186,13 @@ __device__ __forceinline__ float kth_largest_top2_pair(float (&m1)[16], float (&
     return r;
 }
 
-// Bitonic merge of 16 64-bit keys into descending order.
-__device__ __forceinline__ void bitonic_merge_desc_u64(uint64_t (&v)[kMaxTopK]) {
+// Bitonic merge of KM (16 or 32) 64-bit keys into descending order.
+template <int KM>
+__device__ __forceinline__ void bitonic_merge_desc_u64(uint64_t (&v)[KM]) {
 #pragma unroll
-    for (int stride = kMaxTopK >> 1; stride > 0; stride >>= 1)
+    for (int stride = KM >> 1; stride > 0; stride >>= 1)
 #pragma unroll
-        for (int i = 0; i < kMaxTopK; ++i) {
+        for (int i = 0; i < KM; ++i) {
             const int j = i ^ stride;
             if (j > i) {
                 const uint64_t a = v[i], b = v[j];
@@ -202,9 +203,10 @@ __device__ __forceinline__ void bitonic_merge_desc_u64(uint64_t (&v)[kMaxTopK]) 
         }
 }
 
-__device__ __forceinline__ void insert_key(uint64_t (&L)[kMaxTopK], uint64_t x) {
+template <int KM>
+__device__ __forceinline__ void insert_key(uint64_t (&L)[KM], uint64_t x) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
+    for (int j = 0; j < KM; ++j) {
         const uint64_t a = L[j];
         const bool gt = x > a;
         L[j] = gt ? x : a;
@@ -214,16 +216,17 @@ __device__ __forceinline__ void insert_key(uint64_t (&L)[kMaxTopK], uint64_t x) 
 
 // Writes one idx row (row stride `stride`) from a key list sorted by rank
 // (m valid keys).
-__device__ __forceinline__ void write_selection(int32_t* out, const uint64_t (&L)[kMaxTopK],
+template <int KM>
+__device__ __forceinline__ void write_selection(int32_t* out, const uint64_t (&L)[KM],
                                                 int m, int top_k, int stride) {
-    uint32_t cs[kMaxTopK];
+    uint32_t cs[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) cs[j] = j < m ? key_block(L[j]) : 0xFFFFFFFFu;
-    bitonic_sort_asc_u32<kMaxTopK>(cs);
+    for (int j = 0; j < KM; ++j) cs[j] = j < m ? key_block(L[j]) : 0xFFFFFFFFu;
+    bitonic_sort_asc_u32<KM>(cs);
     if (((top_k | stride) & 3) == 0) {  // 16-byte stores (rows are 16-byte aligned)
         typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int j4 = 0; j4 < kMaxTopK / 4; ++j4) {
+        for (int j4 = 0; j4 < KM / 4; ++j4) {
             if (4 * j4 < top_k) {
                 i32x4 v;
 #pragma unroll
@@ -233,7 +236,7 @@ __device__ __forceinline__ void write_selection(int32_t* out, const uint64_t (&L
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j)
+        for (int j = 0; j < KM; ++j)
             if (j < top_k) out[j] = j < m ? (int32_t)cs[j] : -1;
     }
 }
@@ -358,10 +361,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // ------------------------------------------------------------ main kernel
 // Each wave is independent (its own 32 rows and survivor lists); the
 // workgroup only shares the staged candidate chunks.
-template <bool CAUSAL, bool QF32, bool EXACT, bool LEAN>
+// KM: the length of the exact pass's per-lane key lists.  kMaxTopK serves
+// top_k <= 16 (the exact pass then redoes the queued tiles only); with
+// kMaxTopKWide (top_k 17..32) the exact pass routes every tile itself.
+template <bool CAUSAL, bool QF32, bool EXACT, bool LEAN, int KM = kMaxTopK>
 __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(RouteArgs a) {
     static_assert(!(EXACT && LEAN), "the whole-tile exact pass scores b_c directly");
     static_assert(!(QF32 && LEAN), "fp32 queries take the full form");
+    static_assert(KM == kMaxTopK || EXACT, "wide selections are routed by the exact pass");
+    constexpr bool QUEUED = EXACT && KM == kMaxTopK;  // redoes the queued tiles only
     // candidate staging: pass 1 double-buffers the hi parts in s_stage[0..1];
     // pass 2 holds one chunk's hi part in s_stage[0] and lo part in
     // s_stage[1] (two barriers per chunk), which keeps the workgroup's LDS
@@ -382,7 +390,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     // L2 then holds that group's candidate blocks).  Tiles of a head run
     // heavy (late positions, most candidates) first.
     int item;
-    if constexpr (EXACT) {
+    if constexpr (QUEUED) {
         // the queued tiles, when more rows overflowed than the per-row pass takes
         if (__builtin_amdgcn_readfirstlane(*a.ovf_count) <= (uint32_t)FB_ROWS) return;
         if (blockIdx.x >= __builtin_amdgcn_readfirstlane(*a.tile_count)) return;
@@ -550,10 +558,10 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     // downward from slot RT_CAP-1; slots are clamped to the list, so an
     // overflowing list stays in bounds (the row is then redone exactly).
     const int qrow = 32 * w + l32;  // row within the workgroup
-    // whole-tile exact pass: each lane's 16 best selection keys, descending
-    uint64_t Lk[kMaxTopK];
+    // whole-tile exact pass: each lane's KM best selection keys, descending
+    uint64_t Lk[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) Lk[j] = 0;
+    for (int j = 0; j < KM; ++j) Lk[j] = 0;
     // list position kept as the byte offset of the score slot; the block
     // id of slot e sits at byte LIST_IDX + e/2
     constexpr int LIST_IDX = RT_CAP * RT_ROWS * 4;
@@ -627,7 +635,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
                     for (int r = 0; r < 16; ++r) {
                         const int c = cl0 + 8 * (r >> 2) + (r & 3);
                         const uint64_t key = sel_key(acc[r], (uint32_t)c);
-                        if (c < Erow && key > Lk[kMaxTopK - 1]) insert_key(Lk, key);
+                        if (c < Erow && key > Lk[KM - 1]) insert_key(Lk, key);
                     }
                 } else {
                     append_survivors(acc, cb, cl0);
@@ -679,10 +687,10 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     if constexpr (EXACT) {
         // the pair's lists hold disjoint candidates and merge in one
         // bitonic step
-        uint64_t Mx[kMaxTopK];
+        uint64_t Mx[KM];
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-            const uint64_t o = Lk[kMaxTopK - 1 - j];
+        for (int j = 0; j < KM; ++j) {
+            const uint64_t o = Lk[KM - 1 - j];
             const uint32_t olo = __shfl_xor((uint32_t)o, 32, kWave);
             const uint32_t ohi = __shfl_xor((uint32_t)(o >> 32), 32, kWave);
             const uint64_t other = ((uint64_t)ohi << 32) | olo;
@@ -692,7 +700,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         if (rq < P && half == 0) {
             int m = 0;
 #pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) m += (j < a.top_k && Mx[j] != 0ull) ? 1 : 0;
+            for (int j = 0; j < KM; ++j) m += (j < a.top_k && Mx[j] != 0ull) ? 1 : 0;
             write_selection(a.idx + out_row * a.idx_stride, Mx, m, a.top_k, a.idx_stride);
             if (a.idx_stride > a.top_k)
                 a.idx[out_row * a.idx_stride + a.top_k] =
@@ -954,8 +962,10 @@ __device__ __forceinline__ float pair_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int BS>
-__global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
+// KM: the per-lane list length (kMaxTopK; kMaxTopKWide for top_k 17..32,
+// at half the occupancy).
+template <int BS, int KM>
+__global__ __launch_bounds__(256, KM > kMaxTopK ? 2 : 4) void k_route_cumulant(CumArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_k[2][RT_CH * RT_PITCH];
     __shared__ float s_qs[CUM_Q][256];  // queued scores, slot-major
     __shared__ int s_qc[CUM_Q][256];    // queued block ids
@@ -994,10 +1004,10 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
         for (int ks = 0; ks < 4; ++ks) Bq[ks] = bf16x8{};
     }
 
-    float Ls[kMaxTopK];  // kept scores, descending
-    int Lc[kMaxTopK];    // their blocks
+    float Ls[KM];  // kept scores, descending
+    int Lc[KM];    // their blocks
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
+    for (int j = 0; j < KM; ++j) {
         Ls[j] = -INFINITY;
         Lc[j] = 0;
     }
@@ -1007,9 +1017,9 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
             if (i < nq) {
                 float x = s_qs[i][tid];
                 int xc = s_qc[i][tid];
-                if (x > Ls[kMaxTopK - 1]) {
+                if (x > Ls[KM - 1]) {
 #pragma unroll
-                    for (int j = 0; j < kMaxTopK; ++j) {
+                    for (int j = 0; j < KM; ++j) {
                         const bool gt = x > Ls[j];
                         const float ts = Ls[j];
                         const int tc = Lc[j];
@@ -1042,7 +1052,7 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
         const float m = pair_sum(sum) * inv_bs;
         const float var = pair_sum(sq) * inv_bs - m * m;
         const float score = fmaf(hb, var, m);
-        if ((c & 1) == half && c < Erow && score > Ls[kMaxTopK - 1]) {
+        if ((c & 1) == half && c < Erow && score > Ls[KM - 1]) {
             s_qs[nq][tid] = score;
             s_qc[nq][tid] = c;
             ++nq;
@@ -1108,10 +1118,10 @@ __global__ __launch_bounds__(256, 4) void k_route_cumulant(CumArgs a) {
 
     // the pair's lists hold disjoint candidates (even and odd blocks); as
     // 64-bit keys (score, then lower block) they merge in one bitonic step
-    uint64_t Mx[kMaxTopK];
+    uint64_t Mx[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        const int jj = kMaxTopK - 1 - j;
+    for (int j = 0; j < KM; ++j) {
+        const int jj = KM - 1 - j;
         const uint64_t o = Ls[jj] == -INFINITY ? 0ull : sel_key(Ls[jj], (uint32_t)Lc[jj]);
         const uint64_t mine = Ls[j] == -INFINITY ? 0ull : sel_key(Ls[j], (uint32_t)Lc[j]);
         const uint32_t olo = __shfl_xor((uint32_t)o, 32, kWave);
@@ -1299,6 +1309,14 @@ static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
     // (group sums, pooled blocks) always take the full form: their delta
     // carries the q_lo term too, and the lean form's 2 * delta band
     // overflows the survivor lists
+    if (a.top_k > kMaxTopK) {
+        // wide selections (top_k 17..32): the exact pass routes every tile,
+        // each lane keeping its 32 best keys; nothing can overflow
+        hipLaunchKernelGGL((k_route<CAUSAL, QF32, true, false, kMaxTopKWide>), grid, dim3(256), 0,
+                           s, a);
+        mark(ev, 2, s);
+        return;
+    }
     const int cmax = CAUSAL ? (eligible_blocks(a.P - 1, a.bs, a.window) >> a.cshift) : a.nb;
     bool lean = false;
     if constexpr (!QF32) lean = cmax >= kRouteLeanMinCand;
@@ -1473,6 +1491,16 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
     return e;
 }
 
+template <int KM>
+static void launch_cumulant(int bs, dim3 grid, const CumArgs& a, hipStream_t s) {
+    switch (bs) {
+        case 16: hipLaunchKernelGGL((k_route_cumulant<16, KM>), grid, dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((k_route_cumulant<32, KM>), grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((k_route_cumulant<64, KM>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_route_cumulant<128, KM>), grid, dim3(256), 0, s, a); break;
+    }
+}
+
 hipError_t launch_route_cumulant(const Geometry& g, const uint16_t* q, const uint16_t* k,
                                  int32_t* idx, hipStream_t s) {
     CumArgs a;
@@ -1488,12 +1516,10 @@ hipError_t launch_route_cumulant(const Geometry& g, const uint16_t* q, const uin
     a.items = g.B * g.Hq * a.tiles;
     a.half_beta = 0.5f * g.beta;
     const dim3 grid((unsigned)(((int64_t)a.items + 7) / 8 * 8));  // a multiple of the XCD count
-    switch (g.bs) {
-        case 16: hipLaunchKernelGGL(k_route_cumulant<16>, grid, dim3(256), 0, s, a); break;
-        case 32: hipLaunchKernelGGL(k_route_cumulant<32>, grid, dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL(k_route_cumulant<64>, grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL(k_route_cumulant<128>, grid, dim3(256), 0, s, a); break;
-    }
+    if (g.top_k <= kMaxTopK)
+        launch_cumulant<kMaxTopK>(g.bs, grid, a, s);
+    else
+        launch_cumulant<kMaxTopKWide>(g.bs, grid, a, s);
     return hipGetLastError();
 }
 

@@ -11,8 +11,8 @@
 //      per pair (fp32 accuracy), written by pair position (contiguous);
 //   3. k_tree_select: one lane per row merges each used slot's 16 scores,
 //      as sorted 64-bit keys (score, then lower block), into the row's
-//      running top-16 with a bitonic merge.  Blocks of the tail node past
-//      the row's candidates are left out.
+//      running top-16 (top-32 when top_k exceeds 16) with a bitonic merge.
+//      Blocks of the tail node past the row's candidates are left out.
 // The node-major scoring gathers one 128-byte query row per pair instead of
 // a node's 4 KB of block means per pair.
 #include <math.h>
@@ -153,19 +153,20 @@ __device__ __forceinline__ void sort16_desc(uint64_t (&v)[kTreeFanout]) {
 
 // One lane per row.  Per used slot the 16 block scores become 64-bit keys
 // (score, then lower block; 0 for blocks past the row's candidates), are
-// sorted, and merged into the row's running top-16 by one bitonic merge:
-// branch-free, so the lanes of a wave never wait on each other's
-// insertions.  The next slot's scores are loaded while the current one is
-// merged.
+// sorted, and merged into the row's running top-KM (KM = 16, or 32 for
+// top_k above 16) by one bitonic merge: branch-free, so the lanes of a wave
+// never wait on each other's insertions.  The next slot's scores are loaded
+// while the current one is merged.
+template <int KM>
 __global__ __launch_bounds__(256) void k_tree_select(TreeSelectArgs a) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (row >= a.rows) return;
     const int t = (int)(row % a.N);
     const int E = a.causal ? eligible_blocks(t, a.bs, a.window) : a.nb;
     const int stride = a.beam + 1;
-    uint64_t L[kTreeFanout];
+    uint64_t L[KM];
 #pragma unroll
-    for (int j = 0; j < kTreeFanout; ++j) L[j] = 0;
+    for (int j = 0; j < KM; ++j) L[j] = 0;
     int ncand = 0;
     auto fetch = [&](int j, f32x4 (&sc)[4], int& c0) {
         const uint32_t pos = j < stride ? a.rev[(int64_t)j * a.rows + row] : 0xFFFFFFFFu;
@@ -190,15 +191,17 @@ __global__ __launch_bounds__(256) void k_tree_select(TreeSelectArgs a) {
             for (int i = 0; i < kTreeFanout; ++i)
                 Nk[i] = i < nvalid ? sel_key(cur[i >> 2][i & 3], (uint32_t)(c_cur + i)) : 0ull;
             sort16_desc(Nk);
+            // the new keys, zero-padded to KM, reversed against L: the
+            // pairwise maxima are the top KM of the union, in bitonic order
 #pragma unroll
-            for (int i = 0; i < kTreeFanout; ++i) {
-                const uint64_t o = Nk[kTreeFanout - 1 - i];
-                L[i] = L[i] > o ? L[i] : o;  // top 16 of the union, bitonic
+            for (int i = 0; i < KM; ++i) {
+                const int jn = KM - 1 - i;
+                if (jn < kTreeFanout) L[i] = L[i] > Nk[jn] ? L[i] : Nk[jn];
             }
 #pragma unroll
-            for (int stride2 = kTreeFanout >> 1; stride2 > 0; stride2 >>= 1)
+            for (int stride2 = KM >> 1; stride2 > 0; stride2 >>= 1)
 #pragma unroll
-                for (int i = 0; i < kTreeFanout; ++i) {
+                for (int i = 0; i < KM; ++i) {
                     const int jx = i ^ stride2;
                     if (jx > i) cx_desc(L[i], L[jx]);
                 }
@@ -209,15 +212,15 @@ __global__ __launch_bounds__(256) void k_tree_select(TreeSelectArgs a) {
     }
     // the chosen blocks in ascending order, -1 padded
     const int m = ncand < a.top_k ? ncand : a.top_k;
-    uint32_t cs[kMaxTopK];
+    uint32_t cs[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) cs[j] = j < m ? key_block(L[j]) : 0xFFFFFFFFu;
+    for (int j = 0; j < KM; ++j) cs[j] = j < m ? key_block(L[j]) : 0xFFFFFFFFu;
 #pragma unroll
-    for (int size = 2; size <= kMaxTopK; size <<= 1)
+    for (int size = 2; size <= KM; size <<= 1)
 #pragma unroll
         for (int stride2 = size >> 1; stride2 > 0; stride2 >>= 1)
 #pragma unroll
-            for (int i = 0; i < kMaxTopK; ++i) {
+            for (int i = 0; i < KM; ++i) {
                 const int jx = i ^ stride2;
                 if (jx > i) {
                     const uint32_t x = cs[i], y = cs[jx];
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256) void k_tree_select(TreeSelectArgs a) {
             }
     int32_t* out = a.idx + row * a.top_k;
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
+    for (int j = 0; j < KM; ++j)
         if (j < a.top_k) out[j] = j < m ? (int32_t)cs[j] : -1;
 }
 
@@ -308,7 +311,11 @@ hipError_t launch_tree_level2(const Geometry& g, const uint16_t* q, const float*
 
     TreeSelectArgs ta{slots, rev, scores, idx, rows, P, g.bs, g.window, g.top_k, g.beam,
                       g.causal, g.nb};
-    hipLaunchKernelGGL(k_tree_select, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, ta);
+    const dim3 sgrid((unsigned)((rows + 255) / 256));
+    if (g.top_k <= kMaxTopK)
+        hipLaunchKernelGGL(k_tree_select<kMaxTopK>, sgrid, dim3(256), 0, s, ta);
+    else
+        hipLaunchKernelGGL(k_tree_select<kMaxTopKWide>, sgrid, dim3(256), 0, s, ta);
     return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ def good(lsa, **kw):
     (dict(beam=4, consensus=1), 3), (dict(beam=4, beta=0.5), 3),
     (dict(beam=4, causal=0, window=0, block=16, consensus=1), 3),
     (dict(chunk=-64), 2), (dict(chunk=32), 2), (dict(chunk=96), 2),
-    (dict(head_dim=128), 3), (dict(top_k=17), 3), (dict(block=48, window=96, seq_len=960), 3),
+    (dict(head_dim=128), 3), (dict(top_k=33), 3), (dict(block=48, window=96, seq_len=960), 3),
     (dict(causal=0, window=0, block=64), 3), (dict(seq_len=1 << 24, block=16, window=512), 3),
 ])
 def test_invalid_parameters(lsa, kw, code):
@@ -113,6 +113,29 @@ def test_workspace_sizes_are_plausible(lsa):
     img = lsa.params(4, 16, 16, 16384, 64, 16, 8, 0, 0)
     assert lsa.workspace_bytes(img, lsa.OP_ATTEND) == 4 * 16 * 16384 * 64 * 2
     assert lsa.workspace_bytes(img, lsa.OP_ROUTE) >= 4 * 16 * 1024 * 64 * 4
+
+
+def test_wide_top_k_is_accepted(lsa):
+    """top_k 17..32 is part of the boundary: its pair ids take a stride of 32
+    slots (so the attention workspace holds 32 partial rows per query row and
+    the 32-bit pair-id limit binds at half the rows), and decode keeps 32-key
+    chunk sets."""
+    pairs = 14 * 131072
+    vt = 2 * 131072 * 64 * 2
+    for k in (17, 24, 32):
+        p = good(lsa, top_k=k)
+        att = lsa.workspace_bytes(p, lsa.OP_ATTEND)
+        want = pairs * k * 8 + pairs * 32 * 64 * 2 + pairs * k * 4 + vt
+        assert want <= att < want + (1 << 20)
+        assert lsa.idx_shape(p) == (1, 14, 131072, k)
+        assert lsa.workspace_bytes(p, lsa.OP_FORWARD) < lsa.SIZE_MAX
+        d16 = lsa.workspace_bytes(good(lsa), lsa.OP_DECODE)
+        assert lsa.workspace_bytes(p, lsa.OP_DECODE) > d16
+    # B*Hq*N*2^ceil(log2 top_k) + 64 < 2^32: 128 x 14 x 131072 rows fit 16
+    # slots each but not 32
+    assert lsa.workspace_bytes(good(lsa, batch=128), lsa.OP_FORWARD) < lsa.SIZE_MAX
+    big = good(lsa, batch=128, top_k=17)
+    assert lsa.library().lsa_workspace_bytes(ctypes.byref(big), lsa.OP_FORWARD) == lsa.SIZE_MAX
 
 
 def test_consensus_workspace_and_decode(lsa):

@@ -46,6 +46,9 @@ CASES = [
     custom(2, 6, 2, 1024, 16, 8, 0, causal=0, seed=6),
     custom(1, 4, 2, 16 * 65, 16, 4, 32, seed=14),   # N not a multiple of 64
     custom(1, 4, 2, 2048, 16, 6, 48, seed=19),      # odd W / bs
+    custom(2, 4, 2, 2048 + 3 * 64, 64, 32, 128, dist="topics", seed=42),  # top_k 17..32
+    custom(1, 6, 2, 16 * 130, 16, 22, 32, seed=43),
+    custom(1, 4, 2, 2048, 16, 28, 0, causal=0, seed=44),
 ]
 
 

@@ -45,6 +45,8 @@ CASES = [
     (custom(1, 7, 1, 3072, 64, 16, 512, dist="topics", seed=5), 0.5),
     (custom(1, 2, 1, 16 * 65, 16, 4, 32, seed=15), BETA),   # N not a multiple of 64
     (custom(1, 2, 1, 2048, 16, 6, 48, seed=16), BETA),      # odd W / bs: odd block counts
+    (custom(2, 4, 2, 2048 + 3 * 64, 64, 32, 128, dist="topics", seed=53), BETA),  # top_k 17..32
+    (custom(1, 3, 1, 16 * 130, 16, 23, 32, seed=54), -0.5),
 ]
 
 

@@ -44,6 +44,9 @@ CASES = [
     (custom(1, 2, 1, 2048, 128, 3, 256), [300, 1280, 2048]),
     (custom(1, 4, 2, 40960, 16, 16, 128, dist="topics"), [16384, 40000, 40960]),
     (custom(1, 2, 1, 16 * 130, 16, 6, 48, seed=22), [1, 47, 49, 1000, 2080]),  # odd W / bs
+    # top_k 17..32: 32-key chunk sets, one to four chunks per row
+    (custom(2, 4, 2, 2048, 64, 32, 128, dist="topics", seed=24), [1, 700, 2047, 2048]),
+    (custom(1, 2, 1, 40960, 16, 25, 128, seed=25), [5000, 40960]),
 ]
 
 

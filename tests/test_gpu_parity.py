@@ -51,11 +51,19 @@ CAUSAL_CASES = [
     # an odd number of window blocks (W / bs = 3): odd eligible-block counts
     custom(1, 2, 1, 2048, 16, 6, 48, seed=17),
     custom(1, 2, 2, 32 * 40, 32, 3, 96, seed=18),
+    # top_k 17..32 (every routing tile takes the exact pass; 32-entry lists
+    # in the bucketing and the merge): a multiple of 4 and not, E(t) < k on
+    # the first rows, GQA, B = 2, ragged N
+    custom(2, 4, 2, 2048 + 3 * 64, 64, 24, 128, dist="topics", seed=31),
+    custom(1, 3, 1, 16 * 130, 16, 32, 32, seed=32),
+    custom(1, 2, 2, 32 * 70, 32, 19, 96, seed=33),
 ]
 IMAGE_CASES = [
     custom(2, 4, 4, 1024, 16, 8, 0, causal=0),
     custom(1, 4, 2, 4096, 16, 16, 0, causal=0, seed=3),
     custom(1, 2, 2, 272, 16, 3, 0, causal=0, seed=4),
+    custom(1, 2, 1, 1024, 16, 32, 0, causal=0, seed=34),
+    custom(1, 4, 2, 4096, 16, 21, 0, causal=0, seed=35),
 ]
 
 

@@ -25,7 +25,7 @@ lsa = P.lsa  # the module fixture: skips without a GPU
 MAX_ROWS = 120_000  # B * Hq * N per case, so the oracle finishes in about a second
 
 
-def draw(n, seed, causal=True, tag="sw"):
+def draw(n, seed, causal=True, tag="sw", kmin=1, kmax=16):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
@@ -33,7 +33,7 @@ def draw(n, seed, causal=True, tag="sw"):
         m = int(rng.integers(1, 4096 // bs + 1))            # blocks in the sequence
         N = bs * m
         W = bs * int(rng.integers(1, 9)) if causal else 0   # 1 to 8 window blocks
-        k = int(rng.integers(1, 17))
+        k = int(rng.integers(kmin, kmax + 1))
         Hkv = int(rng.integers(1, 4))
         rep = int(rng.choice([1, 2, 3, 7]))
         B = int(rng.integers(1, 3))
@@ -76,6 +76,18 @@ TREE = [(w, int(b)) for w, b in zip(draw(20, 36, tag="tree"),
 DECODE = [(w, sorted({1, w.seq_len, *np.random.default_rng(39 + i).integers(1, w.seq_len + 1, 3)
                       .tolist()}))
           for i, w in enumerate(draw(16, 38, tag="dec"))]
+# top_k 17..32 through every variant
+WIDE = draw(24, 42, tag="wide", kmin=17, kmax=32) + draw(8, 43, causal=False, tag="wideimg",
+                                                         kmin=17, kmax=32)
+WIDE_CONSENSUS = draw(6, 44, tag="widecons", kmin=17, kmax=32) + draw(
+    2, 45, causal=False, tag="wideconsimg", kmin=17, kmax=32)
+WIDE_CUMULANT = [(w, float(b)) for w, b in zip(draw(6, 46, tag="widecum", kmin=17, kmax=32),
+                                               np.random.default_rng(47).choice([0.125, -0.5, 2.0], 6))]
+WIDE_TREE = [(w, int(b)) for w, b in zip(draw(6, 48, tag="widetree", kmin=17, kmax=32),
+                                         np.random.default_rng(49).integers(1, 16, 6))]
+WIDE_DECODE = [(w, sorted({1, w.seq_len, *np.random.default_rng(50 + i).integers(1, w.seq_len + 1, 3)
+                           .tolist()}))
+               for i, w in enumerate(draw(6, 51, tag="widedec", kmin=17, kmax=32))]
 
 
 def name(x):
@@ -114,4 +126,29 @@ def test_sweep_tree_forward(lsa, w, beam):
 
 @pytest.mark.parametrize("w,steps", DECODE, ids=name)
 def test_sweep_decode(lsa, w, steps):
+    D.test_decode_matches_oracle(lsa, w, steps)
+
+
+@pytest.mark.parametrize("w", WIDE, ids=name)
+def test_sweep_wide_forward(lsa, w):
+    P.test_forward_matches_oracle(lsa, w)
+
+
+@pytest.mark.parametrize("w", WIDE_CONSENSUS, ids=name)
+def test_sweep_wide_consensus_forward(lsa, w):
+    C.test_consensus_forward_matches_oracle(lsa, w)
+
+
+@pytest.mark.parametrize("w,beta", WIDE_CUMULANT, ids=name)
+def test_sweep_wide_cumulant_forward(lsa, w, beta):
+    U.test_cumulant_forward_matches_oracle(lsa, w, beta)
+
+
+@pytest.mark.parametrize("w,beam", WIDE_TREE, ids=name)
+def test_sweep_wide_tree_forward(lsa, w, beam):
+    T.test_tree_forward_matches_oracle(lsa, w, beam)
+
+
+@pytest.mark.parametrize("w,steps", WIDE_DECODE, ids=name)
+def test_sweep_wide_decode(lsa, w, steps):
     D.test_decode_matches_oracle(lsa, w, steps)

@@ -42,6 +42,8 @@ CASES = [
     (custom(1, 2, 2, 32768, 128, 3, 256), 2),
     (custom(1, 3, 1, 8192, 16, 5, 32), 1),
     (custom(1, 2, 1, 16 * 1001, 16, 6, 48, seed=73), 3),   # odd W / bs, N not a multiple of 64
+    (custom(1, 4, 2, 16384, 16, 32, 64, dist="topics", seed=74), 4),   # top_k 17..32
+    (custom(1, 2, 1, 8192, 32, 20, 64, seed=75), 1),   # fewer candidates than top_k in a row
 ]
 
 
@@ -173,6 +175,7 @@ IMAGE_CASES = [
     (image(1, 2, 1, 16 * 12, 4), 3),                # no complete node: the tail only
     (image(1, 2, 2, 16 * 16 * 9, 16, seed=92), 15),  # beam covers every node
     (image(1, 4, 4, 16384, 8, "grf", seed=93, side=128), 8),  # one 128 x 128 image (Z-order)
+    (image(1, 2, 1, 4096, 32, seed=95), 3),                    # top_k 17..32
 ]
 
 

@@ -128,7 +128,8 @@ def test_route_monotone_scores(orc, sign):
         assert list(idx[0, 0, t]) == want + [-1] * (k - n), t
 
 
-@pytest.mark.parametrize("bs,W,k,Hq,Hkv", [(16, 32, 3, 4, 2), (8, 8, 2, 2, 1), (32, 96, 1, 3, 3)])
+@pytest.mark.parametrize("bs,W,k,Hq,Hkv", [(16, 32, 3, 4, 2), (8, 8, 2, 2, 1), (32, 96, 1, 3, 3),
+                                            (4, 8, 24, 2, 1)])
 def test_route_matches_rank_brute_force(orc, bs, W, k, Hq, Hkv):
     rng = np.random.default_rng(bs * 100 + k)
     N, D = 256, 16
@@ -328,7 +329,8 @@ def test_sampled_rows_match_full_run(orc):
 # routing scores (SSA page, "Complete 10M transformer result": a cross-head
 # consensus route).
 
-@pytest.mark.parametrize("bs,W,k,Hq,Hkv", [(16, 32, 3, 4, 2), (8, 16, 2, 3, 1), (32, 64, 1, 4, 1)])
+@pytest.mark.parametrize("bs,W,k,Hq,Hkv", [(16, 32, 3, 4, 2), (8, 16, 2, 3, 1), (32, 64, 1, 4, 1),
+                                            (4, 8, 32, 3, 1)])
 def test_consensus_matches_rank_brute_force(orc, bs, W, k, Hq, Hkv):
     rng = np.random.default_rng(bs * 10 + Hq)
     N, D = 256, 16
@@ -438,7 +440,8 @@ def test_cumulant_with_beta_zero_is_the_mean_score(orc):
     np.testing.assert_array_equal(ga, gb)
 
 
-@pytest.mark.parametrize("bs,W,k,beta", [(16, 32, 3, 0.125), (8, 16, 2, 1.0), (32, 64, 4, -0.5)])
+@pytest.mark.parametrize("bs,W,k,beta", [(16, 32, 3, 0.125), (8, 16, 2, 1.0), (32, 64, 4, -0.5),
+                                         (8, 16, 20, 0.5)])
 def test_cumulant_matches_score_variance_brute_force(orc, bs, W, k, beta):
     rng = np.random.default_rng(bs + k)
     N, D, Hq, Hkv = 256, 16, 4, 2
@@ -516,7 +519,8 @@ def test_tree_with_wide_beam_is_flat_routing(orc):
                                   orc.route_image(qbar, kbar, k))
 
 
-@pytest.mark.parametrize("bs,W,k,beam,F", [(8, 16, 4, 2, 16), (4, 8, 3, 1, 4), (8, 32, 6, 3, 8)])
+@pytest.mark.parametrize("bs,W,k,beam,F", [(8, 16, 4, 2, 16), (4, 8, 3, 1, 4), (8, 32, 6, 3, 8),
+                                           (4, 8, 24, 2, 16)])
 def test_tree_matches_rank_brute_force(orc, bs, W, k, beam, F):
     rng = np.random.default_rng(bs * 7 + beam)
     N, D, Hq, Hkv = 1024, 8, 2, 1
