@@ -16,14 +16,16 @@
 // candidates whose indices fall in one residue class mod 32 per register;
 // lanes l and l^32 hold the two halves of the same query's chunk.
 //   pass 1  hi-only scores a_c; every lane keeps the two largest values of
-//           each of its residue classes.  Their k-th largest over the lane
-//           pair, th, is reached by at least k candidates' a_c; delta
-//           bounds |a_c - b_c| against the fp32-accurate score b_c, so at
-//           least k candidates have b_c >= th - delta.
+//           each of its residue classes (three for top_k above 16).  Their
+//           k-th largest over the lane pair, th, is reached by at least k
+//           candidates' a_c; delta bounds |a_c - b_c| against the
+//           fp32-accurate score b_c, so at least k candidates have
+//           b_c >= th - delta.
 //   pass 2  one of two forms, chosen per launch by the row length:
 //           full  hi+lo scores b_c (three MFMA products with fp32 queries,
 //                 two otherwise); candidates with b_c >= th - delta join
-//                 the query's survivor list in LDS (capacity RT_CAP = 29);
+//                 the query's survivor list in LDS (capacity RT_CAP = 29,
+//                 RT_CAP_WIDE = 56 for top_k above 16);
 //           lean  the hi-only a_c again (one product, half the staging and
 //                 one barrier per chunk); candidates with a_c >= th - 2
 //                 delta join the list, and each survivor's b_c = a_c +
@@ -35,16 +37,16 @@
 //           fixed, latency-bound rescoring per row, so it pays off only for
 //           long rows (kRouteLeanMinCand candidates and more) of bf16
 //           queries.
-//   select  each lane of the pair inserts the survivors it found into a
-//           16-entry sorted list of 64-bit keys (score b_c, then lower
-//           index); the two lists are merged and the chosen block ids
-//           written in ascending order.
+//   select  each lane of the pair ranks the survivors it found in a
+//           16-entry (top_k above 16: 32-entry) sorted list of 64-bit keys
+//           (score b_c, then lower index); the two lists are merged and the
+//           chosen block ids written in ascending order.
 // Queries whose survivor list overflows (ties on many blocks, adversarial
 // inputs) are queued, and so is each workgroup holding one.  Up to FB_ROWS
 // such rows are redone one by one by k_route_fallback.  With more, the
 // queued workgroups rerun as k_route<.., EXACT = true>: the same scores,
-// no threshold pass, and each lane keeps its 16 best 64-bit keys, with no
-// capacity to overflow.
+// no threshold pass, and each lane keeps its 16 (32) best 64-bit keys, with
+// no capacity to overflow.
 //
 // Consensus routing (one route per KV group, scored by the sum of the
 // group's query heads' scores; SSA page, "Complete 10M transformer result")
@@ -61,6 +63,7 @@ namespace lsa {
 constexpr int RT_ROWS = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int RT_CH = 32;      // candidates per step
 constexpr int RT_CAP = 29;     // survivor slots per query (five workgroups still fit a CU)
+constexpr int RT_CAP_WIDE = 56;  // the same for top_k 17..32 (three workgroups per CU)
 constexpr int RT_PITCH = 72;   // LDS row pitch of staged candidates (bf16), conflict-free
 constexpr int FB_GRID = 1024;   // workgroups of the per-row exact pass (one row at a time)
 constexpr int FB_ROWS = 16384;  // rows it takes; above this the queued tiles are redone whole
@@ -143,14 +146,15 @@ __device__ __forceinline__ void bitonic_sort_asc_u32(uint32_t* v) {
             }
 }
 
-// Sorts 16 64-bit keys into descending order.
-__device__ __forceinline__ void bitonic_sort_desc_u64(uint64_t (&v)[kMaxTopK]) {
+// Sorts KM (16 or 32) 64-bit keys into descending order.
+template <int KM>
+__device__ __forceinline__ void bitonic_sort_desc_u64(uint64_t (&v)[KM]) {
 #pragma unroll
-    for (int size = 2; size <= kMaxTopK; size <<= 1)
+    for (int size = 2; size <= KM; size <<= 1)
 #pragma unroll
         for (int stride = size >> 1; stride > 0; stride >>= 1)
 #pragma unroll
-            for (int i = 0; i < kMaxTopK; ++i) {
+            for (int i = 0; i < KM; ++i) {
                 const int j = i ^ stride;
                 if (j > i) {
                     const uint64_t a = v[i], b = v[j];
@@ -182,6 +186,38 @@ __device__ __forceinline__ float kth_largest_top2_pair(float (&m1)[16], float (&
     float r = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
+        if (i == k - 1) r = w[i];
+    return r;
+}
+
+// k-th largest (1 <= k <= 32) of the 96 values held as the three largest
+// values (m1 >= m2 >= m3) of 16 classes in this lane and 16 more classes in
+// lane ^ 32.  Both lanes of the pair return the same value.
+__device__ __forceinline__ float kth_largest_top3_pair(float (&m1)[16], float (&m2)[16],
+                                                       float (&m3)[16], int k) {
+    bitonic_sort_desc<16>(m1);
+    bitonic_sort_desc<16>(m2);
+    bitonic_sort_desc<16>(m3);
+    // top 32 of m1 and m2: m1 descending then m2 ascending is bitonic
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        v[i] = m1[i];
+        v[16 + i] = m2[15 - i];
+    }
+    bitonic_merge_desc<32>(v);
+    // top 32 of those and m3 (padded with -inf), bitonic, then sorted
+#pragma unroll
+    for (int i = 16; i < 32; ++i) v[i] = fmaxf(v[i], m3[31 - i]);
+    bitonic_merge_desc<32>(v);
+    // top 32 of the pair's two lists
+    float w[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = fmaxf(v[i], __shfl_xor(v[31 - i], 32, kWave));
+    bitonic_merge_desc<32>(w);
+    float r = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
         if (i == k - 1) r = w[i];
     return r;
 }
@@ -361,15 +397,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // ------------------------------------------------------------ main kernel
 // Each wave is independent (its own 32 rows and survivor lists); the
 // workgroup only shares the staged candidate chunks.
-// KM: the length of the exact pass's per-lane key lists.  kMaxTopK serves
-// top_k <= 16 (the exact pass then redoes the queued tiles only); with
-// kMaxTopKWide (top_k 17..32) the exact pass routes every tile itself.
+// KM: the selection list length, kMaxTopK for top_k <= 16 or kMaxTopKWide
+// for top_k 17..32.  The wide form keeps the three largest values per class
+// in pass 1 (so that its threshold stays close to the k-th score) and
+// RT_CAP_WIDE survivor slots per query, at three workgroups per CU.
 template <bool CAUSAL, bool QF32, bool EXACT, bool LEAN, int KM = kMaxTopK>
-__global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(RouteArgs a) {
+__global__ __launch_bounds__(256, EXACT ? 2 : (KM > kMaxTopK ? 3 : (QF32 ? 4 : 5)))
+void k_route(RouteArgs a) {
     static_assert(!(EXACT && LEAN), "the whole-tile exact pass scores b_c directly");
     static_assert(!(QF32 && LEAN), "fp32 queries take the full form");
-    static_assert(KM == kMaxTopK || EXACT, "wide selections are routed by the exact pass");
-    constexpr bool QUEUED = EXACT && KM == kMaxTopK;  // redoes the queued tiles only
+    constexpr bool WIDE = KM > kMaxTopK;
+    constexpr int CAP = WIDE ? RT_CAP_WIDE : RT_CAP;
     // candidate staging: pass 1 double-buffers the hi parts in s_stage[0..1];
     // pass 2 holds one chunk's hi part in s_stage[0] and lo part in
     // s_stage[1] (two barriers per chunk), which keeps the workgroup's LDS
@@ -378,8 +416,8 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     __shared__ __attribute__((aligned(16))) __bf16 s_stage[2][RT_CH * RT_PITCH];
     // survivor lists, slot-major ([slot][row]) so that the lanes of a wave
     // touch consecutive words
-    // (scores: RT_CAP*RT_ROWS floats, then the block ids as uint16)
-    __shared__ __attribute__((aligned(16))) char s_list[RT_CAP * RT_ROWS * 6];
+    // (scores: CAP*RT_ROWS floats, then the block ids as uint16)
+    __shared__ __attribute__((aligned(16))) char s_list[CAP * RT_ROWS * 6];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
@@ -390,7 +428,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     // L2 then holds that group's candidate blocks).  Tiles of a head run
     // heavy (late positions, most candidates) first.
     int item;
-    if constexpr (QUEUED) {
+    if constexpr (EXACT) {
         // the queued tiles, when more rows overflowed than the per-row pass takes
         if (__builtin_amdgcn_readfirstlane(*a.ovf_count) <= (uint32_t)FB_ROWS) return;
         if (blockIdx.x >= __builtin_amdgcn_readfirstlane(*a.tile_count)) return;
@@ -486,14 +524,16 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         qln = sqrtf(l2);
     }
 
-    // ---- pass 1: hi-only scores, two largest per residue class.
-    // Chunks below Efull are candidates of every row of the wave (no mask).
+    // ---- pass 1: hi-only scores, two (wide form: three) largest per
+    // residue class.  Chunks below Efull are candidates of every row of the
+    // wave (no mask).
     const int Efull = (Emin / RT_CH) * RT_CH;
-    float m1[16], m2[16];
+    float m1[16], m2[16], m3[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         m1[r] = -INFINITY;
         m2[r] = -INFINITY;
+        m3[r] = -INFINITY;
     }
     const int nch = (Ewg + RT_CH - 1) / RT_CH;  // chunks of the workgroup
     if constexpr (!EXACT) {  // the whole-tile exact pass keeps every candidate it needs
@@ -525,7 +565,8 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    // m1 >= m2, so the new second largest is the median
+                    // m1 >= m2 >= m3, so each new lower rank is a median
+                    if constexpr (WIDE) m3[r] = __builtin_amdgcn_fmed3f(m2[r], m3[r], acc[r]);
                     m2[r] = __builtin_amdgcn_fmed3f(m1[r], m2[r], acc[r]);
                     m1[r] = fmaxf(m1[r], acc[r]);
                 }
@@ -548,14 +589,16 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     if constexpr (!EXACT) {
         const float kn_max = __uint_as_float(wave_max_u32(kn_bits));
         const float lo_max = __uint_as_float(wave_max_u32(lo_bits));
-        const float th = kth_largest_top2_pair(m1, m2, a.top_k);
+        float th;
+        if constexpr (WIDE) th = kth_largest_top3_pair(m1, m2, m3, a.top_k);
+        else th = kth_largest_top2_pair(m1, m2, a.top_k);
         const float delta = 1.0625f * (qn * lo_max + qln * kn_max) + 6.2e-5f * (qn + qln) * kn_max;
         theta = th - (LEAN ? 2.f : 1.f) * delta;  // -inf stays -inf
     }
 
     // ---- pass 2: survivors to the row's LDS list.  The lane pair (l, l^32)
     // shares a row's list: half 0 fills it upward from slot 0, half 1
-    // downward from slot RT_CAP-1; slots are clamped to the list, so an
+    // downward from slot CAP-1; slots are clamped to the list, so an
     // overflowing list stays in bounds (the row is then redone exactly).
     const int qrow = 32 * w + l32;  // row within the workgroup
     // whole-tile exact pass: each lane's KM best selection keys, descending
@@ -564,9 +607,9 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     for (int j = 0; j < KM; ++j) Lk[j] = 0;
     // list position kept as the byte offset of the score slot; the block
     // id of slot e sits at byte LIST_IDX + e/2
-    constexpr int LIST_IDX = RT_CAP * RT_ROWS * 4;
+    constexpr int LIST_IDX = CAP * RT_ROWS * 4;
     const int step = half ? -RT_ROWS * 4 : RT_ROWS * 4;
-    const int at_lo = qrow * 4, at_hi = ((RT_CAP - 1) * RT_ROWS + qrow) * 4;
+    const int at_lo = qrow * 4, at_hi = ((CAP - 1) * RT_ROWS + qrow) * 4;
     int at = half ? at_hi : at_lo;
     // appends the chunk's scores at or above theta (masked to the row's
     // candidates in chunks past Efull); cl0 = first candidate of this lane
@@ -712,11 +755,11 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
     const int n_pair = n_mine + __shfl_xor(n_mine, 32, kWave);
     // a workgroup with an overflowing row queues its tile once, for the
     // whole-tile exact pass that runs when many rows overflow
-    if (rq < P && n_pair > RT_CAP && half == 0) s_ovf = 1u;
+    if (rq < P && n_pair > CAP && half == 0) s_ovf = 1u;
     __syncthreads();
     if (tid == 0 && s_ovf != 0u) a.tile_queue[atomicAdd(a.tile_count, 1u)] = (uint32_t)item;
     if (rq >= P) return;
-    if (n_pair > RT_CAP) {
+    if (n_pair > CAP) {
         if (half == 0) {
             const uint32_t slot = atomicAdd(a.ovf_count, 1u);
             a.ovf_rows[slot] = (uint32_t)out_row;
@@ -739,7 +782,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         // an empty entry reads block 0 (a valid row) and is discarded
         auto fetch = [&](int i, bf16x8 (&vA)[4], bf16x8 (&vB)[4]) {
             const int eA = at_lo + i * RT_ROWS * 4;
-            const int eB = at_lo + (RT_CAP - 1 - i) * RT_ROWS * 4;
+            const int eB = at_lo + (CAP - 1 - i) * RT_ROWS * 4;
             const int cA = i < nA ? *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (eA >> 1)) : 0;
             const int cB = i < nB ? *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (eB >> 1)) : 0;
 #pragma unroll
@@ -757,7 +800,7 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
             }
             const float other = __shfl_xor(half ? pA : pB, 32, kWave);
             if (i < n_mine) {
-                const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
+                const int e = at_lo + (half ? CAP - 1 - i : i) * RT_ROWS * 4;
                 float* sp = reinterpret_cast<float*>(s_list + e);
                 *sp = *sp + ((half ? pB : pA) + other);
             }
@@ -768,13 +811,13 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
             apply(i, xA, xB);
         }
     }
-    uint64_t L[kMaxTopK];
-    if (__builtin_amdgcn_ballot_w64(n_mine > kMaxTopK) == 0) {
-        // every lane found at most 16: read them all at once (slots past
+    uint64_t L[KM];
+    if (__builtin_amdgcn_ballot_w64(n_mine > KM) == 0) {
+        // every lane found at most KM: read them all at once (slots past
         // n_mine hold stale values and become the zero key) and sort
 #pragma unroll
-        for (int i = 0; i < kMaxTopK; ++i) {
-            const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
+        for (int i = 0; i < KM; ++i) {
+            const int e = at_lo + (half ? CAP - 1 - i : i) * RT_ROWS * 4;
             const uint64_t key = sel_key(*reinterpret_cast<const float*>(s_list + e),
                                          *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (e >> 1)));
             L[i] = i < n_mine ? key : 0;
@@ -782,17 +825,17 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
         bitonic_sort_desc_u64(L);
     } else {
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
+        for (int j = 0; j < KM; ++j) L[j] = 0;
         for (int i = 0; i < n_mine; ++i) {
-            const int e = at_lo + (half ? RT_CAP - 1 - i : i) * RT_ROWS * 4;
+            const int e = at_lo + (half ? CAP - 1 - i : i) * RT_ROWS * 4;
             insert_key(L, sel_key(*reinterpret_cast<const float*>(s_list + e),
                                   *reinterpret_cast<const uint16_t*>(s_list + LIST_IDX + (e >> 1))));
         }
     }
-    uint64_t M[kMaxTopK];
+    uint64_t M[KM];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-        const uint64_t o = L[kMaxTopK - 1 - j];
+    for (int j = 0; j < KM; ++j) {
+        const uint64_t o = L[KM - 1 - j];
         const uint32_t olo = __shfl_xor((uint32_t)o, 32, kWave);
         const uint32_t ohi = __shfl_xor((uint32_t)(o >> 32), 32, kWave);
         const uint64_t other = ((uint64_t)ohi << 32) | olo;
@@ -811,17 +854,17 @@ __global__ __launch_bounds__(256, EXACT ? 2 : (QF32 ? 4 : 5)) void k_route(Route
 }
 
 // ------------------------------------------------------------ exact fallback
-// The wave's kMaxTopK largest keys, descending (0 past the last), from
-// per-lane lists sorted descending; the lists are consumed.  Rank r takes the
-// largest score word over the lanes' heads, then the largest id word among
-// the heads with that score word; the lane holding it drops its head.  After
-// rank r a list is read at most kMaxTopK - 1 - r more times, so the drop
-// shifts only that many entries.  Returns how many keys are valid.
-__device__ __forceinline__ int wave_top_keys(uint64_t (&L)[kMaxTopK], uint64_t (&R)[kMaxTopK],
-                                             int top_k) {
+// The wave's KM largest keys, descending (0 past the last), from per-lane
+// lists sorted descending; the lists are consumed.  Rank r takes the largest
+// score word over the lanes' heads, then the largest id word among the heads
+// with that score word; the lane holding it drops its head.  After rank r a
+// list is read at most KM - 1 - r more times, so the drop shifts only that
+// many entries.  Returns how many keys are valid.
+template <int KM>
+__device__ __forceinline__ int wave_top_keys(uint64_t (&L)[KM], uint64_t (&R)[KM], int top_k) {
     int m = 0;
 #pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
+    for (int r = 0; r < KM; ++r) {
         R[r] = 0;
         if (r < top_k && m == r) {
             const uint32_t hh = (uint32_t)(L[0] >> 32);
@@ -834,7 +877,7 @@ __device__ __forceinline__ int wave_top_keys(uint64_t (&L)[kMaxTopK], uint64_t (
                 m = r + 1;
                 if (L[0] == mx) {
 #pragma unroll
-                    for (int j = 0; j + 1 < kMaxTopK - r; ++j) L[j] = L[j + 1];
+                    for (int j = 0; j + 1 < KM - r; ++j) L[j] = L[j + 1];
                 }
             }
         }
@@ -848,9 +891,10 @@ __device__ __forceinline__ int wave_top_keys(uint64_t (&L)[kMaxTopK], uint64_t (
 // keeping the 16 best keys of the candidates it scored in registers, then
 // rank-by-rank wave maxima; wave 0 merges the four waves' lists through
 // LDS.  Exact for any input, ties included.
-template <bool CAUSAL, bool QF32>
+// KM: the selection list length, as in k_route.
+template <bool CAUSAL, bool QF32, int KM>
 __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
-    __shared__ uint64_t s_top[4][kMaxTopK];
+    __shared__ uint64_t s_top[4][KM];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t count = __builtin_amdgcn_readfirstlane(*a.ovf_count);
@@ -878,9 +922,9 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
                 qv[2 * d2 + 1] = __uint_as_float(u & 0xFFFF0000u);
             }
         }
-        uint64_t L[kMaxTopK];
+        uint64_t L[KM];
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) L[j] = 0;
+        for (int j = 0; j < KM; ++j) L[j] = 0;
         // one candidate per lane per trip (64 VGPRs of loads, four waves per SIMD)
         for (int c = threadIdx.x; c < E; c += 256) {
             const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (int64_t)c * kD);
@@ -893,20 +937,20 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sc = fmaf(qv[4 * d4 + e], v[d4][e], sc);
             const uint64_t key = sel_key(sc, (uint32_t)c);
-            if (key > L[kMaxTopK - 1]) insert_key(L, key);
+            if (key > L[KM - 1]) insert_key(L, key);
         }
-        uint64_t R[kMaxTopK];
+        uint64_t R[KM];
         int m = wave_top_keys(L, R, a.top_k);
         if (lane == 0) {
 #pragma unroll
-            for (int r = 0; r < kMaxTopK; ++r) s_top[w][r] = R[r];
+            for (int r = 0; r < KM; ++r) s_top[w][r] = R[r];
         }
         __syncthreads();
         if (w == 0) {
-            // one key per lane, four sorted lists of 16
-            L[0] = s_top[lane >> 4][lane & 15];
+            // the four waves' sorted lists: lane l takes entries l % 16 + 16 j
+            // of list l / 16 (descending, so a sorted list of KM / 16 keys)
 #pragma unroll
-            for (int j = 1; j < kMaxTopK; ++j) L[j] = 0;
+            for (int j = 0; j < KM; ++j) L[j] = j < KM / 16 ? s_top[lane >> 4][(lane & 15) + 16 * j] : 0;
             m = wave_top_keys(L, R, a.top_k);
         }
         __syncthreads();
@@ -1302,33 +1346,35 @@ size_t route_workspace_bytes(const Geometry& g) {
     return g.beam > 0 ? tree_route_layout(g).total : route_layout(g).total;
 }
 
-template <bool CAUSAL, bool QF32>
-static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
-                                 const hipEvent_t* ev) {
+template <bool CAUSAL, bool QF32, int KM>
+static void launch_route_kernels_km(const RouteArgs& a, dim3 grid, hipStream_t s,
+                                    const hipEvent_t* ev) {
     // the longest row's candidate count picks the pass-2 form; fp32 queries
     // (group sums, pooled blocks) always take the full form: their delta
     // carries the q_lo term too, and the lean form's 2 * delta band
     // overflows the survivor lists
-    if (a.top_k > kMaxTopK) {
-        // wide selections (top_k 17..32): the exact pass routes every tile,
-        // each lane keeping its 32 best keys; nothing can overflow
-        hipLaunchKernelGGL((k_route<CAUSAL, QF32, true, false, kMaxTopKWide>), grid, dim3(256), 0,
-                           s, a);
-        mark(ev, 2, s);
-        return;
-    }
     const int cmax = CAUSAL ? (eligible_blocks(a.P - 1, a.bs, a.window) >> a.cshift) : a.nb;
     bool lean = false;
     if constexpr (!QF32) lean = cmax >= kRouteLeanMinCand;
     if constexpr (!QF32) {
-        if (lean) hipLaunchKernelGGL((k_route<CAUSAL, false, false, true>), grid, dim3(256), 0, s, a);
+        if (lean)
+            hipLaunchKernelGGL((k_route<CAUSAL, false, false, true, KM>), grid, dim3(256), 0, s, a);
     }
-    if (!lean) hipLaunchKernelGGL((k_route<CAUSAL, QF32, false, false>), grid, dim3(256), 0, s, a);
+    if (!lean) hipLaunchKernelGGL((k_route<CAUSAL, QF32, false, false, KM>), grid, dim3(256), 0, s, a);
     mark(ev, 2, s);
     // exactly one of the two exact passes does work, chosen on the device by
     // the number of overflowing rows
-    hipLaunchKernelGGL((k_route_fallback<CAUSAL, QF32>), dim3(FB_GRID), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((k_route<CAUSAL, QF32, true, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_route_fallback<CAUSAL, QF32, KM>), dim3(FB_GRID), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_route<CAUSAL, QF32, true, false, KM>), grid, dim3(256), 0, s, a);
+}
+
+template <bool CAUSAL, bool QF32>
+static void launch_route_kernels(const RouteArgs& a, dim3 grid, hipStream_t s,
+                                 const hipEvent_t* ev) {
+    if (a.top_k <= kMaxTopK)
+        launch_route_kernels_km<CAUSAL, QF32, kMaxTopK>(a, grid, s, ev);
+    else
+        launch_route_kernels_km<CAUSAL, QF32, kMaxTopKWide>(a, grid, s, ev);
 }
 
 // Flat routing of g's rows over g.nb summaries `summ` into idx (row stride

@@ -39,9 +39,8 @@
  *     the hi product plus a bf16 dot product with the lo part; rows that
  *     overflow the router's fast path are rescored by an exact pass, one by
  *     one with fp32 FMA chains when at most 16384 rows need it, by whole
- *     tiles with the hi+lo products when more do; with top_k above 16 every
- *     tile takes that whole-tile pass), but never on the stream, the run or
- *     the calling thread.
+ *     tiles with the hi+lo products when more do), but never on the stream,
+ *     the run or the calling thread.
  *   - Calls on distinct streams with distinct workspaces may run
  *     concurrently.
  */
@@ -62,8 +61,7 @@ typedef struct lsa_params {
     int32_t seq_len;   /* N, a positive multiple of block; N/block <= 65536 */
     int32_t head_dim;  /* D; this build supports 64 */
     int32_t block;     /* bs: 16, 32, 64 or 128 (key block; in image mode also the query block) */
-    int32_t top_k;     /* 1 .. 32 (17 .. 32: every routing tile takes the
-                          exact pass, see Determinism above) */
+    int32_t top_k;     /* 1 .. 32 */
     int32_t window;    /* causal: a multiple of block, >= block; image mode: 0 */
     int32_t causal;    /* 1: per-query routing + causal window; 0: image mode */
     float scale;       /* softmax scale; <= 0 selects 1/sqrt(D) */

@@ -9,8 +9,8 @@ scores are more than 1e-3 apart.  The first two words of the routing
 workspace count the overflowing rows and the 128-row tiles holding them;
 each case checks that the exact pass ran.  Up to 16384 rows are redone one
 by one (the "few" cases), beyond that whole tiles are (the "many" cases).
-A survivor list holds 29 entries, so an all-ties row overflows once it has
-more than 29 candidates."""
+A survivor list holds 29 entries (56 for top_k above 16), so an all-ties
+row overflows once it has more candidates than that."""
 import sys
 
 import numpy as np
@@ -62,6 +62,12 @@ CASES = [
     case(1, 2, 1, 4096, 64, 16, 128, 1, consensus=1, expect="few"),
     case(1, 4, 2, 16384, 64, 16, 256, 1, consensus=1, expect="many"),
     case(1, 4, 2, 4096, 64, 16, 256, 2, consensus=1),
+    # top_k 17..32 (56-entry survivor lists)
+    case(1, 2, 1, 4096, 64, 32, 128, 1, expect="few"),
+    case(1, 4, 1, 16384, 64, 24, 512, 1, expect="many"),
+    case(1, 2, 1, 16 * 400, 16, 20, 32, 2),
+    case(1, 2, 1, 4096, 16, 32, 0, 1, causal=0, expect="few"),
+    case(1, 4, 2, 16384, 64, 32, 256, 1, consensus=1, expect="many"),
 ]
 
 
