@@ -46,52 +46,52 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18536.6, 8444.0),
-            "bucket scan": (5.4, 12.1),
-            "bucket scatter": (21088.2, 69528.7),
+            "V transpose + bucket count": (18530.6, 8444.0),
+            "bucket scan": (5.6, 12.1),
+            "bucket scatter": (21086.3, 69496.8),
             "key summary": (4141.7, 528.0),
-            "routed-block partials": (460322.5, 963904.0),
-            "routing": (29537.7, 28672.0),
-            "routing fallback": (30.0, 0.0),
-            "window + merge": (530956.4, 114688.8),
+            "routed-block partials": (460033.0, 963924.5),
+            "routing": (29527.0, 28672.0),
+            "routing fallback": (37.5, 0.0),
+            "window + merge": (531117.4, 114688.8),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73834.2, 34808.0),
-            "bucket scan": (11.4, 48.1),
-            "bucket scatter": (115612.9, 480827.6),
-            "key summary": (16430.8, 2112.0),
-            "routed-block partials": (1919022.7, 3909892.2),
-            "routing": (119047.6, 114688.8),
-            "routing fallback": (30.0, 0.0),
-            "window + merge": (2194363.3, 458758.1),
+            "V transpose + bucket count": (73828.0, 34808.0),
+            "bucket scan": (11.6, 48.1),
+            "bucket scatter": (115618.2, 482866.0),
+            "key summary": (16430.6, 2112.0),
+            "routed-block partials": (1918880.3, 3910208.9),
+            "routing": (119052.8, 114688.0),
+            "routing fallback": (37.5, 0.0),
+            "window + merge": (2195014.9, 458757.0),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (65553.5, 131072.0),
-            "key summary": (131162.5, 49282.0),
-            "routing": (16815.4, 2048.0),
-            "routing fallback": (32.0, 0.0),
-            "window + merge": (211808.1, 262169.0),
+            "key summary": (131162.4, 49284.0),
+            "routing": (16811.9, 2048.0),
+            "routing fallback": (30.3, 0.0),
+            "window + merge": (211949.4, 262168.6),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "2402309d5ed09a15", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589931.3, 393151.9),
+            "V transpose + bucket count": (589925.4, 393151.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (955176.9, 6898283.7),
-            "key summary": (131120.5, 16896.0),
-            "routed-block partials": (15570444.5, 31398167.5),
-            "routing": (1430447.8, 917589.0),
-            "routing fallback": (475921.0, 90.8),
-            "window + merge": (20125695.7, 3670086.4),
+            "bucket scatter": (955063.2, 6905586.9),
+            "key summary": (131120.4, 16896.0),
+            "routed-block partials": (15568842.3, 31403596.1),
+            "routing": (1426966.5, 917588.2),
+            "routing fallback": (471453.7, 90.7),
+            "window + merge": (20128585.1, 3670074.9),
         },
     },
 }
