@@ -23,6 +23,9 @@ LIMITS = [
              seed=91),
     # 20000 blocks of 32 keys over a 2:1 group, odd window-block count
     Workload("limit_nb20000_bs32", 1, 2, 1, 32 * 20000, 64, 32, 8, 96, 1, "normal", seed=92),
+    # the maximum block count with 32-entry selection lists
+    Workload("limit_nb65536_bs16_k32", 1, 1, 1, 16 * 65536, 64, 16, 32, 16, 1, "topics", topics=64,
+             seed=93),
 ]
 
 
