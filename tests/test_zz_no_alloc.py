@@ -29,11 +29,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-# (workload of the cache, T: tokens filled); the second is smaller in every
-# dimension and ends mid-block
+# (workload of the cache, T: tokens filled); each call is smaller than the
+# one before (the second takes 32-key chunk sets, top_k above 16), and the
+# last is smaller in every dimension and ends mid-block
 CASES = [
     (Workload("noalloc_big", 2, 8, 2, 16384, 64, 64, 16, 512, 1, "topics", topics=16, seed=81),
      16384),
+    (Workload("noalloc_wide", 1, 8, 2, 8192, 64, 64, 32, 256, 1, "topics", topics=16, seed=83),
+     8000),
     (Workload("noalloc_small", 1, 4, 1, 4096, 64, 32, 8, 256, 1, "normal", seed=82), 3001),
 ]
 
