@@ -74,22 +74,6 @@ __host__ __device__ __forceinline__ int eligible_blocks(int t, int bs, int windo
     return e > 0 ? e : 0;
 }
 
-// Which entries of one idx row are used: entry s counts when it is a
-// candidate (0 <= c < ncand) and larger than the previously used entry.
-// Returns a bit mask over the row's top_k (<= 32) slots.
-__device__ __forceinline__ uint32_t used_slots(const int32_t* row, int top_k, int ncand) {
-    uint32_t mask = 0;
-    int prev = -1;
-    for (int s = 0; s < top_k; ++s) {
-        int c = row[s];
-        if (c > prev && c < ncand) {
-            mask |= 1u << s;
-            prev = c;
-        }
-    }
-    return mask;
-}
-
 // ---------------------------------------------------------------- routing preparation
 // The routing kernels read block means as bf16 hi + lo parts (hi = bf16(x),
 // lo = bf16(x - hi)) and bound their error with the largest norms |x| and

@@ -888,7 +888,7 @@ __device__ __forceinline__ int wave_top_keys(uint64_t (&L)[KM], uint64_t (&R)[KM
 // Queued rows are redone exactly, one workgroup per row, when there are at
 // most FB_ROWS of them (more are redone by whole tiles, k_route<.., true>):
 // fp32 scores of every candidate (fma chain over d = 0..63), each lane
-// keeping the 16 best keys of the candidates it scored in registers, then
+// keeping the KM best keys of the candidates it scored in registers, then
 // rank-by-rank wave maxima; wave 0 merges the four waves' lists through
 // LDS.  Exact for any input, ties included.
 // KM: the selection list length, as in k_route.
@@ -980,14 +980,15 @@ __global__ __launch_bounds__(256) void k_route_fallback(RouteArgs a) {
 // variance = sum of squares / bs - mean^2.
 //
 // Selection: the two lanes of a pair take the even and the odd blocks
-// respectively.  Each lane keeps its 16 best (score, block) pairs sorted by
-// score.  A lane sees its blocks in ascending order, so a newcomer beats a
-// kept entry exactly when its score is strictly larger (equal scores keep
-// the lower, older block): the order (score desc, block asc) needs only
-// float compares.  Blocks that beat the lane's 16th score are appended to a
-// per-lane LDS queue and inserted in batches of CUM_Q offers, so that a wave
-// runs the insertion about as often as its busiest lane needs it rather
-// than whenever any lane does.  The pair's lists are merged once at the end.
+// respectively.  Each lane keeps its KM (16, or 32 for top_k above 16) best
+// (score, block) pairs sorted by score.  A lane sees its blocks in ascending
+// order, so a newcomer beats a kept entry exactly when its score is strictly
+// larger (equal scores keep the lower, older block): the order (score desc,
+// block asc) needs only float compares.  Blocks that beat the lane's last
+// kept score are appended to a per-lane LDS queue and inserted in batches of
+// CUM_Q offers, so that a wave runs the insertion about as often as its
+// busiest lane needs it rather than whenever any lane does.  The pair's
+// lists are merged once at the end.
 // No survivor capacity, so no fallback.
 constexpr int CUM_Q = 8;  // offers per lane between insertion batches
 
