@@ -23,7 +23,8 @@
 //                       Z moves the read by a/(Z+a) times the displacement of
 //                       the new value), and writes fp32 output.
 // Image mode (k_image_attend): one wave per 16-token query block; its
-// selected 16-key blocks are gathered straight into MFMA operands.
+// selected 16-key blocks are gathered straight into MFMA operands (K) or
+// through LDS with transposing reads (V).
 //
 // MFMA orientation: S^T = K . Q^T on 16x16x32 tiles, so lane l holds query
 // row l%16 and keys 16i + 4(l/16) + r.  Those probabilities are exactly the
@@ -52,8 +53,8 @@ constexpr float RESCALE_SLACK = 8.f;  // log2 headroom before a running max is r
 
 // ------------------------------------------------------------ V transpose
 // V [BG][N][64] -> V^T tiles [BG][ceil(N/TW)][64 d][TW keys]; keys >= N are
-// zero.  TW = 64 for the causal kernels; TW = 16 (one image-mode block per
-// tile) makes a block's V^T 2 KB of contiguous memory.
+// zero.  The causal kernels take TW = 64 (image mode reads V rows itself and
+// transposes them on their way out of LDS).
 template <int TW>
 __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict__ v,
                                                      uint16_t* __restrict__ vt, int N, int ntiles) {
@@ -582,27 +583,64 @@ __global__ __launch_bounds__(256, KM > kMaxTopK ? 2 : 4) void k_window_merge(Win
 struct ImgArgs {
     const uint16_t* q;
     const uint16_t* k;
-    const uint16_t* vt;  // V^T per 16-key block [BG][nb][64 d][16 keys]
+    const uint16_t* v;   // [B,Hkv,N,64]: a 16-key block is 2 KB of contiguous rows
     const int32_t* idx;  // [B,Hq,nb,top_k]; group_route: [B,Hkv,nb,top_k]
     float* out;
-    int Hq, Hkv, N, nb, top_k, ntiles;
+    int Hq, Hkv, N, nb, top_k;
     int64_t n_qblocks;   // B*Hq*nb
     float scale_log2;
     int group_route;
 };
 
+// O^T += V^T P^T over four 16-key tiles (KT = 4) whose probabilities are
+// p[i][r] (key 16i + 4(l/16) + r), with V in LDS as [key][dim] rows of pitch
+// vpitch.  The A operand (V^T: a dim per lane, 8 keys) comes from
+// ds_read_b64_tr_b16, which hands lane 4a + b of each 16-lane group element b
+// of the 8-byte chunks addressed by lanes a, a + 4, a + 8 and a + 12 of the
+// group: so lane s of the group addresses key row (base + s / 4) at dims
+// 16 mt + 4 (s % 4), and lane m receives dim 16 mt + m of the four keys
+// base .. base + 3.
+__device__ __forceinline__ void pv_accumulate_rows(const __bf16* s_v, int vpitch, int lane,
+                                                   const float (&p)[4][4], f32x4 (&o)[4]) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 Bp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            Bp[j] = (__bf16)p[2 * ks][j];
+            Bp[4 + j] = (__bf16)p[2 * ks + 1][j];
+        }
+        // key rows of this lane's address: 32 ks + 4 g + s / 4, and 16 more
+        const __bf16* r0 = s_v + (32 * ks + 4 * g + (s >> 2)) * vpitch + 4 * (s & 3);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(r0 + 16 * mt));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(r0 + 16 * vpitch + 16 * mt));
+            const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[mt] = mfma16(__builtin_bit_cast(bf16x8, a8), Bp, o[mt]);
+        }
+    }
+}
+
 // One wave per 16-token query block (block size 16).  The selected blocks
 // are processed four at a time (64 keys) with an online softmax; K feeds the
-// MFMA straight from global memory, the blocks' V^T columns are copied into
+// MFMA straight from global memory, the blocks' V rows are copied into
 // the wave's own LDS region.  KM: the slot list length, as in k_window_merge.
+constexpr int IVP = kD + 8;  // LDS pitch of the image kernel's V rows (bf16): 16-byte rows
 template <int KM>
 __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 s_vt[4][kD * WVP];
+    __shared__ __attribute__((aligned(16))) __bf16 s_v[4][64 * IVP];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
     // item = xcd * (grid / 8) + blockIdx / 8 gives each XCD a contiguous run
-    // of query blocks, i.e. whole heads, whose K and V^T its L2 then holds.
+    // of query blocks, i.e. whole heads, whose K and V its L2 then holds.
     const int per_xcd = gridDim.x / 8;
     const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const int64_t qb = (int64_t)item * 4 + w;
@@ -612,7 +650,6 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
     const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq), g = h / (a.Hq / a.Hkv);
     const int64_t bg = (int64_t)b * a.Hkv + g;
     const int64_t k0 = bg * a.N * kD;
-    const int64_t vt0 = bg * a.ntiles * (kD * VT_TILE);
     const int t = 16 * i + (lane & 15);
     const int64_t row = bh * a.N + t;
 
@@ -628,13 +665,13 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    __bf16* vt = s_vt[w];
+    __bf16* sv = s_v[w];
 
     for (int c0 = 0; c0 < nused; c0 += 4) {
-        // up to four 16-key blocks: their K rows (MFMA operands) and V^T
-        // (lane d takes row d of each block's contiguous 2 KB, two 16-byte
-        // pieces) are all requested before any is used, so the two gathers
-        // overlap
+        // up to four 16-key blocks: their K rows (MFMA operands) and V rows
+        // (lane l takes dims 16 (l % 4) .. +15 of key l / 4 of each block's
+        // contiguous 2 KB, two 16-byte pieces) are all requested before any
+        // is used, so the two gathers overlap
         int cblk[4];
         bf16x8 kop[4][2];
         u32x4 vpart[4][2];
@@ -644,7 +681,7 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
             cblk[jb] = have ? pick<KM>(csel, nth_slot(used, c0 + jb)) : 0;
             const uint16_t* kr =
                 a.k + k0 + ((int64_t)cblk[jb] * 16 + (lane & 15)) * kD + 8 * (lane >> 4);
-            const uint16_t* src = a.vt + vt0 + (int64_t)cblk[jb] * (kD * 16) + lane * 16;
+            const uint16_t* src = a.v + k0 + ((int64_t)cblk[jb] * 16 + (lane >> 2)) * kD + 16 * (lane & 3);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) kop[jb][ks] = load_bf16x8(kr + 32 * ks);
 #pragma unroll
@@ -659,8 +696,8 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
             const bool have = c0 + jb < nused;
 #pragma unroll
             for (int part = 0; part < 2; ++part)
-                lds_store_2x8(vt + lane * WVP + jb * 16 + 8 * part,
-                              have ? vpart[jb][part] : u32x4{0u, 0u, 0u, 0u});
+                *reinterpret_cast<u32x4*>(sv + (jb * 16 + (lane >> 2)) * IVP + 16 * (lane & 3) + 8 * part) =
+                    have ? vpart[jb][part] : u32x4{0u, 0u, 0u, 0u};
         }
         f32x4 sc[4];
         float mx = -INFINITY;
@@ -693,8 +730,8 @@ __global__ __launch_bounds__(256, 2) void k_image_attend(ImgArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
         m_run = m_new;
-        __builtin_amdgcn_wave_barrier();  // the V^T stores above precede these reads
-        pv_accumulate<4>(vt, WVP, 0, lane, p, o);
+        __builtin_amdgcn_wave_barrier();  // the V stores above precede these reads
+        pv_accumulate_rows(sv, IVP, lane, p, o);
     }
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* dst = a.out + row * kD + 4 * (lane >> 4);
@@ -773,8 +810,8 @@ static AttendLayout attend_layout(const Geometry& g) {
     const size_t nbg = (size_t)g.B * g.Hkv;
     const size_t ntiles = ((size_t)g.N + VT_TILE - 1) / VT_TILE;
     size_t off = 0;
-    L.vt = off;       off += align_up(nbg * ntiles * kD * VT_TILE * 2, 256);
-    if (g.causal) {
+    if (g.causal) {  // image mode reads V itself
+        L.vt = off;       off += align_up(nbg * ntiles * kD * VT_TILE * 2, 256);
         L.plan = chunk_plan(g);
         L.NB = (int64_t)L.plan.nchunk * nbg * g.nb;
         L.crows = (int64_t)g.B * g.Hq << L.plan.pc_log2;
@@ -814,14 +851,8 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     uint16_t* vt = reinterpret_cast<uint16_t*>(base + L.vt);
     const int ntiles = (g.N + VT_TILE - 1) / VT_TILE;
     const int nbg = g.B * g.Hkv;
-    if (g.causal)
-        hipLaunchKernelGGL(k_transpose_v<VT_TILE>, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s,
-                           v, vt, g.N, ntiles);
-    else
-        hipLaunchKernelGGL(k_transpose_v<16>, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s, v,
-                           vt, g.N, ntiles);
     if (!g.causal) {
-        ImgArgs a{q, k, vt, idx, out, g.Hq, g.Hkv, g.N, g.nb, g.top_k, ntiles,
+        ImgArgs a{q, k, v, idx, out, g.Hq, g.Hkv, g.N, g.nb, g.top_k,
                   (int64_t)g.B * g.Hq * g.nb, scale_log2, g.consensus};
         const unsigned grid = (unsigned)(((a.n_qblocks + 3) / 4 + 7) / 8 * 8);  // multiple of 8
         for (int i = 4; i < 8; ++i) mark(ev, i, s);
@@ -832,6 +863,8 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
         mark(ev, 8, s);
         return hipGetLastError();
     }
+    hipLaunchKernelGGL(k_transpose_v<VT_TILE>, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s, v,
+                       vt, g.N, ntiles);
     uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
     uint32_t* offsets = reinterpret_cast<uint32_t*>(base + L.offsets);
     uint32_t* cursor = reinterpret_cast<uint32_t*>(base + L.cursor);
