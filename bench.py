@@ -46,52 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18530.6, 8444.0),
-            "bucket scan": (5.6, 12.1),
-            "bucket scatter": (21086.3, 69496.8),
-            "key summary": (4141.7, 528.0),
-            "routed-block partials": (460033.0, 963924.5),
-            "routing": (29527.0, 28672.0),
+            "V transpose + bucket count": (18537.4, 8444.0),
+            "bucket scan": (5.4, 12.1),
+            "bucket scatter": (21091.4, 69543.8),
+            "key summary": (4141.5, 528.0),
+            "routed-block partials": (459996.2, 963996.1),
+            "routing": (29528.8, 28672.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (531117.4, 114688.8),
+            "window + merge": (531004.1, 114688.6),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73828.0, 34808.0),
-            "bucket scan": (11.6, 48.1),
-            "bucket scatter": (115618.2, 482866.0),
-            "key summary": (16430.6, 2112.0),
-            "routed-block partials": (1918880.3, 3910208.9),
-            "routing": (119052.8, 114688.0),
+            "V transpose + bucket count": (73834.6, 34808.0),
+            "bucket scan": (11.4, 48.1),
+            "bucket scatter": (115587.0, 484586.1),
+            "key summary": (16431.0, 2112.0),
+            "routed-block partials": (1918792.9, 3910172.1),
+            "routing": (119070.8, 114688.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (2195014.9, 458757.0),
+            "window + merge": (2194611.7, 458756.0),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (65553.5, 131072.0),
-            "key summary": (131162.4, 49284.0),
-            "routing": (16811.9, 2048.0),
+            "key summary": (65595.6, 32897.3),
+            "routing": (82378.9, 18433.7),
             "routing fallback": (30.3, 0.0),
-            "window + merge": (211949.4, 262168.6),
+            "window + merge": (212798.7, 262165.5),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "440d6f38bb6cdd47", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589925.4, 393151.9),
+            "V transpose + bucket count": (589931.9, 393151.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (955063.2, 6905586.9),
-            "key summary": (131120.4, 16896.0),
-            "routed-block partials": (15568842.3, 31403596.1),
-            "routing": (1426966.5, 917588.2),
-            "routing fallback": (471453.7, 90.7),
-            "window + merge": (20128585.1, 3670074.9),
+            "bucket scatter": (955085.3, 6900950.7),
+            "key summary": (131120.2, 16896.0),
+            "routed-block partials": (15571265.7, 31407366.2),
+            "routing": (1430522.7, 917588.2),
+            "routing fallback": (466985.4, 90.5),
+            "window + merge": (20124462.7, 3670074.1),
         },
     },
 }
