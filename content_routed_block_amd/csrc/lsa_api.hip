@@ -200,7 +200,8 @@ static lsa_status forward_impl(const lsa_params* p, const void* q, const void* k
         lsa::mark(ev, 3, s);
     } else if (g.beam == 0) {
         // flat routing: the key summary also prepares the router's inputs
-        st = from_hip(lsa::launch_summary_and_route_prep(g, static_cast<const uint16_t*>(k), kbar,
+        st = from_hip(lsa::launch_summary_and_route_prep(g, static_cast<const uint16_t*>(k),
+                                                         static_cast<const uint16_t*>(q), kbar,
                                                          rest, s));
         if (st != LSA_OK) return st;
         lsa::mark(ev, 1, s);

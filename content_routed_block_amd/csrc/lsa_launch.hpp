@@ -32,6 +32,11 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s)
 hipError_t launch_summarize_route(const uint16_t* x, float* xbar, int BH, int N, int bs,
                                   uint16_t* khi, uint16_t* klo, float* ckn, float* clo,
                                   int nb_pad, hipStream_t s);
+// The same for blocks of 16 tokens, with the pooling of q [BHq, N, 64] into
+// qbar [BHq, N/16, 64] (fp32) in the same launch (image mode).
+hipError_t launch_summarize_route_pool16(const uint16_t* k, float* kbar, int BHk, const uint16_t* q,
+                                         float* qbar, int BHq, int N, uint16_t* khi, uint16_t* klo,
+                                         float* ckn, float* clo, int nb_pad, hipStream_t s);
 
 // Routing workspace (bytes) and launch.  qbar may be NULL in causal mode.
 size_t route_workspace_bytes(const Geometry& g);
@@ -40,10 +45,11 @@ hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
                         const hipEvent_t* ev = nullptr);
 // A layer's key summary and the preparation of flat routing in one pass:
 // clears the router's counters and norm maxima, then summarises k into kbar
-// and writes the router's inputs; launch_route_prepared then routes.  Only
-// for flat routing (beam = 0, beta = 0).
-hipError_t launch_summary_and_route_prep(const Geometry& g, const uint16_t* k, float* kbar,
-                                         void* ws, hipStream_t s);
+// and writes the router's inputs (in image mode the same launch pools q into
+// the routing workspace); launch_route_prepared then routes.  Only for flat
+// routing (beam = 0, beta = 0).
+hipError_t launch_summary_and_route_prep(const Geometry& g, const uint16_t* k, const uint16_t* q,
+                                         float* kbar, void* ws, hipStream_t s);
 hipError_t launch_route_prepared(const Geometry& g, const uint16_t* q, const float* kbar,
                                  int32_t* idx, void* ws, hipStream_t s,
                                  const hipEvent_t* ev = nullptr);

@@ -1509,23 +1509,31 @@ static hipError_t route_tree(const Geometry& g, const uint16_t* q, const float* 
     return hipGetLastError();
 }
 
-hipError_t launch_summary_and_route_prep(const Geometry& g, const uint16_t* k, float* kbar,
-                                         void* ws, hipStream_t s) {
+hipError_t launch_summary_and_route_prep(const Geometry& g, const uint16_t* k, const uint16_t* q,
+                                         float* kbar, void* ws, hipStream_t s) {
     const RouteLayout L = route_layout(g);
     char* base = static_cast<char*>(ws);
     const size_t nbg = (size_t)g.B * g.Hkv;
     float* ckn = reinterpret_cast<float*>(base + L.cmax);
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(base), L.fill_words, 0u, s);
     if (e != hipSuccess) return e;
-    return launch_summarize_route(k, kbar, g.B * g.Hkv, g.N, g.bs,
-                                  reinterpret_cast<uint16_t*>(base + L.khi),
-                                  reinterpret_cast<uint16_t*>(base + L.klo), ckn,
-                                  ckn + nbg * L.ncb * kChunkMaxStride, L.nb_pad, s);
+    uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
+    uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
+    float* clo = ckn + nbg * L.ncb * kChunkMaxStride;
+    if (!g.causal)  // image mode: the query pooling joins the same launch
+        return launch_summarize_route_pool16(k, kbar, g.B * g.Hkv, q,
+                                             reinterpret_cast<float*>(base + L.qbar), g.B * g.Hq,
+                                             g.N, khi, klo, ckn, clo, L.nb_pad, s);
+    return launch_summarize_route(k, kbar, g.B * g.Hkv, g.N, g.bs, khi, klo, ckn, clo, L.nb_pad, s);
 }
 
 hipError_t launch_route_prepared(const Geometry& g, const uint16_t* q, const float* kbar,
                                  int32_t* idx, void* ws, hipStream_t s, const hipEvent_t* ev) {
-    hipError_t e = route_flat(g, q, kbar, idx, g.top_k, 0, ws, s, ev, nullptr, -1, true);
+    // image mode: the pooled queries were written by the key summary's launch
+    const float* qbar = g.causal ? nullptr
+                                 : reinterpret_cast<const float*>(static_cast<char*>(ws) +
+                                                                  route_layout(g).qbar);
+    hipError_t e = route_flat(g, q, kbar, idx, g.top_k, 0, ws, s, ev, qbar, -1, true);
     mark(ev, 3, s);
     return e;
 }

@@ -30,14 +30,14 @@ struct RouteOut {
 // itself (eight blocks per wave), so no cross-lane reduction is needed; a
 // load instruction still reads whole 128-byte rows (eight lanes per row).
 // With PREP, rows run over heads x nb_pad, so a workgroup (32 rows) is one
-// chunk and stores its maxima itself.
+// chunk and stores its maxima itself.  wg: this workgroup's index.
 template <bool PREP>
-__global__ __launch_bounds__(256) void k_summarize16(const uint16_t* __restrict__ x,
-                                                     float* __restrict__ xbar,
-                                                     int64_t n_blocks, int nb, RouteOut ro) {
+__device__ __forceinline__ void summarize16(const uint16_t* __restrict__ x, float* __restrict__ xbar,
+                                            int64_t n_blocks, int nb, const RouteOut& ro,
+                                            int64_t wg) {
     __shared__ float s_n[2][4];
     const int lane = threadIdx.x & 63;
-    const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
+    const int64_t r = (wg * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
     const int dg = lane & 7;  // dims 8*dg .. 8*dg+7
     int64_t blk = r;          // the block summarised (PREP: row r of the padded layout)
     bool have = r < n_blocks;
@@ -94,14 +94,37 @@ __global__ __launch_bounds__(256) void k_summarize16(const uint16_t* __restrict_
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        const int64_t r0 = (int64_t)blockIdx.x * 32;  // this workgroup's chunk
+        const int64_t r0 = wg * 32;  // this workgroup's chunk
         if ((r0 / ro.nb_pad) * nb < n_blocks) {
-            ro.ckn[blockIdx.x * (int64_t)kChunkMaxStride] =
+            ro.ckn[wg * (int64_t)kChunkMaxStride] =
                 fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3]));
-            ro.clo[blockIdx.x * (int64_t)kChunkMaxStride] =
+            ro.clo[wg * (int64_t)kChunkMaxStride] =
                 fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3]));
         }
     }
+}
+
+template <bool PREP>
+__global__ __launch_bounds__(256) void k_summarize16(const uint16_t* __restrict__ x,
+                                                     float* __restrict__ xbar,
+                                                     int64_t n_blocks, int nb, RouteOut ro) {
+    summarize16<PREP>(x, xbar, n_blocks, nb, ro, blockIdx.x);
+}
+
+// Image mode's two poolings in one launch: the first wg_k workgroups
+// summarise the keys with the routing preparation, the rest pool the
+// queries (both in blocks of 16 tokens).
+__global__ __launch_bounds__(256) void k_summarize16_kq(const uint16_t* __restrict__ k,
+                                                        float* __restrict__ kbar,
+                                                        int64_t nk_blocks, RouteOut ro,
+                                                        int64_t wg_k,
+                                                        const uint16_t* __restrict__ q,
+                                                        float* __restrict__ qbar,
+                                                        int64_t nq_blocks, int nb) {
+    if ((int64_t)blockIdx.x < wg_k)
+        summarize16<true>(k, kbar, nk_blocks, nb, ro, blockIdx.x);
+    else
+        summarize16<false>(q, qbar, nq_blocks, nb, ro, blockIdx.x - wg_k);
 }
 
 // One wave per block.  With PREP, waves run over heads x nb_pad; a
@@ -223,6 +246,18 @@ hipError_t launch_summarize_route(const uint16_t* x, float* xbar, int BH, int N,
                                   uint16_t* khi, uint16_t* klo, float* ckn, float* clo,
                                   int nb_pad, hipStream_t s) {
     return summarize<true>(x, xbar, BH, N, bs, RouteOut{khi, klo, ckn, clo, nb_pad}, s);
+}
+
+hipError_t launch_summarize_route_pool16(const uint16_t* k, float* kbar, int BHk, const uint16_t* q,
+                                         float* qbar, int BHq, int N, uint16_t* khi, uint16_t* klo,
+                                         float* ckn, float* clo, int nb_pad, hipStream_t s) {
+    const int nb = N / 16;
+    const int64_t nk = (int64_t)BHk * nb, nq = (int64_t)BHq * nb;
+    const int64_t wg_k = ((int64_t)BHk * nb_pad + 31) / 32;  // rows over heads x nb_pad
+    const int64_t wg_q = (nq + 31) / 32;
+    hipLaunchKernelGGL(k_summarize16_kq, dim3((unsigned)(wg_k + wg_q)), dim3(256), 0, s, k, kbar,
+                       nk, RouteOut{khi, klo, ckn, clo, nb_pad}, wg_k, q, qbar, nq, nb);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s) {

@@ -254,7 +254,7 @@ lsa_status lsa_decode_noalloc(const lsa_params *p, int32_t cache_len, const void
  * recorded on `stream` at the i-th stage boundary:
  *   0 start, 1 key summary, 2 routing, 3 routing fallback, 4 V transpose and
  *   bucket count, 5 bucket scan, 6 bucket scatter, 7 routed-block partials,
- *   8 window and merge (image mode: 2 includes the query summary, 4-7 are
+ *   8 window and merge (image mode: 1 includes the query pooling, 4-7 are
  *   empty and 8 is the image-mode attention).
  * Elapsed time between events i-1 and i is the duration of stage i.  No
  * synchronisation happens inside; otherwise identical to lsa_forward. */
