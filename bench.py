@@ -46,51 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18537.4, 8444.0),
+            "V transpose + bucket count": (18537.1, 8444.0),
             "bucket scan": (5.4, 12.1),
-            "bucket scatter": (21091.4, 69543.8),
-            "key summary": (4141.5, 528.0),
-            "routed-block partials": (459996.2, 963996.1),
-            "routing": (29528.8, 28672.0),
+            "bucket scatter": (21086.8, 69550.7),
+            "key summary": (4144.7, 528.0),
+            "routed-block partials": (460239.0, 963838.5),
+            "routing": (29524.9, 28672.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (531004.1, 114688.6),
+            "window + merge": (531058.4, 114688.7),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73834.6, 34808.0),
+            "V transpose + bucket count": (73834.4, 34808.0),
             "bucket scan": (11.4, 48.1),
-            "bucket scatter": (115587.0, 484586.1),
-            "key summary": (16431.0, 2112.0),
-            "routed-block partials": (1918792.9, 3910172.1),
-            "routing": (119070.8, 114688.0),
+            "bucket scatter": (115574.1, 482316.3),
+            "key summary": (16433.6, 2112.0),
+            "routed-block partials": (1918629.3, 3910146.3),
+            "routing": (119071.8, 114688.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (2194611.7, 458756.0),
+            "window + merge": (2194508.9, 458756.7),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "key summary": (65595.6, 32897.3),
-            "routing": (82378.9, 18433.7),
+            "key summary": (131145.9, 49283.3),
+            "routing": (16811.9, 2048.0),
             "routing fallback": (30.3, 0.0),
-            "window + merge": (212798.7, 262165.5),
+            "window + merge": (212912.2, 262171.0),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "d5194a25061e717e", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589931.9, 393151.9),
+            "V transpose + bucket count": (589932.0, 393151.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (955085.3, 6900950.7),
-            "key summary": (131120.2, 16896.0),
-            "routed-block partials": (15571265.7, 31407366.2),
-            "routing": (1430522.7, 917588.2),
-            "routing fallback": (466985.4, 90.5),
-            "window + merge": (20124462.7, 3670074.1),
+            "bucket scatter": (954717.0, 6911982.2),
+            "key summary": (131122.7, 16896.0),
+            "routed-block partials": (15569980.0, 31406130.5),
+            "routing": (1430906.4, 917588.1),
+            "routing fallback": (473300.2, 91.0),
+            "window + merge": (20123147.8, 3670073.3),
         },
     },
 }
