@@ -24,8 +24,10 @@
 //                       counter) combines the row's partial (max, mass,
 //                       output) triples.
 // Top-k sets are found by a radix select over the 64-bit keys with wave
-// ballots: the k-th largest key is built bit by bit from the count of keys
-// at or above each candidate, so no shuffles or LDS round trips are needed.
+// ballots: the threshold is built bit by bit from the count of keys at or
+// above each candidate, so no shuffles or LDS round trips are needed; the
+// block-id half of the keys is searched only when scores tie at the k-th
+// place.
 #include <math.h>
 
 #include <algorithm>
@@ -91,14 +93,34 @@ __device__ __forceinline__ float block_sum_f32(float x, float* s_red) {
 }
 
 // ------------------------------------------------------------ wave radix select
-// The k-th largest of the wave's nonzero keys (0 when fewer than k are
-// nonzero), built from the most significant bit down: a bit is set when at
-// least k keys reach the candidate.  Keys are distinct, so exactly
-// min(k, #nonzero) keys are >= the result and nonzero.
+// A threshold th such that exactly min(k, #nonzero) of the wave's nonzero
+// keys are >= th (0 when fewer than k are nonzero), built from the most
+// significant bit down: a bit is set when at least k keys reach the
+// candidate.  The score word (high 32 bits) goes first, on 32-bit compares;
+// when exactly k keys reach the k-th largest score word no lower bit can
+// change the selected set, so the search stops there (score ties at the
+// threshold go on through the block-id word).  Keys are distinct, so the
+// full search ends at the k-th largest key itself.
+template <int n>
+__device__ __forceinline__ int wave_count_ge_hi(const uint64_t (&key)[n], uint32_t cand) {
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+        cnt += __popcll(__builtin_amdgcn_ballot_w64((uint32_t)(key[i] >> 32) >= cand));
+    return cnt;
+}
+
 template <int n>
 __device__ __forceinline__ uint64_t wave_kth_key(const uint64_t (&key)[n], int k) {
-    uint64_t th = 0;
-    for (int bit = 63; bit >= 0; --bit) {
+    uint32_t hi = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = hi | (1u << bit);
+        if (wave_count_ge_hi(key, cand) >= k) hi = cand;
+    }
+    if (hi == 0) return 0;  // fewer than k nonzero keys: take them all
+    uint64_t th = (uint64_t)hi << 32;
+    if (wave_count_ge_hi(key, hi) == k) return th;
+    for (int bit = 31; bit >= 0; --bit) {
         const uint64_t cand = th | (1ull << bit);
         int cnt = 0;
 #pragma unroll
