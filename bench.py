@@ -46,51 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (18537.1, 8444.0),
             "bucket scan": (5.4, 12.1),
-            "bucket scatter": (21086.8, 69550.7),
+            "bucket scatter": (21099.4, 69612.9),
             "key summary": (4144.7, 528.0),
-            "routed-block partials": (460239.0, 963838.5),
-            "routing": (29524.9, 28672.0),
+            "routed-block partials": (460115.5, 964036.4),
+            "routing": (29529.4, 28672.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (531058.4, 114688.7),
+            "window + merge": (531012.2, 114689.5),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73834.4, 34808.0),
+            "V transpose + bucket count": (73834.5, 34808.0),
             "bucket scan": (11.4, 48.1),
-            "bucket scatter": (115574.1, 482316.3),
-            "key summary": (16433.6, 2112.0),
-            "routed-block partials": (1918629.3, 3910146.3),
-            "routing": (119071.8, 114688.0),
+            "bucket scatter": (115580.2, 482189.2),
+            "key summary": (16434.0, 2112.0),
+            "routed-block partials": (1918828.2, 3909967.7),
+            "routing": (119055.5, 114688.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (2194508.9, 458756.7),
+            "window + merge": (2195122.5, 458756.6),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "key summary": (131145.9, 49283.3),
+            "key summary": (131145.9, 49284.1),
             "routing": (16811.9, 2048.0),
             "routing fallback": (30.3, 0.0),
-            "window + merge": (212912.2, 262171.0),
+            "window + merge": (211211.8, 262153.0),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "449d6e43a0faefdd", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589932.0, 393151.9),
+            "V transpose + bucket count": (589931.9, 393151.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (954717.0, 6911982.2),
-            "key summary": (131122.7, 16896.0),
-            "routed-block partials": (15569980.0, 31406130.5),
-            "routing": (1430906.4, 917588.1),
-            "routing fallback": (473300.2, 91.0),
-            "window + merge": (20123147.8, 3670073.3),
+            "bucket scatter": (954894.0, 6904157.3),
+            "key summary": (131123.1, 16896.0),
+            "routed-block partials": (15570700.6, 31412779.4),
+            "routing": (1428576.5, 917587.6),
+            "routing fallback": (469631.5, 90.7),
+            "window + merge": (20123747.7, 3670069.5),
         },
     },
 }
