@@ -81,6 +81,14 @@ __host__ __device__ __forceinline__ int eligible_blocks(int t, int bs, int windo
 // row's 8 lanes are consecutive.  Writes the row's hi and lo parts and
 // returns its norms (the same in all 8 lanes).
 constexpr int kChunkMaxStride = 32;  // floats between chunk maxima: one 128-byte line each
+// Each chunk's maximum is stored as kChunkMaxSlots partial maxima (one per
+// workgroup that summarises part of the chunk; unused slots zero), at the
+// start of its line: every slot is written on every call, so no clearing
+// pass and no atomics are needed, and readers take the largest.
+constexpr int kChunkMaxSlots = 8;
+// Words at the start of the routing workspace holding the router's counters
+// (queued rows, queued tiles), cleared before each routing pass.
+constexpr int kRouteCounterWords = 64;
 
 __device__ __forceinline__ void route_split_store(const float (&f)[8], uint16_t* hi_dst,
                                                   uint16_t* lo_dst, float& kn, float& ln) {

@@ -28,26 +28,28 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t s)
 
 // The key summary of a layer that routes on it: also writes the routing
 // kernels' bf16 hi/lo block means [BH][nb_pad][64] and the chunk maxima of
-// their norms (which must have been cleared).
+// their norms (every slot of every chunk line), and clears the router's
+// kRouteCounterWords counters (when counters is not NULL).
 hipError_t launch_summarize_route(const uint16_t* x, float* xbar, int BH, int N, int bs,
                                   uint16_t* khi, uint16_t* klo, float* ckn, float* clo,
-                                  int nb_pad, hipStream_t s);
+                                  int nb_pad, uint32_t* counters, hipStream_t s);
 // The same for blocks of 16 tokens, with the pooling of q [BHq, N, 64] into
 // qbar [BHq, N/16, 64] (fp32) in the same launch (image mode).
 hipError_t launch_summarize_route_pool16(const uint16_t* k, float* kbar, int BHk, const uint16_t* q,
                                          float* qbar, int BHq, int N, uint16_t* khi, uint16_t* klo,
-                                         float* ckn, float* clo, int nb_pad, hipStream_t s);
+                                         float* ckn, float* clo, int nb_pad, uint32_t* counters,
+                                         hipStream_t s);
 
 // Routing workspace (bytes) and launch.  qbar may be NULL in causal mode.
 size_t route_workspace_bytes(const Geometry& g);
 hipError_t launch_route(const Geometry& g, const uint16_t* q, const float* kbar,
                         int32_t* idx, void* ws, hipStream_t s,
                         const hipEvent_t* ev = nullptr);
-// A layer's key summary and the preparation of flat routing in one pass:
-// clears the router's counters and norm maxima, then summarises k into kbar
-// and writes the router's inputs (in image mode the same launch pools q into
-// the routing workspace); launch_route_prepared then routes.  Only for flat
-// routing (beam = 0, beta = 0).
+// A layer's key summary and the preparation of flat routing in one launch:
+// summarises k into kbar, writes the router's inputs and clears its
+// counters (in image mode the same launch pools q into the routing
+// workspace); launch_route_prepared then routes.  Only for flat routing
+// (beam = 0, beta = 0).
 hipError_t launch_summary_and_route_prep(const Geometry& g, const uint16_t* k, const uint16_t* q,
                                          float* kbar, void* ws, hipStream_t s);
 hipError_t launch_route_prepared(const Geometry& g, const uint16_t* q, const float* kbar,

@@ -76,7 +76,8 @@ struct RouteArgs {
     const float* kbar;    // [B,Hkv,nb,64]
     const uint16_t* khi;  // bf16 hi part of kbar [B*Hkv][nb_pad][64]
     const uint16_t* klo;  // bf16 lo part (kbar - hi) [B*Hkv][nb_pad][64]
-    const float* ckn;     // per chunk of RT_CH blocks: max over its blocks of |kbar_c| [B*Hkv][ncb]
+    const float* ckn;     // per chunk of RT_CH blocks: max over its blocks of |kbar_c|, as
+                          // kChunkMaxSlots partial maxima per chunk line [B*Hkv][ncb]
     const float* clo;     // the same for |lo_c| (lo = kbar - hi) [B*Hkv][ncb]
     int32_t* idx;         // [B,Hq,P,top_k] (Hq = routed heads: Hkv with consensus)
     uint32_t* ovf_count;  // queued overflow rows
@@ -289,7 +290,8 @@ __device__ __forceinline__ int tail_node(int t, int bs, int window) {
 // ------------------------------------------------------------ preparation
 // One thread per (block row, 8 dims): bf16 hi/lo split of the block means
 // (rows padded to a multiple of 32 with zeros), and per chunk of 32 rows
-// (one workgroup) the largest norms |kbar_c| and |lo_c| of its valid rows.
+// (one workgroup) the largest norms |kbar_c| and |lo_c| of its valid rows,
+// in slot 0 of the chunk's line (the other slots zeroed).
 __global__ __launch_bounds__(256) void k_route_prep(const float* __restrict__ kbar,
                                                     uint16_t* __restrict__ khi,
                                                     uint16_t* __restrict__ klo,
@@ -320,12 +322,13 @@ __global__ __launch_bounds__(256) void k_route_prep(const float* __restrict__ kb
         s_n[1][w] = ln;
     }
     __syncthreads();
-    if (threadIdx.x == 0 && (int64_t)blockIdx.x * 32 < (int64_t)n_bg * nb_pad) {
+    if (threadIdx.x < kChunkMaxSlots && (int64_t)blockIdx.x * 32 < (int64_t)n_bg * nb_pad) {
         const int64_t chunk = (int64_t)blockIdx.x;  // = bg * (nb_pad / 32) + c / 32
-        ckn[chunk * kChunkMaxStride] =
-            fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3]));
-        clo[chunk * kChunkMaxStride] =
-            fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3]));
+        const bool first = threadIdx.x == 0;
+        ckn[chunk * kChunkMaxStride + threadIdx.x] =
+            first ? fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3])) : 0.f;
+        clo[chunk * kChunkMaxStride + threadIdx.x] =
+            first ? fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3])) : 0.f;
     }
 }
 
@@ -464,11 +467,19 @@ void k_route(RouteArgs a) {
     if constexpr (!EXACT) {
         const int nc = (Emax + RT_CH - 1) / RT_CH;
         for (int i = lane; i < nc; i += 64) {
+            // the chunk's partial maxima (kChunkMaxSlots = 8 of them)
             const int64_t e = ((int64_t)bg * a.ncb + i) * kChunkMaxStride;
-            const uint32_t kb = __float_as_uint(a.ckn[e]);
-            const uint32_t lb = __float_as_uint(a.clo[e]);
-            kn_bits = kb > kn_bits ? kb : kn_bits;
-            lo_bits = lb > lo_bits ? lb : lo_bits;
+            static_assert(kChunkMaxSlots == 8, "two 16-byte loads per chunk line");
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 kb = *reinterpret_cast<const u32x4*>(a.ckn + e + 4 * h);
+                const u32x4 lb = *reinterpret_cast<const u32x4*>(a.clo + e + 4 * h);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kn_bits = kb[j] > kn_bits ? kb[j] : kn_bits;
+                    lo_bits = lb[j] > lo_bits ? lb[j] : lo_bits;
+                }
+            }
         }
     }
 
@@ -1279,7 +1290,6 @@ static size_t route_items(const Geometry& g) {
 // the block-mean norms; one fill covers them.
 struct RouteLayout {
     size_t cmax, ovf_rows, tiles, qbar, qsum, khi, klo, total;
-    size_t fill_words;  // words cleared from the start of the workspace
     int nb_pad, ncb;
 };
 
@@ -1288,9 +1298,8 @@ static RouteLayout route_layout(const Geometry& g) {
     L.nb_pad = (g.nb + RT_CH - 1) / RT_CH * RT_CH;
     L.ncb = L.nb_pad / RT_CH;
     const size_t nbg = (size_t)g.B * g.Hkv;
-    size_t off = 256;  // overflow counters
+    size_t off = kRouteCounterWords * 4;  // counters (queued rows, queued tiles)
     L.cmax = off;     off += align_up(2 * nbg * L.ncb * kChunkMaxStride * 4, 256);  // norms, then lo
-    L.fill_words = off / 4;
     L.ovf_rows = off; off += align_up(route_rows(g) * 4, 256);
     L.tiles = off;    off += align_up(route_items(g) * 4, 256);
     L.qbar = off;     if (!g.causal) off += align_up((size_t)g.B * g.Hq * route_P(g) * kD * 4, 256);
@@ -1427,7 +1436,7 @@ static hipError_t route_flat(const Geometry& g, const uint16_t* q, const float* 
     a.tail_img = tail_img;
     hipError_t e = hipSuccess;
     if (!prepared) {  // the counters (prepared: cleared by the caller, with the norm maxima)
-        e = launch_fill_u32(a.ovf_count, 64, 0u, s);
+        e = launch_fill_u32(a.ovf_count, kRouteCounterWords, 0u, s);
         if (e != hipSuccess) return e;
     }
     if (!g.causal && !qbar_in) {
@@ -1515,16 +1524,17 @@ hipError_t launch_summary_and_route_prep(const Geometry& g, const uint16_t* k, c
     char* base = static_cast<char*>(ws);
     const size_t nbg = (size_t)g.B * g.Hkv;
     float* ckn = reinterpret_cast<float*>(base + L.cmax);
-    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(base), L.fill_words, 0u, s);
-    if (e != hipSuccess) return e;
+    // the summary writes every chunk line and clears the counters itself
+    uint32_t* counters = reinterpret_cast<uint32_t*>(base);
     uint16_t* khi = reinterpret_cast<uint16_t*>(base + L.khi);
     uint16_t* klo = reinterpret_cast<uint16_t*>(base + L.klo);
     float* clo = ckn + nbg * L.ncb * kChunkMaxStride;
     if (!g.causal)  // image mode: the query pooling joins the same launch
         return launch_summarize_route_pool16(k, kbar, g.B * g.Hkv, q,
                                              reinterpret_cast<float*>(base + L.qbar), g.B * g.Hq,
-                                             g.N, khi, klo, ckn, clo, L.nb_pad, s);
-    return launch_summarize_route(k, kbar, g.B * g.Hkv, g.N, g.bs, khi, klo, ckn, clo, L.nb_pad, s);
+                                             g.N, khi, klo, ckn, clo, L.nb_pad, counters, s);
+    return launch_summarize_route(k, kbar, g.B * g.Hkv, g.N, g.bs, khi, klo, ckn, clo, L.nb_pad,
+                                  counters, s);
 }
 
 hipError_t launch_route_prepared(const Geometry& g, const uint16_t* q, const float* kbar,

@@ -16,15 +16,32 @@ namespace lsa {
 // With RouteOut (the layer's key summary feeding its own routing), the
 // summary kernels also write the routing kernels' inputs: the bf16 hi/lo
 // split of each block mean into rows of nb_pad per head (rows past nb
-// zero), and per chunk of 32 rows the largest norms |mean| and |lo| of its
-// rows (route_split_store).
+// zero), per chunk of 32 rows the largest norms |mean| and |lo| of its
+// rows (route_split_store; kChunkMaxSlots partial maxima per chunk), and
+// zeros into the router's counters.
 struct RouteOut {
     uint16_t* khi;
     uint16_t* klo;
     float* ckn;    // chunk maxima, kChunkMaxStride floats apart
     float* clo;
     int nb_pad;
+    uint32_t* counters;  // kRouteCounterWords words cleared by workgroup 0 (or NULL)
 };
+
+// Stores a workgroup's partial chunk maxima into `slot` of its chunk line
+// (threads 0 .. kChunkMaxSlots - 1 of the workgroup; with fill, the other
+// slots of the line are zeroed, for a workgroup that covers the whole
+// chunk) and clears the router's counters from workgroup 0.
+__device__ __forceinline__ void store_chunk_max(const RouteOut& ro, int64_t chunk, int slot,
+                                                bool fill, float kmax, float lmax, int64_t wg) {
+    const int t = threadIdx.x;
+    if (t < kChunkMaxSlots && (fill || t == slot)) {
+        const int64_t e = chunk * kChunkMaxStride + t;
+        ro.ckn[e] = t == slot ? kmax : 0.f;
+        ro.clo[e] = t == slot ? lmax : 0.f;
+    }
+    if (ro.counters && wg == 0 && t < kRouteCounterWords) ro.counters[t] = 0u;
+}
 
 // Blocks of 16 tokens: a lane owns 8 dims of one block and sums its 16 rows
 // itself (eight blocks per wave), so no cross-lane reduction is needed; a
@@ -93,15 +110,11 @@ __device__ __forceinline__ void summarize16(const uint16_t* __restrict__ x, floa
         s_n[1][w] = ln;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const int64_t r0 = wg * 32;  // this workgroup's chunk
-        if ((r0 / ro.nb_pad) * nb < n_blocks) {
-            ro.ckn[wg * (int64_t)kChunkMaxStride] =
-                fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3]));
-            ro.clo[wg * (int64_t)kChunkMaxStride] =
-                fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3]));
-        }
-    }
+    const int64_t r0 = wg * 32;  // this workgroup's rows: one chunk
+    if ((r0 / ro.nb_pad) * nb < n_blocks)
+        store_chunk_max(ro, wg, 0, true,
+                        fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3])),
+                        fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3])), wg);
 }
 
 template <bool PREP>
@@ -128,8 +141,8 @@ __global__ __launch_bounds__(256) void k_summarize16_kq(const uint16_t* __restri
 }
 
 // One wave per block.  With PREP, waves run over heads x nb_pad; a
-// workgroup (four rows of one chunk) folds its norms into the chunk's
-// maxima with one atomic maximum each (the maxima start at zero).
+// workgroup (four rows of one chunk) stores its norms' maxima into its own
+// slot of the chunk's line (eight workgroups per chunk).
 template <int BS, bool PREP>
 __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ x,
                                                    float* __restrict__ xbar,
@@ -198,18 +211,13 @@ __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ 
         s_n[1][w] = ln;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const int64_t r0 = (int64_t)blockIdx.x * 4;  // this workgroup's rows: one chunk
-        if ((r0 / ro.nb_pad) * nb < n_blocks) {
-            const int64_t e = (r0 / 32) * kChunkMaxStride;
-            atomicMax(reinterpret_cast<uint32_t*>(ro.ckn + e),
-                      __float_as_uint(fmaxf(fmaxf(s_n[0][0], s_n[0][1]),
-                                            fmaxf(s_n[0][2], s_n[0][3]))));
-            atomicMax(reinterpret_cast<uint32_t*>(ro.clo + e),
-                      __float_as_uint(fmaxf(fmaxf(s_n[1][0], s_n[1][1]),
-                                            fmaxf(s_n[1][2], s_n[1][3]))));
-        }
-    }
+    const int64_t r0 = (int64_t)blockIdx.x * 4;  // this workgroup's rows, in one chunk
+    static_assert(32 / 4 == kChunkMaxSlots, "a chunk spans one slot per workgroup");
+    if ((r0 / ro.nb_pad) * nb < n_blocks)
+        store_chunk_max(ro, r0 / 32, (int)(blockIdx.x % kChunkMaxSlots), false,
+                        fmaxf(fmaxf(s_n[0][0], s_n[0][1]), fmaxf(s_n[0][2], s_n[0][3])),
+                        fmaxf(fmaxf(s_n[1][0], s_n[1][1]), fmaxf(s_n[1][2], s_n[1][3])),
+                        blockIdx.x);
 }
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t value) {
@@ -244,19 +252,20 @@ hipError_t launch_summarize(const uint16_t* x, float* xbar, int BH, int N, int b
 
 hipError_t launch_summarize_route(const uint16_t* x, float* xbar, int BH, int N, int bs,
                                   uint16_t* khi, uint16_t* klo, float* ckn, float* clo,
-                                  int nb_pad, hipStream_t s) {
-    return summarize<true>(x, xbar, BH, N, bs, RouteOut{khi, klo, ckn, clo, nb_pad}, s);
+                                  int nb_pad, uint32_t* counters, hipStream_t s) {
+    return summarize<true>(x, xbar, BH, N, bs, RouteOut{khi, klo, ckn, clo, nb_pad, counters}, s);
 }
 
 hipError_t launch_summarize_route_pool16(const uint16_t* k, float* kbar, int BHk, const uint16_t* q,
                                          float* qbar, int BHq, int N, uint16_t* khi, uint16_t* klo,
-                                         float* ckn, float* clo, int nb_pad, hipStream_t s) {
+                                         float* ckn, float* clo, int nb_pad, uint32_t* counters,
+                                         hipStream_t s) {
     const int nb = N / 16;
     const int64_t nk = (int64_t)BHk * nb, nq = (int64_t)BHq * nb;
     const int64_t wg_k = ((int64_t)BHk * nb_pad + 31) / 32;  // rows over heads x nb_pad
     const int64_t wg_q = (nq + 31) / 32;
     hipLaunchKernelGGL(k_summarize16_kq, dim3((unsigned)(wg_k + wg_q)), dim3(256), 0, s, k, kbar,
-                       nk, RouteOut{khi, klo, ckn, clo, nb_pad}, wg_k, q, qbar, nq, nb);
+                       nk, RouteOut{khi, klo, ckn, clo, nb_pad, counters}, wg_k, q, qbar, nq, nb);
     return hipGetLastError();
 }
 
