@@ -54,12 +54,16 @@ constexpr float RESCALE_SLACK = 8.f;  // log2 headroom before a running max is r
 // ------------------------------------------------------------ V transpose
 // V [BG][N][64] -> V^T tiles [BG][ceil(N/TW)][64 d][TW keys]; keys >= N are
 // zero.  The causal kernels take TW = 64 (image mode reads V rows itself and
-// transposes them on their way out of LDS).
+// transposes them on their way out of LDS).  The same launch clears the
+// bucket counts (nzero words at zero) for the bucketing that follows.
 template <int TW>
 __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict__ v,
-                                                     uint16_t* __restrict__ vt, int N, int ntiles) {
+                                                     uint16_t* __restrict__ vt, int N, int ntiles,
+                                                     uint32_t* __restrict__ zero, size_t nzero) {
     __shared__ uint32_t s[VT_TILE][33];  // [key][d pair], odd pitch
     const int tid = threadIdx.x;
+    for (size_t i = (size_t)blockIdx.x * 256 + tid; i < nzero; i += (size_t)gridDim.x * 256)
+        zero[i] = 0u;
     const int bg = blockIdx.x / ntiles, tile = blockIdx.x - bg * ntiles;
     const int key0 = tile * VT_TILE;
     const int nvalid = min(VT_TILE, N - key0);
@@ -863,9 +867,10 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
         mark(ev, 8, s);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_transpose_v<VT_TILE>, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s, v,
-                       vt, g.N, ntiles);
     uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
+    // the transpose also clears the bucket counts
+    hipLaunchKernelGGL(k_transpose_v<VT_TILE>, dim3((unsigned)(nbg * ntiles)), dim3(256), 0, s, v,
+                       vt, g.N, ntiles, counts, (size_t)L.NB);
     uint32_t* offsets = reinterpret_cast<uint32_t*>(base + L.offsets);
     uint32_t* cursor = reinterpret_cast<uint32_t*>(base + L.cursor);
     uint32_t* unit_off = reinterpret_cast<uint32_t*>(base + L.unit_off);
@@ -877,8 +882,6 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     const int NB = (int)L.NB;
     const int sp_log2 = pair_stride_log2(g.top_k);
 
-    hipError_t e = launch_fill_u32(counts, (size_t)NB, 0u, s);
-    if (e != hipSuccess) return e;
     // one route per KV group: bucket (group row, slot) pairs, each gathered
     // once per query head of the group
     const int rep = g.Hq / g.Hkv;
