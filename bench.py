@@ -46,51 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18537.1, 8444.0),
-            "bucket scan": (5.4, 12.1),
-            "bucket scatter": (21099.4, 69612.9),
-            "key summary": (4144.7, 528.0),
-            "routed-block partials": (460115.5, 964036.4),
-            "routing": (29529.4, 28672.0),
+            "V transpose + bucket count": (18536.6, 8448.0),
+            "bucket scan": (5.6, 12.1),
+            "bucket scatter": (21088.4, 69605.2),
+            "key summary": (4145.2, 528.2),
+            "routed-block partials": (460016.7, 964052.4),
+            "routing": (29531.5, 28672.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (531012.2, 114689.5),
+            "window + merge": (531044.6, 114688.9),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73834.5, 34808.0),
-            "bucket scan": (11.4, 48.1),
-            "bucket scatter": (115580.2, 482189.2),
-            "key summary": (16434.0, 2112.0),
-            "routed-block partials": (1918828.2, 3909967.7),
-            "routing": (119055.5, 114688.0),
+            "V transpose + bucket count": (73833.9, 34824.0),
+            "bucket scan": (11.6, 48.1),
+            "bucket scatter": (115562.9, 482643.1),
+            "key summary": (16433.9, 2112.2),
+            "routed-block partials": (1919014.0, 3910359.3),
+            "routing": (119057.0, 114688.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (2195122.5, 458756.6),
+            "window + merge": (2195231.3, 458757.5),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "key summary": (131145.9, 49284.1),
-            "routing": (16811.9, 2048.0),
-            "routing fallback": (30.3, 0.0),
-            "window + merge": (211211.8, 262153.0),
+            "key summary": (131155.4, 49281.1),
+            "routing": (16818.5, 2048.0),
+            "routing fallback": (29.8, 0.0),
+            "window + merge": (212845.0, 262165.8),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "ddd6b48f6a0f7b0b", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589931.9, 393151.9),
+            "V transpose + bucket count": (589931.3, 393279.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (954894.0, 6904157.3),
-            "key summary": (131123.1, 16896.0),
-            "routed-block partials": (15570700.6, 31412779.4),
-            "routing": (1428576.5, 917587.6),
-            "routing fallback": (469631.5, 90.7),
-            "window + merge": (20123747.7, 3670069.5),
+            "bucket scatter": (955256.0, 6896710.1),
+            "key summary": (131123.2, 16896.3),
+            "routed-block partials": (15571000.9, 31404307.1),
+            "routing": (1432380.6, 917587.8),
+            "routing fallback": (470705.3, 90.3),
+            "window + merge": (20122869.1, 3670065.1),
         },
     },
 }
