@@ -119,6 +119,12 @@ __device__ __forceinline__ void write_rev_row(uint32_t* rev, int64_t rows, int64
         if (s < top_k) rev[s * rows + row] = pos[s];
 }
 
+// Threads per bucketing workgroup: a launch has only a few workgroups per CU
+// (one per few thousand rows), so each brings many waves; the longer row
+// lists (wide or runtime-length rows) hold more registers and take fewer.
+template <int KV, int KM>
+constexpr int bucket_threads() { return (KM > kMaxTopK || KV == 0) ? 512 : 1024; }
+
 // Workgroup = (batch, KV head, chunk of tchunk positions) over all query
 // heads of the group.  Histogram in LDS (when nb fits), then one global
 // atomic per touched bucket: counts (SCATTER = false) or a reserved range
@@ -127,7 +133,8 @@ __device__ __forceinline__ void write_rev_row(uint32_t* rev, int64_t rows, int64
 // (top_k = 4 * KV), else 0.  KM: the row list length held per row
 // (kMaxTopK, or kMaxTopKWide for top_k above it).
 template <bool SCATTER, int KV, int KM>
-__global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
+__global__ __launch_bounds__((bucket_threads<KV, KM>())) void k_bucket(BucketArgs a) {
+    constexpr int BT = bucket_threads<KV, KM>();
     extern __shared__ uint32_t s_h[];
     const int tid = threadIdx.x;
     const int nch = (a.N + a.tchunk - 1) / a.tchunk;
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     const int total = nh * span;
     if (!lds) {
         // block counts beyond the LDS histogram: global atomics per pair
-        for (int i = tid; i < total; i += 256) {
+        for (int i = tid; i < total; i += BT) {
             const int hh = i / span, t = t0 + (i - hh * span);
             const int64_t row = row_of(hh, t);
             const int64_t irow = a.group_route ? (int64_t)bg * a.N + t : row;
@@ -189,21 +196,21 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     auto load_rows = [&](int i0, Rows& r) {
 #pragma unroll
         for (int u = 0; u < BU; ++u) {
-            const int i = min(i0 + 256 * u, total - 1);
+            const int i = min(i0 + BT * u, total - 1);
             r.hh[u] = i / span;
             r.t[u] = t0 + (i - r.hh[u] * span);
             const int64_t irow = a.group_route ? (int64_t)bg * a.N + r.t[u] : row_of(r.hh[u], r.t[u]);
             load_idx_row_kv<KV, KM>(a.idx + irow * a.top_k, a.top_k, r.c[u]);
         }
     };
-    for (int c = tid; c < a.nb; c += 256) s_h[c] = 0;
+    for (int c = tid; c < a.nb; c += BT) s_h[c] = 0;
     __syncthreads();
-    for (int i0 = tid; i0 < total; i0 += 256 * BU) {
+    for (int i0 = tid; i0 < total; i0 += BT * BU) {
         Rows r;
         load_rows(i0, r);
 #pragma unroll
         for (int u = 0; u < BU; ++u) {
-            const uint32_t m = (i0 + 256 * u < total)
+            const uint32_t m = (i0 + BT * u < total)
                                    ? used_mask<KM>(r.c[u], a.top_k, bucket_candidates(a, r.t[u]))
                                    : 0u;
 #pragma unroll
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
         }
     }
     __syncthreads();
-    for (int cc = tid; cc < a.nb; cc += 256) {
+    for (int cc = tid; cc < a.nb; cc += BT) {
         const uint32_t n = s_h[cc];
         if (!SCATTER) {
             if (n) atomicAdd(&a.counts[bucket0 + cc], n);
@@ -222,12 +229,12 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     }
     if (!SCATTER) return;
     __syncthreads();
-    for (int i0 = tid; i0 < total; i0 += 256 * BU) {
+    for (int i0 = tid; i0 < total; i0 += BT * BU) {
         Rows r;
         load_rows(i0, r);
 #pragma unroll
         for (int u = 0; u < BU; ++u) {
-            if (i0 + 256 * u >= total) break;
+            if (i0 + BT * u >= total) break;
             const uint32_t m = used_mask<KM>(r.c[u], a.top_k, bucket_candidates(a, r.t[u]));
             const int64_t row = row_of(r.hh[u], r.t[u]);
             // all LDS reservations first (their latencies overlap), then the stores
@@ -244,24 +251,29 @@ __global__ __launch_bounds__(256) void k_bucket(BucketArgs a) {
     }
 }
 
+template <bool SCATTER, int KV, int KM>
+static inline void launch_bucket_kv(dim3 grid, size_t lds, hipStream_t s, const BucketArgs& a) {
+    hipLaunchKernelGGL((k_bucket<SCATTER, KV, KM>), grid, dim3(bucket_threads<KV, KM>()), lds, s, a);
+}
+
 // Launches k_bucket<SCATTER, KV, KM> with KV and KM picked from a.top_k.
 template <bool SCATTER>
 static inline void launch_bucket(dim3 grid, size_t lds, hipStream_t s, const BucketArgs& a) {
-    constexpr int W = kMaxTopKWide;
+    constexpr int K = kMaxTopK, W = kMaxTopKWide;
     switch ((a.top_k & 3) == 0 ? a.top_k / 4 : 0) {
-        case 1: hipLaunchKernelGGL((k_bucket<SCATTER, 1, kMaxTopK>), grid, dim3(256), lds, s, a); break;
-        case 2: hipLaunchKernelGGL((k_bucket<SCATTER, 2, kMaxTopK>), grid, dim3(256), lds, s, a); break;
-        case 3: hipLaunchKernelGGL((k_bucket<SCATTER, 3, kMaxTopK>), grid, dim3(256), lds, s, a); break;
-        case 4: hipLaunchKernelGGL((k_bucket<SCATTER, 4, kMaxTopK>), grid, dim3(256), lds, s, a); break;
-        case 5: hipLaunchKernelGGL((k_bucket<SCATTER, 5, W>), grid, dim3(256), lds, s, a); break;
-        case 6: hipLaunchKernelGGL((k_bucket<SCATTER, 6, W>), grid, dim3(256), lds, s, a); break;
-        case 7: hipLaunchKernelGGL((k_bucket<SCATTER, 7, W>), grid, dim3(256), lds, s, a); break;
-        case 8: hipLaunchKernelGGL((k_bucket<SCATTER, 8, W>), grid, dim3(256), lds, s, a); break;
+        case 1: launch_bucket_kv<SCATTER, 1, K>(grid, lds, s, a); break;
+        case 2: launch_bucket_kv<SCATTER, 2, K>(grid, lds, s, a); break;
+        case 3: launch_bucket_kv<SCATTER, 3, K>(grid, lds, s, a); break;
+        case 4: launch_bucket_kv<SCATTER, 4, K>(grid, lds, s, a); break;
+        case 5: launch_bucket_kv<SCATTER, 5, W>(grid, lds, s, a); break;
+        case 6: launch_bucket_kv<SCATTER, 6, W>(grid, lds, s, a); break;
+        case 7: launch_bucket_kv<SCATTER, 7, W>(grid, lds, s, a); break;
+        case 8: launch_bucket_kv<SCATTER, 8, W>(grid, lds, s, a); break;
         default:
-            if (a.top_k <= kMaxTopK)
-                hipLaunchKernelGGL((k_bucket<SCATTER, 0, kMaxTopK>), grid, dim3(256), lds, s, a);
+            if (a.top_k <= K)
+                launch_bucket_kv<SCATTER, 0, K>(grid, lds, s, a);
             else
-                hipLaunchKernelGGL((k_bucket<SCATTER, 0, W>), grid, dim3(256), lds, s, a);
+                launch_bucket_kv<SCATTER, 0, W>(grid, lds, s, a);
             break;
     }
 }
