@@ -46,51 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18536.6, 8448.0),
+            "V transpose + bucket count": (18534.6, 8448.0),
             "bucket scan": (5.6, 12.1),
-            "bucket scatter": (21088.4, 69605.2),
-            "key summary": (4145.2, 528.2),
-            "routed-block partials": (460016.7, 964052.4),
-            "routing": (29531.5, 28672.0),
+            "bucket scatter": (15705.7, 71824.6),
+            "key summary": (4145.3, 528.2),
+            "routed-block partials": (459403.0, 964096.4),
+            "routing": (29536.2, 28672.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (531044.6, 114688.9),
+            "window + merge": (530917.2, 114689.4),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73833.9, 34824.0),
+            "V transpose + bucket count": (73832.5, 34824.0),
             "bucket scan": (11.6, 48.1),
-            "bucket scatter": (115562.9, 482643.1),
-            "key summary": (16433.9, 2112.2),
-            "routed-block partials": (1919014.0, 3910359.3),
+            "bucket scatter": (119591.2, 535318.0),
+            "key summary": (16434.1, 2112.2),
+            "routed-block partials": (1919158.7, 3909933.3),
             "routing": (119057.0, 114688.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (2195231.3, 458757.5),
+            "window + merge": (2193531.6, 458757.0),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "key summary": (131155.4, 49281.1),
+            "key summary": (131155.4, 49281.4),
             "routing": (16818.5, 2048.0),
             "routing fallback": (29.8, 0.0),
-            "window + merge": (212845.0, 262165.8),
+            "window + merge": (212742.9, 262164.9),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "54c7a28587a62435", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589931.3, 393279.9),
+            "V transpose + bucket count": (589929.9, 393279.9),
             "bucket scan": (67.6, 384.1),
-            "bucket scatter": (955256.0, 6896710.1),
-            "key summary": (131123.2, 16896.3),
-            "routed-block partials": (15571000.9, 31404307.1),
-            "routing": (1432380.6, 917587.8),
-            "routing fallback": (470705.3, 90.3),
-            "window + merge": (20122869.1, 3670065.1),
+            "bucket scatter": (989407.4, 7007152.4),
+            "key summary": (131123.3, 16896.3),
+            "routed-block partials": (15574676.3, 31421517.6),
+            "routing": (1430101.5, 917589.7),
+            "routing fallback": (482025.1, 91.5),
+            "window + merge": (20104529.4, 3670081.1),
         },
     },
 }
