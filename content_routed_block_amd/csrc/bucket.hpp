@@ -101,6 +101,9 @@ struct BucketArgs {
     int nbg = 0;         // B * Hkv (with position chunks)
     int fixed_cand = 0;  // > 0: every row's candidate buckets (image-mode rows); else causal
     int group_pairs = 0;
+    // with position chunks: buckets are (t >> bc_log2, b * Hkv + g, block),
+    // bucket chunks no longer than the chunks (-1: bc_log2 = pc_log2)
+    int bc_log2 = -1;
 };
 
 __device__ __forceinline__ int bucket_candidates(const BucketArgs& a, int t) {
@@ -145,8 +148,9 @@ __global__ __launch_bounds__((bucket_threads<KV, KM>())) void k_bucket(BucketArg
     const int span = t1 - t0;
     const bool lds = a.nb <= BK_LDS_MAX;
     const bool chunked = a.pc_log2 >= 0;
+    const int bc_log2 = a.bc_log2 >= 0 ? a.bc_log2 : a.pc_log2;
     const int64_t bucket0 =
-        chunked ? ((int64_t)(t0 >> a.pc_log2) * a.nbg + bg) * a.nb : (int64_t)bg * a.nb;
+        chunked ? ((int64_t)(t0 >> bc_log2) * a.nbg + bg) * a.nb : (int64_t)bg * a.nb;
     // heads walked per position: the group's query heads, or one group row
     const int nh = a.group_pairs ? 1 : rep;
     // row (of rev) and idx row of head hh at position t
@@ -288,14 +292,27 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
                                                       int expand) {
     __shared__ uint32_t s_p[1024], s_u[1024];
     const int tid = threadIdx.x;
-    const int per = (NB + 1023) / 1024;
+    // each thread scans a run of `per` buckets (a multiple of four, so the
+    // run starts 16-byte aligned and moves in 16-byte loads and stores;
+    // entries past NB read as zero)
+    const int per = ((NB + 1023) / 1024 + 3) & ~3;
     const int lo = min(NB, tid * per), hi = min(NB, lo + per);
+    auto load4 = [&](int i) {
+        if (i + 4 <= NB) return *reinterpret_cast<const u32x4*>(counts + i);
+        u32x4 r = {0u, 0u, 0u, 0u};
+        for (int j = 0; j < 4; ++j)
+            if (i + j < NB) r[j] = counts[i + j];
+        return r;
+    };
     uint32_t sp = 0, su = 0;
-#pragma unroll 8
-    for (int i = lo; i < hi; ++i) {
-        const uint32_t n = counts[i];
-        sp += n;
-        su += (n * expand + UNIT_ROWS - 1) / UNIT_ROWS;
+#pragma unroll 4
+    for (int i = lo; i < hi; i += 4) {
+        const u32x4 n = load4(i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sp += n[j];
+            su += (n[j] * expand + UNIT_ROWS - 1) / UNIT_ROWS;
+        }
     }
     s_p[tid] = sp;
     s_u[tid] = su;
@@ -309,14 +326,28 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
         __syncthreads();
     }
     uint32_t rp = s_p[tid] - sp, ru = s_u[tid] - su;
-#pragma unroll 8
-    for (int i = lo; i < hi; ++i) {
-        const uint32_t n = counts[i];
-        offsets[i] = rp;
-        cursor[i] = rp;
-        unit_off[i] = ru;
-        rp += n;
-        ru += (n * expand + UNIT_ROWS - 1) / UNIT_ROWS;
+#pragma unroll 4
+    for (int i = lo; i < hi; i += 4) {
+        const u32x4 n = load4(i);
+        u32x4 o, u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[j] = rp;
+            u[j] = ru;
+            rp += n[j];
+            ru += (n[j] * expand + UNIT_ROWS - 1) / UNIT_ROWS;
+        }
+        if (i + 4 <= NB) {
+            *reinterpret_cast<u32x4*>(offsets + i) = o;
+            *reinterpret_cast<u32x4*>(cursor + i) = o;
+            *reinterpret_cast<u32x4*>(unit_off + i) = u;
+        } else {
+            for (int j = 0; j < 4 && i + j < NB; ++j) {
+                offsets[i + j] = o[j];
+                cursor[i + j] = o[j];
+                unit_off[i + j] = u[j];
+            }
+        }
     }
     if (tid == 1023) {
         offsets[NB] = s_p[1023];

@@ -126,7 +126,9 @@ def test_wide_top_k_is_accepted(lsa):
         p = good(lsa, top_k=k)
         att = lsa.workspace_bytes(p, lsa.OP_ATTEND)
         want = pairs * k * 8 + pairs * 32 * 64 * 2 + pairs * k * 4 + vt
-        assert want <= att < want + (1 << 20)
+        # plus the bucket tables: four words per (bucket chunk, KV head, key
+        # block), up to 16 bucket chunks of 8192 positions at k = 32
+        assert want <= att < want + (2 << 20)
         assert lsa.idx_shape(p) == (1, 14, 131072, k)
         assert lsa.workspace_bytes(p, lsa.OP_FORWARD) < lsa.SIZE_MAX
         d16 = lsa.workspace_bytes(good(lsa), lsa.OP_DECODE)
