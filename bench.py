@@ -46,51 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18534.6, 8448.0),
-            "bucket scan": (5.6, 12.1),
-            "bucket scatter": (15705.7, 71824.6),
-            "key summary": (4145.3, 528.2),
-            "routed-block partials": (459403.0, 964096.4),
-            "routing": (29536.2, 28672.0),
+            "V transpose + bucket count": (18537.1, 8476.0),
+            "bucket scan": (20.7, 96.1),
+            "bucket scatter": (15715.8, 72382.8),
+            "key summary": (4144.6, 528.2),
+            "routed-block partials": (521620.0, 941412.2),
+            "routing": (29527.2, 28672.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (530917.2, 114689.4),
+            "window + merge": (530584.7, 114688.9),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73832.5, 34824.0),
-            "bucket scan": (11.6, 48.1),
-            "bucket scatter": (119591.2, 535318.0),
-            "key summary": (16434.1, 2112.2),
-            "routed-block partials": (1919158.7, 3909933.3),
-            "routing": (119057.0, 114688.0),
+            "V transpose + bucket count": (73834.4, 34936.0),
+            "bucket scan": (70.4, 384.1),
+            "bucket scatter": (120099.3, 534100.5),
+            "key summary": (16433.1, 2112.2),
+            "routed-block partials": (2064431.9, 3881520.4),
+            "routing": (119056.3, 114688.0),
             "routing fallback": (37.5, 0.0),
-            "window + merge": (2193531.6, 458757.0),
+            "window + merge": (2192004.3, 458756.7),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "key summary": (131155.4, 49281.4),
-            "routing": (16818.5, 2048.0),
-            "routing fallback": (29.8, 0.0),
-            "window + merge": (212742.9, 262164.9),
+            "key summary": (131153.9, 49281.3),
+            "routing": (16818.0, 2048.0),
+            "routing fallback": (29.7, 0.0),
+            "window + merge": (212771.1, 262164.9),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "9a8f7511f76cdca3", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (589929.9, 393279.9),
-            "bucket scan": (67.6, 384.1),
-            "bucket scatter": (989407.4, 7007152.4),
-            "key summary": (131123.3, 16896.3),
-            "routed-block partials": (15574676.3, 31421517.6),
-            "routing": (1430101.5, 917589.7),
-            "routing fallback": (482025.1, 91.5),
-            "window + merge": (20104529.4, 3670081.1),
+            "V transpose + bucket count": (589931.2, 393279.9),
+            "bucket scan": (70.4, 384.1),
+            "bucket scatter": (988634.7, 7025094.8),
+            "key summary": (131121.8, 16896.2),
+            "routed-block partials": (15616758.7, 31247389.4),
+            "routing": (1430016.7, 917588.2),
+            "routing fallback": (471112.7, 91.1),
+            "window + merge": (20099771.1, 3670071.5),
         },
     },
 }
