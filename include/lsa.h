@@ -192,8 +192,10 @@ lsa_status lsa_route_cumulant(const lsa_params *p, const void *q, const void *k,
  * 32 GiB; chunks cost time, as each splits every key block's rows).  The
  * output does not depend on the chunk size; the workspace holds one chunk's
  * partials (B * Hq * chunk * 2^ceil(log2 top_k) rows of 128 bytes, plus
- * 4 bytes per routed pair of the chunk) and 8 bytes per routed pair of the
- * whole layer. */
+ * 4 bytes per routed pair of the chunk), 8 bytes per routed pair of the
+ * whole layer, and 16 bytes per bucket: a bucket is a key block of one
+ * (b, KV head) for one span of query positions, spans short enough for
+ * their query rows to stay cached while the blocks that chose them run. */
 lsa_status lsa_sparse_attend(const lsa_params *p, const void *q, const void *k,
                              const void *v, const int32_t *idx, float *out,
                              void *workspace, size_t workspace_bytes, void *stream);
