@@ -425,11 +425,12 @@ void k_route(RouteArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int half = lane >> 5, l32 = lane & 31;
-    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
-    // item = xcd * (grid / 8) + blockIdx / 8 keeps consecutive items, i.e.
-    // the tiles of one head and the heads of one KV group, on one XCD (whose
-    // L2 then holds that group's candidate blocks).  Tiles of a head run
-    // heavy (late positions, most candidates) first.
+    // Items in workgroup order: workgroups are dealt round-robin to the 8
+    // XCDs, so each XCD takes every 8th tile of every head, the same mix of
+    // heavy and light tiles (a contiguous range per XCD left the busiest
+    // XCD ~10% more candidates than the mean), and at any time all XCDs
+    // work on the same heads, whose KV group's block means their L2s hold.
+    // Tiles of a head run heavy (late positions, most candidates) first.
     int item;
     if constexpr (EXACT) {
         // the queued tiles, when more rows overflowed than the per-row pass takes
@@ -437,8 +438,7 @@ void k_route(RouteArgs a) {
         if (blockIdx.x >= __builtin_amdgcn_readfirstlane(*a.tile_count)) return;
         item = (int)__builtin_amdgcn_readfirstlane(a.tile_queue[blockIdx.x]);
     } else {
-        const int per_xcd = gridDim.x / 8;
-        item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+        item = blockIdx.x;
         if (item >= a.items) return;
     }
     __shared__ uint32_t s_ovf;  // some row of the workgroup overflowed
