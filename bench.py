@@ -46,51 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (18537.1, 8476.0),
             "bucket scan": (20.7, 96.1),
-            "bucket scatter": (15715.8, 72382.8),
+            "bucket scatter": (15620.6, 72892.8),
             "key summary": (4144.6, 528.2),
-            "routed-block partials": (521620.0, 941412.2),
-            "routing": (29527.2, 28672.0),
-            "routing fallback": (37.5, 0.0),
-            "window + merge": (530584.7, 114688.9),
+            "routed-block partials": (521425.1, 941382.5),
+            "routing": (29898.5, 28672.0),
+            "routing fallback": (18.0, 0.0),
+            "window + merge": (530623.5, 114688.8),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (73834.4, 34936.0),
+            "V transpose + bucket count": (73833.9, 34936.0),
             "bucket scan": (70.4, 384.1),
-            "bucket scatter": (120099.3, 534100.5),
-            "key summary": (16433.1, 2112.2),
-            "routed-block partials": (2064431.9, 3881520.4),
-            "routing": (119056.3, 114688.0),
-            "routing fallback": (37.5, 0.0),
-            "window + merge": (2192004.3, 458756.7),
+            "bucket scatter": (119819.3, 532607.7),
+            "key summary": (16433.2, 2112.2),
+            "routed-block partials": (2064382.4, 3881468.0),
+            "routing": (119187.1, 114688.0),
+            "routing fallback": (18.0, 0.0),
+            "window + merge": (2192306.4, 458758.1),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "key summary": (131153.9, 49281.3),
-            "routing": (16818.0, 2048.0),
-            "routing fallback": (29.7, 0.0),
-            "window + merge": (212771.1, 262164.9),
+            "key summary": (131153.9, 49281.4),
+            "routing": (108719.1, 2048.0),
+            "routing fallback": (32.2, 0.0),
+            "window + merge": (212716.5, 262171.1),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "7692f209989e201d", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (589931.2, 393279.9),
             "bucket scan": (70.4, 384.1),
-            "bucket scatter": (988634.7, 7025094.8),
-            "key summary": (131121.8, 16896.2),
-            "routed-block partials": (15616758.7, 31247389.4),
-            "routing": (1430016.7, 917588.2),
-            "routing fallback": (471112.7, 91.1),
-            "window + merge": (20099771.1, 3670071.5),
+            "bucket scatter": (989092.1, 7011327.2),
+            "key summary": (131121.9, 16896.3),
+            "routed-block partials": (15615811.2, 31230664.0),
+            "routing": (1476591.4, 917586.3),
+            "routing fallback": (189498.8, 89.0),
+            "window + merge": (20103058.3, 3670078.1),
         },
     },
 }
