@@ -46,7 +46,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (18537.1, 8476.0),
             "bucket scan": (20.7, 96.1),
@@ -59,7 +59,7 @@ TRAFFIC = {
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (73833.9, 34936.0),
             "bucket scan": (70.4, 384.1),
@@ -72,7 +72,7 @@ TRAFFIC = {
         },
     },
     "image_zorder_128x128": {
-        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "key summary": (131153.9, 49281.4),
             "routing": (108719.1, 2048.0),
@@ -81,7 +81,7 @@ TRAFFIC = {
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "28c9459473c521ac", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (589931.2, 393279.9),
             "bucket scan": (70.4, 384.1),

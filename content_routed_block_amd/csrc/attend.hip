@@ -6,8 +6,9 @@
 // blocks and a query-major gather would reuse nothing:
 //   0. k_transpose_v    V -> V^T in 64-key tiles, so every kernel stages V^T
 //                       with plain 16-byte copies.
-//   1. k_bucket<false>  counts, per (b, KV head, key block), the (row, slot)
-//                       pairs that selected it (LDS histogram per workgroup).
+//   1. k_bucket<false>  counts, per (bucket chunk of query positions, b, KV
+//                       head, key block), the (row, slot) pairs that selected
+//                       it (LDS histogram per workgroup).
 //   2. k_bucket_scan    bucket offsets and the work units (64 rows each).
 //   3. k_bucket<true>   scatters pair ids into bucket order and records, per
 //                       (row, slot), the pair's position in that order.
