@@ -927,7 +927,9 @@ hipError_t launch_attend(const Geometry& g, const uint16_t* q, const uint16_t* k
     const size_t lds = g.nb <= BK_LDS_MAX ? (size_t)g.nb * 4 : 0;
     launch_bucket<false>(bgrid, lds, s, ba);
     mark(ev, 4, s);
-    hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
+    // one scan workgroup per 4096 buckets (at most 16), each finding its base itself
+    const unsigned scan_wg = (unsigned)std::min<int64_t>(16, std::max<int64_t>(1, L.NB / 4096));
+    hipLaunchKernelGGL(k_bucket_scan, dim3(scan_wg), dim3(1024), 0, s, counts, offsets, cursor, unit_off,
                        NB, expand);
     mark(ev, 5, s);
     launch_bucket<true>(bgrid, lds, s, ba);

@@ -282,9 +282,12 @@ static inline void launch_bucket(dim3 grid, size_t lds, hipStream_t s, const Buc
     }
 }
 
-// Single workgroup: exclusive scans of bucket sizes and of work units
-// (ceil(count * expand / UNIT_ROWS): each pair stands for `expand` gathered
-// rows); cursor starts at the bucket offsets.
+// Exclusive scans of bucket sizes and of work units (ceil(count * expand /
+// UNIT_ROWS): each pair stands for `expand` gathered rows); cursor starts at
+// the bucket offsets.  Workgroup w scans segment w of the buckets (segments
+// of a multiple of four buckets); its base is the sum over the buckets
+// before the segment, which it reads itself (coalesced), so the workgroups
+// need nothing from each other.  Any grid size is correct.
 static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __restrict__ counts,
                                                       uint32_t* __restrict__ offsets,
                                                       uint32_t* __restrict__ cursor,
@@ -292,11 +295,37 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
                                                       int expand) {
     __shared__ uint32_t s_p[1024], s_u[1024];
     const int tid = threadIdx.x;
-    // each thread scans a run of `per` buckets (a multiple of four, so the
-    // run starts 16-byte aligned and moves in 16-byte loads and stores;
-    // entries past NB read as zero)
-    const int per = ((NB + 1023) / 1024 + 3) & ~3;
-    const int lo = min(NB, tid * per), hi = min(NB, lo + per);
+    const int seg = ((NB + (int)gridDim.x - 1) / (int)gridDim.x + 3) & ~3;
+    const int s0 = min(NB, (int)blockIdx.x * seg), s1 = min(NB, s0 + seg);
+    // inclusive block scan of (s_p, s_u)
+    auto block_scan = [&]() {
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele
+            const uint32_t ap = tid >= off ? s_p[tid - off] : 0u;
+            const uint32_t au = tid >= off ? s_u[tid - off] : 0u;
+            __syncthreads();
+            s_p[tid] += ap;
+            s_u[tid] += au;
+            __syncthreads();
+        }
+    };
+    uint32_t base_p = 0, base_u = 0;
+    if (s0 > 0) {
+        uint32_t bp = 0, bu = 0;
+        for (int i = tid; i < s0; i += 1024) {
+            const uint32_t n = counts[i];
+            bp += n;
+            bu += (n * expand + UNIT_ROWS - 1) / UNIT_ROWS;
+        }
+        s_p[tid] = bp;
+        s_u[tid] = bu;
+        block_scan();
+        base_p = s_p[1023];
+        base_u = s_u[1023];
+        __syncthreads();  // every thread has read the totals before s_p is reused
+    }
+    const int per = ((s1 - s0 + 1023) / 1024 + 3) & ~3;
+    const int lo = min(s1, s0 + tid * per), hi = min(s1, lo + per);
     auto load4 = [&](int i) {
         if (i + 4 <= NB) return *reinterpret_cast<const u32x4*>(counts + i);
         u32x4 r = {0u, 0u, 0u, 0u};
@@ -316,16 +345,8 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
     }
     s_p[tid] = sp;
     s_u[tid] = su;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-        const uint32_t ap = tid >= off ? s_p[tid - off] : 0u;
-        const uint32_t au = tid >= off ? s_u[tid - off] : 0u;
-        __syncthreads();
-        s_p[tid] += ap;
-        s_u[tid] += au;
-        __syncthreads();
-    }
-    uint32_t rp = s_p[tid] - sp, ru = s_u[tid] - su;
+    block_scan();
+    uint32_t rp = base_p + s_p[tid] - sp, ru = base_u + s_u[tid] - su;
 #pragma unroll 4
     for (int i = lo; i < hi; i += 4) {
         const u32x4 n = load4(i);
@@ -349,9 +370,9 @@ static __global__ __launch_bounds__(1024) void k_bucket_scan(const uint32_t* __r
             }
         }
     }
-    if (tid == 1023) {
-        offsets[NB] = s_p[1023];
-        unit_off[NB] = s_u[1023];
+    if (tid == 1023 && s1 == NB && (s0 < NB || blockIdx.x == 0)) {
+        offsets[NB] = base_p + s_p[1023];
+        unit_off[NB] = base_u + s_u[1023];
     }
 }
 
