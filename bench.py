@@ -46,51 +46,51 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # kernel sources and compile flags they were measured with (kernel_digest).
 TRAFFIC = {
     "qwen05b_n32k": {
-        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "03b9e71acace6ed0", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "V transpose + bucket count": (18537.1, 8476.0),
-            "bucket scan": (20.7, 96.1),
-            "bucket scatter": (15620.6, 72892.8),
-            "key summary": (4144.6, 528.2),
-            "routed-block partials": (521425.1, 941382.5),
-            "routing": (29898.5, 28672.0),
+            "V transpose + bucket count": (18535.3, 8476.0),
+            "bucket scan": (38.6, 96.1),
+            "bucket scatter": (15687.1, 71293.6),
+            "key summary": (4144.8, 528.2),
+            "routed-block partials": (521557.5, 941247.9),
+            "routing": (29898.7, 28672.0),
             "routing fallback": (18.0, 0.0),
-            "window + merge": (530623.5, 114688.8),
+            "window + merge": (530477.5, 114688.8),
         },
     },
     "qwen05b_n128k_needles": {
-        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "03b9e71acace6ed0", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (73833.9, 34936.0),
-            "bucket scan": (70.4, 384.1),
-            "bucket scatter": (119819.3, 532607.7),
+            "bucket scan": (347.2, 384.1),
+            "bucket scatter": (120013.9, 530396.3),
             "key summary": (16433.2, 2112.2),
-            "routed-block partials": (2064382.4, 3881468.0),
-            "routing": (119187.1, 114688.0),
+            "routed-block partials": (2064241.7, 3881456.8),
+            "routing": (119193.1, 114688.0),
             "routing fallback": (18.0, 0.0),
-            "window + merge": (2192306.4, 458758.1),
+            "window + merge": (2191619.8, 458757.3),
         },
     },
     "image_zorder_128x128": {
-        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "03b9e71acace6ed0", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
-            "key summary": (131153.9, 49281.4),
+            "key summary": (131153.8, 49281.8),
             "routing": (108719.1, 2048.0),
             "routing fallback": (32.2, 0.0),
-            "window + merge": (212716.5, 262171.1),
+            "window + merge": (212821.5, 262167.2),
         },
     },
     "qwen05b_n1m_needles": {
-        "csrc": "16a6302afcbba1f8", "fetch_factor": 2.0, "write_factor": 1.0,
+        "csrc": "03b9e71acace6ed0", "fetch_factor": 2.0, "write_factor": 1.0,
         "kib": {
             "V transpose + bucket count": (589931.2, 393279.9),
-            "bucket scan": (70.4, 384.1),
-            "bucket scatter": (989092.1, 7011327.2),
-            "key summary": (131121.9, 16896.3),
-            "routed-block partials": (15615811.2, 31230664.0),
-            "routing": (1476591.4, 917586.3),
-            "routing fallback": (189498.8, 89.0),
-            "window + merge": (20103058.3, 3670078.1),
+            "bucket scan": (347.2, 384.1),
+            "bucket scatter": (989062.9, 7022027.4),
+            "key summary": (131121.9, 16896.2),
+            "routed-block partials": (15615502.5, 31231887.8),
+            "routing": (1475803.4, 917586.2),
+            "routing fallback": (186619.1, 89.2),
+            "window + merge": (20101588.8, 3670079.7),
         },
     },
 }
